@@ -1,0 +1,177 @@
+"""numpy front end of the CPU oracle (oracle/lsa_ref.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the CPU-baseline leg of
+the bench, never by the product path.  It shares nothing with the HIP library.
+
+bf16 tensors travel as uint16 bit patterns, e4m3fn keys as uint8 codes.  Every function works on
+one sequence; the *_batch helpers loop over the batch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblsa_ref.so")
+KEY_BF16, KEY_E4M3 = 1, 2
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"oracle library missing: build it with python oracle/build.py "
+                               f"({LIB_PATH})")
+        L = ctypes.CDLL(LIB_PATH)
+        L.lsa_ref_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.lsa_ref_bf16_to_double.restype = ctypes.c_double
+        L.lsa_ref_e4m3fn_to_double.argtypes = [ctypes.c_uint8]
+        L.lsa_ref_e4m3fn_to_double.restype = ctypes.c_double
+        L.lsa_ref_f32_to_bf16_rne.argtypes = [ctypes.c_float]
+        L.lsa_ref_f32_to_bf16_rne.restype = ctypes.c_uint16
+        L.lsa_ref_index_scores.argtypes = [_I64, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _P,
+                                           _P, _P, _P]
+        L.lsa_ref_select.argtypes = [_I64, _I64, _P, _P, _P, _I32, _I32, _I32, _P]
+        L.lsa_ref_page_keys.argtypes = [_I64, _I32, _I32, _P, _I32, _P, _P]
+        L.lsa_ref_page_recall.argtypes = [_I64, _I32, _I32, _I64, _P, _P, _P, _P, _P, _I32, _P,
+                                          _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]
+        L.lsa_ref_sparse_attn.argtypes = [_I64, _I32, _I32, _I32, _I32, _P, _P, _I64, _P, _I64,
+                                          _P, ctypes.c_double, _P, _P]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _key_args(keys, scale):
+    keys = np.ascontiguousarray(keys)
+    if keys.dtype == np.uint16:
+        return keys, KEY_BF16, None
+    assert keys.dtype == np.uint8 and scale is not None
+    return keys, KEY_E4M3, _c(scale, np.float32)
+
+
+# --------------------------------------------------------------------------------- formats
+def bf16_to_double(bits: int) -> float:
+    return lib().lsa_ref_bf16_to_double(int(bits))
+
+
+def e4m3fn_to_double(code: int) -> float:
+    return lib().lsa_ref_e4m3fn_to_double(int(code))
+
+
+def f32_to_bf16_rne(x: float) -> int:
+    return lib().lsa_ref_f32_to_bf16_rne(float(x))
+
+
+# --------------------------------------------------------------------------------- a1 scores
+def index_scores(q, w, keys, scale, pos):
+    """q uint16 [T,H,d], w f32 [T,H], keys [L,d] (uint16 bf16 bits or uint8 e4m3 codes),
+    scale f32 [L] or None, pos int64 [T] -> (I, A, E) fp64 [T,L]."""
+    q = _c(q, np.uint16)
+    T, H, d = q.shape
+    keys, kd, scale = _key_args(keys, scale)
+    L = keys.shape[0]
+    w = _c(w, np.float32)
+    pos = _c(pos, np.int64)
+    I = np.empty((T, L), np.float64)
+    A = np.empty((T, L), np.float64)
+    E = np.empty((T, L), np.float64)
+    lib().lsa_ref_index_scores(T, H, d, L, _ptr(pos), _ptr(q), _ptr(w), _ptr(keys), kd,
+                               _ptr(scale), _ptr(I), _ptr(A), _ptr(E))
+    return I, A, E
+
+
+# --------------------------------------------------------------------------------- a2 select
+def select(scores, V, k, S, W, cand_ids=None):
+    """scores f32 [T,n] (flat: n == L), V int64 [T] valid lengths, cand_ids int32 [T,n] or None
+    -> idx int32 [T,k]."""
+    scores = _c(scores, np.float32)
+    T, n = scores.shape
+    V = _c(V, np.int64)
+    cid = None if cand_ids is None else _c(cand_ids, np.int32)
+    idx = np.empty((T, k), np.int32)
+    lib().lsa_ref_select(T, n, _ptr(scores), _ptr(cid), _ptr(V), k, S, W, _ptr(idx))
+    return idx
+
+
+# --------------------------------------------------------------------------------- a3 pages
+def page_keys(keys, scale, P):
+    keys, kd, scale = _key_args(keys, scale)
+    L, d = keys.shape
+    pk = np.empty(((L + P - 1) // P, d), np.uint16)
+    lib().lsa_ref_page_keys(L, d, P, _ptr(keys), kd, _ptr(scale), _ptr(pk))
+    return pk
+
+
+# --------------------------------------------------------------------------------- a4/a5 HI
+def page_recall(q, w, pk, keys, scale, pos, k, S, W, P, M):
+    """-> dict(page_ids [T,M], cand_ids [T,M*P], cand_scores fp64 [T,M*P],
+    coarse fp64 [T,n_pages], n_scored [T])."""
+    q = _c(q, np.uint16)
+    T, H, d = q.shape
+    keys, kd, scale = _key_args(keys, scale)
+    L = keys.shape[0]
+    n_pages = (L + P - 1) // P
+    pk = _c(pk, np.uint16)
+    assert pk.shape == (n_pages, d)
+    w = _c(w, np.float32)
+    pos = _c(pos, np.int64)
+    out = dict(page_ids=np.empty((T, M), np.int32), cand_ids=np.empty((T, M * P), np.int32),
+               cand_scores=np.empty((T, M * P), np.float64),
+               coarse=np.empty((T, n_pages), np.float64), n_scored=np.empty(T, np.int64))
+    lib().lsa_ref_page_recall(T, H, d, L, _ptr(pos), _ptr(q), _ptr(w), _ptr(pk), _ptr(keys), kd,
+                              _ptr(scale), k, S, W, P, M, _ptr(out["page_ids"]),
+                              _ptr(out["cand_ids"]), _ptr(out["cand_scores"]),
+                              _ptr(out["coarse"]), _ptr(out["n_scored"]))
+    return out
+
+
+# --------------------------------------------------------------------------------- a6/a7 attn
+def sparse_attn(q, kmat, vmat, idx, tau, d_qk=None, d_v=None):
+    """q uint16 [T,Hq,d_qk]; kmat uint16 [L,ks] (first d_qk columns are K); vmat uint16 [L,vs]
+    (first d_v columns are V; may be the same array as kmat for a latent cache);
+    idx int32 [T,k] -> (o fp64 [T,Hq,d_v], lse fp64 [T,Hq])."""
+    q = _c(q, np.uint16)
+    T, Hq, dq = q.shape
+    d_qk = dq if d_qk is None else d_qk
+    kmat = _c(kmat, np.uint16)
+    vmat = kmat if vmat is None else _c(vmat, np.uint16)
+    d_v = vmat.shape[1] if d_v is None else d_v
+    idx = _c(idx, np.int32)
+    k = idx.shape[1]
+    o = np.empty((T, Hq, d_v), np.float64)
+    lse = np.empty((T, Hq), np.float64)
+    lib().lsa_ref_sparse_attn(T, Hq, d_qk, d_v, k, _ptr(q), _ptr(kmat), kmat.shape[1],
+                              _ptr(vmat), vmat.shape[1], _ptr(idx), float(tau), _ptr(o),
+                              _ptr(lse))
+    return o, lse
+
+
+def cross_layer_attn(layers, idx, tau, d_qk=None, d_v=None):
+    """Cross-Layer Indexing: every layer (q, kmat, vmat) attends over the same idx."""
+    return [sparse_attn(q, km, vm, idx, tau, d_qk, d_v) for (q, km, vm) in layers]
+
+
+# --------------------------------------------------------------------------------- helpers
+def valid_lengths(L: int, q_pos0: int, n_q: int) -> np.ndarray:
+    """V_t = min(L, q_pos0 + t + 1) for t in [0, n_q)."""
+    return np.minimum(L, q_pos0 + np.arange(n_q, dtype=np.int64) + 1)
+
+
+def positions(q_pos0: int, n_q: int) -> np.ndarray:
+    return q_pos0 + np.arange(n_q, dtype=np.int64)

@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _oracle_built():
+    """The CPU oracle is C; build it once if it is missing (building the checker is not using
+    it)."""
+    from oracle import build, ref
+    if not os.path.exists(ref.LIB_PATH):
+        build.build()
+    yield
