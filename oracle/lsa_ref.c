@@ -26,12 +26,16 @@
  * closed forms, invariants, brute force on tiny inputs); no function is "parity unpinned".
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define REF_KEY_BF16 1
 #define REF_KEY_E4M3 2
+
+/* Threads the parallel loops below use (for reporting CPU timings). */
+int lsa_ref_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------------------------ */
 /* Number formats.                                                                             */

@@ -31,6 +31,7 @@ def lib():
             raise RuntimeError(f"oracle library missing: build it with python oracle/build.py "
                                f"({LIB_PATH})")
         L = ctypes.CDLL(LIB_PATH)
+        L.lsa_ref_num_threads.restype = ctypes.c_int
         L.lsa_ref_bf16_to_double.argtypes = [ctypes.c_uint16]
         L.lsa_ref_bf16_to_double.restype = ctypes.c_double
         L.lsa_ref_e4m3fn_to_double.argtypes = [ctypes.c_uint8]
@@ -63,6 +64,10 @@ def _key_args(keys, scale):
         return keys, KEY_BF16, None
     assert keys.dtype == np.uint8 and scale is not None
     return keys, KEY_E4M3, _c(scale, np.float32)
+
+
+def num_threads() -> int:
+    return lib().lsa_ref_num_threads()
 
 
 # --------------------------------------------------------------------------------- formats

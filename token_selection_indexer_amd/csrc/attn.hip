@@ -1,0 +1,377 @@
+// attn.hip -- attention restricted to the selected tokens.
+//
+// (Baidu Cloud article, "3. Sparse Attention Calculator": ordinary softmax attention over the
+// top-k tokens only; model card: LSA replaces the dense MLA of LongCat-Flash-Lite, so the cache
+// is a latent one whose rows serve as both K (all d_qk columns) and V (the first d_v columns),
+// shared by every query head.  Paper summary page, strategy (2): the same index list serves
+// several consecutive layers.)
+//
+// Latent (MLA) kernel.  A workgroup of 4 waves owns one (sequence, query, group of 16 heads) and
+// a contiguous chunk of the index list.  Per round, 64 selected rows (d_qk bf16 each) are
+// gathered into LDS with 16-byte loads -- each row is one contiguous run in HBM, and the
+// sink / window runs are contiguous across rows -- then
+//   logits  S[16 x 64] = Q[16 x d_qk] . K^T   v_mfma_f32_16x16x32_bf16, one 16-row tile per wave
+//   softmax online, fp32, base-2 exponent, per head over the rounds
+//   output  O[16 x d_v] += P[16 x 64] . V     v_mfma_f32_16x16x32_bf16, d_v/4 columns per wave
+// When the list is split over several workgroups, each writes (max, sum, unnormalised O) and a
+// combine kernel merges the splits in a fixed order (no atomics: identical inputs give
+// identical bits, which also makes reuse across layers reproducible).
+//
+// Per-head kernel (any head count, d <= 256, separate K and V): one wave per (query, head);
+// lanes score one selected row each, then own output columns and stream the V rows.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace lsa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+constexpr int AR = 64;          // rows per round
+constexpr int MLA_MAX_DQK = 576;
+constexpr int MLA_MAX_DV = 512;
+
+__device__ __forceinline__ bool row_ok(int32_t id, int64_t kv_len) { return id >= 0 && id < kv_len; }
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
+{
+    constexpr int ROWB = DQK * 2 + 32;     // LDS bytes per gathered row (pad: see P.V below)
+    constexpr int KS = DQK / 32;           // K-steps of the logit product
+    constexpr int CPR = DQK * 2 / 16;      // 16-byte chunks per row
+    constexpr int NTW = DV / 4 / 16;       // 16-column output tiles per wave
+    static_assert(DQK % 32 == 0 && DV % 64 == 0, "shape");
+
+    __shared__ __attribute__((aligned(16))) uint8_t rows[AR * ROWB];
+    __shared__ float S[16][AR + 1];
+    __shared__ __attribute__((aligned(16))) uint16_t Pm[16][AR + 8];
+    __shared__ int32_t rid[AR];
+    __shared__ float m_run[16], l_run[16], alpha[16];
+
+    const int HG = a.heads / 16;
+    const int b = blockIdx.z;
+    const int t = blockIdx.y / HG;
+    const int hg = blockIdx.y % HG;
+    const int split = blockIdx.x;
+    const int l = lane_id(), w = wave_id();
+    const int64_t qrow = (int64_t)b * a.n_q + t;
+
+    const int chunk = ((a.n_idx + a.n_split - 1) / a.n_split + AR - 1) / AR * AR;
+    const int c_begin = split * chunk;
+    const int c_end = min(a.n_idx, c_begin + chunk);
+
+    // Q fragments: lane l holds head 16*hg + l%16, d = 32*kk + 8*(l/16) + [0,8)
+    bf16x8_t qf[KS];
+    {
+        const uint16_t *qp = a.q + (qrow * a.heads + 16 * hg + (l & 15)) * DQK + 8 * (l >> 4);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) qf[kk] = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(qp + 32 * kk));
+    }
+    if (threadIdx.x < 16) {
+        m_run[threadIdx.x] = -INFINITY;
+        l_run[threadIdx.x] = 0.0f;
+    }
+    f32x4_t oacc[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) oacc[nt] = f32x4_t{};
+
+    const int32_t *idx_row = a.idx + qrow * a.n_idx;
+    const uint8_t *kv_b = reinterpret_cast<const uint8_t *>(a.k) + (int64_t)b * a.kv_len * a.k_stride * 2;
+    const float sl2 = a.scale * kLog2e;
+
+    for (int c0 = c_begin; c0 < c_end; c0 += AR) {
+        if (threadIdx.x < AR) {
+            const int j = c0 + threadIdx.x;
+            const int32_t id = j < c_end ? idx_row[j] : -1;
+            rid[threadIdx.x] = row_ok(id, a.kv_len) ? id : -1;
+        }
+        __syncthreads();
+        // gather the rows (invalid rows are zero-filled so no NaN can reach the MFMA)
+        for (int c = threadIdx.x; c < AR * CPR; c += 256) {
+            const int r = c / CPR, col = c % CPR;
+            const int32_t id = rid[r];
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (id >= 0) v = reinterpret_cast<const uint4 *>(kv_b + (int64_t)id * a.k_stride * 2)[col];
+            *reinterpret_cast<uint4 *>(&rows[r * ROWB + col * 16]) = v;
+        }
+        __syncthreads();
+        // logits: wave w takes rows 16w .. 16w+15
+        {
+            f32x4_t acc = f32x4_t{};
+            const uint8_t *kr = &rows[(16 * w + (l & 15)) * ROWB + 16 * (l >> 4)];
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const bf16x8_t bk = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(kr + 64 * kk));
+                acc = mfma_16x16x32(qf[kk], bk, acc);
+            }
+            const int r = 16 * w + (l & 15);
+            const bool ok = rid[r] >= 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[4 * (l >> 4) + i][r] = ok ? acc[i] * sl2 : -INFINITY;
+        }
+        __syncthreads();
+        // online softmax: 16 threads per head, 4 rows each
+        {
+            const int h = threadIdx.x >> 4, part = threadIdx.x & 15;
+            float s[4], mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s[i] = S[h][4 * part + i];
+                mx = fmaxf(mx, s[i]);
+            }
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+            const float m_old = m_run[h];
+            const float m_new = fmaxf(m_old, mx);
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = (m_new == -INFINITY || s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_new);
+                const uint32_t bits = f32_to_bf16_bits(p);
+                sum += bf16_bits_to_f32(bits); // normalise by what the product actually uses
+                // row r = 4*part + i sits at K position 32*(r/32) + 8*(r%4) + (r%32)/4
+                Pm[h][32 * (part >> 3) + 8 * i + (part & 7)] = (uint16_t)bits;
+            }
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
+            __syncthreads(); // every reader of m_run has it before it changes
+            if (part == 0) {
+                const float al = (m_old == -INFINITY) ? 0.0f : exp2f(m_old - m_new);
+                alpha[h] = al;
+                l_run[h] = l_run[h] * al + sum;
+                m_run[h] = m_new;
+            }
+        }
+        __syncthreads();
+        // O = O * alpha + P . V ; wave w owns columns [w*DV/4, (w+1)*DV/4).  The K index of
+        // this product is permuted within each 32-row step: lane group g = l/16 element e
+        // is row g + 4e, so the four groups of one read touch four consecutive rows (disjoint
+        // LDS banks with the row padding) instead of rows 8 apart (same banks).  P was stored in
+        // the same permuted order.
+        {
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = alpha[4 * (l >> 4) + i];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) oacc[nt][i] *= al[i];
+#pragma unroll
+            for (int kk = 0; kk < AR / 32; ++kk) {
+                const bf16x8_t pf = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(&Pm[l & 15][32 * kk + 8 * (l >> 4)]));
+                const int r0 = 32 * kk + (l >> 4);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const int col = w * (DV / 4) + 16 * nt + (l & 15);
+                    const uint16_t *vp = reinterpret_cast<const uint16_t *>(&rows[r0 * ROWB]) + col;
+                    constexpr int RS = 4 * (ROWB / 2); // 4 rows, in uint16 elements
+                    uint32_t v01 = vp[0] | ((uint32_t)vp[RS] << 16);
+                    uint32_t v23 = vp[2 * RS] | ((uint32_t)vp[3 * RS] << 16);
+                    uint32_t v45 = vp[4 * RS] | ((uint32_t)vp[5 * RS] << 16);
+                    uint32_t v67 = vp[6 * RS] | ((uint32_t)vp[7 * RS] << 16);
+                    const bf16x8_t vf = bitcast<bf16x8_t>(make_uint4(v01, v23, v45, v67));
+                    oacc[nt] = mfma_16x16x32(pf, vf, oacc[nt]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // epilogue: lane holds O[head 4*(l/16)+i][col w*DV/4 + 16*nt + l%16]
+    if (a.n_split == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * (l >> 4) + i;
+            const float lr = l_run[h];
+            const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+            uint16_t *op = a.out + (qrow * a.heads + 16 * hg + h) * DV;
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                const int col = w * (DV / 4) + 16 * nt + (l & 15);
+                op[col] = (uint16_t)f32_to_bf16_bits(oacc[nt][i] * inv);
+            }
+        }
+        if (a.lse && threadIdx.x < 16) {
+            const float lr = l_run[threadIdx.x];
+            a.lse[qrow * a.heads + 16 * hg + threadIdx.x] =
+                lr > 0.0f ? (m_run[threadIdx.x] + log2f(lr)) * kLn2 : -INFINITY;
+        }
+    } else {
+        // partial block: [DV] O values, then (m, l), per (query, head, split)
+        const int64_t stride = DV + 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = 4 * (l >> 4) + i;
+            float *pp = a.ws + ((qrow * a.heads + 16 * hg + h) * a.n_split + split) * stride;
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) pp[w * (DV / 4) + 16 * nt + (l & 15)] = oacc[nt][i];
+        }
+        if (threadIdx.x < 16) {
+            float *pp = a.ws + ((qrow * a.heads + 16 * hg + threadIdx.x) * a.n_split + split) * stride;
+            pp[DV] = m_run[threadIdx.x];
+            pp[DV + 1] = l_run[threadIdx.x];
+        }
+    }
+}
+
+// Merge the splits of one (query, head): fixed order over splits.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
+{
+    const int64_t qh = blockIdx.x; // (b * n_q + t) * heads + h
+    const int64_t stride = a.d_v + 2;
+    const float *base = a.ws + qh * a.n_split * stride;
+    float M = -INFINITY;
+    for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, base[s * stride + a.d_v]);
+    float L = 0.0f;
+    for (int s = 0; s < a.n_split; ++s) {
+        const float m = base[s * stride + a.d_v];
+        if (m != -INFINITY) L += base[s * stride + a.d_v + 1] * exp2f(m - M);
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    for (int c = threadIdx.x; c < a.d_v; c += blockDim.x) {
+        float o = 0.0f;
+        for (int s = 0; s < a.n_split; ++s) {
+            const float m = base[s * stride + a.d_v];
+            if (m != -INFINITY) o += base[s * stride + c] * exp2f(m - M);
+        }
+        a.out[qh * a.d_v + c] = (uint16_t)f32_to_bf16_bits(o * inv);
+    }
+    if (a.lse && threadIdx.x == 0) a.lse[qh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+// Per-head kernel: one wave per (query, head).
+constexpr int MHA_CHUNK = 256;
+constexpr int MHA_MAXD = 256;
+
+__global__ __launch_bounds__(256) void mha_attn_kernel(AttnArgs a)
+{
+    __shared__ float qs[4][MHA_MAXD];
+    __shared__ float ps[4][MHA_CHUNK];
+    __shared__ int32_t ids[4][MHA_CHUNK];
+    const int l = lane_id(), w = wave_id();
+    const int64_t total = (int64_t)a.batch * a.n_q * a.heads;
+    const int64_t unit_raw = (int64_t)blockIdx.x * 4 + w; // (b * n_q + t) * heads + h
+    const bool live = unit_raw < total;                   // idle waves still reach the barriers
+    const int64_t unit = live ? unit_raw : total - 1;
+    const int64_t qrow = unit / a.heads;
+    const int b = (int)(qrow / a.n_q);
+    const uint16_t *qp = a.q + unit * a.d_qk;
+    for (int d = l; d < a.d_qk; d += kWave) qs[w][d] = bf16_bits_to_f32(qp[d]);
+    const uint16_t *kb = a.k + (int64_t)b * a.kv_len * a.k_stride;
+    const uint16_t *vb = a.v + (int64_t)b * a.kv_len * a.v_stride;
+    const int32_t *idx_row = a.idx + qrow * a.n_idx;
+    const float sl2 = a.scale * kLog2e;
+    constexpr int VPL = MHA_MAXD / kWave; // output columns per lane (at most)
+    float acc[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) acc[i] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+    __syncthreads();
+    for (int c0 = 0; c0 < a.n_idx; c0 += MHA_CHUNK) {
+        const int cn = min(MHA_CHUNK, a.n_idx - c0);
+        float cmax = -INFINITY;
+        for (int j = l; j < cn; j += kWave) {
+            const int32_t id = idx_row[c0 + j];
+            float lg = -INFINITY;
+            if (row_ok(id, a.kv_len)) {
+                const uint16_t *kr = kb + (int64_t)id * a.k_stride;
+                float dot = 0.0f;
+                for (int d = 0; d < a.d_qk; d += 8) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(kr + d);
+                    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dot = fmaf(qs[w][d + 2 * e], __uint_as_float(u[e] << 16), dot);
+                        dot = fmaf(qs[w][d + 2 * e + 1], __uint_as_float(u[e] & 0xffff0000u), dot);
+                    }
+                }
+                lg = dot * sl2;
+            }
+            ps[w][j] = lg;
+            ids[w][j] = row_ok(id, a.kv_len) ? id : -1;
+            cmax = fmaxf(cmax, lg);
+        }
+        cmax = wave_max(cmax);
+        __syncthreads();
+        const float m_new = fmaxf(m_run, cmax);
+        const float al = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+        float csum = 0.0f;
+        for (int j = l; j < cn; j += kWave) {
+            const float p = (m_new == -INFINITY || ps[w][j] == -INFINITY) ? 0.0f : exp2f(ps[w][j] - m_new);
+            ps[w][j] = p;
+            csum += p;
+        }
+        csum = wave_sum(csum);
+        __syncthreads();
+        l_run = l_run * al + csum;
+        m_run = m_new;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) acc[i] *= al;
+        for (int j = 0; j < cn; ++j) {
+            const int32_t id = ids[w][j];
+            if (id < 0) continue;
+            const float p = ps[w][j];
+            const uint16_t *vr = vb + (int64_t)id * a.v_stride;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int c = l + kWave * i;
+                if (c < a.d_v) acc[i] = fmaf(p, bf16_bits_to_f32(vr[c]), acc[i]);
+            }
+        }
+        __syncthreads();
+    }
+    if (!live) return;
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    uint16_t *op = a.out + unit * a.d_v;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int c = l + kWave * i;
+        if (c < a.d_v) op[c] = (uint16_t)f32_to_bf16_bits(acc[i] * inv);
+    }
+    if (a.lse && l == 0) a.lse[unit] = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+}
+
+} // namespace
+
+bool attn_supported(int heads, int d_qk, int d_v, int latent)
+{
+    if (latent) return heads % 16 == 0 && d_qk == MLA_MAX_DQK && d_v == MLA_MAX_DV;
+    return heads >= 1 && d_qk % 8 == 0 && d_v % 8 == 0 && d_qk <= MHA_MAXD && d_v <= MHA_MAXD;
+}
+
+int attn_splits(int batch, int n_q, int heads, int n_idx, int latent)
+{
+    if (!latent) return 1;
+    const int64_t units = (int64_t)batch * n_q * (heads / 16);
+    const int max_split = (n_idx + AR - 1) / AR;
+    int64_t want = (512 + units - 1) / units;
+    if (want > max_split) want = max_split;
+    if (want > 32) want = 32;
+    return want < 1 ? 1 : (int)want;
+}
+
+size_t attn_workspace_bytes(int batch, int n_q, int heads, int d_v, int n_idx, int latent)
+{
+    const int s = attn_splits(batch, n_q, heads, n_idx, latent);
+    if (s <= 1) return 0;
+    return (size_t)batch * n_q * heads * s * (d_v + 2) * sizeof(float);
+}
+
+hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t st)
+{
+    const int64_t rows = (int64_t)a.batch * a.n_q;
+    if (rows == 0) return hipSuccess;
+    if (a.latent) {
+        dim3 grid((unsigned)a.n_split, (unsigned)(a.n_q * (a.heads / 16)), (unsigned)a.batch);
+        hipLaunchKernelGGL((mla_attn_kernel<MLA_MAX_DQK, MLA_MAX_DV>), grid, dim3(256), 0, st, a);
+        if (a.n_split > 1)
+            hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows * a.heads)), dim3(256), 0, st, a);
+    } else {
+        const int64_t units = rows * a.heads;
+        hipLaunchKernelGGL(mha_attn_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+} // namespace lsa

@@ -1,0 +1,512 @@
+// score.hip -- Lightning-Indexer scoring on gfx950 bf16 MFMA.
+//
+//   I[t,s] = sum_h w[t,h] * ReLU( q[t,h] . k[s] )       (times scale[s] for e4m3 keys)
+//
+// (Baidu Cloud article on DeepSeek's Lightning Indexer, "1. Lightweight Scoring Module": ReLU of
+// query-key dot products; the indexer weights its heads per query.)
+//
+// The contraction over d runs on v_mfma_f32_32x32x16_bf16: the M dimension holds indexer rows
+// (query, head) pairs, N holds 32 keys, K is d.  The ReLU, the head weights and the head sum are
+// fused into the epilogue on the fp32 accumulators, so only one fp32 per (query, key) leaves the
+// kernel.  e4m3 keys are widened to bf16 exactly (gfx950 cvt_scalef32_pk_bf16_fp8, unit scale) and
+// their per-token scale is applied once after the head sum.
+//
+// Two kernels:
+//  * stream: each wave owns its own 32-key blocks and loads them straight from HBM into the
+//    MFMA operand registers (no reuse between waves: decode has one query per sequence, so the
+//    key cache is read exactly once).  Also runs the fine stage of Hierarchical Indexing, where
+//    the blocks come from each query's recalled pages.
+//  * tile: prefill.  A workgroup owns WAVES*NQW queries; 64-key tiles are staged once in LDS
+//    (bf16, padded rows) and shared by every wave, double-buffered against the next tile's
+//    global loads.
+//
+// Operand layout.  The two lane halves split d: half g = l/32 holds d in [g*D/2, (g+1)*D/2);
+// K-step kk feeds d = g*D/2 + 8*kk + [0,8) as the MFMA's K index 8*g + [0,8).  This permutes the
+// contraction index identically for q and k, so a lane loads D/2 contiguous elements of a key
+// row.  Accumulator register r of M-tile mt in lane half g is indexer row
+//   r' = 16*MT*g + 16*mt + r,   (query slot, head) = (r' / H, r' % H)
+// so with 16*MT >= H every lane holds whole queries and the head sum stays in the lane; with
+// H = 32*MT the two halves each hold half of one query's heads and one cross-half add finishes.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace lsa {
+namespace {
+
+// Indexer-row geometry of a wave.
+template <int H, int MT, bool ONEQ>
+struct Geo {
+    static constexpr int ROWS = 32 * MT;
+    static constexpr int VPL = 16 * MT;                       // accumulator values per lane
+    static constexpr bool SPLIT = ONEQ || (H > VPL);          // query spans both lane halves
+    static constexpr int NQW = ONEQ ? 1 : (ROWS / H);         // queries per wave
+    static constexpr int NQL = SPLIT ? 1 : (VPL / H);         // queries per lane half
+    static_assert(ONEQ || ROWS % H == 0, "heads must divide the wave's rows");
+    static_assert(ONEQ || H <= VPL || H == ROWS, "unsupported head split");
+};
+
+// Indexer row r' of A-operand row rho of M-tile mt.
+template <int MT>
+__device__ __forceinline__ int a_row_to_rprime(int mt, int rho)
+{
+    return 16 * MT * ((rho >> 2) & 1) + 16 * mt + 4 * (rho >> 3) + (rho & 3);
+}
+
+template <int H, bool ONEQ>
+__device__ __forceinline__ void rprime_to_qh(int rp, int &qs, int &h, bool &valid)
+{
+    if (ONEQ) {
+        qs = 0;
+        h = rp;
+        valid = rp < H;
+    } else {
+        qs = rp / H;
+        h = rp % H;
+        valid = true;
+    }
+}
+
+// Valid key range [lo, hi) of query t.
+__device__ __forceinline__ void row_range(const ScoreArgs &a, int64_t t, int64_t &lo, int64_t &hi)
+{
+    int64_t V = a.q_pos0 + t + 1;
+    if (V > a.kv_len) V = a.kv_len;
+    if (a.mask == MASK_CAUSAL) {
+        lo = 0;
+        hi = V;
+    } else { // MASK_PAGES
+        if (V <= a.k) {
+            lo = 0;
+            hi = 0;
+        } else {
+            lo = a.sink / a.page;
+            hi = (V - a.window - 1) / a.page + 1;
+        }
+    }
+}
+
+template <int D, int H, int MT, bool ONEQ>
+__device__ __forceinline__ void load_q(bf16x8_t (&qf)[MT][D / 16], const uint16_t *qbase,
+                                       int nq_avail)
+{
+    const int l = lane_id(), rho = l & 31, gk = l >> 5;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        int qs, h;
+        bool valid;
+        rprime_to_qh<H, ONEQ>(a_row_to_rprime<MT>(mt, rho), qs, h, valid);
+        valid = valid && qs < nq_avail;
+        const uint16_t *src = qbase + ((int64_t)qs * H + h) * D + (D / 2) * gk;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            uint4 v = valid ? *reinterpret_cast<const uint4 *>(src + 8 * kk) : make_uint4(0, 0, 0, 0);
+            qf[mt][kk] = bitcast<bf16x8_t>(v);
+        }
+    }
+}
+
+template <int H, int MT, bool ONEQ>
+__device__ __forceinline__ void load_w(float (&wv)[16 * MT], const float *wbase, int nq_avail)
+{
+    const int g = lane_id() >> 5;
+#pragma unroll
+    for (int v = 0; v < 16 * MT; ++v) {
+        int qs, h;
+        bool valid;
+        rprime_to_qh<H, ONEQ>(16 * MT * g + v, qs, h, valid);
+        wv[v] = (valid && qs < nq_avail) ? wbase[qs * H + h] : 0.0f;
+    }
+}
+
+// ReLU, head weights and head sum over the lane's accumulators.  part[u] is the partial score of
+// lane-half query slot u (all slots complete unless SPLIT, where a cross-half add follows).
+template <int H, int MT, bool ONEQ>
+__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[MT], const float (&wv)[16 * MT],
+                                         float (&part)[Geo<H, MT, ONEQ>::NQL])
+{
+    using G = Geo<H, MT, ONEQ>;
+#pragma unroll
+    for (int u = 0; u < G::NQL; ++u) part[u] = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int v = 16 * mt + r;
+            const int u = G::SPLIT ? 0 : v / H;
+            part[u] = fmaf(wv[v], fmaxf(acc[mt][r], 0.0f), part[u]);
+        }
+    }
+    if (G::SPLIT) part[0] += __shfl_xor(part[0], 32, kWave);
+}
+
+// ------------------------------------------------------------------------------------------
+// stream kernel
+// ------------------------------------------------------------------------------------------
+
+// One key row's operand: lane's D/2 elements as D/16 bf16x8 fragments.
+template <bool FP8, int D>
+struct KeyFrag {
+    static constexpr int NLOAD = FP8 ? D / 32 : D / 16; // uint4 loads per lane
+    uint4 raw[NLOAD];
+
+    __device__ __forceinline__ void load(const void *keys, int64_t row, int gk)
+    {
+        const uint8_t *p = reinterpret_cast<const uint8_t *>(keys) +
+                           (row * D + (D / 2) * gk) * (FP8 ? 1 : 2);
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) raw[i] = reinterpret_cast<const uint4 *>(p)[i];
+    }
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) raw[i] = make_uint4(0, 0, 0, 0);
+    }
+    __device__ __forceinline__ bf16x8_t frag(int kk) const
+    {
+        if (FP8) {
+            const uint4 c = raw[kk >> 1];
+            return (kk & 1) ? e4m3x8_to_bf16x8(make_uint2(c.z, c.w))
+                            : e4m3x8_to_bf16x8(make_uint2(c.x, c.y));
+        }
+        return bitcast<bf16x8_t>(raw[kk]);
+    }
+};
+
+template <bool FP8, int D, int H, int MT, bool ONEQ, bool FINE, int WAVES, int BPW>
+__global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
+{
+    using G = Geo<H, MT, ONEQ>;
+    constexpr int KS = D / 16;
+    const int b = blockIdx.z;
+    const int64_t t0 = (int64_t)blockIdx.y * G::NQW;
+    const int nq_avail = (int)min((int64_t)G::NQW, (int64_t)a.n_q - t0);
+    const int l = lane_id(), wv_id = wave_id(), g = l >> 5, n = l & 31;
+
+    bf16x8_t qf[MT][KS];
+    load_q<D, H, MT, ONEQ>(qf, a.q + ((int64_t)b * a.n_q + t0) * H * D, nq_avail);
+    float wv[G::VPL];
+    load_w<H, MT, ONEQ>(wv, a.w + ((int64_t)b * a.n_q + t0) * H, nq_avail);
+
+    // Valid ranges of the lane's query slots, and the wave-wide hull.
+    int64_t lo[G::NQL], hi[G::NQL];
+    int64_t lo_all = INT64_MAX, hi_all = 0;
+#pragma unroll
+    for (int u = 0; u < G::NQL; ++u) {
+        const int qs = G::SPLIT ? 0 : g * G::NQL + u;
+        if (qs < nq_avail) {
+            row_range(a, t0 + qs, lo[u], hi[u]);
+        } else {
+            lo[u] = 0;
+            hi[u] = 0;
+        }
+    }
+    if (FINE) {
+        int64_t V = a.q_pos0 + t0 + 1;
+        if (V > a.kv_len) V = a.kv_len;
+        lo_all = a.sink;
+        hi_all = V > a.k ? V - a.window : 0;
+        lo[0] = lo_all;
+        hi[0] = hi_all;
+    } else {
+        for (int qs = 0; qs < nq_avail; ++qs) {
+            int64_t x, y;
+            row_range(a, t0 + qs, x, y);
+            if (y > x) {
+                lo_all = min(lo_all, x);
+                hi_all = max(hi_all, y);
+            }
+        }
+    }
+
+    const uint8_t *keys_b = reinterpret_cast<const uint8_t *>(a.keys) +
+                            (int64_t)b * a.n_keys * D * (FP8 ? 1 : 2);
+    const float *scale_b = FP8 ? a.kscale + (int64_t)b * a.n_keys : nullptr;
+    const int32_t *pages_row = FINE ? a.pages + ((int64_t)b * a.n_q + t0) * a.m_pages : nullptr;
+    const int64_t n_blocks = (a.n_out + 31) / 32;
+
+    for (int it = 0; it < BPW; ++it) {
+        const int64_t blk = ((int64_t)blockIdx.x * BPW + it) * WAVES + wv_id;
+        if (blk >= n_blocks) break;
+        const int64_t s0 = blk * 32; // output slot of lane n is s0 + n
+
+        // Key row of this lane's slot and whether the block needs any compute.
+        int64_t row;
+        bool block_live;
+        if (FINE) {
+            const int64_t pi = s0 / a.page;
+            const int pid = pages_row[pi];
+            const int64_t tok0 = (int64_t)pid * a.page + (s0 - pi * a.page);
+            row = tok0 + n;
+            block_live = pid >= 0 && tok0 < hi_all && tok0 + 32 > lo_all;
+        } else {
+            row = s0 + n;
+            block_live = s0 < hi_all && s0 + 32 > lo_all;
+        }
+
+        float part[G::NQL];
+        if (block_live) {
+            KeyFrag<FP8, D> kf;
+            const int64_t lrow = row < a.n_keys ? row : a.n_keys - 1;
+            kf.load(keys_b, lrow, g);
+            f32x16_t acc[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16_t{};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const bf16x8_t bk = kf.frag(kk);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_32x32x16(qf[mt][kk], bk, acc[mt]);
+            }
+            epilogue<H, MT, ONEQ>(acc, wv, part);
+            if (FP8) {
+                const float sc = scale_b[lrow];
+#pragma unroll
+                for (int u = 0; u < G::NQL; ++u) part[u] *= sc;
+            }
+        }
+
+        if (G::SPLIT && g != 0) continue;
+#pragma unroll
+        for (int u = 0; u < G::NQL; ++u) {
+            const int qs = G::SPLIT ? 0 : g * G::NQL + u;
+            if (qs >= nq_avail || s0 + n >= a.n_out) continue;
+            const bool ok = block_live && row >= lo[u] && row < hi[u] && row < a.n_keys;
+            const int64_t o = ((int64_t)b * a.n_q + t0 + qs) * a.n_out + s0 + n;
+            a.out[o] = ok ? part[u] : -INFINITY;
+            if (FINE) a.out_ids[o] = ok ? (int32_t)row : -1;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// tile kernel (prefill)
+// ------------------------------------------------------------------------------------------
+
+template <bool FP8, int D, int H, int MT, int WAVES, int KB>
+__global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
+{
+    using G = Geo<H, MT, false>;
+    constexpr int KS = D / 16;
+    constexpr int QPB = WAVES * G::NQW;
+    constexpr int ROWB = D * 2 + 16;                  // LDS bytes per staged key (bf16 + pad)
+    constexpr int ESZ = FP8 ? 1 : 2;
+    constexpr int CPR = D * ESZ / 16;                 // 16-byte source chunks per key row
+    constexpr int CHUNKS = KB * CPR;
+    constexpr int NT = WAVES * kWave;
+    constexpr int CPT = (CHUNKS + NT - 1) / NT;       // chunks per thread per tile
+    static_assert(KB % 32 == 0, "tile of whole MFMA blocks");
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][KB * ROWB];
+    __shared__ float lds_s[2][KB];
+
+    const int b = blockIdx.y;
+    const int64_t tq0 = (int64_t)blockIdx.x * QPB;
+    const int l = lane_id(), wv_id = wave_id(), g = l >> 5, n = l & 31;
+    const int64_t t0 = tq0 + (int64_t)wv_id * G::NQW;
+    const int nq_avail = (int)max((int64_t)0, min((int64_t)G::NQW, (int64_t)a.n_q - t0));
+
+    bf16x8_t qf[MT][KS];
+    float wv[G::VPL];
+    if (nq_avail > 0) {
+        load_q<D, H, MT, false>(qf, a.q + ((int64_t)b * a.n_q + t0) * H * D, nq_avail);
+        load_w<H, MT, false>(wv, a.w + ((int64_t)b * a.n_q + t0) * H, nq_avail);
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) qf[mt][kk] = bf16x8_t{};
+#pragma unroll
+        for (int v = 0; v < G::VPL; ++v) wv[v] = 0.0f;
+    }
+    int64_t lo[G::NQL], hi[G::NQL];
+#pragma unroll
+    for (int u = 0; u < G::NQL; ++u) {
+        const int qs = G::SPLIT ? 0 : g * G::NQL + u;
+        if (qs < nq_avail) {
+            row_range(a, t0 + qs, lo[u], hi[u]);
+        } else {
+            lo[u] = 0;
+            hi[u] = 0;
+        }
+    }
+    // Hull of the block's ranges (ranges are monotone in t, but compute it plainly).
+    const int nq_blk = (int)min((int64_t)QPB, (int64_t)a.n_q - tq0);
+    int64_t lo_blk = INT64_MAX, hi_blk = 0;
+    for (int qs = 0; qs < nq_blk; ++qs) {
+        int64_t x, y;
+        row_range(a, tq0 + qs, x, y);
+        if (y > x) {
+            lo_blk = min(lo_blk, x);
+            hi_blk = max(hi_blk, y);
+        }
+    }
+    int64_t kt_begin = 0, kt_end = 0;
+    if (hi_blk > lo_blk) {
+        kt_begin = lo_blk / KB;
+        kt_end = (hi_blk + KB - 1) / KB;
+    }
+
+    const uint8_t *keys_b = reinterpret_cast<const uint8_t *>(a.keys) + (int64_t)b * a.n_keys * D * ESZ;
+    const float *scale_b = FP8 ? a.kscale + (int64_t)b * a.n_keys : nullptr;
+
+    uint4 stage[CPT];
+    float stage_s = 0.0f;
+    auto fetch = [&](int64_t kt) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = threadIdx.x + i * NT;
+            const int key = c / CPR, col = c % CPR;
+            const int64_t row = kt * KB + key;
+            stage[i] = (c < CHUNKS && row < a.n_keys)
+                           ? reinterpret_cast<const uint4 *>(keys_b + row * D * ESZ)[col]
+                           : make_uint4(0, 0, 0, 0);
+        }
+        if (FP8 && threadIdx.x < KB) {
+            const int64_t row = kt * KB + threadIdx.x;
+            stage_s = row < a.n_keys ? scale_b[row] : 0.0f;
+        }
+    };
+    auto commit = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = threadIdx.x + i * NT;
+            if (c >= CHUNKS) continue;
+            const int key = c / CPR, col = c % CPR;
+            uint8_t *dst = &lds_k[buf][key * ROWB];
+            if (FP8) {
+                const uint2 lo2 = e4m3x4_to_bf16x4(stage[i].x), hi2 = e4m3x4_to_bf16x4(stage[i].y);
+                const uint2 lo3 = e4m3x4_to_bf16x4(stage[i].z), hi3 = e4m3x4_to_bf16x4(stage[i].w);
+                reinterpret_cast<uint4 *>(dst + col * 32)[0] = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
+                reinterpret_cast<uint4 *>(dst + col * 32)[1] = make_uint4(lo3.x, lo3.y, hi3.x, hi3.y);
+            } else {
+                reinterpret_cast<uint4 *>(dst)[col] = stage[i];
+            }
+        }
+        if (FP8 && threadIdx.x < KB) lds_s[buf][threadIdx.x] = stage_s;
+    };
+
+    if (kt_begin < kt_end) {
+        fetch(kt_begin);
+        commit(0);
+    }
+    __syncthreads();
+    for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
+        const int buf = (int)((kt - kt_begin) & 1);
+        if (kt + 1 < kt_end) fetch(kt + 1);
+        if (nq_avail > 0) {
+#pragma unroll
+            for (int nt = 0; nt < KB / 32; ++nt) {
+                const int key = nt * 32 + n;
+                const uint8_t *src = &lds_k[buf][key * ROWB + D * g];
+                f32x16_t acc[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16_t{};
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) {
+                    const bf16x8_t bk = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(src + 16 * kk));
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_32x32x16(qf[mt][kk], bk, acc[mt]);
+                }
+                float part[G::NQL];
+                epilogue<H, MT, false>(acc, wv, part);
+                const int64_t s = kt * KB + key;
+                if (FP8) {
+                    const float sc = lds_s[buf][key];
+#pragma unroll
+                    for (int u = 0; u < G::NQL; ++u) part[u] *= sc;
+                }
+                if (!(G::SPLIT && g != 0)) {
+#pragma unroll
+                    for (int u = 0; u < G::NQL; ++u) {
+                        const int qs = G::SPLIT ? 0 : g * G::NQL + u;
+                        if (qs >= nq_avail || s >= a.n_out) continue;
+                        const bool ok = s >= lo[u] && s < hi[u];
+                        a.out[((int64_t)b * a.n_q + t0 + qs) * a.n_out + s] = ok ? part[u] : -INFINITY;
+                    }
+                }
+            }
+        }
+        if (kt + 1 < kt_end) commit(buf ^ 1);
+        __syncthreads();
+    }
+
+    // -inf outside the computed tiles, for every query row of the block.
+    int64_t c_lo = kt_begin * KB, c_hi = min(kt_end * KB, a.n_out);
+    if (kt_begin >= kt_end) c_lo = c_hi = 0;
+    for (int qs = 0; qs < nq_blk; ++qs) {
+        float *orow = a.out + ((int64_t)b * a.n_q + tq0 + qs) * a.n_out;
+        for (int64_t s = threadIdx.x; s < c_lo; s += NT) orow[s] = -INFINITY;
+        for (int64_t s = c_hi + threadIdx.x; s < a.n_out; s += NT) orow[s] = -INFINITY;
+    }
+}
+
+template <bool FP8, int D, int H>
+hipError_t launch_flat(const ScoreArgs &a, hipStream_t st)
+{
+    constexpr int MT = H == 64 ? 2 : 1;
+    using G = Geo<H, MT, false>;
+    if (a.n_q <= 2 * G::NQW) {
+        constexpr int WAVES = 4, BPW = 8;
+        const int64_t n_blocks = (a.n_out + 31) / 32;
+        dim3 grid((unsigned)((n_blocks + WAVES * BPW - 1) / (WAVES * BPW)),
+                  (unsigned)((a.n_q + G::NQW - 1) / G::NQW), (unsigned)a.batch);
+        hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, false, false, WAVES, BPW>), grid,
+                           dim3(WAVES * kWave), 0, st, a);
+    } else {
+        constexpr int WAVES = 8, KB = 64;
+        constexpr int QPB = WAVES * G::NQW;
+        dim3 grid((unsigned)((a.n_q + QPB - 1) / QPB), (unsigned)a.batch);
+        hipLaunchKernelGGL((score_tile_kernel<FP8, D, H, MT, WAVES, KB>), grid,
+                           dim3(WAVES * kWave), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+template <bool FP8, int D, int H>
+hipError_t launch_fine(const ScoreArgs &a, hipStream_t st)
+{
+    constexpr int MT = H > 32 ? 2 : 1;
+    constexpr int WAVES = 4, BPW = 4;
+    const int64_t n_blocks = (a.n_out + 31) / 32;
+    dim3 grid((unsigned)((n_blocks + WAVES * BPW - 1) / (WAVES * BPW)), (unsigned)a.n_q,
+              (unsigned)a.batch);
+    hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, true, true, WAVES, BPW>), grid,
+                       dim3(WAVES * kWave), 0, st, a);
+    return hipGetLastError();
+}
+
+template <bool FP8, int D>
+hipError_t dispatch_heads(const ScoreArgs &a, hipStream_t st, bool fine)
+{
+    switch (a.heads) {
+    case 4: return fine ? launch_fine<FP8, D, 4>(a, st) : launch_flat<FP8, D, 4>(a, st);
+    case 8: return fine ? launch_fine<FP8, D, 8>(a, st) : launch_flat<FP8, D, 8>(a, st);
+    case 16: return fine ? launch_fine<FP8, D, 16>(a, st) : launch_flat<FP8, D, 16>(a, st);
+    case 32: return fine ? launch_fine<FP8, D, 32>(a, st) : launch_flat<FP8, D, 32>(a, st);
+    case 64: return fine ? launch_fine<FP8, D, 64>(a, st) : launch_flat<FP8, D, 64>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t dispatch(const ScoreArgs &a, hipStream_t st, bool fine)
+{
+    if (a.dim == 128)
+        return a.fp8 ? dispatch_heads<true, 128>(a, st, fine) : dispatch_heads<false, 128>(a, st, fine);
+    if (a.dim == 64)
+        return a.fp8 ? dispatch_heads<true, 64>(a, st, fine) : dispatch_heads<false, 64>(a, st, fine);
+    return hipErrorInvalidValue;
+}
+
+} // namespace
+
+bool scores_supported(int heads, int dim)
+{
+    return (dim == 64 || dim == 128) &&
+           (heads == 4 || heads == 8 || heads == 16 || heads == 32 || heads == 64);
+}
+
+hipError_t launch_scores(const ScoreArgs &a, hipStream_t stream) { return dispatch(a, stream, false); }
+
+hipError_t launch_fine_scores(const ScoreArgs &a, hipStream_t stream) { return dispatch(a, stream, true); }
+
+} // namespace lsa
