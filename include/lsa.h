@@ -119,7 +119,8 @@ LSA_API lsa_status lsa_index_scores(const lsa_index_shape *shape, const void *q,
  *   for empty slots (the output of lsa_page_recall).  Only ids in the middle [S, V-W) compete;
  *   with fewer than k-S-W of them all are taken and the tail of idx is -1.
  *   idx        [B, n_q, k] int32, written completely
- *   ws         workspace of lsa_workspace_bytes(LSA_OP_TOPK_SELECT, ...) bytes (may be 0)
+ *   ws         workspace of lsa_workspace_bytes(LSA_OP_TOPK_SELECT, shape, budget, 0, 0, n_cand,
+ *              NULL) bytes (0 for many short rows; few long rows are split over workgroups)
  * Limits: k - S - W <= 65536.
  */
 LSA_API lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budget, const float *scores,
@@ -199,7 +200,8 @@ LSA_API lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_
 enum { LSA_OP_TOPK_SELECT = 1, LSA_OP_PAGE_RECALL = 2, LSA_OP_SPARSE_ATTN = 3 };
 
 /* Workspace bytes needed by `op` for these arguments (0 if none).  Arguments an op does not
- * use may be NULL / 0.  Returns (size_t)-1 for invalid arguments. */
+ * use may be NULL / 0 (LSA_OP_TOPK_SELECT reads n_cand; 0 means flat, n_cand = kv_len).
+ * Returns (size_t)-1 for invalid arguments. */
 LSA_API size_t lsa_workspace_bytes(int op, const lsa_index_shape *shape, lsa_budget budget,
                            int32_t page_size, int32_t m_pages, int64_t n_cand,
                            const lsa_attn_shape *attn);

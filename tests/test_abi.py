@@ -57,7 +57,10 @@ def test_workspace_sizes(L):
     b = lsa.Budget(2048, 128, 896)
     n = lsa.lsa_workspace_bytes(lsa.OP_PAGE_RECALL, sh, b, 64, 256)
     assert n == 4 * 1 * (1 << 14) * 4
-    assert lsa.lsa_workspace_bytes(lsa.OP_TOPK_SELECT, sh, b) == 0
+    # few long rows are split over workgroups (workspace); many rows use one workgroup each
+    assert lsa.lsa_workspace_bytes(lsa.OP_TOPK_SELECT, sh, b) > 0
+    assert lsa.lsa_workspace_bytes(lsa.OP_TOPK_SELECT, _shape(B=1, T=8192, Lk=131072), b) == 0
+    assert lsa.lsa_workspace_bytes(lsa.OP_TOPK_SELECT, _shape(B=4, Lk=4096), b) == 0
     att = lsa.AttnShape(16, 576, 512, 1, 576, 576, 576 ** -0.5)
     n_att = lsa.lsa_workspace_bytes(lsa.OP_SPARSE_ATTN, _shape(B=32), b, attn=att)
     assert n_att > 0 and n_att % 256 == 0
@@ -107,6 +110,8 @@ def test_topk_rejects(L):
     assert _topk_call(L, sh, lsa.Budget(64, 4, 4), sh.kv_len, scores=0) == 1
     assert _topk_call(L, sh, lsa.Budget(64, 4, 4), sh.kv_len, scores=FAKE + 4) == 2
     assert _topk_call(L, sh, lsa.Budget(1 << 20, 0, 0), sh.kv_len) == 4
+    big = _shape(B=4, Lk=1 << 20)  # chunked selection: the workspace is required
+    assert _topk_call(L, big, lsa.Budget(2048, 128, 896), big.kv_len) == 5
 
 
 def test_page_summary_rejects(L):

@@ -180,6 +180,38 @@ def test_select_decode_128k_full_exact():
         assert np.array_equal(idx[r], expect), r
 
 
+@pytest.mark.parametrize("ties", ["none", "zeros", "coarse", "const"])
+def test_select_chunked_rows_exact(ties):
+    """Few long rows (the chunked path), every tie pattern: heavy ties overflow the per-chunk
+    slices and fall back to one workgroup per row; rows with V <= k take everything."""
+    B, T, L = 2, 3, 40000
+    k, S, W = 2048, 64, 960
+    sc = inputs.synthetic_scores(B * T, L, seed=10, ties=ties, device=DEV).reshape(B, T, L)
+    for pos0 in (L - T, 2046, 0):
+        idx = lsa.topk_select(sc, k, S, W, kv_len=L, q_pos0=pos0).cpu().numpy()
+        V = ref.valid_lengths(L, pos0, T)
+        for b in range(B):
+            expect = ref.select(sc[b].cpu().numpy(), V, k, S, W)
+            assert np.array_equal(idx[b], expect), (ties, pos0, b)
+
+
+def test_select_chunked_candidate_mode_exact():
+    B, n = 4, 16384
+    k, S, W = 2048, 128, 896
+    sc = inputs.synthetic_scores(B, n, seed=11, ties="coarse", device=DEV).reshape(B, 1, n)
+    g = torch.Generator().manual_seed(1)
+    ids = torch.stack([torch.sort(torch.randperm(1 << 20, generator=g)[:n]).values for _ in range(B)])
+    ids = ids.to(torch.int32).reshape(B, 1, n)
+    ids[:, :, 3::5] = -1
+    ids[1, 0, 900:] = -1  # fewer candidates than the dynamic budget
+    idx = lsa.topk_select(sc, k, S, W, kv_len=1 << 20, q_pos0=(1 << 20) - 1,
+                          cand_ids=ids.to(DEV)).cpu().numpy()
+    for b in range(B):
+        expect = ref.select(sc[b].cpu().numpy(), np.array([1 << 20]), k, S, W,
+                            cand_ids=ids[b].numpy())
+        assert np.array_equal(idx[b], expect), b
+
+
 def test_select_prefill_rows_sampled():
     """Selection rows at the chunked-prefill shape (8192 rows x 131072); sampled rows checked."""
     w = PREFILL_8K_AT_128K

@@ -94,9 +94,13 @@ size_t lsa_workspace_bytes(int op, const lsa_index_shape *shape, lsa_budget budg
 {
     (void)n_cand;
     switch (op) {
-    case LSA_OP_TOPK_SELECT:
-        if (check_index_shape(shape) != LSA_OK || check_budget(budget) != LSA_OK) return (size_t)-1;
-        return 0;
+    case LSA_OP_TOPK_SELECT: {
+        if (!shape || shape->batch < 0 || shape->n_q < 0 || shape->kv_len < 1 ||
+            check_budget(budget) != LSA_OK || n_cand < 0)
+            return (size_t)-1;
+        const int64_t n = n_cand == 0 ? shape->kv_len : n_cand;
+        return lsa::select_workspace_bytes((int64_t)shape->batch * shape->n_q, n, lsa::SELECT_SI);
+    }
     case LSA_OP_PAGE_RECALL:
         if (check_index_shape(shape) != LSA_OK || !pow2(page_size) || page_size < 32 ||
             page_size > 256 || m_pages < 1)
@@ -144,8 +148,6 @@ lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budget, cons
                            int64_t n_cand, const int32_t *cand_ids, int32_t *idx, void *ws,
                            size_t ws_bytes, void *stream)
 {
-    (void)ws;
-    (void)ws_bytes;
     if (!shape) return LSA_ERR_NULL_POINTER;
     if (shape->batch < 0 || shape->n_q < 0 || shape->kv_len < 1 ||
         shape->kv_len >= (int64_t(1) << 31) || shape->q_pos0 < 0)
@@ -161,6 +163,8 @@ lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budget, cons
     const int64_t rows = (int64_t)shape->batch * shape->n_q;
     if (rows >= (int64_t(1) << 31)) return LSA_ERR_UNSUPPORTED;
     if (rows == 0) return LSA_OK;
+    const size_t need = lsa::select_workspace_bytes(rows, n_cand, lsa::SELECT_SI);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, 256))) return LSA_ERR_WORKSPACE_TOO_SMALL;
     lsa::SelectArgs a{};
     a.scores = scores;
     a.cand_ids = cand_ids;
@@ -175,7 +179,7 @@ lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budget, cons
     a.window = budget.window;
     a.mode = lsa::SELECT_SI;
     a.out_stride = budget.k;
-    return device_status(lsa::launch_select(a, static_cast<hipStream_t>(stream)));
+    return device_status(lsa::launch_select(a, ws, static_cast<hipStream_t>(stream)));
 }
 
 lsa_status lsa_page_summary(const lsa_index_shape *shape, int32_t page_size, const void *keys,
@@ -269,7 +273,7 @@ lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int3
     s.page = page_size;
     s.m_pages = m_pages;
     s.out_stride = m_pages;
-    if ((st = device_status(lsa::launch_select(s, sm))) != LSA_OK) return st;
+    if ((st = device_status(lsa::launch_select(s, nullptr, sm))) != LSA_OK) return st;
 
     // stage 2: fine scores of the tokens of the recalled pages
     lsa::ScoreArgs f{};

@@ -8,8 +8,9 @@
 //
 // Latent (MLA) kernel.  A workgroup of 4 waves owns one (sequence, query, group of 16 heads) and
 // a contiguous chunk of the index list.  Per round, 64 selected rows (d_qk bf16 each) are
-// gathered into LDS with 16-byte loads -- each row is one contiguous run in HBM, and the
-// sink / window runs are contiguous across rows -- then
+// gathered into LDS by gfx950's LDS-DMA loads (16 bytes per lane, no register staging) while
+// the previous round computes -- each row is one contiguous run in HBM, and the sink / window
+// runs are contiguous across rows -- then
 //   logits  S[16 x 64] = Q[16 x d_qk] . K^T   v_mfma_f32_16x16x32_bf16, one 16-row tile per wave
 //   softmax online, fp32, base-2 exponent, per head over the rounds
 //   output  O[16 x d_v] += P[16 x 64] . V     v_mfma_f32_16x16x32_bf16, d_v/4 columns per wave
@@ -34,19 +35,27 @@ constexpr int MLA_MAX_DV = 512;
 
 __device__ __forceinline__ bool row_ok(int32_t id, int64_t kv_len) { return id >= 0 && id < kv_len; }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glb_void_t;
+
 template <int DQK, int DV>
 __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
 {
-    constexpr int ROWB = DQK * 2 + 32;     // LDS bytes per gathered row (pad: see P.V below)
+    constexpr int ROWB = DQK * 2;          // LDS bytes per gathered row
+    constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
     constexpr int KS = DQK / 32;           // K-steps of the logit product
-    constexpr int CPR = DQK * 2 / 16;      // 16-byte chunks per row
     constexpr int NTW = DV / 4 / 16;       // 16-column output tiles per wave
-    static_assert(DQK % 32 == 0 && DV % 64 == 0, "shape");
+    constexpr int DMA_PER_WAVE = AR * CPR / 64 / 4;
+    static_assert(DQK % 32 == 0 && DV % 64 == 0 && CPR % 8 == 0, "shape");
+    static_assert((AR * CPR) % 256 == 0, "whole DMA instructions per wave");
 
-    __shared__ __attribute__((aligned(16))) uint8_t rows[AR * ROWB];
+    // Two row buffers: round i is computed from buf[i&1] while round i+1 streams into the other
+    // one.  Chunk c of row r is stored at chunk slot c ^ (r & 7) of the row (an XOR swizzle that
+    // keeps the 16-byte logit reads of 8 consecutive rows on distinct LDS banks).
+    __shared__ __attribute__((aligned(16))) uint8_t buf[2][AR * ROWB];
     __shared__ float S[16][AR + 1];
     __shared__ __attribute__((aligned(16))) uint16_t Pm[16][AR + 8];
-    __shared__ int32_t rid[AR];
+    __shared__ int32_t rid[2][AR];
     __shared__ float m_run[16], l_run[16], alpha[16];
 
     const int HG = a.heads / 16;
@@ -60,6 +69,7 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
     const int chunk = ((a.n_idx + a.n_split - 1) / a.n_split + AR - 1) / AR * AR;
     const int c_begin = split * chunk;
     const int c_end = min(a.n_idx, c_begin + chunk);
+    const int n_rounds = c_end > c_begin ? (c_end - c_begin + AR - 1) / AR : 0;
 
     // Q fragments: lane l holds head 16*hg + l%16, d = 32*kk + 8*(l/16) + [0,8)
     bf16x8_t qf[KS];
@@ -80,45 +90,65 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
     const uint8_t *kv_b = reinterpret_cast<const uint8_t *>(a.k) + (int64_t)b * a.kv_len * a.k_stride * 2;
     const float sl2 = a.scale * kLog2e;
 
-    for (int c0 = c_begin; c0 < c_end; c0 += AR) {
+    auto load_ids = [&](int round, int slot) {
         if (threadIdx.x < AR) {
-            const int j = c0 + threadIdx.x;
+            const int j = c_begin + round * AR + threadIdx.x;
             const int32_t id = j < c_end ? idx_row[j] : -1;
-            rid[threadIdx.x] = row_ok(id, a.kv_len) ? id : -1;
+            rid[slot][threadIdx.x] = row_ok(id, a.kv_len) ? id : -1;
         }
-        __syncthreads();
-        // gather the rows (invalid rows are zero-filled so no NaN can reach the MFMA)
-        for (int c = threadIdx.x; c < AR * CPR; c += 256) {
-            const int r = c / CPR, col = c % CPR;
-            const int32_t id = rid[r];
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (id >= 0) v = reinterpret_cast<const uint4 *>(kv_b + (int64_t)id * a.k_stride * 2)[col];
-            *reinterpret_cast<uint4 *>(&rows[r * ROWB + col * 16]) = v;
+    };
+    // Rows of a round into buf[slot], straight from HBM into LDS (no registers): each lane of
+    // DMA instruction j writes the 16 bytes at LDS offset 1024*j + 16*lane.  Skipped rows fetch
+    // row 0 instead (always valid); their logits are masked, so they never contribute.
+    auto issue_rows = [&](int slot) {
+#pragma unroll
+        for (int j = 0; j < DMA_PER_WAVE; ++j) {
+            const int f = (w * DMA_PER_WAVE + j) * kWave + l; // flat chunk slot
+            const int r = f / CPR, cs = f % CPR;
+            const int gc = cs ^ (r & 7);
+            const int32_t id = rid[slot][r];
+            const uint8_t *src = kv_b + (int64_t)(id < 0 ? 0 : id) * a.k_stride * 2 + gc * 16;
+            __builtin_amdgcn_global_load_lds((glb_void_t *)src,
+                                             (lds_void_t *)&buf[slot][(w * DMA_PER_WAVE + j) * 1024],
+                                             16, 0, 0);
         }
+    };
+
+    if (n_rounds > 0) {
+        load_ids(0, 0);
         __syncthreads();
+        issue_rows(0);
+        if (n_rounds > 1) load_ids(1, 1);
+    }
+    for (int i = 0; i < n_rounds; ++i) {
+        const int cur = i & 1;
+        __builtin_amdgcn_s_waitcnt(0); // this wave's row loads of round i have landed
+        __syncthreads();                // ... and every other wave's; rid of round i+1 visible
+        if (i + 1 < n_rounds) issue_rows(cur ^ 1);
         // logits: wave w takes rows 16w .. 16w+15
         {
             f32x4_t acc = f32x4_t{};
-            const uint8_t *kr = &rows[(16 * w + (l & 15)) * ROWB + 16 * (l >> 4)];
+            const int r = 16 * w + (l & 15);
+            const uint8_t *kr = &buf[cur][r * ROWB];
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
-                const bf16x8_t bk = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(kr + 64 * kk));
+                const int c = 4 * kk + (l >> 4);
+                const bf16x8_t bk = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(kr + 16 * (c ^ (r & 7))));
                 acc = mfma_16x16x32(qf[kk], bk, acc);
             }
-            const int r = 16 * w + (l & 15);
-            const bool ok = rid[r] >= 0;
+            const bool ok = rid[cur][r] >= 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[4 * (l >> 4) + i][r] = ok ? acc[i] * sl2 : -INFINITY;
+            for (int e = 0; e < 4; ++e) S[4 * (l >> 4) + e][r] = ok ? acc[e] * sl2 : -INFINITY;
         }
         __syncthreads();
         // online softmax: 16 threads per head, 4 rows each
         {
             const int h = threadIdx.x >> 4, part = threadIdx.x & 15;
-            float s[4], mx = -INFINITY;
+            float sv[4], mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s[i] = S[h][4 * part + i];
-                mx = fmaxf(mx, s[i]);
+            for (int e = 0; e < 4; ++e) {
+                sv[e] = S[h][4 * part + e];
+                mx = fmaxf(mx, sv[e]);
             }
 #pragma unroll
             for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
@@ -126,12 +156,12 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
             const float m_new = fmaxf(m_old, mx);
             float sum = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = (m_new == -INFINITY || s[i] == -INFINITY) ? 0.0f : exp2f(s[i] - m_new);
+            for (int e = 0; e < 4; ++e) {
+                const float p = (m_new == -INFINITY || sv[e] == -INFINITY) ? 0.0f : exp2f(sv[e] - m_new);
                 const uint32_t bits = f32_to_bf16_bits(p);
                 sum += bf16_bits_to_f32(bits); // normalise by what the product actually uses
-                // row r = 4*part + i sits at K position 32*(r/32) + 8*(r%4) + (r%32)/4
-                Pm[h][32 * (part >> 3) + 8 * i + (part & 7)] = (uint16_t)bits;
+                // row rr = 4*part + e sits at K position 32*(rr/32) + 8*(rr%4) + (rr%32)/4
+                Pm[h][32 * (part >> 3) + 8 * e + (part & 7)] = (uint16_t)bits;
             }
 #pragma unroll
             for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
@@ -145,18 +175,17 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
         }
         __syncthreads();
         // O = O * alpha + P . V ; wave w owns columns [w*DV/4, (w+1)*DV/4).  The K index of
-        // this product is permuted within each 32-row step: lane group g = l/16 element e
-        // is row g + 4e, so the four groups of one read touch four consecutive rows (disjoint
-        // LDS banks with the row padding) instead of rows 8 apart (same banks).  P was stored in
-        // the same permuted order.
+        // this product is permuted within each 32-row step: lane group g = l/16 element e is
+        // row g + 4e, so the four groups of one read touch four consecutive rows.  P was stored
+        // in the same permuted order.
         {
             float al[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) al[i] = alpha[4 * (l >> 4) + i];
+            for (int e = 0; e < 4; ++e) al[e] = alpha[4 * (l >> 4) + e];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) oacc[nt][i] *= al[i];
+                for (int e = 0; e < 4; ++e) oacc[nt][e] *= al[e];
 #pragma unroll
             for (int kk = 0; kk < AR / 32; ++kk) {
                 const bf16x8_t pf = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(&Pm[l & 15][32 * kk + 8 * (l >> 4)]));
@@ -164,32 +193,35 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
                     const int col = w * (DV / 4) + 16 * nt + (l & 15);
-                    const uint16_t *vp = reinterpret_cast<const uint16_t *>(&rows[r0 * ROWB]) + col;
-                    constexpr int RS = 4 * (ROWB / 2); // 4 rows, in uint16 elements
-                    uint32_t v01 = vp[0] | ((uint32_t)vp[RS] << 16);
-                    uint32_t v23 = vp[2 * RS] | ((uint32_t)vp[3 * RS] << 16);
-                    uint32_t v45 = vp[4 * RS] | ((uint32_t)vp[5 * RS] << 16);
-                    uint32_t v67 = vp[6 * RS] | ((uint32_t)vp[7 * RS] << 16);
-                    const bf16x8_t vf = bitcast<bf16x8_t>(make_uint4(v01, v23, v45, v67));
+                    uint32_t v16[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int r = r0 + 4 * e;
+                        const int slot = (col >> 3) ^ (r & 7);
+                        v16[e] = *reinterpret_cast<const uint16_t *>(&buf[cur][r * ROWB + slot * 16 + (col & 7) * 2]);
+                    }
+                    const bf16x8_t vf = bitcast<bf16x8_t>(make_uint4(v16[0] | (v16[1] << 16), v16[2] | (v16[3] << 16),
+                                                                     v16[4] | (v16[5] << 16), v16[6] | (v16[7] << 16)));
                     oacc[nt] = mfma_16x16x32(pf, vf, oacc[nt]);
                 }
             }
         }
+        if (i + 2 < n_rounds) load_ids(i + 2, cur); // rid[cur] is no longer read this round
         __syncthreads();
     }
 
-    // epilogue: lane holds O[head 4*(l/16)+i][col w*DV/4 + 16*nt + l%16]
+    // epilogue: lane holds O[head 4*(l/16)+e][col w*DV/4 + 16*nt + l%16]
     if (a.n_split == 1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 4 * (l >> 4) + i;
+        for (int e = 0; e < 4; ++e) {
+            const int h = 4 * (l >> 4) + e;
             const float lr = l_run[h];
             const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
             uint16_t *op = a.out + (qrow * a.heads + 16 * hg + h) * DV;
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
                 const int col = w * (DV / 4) + 16 * nt + (l & 15);
-                op[col] = (uint16_t)f32_to_bf16_bits(oacc[nt][i] * inv);
+                op[col] = (uint16_t)f32_to_bf16_bits(oacc[nt][e] * inv);
             }
         }
         if (a.lse && threadIdx.x < 16) {
@@ -201,11 +233,11 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
         // partial block: [DV] O values, then (m, l), per (query, head, split)
         const int64_t stride = DV + 2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = 4 * (l >> 4) + i;
+        for (int e = 0; e < 4; ++e) {
+            const int h = 4 * (l >> 4) + e;
             float *pp = a.ws + ((qrow * a.heads + 16 * hg + h) * a.n_split + split) * stride;
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) pp[w * (DV / 4) + 16 * nt + (l & 15)] = oacc[nt][i];
+            for (int nt = 0; nt < NTW; ++nt) pp[w * (DV / 4) + 16 * nt + (l & 15)] = oacc[nt][e];
         }
         if (threadIdx.x < 16) {
             float *pp = a.ws + ((qrow * a.heads + 16 * hg + threadIdx.x) * a.n_split + split) * stride;
@@ -216,28 +248,36 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
 }
 
 // Merge the splits of one (query, head): fixed order over splits.
+constexpr int MAX_SPLIT = 32;
+
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
 {
+    __shared__ float wsp[MAX_SPLIT];
+    __shared__ float inv_l;
     const int64_t qh = blockIdx.x; // (b * n_q + t) * heads + h
     const int64_t stride = a.d_v + 2;
     const float *base = a.ws + qh * a.n_split * stride;
-    float M = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, base[s * stride + a.d_v]);
-    float L = 0.0f;
-    for (int s = 0; s < a.n_split; ++s) {
-        const float m = base[s * stride + a.d_v];
-        if (m != -INFINITY) L += base[s * stride + a.d_v + 1] * exp2f(m - M);
+    if (threadIdx.x < kWave) {
+        const int s = threadIdx.x;
+        const float m = s < a.n_split ? base[s * stride + a.d_v] : -INFINITY;
+        const float lsum = s < a.n_split ? base[s * stride + a.d_v + 1] : 0.0f;
+        const float M = wave_max(m);
+        const float e = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+        const float L = wave_sum(e * lsum);
+        if (s < MAX_SPLIT) wsp[s] = e;
+        if (s == 0) {
+            inv_l = L > 0.0f ? 1.0f / L : 0.0f;
+            if (a.lse) a.lse[qh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+        }
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    __syncthreads();
+    const float il = inv_l;
     for (int c = threadIdx.x; c < a.d_v; c += blockDim.x) {
         float o = 0.0f;
-        for (int s = 0; s < a.n_split; ++s) {
-            const float m = base[s * stride + a.d_v];
-            if (m != -INFINITY) o += base[s * stride + c] * exp2f(m - M);
-        }
-        a.out[qh * a.d_v + c] = (uint16_t)f32_to_bf16_bits(o * inv);
+#pragma unroll 8
+        for (int s = 0; s < a.n_split; ++s) o = fmaf(base[s * stride + c], wsp[s], o);
+        a.out[qh * a.d_v + c] = (uint16_t)f32_to_bf16_bits(o * il);
     }
-    if (a.lse && threadIdx.x == 0) a.lse[qh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // Per-head kernel: one wave per (query, head).
@@ -345,9 +385,9 @@ int attn_splits(int batch, int n_q, int heads, int n_idx, int latent)
     if (!latent) return 1;
     const int64_t units = (int64_t)batch * n_q * (heads / 16);
     const int max_split = (n_idx + AR - 1) / AR;
-    int64_t want = (512 + units - 1) / units;
+    int64_t want = (256 + units - 1) / units;
     if (want > max_split) want = max_split;
-    if (want > 32) want = 32;
+    if (want > MAX_SPLIT) want = MAX_SPLIT;
     return want < 1 ? 1 : (int)want;
 }
 

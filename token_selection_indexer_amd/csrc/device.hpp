@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lsa {
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
@@ -15,11 +17,31 @@ typedef float f32x4_t __attribute__((__vector_size__(16)));
 
 constexpr int kWave = 64;
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).  Indices into register
+// arrays stay constant expressions, so the arrays never leave registers.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 template <typename To, typename From>
 __device__ __forceinline__ To bitcast(const From &f)
 {
     static_assert(sizeof(To) == sizeof(From), "size");
     return __builtin_bit_cast(To, f);
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load as one native vector value (a struct copy of uint4 becomes a memcpy that keeps
+// register arrays of it in scratch memory).
+__device__ __forceinline__ uint4 ld16(const void *p)
+{
+    return bitcast<uint4>(*reinterpret_cast<const u32x4_t *>(p));
 }
 
 // D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).  Lane l supplies A row l%32 and B column
@@ -39,6 +61,11 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// ReLU as one integer max on the bit pattern: every float with the sign bit set (including -0)
+// is a negative int32, every other one a non-negative int32 in the same order.  Exact, and one
+// instruction (fmaxf would also quiet NaNs first).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // binary32 -> bfloat16 bits, round to nearest even (finite inputs; NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)

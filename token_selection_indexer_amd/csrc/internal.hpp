@@ -57,7 +57,9 @@ enum SelectMode : int {
     SELECT_PAGES = 1, // top-m_pages of the eligible pages of a coarse-score row, ids ascending
 };
 
-hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
+// Workspace of the selection (0 when one workgroup per row is used).
+size_t select_workspace_bytes(int64_t rows, int64_t n_in, int mode);
+hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream);
 
 hipError_t launch_page_summary(const void *keys, int fp8, const float *kscale, int batch,
                                int64_t kv_len, int dim, int page, int64_t page_lo,

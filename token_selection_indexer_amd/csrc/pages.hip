@@ -33,10 +33,13 @@ __global__ __launch_bounds__(256) void page_summary_kernel(const void *keys, con
     const int64_t s0 = p * P;
     const int64_t n_p = min((int64_t)P, kv_len - s0);
 
+    // binary counter over the tokens: before token j the stack holds popcount(j) completed
+    // subtrees; token j closes ctz(~j) of them (left + right), all positions known at compile time
     float stk0[10], stk1[10];
-    int sp = 0;
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
+    static_for<0, P>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        constexpr int depth = __builtin_popcount(j);
+        constexpr int merges = __builtin_ctz(~j);
         const int64_t s = s0 + j;
         float x0 = 0.0f, x1 = 0.0f;
         if (j < n_p) {
@@ -54,17 +57,14 @@ __global__ __launch_bounds__(256) void page_summary_kernel(const void *keys, con
                 x1 = __uint_as_float(c & 0xffff0000u);
             }
         }
-        // binary counter: merge completed subtrees (left + right)
-#pragma unroll
-        for (int m = j; m & 1; m >>= 1) {
-            --sp;
-            x0 = __fadd_rn(stk0[sp], x0);
-            x1 = __fadd_rn(stk1[sp], x1);
-        }
-        stk0[sp] = x0;
-        stk1[sp] = x1;
-        ++sp;
-    }
+        static_for<0, merges>([&](auto M) {
+            constexpr int m = decltype(M)::value;
+            x0 = __fadd_rn(stk0[depth - 1 - m], x0);
+            x1 = __fadd_rn(stk1[depth - 1 - m], x1);
+        });
+        stk0[depth - merges] = x0;
+        stk1[depth - merges] = x1;
+    });
     const float nf = (float)n_p;
     const float m0 = __fdiv_rn(stk0[0], nf), m1 = __fdiv_rn(stk1[0], nf);
     const uint32_t out = f32_to_bf16_bits(m0) | (f32_to_bf16_bits(m1) << 16);

@@ -120,22 +120,30 @@ __device__ __forceinline__ void load_w(float (&wv)[16 * MT], const float *wbase,
 
 // ReLU, head weights and head sum over the lane's accumulators.  part[u] is the partial score of
 // lane-half query slot u (all slots complete unless SPLIT, where a cross-half add follows).
-template <int H, int MT, bool ONEQ>
-__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[MT], const float (&wv)[16 * MT],
+// wf(v) is the head weight of accumulator value v of this lane (registers or LDS).
+template <int H, int MT, bool ONEQ, typename WF>
+__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[MT], WF wf,
                                          float (&part)[Geo<H, MT, ONEQ>::NQL])
 {
     using G = Geo<H, MT, ONEQ>;
+    // four independent accumulation chains per query slot, combined in a fixed order
+    constexpr int NC = H >= 4 ? 4 : H;
+    float p[G::NQL][NC];
 #pragma unroll
-    for (int u = 0; u < G::NQL; ++u) part[u] = 0.0f;
+    for (int u = 0; u < G::NQL; ++u)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) p[u][c] = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int v = 16 * mt + r;
             const int u = G::SPLIT ? 0 : v / H;
-            part[u] = fmaf(wv[v], fmaxf(acc[mt][r], 0.0f), part[u]);
+            p[u][r % NC] = fmaf(wf(v), relu(acc[mt][r]), p[u][r % NC]);
         }
     }
+#pragma unroll
+    for (int u = 0; u < G::NQL; ++u) part[u] = (p[u][0] + p[u][1]) + (p[u][2] + p[u][3]);
     if (G::SPLIT) part[0] += __shfl_xor(part[0], 32, kWave);
 }
 
@@ -143,53 +151,81 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[MT], const float 
 // stream kernel
 // ------------------------------------------------------------------------------------------
 
-// One key row's operand: lane's D/2 elements as D/16 bf16x8 fragments.
+// A block of 32 consecutive key rows, loaded with fully contiguous 16-byte pieces (lane l of
+// piece i reads bytes 1024*i + 16*l of the block: every load instruction covers 1 KB of HBM
+// without gaps), then passed through the wave's LDS slab to reach the MFMA operand layout.
+// In the slab, 16-byte chunk c of row n sits at chunk slot c ^ (n & SW): the writes of 8
+// consecutive lanes cover one row and the operand reads of 8 consecutive lanes hit 8 rows, and
+// both land on distinct banks.
 template <bool FP8, int D>
-struct KeyFrag {
-    static constexpr int NLOAD = FP8 ? D / 32 : D / 16; // uint4 loads per lane
-    uint4 raw[NLOAD];
+struct KeyBlock {
+    static constexpr int ESZ = FP8 ? 1 : 2;
+    static constexpr int RB = D * ESZ;                  // bytes per key row
+    static constexpr int BB = 32 * RB;                  // bytes per block
+    static constexpr int NP = BB / 1024;                // 16-byte pieces per lane
+    static constexpr int CPR = RB / 16;                 // chunks per row
+    static constexpr int SW = (CPR < 8 ? CPR : 8) - 1;  // swizzle mask
+    static_assert(BB % 1024 == 0, "whole pieces");
+    uint4 raw[NP];
 
-    __device__ __forceinline__ void load(const void *keys, int64_t row, int gk)
-    {
-        const uint8_t *p = reinterpret_cast<const uint8_t *>(keys) +
-                           (row * D + (D / 2) * gk) * (FP8 ? 1 : 2);
-#pragma unroll
-        for (int i = 0; i < NLOAD; ++i) raw[i] = reinterpret_cast<const uint4 *>(p)[i];
-    }
-    __device__ __forceinline__ void zero()
+    __device__ __forceinline__ void load(const uint8_t *keys_b, int64_t row0, int64_t n_keys, int l)
     {
 #pragma unroll
-        for (int i = 0; i < NLOAD; ++i) raw[i] = make_uint4(0, 0, 0, 0);
-    }
-    __device__ __forceinline__ bf16x8_t frag(int kk) const
-    {
-        if (FP8) {
-            const uint4 c = raw[kk >> 1];
-            return (kk & 1) ? e4m3x8_to_bf16x8(make_uint2(c.z, c.w))
-                            : e4m3x8_to_bf16x8(make_uint2(c.x, c.y));
+        for (int i = 0; i < NP; ++i) {
+            const int f = i * kWave + l;
+            int64_t row = row0 + f / CPR;
+            if (row >= n_keys) row = n_keys - 1; // tail block: any valid row, masked later
+            raw[i] = ld16(keys_b + row * RB + (f % CPR) * 16);
         }
-        return bitcast<bf16x8_t>(raw[kk]);
+    }
+    __device__ __forceinline__ void to_slab(uint8_t *slab, int l) const
+    {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int f = i * kWave + l;
+            const int n = f / CPR, c = f % CPR;
+            *reinterpret_cast<uint4 *>(slab + n * RB + ((c ^ (n & SW)) * 16)) = raw[i];
+        }
+    }
+    // Operand chunk j (16 bytes) of lane (n = l%32, half g): key bytes [RB/2*g + 16j, +16).
+    __device__ static __forceinline__ uint4 chunk(const uint8_t *slab, int l, int j)
+    {
+        const int n = l & 31, c = (CPR / 2) * (l >> 5) + j;
+        return *reinterpret_cast<const uint4 *>(slab + n * RB + ((c ^ (n & SW)) * 16));
     }
 };
 
-template <bool FP8, int D, int H, int MT, bool ONEQ, bool FINE, int WAVES, int BPW>
+// PD: blocks prefetched ahead of the one being computed; UNR: blocks per unrolled loop body
+// (a multiple of PD + 1, so every ring slot index is a compile-time constant).
+template <bool FP8, int D, int H, int MT, bool ONEQ, bool FINE, int WAVES, int BPW, int PD = 3,
+          int UNR = BPW>
 __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
 {
     using G = Geo<H, MT, ONEQ>;
     constexpr int KS = D / 16;
+    using KB = KeyBlock<FP8, D>;
+    __shared__ __attribute__((aligned(16))) float w_lds[G::ROWS];
+    __shared__ __attribute__((aligned(16))) uint8_t slabs[WAVES][KB::BB];
     const int b = blockIdx.z;
     const int64_t t0 = (int64_t)blockIdx.y * G::NQW;
     const int nq_avail = (int)min((int64_t)G::NQW, (int64_t)a.n_q - t0);
     const int l = lane_id(), wv_id = wave_id(), g = l >> 5, n = l & 31;
 
+    // Every wave of the block serves the same queries: their head weights go to LDS once,
+    // indexed by indexer row r' (the epilogue reads 4 at a time).
+    if (threadIdx.x < G::ROWS) {
+        int qs, h;
+        bool valid;
+        rprime_to_qh<H, ONEQ>(threadIdx.x, qs, h, valid);
+        w_lds[threadIdx.x] = (valid && qs < nq_avail) ? a.w[((int64_t)b * a.n_q + t0 + qs) * H + h] : 0.0f;
+    }
     bf16x8_t qf[MT][KS];
     load_q<D, H, MT, ONEQ>(qf, a.q + ((int64_t)b * a.n_q + t0) * H * D, nq_avail);
-    float wv[G::VPL];
-    load_w<H, MT, ONEQ>(wv, a.w + ((int64_t)b * a.n_q + t0) * H, nq_avail);
 
     // Valid ranges of the lane's query slots, and the wave-wide hull.
     int64_t lo[G::NQL], hi[G::NQL];
-    int64_t lo_all = INT64_MAX, hi_all = 0;
+    int64_t lo_all = INT64_MAX, hi_all = 0;   // hull of the wave's ranges
+    int64_t lo_in = 0, hi_in = INT64_MAX;     // their intersection
 #pragma unroll
     for (int u = 0; u < G::NQL; ++u) {
         const int qs = G::SPLIT ? 0 : g * G::NQL + u;
@@ -203,20 +239,25 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
     if (FINE) {
         int64_t V = a.q_pos0 + t0 + 1;
         if (V > a.kv_len) V = a.kv_len;
-        lo_all = a.sink;
-        hi_all = V > a.k ? V - a.window : 0;
+        lo_all = lo_in = a.sink;
+        hi_all = hi_in = V > a.k ? V - a.window : 0;
         lo[0] = lo_all;
         hi[0] = hi_all;
     } else {
         for (int qs = 0; qs < nq_avail; ++qs) {
             int64_t x, y;
             row_range(a, t0 + qs, x, y);
+            lo_in = max(lo_in, x);
+            hi_in = min(hi_in, y);
             if (y > x) {
                 lo_all = min(lo_all, x);
                 hi_all = max(hi_all, y);
             }
         }
     }
+    hi_in = min(hi_in, a.n_keys);
+    __syncthreads();
+    const float *wl = &w_lds[G::VPL * g];
 
     const uint8_t *keys_b = reinterpret_cast<const uint8_t *>(a.keys) +
                             (int64_t)b * a.n_keys * D * (FP8 ? 1 : 2);
@@ -224,58 +265,124 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
     const int32_t *pages_row = FINE ? a.pages + ((int64_t)b * a.n_q + t0) * a.m_pages : nullptr;
     const int64_t n_blocks = (a.n_out + 31) / 32;
 
-    for (int it = 0; it < BPW; ++it) {
+    // Block `it` of this wave: output slots s0 .. s0+31, the lane's key row, whether it exists
+    // and whether it needs any compute.
+    struct Blk {
+        int64_t s0, row0, row, lrow; // row0: key row of slot s0; row: this lane's key row
+        bool valid, live;
+    };
+    auto locate = [&](int it) {
+        Blk k;
         const int64_t blk = ((int64_t)blockIdx.x * BPW + it) * WAVES + wv_id;
-        if (blk >= n_blocks) break;
-        const int64_t s0 = blk * 32; // output slot of lane n is s0 + n
-
-        // Key row of this lane's slot and whether the block needs any compute.
-        int64_t row;
-        bool block_live;
+        k.valid = blk < n_blocks;
+        k.s0 = blk * 32;
+        k.live = false;
+        k.row = k.row0 = 0;
+        if (!k.valid) return k;
         if (FINE) {
-            const int64_t pi = s0 / a.page;
+            const int64_t pi = k.s0 / a.page;
             const int pid = pages_row[pi];
-            const int64_t tok0 = (int64_t)pid * a.page + (s0 - pi * a.page);
-            row = tok0 + n;
-            block_live = pid >= 0 && tok0 < hi_all && tok0 + 32 > lo_all;
+            k.row0 = (int64_t)pid * a.page + (k.s0 - pi * a.page);
+            k.live = pid >= 0 && k.row0 < hi_all && k.row0 + 32 > lo_all;
         } else {
-            row = s0 + n;
-            block_live = s0 < hi_all && s0 + 32 > lo_all;
+            k.row0 = k.s0;
+            k.live = k.s0 < hi_all && k.s0 + 32 > lo_all;
         }
+        k.row = k.row0 + n;
+        k.lrow = k.row < a.n_keys ? k.row : a.n_keys - 1;
+        return k;
+    };
+
+    // PD + 1 blocks in flight per wave: blocks it+1 .. it+PD are loading while block it is
+    // computed (a register ring whose slot indices are all static).
+    static_assert(PD >= 1 && PD < BPW && UNR % (PD + 1) == 0 && BPW % UNR == 0, "ring shape");
+    Blk bq[PD + 1];
+    KB kq[PD + 1];
+    float sq[PD + 1];
+    uint8_t *slab = slabs[wv_id];
+    static_for<0, PD>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        bq[i] = locate(i);
+        sq[i] = 1.0f;
+        if (bq[i].live) {
+            kq[i].load(keys_b, bq[i].row0, a.n_keys, l);
+            if (FP8) sq[i] = scale_b[bq[i].lrow];
+        }
+    });
+    for (int grp = 0; grp < BPW / UNR; ++grp)
+    static_for<0, UNR>([&](auto IS) {
+        constexpr int cs = decltype(IS)::value % (PD + 1); // slot of block it
+        constexpr int ns = (cs + PD) % (PD + 1);           // slot that receives block it + PD
+        const int it = grp * UNR + decltype(IS)::value;
+        if (it + PD < BPW) {
+            bq[ns] = locate(it + PD);
+            sq[ns] = 1.0f;
+            if (bq[ns].live) {
+                kq[ns].load(keys_b, bq[ns].row0, a.n_keys, l);
+                if (FP8) sq[ns] = scale_b[bq[ns].lrow];
+            }
+        }
+        const Blk cb = bq[cs];
+        if (!cb.valid) return; // later blocks are past the end too
 
         float part[G::NQL];
-        if (block_live) {
-            KeyFrag<FP8, D> kf;
-            const int64_t lrow = row < a.n_keys ? row : a.n_keys - 1;
-            kf.load(keys_b, lrow, g);
+        if (cb.live) {
             f32x16_t acc[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16_t{};
+            // through the slab into operand layout (in-order LDS access within the wave)
+            kq[cs].to_slab(slab, l);
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const bf16x8_t bk = kf.frag(kk);
+            for (int j = 0; j < KB::CPR / 2; ++j) {
+                const uint4 c = KB::chunk(slab, l, j);
+                if (FP8) { // one chunk = two K-steps
+                    const bf16x8_t b0 = e4m3x8_to_bf16x8(make_uint2(c.x, c.y));
+                    const bf16x8_t b1 = e4m3x8_to_bf16x8(make_uint2(c.z, c.w));
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_32x32x16(qf[mt][kk], bk, acc[mt]);
+                    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_32x32x16(qf[mt][2 * j], b0, acc[mt]);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_32x32x16(qf[mt][2 * j + 1], b1, acc[mt]);
+                } else {
+                    const bf16x8_t b0 = bitcast<bf16x8_t>(c);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_32x32x16(qf[mt][j], b0, acc[mt]);
+                }
             }
-            epilogue<H, MT, ONEQ>(acc, wv, part);
+            __builtin_amdgcn_wave_barrier();
+            epilogue<H, MT, ONEQ>(acc, [&](int v) { return wl[v]; }, part);
             if (FP8) {
-                const float sc = scale_b[lrow];
 #pragma unroll
-                for (int u = 0; u < G::NQL; ++u) part[u] *= sc;
+                for (int u = 0; u < G::NQL; ++u) part[u] *= sq[cs];
             }
         }
 
-        if (G::SPLIT && g != 0) continue;
+        if (!(G::SPLIT && g != 0)) {
+            // a block inside every query's range and inside the output needs no lane masks
+            const bool full = cb.live && cb.row0 >= lo_in && cb.row0 + 32 <= hi_in &&
+                              cb.s0 + 32 <= a.n_out && nq_avail == G::NQW;
+            if (full) {
 #pragma unroll
-        for (int u = 0; u < G::NQL; ++u) {
-            const int qs = G::SPLIT ? 0 : g * G::NQL + u;
-            if (qs >= nq_avail || s0 + n >= a.n_out) continue;
-            const bool ok = block_live && row >= lo[u] && row < hi[u] && row < a.n_keys;
-            const int64_t o = ((int64_t)b * a.n_q + t0 + qs) * a.n_out + s0 + n;
-            a.out[o] = ok ? part[u] : -INFINITY;
-            if (FINE) a.out_ids[o] = ok ? (int32_t)row : -1;
+                for (int u = 0; u < G::NQL; ++u) {
+                    const int qs = G::SPLIT ? 0 : g * G::NQL + u;
+                    const int64_t o = ((int64_t)b * a.n_q + t0 + qs) * a.n_out + cb.s0 + n;
+                    a.out[o] = part[u];
+                    if (FINE) a.out_ids[o] = (int32_t)cb.row;
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < G::NQL; ++u) {
+                    const int qs = G::SPLIT ? 0 : g * G::NQL + u;
+                    if (qs >= nq_avail || cb.s0 + n >= a.n_out) continue;
+                    const int64_t row = cb.row;
+                    const bool ok = cb.live && row >= lo[u] && row < hi[u] && row < a.n_keys;
+                    const int64_t o = ((int64_t)b * a.n_q + t0 + qs) * a.n_out + cb.s0 + n;
+                    a.out[o] = ok ? part[u] : -INFINITY;
+                    if (FINE) a.out_ids[o] = ok ? (int32_t)row : -1;
+                }
+            }
         }
-    }
+    });
 }
 
 // ------------------------------------------------------------------------------------------
@@ -408,7 +515,7 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
                     for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_32x32x16(qf[mt][kk], bk, acc[mt]);
                 }
                 float part[G::NQL];
-                epilogue<H, MT, false>(acc, wv, part);
+                epilogue<H, MT, false>(acc, [&](int v) { return wv[v]; }, part);
                 const int64_t s = kt * KB + key;
                 if (FP8) {
                     const float sc = lds_s[buf][key];
@@ -446,7 +553,7 @@ hipError_t launch_flat(const ScoreArgs &a, hipStream_t st)
     constexpr int MT = H == 64 ? 2 : 1;
     using G = Geo<H, MT, false>;
     if (a.n_q <= 2 * G::NQW) {
-        constexpr int WAVES = 4, BPW = 8;
+        constexpr int WAVES = 4, BPW = 16;
         const int64_t n_blocks = (a.n_out + 31) / 32;
         dim3 grid((unsigned)((n_blocks + WAVES * BPW - 1) / (WAVES * BPW)),
                   (unsigned)((a.n_q + G::NQW - 1) / G::NQW), (unsigned)a.batch);

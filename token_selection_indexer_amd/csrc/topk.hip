@@ -5,37 +5,43 @@
 // rest to dynamic sparse selection; Baidu Cloud article, "2. Dynamic Token Selector": top-k of
 // the score row.  Model card, HI bullet: candidate blocks are recalled by coarse scores.)
 //
-// One workgroup of 1024 threads owns one query row.  The selection is an exact radix select on
-// an order-preserving uint32 image of the fp32 scores (larger key = larger score, -0 == +0), with
-// ties going to the lower position -- which is the lower token index, because rows are in token
-// order and candidate lists are ascending:
-//   1. histogram of key bits 31..21 (2048 bins in LDS) over the row;
-//   2. the bin holding the k-th key; everything above it is selected;
-//   3. if the elements of that bin and above fit in LDS, one ordered pass compacts them there and
-//      the remaining digits (bits 20..10, 9..0) are resolved in LDS; otherwise the next digit is
-//      histogrammed from the row again (heavy ties), until the threshold key T is exact;
-//   4. one ordered pass emits keys > T plus the first (k - #greater) keys == T in position order,
-//      so the picks come out ascending without a sort.
-// Sink [0,S) and window [V-W,V) are written arithmetically, never scored or compared.
+// Exact radix select on an order-preserving uint32 image of the fp32 scores (larger key = larger
+// score, -0 == +0).  Ties go to the lower position, which is the lower token index because rows
+// are in token order and candidate lists are ascending.  Picks are emitted by ordered compaction,
+// so they come out ascending without a sort.  Sink [0,S) and window [V-W,V) are written
+// arithmetically, never scored or compared.
+//
+// Two paths:
+//  * one workgroup per row (many rows: prefill, page recall):
+//      1. histogram of key bits 31..21 (2048 bins in LDS) over the row;
+//      2. the bin b* holding the k-th key; bins above are taken outright;
+//      3. if bins >= b* fit in LDS, one ordered pass compacts them there and bits 20..10, 9..0
+//         are resolved in LDS; otherwise the next digit is histogrammed from the row again;
+//      4. keys > T, then the first (k - #greater) keys == T, in position order.
+//  * chunked (few long rows: decode): the row is cut into 4096-element chunks, one workgroup
+//    each, so a handful of rows still fills the chip:
+//      zero      clear the per-row histograms
+//      hist      per-chunk LDS histogram, nonzero bins added to the row's global histogram
+//      collect   every chunk finds b* from the row histogram and compacts its elements with
+//                bin >= b* (in order) into its own slice of the workspace
+//      finish    one workgroup per row concatenates the slices (chunk order = position order)
+//                into LDS and finishes as in step 3-4; a row whose slices overflowed falls back
+//                to the one-workgroup path over the row.
 #include "device.hpp"
 #include "internal.hpp"
 
 namespace lsa {
 namespace {
 
-constexpr int NT = 1024;
-constexpr int NW = NT / kWave;
-constexpr int ITEMS = 4;            // contiguous elements per thread per round
-constexpr int ROUND = NT * ITEMS;
-constexpr int CAP = 8192;           // LDS candidate buffer (key, id) entries
+constexpr int NBIN = 2048;          // 11-bit digits
+constexpr int CAP = 8192;           // LDS candidate buffer entries (key, id)
+constexpr int CHUNK = 4096;         // chunked path: elements per workgroup
+constexpr int CHUNK_CAP = 512;      // chunked path: candidates kept per chunk
+constexpr int CNT_THREADS = 256;    // chunked path: threads per chunk workgroup
 
-struct Smem {
-    int hist[2048];
-    int scan[NW + 1];
-    int misc[8];
-    uint32_t buf_key[CAP];
-    int32_t buf_id[CAP];
-};
+// ------------------------------------------------------------------------------------------
+// Row access
+// ------------------------------------------------------------------------------------------
 
 // A row's competing elements: positions [lo, hi) of `sc` (and `ids` in candidate mode); an
 // element competes iff its id lies in [id_lo, id_hi).  Position order is id order.
@@ -44,61 +50,131 @@ struct Row {
     const int32_t *ids; // nullptr: id = position
     int64_t lo, hi;
     int64_t id_lo, id_hi;
-    bool vec;           // 16-byte aligned rows: vector loads
 };
 
-__device__ __forceinline__ void load_items(const Row &r, int64_t base, uint32_t (&key)[ITEMS],
-                                           int32_t (&id)[ITEMS])
+// Element at position p: (key, id); key 0 = does not compete.
+__device__ __forceinline__ uint32_t elem(const Row &r, int64_t p, int32_t &id)
 {
-    const int64_t p0 = base + (int64_t)threadIdx.x * ITEMS;
-    float s[ITEMS];
-    int32_t c[ITEMS];
-    if (r.vec && p0 + ITEMS <= r.hi && p0 >= r.lo) {
-        const float4 v = *reinterpret_cast<const float4 *>(r.sc + p0);
-        s[0] = v.x; s[1] = v.y; s[2] = v.z; s[3] = v.w;
-        if (r.ids) {
-            const int4 iv = *reinterpret_cast<const int4 *>(r.ids + p0);
-            c[0] = iv.x; c[1] = iv.y; c[2] = iv.z; c[3] = iv.w;
-        } else {
-#pragma unroll
-            for (int j = 0; j < ITEMS; ++j) c[j] = (int32_t)(p0 + j);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const int64_t p = p0 + j;
-            const bool in = p >= r.lo && p < r.hi;
-            s[j] = in ? r.sc[p] : 0.0f;
-            c[j] = in ? (r.ids ? r.ids[p] : (int32_t)p) : -1;
-        }
+    if (p < r.lo || p >= r.hi) {
+        id = -1;
+        return 0u;
     }
-#pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        const int64_t p = p0 + j;
-        const bool ok = p >= r.lo && p < r.hi && c[j] >= r.id_lo && c[j] < r.id_hi;
-        key[j] = ok ? order_key(s[j]) : 0u;
-        id[j] = c[j];
-    }
+    const int32_t c = r.ids ? r.ids[p] : (int32_t)p;
+    id = c;
+    if (c < r.id_lo || c >= r.id_hi) return 0u;
+    return order_key(r.sc[p]);
 }
 
-__device__ __forceinline__ int64_t round_begin(const Row &r) { return (r.lo / ITEMS) * ITEMS; }
+// Exclusive position of flagged items in (item, wave, lane) order -- which is position order
+// when item j of thread t sits at base + j*NT + t.  cnt holds ITEMS*NT/64 ints of LDS.
+// Barriers inside: every thread of the block must call it.
+template <int NT, int ITEMS>
+__device__ __forceinline__ void ordered_slots(const bool (&flag)[ITEMS], int (&slot)[ITEMS],
+                                              int *cnt, int &total)
+{
+    constexpr int NW = NT / kWave;
+    static_assert(ITEMS * NW <= kWave, "one wave scans the per-(item, wave) counts");
+    const int lane = lane_id(), w = wave_id();
+    uint64_t m[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        m[j] = __ballot(flag[j]);
+        if (lane == 0) cnt[j * NW + w] = __popcll(m[j]);
+    }
+    __syncthreads();
+    const int c = lane < ITEMS * NW ? cnt[lane] : 0;
+    const int inc = wave_inclusive_scan(c);
+    total = __shfl(inc, ITEMS * NW - 1, kWave);
+    const int ex = inc - c;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const int base = __shfl(ex, j * NW + w, kWave);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m[j] >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m[j], 0u));
+        slot[j] = flag[j] ? base + below : -1;
+    }
+    __syncthreads();
+}
+
+// From the top bin down: the bin where the running count first reaches `need`.
+struct Digit {
+    int d, above, at, total;
+};
+
+template <int NT>
+__device__ Digit find_digit(const int *hist, int nbins, int need, int *scratch)
+{
+    // thread i owns bins [nbins - (i+1)*per, nbins - i*per), scanned top-down
+    const int per = nbins / NT;
+    const int top = nbins - 1 - per * (int)threadIdx.x;
+    int mine = 0;
+    for (int j = 0; j < per; ++j) mine += hist[top - j];
+    int tot;
+    const int ex = block_exclusive_scan<NT / kWave>(mine, scratch, &tot);
+    if (threadIdx.x == 0) scratch[NT / kWave + 1] = -1;
+    __syncthreads();
+    if (ex < need && ex + mine >= need) {
+        int cum = ex;
+        for (int j = 0; j < per; ++j) {
+            const int c = hist[top - j];
+            if (cum + c >= need) {
+                scratch[NT / kWave + 1] = top - j;
+                scratch[NT / kWave + 2] = cum;
+                scratch[NT / kWave + 3] = c;
+                break;
+            }
+            cum += c;
+        }
+    }
+    __syncthreads();
+    Digit r;
+    r.d = scratch[NT / kWave + 1];
+    r.above = scratch[NT / kWave + 2];
+    r.at = scratch[NT / kWave + 3];
+    r.total = tot;
+    __syncthreads();
+    return r;
+}
+
+// ------------------------------------------------------------------------------------------
+// One workgroup per row
+// ------------------------------------------------------------------------------------------
+
+constexpr int NT = 1024;
+constexpr int NW = NT / kWave;
+constexpr int ITEMS = 4;
+constexpr int ROUND = NT * ITEMS;
+
+struct Smem {
+    int hist[NBIN];
+    int scratch[NW + 8];
+    int cnt[ITEMS * NW];
+    uint32_t buf_key[CAP];
+    int32_t buf_id[CAP];
+};
+
+__device__ __forceinline__ int64_t round_begin(const Row &r) { return r.lo; }
+
+__device__ void clear_hist(Smem &sm)
+{
+    for (int i = threadIdx.x; i < NBIN; i += NT) sm.hist[i] = 0;
+    __syncthreads();
+}
 
 // Histogram of digit (key >> shift) & (nbins-1) over the row's elements whose bits above the
 // digit equal `prefix` (all elements when pbits == 0).
 __device__ void hist_row(Smem &sm, const Row &r, int shift, int nbins, int pbits, uint32_t prefix)
 {
-    for (int i = threadIdx.x; i < 2048; i += NT) sm.hist[i] = 0;
-    __syncthreads();
+    clear_hist(sm);
     const int hs = shift + __builtin_ctz((unsigned)nbins);
     for (int64_t base = round_begin(r); base < r.hi; base += ROUND) {
-        uint32_t key[ITEMS];
-        int32_t id[ITEMS];
-        load_items(r, base, key, id);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            if (!key[j]) continue;
-            if (pbits && (hs >= 32 ? 0u : (key[j] >> hs)) != prefix) continue;
-            atomicAdd(&sm.hist[(key[j] >> shift) & (uint32_t)(nbins - 1)], 1);
+            int32_t id;
+            const uint32_t key = elem(r, base + (int64_t)j * NT + threadIdx.x, id);
+            if (!key) continue;
+            if (pbits && (hs >= 32 ? 0u : (key >> hs)) != prefix) continue;
+            atomicAdd(&sm.hist[(key >> shift) & (uint32_t)(nbins - 1)], 1);
         }
     }
     __syncthreads();
@@ -106,8 +182,7 @@ __device__ void hist_row(Smem &sm, const Row &r, int shift, int nbins, int pbits
 
 __device__ void hist_buf(Smem &sm, int nbuf, int shift, int nbins, uint32_t prefix)
 {
-    for (int i = threadIdx.x; i < 2048; i += NT) sm.hist[i] = 0;
-    __syncthreads();
+    clear_hist(sm);
     const int hs = shift + __builtin_ctz((unsigned)nbins);
     for (int i = threadIdx.x; i < nbuf; i += NT) {
         const uint32_t key = sm.buf_key[i];
@@ -117,47 +192,8 @@ __device__ void hist_buf(Smem &sm, int nbuf, int shift, int nbins, uint32_t pref
     __syncthreads();
 }
 
-// From the top bin down: the bin d where the running count first reaches `need`.  Returns d;
-// *above = elements in bins > d, *at = elements in bin d, *total = all counted elements.
-__device__ int find_digit(Smem &sm, int nbins, int need, int *above, int *at, int *total)
-{
-    // thread i owns bins (nbins-1 - 2i) and (nbins-2 - 2i): descending order over threads
-    const int per = nbins / NT; // 2 or 1
-    int mine = 0;
-    int b0 = nbins - 1 - per * (int)threadIdx.x;
-    for (int j = 0; j < per; ++j) mine += sm.hist[b0 - j];
-    int tot;
-    const int ex = block_exclusive_scan<NW>(mine, sm.scan, &tot);
-    if (threadIdx.x == 0) {
-        sm.misc[0] = -1;
-        sm.misc[3] = tot;
-    }
-    __syncthreads();
-    if (ex < need && ex + mine >= need) {
-        int cum = ex;
-        for (int j = 0; j < per; ++j) {
-            const int c = sm.hist[b0 - j];
-            if (cum + c >= need) {
-                sm.misc[0] = b0 - j;
-                sm.misc[1] = cum;
-                sm.misc[2] = c;
-                break;
-            }
-            cum += c;
-        }
-    }
-    __syncthreads();
-    const int d = sm.misc[0];
-    *above = sm.misc[1];
-    *at = sm.misc[2];
-    *total = sm.misc[3];
-    __syncthreads();
-    return d;
-}
-
-// Ordered selection pass over the row: an element is taken iff key > T, or key == T and fewer
-// than `eq_take` earlier elements had key == T (T == 0: every competing element).  Taken ids go
-// to dst[0..) in position order, or into the LDS buffer when to_buf.  Returns the count taken.
+// Ordered pass over the row: take key > T, or key == T while fewer than eq_take earlier
+// elements had key == T.  Taken ids go to dst (or into the LDS buffer).  Returns the count.
 __device__ int select_row(Smem &sm, const Row &r, uint32_t T, int eq_take, int32_t *dst,
                           bool to_buf, int limit)
 {
@@ -165,36 +201,30 @@ __device__ int select_row(Smem &sm, const Row &r, uint32_t T, int eq_take, int32
     for (int64_t base = round_begin(r); base < r.hi && taken < limit; base += ROUND) {
         uint32_t key[ITEMS];
         int32_t id[ITEMS];
-        load_items(r, base, key, id);
-        int n_eq = 0;
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) n_eq += (key[j] && key[j] == T) ? 1 : 0;
-        int eq_tot;
-        const int eq_ex = block_exclusive_scan<NW>(n_eq, sm.scan, &eq_tot);
-        bool take[ITEMS];
-        int n_take = 0, eq_rank = eq_seen + eq_ex;
+        bool is_eq[ITEMS], take[ITEMS];
+        int eq_slot[ITEMS], slot[ITEMS];
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            take[j] = false;
-            if (!key[j]) continue;
-            if (key[j] > T) take[j] = true;
-            else if (key[j] == T) take[j] = (eq_rank++ < eq_take);
-            n_take += take[j] ? 1 : 0;
+            key[j] = elem(r, base + (int64_t)j * NT + threadIdx.x, id[j]);
+            is_eq[j] = key[j] && key[j] == T;
         }
+        int eq_tot;
+        ordered_slots<NT, ITEMS>(is_eq, eq_slot, sm.cnt, eq_tot);
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j)
+            take[j] = key[j] && (key[j] > T || (is_eq[j] && eq_seen + eq_slot[j] < eq_take));
         int tot;
-        int pos = taken + block_exclusive_scan<NW>(n_take, sm.scan, &tot);
+        ordered_slots<NT, ITEMS>(take, slot, sm.cnt, tot);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            if (!take[j]) continue;
-            if (pos < limit) {
-                if (to_buf) {
-                    sm.buf_key[pos] = key[j];
-                    sm.buf_id[pos] = id[j];
-                } else {
-                    dst[pos] = id[j];
-                }
+            const int pos = taken + slot[j];
+            if (!take[j] || pos >= limit) continue;
+            if (to_buf) {
+                sm.buf_key[pos] = key[j];
+                sm.buf_id[pos] = id[j];
+            } else {
+                dst[pos] = id[j];
             }
-            ++pos;
         }
         taken += tot;
         eq_seen += eq_tot;
@@ -206,88 +236,107 @@ __device__ int select_row(Smem &sm, const Row &r, uint32_t T, int eq_take, int32
 __device__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq_take, int32_t *dst, int limit)
 {
     int taken = 0, eq_seen = 0;
-    for (int base = 0; base < nbuf; base += NT) {
-        const int i = base + threadIdx.x;
-        const uint32_t key = i < nbuf ? sm.buf_key[i] : 0u;
-        const int is_eq = (key && key == T) ? 1 : 0;
+    for (int base = 0; base < nbuf; base += ROUND) {
+        uint32_t key[ITEMS];
+        bool is_eq[ITEMS], take[ITEMS];
+        int eq_slot[ITEMS], slot[ITEMS];
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const int i = base + j * NT + threadIdx.x;
+            key[j] = i < nbuf ? sm.buf_key[i] : 0u;
+            is_eq[j] = key[j] && key[j] == T;
+        }
         int eq_tot;
-        const int eq_ex = block_exclusive_scan<NW>(is_eq, sm.scan, &eq_tot);
-        const bool take = key && (key > T || (is_eq && eq_seen + eq_ex < eq_take));
+        ordered_slots<NT, ITEMS>(is_eq, eq_slot, sm.cnt, eq_tot);
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j)
+            take[j] = key[j] && (key[j] > T || (is_eq[j] && eq_seen + eq_slot[j] < eq_take));
         int tot;
-        const int pos = taken + block_exclusive_scan<NW>(take ? 1 : 0, sm.scan, &tot);
-        if (take && pos < limit) dst[pos] = sm.buf_id[i];
+        ordered_slots<NT, ITEMS>(take, slot, sm.cnt, tot);
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const int pos = taken + slot[j];
+            if (take[j] && pos < limit) dst[pos] = sm.buf_id[base + j * NT + threadIdx.x];
+        }
         taken += tot;
         eq_seen += eq_tot;
     }
     return taken;
 }
 
+// The buffer holds, in position order, every element whose top `pbits` key bits are >= prefix
+// (pbits == 11).  Resolve the remaining digits and emit `need` picks.
+__device__ void finish_in_buf(Smem &sm, int nbuf, uint32_t prefix, int need_rem, int32_t *dst,
+                              int need)
+{
+    const int shifts[2] = {10, 0};
+    const int bitsv[2] = {11, 10};
+    for (int lvl = 0; lvl < 2; ++lvl) {
+        hist_buf(sm, nbuf, shifts[lvl], 1 << bitsv[lvl], prefix);
+        const Digit g = find_digit<NT>(sm.hist, 1 << bitsv[lvl], need_rem, sm.scratch);
+        prefix = (prefix << bitsv[lvl]) | (uint32_t)g.d;
+        need_rem -= g.above;
+    }
+    select_buf(sm, nbuf, prefix, need_rem, dst, need);
+}
+
 // Select `need` elements of the row by (key desc, position asc) into dst, ascending; pad -1.
 __device__ void select_top(Smem &sm, const Row &r, int need, int32_t *dst)
 {
     if (need <= 0) return;
-    // level 0 over the row
-    hist_row(sm, r, 21, 2048, 0, 0u);
-    int above, at, total;
-    int d = find_digit(sm, 2048, need, &above, &at, &total);
-    if (total <= need) { // everything competes: take all, pad
+    hist_row(sm, r, 21, NBIN, 0, 0u);
+    Digit g = find_digit<NT>(sm.hist, NBIN, need, sm.scratch);
+    if (g.total <= need) { // everything competes: take all, pad
         const int got = select_row(sm, r, 0u, 0, dst, false, need);
         for (int i = got + (int)threadIdx.x; i < need; i += NT) dst[i] = -1;
         return;
     }
-    uint32_t prefix = (uint32_t)d;
+    uint32_t prefix = (uint32_t)g.d;
     int pbits = 11;
-    int need_rem = need - above;
-    int taken_above = above;
-    // Further digits: (shift, bits) = (10, 11), (0, 10).
+    int need_rem = need - g.above;
+    int taken_above = g.above, at = g.at;
+    if (taken_above + at <= CAP) {
+        const int nbuf = select_row(sm, r, prefix << 21, INT32_MAX, nullptr, true, CAP);
+        __syncthreads();
+        finish_in_buf(sm, nbuf, prefix, need_rem, dst, need);
+        return;
+    }
+    // heavy ties: refine the threshold from the row itself
     const int shifts[2] = {10, 0};
     const int bitsv[2] = {11, 10};
-    bool in_buf = false;
-    int nbuf = 0;
     for (int lvl = 0; lvl < 2; ++lvl) {
-        if (!in_buf && taken_above + at <= CAP) {
-            // compact every element with (key >> (32 - pbits)) >= prefix into LDS, in order
-            const uint32_t lowest = prefix << (32 - pbits);
-            nbuf = select_row(sm, r, lowest, INT32_MAX, nullptr, true, CAP);
-            __syncthreads();
-            in_buf = true;
-        }
-        const int sh = shifts[lvl], nb = 1 << bitsv[lvl];
-        if (in_buf) hist_buf(sm, nbuf, sh, nb, prefix);
-        else hist_row(sm, r, sh, nb, pbits, prefix);
-        int a2, at2, tot2;
-        d = find_digit(sm, nb, need_rem, &a2, &at2, &tot2);
-        prefix = (prefix << bitsv[lvl]) | (uint32_t)d;
+        hist_row(sm, r, shifts[lvl], 1 << bitsv[lvl], pbits, prefix);
+        const Digit h = find_digit<NT>(sm.hist, 1 << bitsv[lvl], need_rem, sm.scratch);
+        prefix = (prefix << bitsv[lvl]) | (uint32_t)h.d;
         pbits += bitsv[lvl];
-        need_rem -= a2;
-        taken_above += a2;
-        at = at2;
+        need_rem -= h.above;
+        taken_above += h.above;
     }
-    // prefix is now the exact threshold key T; need_rem elements equal to T are taken.
-    if (in_buf) select_buf(sm, nbuf, prefix, need_rem, dst, need);
-    else select_row(sm, r, prefix, need_rem, dst, false, need);
+    select_row(sm, r, prefix, need_rem, dst, false, need);
 }
 
-__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
+// Row setup shared by both paths.  Returns false when the row needs no selection (all of it
+// written already).
+__device__ bool setup_row(const SelectArgs &a, int64_t row, Row &r, int32_t *&dst, int &need,
+                          bool write_fixed)
 {
-    __shared__ Smem sm;
-    const int64_t row = blockIdx.x;
     const int64_t t = row % a.n_q;
     int64_t V = a.q_pos0 + t + 1;
     if (V > a.kv_len) V = a.kv_len;
     int32_t *out = a.out + row * a.out_stride;
-    Row r;
     r.sc = a.scores + row * a.n_in;
     r.ids = a.cand_ids ? a.cand_ids + row * a.n_in : nullptr;
-    r.vec = (a.n_in % 4) == 0;
-
     if (a.mode == SELECT_SI) {
         if (V <= a.k) {
-            for (int i = threadIdx.x; i < a.k; i += NT) out[i] = i < V ? i : -1;
-            return;
+            if (write_fixed)
+                for (int i = threadIdx.x; i < a.k; i += blockDim.x) out[i] = i < V ? i : -1;
+            return false;
         }
-        for (int i = threadIdx.x; i < a.sink; i += NT) out[i] = i;
-        for (int i = threadIdx.x; i < a.window; i += NT) out[a.sink + i] = (int32_t)(V - a.window + i);
+        if (write_fixed) {
+            for (int i = threadIdx.x; i < a.sink; i += blockDim.x) out[i] = i;
+            for (int i = threadIdx.x; i < a.window; i += blockDim.x)
+                out[a.sink + i] = (int32_t)(V - a.window + i);
+        }
         r.id_lo = a.sink;
         r.id_hi = V - a.window;
         if (r.ids) {
@@ -297,25 +346,237 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
             r.lo = r.id_lo;
             r.hi = r.id_hi;
         }
-        select_top(sm, r, a.k - a.sink - a.window, out + a.sink + a.window);
+        dst = out + a.sink + a.window;
+        need = a.k - a.sink - a.window;
     } else { // SELECT_PAGES
         if (V <= a.k) {
-            for (int i = threadIdx.x; i < a.m_pages; i += NT) out[i] = -1;
-            return;
+            if (write_fixed)
+                for (int i = threadIdx.x; i < a.m_pages; i += blockDim.x) out[i] = -1;
+            return false;
         }
         r.lo = r.id_lo = a.sink / a.page;
         r.hi = r.id_hi = (V - a.window - 1) / a.page + 1;
-        select_top(sm, r, a.m_pages, out);
+        dst = out;
+        need = a.m_pages;
     }
+    return need > 0;
+}
+
+__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
+{
+    __shared__ Smem sm;
+    Row r;
+    int32_t *dst;
+    int need;
+    if (!setup_row(a, blockIdx.x, r, dst, need, true)) return;
+    select_top(sm, r, need, dst);
+}
+
+// ------------------------------------------------------------------------------------------
+// Chunked path
+// ------------------------------------------------------------------------------------------
+
+struct ChunkWs {
+    int *hist;       // [rows][NBIN]
+    int *info;       // [rows][4]: d0, above0, total, take_all
+    int *count;      // [rows][n_chunks]  (CHUNK_CAP + 1 = overflow)
+    uint32_t *ckey;  // [rows][n_chunks][CHUNK_CAP]
+    int32_t *cid;    // [rows][n_chunks][CHUNK_CAP]
+    int n_chunks;
+};
+
+__global__ __launch_bounds__(256) void chunk_zero_kernel(int *hist, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) hist[i] = 0;
+}
+
+__global__ __launch_bounds__(CNT_THREADS) void chunk_hist_kernel(SelectArgs a, ChunkWs ws)
+{
+    __shared__ int hist[NBIN];
+    const int64_t row = blockIdx.y;
+    Row r;
+    int32_t *dst;
+    int need;
+    if (!setup_row(a, row, r, dst, need, false)) return;
+    const int64_t c0 = (int64_t)blockIdx.x * CHUNK;
+    if (c0 + CHUNK <= r.lo || c0 >= r.hi) return;
+    for (int i = threadIdx.x; i < NBIN; i += CNT_THREADS) hist[i] = 0;
+    __syncthreads();
+    constexpr int CI = CHUNK / CNT_THREADS;
+    uint32_t key[CI];
+#pragma unroll
+    for (int j = 0; j < CI; ++j) {
+        int32_t id;
+        key[j] = elem(r, c0 + (int64_t)j * CNT_THREADS + threadIdx.x, id);
+    }
+#pragma unroll
+    for (int j = 0; j < CI; ++j)
+        if (key[j]) atomicAdd(&hist[key[j] >> 21], 1);
+    __syncthreads();
+    int *g = ws.hist + row * NBIN;
+    for (int i = threadIdx.x; i < NBIN; i += CNT_THREADS)
+        if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
+__global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a, ChunkWs ws)
+{
+    constexpr int CI = CHUNK / CNT_THREADS; // items per thread
+    __shared__ int hist[NBIN];
+    __shared__ int scratch[CNT_THREADS / kWave + 8];
+    __shared__ int cnt[kWave];
+    const int64_t row = blockIdx.y;
+    const int chunk = blockIdx.x;
+    Row r;
+    int32_t *dst;
+    int need;
+    if (!setup_row(a, row, r, dst, need, false)) return;
+    const int *g = ws.hist + row * NBIN;
+    for (int i = threadIdx.x; i < NBIN; i += CNT_THREADS) hist[i] = g[i];
+    __syncthreads();
+    Digit d = find_digit<CNT_THREADS>(hist, NBIN, need, scratch);
+    const bool take_all = d.total <= need;
+    const uint32_t lowest = take_all ? 1u : ((uint32_t)d.d << 21);
+    if (chunk == 0 && threadIdx.x == 0) {
+        int *info = ws.info + row * 4;
+        info[0] = take_all ? 0 : d.d;
+        info[1] = take_all ? 0 : d.above;
+        info[2] = d.total;
+        info[3] = take_all ? 1 : 0;
+    }
+    const int64_t c0 = (int64_t)chunk * CHUNK;
+    int *cntp = ws.count + row * ws.n_chunks + chunk;
+    if (c0 + CHUNK <= r.lo || c0 >= r.hi) {
+        if (threadIdx.x == 0) *cntp = 0;
+        return;
+    }
+    uint32_t *okey = ws.ckey + (row * ws.n_chunks + chunk) * CHUNK_CAP;
+    int32_t *oid = ws.cid + (row * ws.n_chunks + chunk) * CHUNK_CAP;
+    // CI items per thread: item j of thread t is element c0 + j*CNT_THREADS + t
+    uint32_t key[CI];
+    int32_t id[CI];
+    bool take[CI];
+    int slot[CI];
+#pragma unroll
+    for (int j = 0; j < CI; ++j) {
+        key[j] = elem(r, c0 + (int64_t)j * CNT_THREADS + threadIdx.x, id[j]);
+        take[j] = key[j] >= lowest;
+    }
+    int taken;
+    ordered_slots<CNT_THREADS, CI>(take, slot, cnt, taken);
+#pragma unroll
+    for (int j = 0; j < CI; ++j) {
+        if (take[j] && slot[j] < CHUNK_CAP) {
+            okey[slot[j]] = key[j];
+            oid[slot[j]] = id[j];
+        }
+    }
+    if (threadIdx.x == 0) *cntp = taken > CHUNK_CAP ? CHUNK_CAP + 1 : taken;
+}
+
+__global__ __launch_bounds__(NT) void chunk_finish_kernel(SelectArgs a, ChunkWs ws)
+{
+    __shared__ Smem sm;
+    const int64_t row = blockIdx.x;
+    Row r;
+    int32_t *dst;
+    int need;
+    if (!setup_row(a, row, r, dst, need, true)) return;
+    const int *info = ws.info + row * 4;
+    const int d0 = info[0], above0 = info[1], take_all = info[3];
+    // slice offsets (exclusive scan of the counts) into sm.hist, which is free until the end
+    const int *counts = ws.count + row * ws.n_chunks;
+    int overflow = 0, total = 0;
+    for (int base = 0; base < ws.n_chunks; base += NT) {
+        const int i = base + threadIdx.x;
+        const int c = i < ws.n_chunks ? counts[i] : 0;
+        overflow |= c > CHUNK_CAP;
+        int tot;
+        const int ex = block_exclusive_scan<NW>(c > CHUNK_CAP ? 0 : c, sm.scratch, &tot);
+        if (i < ws.n_chunks) sm.hist[i] = total + ex;
+        total += tot;
+    }
+    __syncthreads();
+    // copy the slices in chunk order: one wave per slice, coalesced
+    if (total <= CAP) {
+        for (int i = wave_id(); i < ws.n_chunks; i += NW) {
+            const int c = counts[i];
+            if (c > CHUNK_CAP) continue;
+            const int off = sm.hist[i];
+            const uint32_t *ck = ws.ckey + (row * ws.n_chunks + i) * CHUNK_CAP;
+            const int32_t *ci = ws.cid + (row * ws.n_chunks + i) * CHUNK_CAP;
+            for (int e = lane_id(); e < c; e += kWave) {
+                sm.buf_key[off + e] = ck[e];
+                sm.buf_id[off + e] = ci[e];
+            }
+        }
+    }
+    overflow = __syncthreads_or(overflow);
+    if (overflow || total > CAP) { // fall back to the one-workgroup path over the row
+        select_top(sm, r, need, dst);
+        return;
+    }
+    if (take_all) {
+        const int got = select_buf(sm, total, 0u, 0, dst, need);
+        for (int i = got + (int)threadIdx.x; i < need; i += NT) dst[i] = -1;
+        return;
+    }
+    finish_in_buf(sm, total, (uint32_t)d0, need - above0, dst, need);
+}
+
+bool use_chunked(const SelectArgs &a)
+{
+    const int64_t rows = (int64_t)a.batch * a.n_q;
+    return a.mode == SELECT_SI && rows < 1024 && a.n_in >= 8 * CHUNK &&
+           (a.n_in + CHUNK - 1) / CHUNK <= NBIN;
 }
 
 } // namespace
 
-hipError_t launch_select(const SelectArgs &a, hipStream_t stream)
+size_t select_workspace_bytes(int64_t rows, int64_t n_in, int mode)
+{
+    SelectArgs a{};
+    a.batch = (int)rows;
+    a.n_q = 1;
+    a.n_in = n_in;
+    a.mode = mode;
+    if (!use_chunked(a)) return 0;
+    const int64_t nc = (n_in + CHUNK - 1) / CHUNK;
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    return r256(rows * NBIN * 4) + r256(rows * 4 * 4) + r256(rows * nc * 4) +
+           2 * r256(rows * nc * CHUNK_CAP * 4);
+}
+
+hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream)
 {
     const int64_t rows = (int64_t)a.batch * a.n_q;
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)rows), dim3(NT), 0, stream, a);
+    if (!use_chunked(a)) {
+        hipLaunchKernelGGL(select_kernel, dim3((unsigned)rows), dim3(NT), 0, stream, a);
+        return hipGetLastError();
+    }
+    const int64_t nc = (a.n_in + CHUNK - 1) / CHUNK;
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    uint8_t *p = static_cast<uint8_t *>(ws);
+    ChunkWs w;
+    w.hist = reinterpret_cast<int *>(p);
+    p += r256(rows * NBIN * 4);
+    w.info = reinterpret_cast<int *>(p);
+    p += r256(rows * 4 * 4);
+    w.count = reinterpret_cast<int *>(p);
+    p += r256(rows * nc * 4);
+    w.ckey = reinterpret_cast<uint32_t *>(p);
+    p += r256(rows * nc * CHUNK_CAP * 4);
+    w.cid = reinterpret_cast<int32_t *>(p);
+    w.n_chunks = (int)nc;
+    const int64_t nh = rows * NBIN;
+    hipLaunchKernelGGL(chunk_zero_kernel, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, stream,
+                       w.hist, nh);
+    hipLaunchKernelGGL(chunk_hist_kernel, dim3((unsigned)nc, (unsigned)rows), dim3(CNT_THREADS), 0,
+                       stream, a, w);
+    hipLaunchKernelGGL(chunk_collect_kernel, dim3((unsigned)nc, (unsigned)rows), dim3(CNT_THREADS),
+                       0, stream, a, w);
+    hipLaunchKernelGGL(chunk_finish_kernel, dim3((unsigned)rows), dim3(NT), 0, stream, a, w);
     return hipGetLastError();
 }
 

@@ -200,7 +200,8 @@ def index_scores(q, w, keys, key_scale=None, q_pos0=None, out=None, stream=None)
     return out
 
 
-def topk_select(scores, k, sink, window, kv_len, q_pos0, cand_ids=None, out=None, stream=None):
+def topk_select(scores, k, sink, window, kv_len, q_pos0, cand_ids=None, out=None,
+                ws: Optional[Workspace] = None, stream=None):
     """idx [B, n_q, k] int32 from flat scores [B, n_q, L] or candidates (scores, cand_ids)."""
     _need(scores, "scores", torch.float32, 3)
     B, T, n = scores.shape
@@ -209,7 +210,10 @@ def topk_select(scores, k, sink, window, kv_len, q_pos0, cand_ids=None, out=None
         _need(cand_ids, "cand_ids", torch.int32, 3)
     if out is None:
         out = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
-    lsa_topk_select(shape, Budget(k, sink, window), scores, n, cand_ids, out, None, 0, stream)
+    bud = Budget(k, sink, window)
+    nb = lsa_workspace_bytes(OP_TOPK_SELECT, shape, bud, n_cand=n)
+    wsb = (ws or Workspace()).get(nb, scores.device)
+    lsa_topk_select(shape, bud, scores, n, cand_ids, out, wsb, nb, stream)
     return out
 
 
