@@ -300,6 +300,41 @@ def cpu_baseline(inputs, cfg, budget_s=15.0):
                       f"selection, 16-head MLA attention), {dt:.1f} s"}
 
 
+def only_stage(torch, lsa, inputs, cfg, stage, steps):
+    """One stage of the headline decode step, `steps` times (counter runs).  `copy` is the
+    calibration kernel: out = src + 0 over 256 MiB of fp32 (reads and writes 256 MiB)."""
+    dev = "cuda"
+    if stage == "copy":
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(steps):
+            torch.add(src, 0.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy x{steps}: {src.numel() * 4} bytes read and written per launch")
+        return
+    w = cfg.DECODE_128K
+    s, b, a = w.index, w.budget, w.attn
+    inp = inputs.index_inputs(w, dev)
+    L = s.kv_len
+    scores = lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0)
+    ws = lsa.Workspace()
+    idx = lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=L, q_pos0=s.q_pos0, ws=ws)
+    att = inputs.attn_inputs(w, 0, dev) if stage == "attn" else None
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        if stage == "score":
+            lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0,
+                             out=scores)
+        elif stage == "topk":
+            lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=L, q_pos0=s.q_pos0, out=idx,
+                            ws=ws)
+        else:
+            lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale, b.sink, b.window,
+                            d_v=a.d_v, ws=ws)
+    torch.cuda.synchronize()
+    log(f"[bench] {stage} x{steps} done")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +342,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--extras", action=argparse.BooleanOptionalAction, default=True)
     ap.add_argument("--cpu-baseline", action=argparse.BooleanOptionalAction, default=True)
+    ap.add_argument("--only", choices=["score", "topk", "attn", "copy"],
+                    help="run one stage of the headline step (or a plain 256 MiB device copy) "
+                         "--steps times and exit; for hardware-counter runs under rocprofv3")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -324,6 +362,9 @@ def main():
         sys.exit(2)
     lsa.lib()
     torch.cuda.set_device(0)
+    if args.only:
+        only_stage(torch, lsa, inputs, cfg, args.only, args.steps)
+        return
 
     w, head = headline(torch, lsa, inputs, cfg, args.steps, args.warmup)
     s, b = w.index, w.budget

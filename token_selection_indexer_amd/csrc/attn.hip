@@ -37,6 +37,27 @@ __device__ __forceinline__ bool row_ok(int32_t id, int64_t kv_len) { return id >
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void glb_void_t;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// LDS chunk slot of 16-byte chunk c of gathered row r: c ^ sigma(r & 7), sigma(x) = 2(x&3) + x/4.
+// sigma is a bijection on 0..7, so the logit reads (8 consecutive rows, one chunk) hit 8
+// distinct bank groups; and rows x and x+4 land on opposite halves of each pair of slots, so the
+// transposing V reads (4 rows x 2 chunks per 16 lanes) hit 8 distinct bank groups too.
+__device__ __forceinline__ int swz(int c, int r)
+{
+    const int x = r & 7;
+    return c ^ ((2 * (x & 3)) | (x >> 2));
+}
+
+// gfx950 transposing LDS read: within each group of 16 lanes, lane j receives element j%4 of
+// the 8 bytes addressed by lanes j/4 + 4e of the group, e = 0..3.
+__device__ __forceinline__ uint2 ds_read_tr16(const uint8_t *lds_byte_ptr)
+{
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t *)(__attribute__((address_space(3))) uint8_t *)lds_byte_ptr);
+    return bitcast<uint2>(v);
+}
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
@@ -50,8 +71,7 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
     static_assert((AR * CPR) % 256 == 0, "whole DMA instructions per wave");
 
     // Two row buffers: round i is computed from buf[i&1] while round i+1 streams into the other
-    // one.  Chunk c of row r is stored at chunk slot c ^ (r & 7) of the row (an XOR swizzle that
-    // keeps the 16-byte logit reads of 8 consecutive rows on distinct LDS banks).
+    // one.  Chunk c of row r is stored at chunk slot swz(c, r) of the row.
     __shared__ __attribute__((aligned(16))) uint8_t buf[2][AR * ROWB];
     __shared__ float S[16][AR + 1];
     __shared__ __attribute__((aligned(16))) uint16_t Pm[16][AR + 8];
@@ -105,7 +125,7 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
         for (int j = 0; j < DMA_PER_WAVE; ++j) {
             const int f = (w * DMA_PER_WAVE + j) * kWave + l; // flat chunk slot
             const int r = f / CPR, cs = f % CPR;
-            const int gc = cs ^ (r & 7);
+            const int gc = swz(cs, r); // swz is an involution within each group of 8 chunks
             const int32_t id = rid[slot][r];
             const uint8_t *src = kv_b + (int64_t)(id < 0 ? 0 : id) * a.k_stride * 2 + gc * 16;
             __builtin_amdgcn_global_load_lds((glb_void_t *)src,
@@ -133,7 +153,7 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 const int c = 4 * kk + (l >> 4);
-                const bf16x8_t bk = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(kr + 16 * (c ^ (r & 7))));
+                const bf16x8_t bk = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(kr + 16 * swz(c, r)));
                 acc = mfma_16x16x32(qf[kk], bk, acc);
             }
             const bool ok = rid[cur][r] >= 0;
@@ -160,8 +180,7 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
                 const float p = (m_new == -INFINITY || sv[e] == -INFINITY) ? 0.0f : exp2f(sv[e] - m_new);
                 const uint32_t bits = f32_to_bf16_bits(p);
                 sum += bf16_bits_to_f32(bits); // normalise by what the product actually uses
-                // row rr = 4*part + e sits at K position 32*(rr/32) + 8*(rr%4) + (rr%32)/4
-                Pm[h][32 * (part >> 3) + 8 * e + (part & 7)] = (uint16_t)bits;
+                Pm[h][4 * part + e] = (uint16_t)bits;
             }
 #pragma unroll
             for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
@@ -174,10 +193,8 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
             }
         }
         __syncthreads();
-        // O = O * alpha + P . V ; wave w owns columns [w*DV/4, (w+1)*DV/4).  The K index of
-        // this product is permuted within each 32-row step: lane group g = l/16 element e is
-        // row g + 4e, so the four groups of one read touch four consecutive rows.  P was stored
-        // in the same permuted order.
+        // O = O * alpha + P . V ; wave w owns columns [w*DV/4, (w+1)*DV/4).  K = the 64 rows:
+        // lane group q = l/16 takes rows 32kk + 8q + [0,8) as two transposing reads of 4 rows.
         {
             float al[4];
 #pragma unroll
@@ -186,22 +203,21 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) oacc[nt][e] *= al[e];
+            const int q = l >> 4, j = l & 15;       // lane group, lane within group
+            const int re = j >> 2, c4 = j & 3;      // source lane role: row e, 4-column segment
 #pragma unroll
             for (int kk = 0; kk < AR / 32; ++kk) {
-                const bf16x8_t pf = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(&Pm[l & 15][32 * kk + 8 * (l >> 4)]));
-                const int r0 = 32 * kk + (l >> 4);
+                const bf16x8_t pf = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(&Pm[l & 15][32 * kk + 8 * q]));
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt) {
-                    const int col = w * (DV / 4) + 16 * nt + (l & 15);
-                    uint32_t v16[8];
+                    const int col = w * (DV / 4) + 16 * nt + 4 * c4; // this lane's source segment
+                    uint2 half[2];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int r = r0 + 4 * e;
-                        const int slot = (col >> 3) ^ (r & 7);
-                        v16[e] = *reinterpret_cast<const uint16_t *>(&buf[cur][r * ROWB + slot * 16 + (col & 7) * 2]);
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int r = 32 * kk + 8 * q + 4 * hh + re;
+                        half[hh] = ds_read_tr16(&buf[cur][r * ROWB + swz(col >> 3, r) * 16 + (col & 7) * 2]);
                     }
-                    const bf16x8_t vf = bitcast<bf16x8_t>(make_uint4(v16[0] | (v16[1] << 16), v16[2] | (v16[3] << 16),
-                                                                     v16[4] | (v16[5] << 16), v16[6] | (v16[7] << 16)));
+                    const bf16x8_t vf = bitcast<bf16x8_t>(make_uint4(half[0].x, half[0].y, half[1].x, half[1].y));
                     oacc[nt] = mfma_16x16x32(pf, vf, oacc[nt]);
                 }
             }

@@ -144,7 +144,11 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[MT], WF wf,
     }
 #pragma unroll
     for (int u = 0; u < G::NQL; ++u) part[u] = (p[u][0] + p[u][1]) + (p[u][2] + p[u][3]);
-    if (G::SPLIT) part[0] += __shfl_xor(part[0], 32, kWave);
+    if (G::SPLIT) { // lanes l < 32 receive lane l + 32's partial (gfx950 v_permlane32_swap)
+        const float other = bitcast<float>(__builtin_amdgcn_permlane32_swap(
+            bitcast<uint32_t>(part[0]), bitcast<uint32_t>(part[0]), false, false)[1]);
+        part[0] += other;
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -195,37 +199,32 @@ struct KeyBlock {
     }
 };
 
-// PD: blocks prefetched ahead of the one being computed; UNR: blocks per unrolled loop body
-// (a multiple of PD + 1, so every ring slot index is a compile-time constant).
-template <bool FP8, int D, int H, int MT, bool ONEQ, bool FINE, int WAVES, int BPW, int PD = 3,
-          int UNR = BPW>
+// PD: blocks prefetched ahead of the one being computed (register ring of PD + 1 blocks).  The
+// block loop is fully unrolled: every ring slot and LDS slab index is a compile-time constant and
+// consecutive blocks' instructions can interleave.
+template <bool FP8, int D, int H, int MT, bool ONEQ, bool FINE, int WAVES, int BPW, int PD = 1>
 __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
 {
     using G = Geo<H, MT, ONEQ>;
-    constexpr int KS = D / 16;
     using KB = KeyBlock<FP8, D>;
-    __shared__ __attribute__((aligned(16))) float w_lds[G::ROWS];
-    __shared__ __attribute__((aligned(16))) uint8_t slabs[WAVES][KB::BB];
+    constexpr int KS = D / 16;
+    static_assert(PD >= 1 && PD < BPW, "ring shape");
+    // two slabs per wave: block i is transposed in slab i&1 while block i-1 may still be read
+    __shared__ __attribute__((aligned(16))) uint8_t slabs[WAVES][2][KB::BB];
     const int b = blockIdx.z;
     const int64_t t0 = (int64_t)blockIdx.y * G::NQW;
     const int nq_avail = (int)min((int64_t)G::NQW, (int64_t)a.n_q - t0);
     const int l = lane_id(), wv_id = wave_id(), g = l >> 5, n = l & 31;
 
-    // Every wave of the block serves the same queries: their head weights go to LDS once,
-    // indexed by indexer row r' (the epilogue reads 4 at a time).
-    if (threadIdx.x < G::ROWS) {
-        int qs, h;
-        bool valid;
-        rprime_to_qh<H, ONEQ>(threadIdx.x, qs, h, valid);
-        w_lds[threadIdx.x] = (valid && qs < nq_avail) ? a.w[((int64_t)b * a.n_q + t0 + qs) * H + h] : 0.0f;
-    }
     bf16x8_t qf[MT][KS];
     load_q<D, H, MT, ONEQ>(qf, a.q + ((int64_t)b * a.n_q + t0) * H * D, nq_avail);
+    float wv[G::VPL];
+    load_w<H, MT, ONEQ>(wv, a.w + ((int64_t)b * a.n_q + t0) * H, nq_avail);
 
-    // Valid ranges of the lane's query slots, and the wave-wide hull.
+    // Valid ranges of the lane's query slots, their hull and their intersection.
     int64_t lo[G::NQL], hi[G::NQL];
-    int64_t lo_all = INT64_MAX, hi_all = 0;   // hull of the wave's ranges
-    int64_t lo_in = 0, hi_in = INT64_MAX;     // their intersection
+    int64_t lo_all = INT64_MAX, hi_all = 0;
+    int64_t lo_in = 0, hi_in = INT64_MAX;
 #pragma unroll
     for (int u = 0; u < G::NQL; ++u) {
         const int qs = G::SPLIT ? 0 : g * G::NQL + u;
@@ -256,19 +255,21 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         }
     }
     hi_in = min(hi_in, a.n_keys);
-    __syncthreads();
-    const float *wl = &w_lds[G::VPL * g];
 
-    const uint8_t *keys_b = reinterpret_cast<const uint8_t *>(a.keys) +
-                            (int64_t)b * a.n_keys * D * (FP8 ? 1 : 2);
+    const uint8_t *keys_b = reinterpret_cast<const uint8_t *>(a.keys) + (int64_t)b * a.n_keys * KB::RB;
     const float *scale_b = FP8 ? a.kscale + (int64_t)b * a.n_keys : nullptr;
     const int32_t *pages_row = FINE ? a.pages + ((int64_t)b * a.n_q + t0) * a.m_pages : nullptr;
     const int64_t n_blocks = (a.n_out + 31) / 32;
+    // this lane's byte offsets inside a block (contiguous 1 KB pieces)
+    uint32_t lane_off[KB::NP];
+#pragma unroll
+    for (int i = 0; i < KB::NP; ++i) {
+        const int f = i * kWave + l;
+        lane_off[i] = (uint32_t)((f / KB::CPR) * KB::RB + (f % KB::CPR) * 16);
+    }
 
-    // Block `it` of this wave: output slots s0 .. s0+31, the lane's key row, whether it exists
-    // and whether it needs any compute.
     struct Blk {
-        int64_t s0, row0, row, lrow; // row0: key row of slot s0; row: this lane's key row
+        int64_t s0, row0; // first output slot and first key row of the block
         bool valid, live;
     };
     auto locate = [&](int it) {
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         k.valid = blk < n_blocks;
         k.s0 = blk * 32;
         k.live = false;
-        k.row = k.row0 = 0;
+        k.row0 = 0;
         if (!k.valid) return k;
         if (FINE) {
             const int64_t pi = k.s0 / a.page;
@@ -288,51 +289,50 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
             k.row0 = k.s0;
             k.live = k.s0 < hi_all && k.s0 + 32 > lo_all;
         }
-        k.row = k.row0 + n;
-        k.lrow = k.row < a.n_keys ? k.row : a.n_keys - 1;
         return k;
     };
+    auto fetch = [&](const Blk &k, KB &kb, float &sc) {
+        if (!k.live) return;
+        if (k.row0 + 32 <= a.n_keys) {
+            const uint8_t *base = keys_b + k.row0 * KB::RB;
+#pragma unroll
+            for (int i = 0; i < KB::NP; ++i) kb.raw[i] = ld16(base + lane_off[i]);
+            if (FP8) sc = scale_b[k.row0 + n];
+        } else {
+            kb.load(keys_b, k.row0, a.n_keys, l);
+            if (FP8) sc = scale_b[min(k.row0 + n, a.n_keys - 1)];
+        }
+    };
 
-    // PD + 1 blocks in flight per wave: blocks it+1 .. it+PD are loading while block it is
-    // computed (a register ring whose slot indices are all static).
-    static_assert(PD >= 1 && PD < BPW && UNR % (PD + 1) == 0 && BPW % UNR == 0, "ring shape");
     Blk bq[PD + 1];
     KB kq[PD + 1];
     float sq[PD + 1];
-    uint8_t *slab = slabs[wv_id];
     static_for<0, PD>([&](auto I) {
         constexpr int i = decltype(I)::value;
         bq[i] = locate(i);
         sq[i] = 1.0f;
-        if (bq[i].live) {
-            kq[i].load(keys_b, bq[i].row0, a.n_keys, l);
-            if (FP8) sq[i] = scale_b[bq[i].lrow];
-        }
+        fetch(bq[i], kq[i], sq[i]);
     });
-    for (int grp = 0; grp < BPW / UNR; ++grp)
-    static_for<0, UNR>([&](auto IS) {
-        constexpr int cs = decltype(IS)::value % (PD + 1); // slot of block it
-        constexpr int ns = (cs + PD) % (PD + 1);           // slot that receives block it + PD
-        const int it = grp * UNR + decltype(IS)::value;
-        if (it + PD < BPW) {
+    static_for<0, BPW>([&](auto IT) {
+        constexpr int it = decltype(IT)::value;
+        constexpr int cs = it % (PD + 1);        // slot of block it
+        constexpr int ns = (it + PD) % (PD + 1); // slot that receives block it + PD
+        if constexpr (it + PD < BPW) {
             bq[ns] = locate(it + PD);
             sq[ns] = 1.0f;
-            if (bq[ns].live) {
-                kq[ns].load(keys_b, bq[ns].row0, a.n_keys, l);
-                if (FP8) sq[ns] = scale_b[bq[ns].lrow];
-            }
+            fetch(bq[ns], kq[ns], sq[ns]);
         }
         const Blk cb = bq[cs];
         if (!cb.valid) return; // later blocks are past the end too
 
         float part[G::NQL];
         if (cb.live) {
+            uint8_t *slab = slabs[wv_id][it & 1];
             f32x16_t acc[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16_t{};
-            // through the slab into operand layout (in-order LDS access within the wave)
+            // through the slab into operand layout (a wave's LDS accesses complete in order)
             kq[cs].to_slab(slab, l);
-            __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int j = 0; j < KB::CPR / 2; ++j) {
                 const uint4 c = KB::chunk(slab, l, j);
@@ -349,8 +349,7 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
                     for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_32x32x16(qf[mt][j], b0, acc[mt]);
                 }
             }
-            __builtin_amdgcn_wave_barrier();
-            epilogue<H, MT, ONEQ>(acc, [&](int v) { return wl[v]; }, part);
+            epilogue<H, MT, ONEQ>(acc, [&](int v) { return wv[v]; }, part);
             if (FP8) {
 #pragma unroll
                 for (int u = 0; u < G::NQL; ++u) part[u] *= sq[cs];
@@ -361,24 +360,24 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
             // a block inside every query's range and inside the output needs no lane masks
             const bool full = cb.live && cb.row0 >= lo_in && cb.row0 + 32 <= hi_in &&
                               cb.s0 + 32 <= a.n_out && nq_avail == G::NQW;
+            float *ob = a.out + ((int64_t)b * a.n_q + t0) * a.n_out + cb.s0;
+            int32_t *ib = FINE ? a.out_ids + ((int64_t)b * a.n_q + t0) * a.n_out + cb.s0 : nullptr;
             if (full) {
 #pragma unroll
                 for (int u = 0; u < G::NQL; ++u) {
                     const int qs = G::SPLIT ? 0 : g * G::NQL + u;
-                    const int64_t o = ((int64_t)b * a.n_q + t0 + qs) * a.n_out + cb.s0 + n;
-                    a.out[o] = part[u];
-                    if (FINE) a.out_ids[o] = (int32_t)cb.row;
+                    ob[(int64_t)qs * a.n_out + n] = part[u];
+                    if (FINE) ib[(int64_t)qs * a.n_out + n] = (int32_t)(cb.row0 + n);
                 }
             } else {
+                const int64_t row = cb.row0 + n;
 #pragma unroll
                 for (int u = 0; u < G::NQL; ++u) {
                     const int qs = G::SPLIT ? 0 : g * G::NQL + u;
                     if (qs >= nq_avail || cb.s0 + n >= a.n_out) continue;
-                    const int64_t row = cb.row;
                     const bool ok = cb.live && row >= lo[u] && row < hi[u] && row < a.n_keys;
-                    const int64_t o = ((int64_t)b * a.n_q + t0 + qs) * a.n_out + cb.s0 + n;
-                    a.out[o] = ok ? part[u] : -INFINITY;
-                    if (FINE) a.out_ids[o] = ok ? (int32_t)row : -1;
+                    ob[(int64_t)qs * a.n_out + n] = ok ? part[u] : -INFINITY;
+                    if (FINE) ib[(int64_t)qs * a.n_out + n] = ok ? (int32_t)row : -1;
                 }
             }
         }

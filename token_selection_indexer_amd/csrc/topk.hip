@@ -50,7 +50,43 @@ struct Row {
     const int32_t *ids; // nullptr: id = position
     int64_t lo, hi;
     int64_t id_lo, id_hi;
+    bool vec;           // rows start 16-byte aligned: 4-element vector loads
 };
+
+// Elements p .. p+3 (p a multiple of 4): keys (0 = does not compete) and ids.
+__device__ __forceinline__ void elem4(const Row &r, int64_t p, uint32_t (&key)[4], int32_t (&id)[4])
+{
+    if (r.vec && p >= r.lo && p + 4 <= r.hi) {
+        const float4 v = *reinterpret_cast<const float4 *>(r.sc + p);
+        const float f[4] = {v.x, v.y, v.z, v.w};
+        int32_t c[4];
+        if (r.ids) {
+            const int4 iv = *reinterpret_cast<const int4 *>(r.ids + p);
+            c[0] = iv.x; c[1] = iv.y; c[2] = iv.z; c[3] = iv.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[j] = (int32_t)(p + j);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            id[j] = c[j];
+            key[j] = (c[j] >= r.id_lo && c[j] < r.id_hi) ? order_key(f[j]) : 0u;
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t q = p + j;
+        if (q < r.lo || q >= r.hi) {
+            id[j] = -1;
+            key[j] = 0u;
+            continue;
+        }
+        const int32_t c = r.ids ? r.ids[q] : (int32_t)q;
+        id[j] = c;
+        key[j] = (c >= r.id_lo && c < r.id_hi) ? order_key(r.sc[q]) : 0u;
+    }
+}
 
 // Element at position p: (key, id); key 0 = does not compete.
 __device__ __forceinline__ uint32_t elem(const Row &r, int64_t p, int32_t &id)
@@ -280,11 +316,120 @@ __device__ void finish_in_buf(Smem &sm, int nbuf, uint32_t prefix, int need_rem,
     select_buf(sm, nbuf, prefix, need_rem, dst, need);
 }
 
+// ---- streaming passes: each wave owns a contiguous segment of the row (no block barriers) ----
+
+constexpr int WCAP = CAP / NW; // candidate list entries per wave
+
+struct Seg {
+    int64_t b0, b1; // [b0, b1): multiples of 4, covering the wave's part of [lo, hi)
+};
+
+__device__ __forceinline__ Seg wave_segment(const Row &r)
+{
+    const int64_t a0 = r.lo & ~int64_t(3);
+    const int64_t n = r.hi - a0;
+    const int64_t seg = ((n + NW - 1) / NW + 255) / 256 * 256;
+    Seg s;
+    s.b0 = a0 + (int64_t)wave_id() * seg;
+    s.b1 = min(s.b0 + seg, r.hi);
+    return s;
+}
+
+// Level-0 histogram (key bits 31..21) of the row.
+__device__ void hist_row_seg(Smem &sm, const Row &r)
+{
+    clear_hist(sm);
+    const Seg sg = wave_segment(r);
+#pragma unroll 4
+    for (int64_t p = sg.b0 + 4 * lane_id(); p < sg.b1; p += 4 * kWave) {
+        uint32_t key[4];
+        int32_t id[4];
+        elem4(r, p, key, id);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (key[j]) atomicAdd(&sm.hist[key[j] >> 21], 1);
+    }
+    __syncthreads();
+}
+
+// Every element with key >= lowest, into the LDS buffer in position order.  Each wave appends
+// its segment's elements to its own list (order kept by a wave prefix sum), then the lists are
+// concatenated in wave order.  Returns false if a wave's list overflowed (caller falls back).
+__device__ bool collect_row_seg(Smem &sm, const Row &r, uint32_t lowest, int &nbuf)
+{
+    const int w = wave_id(), lane = lane_id();
+    const Seg sg = wave_segment(r);
+    const int base = w * WCAP;
+    int cnt = 0;
+    // The trip count is uniform over the wave (the scan below needs every lane): segments are
+    // whole multiples of 4*64 elements, so p never reaches the next wave's segment, and
+    // positions at or past hi read as "does not compete".
+#pragma unroll 4
+    for (int64_t p0 = sg.b0; p0 < sg.b1; p0 += 4 * kWave) {
+        const int64_t p = p0 + 4 * lane;
+        uint32_t key[4];
+        int32_t id[4];
+        elem4(r, p, key, id);
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c += (key[j] >= lowest) ? 1 : 0;
+        if (__ballot(c > 0) == 0) continue;
+        const int inc = wave_inclusive_scan(c);
+        const int tot = __shfl(inc, kWave - 1, kWave);
+        int pos = cnt + inc - c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (key[j] < lowest) continue;
+            if (pos < WCAP) {
+                sm.buf_key[base + pos] = key[j];
+                sm.buf_id[base + pos] = id[j];
+            }
+            ++pos;
+        }
+        cnt += tot;
+    }
+    if (lane == 0) sm.cnt[w] = cnt;
+    __syncthreads();
+    int off = 0, total = 0, over = 0;
+    for (int u = 0; u < NW; ++u) {
+        const int c = sm.cnt[u];
+        if (u < w) off += c;
+        total += c;
+        over |= c > WCAP;
+    }
+    if (over || total > CAP) {
+        __syncthreads();
+        return false;
+    }
+    // concatenate: lists are read into registers first, so no list is overwritten unread
+    constexpr int PER = WCAP / kWave;
+    uint32_t k[PER];
+    int32_t id[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + i * kWave;
+        k[i] = e < cnt ? sm.buf_key[base + e] : 0u;
+        id[i] = e < cnt ? sm.buf_id[base + e] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + i * kWave;
+        if (e < cnt) {
+            sm.buf_key[off + e] = k[i];
+            sm.buf_id[off + e] = id[i];
+        }
+    }
+    __syncthreads();
+    nbuf = total;
+    return true;
+}
+
 // Select `need` elements of the row by (key desc, position asc) into dst, ascending; pad -1.
 __device__ void select_top(Smem &sm, const Row &r, int need, int32_t *dst)
 {
     if (need <= 0) return;
-    hist_row(sm, r, 21, NBIN, 0, 0u);
+    hist_row_seg(sm, r);
     Digit g = find_digit<NT>(sm.hist, NBIN, need, sm.scratch);
     if (g.total <= need) { // everything competes: take all, pad
         const int got = select_row(sm, r, 0u, 0, dst, false, need);
@@ -296,8 +441,11 @@ __device__ void select_top(Smem &sm, const Row &r, int need, int32_t *dst)
     int need_rem = need - g.above;
     int taken_above = g.above, at = g.at;
     if (taken_above + at <= CAP) {
-        const int nbuf = select_row(sm, r, prefix << 21, INT32_MAX, nullptr, true, CAP);
-        __syncthreads();
+        int nbuf;
+        if (!collect_row_seg(sm, r, prefix << 21, nbuf)) { // uneven segments: one ordered pass
+            nbuf = select_row(sm, r, prefix << 21, INT32_MAX, nullptr, true, CAP);
+            __syncthreads();
+        }
         finish_in_buf(sm, nbuf, prefix, need_rem, dst, need);
         return;
     }
@@ -326,6 +474,8 @@ __device__ bool setup_row(const SelectArgs &a, int64_t row, Row &r, int32_t *&ds
     int32_t *out = a.out + row * a.out_stride;
     r.sc = a.scores + row * a.n_in;
     r.ids = a.cand_ids ? a.cand_ids + row * a.n_in : nullptr;
+    r.vec = (a.n_in % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0 &&
+            (!a.cand_ids || (reinterpret_cast<uintptr_t>(a.cand_ids) & 15) == 0);
     if (a.mode == SELECT_SI) {
         if (V <= a.k) {
             if (write_fixed)
