@@ -250,11 +250,17 @@ def test_tiny_prefill_end_to_end_selection():
 
 
 # ------------------------------------------------------------------------------ page keys
-@pytest.mark.parametrize("kd,P,L", [("fp8", 64, 5000), ("bf16", 64, 4096), ("fp8", 32, 999),
-                                    ("bf16", 256, 1300), ("fp8", 1, 77)])
-def test_page_summary_bit_exact(kd, P, L):
+@pytest.mark.parametrize("kd,P,L,d", [
+    ("fp8", 64, 5000, 128), ("bf16", 64, 4096, 128), ("fp8", 32, 999, 128), ("bf16", 256, 1300, 128),
+    ("fp8", 1, 77, 128), ("fp8", 8, 1000, 128), ("bf16", 4, 333, 128), ("bf16", 2, 301, 128),
+    ("fp8", 256, 3000, 128), ("fp8", 16, 1000, 64), ("bf16", 8, 700, 64), ("fp8", 128, 2000, 64),
+    ("fp8", 4, 500, 64)])
+def test_page_summary_bit_exact(kd, P, L, d):
+    """Pages of at least one 16-byte piece per lane group take the one-wave-per-page kernel,
+    smaller pages the per-element one; both must give the oracle's bits, partial last page
+    included."""
     w = Workload(name="p", index=IndexShape(
-        batch=2, n_q=1, kv_len=L, q_pos0=L - 1, heads=64, head_dim=128, key_dtype=kd),
+        batch=2, n_q=1, kv_len=L, q_pos0=L - 1, heads=64, head_dim=d, key_dtype=kd),
         budget=TINY_PREFILL_4K.budget, attn=TINY_PREFILL_4K.attn, seed=12)
     inp = inputs.index_inputs(w, DEV)
     pk = lsa.page_summary(inp["keys"], inp["scale"], P)

@@ -27,7 +27,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
 
 # per-file extras: the scoring kernels keep their MFMA accumulators in VGPRs (their epilogue
 # reads every accumulator with VALU instructions; AGPR-resident results would each need a copy)
-EXTRA = {"score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# the page keys are defined with separately rounded multiplies and adds: no FMA contraction
+EXTRA = {"score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "pages.hip": ["-ffp-contract=off"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -6,14 +6,24 @@
 //   v[j]  = fp32(scale[s] * e4m3(kq[s][i]))  (bf16 keys: the value), s = p*P + j; +0 past kv_len
 //   sum   = pairwise tree sum of v[0..P): halves summed separately, then added, recursively
 //   pk    = bf16_rne(sum / n_p), n_p = tokens of the page that exist
-// No FMA contraction anywhere (explicit round-to-nearest multiply / add / divide), so the result
-// is reproducible bit for bit.
+// Every multiply, add and divide rounds on its own: contraction into FMA is switched off for
+// this file (pragma below, and -ffp-contract=off on its compile line), because HIP's
+// __fmul_rn / __fadd_rn are plain operators that the compiler may otherwise fuse.
 //
-// Layout: D/2 threads per page, each owning two adjacent key elements, so every token of the
-// page is one contiguous D-element load across the threads.  The tree is a binary counter over
-// the P tokens held in registers (fully unrolled per P).
+// Layout (pages of at least G tokens, G = 64 / LPR): a wave per page at a time, looping over
+// pages with the next page's loads in flight.  A key row is LPR
+// 16-byte pieces; lane (g, c) = (lane / LPR, lane % LPR) loads piece c of the TPL = P / G
+// consecutive tokens g*TPL .. g*TPL + TPL - 1, so each load instruction reads whole rows and every
+// lane's register data is the subtree of TPL adjacent tokens.  Those subtrees are summed in
+// registers (a binary counter, fully unrolled), then combined across the G lane groups by xor
+// shuffles: group g meets g^1, then pairs meet pairs, ... -- exactly the levels of the pairwise
+// tree above the subtrees (binary32 addition is commutative, so which operand is on the left
+// does not change the bits).  Smaller pages: D/2 threads per page, each owning two adjacent key
+// elements and the whole tree of its page.
 #include "device.hpp"
 #include "internal.hpp"
+
+#pragma clang fp contract(off)
 
 namespace lsa {
 namespace {
@@ -71,10 +81,167 @@ __global__ __launch_bounds__(256) void page_summary_kernel(const void *keys, con
     *reinterpret_cast<uint32_t *>(pk + ((int64_t)b * n_pages + p) * D + 2 * pair) = out;
 }
 
+// Lanes per key row (16-byte pieces) and lane groups per wave.
+template <bool FP8, int D>
+struct PageGeo {
+    static constexpr int EB = FP8 ? 1 : 2;      // bytes per element
+    static constexpr int EPL = 16 / EB;         // elements per 16-byte piece
+    static constexpr int LPR = D * EB / 16;     // lanes per row
+    static constexpr int G = kWave / LPR;       // lane groups
+};
+
+template <bool FP8, int D, int P>
+__global__ __launch_bounds__(256) void page_summary_wave_kernel(const void *keys, const float *kscale,
+                                                                int64_t kv_len, int64_t page_lo,
+                                                                int64_t page_hi, int64_t n_pages,
+                                                                uint16_t *pk)
+{
+    using Geo = PageGeo<FP8, D>;
+    constexpr int EPL = Geo::EPL, LPR = Geo::LPR, G = Geo::G;
+    static_assert(P >= G && P % G == 0, "page must cover every lane group");
+    constexpr int TPL = P / G;                  // tokens per lane
+    constexpr int LEV = __builtin_ctz(TPL) + 1; // binary-counter stack depth
+    constexpr int ROW = D * Geo::EB;            // bytes per key row
+    const int b = blockIdx.y;
+    const int lane = lane_id(), g = lane / LPR, c = lane % LPR;
+    const uint8_t *kb = reinterpret_cast<const uint8_t *>(keys) + (int64_t)b * kv_len * ROW + 16 * c;
+    const float *sb = FP8 ? kscale + (int64_t)b * kv_len : nullptr;
+
+    // a lane's raw data for one page: TPL pieces (+ TPL scales); zero past kv_len
+    uint4 raw[TPL];
+    float scl[TPL];
+    auto load = [&](int64_t p) {
+        const int64_t t0 = p * P + g * TPL;
+        static_for<0, TPL>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            const bool ok = t0 + j < kv_len;
+            raw[j] = ok ? ld16(kb + (t0 + j) * ROW) : make_uint4(0u, 0u, 0u, 0u);
+            if constexpr (FP8) scl[j] = ok ? sb[t0 + j] : 0.0f;
+        });
+    };
+
+    // grid-stride over pages; the next page's loads are issued before this page's arithmetic
+    const int64_t stride = (int64_t)gridDim.x * (blockDim.x / kWave);
+    int64_t p = page_lo + (int64_t)blockIdx.x * (blockDim.x / kWave) + wave_id();
+    if (p >= page_hi) return; // whole wave
+    load(p);
+    for (; p < page_hi; p += stride) {
+        uint4 cur[TPL];
+        float cs[TPL];
+        static_for<0, TPL>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            cur[j] = raw[j];
+            if constexpr (FP8) cs[j] = scl[j];
+        });
+        if (p + stride < page_hi) load(p + stride);
+
+        float stk[LEV][EPL];
+        static_for<0, TPL>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            constexpr int depth = __builtin_popcount(j);
+            constexpr int merges = __builtin_ctz(~j);
+            const uint32_t wd[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
+            float x[EPL];
+            if constexpr (FP8) {
+                // a zero code times a zero scale is +0: slots past kv_len add +0, as defined
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint2 bf = e4m3x4_to_bf16x4(wd[u]);
+                    x[4 * u + 0] = __fmul_rn(cs[j], __uint_as_float(bf.x << 16));
+                    x[4 * u + 1] = __fmul_rn(cs[j], __uint_as_float(bf.x & 0xffff0000u));
+                    x[4 * u + 2] = __fmul_rn(cs[j], __uint_as_float(bf.y << 16));
+                    x[4 * u + 3] = __fmul_rn(cs[j], __uint_as_float(bf.y & 0xffff0000u));
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    x[2 * u + 0] = __uint_as_float(wd[u] << 16);
+                    x[2 * u + 1] = __uint_as_float(wd[u] & 0xffff0000u);
+                }
+            }
+            static_for<0, merges>([&](auto M) {
+                constexpr int m = decltype(M)::value;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) x[e] = __fadd_rn(stk[depth - 1 - m][e], x[e]);
+            });
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) stk[depth - merges][e] = x[e];
+        });
+        // levels above the per-lane subtrees
+#pragma unroll
+        for (int m = LPR; m < kWave; m <<= 1)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                stk[0][e] = __fadd_rn(stk[0][e], __shfl_xor(stk[0][e], m, kWave));
+        if (g == 0) {
+            const int64_t n_p = min((int64_t)P, kv_len - p * P);
+            // a full page divides by P = 2^k: multiplying by the exact 2^-k rounds identically
+            const bool full = n_p == P;
+            const float nf = (float)n_p;
+            uint32_t o[EPL / 2];
+#pragma unroll
+            for (int e = 0; e < EPL / 2; ++e) {
+                const float m0 = full ? __fmul_rn(stk[0][2 * e], 1.0f / P) : __fdiv_rn(stk[0][2 * e], nf);
+                const float m1 = full ? __fmul_rn(stk[0][2 * e + 1], 1.0f / P) : __fdiv_rn(stk[0][2 * e + 1], nf);
+                o[e] = f32_to_bf16_bits(m0) | (f32_to_bf16_bits(m1) << 16);
+            }
+            uint16_t *dst = pk + ((int64_t)b * n_pages + p) * D + c * EPL;
+#pragma unroll
+            for (int e = 0; e < EPL / 8; ++e)
+                *reinterpret_cast<uint4 *>(dst + 8 * e) =
+                    make_uint4(o[4 * e], o[4 * e + 1], o[4 * e + 2], o[4 * e + 3]);
+        }
+    }
+}
+
+template <bool FP8, int D, int P>
+hipError_t launch_wave(const void *keys, const float *kscale, int batch, int64_t kv_len,
+                       int64_t page_lo, int64_t page_hi, uint16_t *pk, hipStream_t st)
+{
+    const int64_t n_pages = (kv_len + P - 1) / P;
+    // about 2048 workgroups in all (8 per CU), each wave looping over its share of the pages
+    const int64_t want = batch >= 2048 ? 1 : 2048 / batch;
+    const int64_t need = (page_hi - page_lo + 3) / 4;
+    const int64_t wg = need < want ? need : want;
+    const dim3 grid((unsigned)wg, (unsigned)batch);
+    hipLaunchKernelGGL((page_summary_wave_kernel<FP8, D, P>), grid, dim3(256), 0, st, keys, kscale,
+                       kv_len, page_lo, page_hi, n_pages, pk);
+    return hipGetLastError();
+}
+
+template <bool FP8, int D>
+hipError_t launch_wave_p(const void *keys, const float *kscale, int batch, int64_t kv_len, int P,
+                         int64_t page_lo, int64_t page_hi, uint16_t *pk, hipStream_t st, bool &done)
+{
+    done = true;
+    switch (P) {
+#define LSA_PW(PP)                                                                                  \
+    case PP:                                                                                        \
+        if constexpr (PP >= PageGeo<FP8, D>::G)                                                     \
+            return launch_wave<FP8, D, PP>(keys, kscale, batch, kv_len, page_lo, page_hi, pk, st); \
+        break;
+        LSA_PW(1) LSA_PW(2) LSA_PW(4) LSA_PW(8) LSA_PW(16) LSA_PW(32) LSA_PW(64) LSA_PW(128) LSA_PW(256)
+#undef LSA_PW
+    default: break;
+    }
+    done = false;
+    return hipSuccess;
+}
+
 template <bool FP8>
 hipError_t launch_p(const void *keys, const float *kscale, int batch, int64_t kv_len, int D,
                     int P, int64_t page_lo, int64_t page_hi, uint16_t *pk, hipStream_t st)
 {
+    bool done = false;
+    hipError_t e = hipSuccess;
+    const bool a16 = ((reinterpret_cast<uintptr_t>(keys) | reinterpret_cast<uintptr_t>(pk)) & 15) == 0;
+    if (!a16)
+        ;
+    else if (D == 128)
+        e = launch_wave_p<FP8, 128>(keys, kscale, batch, kv_len, P, page_lo, page_hi, pk, st, done);
+    else if (D == 64)
+        e = launch_wave_p<FP8, 64>(keys, kscale, batch, kv_len, P, page_lo, page_hi, pk, st, done);
+    if (done) return e;
     const int64_t n_pages = (kv_len + P - 1) / P;
     const int64_t threads = (page_hi - page_lo) * (D / 2);
     const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)batch);
