@@ -552,12 +552,26 @@ hipError_t launch_flat(const ScoreArgs &a, hipStream_t st)
     constexpr int MT = H == 64 ? 2 : 1;
     using G = Geo<H, MT, false>;
     if (a.n_q <= 2 * G::NQW) {
-        constexpr int WAVES = 4, BPW = 16;
+        // Long-lived waves (32 blocks = 1024 keys each) amortise the per-wave load of q and w,
+        // and up to 3 blocks in flight per wave (12 KB of keys at 4 KB per block) keep enough
+        // bytes outstanding per CU at two waves per SIMD.
+        // Short launches (page keys of Hierarchical Indexing, small batches) need many
+        // workgroups more than long waves: two blocks per wave there.
+        constexpr int WAVES = 4, BPW = 32, BPW_SHORT = 2;
+        constexpr int PD = KeyBlock<FP8, D>::BB <= 4096 ? 3 : 1;
         const int64_t n_blocks = (a.n_out + 31) / 32;
-        dim3 grid((unsigned)((n_blocks + WAVES * BPW - 1) / (WAVES * BPW)),
-                  (unsigned)((a.n_q + G::NQW - 1) / G::NQW), (unsigned)a.batch);
-        hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, false, false, WAVES, BPW>), grid,
-                           dim3(WAVES * kWave), 0, st, a);
+        const int64_t rows = (a.n_q + G::NQW - 1) / G::NQW;
+        if (n_blocks * rows * a.batch >= (int64_t)512 * WAVES * BPW) {
+            dim3 grid((unsigned)((n_blocks + WAVES * BPW - 1) / (WAVES * BPW)), (unsigned)rows,
+                      (unsigned)a.batch);
+            hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, false, false, WAVES, BPW, PD>),
+                               grid, dim3(WAVES * kWave), 0, st, a);
+        } else {
+            dim3 grid((unsigned)((n_blocks + WAVES * BPW_SHORT - 1) / (WAVES * BPW_SHORT)),
+                      (unsigned)rows, (unsigned)a.batch);
+            hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, false, false, WAVES, BPW_SHORT, 1>),
+                               grid, dim3(WAVES * kWave), 0, st, a);
+        }
     } else {
         constexpr int WAVES = 8, KB = 64;
         constexpr int QPB = WAVES * G::NQW;
