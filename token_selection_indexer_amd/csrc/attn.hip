@@ -7,13 +7,16 @@
 // several consecutive layers.)
 //
 // Latent (MLA) kernel.  A workgroup of 4 waves owns one (sequence, query, group of 16 heads) and
-// a contiguous chunk of the index list.  Per round, 64 selected rows (d_qk bf16 each) are
-// gathered into LDS by gfx950's LDS-DMA loads (16 bytes per lane, no register staging) while
-// the previous round computes -- each row is one contiguous run in HBM, and the sink / window
-// runs are contiguous across rows -- then
-//   logits  S[16 x 64] = Q[16 x d_qk] . K^T   v_mfma_f32_16x16x32_bf16, one 16-row tile per wave
+// a contiguous chunk of the index list, in rounds of 32 selected rows (d_qk bf16 each).  While
+// round i is computed from LDS, every thread holds its share of round i+1's rows in registers
+// (16-byte loads; each row is one contiguous run in HBM, and the sink / window runs are
+// contiguous across rows) and writes them to the other LDS buffer afterwards.  The workgroup
+// uses under half a CU's LDS, so two of them share a CU and hide each other's latencies.
+//   logits  S[16 x 32] = Q[16 x d_qk] . K^T   v_mfma_f32_16x16x32_bf16; each wave takes one
+//                                              16-row tile over half of d_qk
 //   softmax online, fp32, base-2 exponent, per head over the rounds
-//   output  O[16 x d_v] += P[16 x 64] . V     v_mfma_f32_16x16x32_bf16, d_v/4 columns per wave
+//   output  O[16 x d_v] += P[16 x 32] . V     v_mfma_f32_16x16x32_bf16, d_v/4 columns per wave;
+//                                              V operands by transposing LDS reads
 // When the list is split over several workgroups, each writes (max, sum, unnormalised O) and a
 // combine kernel merges the splits in a fixed order (no atomics: identical inputs give
 // identical bits, which also makes reuse across layers reproducible).
@@ -29,14 +32,13 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-constexpr int AR = 64;          // rows per round
+constexpr int AR = 32;          // rows per round
+constexpr int NBUF = 2;         // row buffers: round i+1 streams in while round i is computed
 constexpr int MLA_MAX_DQK = 576;
 constexpr int MLA_MAX_DV = 512;
 
 __device__ __forceinline__ bool row_ok(int32_t id, int64_t kv_len) { return id >= 0 && id < kv_len; }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void glb_void_t;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -59,24 +61,45 @@ __device__ __forceinline__ uint2 ds_read_tr16(const uint8_t *lds_byte_ptr)
     return bitcast<uint2>(v);
 }
 
+// Workgroup barrier inside the latent kernel's round loop.  __syncthreads() carries a release
+// fence, which on this target waits for every vector-memory operation still outstanding --
+// including the next round's row loads, which are meant to stay in flight across the barrier.
+// Here only the LDS writes are completed (lgkmcnt(0)) before the barrier, which is all the
+// LDS hand-over between waves needs; the compiler-only fences keep memory accesses from being
+// moved across it.
+__device__ __forceinline__ void ring_barrier()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0); vmcnt and expcnt: no wait
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int DQK, int DV>
-__global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
+__global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
 {
     constexpr int ROWB = DQK * 2;          // LDS bytes per gathered row
     constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
     constexpr int KS = DQK / 32;           // K-steps of the logit product
+    constexpr int KH = KS / 2;             // K-steps per wave (two waves per 16-row tile)
     constexpr int NTW = DV / 4 / 16;       // 16-column output tiles per wave
-    constexpr int DMA_PER_WAVE = AR * CPR / 64 / 4;
-    static_assert(DQK % 32 == 0 && DV % 64 == 0 && CPR % 8 == 0, "shape");
-    static_assert((AR * CPR) % 256 == 0, "whole DMA instructions per wave");
+    constexpr int CPT = AR * CPR / 256;    // 16-byte chunks per thread per round
+    static_assert(KS % 2 == 0 && DV % 64 == 0 && CPR % 8 == 0 && AR == 32, "shape");
+    static_assert((AR * CPR) % 256 == 0, "whole chunks per thread");
 
-    // Two row buffers: round i is computed from buf[i&1] while round i+1 streams into the other
-    // one.  Chunk c of row r is stored at chunk slot swz(c, r) of the row.
-    __shared__ __attribute__((aligned(16))) uint8_t buf[2][AR * ROWB];
-    __shared__ float S[16][AR + 1];
+    // Two distinct row buffers (not one indexed array, so every access names its buffer at
+    // compile time).  LDS stays under half a CU's 160 KB: two workgroups share a CU, and one
+    // computes while the other's rows stream in.  Chunk c of row r sits at chunk slot swz(c, r).
+    __shared__ __attribute__((aligned(16))) uint8_t buf0[AR * ROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t buf1[AR * ROWB];
+    __shared__ float S2[2][16][AR + 1];    // logit halves (two K halves)
     __shared__ __attribute__((aligned(16))) uint16_t Pm[16][AR + 8];
-    __shared__ int32_t rid[2][AR];
+    __shared__ int32_t rid[NBUF][AR];      // row ids of the rounds in the buffers, -1 = skip
     __shared__ float m_run[16], l_run[16], alpha[16];
+    auto slot_buf = [&](auto SLOT) -> uint8_t * {
+        if constexpr (decltype(SLOT)::value == 0) return buf0;
+        else return buf1;
+    };
 
     const int HG = a.heads / 16;
     const int b = blockIdx.z;
@@ -91,12 +114,30 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
     const int c_end = min(a.n_idx, c_begin + chunk);
     const int n_rounds = c_end > c_begin ? (c_end - c_begin + AR - 1) / AR : 0;
 
-    // Q fragments: lane l holds head 16*hg + l%16, d = 32*kk + 8*(l/16) + [0,8)
-    bf16x8_t qf[KS];
+    const int32_t *idx_row = a.idx + qrow * a.n_idx;
+    // Row id (threadIdx.x % AR) of a round: an unconditional load of a clamped, always valid
+    // entry (a conditional load would make the compiler wait for it at once), masked at use.
+    auto id_load = [&](int round) -> int32_t {
+        const int j = c_begin + round * AR + (int)(threadIdx.x % AR);
+        return idx_row[min(j, c_end - 1)];
+    };
+    auto id_mask = [&](int round, int32_t raw) -> int32_t {
+        const int j = c_begin + round * AR + (int)(threadIdx.x % AR);
+        return (round < n_rounds && j < c_end && row_ok(raw, a.kv_len)) ? raw : -1;
+    };
+    auto id_of = [&](int round) -> int32_t { return id_mask(round, id_load(round)); };
+    if (threadIdx.x < AR) {
+        rid[0][threadIdx.x] = n_rounds > 0 ? id_of(0) : -1;
+        rid[1][threadIdx.x] = n_rounds > 1 ? id_of(1) : -1;
+    }
+    // Q fragments: wave w computes row tile (w & 1) over K-half (w >> 1); lane l holds head
+    // 16*hg + l%16, d = 32*(KH*(w>>1) + kk) + 8*(l/16) + [0,8)
+    const int tile = w & 1, kh = w >> 1;
+    bf16x8_t qf[KH];
     {
-        const uint16_t *qp = a.q + (qrow * a.heads + 16 * hg + (l & 15)) * DQK + 8 * (l >> 4);
+        const uint16_t *qp = a.q + (qrow * a.heads + 16 * hg + (l & 15)) * DQK + 8 * (l >> 4) + 32 * KH * kh;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) qf[kk] = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(qp + 32 * kk));
+        for (int kk = 0; kk < KH; ++kk) qf[kk] = bitcast<bf16x8_t>(ld16(qp + 32 * kk));
     }
     if (threadIdx.x < 16) {
         m_run[threadIdx.x] = -INFINITY;
@@ -105,69 +146,77 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
     f32x4_t oacc[NTW];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) oacc[nt] = f32x4_t{};
-
-    const int32_t *idx_row = a.idx + qrow * a.n_idx;
     const uint8_t *kv_b = reinterpret_cast<const uint8_t *>(a.k) + (int64_t)b * a.kv_len * a.k_stride * 2;
     const float sl2 = a.scale * kLog2e;
+    __syncthreads();
 
-    auto load_ids = [&](int round, int slot) {
-        if (threadIdx.x < AR) {
-            const int j = c_begin + round * AR + threadIdx.x;
-            const int32_t id = j < c_end ? idx_row[j] : -1;
-            rid[slot][threadIdx.x] = row_ok(id, a.kv_len) ? id : -1;
+    // A round's rows through registers: thread t loads the 16-byte chunks f = 256*j + t of the
+    // round (row f / CPR, chunk f % CPR; consecutive threads read consecutive chunks of a row)
+    // while the previous round is computed, and stores them after it.  Skipped rows read row 0
+    // instead (always valid); their logits are masked, so they never contribute.
+    uint4 stage[CPT];
+    auto load_round = [&](const int32_t *ids) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int f = j * 256 + (int)threadIdx.x;
+            const int r = f / CPR, c = f % CPR;
+            const int32_t id = ids[r];
+            stage[j] = ld16(kv_b + (int64_t)(id < 0 ? 0 : id) * a.k_stride * 2 + c * 16);
         }
     };
-    // Rows of a round into buf[slot], straight from HBM into LDS (no registers): each lane of
-    // DMA instruction j writes the 16 bytes at LDS offset 1024*j + 16*lane.  Skipped rows fetch
-    // row 0 instead (always valid); their logits are masked, so they never contribute.
-    auto issue_rows = [&](int slot) {
+    auto store_round = [&](uint8_t *dst) {
 #pragma unroll
-        for (int j = 0; j < DMA_PER_WAVE; ++j) {
-            const int f = (w * DMA_PER_WAVE + j) * kWave + l; // flat chunk slot
-            const int r = f / CPR, cs = f % CPR;
-            const int gc = swz(cs, r); // swz is an involution within each group of 8 chunks
-            const int32_t id = rid[slot][r];
-            const uint8_t *src = kv_b + (int64_t)(id < 0 ? 0 : id) * a.k_stride * 2 + gc * 16;
-            __builtin_amdgcn_global_load_lds((glb_void_t *)src,
-                                             (lds_void_t *)&buf[slot][(w * DMA_PER_WAVE + j) * 1024],
-                                             16, 0, 0);
+        for (int j = 0; j < CPT; ++j) {
+            const int f = j * 256 + (int)threadIdx.x;
+            const int r = f / CPR, c = f % CPR;
+            *reinterpret_cast<uint4 *>(dst + r * ROWB + swz(c, r) * 16) = stage[j];
         }
     };
 
     if (n_rounds > 0) {
-        load_ids(0, 0);
-        __syncthreads();
-        issue_rows(0);
-        if (n_rounds > 1) load_ids(1, 1);
+        load_round(rid[0]);
+        store_round(buf0);
     }
-    for (int i = 0; i < n_rounds; ++i) {
-        const int cur = i & 1;
-        __builtin_amdgcn_s_waitcnt(0); // this wave's row loads of round i have landed
-        __syncthreads();                // ... and every other wave's; rid of round i+1 visible
-        if (i + 1 < n_rounds) issue_rows(cur ^ 1);
-        // logits: wave w takes rows 16w .. 16w+15
+    // Q, the ids and round 0 are in: the loop starts with nothing outstanding, so the waits the
+    // compiler places inside it count only the loads the loop itself issues
+    __builtin_amdgcn_s_waitcnt(0);
+    // rounds in pairs: the ring slot is a compile-time constant in each copy of the body
+    for (int i0 = 0; i0 < n_rounds; i0 += NBUF) static_for<0, NBUF>([&](auto SLOT) {
+        constexpr int S = decltype(SLOT)::value;
+        constexpr int O = S ^ 1; // the other slot
+        const int i = i0 + S;
+        if (i >= n_rounds) return;
+        ring_barrier(); // round i is in buf[S]; round i-1 is fully consumed
+        // the rows of round i+1 (into registers) and the ids of round i+2 are loaded while
+        // round i is computed.  Unconditionally: after the last round rid[O] is all -1, so the
+        // surplus loads read row 0 into a buffer no one reads (a conditional load would make
+        // the compiler wait for every load at the merge that follows it).
+        const int32_t next_raw = id_load(i + 2); // first: waiting for it then waits for no row
+        load_round(rid[O]);
+        const uint8_t *cb = slot_buf(SLOT);
+        // logits, half of d per wave: S2[kh][h][r] for rows 16*tile .. 16*tile + 15
         {
             f32x4_t acc = f32x4_t{};
-            const int r = 16 * w + (l & 15);
-            const uint8_t *kr = &buf[cur][r * ROWB];
+            const int r = 16 * tile + (l & 15);
+            const uint8_t *kr = cb + r * ROWB;
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const int c = 4 * kk + (l >> 4);
-                const bf16x8_t bk = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(kr + 16 * swz(c, r)));
-                acc = mfma_16x16x32(qf[kk], bk, acc);
+            for (int kk = 0; kk < KH; ++kk) {
+                const int c = 4 * (KH * kh + kk) + (l >> 4);
+                acc = mfma_16x16x32(qf[kk], bitcast<bf16x8_t>(ld16(kr + 16 * swz(c, r))), acc);
             }
-            const bool ok = rid[cur][r] >= 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S[4 * (l >> 4) + e][r] = ok ? acc[e] * sl2 : -INFINITY;
+            for (int e = 0; e < 4; ++e) S2[kh][4 * (l >> 4) + e][r] = acc[e];
         }
-        __syncthreads();
-        // online softmax: 16 threads per head, 4 rows each
+        ring_barrier();
+        // online softmax: 16 threads per head, 2 rows each
         {
             const int h = threadIdx.x >> 4, part = threadIdx.x & 15;
-            float sv[4], mx = -INFINITY;
+            float sv[2], mx = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sv[e] = S[h][4 * part + e];
+            for (int e = 0; e < 2; ++e) {
+                const int r = 2 * part + e;
+                const float x = (S2[0][h][r] + S2[1][h][r]) * sl2;
+                sv[e] = rid[S][r] >= 0 ? x : -INFINITY;
                 mx = fmaxf(mx, sv[e]);
             }
 #pragma unroll
@@ -175,56 +224,54 @@ __global__ __launch_bounds__(256) void mla_attn_kernel(AttnArgs a)
             const float m_old = m_run[h];
             const float m_new = fmaxf(m_old, mx);
             float sum = 0.0f;
+            uint32_t pb[2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < 2; ++e) {
                 const float p = (m_new == -INFINITY || sv[e] == -INFINITY) ? 0.0f : exp2f(sv[e] - m_new);
-                const uint32_t bits = f32_to_bf16_bits(p);
-                sum += bf16_bits_to_f32(bits); // normalise by what the product actually uses
-                Pm[h][4 * part + e] = (uint16_t)bits;
+                pb[e] = f32_to_bf16_bits(p);
+                sum += bf16_bits_to_f32(pb[e]); // normalise by what the product actually uses
             }
+            *reinterpret_cast<uint32_t *>(&Pm[h][2 * part]) = pb[0] | (pb[1] << 16);
 #pragma unroll
             for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
-            __syncthreads(); // every reader of m_run has it before it changes
+            ring_barrier(); // every reader of m_run and of rid[S] is done
             if (part == 0) {
                 const float al = (m_old == -INFINITY) ? 0.0f : exp2f(m_old - m_new);
                 alpha[h] = al;
                 l_run[h] = l_run[h] * al + sum;
                 m_run[h] = m_new;
             }
+            if (threadIdx.x < AR) rid[S][threadIdx.x] = id_mask(i + 2, next_raw);
         }
-        __syncthreads();
-        // O = O * alpha + P . V ; wave w owns columns [w*DV/4, (w+1)*DV/4).  K = the 64 rows:
-        // lane group q = l/16 takes rows 32kk + 8q + [0,8) as two transposing reads of 4 rows.
+        ring_barrier();
+        // O = O * alpha + P . V ; wave w owns columns [w*DV/4, (w+1)*DV/4).  K = the 32 rows:
+        // lane group q = l/16 takes rows 8q + [0,8) as two transposing reads of 4 rows.
         {
-            float al[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) al[e] = alpha[4 * (l >> 4) + e];
+            for (int e = 0; e < 4; ++e) {
+                const float al = alpha[4 * (l >> 4) + e];
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
+                for (int nt = 0; nt < NTW; ++nt) oacc[nt][e] *= al;
+            }
+            const int q = l >> 4, j = l & 15;   // lane group, lane within group
+            const int re = j >> 2, c4 = j & 3;  // source lane role: row e, 4-column segment
+            const bf16x8_t pf = bitcast<bf16x8_t>(ld16(reinterpret_cast<const uint8_t *>(&Pm[l & 15][8 * q])));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) oacc[nt][e] *= al[e];
-            const int q = l >> 4, j = l & 15;       // lane group, lane within group
-            const int re = j >> 2, c4 = j & 3;      // source lane role: row e, 4-column segment
+            for (int nt = 0; nt < NTW; ++nt) {
+                const int col = w * (DV / 4) + 16 * nt + 4 * c4; // this lane's source segment
+                uint2 half[2];
 #pragma unroll
-            for (int kk = 0; kk < AR / 32; ++kk) {
-                const bf16x8_t pf = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(&Pm[l & 15][32 * kk + 8 * q]));
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
-                    const int col = w * (DV / 4) + 16 * nt + 4 * c4; // this lane's source segment
-                    uint2 half[2];
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int r = 32 * kk + 8 * q + 4 * hh + re;
-                        half[hh] = ds_read_tr16(&buf[cur][r * ROWB + swz(col >> 3, r) * 16 + (col & 7) * 2]);
-                    }
-                    const bf16x8_t vf = bitcast<bf16x8_t>(make_uint4(half[0].x, half[0].y, half[1].x, half[1].y));
-                    oacc[nt] = mfma_16x16x32(pf, vf, oacc[nt]);
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int r = 8 * q + 4 * hh + re;
+                    half[hh] = ds_read_tr16(cb + r * ROWB + swz(col >> 3, r) * 16 + (col & 7) * 2);
                 }
+                const bf16x8_t vf = bitcast<bf16x8_t>(make_uint4(half[0].x, half[0].y, half[1].x, half[1].y));
+                oacc[nt] = mfma_16x16x32(pf, vf, oacc[nt]);
             }
         }
-        if (i + 2 < n_rounds) load_ids(i + 2, cur); // rid[cur] is no longer read this round
-        __syncthreads();
-    }
+        store_round(slot_buf(std::integral_constant<int, O>{}));
+    });
+    __syncthreads(); // m_run / l_run final
 
     // epilogue: lane holds O[head 4*(l/16)+e][col w*DV/4 + 16*nt + l%16]
     if (a.n_split == 1) {
@@ -401,7 +448,7 @@ int attn_splits(int batch, int n_q, int heads, int n_idx, int latent)
     if (!latent) return 1;
     const int64_t units = (int64_t)batch * n_q * (heads / 16);
     const int max_split = (n_idx + AR - 1) / AR;
-    int64_t want = (256 + units - 1) / units;
+    int64_t want = (512 + units - 1) / units; // two workgroups per CU
     if (want > max_split) want = max_split;
     if (want > MAX_SPLIT) want = MAX_SPLIT;
     return want < 1 ? 1 : (int)want;
