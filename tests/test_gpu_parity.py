@@ -180,7 +180,23 @@ def test_select_decode_128k_full_exact():
         assert np.array_equal(idx[r], expect), r
 
 
-@pytest.mark.parametrize("ties", ["none", "zeros", "coarse", "const"])
+@pytest.mark.parametrize("ties", ["none", "zeros", "coarse", "const", "ramp"])
+def test_select_sampled_rows_exact(ties):
+    """Rows longer than the LDS buffer on the one-workgroup path: the sampled threshold and its
+    fallbacks (heavy ties: too many elements reach the threshold; "ramp": every pick in the last
+    wave's segment, whose list overflows, so an ordered pass collects them)."""
+    B, T, L = 3, 4, 20000
+    k, S, W = 2048, 64, 960
+    sc = inputs.synthetic_scores(B * T, L, seed=13, ties=ties, device=DEV).reshape(B, T, L)
+    for pos0 in (L - T, 9000):
+        idx = lsa.topk_select(sc, k, S, W, kv_len=L, q_pos0=pos0).cpu().numpy()
+        V = ref.valid_lengths(L, pos0, T)
+        for b in range(B):
+            expect = ref.select(sc[b].cpu().numpy(), V, k, S, W)
+            assert np.array_equal(idx[b], expect), (ties, pos0, b)
+
+
+@pytest.mark.parametrize("ties", ["none", "zeros", "coarse", "const", "ramp"])
 def test_select_chunked_rows_exact(ties):
     """Few long rows (the chunked path), every tie pattern: heavy ties overflow the per-chunk
     slices and fall back to one workgroup per row; rows with V <= k take everything."""

@@ -11,8 +11,16 @@
 // so they come out ascending without a sort.  Sink [0,S) and window [V-W,V) are written
 // arithmetically, never scored or compared.
 //
+// A sampled threshold makes the common case one pass over long rows: 64-element blocks spread
+// over the row give T (from the sampled key of a rank that puts about twice the needed count of
+// the row at or above T); every element >= T is compacted (in position order) into LDS, and the
+// exact selection runs there -- the buffer then holds every element that can be picked, ties at
+// the boundary included.  When fewer than the needed count, or more than the buffer holds, reach
+// T, the exact histogram path below runs instead, so T affects speed only.
+//
 // Two paths:
 //  * one workgroup per row (many rows: prefill, page recall):
+//      rows of 32K and more: the sampled threshold as above; otherwise, or if it fails,
 //      1. histogram of key bits 31..21 (2048 bins in LDS) over the row;
 //      2. the bin b* holding the k-th key; bins above are taken outright;
 //      3. if bins >= b* fit in LDS, one ordered pass compacts them there and bits 20..10, 9..0
@@ -20,13 +28,11 @@
 //      4. keys > T, then the first (k - #greater) keys == T, in position order.
 //  * chunked (few long rows: decode): the row is cut into 4096-element chunks, one workgroup
 //    each, so a handful of rows still fills the chip:
-//      zero      clear the per-row histograms
-//      hist      per-chunk LDS histogram, nonzero bins added to the row's global histogram
-//      collect   every chunk finds b* from the row histogram and compacts its elements with
-//                bin >= b* (in order) into its own slice of the workspace
+//      collect   every chunk derives the row's sampled threshold (the same in every chunk) and
+//                compacts its elements >= T (in order) into its own slice of the workspace
 //      finish    one workgroup per row concatenates the slices (chunk order = position order)
-//                into LDS and finishes as in step 3-4; a row whose slices overflowed falls back
-//                to the one-workgroup path over the row.
+//                into LDS and selects exactly there; a row whose slices overflowed, or hold
+//                fewer than the needed count, falls back to the one-workgroup path over the row.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -38,6 +44,7 @@ constexpr int CAP = 8192;           // LDS candidate buffer entries (key, id)
 constexpr int CHUNK = 4096;         // chunked path: elements per workgroup
 constexpr int CHUNK_CAP = 512;      // chunked path: candidates kept per chunk
 constexpr int CNT_THREADS = 256;    // chunked path: threads per chunk workgroup
+constexpr int64_t SAMPLE_MIN = 32768; // one-workgroup rows at least this long use the sample
 
 // ------------------------------------------------------------------------------------------
 // Row access
@@ -140,16 +147,19 @@ struct Digit {
 template <int NT>
 __device__ Digit find_digit(const int *hist, int nbins, int need, int *scratch)
 {
-    // thread i owns bins [nbins - (i+1)*per, nbins - i*per), scanned top-down
-    const int per = nbins / NT;
+    // thread i owns bins [nbins - (i+1)*per, nbins - i*per), scanned top-down (with fewer bins
+    // than threads, threads past the last bin own none)
+    const int per = nbins >= NT ? nbins / NT : 1;
+    const bool owner = (int)threadIdx.x * per < nbins;
     const int top = nbins - 1 - per * (int)threadIdx.x;
     int mine = 0;
-    for (int j = 0; j < per; ++j) mine += hist[top - j];
+    if (owner)
+        for (int j = 0; j < per; ++j) mine += hist[top - j];
     int tot;
     const int ex = block_exclusive_scan<NT / kWave>(mine, scratch, &tot);
     if (threadIdx.x == 0) scratch[NT / kWave + 1] = -1;
     __syncthreads();
-    if (ex < need && ex + mine >= need) {
+    if (owner && ex < need && ex + mine >= need) {
         int cum = ex;
         for (int j = 0; j < per; ++j) {
             const int c = hist[top - j];
@@ -170,6 +180,54 @@ __device__ Digit find_digit(const int *hist, int nbins, int need, int *scratch)
     r.total = tot;
     __syncthreads();
     return r;
+}
+
+// Threshold from a sample of the row.  NTH/64 * KPT blocks of 64 consecutive positions, evenly
+// spread over [lo, hi) (len = hi - lo > 64 * blocks), are read; T is the lower edge of the
+// 22-bit key prefix holding the rr-th largest sampled key, rr = 2 * need * (sampled / len) + 8,
+// so about twice `need` elements of the row are expected at or above T.  Returns 0 when the
+// sample has fewer than rr competing keys.  The caller checks what it collects against T (at
+// least `need`, within capacity) and falls back to the exact histogram path otherwise, so T
+// only ever affects speed, never the result.  Every workgroup computing T for the same row
+// gets the same T.  `hist` holds NBIN ints.
+template <int NTH, int KPT>
+__device__ uint32_t sample_threshold(int *hist, int *scratch, const Row &r, int need, int64_t len)
+{
+    constexpr int NWV = NTH / kWave;
+    constexpr int NSB = NWV * KPT; // sample blocks
+    const int l = lane_id(), wv = wave_id();
+    uint32_t key[KPT];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int sb = j * NWV + wv;
+        const int64_t start = r.lo + (len - kWave) * sb / (NSB - 1);
+        int32_t id;
+        key[j] = elem(r, start + l, id);
+        cnt += key[j] != 0u;
+    }
+    int m;
+    block_exclusive_scan<NWV>(cnt, scratch, &m);
+    const int64_t ns = (int64_t)NSB * kWave;
+    const int64_t want = (2 * (int64_t)need * ns + len - 1) / len + 8;
+    if (want > m) return 0u;
+    int rem = (int)want;
+    uint32_t prefix = 0u;
+    // two 11-bit digits (key bits 31..21, then 20..10)
+    for (int lvl = 0; lvl < 2; ++lvl) {
+        const int shift = 21 - 11 * lvl;
+        for (int i = threadIdx.x; i < NBIN; i += NTH) hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if (key[j] && (lvl == 0 || (key[j] >> 21) == prefix))
+                atomicAdd(&hist[(key[j] >> shift) & (NBIN - 1)], 1);
+        __syncthreads();
+        const Digit g = find_digit<NTH>(hist, NBIN, rem, scratch);
+        prefix = (prefix << 11) | (uint32_t)g.d;
+        rem -= g.above;
+    }
+    return prefix << 10;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -216,13 +274,14 @@ __device__ void hist_row(Smem &sm, const Row &r, int shift, int nbins, int pbits
     __syncthreads();
 }
 
-__device__ void hist_buf(Smem &sm, int nbuf, int shift, int nbins, uint32_t prefix)
+// pbits == 0: every buffered key counts (the level-0 digit).
+__device__ void hist_buf(Smem &sm, int nbuf, int shift, int nbins, uint32_t prefix, int pbits = 1)
 {
     clear_hist(sm);
     const int hs = shift + __builtin_ctz((unsigned)nbins);
     for (int i = threadIdx.x; i < nbuf; i += NT) {
         const uint32_t key = sm.buf_key[i];
-        if ((key >> hs) != prefix) continue;
+        if (pbits && (key >> hs) != prefix) continue;
         atomicAdd(&sm.hist[(key >> shift) & (uint32_t)(nbins - 1)], 1);
     }
     __syncthreads();
@@ -265,7 +324,7 @@ __device__ int select_row(Smem &sm, const Row &r, uint32_t T, int eq_take, int32
         taken += tot;
         eq_seen += eq_tot;
     }
-    return taken < limit ? taken : limit;
+    return taken; // may exceed limit: only the first `limit` were written
 }
 
 // The same over the LDS buffer (already in position order).
@@ -316,6 +375,20 @@ __device__ void finish_in_buf(Smem &sm, int nbuf, uint32_t prefix, int need_rem,
     select_buf(sm, nbuf, prefix, need_rem, dst, need);
 }
 
+// The buffer holds, in position order, a set of elements that contains the row's `need` best.
+// Emit exactly those (all of them, padded with -1, if there are at most `need`).
+__device__ void select_in_buf(Smem &sm, int nbuf, int need, int32_t *dst)
+{
+    if (nbuf <= need) {
+        const int got = select_buf(sm, nbuf, 0u, 0, dst, need);
+        for (int i = got + (int)threadIdx.x; i < need; i += NT) dst[i] = -1;
+        return;
+    }
+    hist_buf(sm, nbuf, 21, NBIN, 0u, 0);
+    const Digit g = find_digit<NT>(sm.hist, NBIN, need, sm.scratch);
+    finish_in_buf(sm, nbuf, (uint32_t)g.d, need - g.above, dst, need);
+}
+
 // ---- streaming passes: each wave owns a contiguous segment of the row (no block barriers) ----
 
 constexpr int WCAP = CAP / NW; // candidate list entries per wave
@@ -355,7 +428,7 @@ __device__ void hist_row_seg(Smem &sm, const Row &r)
 // Every element with key >= lowest, into the LDS buffer in position order.  Each wave appends
 // its segment's elements to its own list (order kept by a wave prefix sum), then the lists are
 // concatenated in wave order.  Returns false if a wave's list overflowed (caller falls back).
-__device__ bool collect_row_seg(Smem &sm, const Row &r, uint32_t lowest, int &nbuf)
+__device__ bool collect_row_seg(Smem &sm, const Row &r, uint32_t lowest, int &nbuf, int &total_out)
 {
     const int w = wave_id(), lane = lane_id();
     const Seg sg = wave_segment(r);
@@ -364,7 +437,6 @@ __device__ bool collect_row_seg(Smem &sm, const Row &r, uint32_t lowest, int &nb
     // The trip count is uniform over the wave (the scan below needs every lane): segments are
     // whole multiples of 4*64 elements, so p never reaches the next wave's segment, and
     // positions at or past hi read as "does not compete".
-#pragma unroll 4
     for (int64_t p0 = sg.b0; p0 < sg.b1; p0 += 4 * kWave) {
         const int64_t p = p0 + 4 * lane;
         uint32_t key[4];
@@ -397,6 +469,7 @@ __device__ bool collect_row_seg(Smem &sm, const Row &r, uint32_t lowest, int &nb
         total += c;
         over |= c > WCAP;
     }
+    total_out = total;
     if (over || total > CAP) {
         __syncthreads();
         return false;
@@ -429,10 +502,27 @@ __device__ bool collect_row_seg(Smem &sm, const Row &r, uint32_t lowest, int &nb
 __device__ void select_top(Smem &sm, const Row &r, int need, int32_t *dst)
 {
     if (need <= 0) return;
+    const int64_t len = r.hi - r.lo;
+    // long rows: a sampled threshold lets one pass collect everything at or above it
+    const uint32_t T = len >= SAMPLE_MIN ? sample_threshold<NT, 4>(sm.hist, sm.scratch, r, need, len) : 0u;
+    if (T != 0u) {
+        int nbuf = 0, total = 0;
+        bool ok = collect_row_seg(sm, r, T, nbuf, total);
+        if (!ok && total <= CAP) { // a wave's list overflowed, the buffer would not: ordered pass
+            nbuf = select_row(sm, r, T, INT32_MAX, nullptr, true, CAP);
+            __syncthreads();
+            ok = true;
+        }
+        if (ok && nbuf >= need) {
+            select_in_buf(sm, nbuf, need, dst);
+            return;
+        }
+    }
+    // exact histogram path
     hist_row_seg(sm, r);
     Digit g = find_digit<NT>(sm.hist, NBIN, need, sm.scratch);
     if (g.total <= need) { // everything competes: take all, pad
-        const int got = select_row(sm, r, 0u, 0, dst, false, need);
+        const int got = min(select_row(sm, r, 0u, 0, dst, false, need), need);
         for (int i = got + (int)threadIdx.x; i < need; i += NT) dst[i] = -1;
         return;
     }
@@ -441,8 +531,8 @@ __device__ void select_top(Smem &sm, const Row &r, int need, int32_t *dst)
     int need_rem = need - g.above;
     int taken_above = g.above, at = g.at;
     if (taken_above + at <= CAP) {
-        int nbuf;
-        if (!collect_row_seg(sm, r, prefix << 21, nbuf)) { // uneven segments: one ordered pass
+        int nbuf, total;
+        if (!collect_row_seg(sm, r, prefix << 21, nbuf, total)) { // uneven segments: ordered pass
             nbuf = select_row(sm, r, prefix << 21, INT32_MAX, nullptr, true, CAP);
             __syncthreads();
         }
@@ -527,48 +617,14 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
 // ------------------------------------------------------------------------------------------
 
 struct ChunkWs {
-    int *hist;       // [rows][NBIN]
-    int *info;       // [rows][4]: d0, above0, total, take_all
-    int *count;      // [rows][n_chunks]  (CHUNK_CAP + 1 = overflow)
+    int *count;      // [rows][n_chunks]  (CHUNK_CAP + 1 = overflow or no threshold)
     uint32_t *ckey;  // [rows][n_chunks][CHUNK_CAP]
     int32_t *cid;    // [rows][n_chunks][CHUNK_CAP]
     int n_chunks;
 };
 
-__global__ __launch_bounds__(256) void chunk_zero_kernel(int *hist, int64_t n)
-{
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) hist[i] = 0;
-}
-
-__global__ __launch_bounds__(CNT_THREADS) void chunk_hist_kernel(SelectArgs a, ChunkWs ws)
-{
-    __shared__ int hist[NBIN];
-    const int64_t row = blockIdx.y;
-    Row r;
-    int32_t *dst;
-    int need;
-    if (!setup_row(a, row, r, dst, need, false)) return;
-    const int64_t c0 = (int64_t)blockIdx.x * CHUNK;
-    if (c0 + CHUNK <= r.lo || c0 >= r.hi) return;
-    for (int i = threadIdx.x; i < NBIN; i += CNT_THREADS) hist[i] = 0;
-    __syncthreads();
-    constexpr int CI = CHUNK / CNT_THREADS;
-    uint32_t key[CI];
-#pragma unroll
-    for (int j = 0; j < CI; ++j) {
-        int32_t id;
-        key[j] = elem(r, c0 + (int64_t)j * CNT_THREADS + threadIdx.x, id);
-    }
-#pragma unroll
-    for (int j = 0; j < CI; ++j)
-        if (key[j]) atomicAdd(&hist[key[j] >> 21], 1);
-    __syncthreads();
-    int *g = ws.hist + row * NBIN;
-    for (int i = threadIdx.x; i < NBIN; i += CNT_THREADS)
-        if (hist[i]) atomicAdd(&g[i], hist[i]);
-}
-
+// Every chunk of a row derives the row's sampled threshold T (the same T in every workgroup)
+// and compacts its elements with key >= T, in position order, into its slice of the workspace.
 __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a, ChunkWs ws)
 {
     constexpr int CI = CHUNK / CNT_THREADS; // items per thread
@@ -581,21 +637,16 @@ __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a
     int32_t *dst;
     int need;
     if (!setup_row(a, row, r, dst, need, false)) return;
-    const int *g = ws.hist + row * NBIN;
-    for (int i = threadIdx.x; i < NBIN; i += CNT_THREADS) hist[i] = g[i];
-    __syncthreads();
-    Digit d = find_digit<CNT_THREADS>(hist, NBIN, need, scratch);
-    const bool take_all = d.total <= need;
-    const uint32_t lowest = take_all ? 1u : ((uint32_t)d.d << 21);
-    if (chunk == 0 && threadIdx.x == 0) {
-        int *info = ws.info + row * 4;
-        info[0] = take_all ? 0 : d.d;
-        info[1] = take_all ? 0 : d.above;
-        info[2] = d.total;
-        info[3] = take_all ? 1 : 0;
+    int *cntp = ws.count + row * ws.n_chunks + chunk;
+    // 1024 samples up to 256K positions, 4096 beyond (the expected sampled rank stays >= 16)
+    const int64_t len = r.hi - r.lo;
+    const uint32_t T = len <= (int64_t)1 << 18 ? sample_threshold<CNT_THREADS, 4>(hist, scratch, r, need, len)
+                                               : sample_threshold<CNT_THREADS, 16>(hist, scratch, r, need, len);
+    if (T == 0u) { // no usable threshold: the finish kernel falls back to the exact path
+        if (threadIdx.x == 0) *cntp = CHUNK_CAP + 1;
+        return;
     }
     const int64_t c0 = (int64_t)chunk * CHUNK;
-    int *cntp = ws.count + row * ws.n_chunks + chunk;
     if (c0 + CHUNK <= r.lo || c0 >= r.hi) {
         if (threadIdx.x == 0) *cntp = 0;
         return;
@@ -610,7 +661,7 @@ __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a
 #pragma unroll
     for (int j = 0; j < CI; ++j) {
         key[j] = elem(r, c0 + (int64_t)j * CNT_THREADS + threadIdx.x, id[j]);
-        take[j] = key[j] >= lowest;
+        take[j] = key[j] >= T;
     }
     int taken;
     ordered_slots<CNT_THREADS, CI>(take, slot, cnt, taken);
@@ -632,8 +683,6 @@ __global__ __launch_bounds__(NT) void chunk_finish_kernel(SelectArgs a, ChunkWs 
     int32_t *dst;
     int need;
     if (!setup_row(a, row, r, dst, need, true)) return;
-    const int *info = ws.info + row * 4;
-    const int d0 = info[0], above0 = info[1], take_all = info[3];
     // slice offsets (exclusive scan of the counts) into sm.hist, which is free until the end
     const int *counts = ws.count + row * ws.n_chunks;
     int overflow = 0, total = 0;
@@ -662,16 +711,12 @@ __global__ __launch_bounds__(NT) void chunk_finish_kernel(SelectArgs a, ChunkWs 
         }
     }
     overflow = __syncthreads_or(overflow);
-    if (overflow || total > CAP) { // fall back to the one-workgroup path over the row
+    // the slices hold every element >= T of the row; enough of them contain the `need` best
+    if (overflow || total > CAP || total < need) { // fall back to the one-workgroup path
         select_top(sm, r, need, dst);
         return;
     }
-    if (take_all) {
-        const int got = select_buf(sm, total, 0u, 0, dst, need);
-        for (int i = got + (int)threadIdx.x; i < need; i += NT) dst[i] = -1;
-        return;
-    }
-    finish_in_buf(sm, total, (uint32_t)d0, need - above0, dst, need);
+    select_in_buf(sm, total, need, dst);
 }
 
 bool use_chunked(const SelectArgs &a)
@@ -693,8 +738,7 @@ size_t select_workspace_bytes(int64_t rows, int64_t n_in, int mode)
     if (!use_chunked(a)) return 0;
     const int64_t nc = (n_in + CHUNK - 1) / CHUNK;
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
-    return r256(rows * NBIN * 4) + r256(rows * 4 * 4) + r256(rows * nc * 4) +
-           2 * r256(rows * nc * CHUNK_CAP * 4);
+    return r256(rows * nc * 4) + 2 * r256(rows * nc * CHUNK_CAP * 4);
 }
 
 hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream)
@@ -709,21 +753,12 @@ hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream)
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
     uint8_t *p = static_cast<uint8_t *>(ws);
     ChunkWs w;
-    w.hist = reinterpret_cast<int *>(p);
-    p += r256(rows * NBIN * 4);
-    w.info = reinterpret_cast<int *>(p);
-    p += r256(rows * 4 * 4);
     w.count = reinterpret_cast<int *>(p);
     p += r256(rows * nc * 4);
     w.ckey = reinterpret_cast<uint32_t *>(p);
     p += r256(rows * nc * CHUNK_CAP * 4);
     w.cid = reinterpret_cast<int32_t *>(p);
     w.n_chunks = (int)nc;
-    const int64_t nh = rows * NBIN;
-    hipLaunchKernelGGL(chunk_zero_kernel, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, stream,
-                       w.hist, nh);
-    hipLaunchKernelGGL(chunk_hist_kernel, dim3((unsigned)nc, (unsigned)rows), dim3(CNT_THREADS), 0,
-                       stream, a, w);
     hipLaunchKernelGGL(chunk_collect_kernel, dim3((unsigned)nc, (unsigned)rows), dim3(CNT_THREADS),
                        0, stream, a, w);
     hipLaunchKernelGGL(chunk_finish_kernel, dim3((unsigned)rows), dim3(NT), 0, stream, a, w);

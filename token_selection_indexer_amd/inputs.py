@@ -115,7 +115,8 @@ def attn_inputs(w: Workload, layer: int = 0, device="cpu") -> Dict[str, torch.Te
 def synthetic_scores(rows: int, n: int, seed: int, ties: str = "none", device="cpu"):
     """Score rows for selection tests.  ties: "none" (continuous N(0,1)), "zeros" (a third of the
     entries exactly +0 or -0), "coarse" (values on a grid of 17 levels: heavy exact ties),
-    "const" (every entry equal)."""
+    "const" (every entry equal), "ramp" (rising with position plus small noise: the best
+    entries all sit at the end of the row)."""
     x = _randn((rows, n), device, seed, "scores")
     if ties == "zeros":
         g = _gen(device, seed, "scores", 1)
@@ -126,6 +127,8 @@ def synthetic_scores(rows: int, n: int, seed: int, ties: str = "none", device="c
         x = torch.round(x * 4.0) / 4.0
     elif ties == "const":
         x = torch.full_like(x, 0.75)
+    elif ties == "ramp":
+        x = torch.linspace(-1.0, 1.0, n, device=device).unsqueeze(0) + 0.01 * x
     return x.contiguous()
 
 
