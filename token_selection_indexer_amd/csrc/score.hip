@@ -500,21 +500,24 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
         const int buf = (int)((kt - kt_begin) & 1);
         if (kt + 1 < kt_end) fetch(kt + 1);
         if (nq_avail > 0) {
+            // Software-pipelined over the tile's 32-key blocks: the MFMAs of block nt+1 are
+            // issued before the epilogue of block nt, so the epilogue's VALU work overlaps them.
+            f32x16_t acc[2][MT];
+            auto mma = [&](int nt, f32x16_t (&ac)[MT]) {
+                const uint8_t *src = &lds_k[buf][(nt * 32 + n) * ROWB + D * g];
 #pragma unroll
-            for (int nt = 0; nt < KB / 32; ++nt) {
-                const int key = nt * 32 + n;
-                const uint8_t *src = &lds_k[buf][key * ROWB + D * g];
-                f32x16_t acc[MT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16_t{};
+                for (int mt = 0; mt < MT; ++mt) ac[mt] = f32x16_t{};
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
                     const bf16x8_t bk = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(src + 16 * kk));
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_32x32x16(qf[mt][kk], bk, acc[mt]);
+                    for (int mt = 0; mt < MT; ++mt) ac[mt] = mfma_32x32x16(qf[mt][kk], bk, ac[mt]);
                 }
+            };
+            auto epi = [&](int nt, const f32x16_t (&ac)[MT]) {
+                const int key = nt * 32 + n;
                 float part[G::NQL];
-                epilogue<H, MT, false>(acc, [&](int v) { return wv[v]; }, part);
+                epilogue<H, MT, false>(ac, [&](int v) { return wv[v]; }, part);
                 const int64_t s = kt * KB + key;
                 if (FP8) {
                     const float sc = lds_s[buf][key];
@@ -530,7 +533,13 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
                         a.out[((int64_t)b * a.n_q + t0 + qs) * a.n_out + s] = ok ? part[u] : -INFINITY;
                     }
                 }
-            }
+            };
+            mma(0, acc[0]);
+            static_for<0, KB / 32>([&](auto NTI) {
+                constexpr int nt = decltype(NTI)::value;
+                if constexpr (nt + 1 < KB / 32) mma(nt + 1, acc[(nt + 1) & 1]);
+                epi(nt, acc[nt & 1]);
+            });
         }
         if (kt + 1 < kt_end) commit(buf ^ 1);
         __syncthreads();
@@ -573,7 +582,7 @@ hipError_t launch_flat(const ScoreArgs &a, hipStream_t st)
                                grid, dim3(WAVES * kWave), 0, st, a);
         }
     } else {
-        constexpr int WAVES = 8, KB = 64;
+        constexpr int WAVES = 8, KB = 128; // 128-key tiles: half the barriers of 64
         constexpr int QPB = WAVES * G::NQW;
         dim3 grid((unsigned)((a.n_q + QPB - 1) / QPB), (unsigned)a.batch);
         hipLaunchKernelGGL((score_tile_kernel<FP8, D, H, MT, WAVES, KB>), grid,
