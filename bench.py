@@ -301,9 +301,27 @@ def cpu_baseline(inputs, cfg, budget_s=15.0):
 
 
 def only_stage(torch, lsa, inputs, cfg, stage, steps):
-    """One stage of the headline decode step, `steps` times (counter runs).  `copy` is the
-    calibration kernel: out = src + 0 over 256 MiB of fp32 (reads and writes 256 MiB)."""
+    """One stage of the headline decode step (or of the chunked prefill), `steps` times, for
+    counter runs.  `copy` is the calibration kernel: out = src + 0 over 256 MiB of fp32 (reads
+    and writes 256 MiB)."""
     dev = "cuda"
+    if stage.startswith("prefill_"):
+        w = cfg.PREFILL_8K_AT_128K
+        s, b = w.index, w.budget
+        inp = inputs.index_inputs(w, dev)
+        scores = lsa.index_scores(inp["q"], inp["w"], inp["keys"], None, q_pos0=s.q_pos0)
+        ws = lsa.Workspace()
+        idx = lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=s.kv_len, q_pos0=s.q_pos0, ws=ws)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            if stage == "prefill_score":
+                lsa.index_scores(inp["q"], inp["w"], inp["keys"], None, q_pos0=s.q_pos0, out=scores)
+            else:
+                lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=s.kv_len, q_pos0=s.q_pos0,
+                                out=idx, ws=ws)
+        torch.cuda.synchronize()
+        log(f"[bench] {stage} x{steps} done")
+        return
     if stage == "copy":
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -342,7 +360,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--extras", action=argparse.BooleanOptionalAction, default=True)
     ap.add_argument("--cpu-baseline", action=argparse.BooleanOptionalAction, default=True)
-    ap.add_argument("--only", choices=["score", "topk", "attn", "copy"],
+    ap.add_argument("--only", choices=["score", "topk", "attn", "copy", "prefill_score", "prefill_topk"],
                     help="run one stage of the headline step (or a plain 256 MiB device copy) "
                          "--steps times and exit; for hardware-counter runs under rocprofv3")
     args = ap.parse_args()

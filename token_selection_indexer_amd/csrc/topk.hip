@@ -60,10 +60,12 @@ struct Row {
     bool vec;           // rows start 16-byte aligned: 4-element vector loads
 };
 
-// Elements p .. p+3 (p a multiple of 4): keys (0 = does not compete) and ids.
-__device__ __forceinline__ void elem4(const Row &r, int64_t p, uint32_t (&key)[4], int32_t (&id)[4])
+// Elements p .. p+3 (p a multiple of 4) below `hi` (<= r.hi): keys (0 = does not compete) and
+// ids.
+__device__ __forceinline__ void elem4(const Row &r, int64_t p, uint32_t (&key)[4], int32_t (&id)[4],
+                                      int64_t hi)
 {
-    if (r.vec && p >= r.lo && p + 4 <= r.hi) {
+    if (r.vec && p >= r.lo && p + 4 <= hi) {
         const float4 v = *reinterpret_cast<const float4 *>(r.sc + p);
         const float f[4] = {v.x, v.y, v.z, v.w};
         int32_t c[4];
@@ -84,7 +86,7 @@ __device__ __forceinline__ void elem4(const Row &r, int64_t p, uint32_t (&key)[4
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t q = p + j;
-        if (q < r.lo || q >= r.hi) {
+        if (q < r.lo || q >= hi) {
             id[j] = -1;
             key[j] = 0u;
             continue;
@@ -93,6 +95,43 @@ __device__ __forceinline__ void elem4(const Row &r, int64_t p, uint32_t (&key)[4
         id[j] = c;
         key[j] = (c >= r.id_lo && c < r.id_hi) ? order_key(r.sc[q]) : 0u;
     }
+}
+
+// Elements p .. p+3 (p a multiple of 4) below `hi` (<= r.hi) as raw scores, -inf for elements
+// that do not compete, plus (candidate rows) their ids.  For a finite threshold t,
+// "key(f) >= T" is "f >= t" (order_key is monotone and equates -0 with +0, as float comparison
+// does), so a pass against a threshold needs no key per element.
+__device__ __forceinline__ void elem4f(const Row &r, int64_t p, float (&f)[4], int32_t (&id)[4],
+                                       int64_t hi)
+{
+    if (r.vec && p >= r.lo && p + 4 <= hi) {
+        const float4 v = *reinterpret_cast<const float4 *>(r.sc + p);
+        f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+        if (r.ids) {
+            const int4 iv = *reinterpret_cast<const int4 *>(r.ids + p);
+            id[0] = iv.x; id[1] = iv.y; id[2] = iv.z; id[3] = iv.w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (!(id[j] >= r.id_lo && id[j] < r.id_hi)) f[j] = -INFINITY;
+        }
+        return; // flat rows: every position in [lo, hi) competes, id = position
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t q = p + j;
+        f[j] = -INFINITY;
+        id[j] = -1;
+        if (q < r.lo || q >= hi) continue;
+        const int32_t c = r.ids ? r.ids[q] : (int32_t)q;
+        id[j] = c;
+        if (c >= r.id_lo && c < r.id_hi) f[j] = r.sc[q];
+    }
+}
+
+// The float whose order key is T (the smallest float f with key(f) >= T).
+__device__ __forceinline__ float key_to_float(uint32_t T)
+{
+    return __uint_as_float((T & 0x80000000u) ? (T & 0x7fffffffu) : ~T);
 }
 
 // Element at position p: (key, id); key 0 = does not compete.
@@ -145,7 +184,7 @@ struct Digit {
 };
 
 template <int NT>
-__device__ Digit find_digit(const int *hist, int nbins, int need, int *scratch)
+__device__ __forceinline__ Digit find_digit(const int *hist, int nbins, int need, int *scratch)
 {
     // thread i owns bins [nbins - (i+1)*per, nbins - i*per), scanned top-down (with fewer bins
     // than threads, threads past the last bin own none)
@@ -191,7 +230,8 @@ __device__ Digit find_digit(const int *hist, int nbins, int need, int *scratch)
 // only ever affects speed, never the result.  Every workgroup computing T for the same row
 // gets the same T.  `hist` holds NBIN ints.
 template <int NTH, int KPT>
-__device__ uint32_t sample_threshold(int *hist, int *scratch, const Row &r, int need, int64_t len)
+__device__ __forceinline__ uint32_t sample_threshold(int *hist, int *scratch, const Row &r, int need,
+                                                     int64_t len)
 {
     constexpr int NWV = NTH / kWave;
     constexpr int NSB = NWV * KPT; // sample blocks
@@ -227,7 +267,10 @@ __device__ uint32_t sample_threshold(int *hist, int *scratch, const Row &r, int 
         prefix = (prefix << 11) | (uint32_t)g.d;
         rem -= g.above;
     }
-    return prefix << 10;
+    // passes compare floats against T: keep it above the key of -inf (always so for finite
+    // sampled scores; a -inf threshold would also admit elements that do not compete)
+    const uint32_t T = prefix << 10;
+    return T > order_key(-INFINITY) ? T : 0u;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -249,7 +292,7 @@ struct Smem {
 
 __device__ __forceinline__ int64_t round_begin(const Row &r) { return r.lo; }
 
-__device__ void clear_hist(Smem &sm)
+__device__ __forceinline__ void clear_hist(Smem &sm)
 {
     for (int i = threadIdx.x; i < NBIN; i += NT) sm.hist[i] = 0;
     __syncthreads();
@@ -257,7 +300,8 @@ __device__ void clear_hist(Smem &sm)
 
 // Histogram of digit (key >> shift) & (nbins-1) over the row's elements whose bits above the
 // digit equal `prefix` (all elements when pbits == 0).
-__device__ void hist_row(Smem &sm, const Row &r, int shift, int nbins, int pbits, uint32_t prefix)
+__device__ __forceinline__ void hist_row(Smem &sm, const Row &r, int shift, int nbins, int pbits,
+                                         uint32_t prefix)
 {
     clear_hist(sm);
     const int hs = shift + __builtin_ctz((unsigned)nbins);
@@ -275,7 +319,8 @@ __device__ void hist_row(Smem &sm, const Row &r, int shift, int nbins, int pbits
 }
 
 // pbits == 0: every buffered key counts (the level-0 digit).
-__device__ void hist_buf(Smem &sm, int nbuf, int shift, int nbins, uint32_t prefix, int pbits = 1)
+__device__ __forceinline__ void hist_buf(Smem &sm, int nbuf, int shift, int nbins, uint32_t prefix,
+                                         int pbits = 1)
 {
     clear_hist(sm);
     const int hs = shift + __builtin_ctz((unsigned)nbins);
@@ -289,7 +334,7 @@ __device__ void hist_buf(Smem &sm, int nbuf, int shift, int nbins, uint32_t pref
 
 // Ordered pass over the row: take key > T, or key == T while fewer than eq_take earlier
 // elements had key == T.  Taken ids go to dst (or into the LDS buffer).  Returns the count.
-__device__ int select_row(Smem &sm, const Row &r, uint32_t T, int eq_take, int32_t *dst,
+__device__ __forceinline__ int select_row(Smem &sm, const Row &r, uint32_t T, int eq_take, int32_t *dst,
                           bool to_buf, int limit)
 {
     int taken = 0, eq_seen = 0;
@@ -328,7 +373,8 @@ __device__ int select_row(Smem &sm, const Row &r, uint32_t T, int eq_take, int32
 }
 
 // The same over the LDS buffer (already in position order).
-__device__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq_take, int32_t *dst, int limit)
+__device__ __forceinline__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq_take, int32_t *dst,
+                                          int limit)
 {
     int taken = 0, eq_seen = 0;
     for (int base = 0; base < nbuf; base += ROUND) {
@@ -361,7 +407,8 @@ __device__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq_take, int32_t *
 
 // The buffer holds, in position order, every element whose top `pbits` key bits are >= prefix
 // (pbits == 11).  Resolve the remaining digits and emit `need` picks.
-__device__ void finish_in_buf(Smem &sm, int nbuf, uint32_t prefix, int need_rem, int32_t *dst,
+__device__ __forceinline__ void finish_in_buf(Smem &sm, int nbuf, uint32_t prefix, int need_rem,
+                                              int32_t *dst,
                               int need)
 {
     const int shifts[2] = {10, 0};
@@ -377,7 +424,7 @@ __device__ void finish_in_buf(Smem &sm, int nbuf, uint32_t prefix, int need_rem,
 
 // The buffer holds, in position order, a set of elements that contains the row's `need` best.
 // Emit exactly those (all of them, padded with -1, if there are at most `need`).
-__device__ void select_in_buf(Smem &sm, int nbuf, int need, int32_t *dst)
+__device__ __forceinline__ void select_in_buf(Smem &sm, int nbuf, int need, int32_t *dst)
 {
     if (nbuf <= need) {
         const int got = select_buf(sm, nbuf, 0u, 0, dst, need);
@@ -409,18 +456,25 @@ __device__ __forceinline__ Seg wave_segment(const Row &r)
 }
 
 // Level-0 histogram (key bits 31..21) of the row.
-__device__ void hist_row_seg(Smem &sm, const Row &r)
+__device__ __forceinline__ void hist_row_seg(Smem &sm, const Row &r)
 {
     clear_hist(sm);
     const Seg sg = wave_segment(r);
-#pragma unroll 4
-    for (int64_t p = sg.b0 + 4 * lane_id(); p < sg.b1; p += 4 * kWave) {
-        uint32_t key[4];
-        int32_t id[4];
-        elem4(r, p, key, id);
+    const int64_t whi = min(r.hi, sg.b1); // this wave's part of the row ends here
+    constexpr int U = 4; // 4 x 1 KB of the segment in flight per wave
+    for (int64_t p0 = sg.b0; p0 < sg.b1; p0 += U * 4 * kWave) {
+        uint32_t key[U][4];
+        int32_t id[U][4];
+        static_for<0, U>([&](auto UI) {
+            constexpr int u = decltype(UI)::value;
+            elem4(r, p0 + u * 4 * kWave + 4 * lane_id(), key[u], id[u], whi);
+        });
+        static_for<0, U>([&](auto UI) {
+            constexpr int u = decltype(UI)::value;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (key[j]) atomicAdd(&sm.hist[key[j] >> 21], 1);
+            for (int j = 0; j < 4; ++j)
+                if (key[u][j]) atomicAdd(&sm.hist[key[u][j] >> 21], 1);
+        });
     }
     __syncthreads();
 }
@@ -428,37 +482,55 @@ __device__ void hist_row_seg(Smem &sm, const Row &r)
 // Every element with key >= lowest, into the LDS buffer in position order.  Each wave appends
 // its segment's elements to its own list (order kept by a wave prefix sum), then the lists are
 // concatenated in wave order.  Returns false if a wave's list overflowed (caller falls back).
-__device__ bool collect_row_seg(Smem &sm, const Row &r, uint32_t lowest, int &nbuf, int &total_out)
+__device__ __forceinline__ bool collect_row_seg(Smem &sm, const Row &r, uint32_t lowest, int &nbuf,
+                                                int &total_out)
 {
     const int w = wave_id(), lane = lane_id();
     const Seg sg = wave_segment(r);
+    const int64_t whi = min(r.hi, sg.b1); // this wave's part ends here; later positions read as
+                                          // "does not compete"
     const int base = w * WCAP;
+    const float tf = key_to_float(lowest);
+    if (!(tf > -INFINITY)) { // threshold at or below -inf (only with -inf scores): the caller's
+        total_out = 0;        // key-based ordered pass collects instead
+        return false;
+    }
     int cnt = 0;
-    // The trip count is uniform over the wave (the scan below needs every lane): segments are
-    // whole multiples of 4*64 elements, so p never reaches the next wave's segment, and
-    // positions at or past hi read as "does not compete".
-    for (int64_t p0 = sg.b0; p0 < sg.b1; p0 += 4 * kWave) {
-        const int64_t p = p0 + 4 * lane;
-        uint32_t key[4];
-        int32_t id[4];
-        elem4(r, p, key, id);
-        int c = 0;
+    // The trip count is uniform over the wave (the scan below needs every lane).  U steps of
+    // 4 x 64 elements are loaded before any is appended, so 4 KB per wave are in flight; the
+    // steps are then appended in position order.  Elements are compared as floats; keys are
+    // formed only for the few that are kept.
+    constexpr int U = 4;
+    for (int64_t p0 = sg.b0; p0 < sg.b1; p0 += U * 4 * kWave) {
+        float fv[U][4];
+        int32_t id[U][4];
+        static_for<0, U>([&](auto UI) {
+            constexpr int u = decltype(UI)::value;
+            elem4f(r, p0 + u * 4 * kWave + 4 * lane, fv[u], id[u], whi);
+        });
+        // (static_for: the compiler does not unroll loops holding wave scans, and a rolled loop
+        // would index the key arrays dynamically, i.e. from scratch memory)
+        static_for<0, U>([&](auto UI) {
+            constexpr int u = decltype(UI)::value;
+            int c = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) c += (key[j] >= lowest) ? 1 : 0;
-        if (__ballot(c > 0) == 0) continue;
-        const int inc = wave_inclusive_scan(c);
-        const int tot = __shfl(inc, kWave - 1, kWave);
-        int pos = cnt + inc - c;
+            for (int j = 0; j < 4; ++j) c += (fv[u][j] >= tf) ? 1 : 0;
+            if (__ballot(c > 0) == 0) return;
+            const int inc = wave_inclusive_scan(c);
+            const int tot = __shfl(inc, kWave - 1, kWave);
+            int pos = cnt + inc - c;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (key[j] < lowest) continue;
-            if (pos < WCAP) {
-                sm.buf_key[base + pos] = key[j];
-                sm.buf_id[base + pos] = id[j];
+            for (int j = 0; j < 4; ++j) {
+                if (!(fv[u][j] >= tf)) continue;
+                if (pos < WCAP) {
+                    sm.buf_key[base + pos] = order_key(fv[u][j]);
+                    sm.buf_id[base + pos] =
+                        r.ids ? id[u][j] : (int32_t)(p0 + u * 4 * kWave + 4 * lane + j);
+                }
+                ++pos;
             }
-            ++pos;
-        }
-        cnt += tot;
+            cnt += tot;
+        });
     }
     if (lane == 0) sm.cnt[w] = cnt;
     __syncthreads();
@@ -499,12 +571,13 @@ __device__ bool collect_row_seg(Smem &sm, const Row &r, uint32_t lowest, int &nb
 }
 
 // Select `need` elements of the row by (key desc, position asc) into dst, ascending; pad -1.
-__device__ void select_top(Smem &sm, const Row &r, int need, int32_t *dst)
+__device__ __forceinline__ void select_top(Smem &sm, const Row &r, int need, int32_t *dst)
 {
     if (need <= 0) return;
     const int64_t len = r.hi - r.lo;
     // long rows: a sampled threshold lets one pass collect everything at or above it
-    const uint32_t T = len >= SAMPLE_MIN ? sample_threshold<NT, 4>(sm.hist, sm.scratch, r, need, len) : 0u;
+    const uint32_t T =
+        len >= SAMPLE_MIN ? sample_threshold<NT, 4>(sm.hist, sm.scratch, r, need, len) : 0u;
     if (T != 0u) {
         int nbuf = 0, total = 0;
         bool ok = collect_row_seg(sm, r, T, nbuf, total);
@@ -555,7 +628,8 @@ __device__ void select_top(Smem &sm, const Row &r, int need, int32_t *dst)
 
 // Row setup shared by both paths.  Returns false when the row needs no selection (all of it
 // written already).
-__device__ bool setup_row(const SelectArgs &a, int64_t row, Row &r, int32_t *&dst, int &need,
+__device__ __forceinline__ bool setup_row(const SelectArgs &a, int64_t row, Row &r, int32_t *&dst,
+                                          int &need,
                           bool write_fixed)
 {
     const int64_t t = row % a.n_q;
@@ -640,8 +714,9 @@ __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a
     int *cntp = ws.count + row * ws.n_chunks + chunk;
     // 1024 samples up to 256K positions, 4096 beyond (the expected sampled rank stays >= 16)
     const int64_t len = r.hi - r.lo;
-    const uint32_t T = len <= (int64_t)1 << 18 ? sample_threshold<CNT_THREADS, 4>(hist, scratch, r, need, len)
-                                               : sample_threshold<CNT_THREADS, 16>(hist, scratch, r, need, len);
+    const uint32_t T = len <= (int64_t)1 << 18
+                           ? sample_threshold<CNT_THREADS, 4>(hist, scratch, r, need, len)
+                           : sample_threshold<CNT_THREADS, 16>(hist, scratch, r, need, len);
     if (T == 0u) { // no usable threshold: the finish kernel falls back to the exact path
         if (threadIdx.x == 0) *cntp = CHUNK_CAP + 1;
         return;
@@ -658,10 +733,18 @@ __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a
     int32_t id[CI];
     bool take[CI];
     int slot[CI];
+    const float tf = key_to_float(T);
 #pragma unroll
     for (int j = 0; j < CI; ++j) {
-        key[j] = elem(r, c0 + (int64_t)j * CNT_THREADS + threadIdx.x, id[j]);
-        take[j] = key[j] >= T;
+        const int64_t p = c0 + (int64_t)j * CNT_THREADS + threadIdx.x;
+        float f = -INFINITY;
+        id[j] = -1;
+        if (p >= r.lo && p < r.hi) {
+            id[j] = r.ids ? r.ids[p] : (int32_t)p;
+            if (id[j] >= r.id_lo && id[j] < r.id_hi) f = r.sc[p];
+        }
+        take[j] = f >= tf;
+        key[j] = take[j] ? order_key(f) : 0u;
     }
     int taken;
     ordered_slots<CNT_THREADS, CI>(take, slot, cnt, taken);
