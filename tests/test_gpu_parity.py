@@ -509,3 +509,52 @@ def test_determinism_decode_path():
     i1 = lsa.topk_select(r1, b.k, b.sink, b.window, kv_len=20000, q_pos0=19999)
     i2 = lsa.topk_select(r2, b.k, b.sink, b.window, kv_len=20000, q_pos0=19999)
     assert torch.equal(i1, i2)
+
+
+def test_graph_replay_of_decode_step_matches_eager():
+    """The decode step (scores -> chunked selection -> split MLA attention) captured in a HIP
+    graph and replayed several times, with eager work and synchronisations in between: every
+    replay's outputs equal the eager step's bit for bit."""
+    w = shrink(DECODE_128K, batch=4, kv_len=40000)
+    s, bud, a = w.index, w.budget, w.attn
+    inp = inputs.index_inputs(w, DEV)
+    att = inputs.attn_inputs(w, 0, DEV)
+    B, L = s.batch, s.kv_len
+    ws_sel, ws_att = lsa.Workspace(), lsa.Workspace()
+
+    def run(scores, idx, out):
+        lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0, out=scores)
+        lsa.topk_select(scores, bud.k, bud.sink, bud.window, kv_len=L, q_pos0=s.q_pos0, out=idx,
+                        ws=ws_sel)
+        lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale, bud.sink, bud.window, d_v=a.d_v,
+                        ws=ws_att, out=out)
+
+    def bufs():
+        return (torch.empty((B, 1, L), dtype=torch.float32, device=DEV),
+                torch.empty((B, 1, bud.k), dtype=torch.int32, device=DEV),
+                torch.empty((B, 1, a.heads, a.d_v), dtype=torch.bfloat16, device=DEV))
+
+    ref_b = bufs()
+    run(*ref_b)
+    torch.cuda.synchronize()
+    g_b = bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(*g_b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(*g_b)
+    other = bufs()
+    for rep in range(3):
+        for t in g_b:
+            t.zero_()
+        graph.replay()
+        run(*other)  # eager work between replays
+        torch.cuda.synchronize()
+        for got, ref_t in zip(g_b, ref_b):
+            assert torch.equal(got.view(torch.int32) if got.dtype != torch.bfloat16 else got,
+                               ref_t.view(torch.int32) if ref_t.dtype != torch.bfloat16 else ref_t), rep
+        say(f"graph replay {rep} ok")
