@@ -512,16 +512,27 @@ __device__ __forceinline__ bool collect_row_seg(Smem &sm, const Row &r, uint32_t
         // would index the key arrays dynamically, i.e. from scratch memory)
         static_for<0, U>([&](auto UI) {
             constexpr int u = decltype(UI)::value;
-            int c = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) c += (fv[u][j] >= tf) ? 1 : 0;
-            if (__ballot(c > 0) == 0) return;
-            const int inc = wave_inclusive_scan(c);
-            const int tot = __shfl(inc, kWave - 1, kWave);
-            int pos = cnt + inc - c;
+            // position among the wave's kept elements in (lane, j) order: one ballot per j
+            // (flags of lanes below this one via mbcnt), no scan
+            bool fl[4];
+            uint64_t m[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if (!(fv[u][j] >= tf)) continue;
+                fl[j] = fv[u][j] >= tf;
+                m[j] = __ballot(fl[j]);
+            }
+            if ((m[0] | m[1] | m[2] | m[3]) == 0) return;
+            int below = 0, tot = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                below += __builtin_amdgcn_mbcnt_hi((uint32_t)(m[j] >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m[j], 0u));
+                tot += __popcll(m[j]);
+            }
+            int pos = cnt + below;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (!fl[j]) continue;
                 if (pos < WCAP) {
                     sm.buf_key[base + pos] = order_key(fv[u][j]);
                     sm.buf_id[base + pos] =
