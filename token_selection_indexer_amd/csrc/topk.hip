@@ -221,55 +221,162 @@ __device__ __forceinline__ Digit find_digit(const int *hist, int nbins, int need
     return r;
 }
 
+// Wave-level exact rank among n <= 64 keys held in LDS (1 <= rem <= n): writes out[0] = the
+// rem-th largest key, out[1] = how many of the keys equal to it fall within the top rem
+// (rem - #greater), out[2] = whether that is all of them.  Lanes holding equal keys write equal
+// values.  Call from one whole wave.
+__device__ __forceinline__ void rank_small(const uint32_t *small, int n, int rem, int *out)
+{
+    const int l = lane_id();
+    const uint32_t v = l < n ? small[l] : 0u;
+    int gt = 0, ge = 0;
+    for (int j = 0; j < n; ++j) {
+        const uint32_t u = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+        gt += u > v;
+        ge += u >= v;
+    }
+    if (l < n && gt < rem && rem <= ge) {
+        out[0] = (int)v;
+        out[1] = rem - gt;
+        out[2] = rem == ge;
+    }
+}
+
+// find_digit for NBIN = 2048 bins, scanned by wave 0 alone (32 bins per lane, lanes top-down),
+// so it costs one barrier.  The histogram must be complete (a barrier after its last update).
+// Uses scratch[NTH/64 .. NTH/64 + 3]; the values read back stay valid until the caller's next
+// barrier-separated write to those slots.
+template <int NTH>
+__device__ __forceinline__ Digit find_digit_w0(const int *hist, int need, int *scratch)
+{
+    constexpr int NWV = NTH / kWave;
+    static_assert(NBIN == 32 * kWave, "32 bins per lane");
+    if (threadIdx.x < kWave) {
+        const int l = (int)threadIdx.x;
+        const int b0 = NBIN - 32 * (l + 1); // the lane owns bins [b0, b0 + 32)
+        const int4 *h4 = reinterpret_cast<const int4 *>(hist + b0);
+        int c[32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int4 v = h4[i];
+            c[4 * i] = v.x;
+            c[4 * i + 1] = v.y;
+            c[4 * i + 2] = v.z;
+            c[4 * i + 3] = v.w;
+        }
+        int mine = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) mine += c[i];
+        const int inc = wave_inclusive_scan(mine);
+        const int ex = inc - mine;
+        if (l == kWave - 1) {
+            scratch[NWV] = inc; // total
+            scratch[NWV + 1] = -1;
+        }
+        if (ex < need && inc >= need) { // one lane: the crossing, from its top bin down
+            int cum = ex, d = b0, above = ex, at = c[0];
+            bool found = false;
+#pragma unroll
+            for (int i = 31; i >= 0; --i) {
+                if (!found && cum + c[i] >= need) {
+                    found = true;
+                    d = b0 + i;
+                    above = cum;
+                    at = c[i];
+                }
+                cum += c[i];
+            }
+            scratch[NWV + 1] = d;
+            scratch[NWV + 2] = above;
+            scratch[NWV + 3] = at;
+        }
+    }
+    __syncthreads();
+    Digit r;
+    r.total = scratch[NWV];
+    r.d = scratch[NWV + 1];
+    r.above = scratch[NWV + 2];
+    r.at = scratch[NWV + 3];
+    return r;
+}
+
 // Threshold from a sample of the row.  NTH/64 * KPT blocks of 64 consecutive positions, evenly
-// spread over [lo, hi) (len = hi - lo > 64 * blocks), are read; T is the lower edge of the
-// 22-bit key prefix holding the rr-th largest sampled key, rr = 2 * need * (sampled / len) + 8,
-// so about twice `need` elements of the row are expected at or above T.  Returns 0 when the
-// sample has fewer than rr competing keys.  The caller checks what it collects against T (at
-// least `need`, within capacity) and falls back to the exact histogram path otherwise, so T
-// only ever affects speed, never the result.  Every workgroup computing T for the same row
-// gets the same T.  `hist` holds NBIN ints.
+// spread over [lo, hi), are read; T is the rr-th largest sampled key (or, when the 11-bit bin
+// holding it has more than 64 sampled keys, the lower edge of its 22-bit key prefix),
+// rr = 2 * need * (sampled / len) + 8, so about twice `need` elements of the row are expected
+// at or above T.  Returns 0 when the row is shorter than the sample or the sample has fewer
+// than rr competing keys.  The caller checks what it collects against T (at least `need`,
+// within capacity) and falls back to the exact histogram path otherwise, so T only ever affects
+// speed, never the result.  Every workgroup computing T for the same row gets the same T.
+// `hist` holds NBIN ints, `small` 64, `scratch` NTH/64 + 8.
 template <int NTH, int KPT>
-__device__ __forceinline__ uint32_t sample_threshold(int *hist, int *scratch, const Row &r, int need,
-                                                     int64_t len)
+__device__ __forceinline__ uint32_t sample_threshold(int *hist, int *scratch, uint32_t *small,
+                                                     const Row &r, int need, int64_t len)
 {
     constexpr int NWV = NTH / kWave;
     constexpr int NSB = NWV * KPT; // sample blocks
-    const int l = lane_id(), wv = wave_id();
+    if (len < (int64_t)kWave * NSB) return 0u;
+    const int l = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(wave_id());
+    // block sb = j*NWV + wv starts at lo + (len - 64) * sb / (NSB - 1): wave-uniform, and its 64
+    // positions lie in [lo, hi)
     uint32_t key[KPT];
-    int cnt = 0;
+    float f[KPT];
+    int32_t c[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-        const int sb = j * NWV + wv;
-        const int64_t start = r.lo + (len - kWave) * sb / (NSB - 1);
-        int32_t id;
-        key[j] = elem(r, start + l, id);
-        cnt += key[j] != 0u;
+        const int64_t start = r.lo + (len - kWave) * (j * NWV + wv) / (NSB - 1);
+        f[j] = r.sc[start + l];
+        if (r.ids) c[j] = r.ids[start + l];
     }
-    int m;
-    block_exclusive_scan<NWV>(cnt, scratch, &m);
+    {
+        int4 *h4 = reinterpret_cast<int4 *>(hist);
+        for (int i = threadIdx.x; i < NBIN / 4; i += NTH) h4[i] = make_int4(0, 0, 0, 0);
+    }
+    if (threadIdx.x == 0) scratch[NWV + 4] = 0;
+    const int32_t id_lo = (int32_t)r.id_lo, id_hi = (int32_t)r.id_hi;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const bool in = !r.ids || (c[j] >= id_lo && c[j] < id_hi);
+        key[j] = in ? order_key(f[j]) : 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (key[j]) atomicAdd(&hist[key[j] >> 21], 1);
+    __syncthreads();
     const int64_t ns = (int64_t)NSB * kWave;
     const int64_t want = (2 * (int64_t)need * ns + len - 1) / len + 8;
-    if (want > m) return 0u;
-    int rem = (int)want;
-    uint32_t prefix = 0u;
-    // two 11-bit digits (key bits 31..21, then 20..10)
-    for (int lvl = 0; lvl < 2; ++lvl) {
-        const int shift = 21 - 11 * lvl;
-        for (int i = threadIdx.x; i < NBIN; i += NTH) hist[i] = 0;
+    if (want > ns) return 0u;
+    const Digit g = find_digit_w0<NTH>(hist, (int)want, scratch);
+    if (want > g.total) return 0u;
+    const int rem = (int)want - g.above;
+    uint32_t T;
+    if (g.at <= kWave) { // rank the crossing bin's sampled keys exactly
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if (key[j] && (key[j] >> 21) == (uint32_t)g.d)
+                small[atomicAdd(&scratch[NWV + 4], 1)] = key[j];
+        __syncthreads();
+        if (threadIdx.x < kWave) rank_small(small, g.at, rem, scratch + NWV + 5);
+        __syncthreads();
+        T = (uint32_t)scratch[NWV + 5];
+    } else { // second 11-bit digit (key bits 20..10)
+        {
+            int4 *h4 = reinterpret_cast<int4 *>(hist);
+            for (int i = threadIdx.x; i < NBIN / 4; i += NTH) h4[i] = make_int4(0, 0, 0, 0);
+        }
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < KPT; ++j)
-            if (key[j] && (lvl == 0 || (key[j] >> 21) == prefix))
-                atomicAdd(&hist[(key[j] >> shift) & (NBIN - 1)], 1);
+            if (key[j] && (key[j] >> 21) == (uint32_t)g.d)
+                atomicAdd(&hist[(key[j] >> 10) & (NBIN - 1)], 1);
         __syncthreads();
-        const Digit g = find_digit<NTH>(hist, NBIN, rem, scratch);
-        prefix = (prefix << 11) | (uint32_t)g.d;
-        rem -= g.above;
+        const Digit h = find_digit_w0<NTH>(hist, rem, scratch);
+        T = (((uint32_t)g.d << 11) | (uint32_t)h.d) << 10;
     }
     // passes compare floats against T: keep it above the key of -inf (always so for finite
     // sampled scores; a -inf threshold would also admit elements that do not compete)
-    const uint32_t T = prefix << 10;
     return T > order_key(-INFINITY) ? T : 0u;
 }
 
@@ -283,7 +390,7 @@ constexpr int ITEMS = 4;
 constexpr int ROUND = NT * ITEMS;
 
 struct Smem {
-    int hist[NBIN];
+    alignas(16) int hist[NBIN];
     int scratch[NW + 8];
     int cnt[ITEMS * NW];
     uint32_t buf_key[CAP];
@@ -372,9 +479,10 @@ __device__ __forceinline__ int select_row(Smem &sm, const Row &r, uint32_t T, in
     return taken; // may exceed limit: only the first `limit` were written
 }
 
-// The same over the LDS buffer (already in position order).
+// The same over the LDS buffer (already in position order).  eq_all: every key == T is taken
+// (eq_take is their count), so one compaction of key >= T does.
 __device__ __forceinline__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq_take, int32_t *dst,
-                                          int limit)
+                                          int limit, bool eq_all = false)
 {
     int taken = 0, eq_seen = 0;
     for (int base = 0; base < nbuf; base += ROUND) {
@@ -387,11 +495,17 @@ __device__ __forceinline__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq
             key[j] = i < nbuf ? sm.buf_key[i] : 0u;
             is_eq[j] = key[j] && key[j] == T;
         }
-        int eq_tot;
-        ordered_slots<NT, ITEMS>(is_eq, eq_slot, sm.cnt, eq_tot);
+        if (eq_all) {
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j)
-            take[j] = key[j] && (key[j] > T || (is_eq[j] && eq_seen + eq_slot[j] < eq_take));
+            for (int j = 0; j < ITEMS; ++j) take[j] = key[j] && key[j] >= T;
+        } else {
+            int eq_tot;
+            ordered_slots<NT, ITEMS>(is_eq, eq_slot, sm.cnt, eq_tot);
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j)
+                take[j] = key[j] && (key[j] > T || (is_eq[j] && eq_seen + eq_slot[j] < eq_take));
+            eq_seen += eq_tot;
+        }
         int tot;
         ordered_slots<NT, ITEMS>(take, slot, sm.cnt, tot);
 #pragma unroll
@@ -400,7 +514,6 @@ __device__ __forceinline__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq
             if (take[j] && pos < limit) dst[pos] = sm.buf_id[base + j * NT + threadIdx.x];
         }
         taken += tot;
-        eq_seen += eq_tot;
     }
     return taken;
 }
@@ -408,18 +521,101 @@ __device__ __forceinline__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq
 // The buffer holds, in position order, every element whose top `pbits` key bits are >= prefix
 // (pbits == 11).  Resolve the remaining digits and emit `need` picks.
 __device__ __forceinline__ void finish_in_buf(Smem &sm, int nbuf, uint32_t prefix, int need_rem,
-                                              int32_t *dst,
-                              int need)
+                                              int32_t *dst, int need)
 {
     const int shifts[2] = {10, 0};
     const int bitsv[2] = {11, 10};
+    int at = 0;
     for (int lvl = 0; lvl < 2; ++lvl) {
         hist_buf(sm, nbuf, shifts[lvl], 1 << bitsv[lvl], prefix);
         const Digit g = find_digit<NT>(sm.hist, 1 << bitsv[lvl], need_rem, sm.scratch);
         prefix = (prefix << bitsv[lvl]) | (uint32_t)g.d;
         need_rem -= g.above;
+        at = g.at;
     }
-    select_buf(sm, nbuf, prefix, need_rem, dst, need);
+    select_buf(sm, nbuf, prefix, need_rem, dst, need, need_rem == at);
+}
+
+__device__ __forceinline__ uint32_t wave_umin(uint32_t x)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, off, kWave));
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off, kWave));
+    return x;
+}
+
+// The buffer holds, in position order, a set of elements that contains the row's `need` best,
+// nbuf > need of them, with keys in [kmin, kmax].  Emit exactly the `need` best.  On entry
+// sm.hist is zero, sm.scratch[NW + 4] is zero and a barrier has passed since.
+//
+// Level 0 bins the buffer over its own key range, digit (key - kmin) >> s with the smallest s
+// that fits 2048 bins, so the bins spread evenly however narrow the range.  When the bin holding
+// the need-th key has at most 64 keys, one wave ranks them exactly; otherwise two more digits of
+// the key are resolved as usual.
+__device__ __forceinline__ void select_in_buf_range(Smem &sm, int nbuf, int need, int32_t *dst,
+                                                    uint32_t kmin, uint32_t kmax)
+{
+    const uint32_t range = kmax - kmin;
+    const int s = range ? max(0, 32 - (int)__builtin_clz(range) - 11) : 0;
+    for (int i = threadIdx.x; i < nbuf; i += NT) atomicAdd(&sm.hist[(sm.buf_key[i] - kmin) >> s], 1);
+    __syncthreads();
+    const Digit g = find_digit_w0<NT>(sm.hist, need, sm.scratch);
+    if (g.at <= kWave) {
+        uint32_t *small = reinterpret_cast<uint32_t *>(sm.cnt);
+        for (int i = threadIdx.x; i < nbuf; i += NT) {
+            const uint32_t k = sm.buf_key[i];
+            if (((k - kmin) >> s) == (uint32_t)g.d) small[atomicAdd(&sm.scratch[NW + 4], 1)] = k;
+        }
+        __syncthreads();
+        if (threadIdx.x < kWave) rank_small(small, g.at, need - g.above, sm.scratch + NW + 5);
+        __syncthreads();
+        const uint32_t T = (uint32_t)sm.scratch[NW + 5];
+        const int eq_take = sm.scratch[NW + 6];
+        const bool eq_all = sm.scratch[NW + 7] != 0;
+        select_buf(sm, nbuf, T, eq_take, dst, need, eq_all);
+        return;
+    }
+    hist_buf(sm, nbuf, 21, NBIN, 0u, 0);
+    const Digit h = find_digit<NT>(sm.hist, NBIN, need, sm.scratch);
+    finish_in_buf(sm, nbuf, (uint32_t)h.d, need - h.above, dst, need);
+}
+
+// Per-wave extremes -> LDS (the caller's next barrier publishes them); read back with
+// block_extremes after that barrier.  Uses sm.cnt[0 .. 2*NW).
+__device__ __forceinline__ void wave_extremes(Smem &sm, uint32_t kmin, uint32_t kmax)
+{
+    kmin = wave_umin(kmin);
+    kmax = wave_umax(kmax);
+    uint32_t *mm = reinterpret_cast<uint32_t *>(sm.cnt);
+    if (lane_id() == 0) {
+        mm[wave_id()] = kmin;
+        mm[NW + wave_id()] = kmax;
+    }
+}
+
+__device__ __forceinline__ void block_extremes(const Smem &sm, uint32_t &kmin, uint32_t &kmax)
+{
+    const uint32_t *mm = reinterpret_cast<const uint32_t *>(sm.cnt);
+    kmin = ~0u;
+    kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        kmin = min(kmin, mm[i]);
+        kmax = max(kmax, mm[NW + i]);
+    }
+}
+
+__device__ __forceinline__ void clear_hist_nobar(Smem &sm)
+{
+    int4 *h4 = reinterpret_cast<int4 *>(sm.hist);
+    for (int i = threadIdx.x; i < NBIN / 4; i += NT) h4[i] = make_int4(0, 0, 0, 0);
+    if (threadIdx.x == 0) sm.scratch[NW + 4] = 0;
 }
 
 // The buffer holds, in position order, a set of elements that contains the row's `need` best.
@@ -431,9 +627,17 @@ __device__ __forceinline__ void select_in_buf(Smem &sm, int nbuf, int need, int3
         for (int i = got + (int)threadIdx.x; i < need; i += NT) dst[i] = -1;
         return;
     }
-    hist_buf(sm, nbuf, 21, NBIN, 0u, 0);
-    const Digit g = find_digit<NT>(sm.hist, NBIN, need, sm.scratch);
-    finish_in_buf(sm, nbuf, (uint32_t)g.d, need - g.above, dst, need);
+    uint32_t kmin = ~0u, kmax = 0u;
+    for (int i = threadIdx.x; i < nbuf; i += NT) {
+        const uint32_t k = sm.buf_key[i];
+        kmin = min(kmin, k);
+        kmax = max(kmax, k);
+    }
+    wave_extremes(sm, kmin, kmax);
+    clear_hist_nobar(sm);
+    __syncthreads();
+    block_extremes(sm, kmin, kmax);
+    select_in_buf_range(sm, nbuf, need, dst, kmin, kmax);
 }
 
 // ---- streaming passes: each wave owns a contiguous segment of the row (no block barriers) ----
@@ -587,8 +791,11 @@ __device__ __forceinline__ void select_top(Smem &sm, const Row &r, int need, int
     if (need <= 0) return;
     const int64_t len = r.hi - r.lo;
     // long rows: a sampled threshold lets one pass collect everything at or above it
-    const uint32_t T =
-        len >= SAMPLE_MIN ? sample_threshold<NT, 4>(sm.hist, sm.scratch, r, need, len) : 0u;
+    const uint32_t T = len >= SAMPLE_MIN
+                           ? sample_threshold<NT, 4>(sm.hist, sm.scratch,
+                                                     reinterpret_cast<uint32_t *>(sm.cnt), r, need,
+                                                     len)
+                           : 0u;
     if (T != 0u) {
         int nbuf = 0, total = 0;
         bool ok = collect_row_seg(sm, r, T, nbuf, total);
@@ -701,21 +908,28 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
 // Chunked path
 // ------------------------------------------------------------------------------------------
 
+constexpr int CNT_WAVES = CNT_THREADS / kWave;
+constexpr int WSEG = CHUNK / CNT_WAVES; // positions per wave (contiguous)
+constexpr int CI = WSEG / kWave;        // items per lane
+
 struct ChunkWs {
-    int *count;      // [rows][n_chunks]  (CHUNK_CAP + 1 = overflow or no threshold)
-    uint32_t *ckey;  // [rows][n_chunks][CHUNK_CAP]
-    int32_t *cid;    // [rows][n_chunks][CHUNK_CAP]
+    int *count;     // [rows][n_chunks]  (CHUNK_CAP + 1 = overflow or no threshold)
+    float *cval;    // [rows][n_chunks][CHUNK_CAP] scores of the collected elements
+    int32_t *cid;   // [rows][n_chunks][CHUNK_CAP] their ids
     int n_chunks;
 };
 
 // Every chunk of a row derives the row's sampled threshold T (the same T in every workgroup)
 // and compacts its elements with key >= T, in position order, into its slice of the workspace.
+// Wave w owns positions [c0 + w*WSEG, c0 + (w+1)*WSEG); item j of lane l is position
+// c0 + w*WSEG + j*64 + l.  CAND: candidate rows (ids read from the list).
+template <bool CAND>
 __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a, ChunkWs ws)
 {
-    constexpr int CI = CHUNK / CNT_THREADS; // items per thread
-    __shared__ int hist[NBIN];
-    __shared__ int scratch[CNT_THREADS / kWave + 8];
-    __shared__ int cnt[kWave];
+    __shared__ __align__(16) int hist[NBIN];
+    __shared__ int scratch[CNT_WAVES + 8];
+    __shared__ uint32_t small[kWave];
+    __shared__ int wcnt[CNT_WAVES];
     const int64_t row = blockIdx.y;
     const int chunk = blockIdx.x;
     Row r;
@@ -723,52 +937,93 @@ __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a
     int need;
     if (!setup_row(a, row, r, dst, need, false)) return;
     int *cntp = ws.count + row * ws.n_chunks + chunk;
-    // 1024 samples up to 256K positions, 4096 beyond (the expected sampled rank stays >= 16)
-    const int64_t len = r.hi - r.lo;
-    const uint32_t T = len <= (int64_t)1 << 18
-                           ? sample_threshold<CNT_THREADS, 4>(hist, scratch, r, need, len)
-                           : sample_threshold<CNT_THREADS, 16>(hist, scratch, r, need, len);
-    if (T == 0u) { // no usable threshold: the finish kernel falls back to the exact path
-        if (threadIdx.x == 0) *cntp = CHUNK_CAP + 1;
-        return;
-    }
     const int64_t c0 = (int64_t)chunk * CHUNK;
+    // a chunk outside the row collects nothing; the row's other chunks report its threshold
     if (c0 + CHUNK <= r.lo || c0 >= r.hi) {
         if (threadIdx.x == 0) *cntp = 0;
         return;
     }
-    uint32_t *okey = ws.ckey + (row * ws.n_chunks + chunk) * CHUNK_CAP;
-    int32_t *oid = ws.cid + (row * ws.n_chunks + chunk) * CHUNK_CAP;
-    // CI items per thread: item j of thread t is element c0 + j*CNT_THREADS + t
-    uint32_t key[CI];
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+    const int64_t wb = c0 + (int64_t)w * WSEG;
+    const bool inner = wb >= r.lo && wb + WSEG <= r.hi; // wave-uniform
+    // the chunk's loads go out first, so their latency overlaps the sample's
+    float f[CI];
     int32_t id[CI];
-    bool take[CI];
-    int slot[CI];
+    if (inner) {
+        const float *ps = r.sc + wb + lane;
+#pragma unroll
+        for (int j = 0; j < CI; ++j) f[j] = ps[j * kWave];
+        if (CAND) {
+            const int32_t *pi = r.ids + wb + lane;
+#pragma unroll
+            for (int j = 0; j < CI; ++j) id[j] = pi[j * kWave];
+        }
+    } else { // positions clamped into the row (non-empty), used only when inside it
+#pragma unroll
+        for (int j = 0; j < CI; ++j) {
+            const int64_t p = wb + j * kWave + lane;
+            const int64_t pc = p < r.lo ? r.lo : (p >= r.hi ? r.hi - 1 : p);
+            f[j] = r.sc[pc];
+            if (CAND) id[j] = r.ids[pc];
+        }
+    }
+    // 1024 samples up to 256K positions, 4096 beyond (the expected sampled rank stays >= 16)
+    const int64_t len = r.hi - r.lo;
+    const uint32_t T = len <= (int64_t)1 << 18
+                           ? sample_threshold<CNT_THREADS, 4>(hist, scratch, small, r, need, len)
+                           : sample_threshold<CNT_THREADS, 16>(hist, scratch, small, r, need, len);
+    if (T == 0u) { // no usable threshold: the finish kernel falls back to the exact path
+        if (threadIdx.x == 0) *cntp = CHUNK_CAP + 1;
+        return;
+    }
     const float tf = key_to_float(T);
+    const int32_t id_lo = (int32_t)r.id_lo, id_hi = (int32_t)r.id_hi;
+    uint64_t m[CI];
+    int cnt = 0;
 #pragma unroll
     for (int j = 0; j < CI; ++j) {
-        const int64_t p = c0 + (int64_t)j * CNT_THREADS + threadIdx.x;
-        float f = -INFINITY;
-        id[j] = -1;
-        if (p >= r.lo && p < r.hi) {
-            id[j] = r.ids ? r.ids[p] : (int32_t)p;
-            if (id[j] >= r.id_lo && id[j] < r.id_hi) f = r.sc[p];
+        bool take = f[j] >= tf;
+        if (CAND) take = take && id[j] >= id_lo && id[j] < id_hi;
+        if (!inner) {
+            const int64_t p = wb + j * kWave + lane;
+            take = take && p >= r.lo && p < r.hi;
         }
-        take[j] = f >= tf;
-        key[j] = take[j] ? order_key(f) : 0u;
+        m[j] = __ballot(take);
+        cnt += __popcll(m[j]);
     }
-    int taken;
-    ordered_slots<CNT_THREADS, CI>(take, slot, cnt, taken);
+    if (lane == 0) wcnt[w] = cnt;
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < CNT_WAVES; ++i) {
+        const int c = wcnt[i];
+        base += i < w ? c : 0;
+        total += c;
+    }
+    if (total > CHUNK_CAP) {
+        if (threadIdx.x == 0) *cntp = CHUNK_CAP + 1;
+        return;
+    }
+    float *ov = ws.cval + (row * ws.n_chunks + chunk) * CHUNK_CAP;
+    int32_t *oi = ws.cid + (row * ws.n_chunks + chunk) * CHUNK_CAP;
+    int pos = base;
 #pragma unroll
     for (int j = 0; j < CI; ++j) {
-        if (take[j] && slot[j] < CHUNK_CAP) {
-            okey[slot[j]] = key[j];
-            oid[slot[j]] = id[j];
+        if (m[j] == 0) continue;
+        if ((m[j] >> lane) & 1) {
+            const int s = pos + (int)__builtin_amdgcn_mbcnt_hi(
+                                    (uint32_t)(m[j] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[j], 0u));
+            ov[s] = f[j];
+            oi[s] = CAND ? id[j] : (int32_t)(wb + j * kWave + lane);
         }
+        pos += __popcll(m[j]);
     }
-    if (threadIdx.x == 0) *cntp = taken > CHUNK_CAP ? CHUNK_CAP + 1 : taken;
+    if (threadIdx.x == 0) *cntp = total;
 }
 
+// One workgroup per row: concatenates the row's slices (chunk order = position order) into LDS
+// and selects exactly there.
 __global__ __launch_bounds__(NT) void chunk_finish_kernel(SelectArgs a, ChunkWs ws)
 {
     __shared__ Smem sm;
@@ -777,40 +1032,77 @@ __global__ __launch_bounds__(NT) void chunk_finish_kernel(SelectArgs a, ChunkWs 
     int32_t *dst;
     int need;
     if (!setup_row(a, row, r, dst, need, true)) return;
-    // slice offsets (exclusive scan of the counts) into sm.hist, which is free until the end
-    const int *counts = ws.count + row * ws.n_chunks;
-    int overflow = 0, total = 0;
-    for (int base = 0; base < ws.n_chunks; base += NT) {
-        const int i = base + threadIdx.x;
-        const int c = i < ws.n_chunks ? counts[i] : 0;
-        overflow |= c > CHUNK_CAP;
-        int tot;
-        const int ex = block_exclusive_scan<NW>(c > CHUNK_CAP ? 0 : c, sm.scratch, &tot);
-        if (i < ws.n_chunks) sm.hist[i] = total + ex;
-        total += tot;
-    }
-    __syncthreads();
-    // copy the slices in chunk order: one wave per slice, coalesced
-    if (total <= CAP) {
-        for (int i = wave_id(); i < ws.n_chunks; i += NW) {
-            const int c = counts[i];
-            if (c > CHUNK_CAP) continue;
-            const int off = sm.hist[i];
-            const uint32_t *ck = ws.ckey + (row * ws.n_chunks + i) * CHUNK_CAP;
-            const int32_t *ci = ws.cid + (row * ws.n_chunks + i) * CHUNK_CAP;
-            for (int e = lane_id(); e < c; e += kWave) {
-                sm.buf_key[off + e] = ck[e];
-                sm.buf_id[off + e] = ci[e];
-            }
+    const int nc = ws.n_chunks;
+    const int *counts = ws.count + row * nc;
+    const int lane = lane_id(), w = wave_id();
+    // every wave scans the counts itself (no block barrier); the first 64 stay in registers
+    const int cfirst = lane < nc ? counts[lane] : 0;
+    bool bad = cfirst > CHUNK_CAP;
+    int total = 0;
+    {
+        const int c = cfirst > CHUNK_CAP ? 0 : cfirst;
+        total = __shfl(wave_inclusive_scan(c), kWave - 1, kWave);
+        for (int g = kWave; g < nc; g += kWave) {
+            const int i = g + lane;
+            int cg = i < nc ? counts[i] : 0;
+            bad |= cg > CHUNK_CAP;
+            cg = cg > CHUNK_CAP ? 0 : cg;
+            total += __shfl(wave_inclusive_scan(cg), kWave - 1, kWave);
         }
     }
-    overflow = __syncthreads_or(overflow);
-    // the slices hold every element >= T of the row; enough of them contain the `need` best
-    if (overflow || total > CAP || total < need) { // fall back to the one-workgroup path
+    // the same in every wave: every element >= T of the row sits in the slices, which hold at
+    // least `need` elements and fit the buffer -- else the one-workgroup path over the row
+    if (__ballot(bad) != 0 || total > CAP || total < need) {
         select_top(sm, r, need, dst);
         return;
     }
-    select_in_buf(sm, total, need, dst);
+    clear_hist_nobar(sm);
+    uint32_t kmin = ~0u, kmax = 0u;
+    int run = 0;
+    for (int g = 0; g < nc; g += kWave) {
+        const int cg = g == 0 ? cfirst : (g + lane < nc ? counts[g + lane] : 0);
+        const int inc = wave_inclusive_scan(cg);
+        const int off = run + inc - cg;
+        run += __shfl(inc, kWave - 1, kWave);
+        // this wave copies slices g + s, s = w, w + NW, ...: loads of up to 4 rounds of 64 are
+        // issued together (clamped to the slice's first element), then written
+        for (int s = w; s < kWave && g + s < nc; s += NW) {
+            const int cs = __shfl(cg, s, kWave), os = __shfl(off, s, kWave);
+            const float *sv = ws.cval + (row * nc + g + s) * CHUNK_CAP;
+            const int32_t *si = ws.cid + (row * nc + g + s) * CHUNK_CAP;
+            for (int e0 = 0; e0 < cs; e0 += 4 * kWave) {
+                float v[4];
+                int32_t d[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int e = e0 + u * kWave + lane;
+                    const int ec = e < cs ? e : 0;
+                    v[u] = sv[ec];
+                    d[u] = si[ec];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int e = e0 + u * kWave + lane;
+                    if (e < cs) {
+                        const uint32_t k = order_key(v[u]);
+                        sm.buf_key[os + e] = k;
+                        sm.buf_id[os + e] = d[u];
+                        kmin = min(kmin, k);
+                        kmax = max(kmax, k);
+                    }
+                }
+            }
+        }
+    }
+    if (total <= need) { // exactly `need` (total >= need): take them all
+        __syncthreads();
+        select_in_buf(sm, total, need, dst);
+        return;
+    }
+    wave_extremes(sm, kmin, kmax);
+    __syncthreads();
+    block_extremes(sm, kmin, kmax);
+    select_in_buf_range(sm, total, need, dst, kmin, kmax);
 }
 
 bool use_chunked(const SelectArgs &a)
@@ -849,12 +1141,16 @@ hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream)
     ChunkWs w;
     w.count = reinterpret_cast<int *>(p);
     p += r256(rows * nc * 4);
-    w.ckey = reinterpret_cast<uint32_t *>(p);
+    w.cval = reinterpret_cast<float *>(p);
     p += r256(rows * nc * CHUNK_CAP * 4);
     w.cid = reinterpret_cast<int32_t *>(p);
     w.n_chunks = (int)nc;
-    hipLaunchKernelGGL(chunk_collect_kernel, dim3((unsigned)nc, (unsigned)rows), dim3(CNT_THREADS),
-                       0, stream, a, w);
+    if (a.cand_ids)
+        hipLaunchKernelGGL(chunk_collect_kernel<true>, dim3((unsigned)nc, (unsigned)rows),
+                           dim3(CNT_THREADS), 0, stream, a, w);
+    else
+        hipLaunchKernelGGL(chunk_collect_kernel<false>, dim3((unsigned)nc, (unsigned)rows),
+                           dim3(CNT_THREADS), 0, stream, a, w);
     hipLaunchKernelGGL(chunk_finish_kernel, dim3((unsigned)rows), dim3(NT), 0, stream, a, w);
     return hipGetLastError();
 }
