@@ -104,15 +104,18 @@ __device__ __forceinline__ uint32_t order_key(float f)
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
+// Inclusive prefix sum across the 64 lanes of a wave, in DPP steps (no LDS round trips):
+// shifts by 1, 2, 4 and 8 within each row of 16 lanes, then lane 15 of each row added to the
+// next row (rows 1 and 3) and lane 31 to the upper half (rows 2 and 3).  Lanes whose source lies
+// outside the row, and rows outside the row mask, add 0.
 __device__ __forceinline__ int wave_inclusive_scan(int x)
 {
-    const int lane = lane_id();
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        int y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false); // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false); // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false); // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false); // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false); // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false); // row_bcast:31
     return x;
 }
 

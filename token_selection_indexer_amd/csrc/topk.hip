@@ -221,7 +221,8 @@ __device__ __forceinline__ Digit find_digit(const int *hist, int nbins, int need
     return r;
 }
 
-// Wave-level exact rank among n <= 64 keys held in LDS (1 <= rem <= n): writes out[0] = the
+// Wave-level exact rank among n <= 64 nonzero keys held in LDS (16-byte aligned, zero from
+// entry n up to the next multiple of 4), 1 <= rem <= n: writes out[0] = the
 // rem-th largest key, out[1] = how many of the keys equal to it fall within the top rem
 // (rem - #greater), out[2] = whether that is all of them.  Lanes holding equal keys write equal
 // values.  Call from one whole wave.
@@ -230,10 +231,12 @@ __device__ __forceinline__ void rank_small(const uint32_t *small, int n, int rem
     const int l = lane_id();
     const uint32_t v = l < n ? small[l] : 0u;
     int gt = 0, ge = 0;
-    for (int j = 0; j < n; ++j) {
-        const uint32_t u = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
-        gt += u > v;
-        ge += u >= v;
+    // small[n .. 4*ceil(n/4)) are zero: no key of the n is below 1, so they count nowhere
+    const uint4 *s4 = reinterpret_cast<const uint4 *>(small);
+    for (int j = 0; j < (n + 3) / 4; ++j) {
+        const uint4 u = s4[j];
+        gt += (u.x > v) + (u.y > v) + (u.z > v) + (u.w > v);
+        ge += (u.x >= v) + (u.y >= v) + (u.z >= v) + (u.w >= v);
     }
     if (l < n && gt < rem && rem <= ge) {
         out[0] = (int)v;
@@ -242,9 +245,11 @@ __device__ __forceinline__ void rank_small(const uint32_t *small, int n, int rem
     }
 }
 
-// find_digit for NBIN = 2048 bins, scanned by wave 0 alone (32 bins per lane, lanes top-down),
-// so it costs one barrier.  The histogram must be complete (a barrier after its last update).
-// Uses scratch[NTH/64 .. NTH/64 + 3]; the values read back stay valid until the caller's next
+// find_digit for NBIN = 2048 bins, scanned by wave 0 alone, so it costs one barrier: lane l
+// sums bins [2048 - 32(l+1), 2048 - 32l) (lanes in top-down order); the first lane whose
+// inclusive sum reaches `need` holds the digit, and 32 lanes then scan its 32 bins from the top.
+// The histogram must be complete (a barrier after its last update).  Uses
+// scratch[NTH/64 .. NTH/64 + 3]; the values read back stay valid until the caller's next
 // barrier-separated write to those slots.
 template <int NTH>
 __device__ __forceinline__ Digit find_digit_w0(const int *hist, int need, int *scratch)
@@ -253,42 +258,33 @@ __device__ __forceinline__ Digit find_digit_w0(const int *hist, int need, int *s
     static_assert(NBIN == 32 * kWave, "32 bins per lane");
     if (threadIdx.x < kWave) {
         const int l = (int)threadIdx.x;
-        const int b0 = NBIN - 32 * (l + 1); // the lane owns bins [b0, b0 + 32)
-        const int4 *h4 = reinterpret_cast<const int4 *>(hist + b0);
-        int c[32];
+        const int4 *h4 = reinterpret_cast<const int4 *>(hist + NBIN - 32 * (l + 1));
+        int mine = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int4 v = h4[i];
-            c[4 * i] = v.x;
-            c[4 * i + 1] = v.y;
-            c[4 * i + 2] = v.z;
-            c[4 * i + 3] = v.w;
+            mine += v.x + v.y + v.z + v.w;
         }
-        int mine = 0;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) mine += c[i];
         const int inc = wave_inclusive_scan(mine);
-        const int ex = inc - mine;
-        if (l == kWave - 1) {
-            scratch[NWV] = inc; // total
-            scratch[NWV + 1] = -1;
-        }
-        if (ex < need && inc >= need) { // one lane: the crossing, from its top bin down
-            int cum = ex, d = b0, above = ex, at = c[0];
-            bool found = false;
-#pragma unroll
-            for (int i = 31; i >= 0; --i) {
-                if (!found && cum + c[i] >= need) {
-                    found = true;
-                    d = b0 + i;
-                    above = cum;
-                    at = c[i];
-                }
-                cum += c[i];
+        const int total = __builtin_amdgcn_readlane(inc, kWave - 1);
+        const uint64_t ge = __ballot(inc >= need);
+        if (ge != 0u) {
+            const int L = (int)__builtin_ctzll(ge);
+            const int exL = __builtin_amdgcn_readlane(inc, L) - __builtin_amdgcn_readlane(mine, L);
+            const int top = NBIN - 32 * L - 1; // lane i < 32 takes bin top - i
+            const int c = l < 32 ? hist[top - (l & 31)] : 0;
+            const int inc2 = exL + wave_inclusive_scan(c);
+            const uint64_t ge2 = __ballot(l < 32 && inc2 >= need);
+            const int i = (int)__builtin_ctzll(ge2); // exists: exL + (sum of the 32) >= need
+            if (l == i) {
+                scratch[NWV] = total;
+                scratch[NWV + 1] = top - i;
+                scratch[NWV + 2] = inc2 - c;
+                scratch[NWV + 3] = c;
             }
-            scratch[NWV + 1] = d;
-            scratch[NWV + 2] = above;
-            scratch[NWV + 3] = at;
+        } else if (l == 0) {
+            scratch[NWV] = total;
+            scratch[NWV + 1] = -1;
         }
     }
     __syncthreads();
@@ -308,7 +304,7 @@ __device__ __forceinline__ Digit find_digit_w0(const int *hist, int need, int *s
 // than rr competing keys.  The caller checks what it collects against T (at least `need`,
 // within capacity) and falls back to the exact histogram path otherwise, so T only ever affects
 // speed, never the result.  Every workgroup computing T for the same row gets the same T.
-// `hist` holds NBIN ints, `small` 64, `scratch` NTH/64 + 8.
+// `hist` holds NBIN ints, `small` 64 (16-byte aligned), `scratch` NTH/64 + 8.
 template <int NTH, int KPT>
 __device__ __forceinline__ uint32_t sample_threshold(int *hist, int *scratch, uint32_t *small,
                                                      const Row &r, int need, int64_t len)
@@ -333,6 +329,7 @@ __device__ __forceinline__ uint32_t sample_threshold(int *hist, int *scratch, ui
         int4 *h4 = reinterpret_cast<int4 *>(hist);
         for (int i = threadIdx.x; i < NBIN / 4; i += NTH) h4[i] = make_int4(0, 0, 0, 0);
     }
+    if (threadIdx.x < kWave) small[threadIdx.x] = 0u;
     if (threadIdx.x == 0) scratch[NWV + 4] = 0;
     const int32_t id_lo = (int32_t)r.id_lo, id_hi = (int32_t)r.id_hi;
 #pragma unroll
@@ -393,6 +390,7 @@ struct Smem {
     alignas(16) int hist[NBIN];
     int scratch[NW + 8];
     int cnt[ITEMS * NW];
+    alignas(16) uint32_t small[kWave];
     uint32_t buf_key[CAP];
     int32_t buf_id[CAP];
 };
@@ -479,41 +477,68 @@ __device__ __forceinline__ int select_row(Smem &sm, const Row &r, uint32_t T, in
     return taken; // may exceed limit: only the first `limit` were written
 }
 
-// The same over the LDS buffer (already in position order).  eq_all: every key == T is taken
-// (eq_take is their count), so one compaction of key >= T does.
+// The same over the LDS buffer (already in position order).  Wave w takes the contiguous
+// entries [512w, 512(w+1)) (item j of lane l: + 64j + l), so one exchange of per-wave counts
+// orders the picks.  eq_all: every key == T is taken (eq_take is
+// their count).
 __device__ __forceinline__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq_take, int32_t *dst,
                                           int limit, bool eq_all = false)
 {
+    constexpr int BI = CAP / NT; // items per lane: one round covers the buffer
+    constexpr int WSPAN = BI * kWave;
+    const int lane = lane_id(), w = wave_id();
     int taken = 0, eq_seen = 0;
-    for (int base = 0; base < nbuf; base += ROUND) {
-        uint32_t key[ITEMS];
-        bool is_eq[ITEMS], take[ITEMS];
-        int eq_slot[ITEMS], slot[ITEMS];
+    for (int base = 0; base < nbuf; base += NT * BI) {
+        const int i0 = base + w * WSPAN + lane;
+        uint64_t mg[BI], me[BI];
+        int cg = 0, ce = 0;
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const int i = base + j * NT + threadIdx.x;
-            key[j] = i < nbuf ? sm.buf_key[i] : 0u;
-            is_eq[j] = key[j] && key[j] == T;
+        for (int j = 0; j < BI; ++j) {
+            const int i = i0 + j * kWave;
+            const uint32_t key = i < nbuf ? sm.buf_key[i] : 0u;
+            mg[j] = __ballot(eq_all ? (key != 0u && key >= T) : key > T);
+            me[j] = eq_all ? 0u : __ballot(key != 0u && key == T);
+            cg += (int)__popcll(mg[j]);
+            ce += (int)__popcll(me[j]);
         }
-        if (eq_all) {
-#pragma unroll
-            for (int j = 0; j < ITEMS; ++j) take[j] = key[j] && key[j] >= T;
-        } else {
-            int eq_tot;
-            ordered_slots<NT, ITEMS>(is_eq, eq_slot, sm.cnt, eq_tot);
-#pragma unroll
-            for (int j = 0; j < ITEMS; ++j)
-                take[j] = key[j] && (key[j] > T || (is_eq[j] && eq_seen + eq_slot[j] < eq_take));
-            eq_seen += eq_tot;
+        if (lane == 0) {
+            sm.cnt[w] = cg;
+            sm.cnt[NW + w] = ce;
         }
-        int tot;
-        ordered_slots<NT, ITEMS>(take, slot, sm.cnt, tot);
+        __syncthreads();
+        // lane k < NW holds wave k's counts; prefix sums give this wave's bases
+        const int wu = __builtin_amdgcn_readfirstlane(w);
+        const int ck = lane < NW ? sm.cnt[lane] : 0, ek = lane < NW ? sm.cnt[NW + lane] : 0;
+        const int ick = wave_inclusive_scan(ck), iek = wave_inclusive_scan(ek);
+        const int bg = __builtin_amdgcn_readlane(ick, wu) - __builtin_amdgcn_readlane(ck, wu);
+        const int be = __builtin_amdgcn_readlane(iek, wu) - __builtin_amdgcn_readlane(ek, wu);
+        const int tg = __builtin_amdgcn_readlane(ick, NW - 1);
+        const int te = __builtin_amdgcn_readlane(iek, NW - 1);
+        // equal keys of earlier waves that are taken: global equal ranks [eq_seen, eq_seen + be)
+        auto eq_taken = [&](int before) { return max(0, min(eq_take - eq_seen, before)); };
+        int pos = taken + bg + eq_taken(be);
+        int er = eq_seen + be; // equal rank of the wave's next equal key
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const int pos = taken + slot[j];
-            if (take[j] && pos < limit) dst[pos] = sm.buf_id[base + j * NT + threadIdx.x];
+        for (int j = 0; j < BI; ++j) {
+            uint64_t mt = mg[j];
+            if (me[j]) {
+                const int r = er + (int)__builtin_amdgcn_mbcnt_hi(
+                                       (uint32_t)(me[j] >> 32),
+                                       __builtin_amdgcn_mbcnt_lo((uint32_t)me[j], 0u));
+                mt |= __ballot(((me[j] >> lane) & 1u) && r < eq_take);
+                er += (int)__popcll(me[j]);
+            }
+            if ((mt >> lane) & 1u) {
+                const int slot = pos + (int)__builtin_amdgcn_mbcnt_hi(
+                                           (uint32_t)(mt >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mt, 0u));
+                if (slot < limit) dst[slot] = sm.buf_id[i0 + j * kWave];
+            }
+            pos += (int)__popcll(mt);
         }
-        taken += tot;
+        taken += tg + eq_taken(te);
+        eq_seen += te;
+        if (base + NT * BI < nbuf) __syncthreads(); // sm.cnt is rewritten by the next round
     }
     return taken;
 }
@@ -536,23 +561,25 @@ __device__ __forceinline__ void finish_in_buf(Smem &sm, int nbuf, uint32_t prefi
     select_buf(sm, nbuf, prefix, need_rem, dst, need, need_rem == at);
 }
 
-__device__ __forceinline__ uint32_t wave_umin(uint32_t x)
+// Wave-wide unsigned min / max in the DPP steps of wave_inclusive_scan (lane 63 ends with the
+// whole wave's result; out-of-row sources and masked rows contribute the identity).
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u(uint32_t x)
 {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, off, kWave));
-    return x;
-}
-
-__device__ __forceinline__ uint32_t wave_umax(uint32_t x)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off, kWave));
-    return x;
+    const int id = MAX ? 0 : -1;
+    auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x111, 0xf, 0xf, false));
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x112, 0xf, 0xf, false));
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x114, 0xf, 0xf, false));
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x118, 0xf, 0xf, false));
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x142, 0xa, 0xf, false));
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x143, 0xc, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, kWave - 1);
 }
 
 // The buffer holds, in position order, a set of elements that contains the row's `need` best,
 // nbuf > need of them, with keys in [kmin, kmax].  Emit exactly the `need` best.  On entry
-// sm.hist is zero, sm.scratch[NW + 4] is zero and a barrier has passed since.
+// sm.hist, sm.small and sm.scratch[NW + 4] are zero and a barrier has passed since.
 //
 // Level 0 bins the buffer over its own key range, digit (key - kmin) >> s with the smallest s
 // that fits 2048 bins, so the bins spread evenly however narrow the range.  When the bin holding
@@ -567,7 +594,7 @@ __device__ __forceinline__ void select_in_buf_range(Smem &sm, int nbuf, int need
     __syncthreads();
     const Digit g = find_digit_w0<NT>(sm.hist, need, sm.scratch);
     if (g.at <= kWave) {
-        uint32_t *small = reinterpret_cast<uint32_t *>(sm.cnt);
+        uint32_t *small = sm.small;
         for (int i = threadIdx.x; i < nbuf; i += NT) {
             const uint32_t k = sm.buf_key[i];
             if (((k - kmin) >> s) == (uint32_t)g.d) small[atomicAdd(&sm.scratch[NW + 4], 1)] = k;
@@ -590,8 +617,8 @@ __device__ __forceinline__ void select_in_buf_range(Smem &sm, int nbuf, int need
 // block_extremes after that barrier.  Uses sm.cnt[0 .. 2*NW).
 __device__ __forceinline__ void wave_extremes(Smem &sm, uint32_t kmin, uint32_t kmax)
 {
-    kmin = wave_umin(kmin);
-    kmax = wave_umax(kmax);
+    kmin = wave_reduce_u<false>(kmin);
+    kmax = wave_reduce_u<true>(kmax);
     uint32_t *mm = reinterpret_cast<uint32_t *>(sm.cnt);
     if (lane_id() == 0) {
         mm[wave_id()] = kmin;
@@ -602,19 +629,16 @@ __device__ __forceinline__ void wave_extremes(Smem &sm, uint32_t kmin, uint32_t 
 __device__ __forceinline__ void block_extremes(const Smem &sm, uint32_t &kmin, uint32_t &kmax)
 {
     const uint32_t *mm = reinterpret_cast<const uint32_t *>(sm.cnt);
-    kmin = ~0u;
-    kmax = 0u;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        kmin = min(kmin, mm[i]);
-        kmax = max(kmax, mm[NW + i]);
-    }
+    const int l = lane_id();
+    kmin = wave_reduce_u<false>(l < NW ? mm[l] : ~0u);
+    kmax = wave_reduce_u<true>(l < NW ? mm[NW + l] : 0u);
 }
 
 __device__ __forceinline__ void clear_hist_nobar(Smem &sm)
 {
     int4 *h4 = reinterpret_cast<int4 *>(sm.hist);
     for (int i = threadIdx.x; i < NBIN / 4; i += NT) h4[i] = make_int4(0, 0, 0, 0);
+    if (threadIdx.x < kWave) sm.small[threadIdx.x] = 0u;
     if (threadIdx.x == 0) sm.scratch[NW + 4] = 0;
 }
 
@@ -792,9 +816,7 @@ __device__ __forceinline__ void select_top(Smem &sm, const Row &r, int need, int
     const int64_t len = r.hi - r.lo;
     // long rows: a sampled threshold lets one pass collect everything at or above it
     const uint32_t T = len >= SAMPLE_MIN
-                           ? sample_threshold<NT, 4>(sm.hist, sm.scratch,
-                                                     reinterpret_cast<uint32_t *>(sm.cnt), r, need,
-                                                     len)
+                           ? sample_threshold<NT, 4>(sm.hist, sm.scratch, sm.small, r, need, len)
                            : 0u;
     if (T != 0u) {
         int nbuf = 0, total = 0;
@@ -928,7 +950,7 @@ __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a
 {
     __shared__ __align__(16) int hist[NBIN];
     __shared__ int scratch[CNT_WAVES + 8];
-    __shared__ uint32_t small[kWave];
+    __shared__ __align__(16) uint32_t small[kWave];
     __shared__ int wcnt[CNT_WAVES];
     const int64_t row = blockIdx.y;
     const int chunk = blockIdx.x;
@@ -980,18 +1002,26 @@ __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a
     const float tf = key_to_float(T);
     const int32_t id_lo = (int32_t)r.id_lo, id_hi = (int32_t)r.id_hi;
     uint64_t m[CI];
+    if (inner) {
+#pragma unroll
+        for (int j = 0; j < CI; ++j) {
+            bool take = f[j] >= tf;
+            if (CAND) take = take && id[j] >= id_lo && id[j] < id_hi;
+            m[j] = __ballot(take);
+        }
+    } else { // row-relative positions, compared unsigned against the row length
+        const int32_t q0 = (int32_t)(wb - r.lo) + lane;
+        const uint32_t ulen = (uint32_t)len;
+#pragma unroll
+        for (int j = 0; j < CI; ++j) {
+            bool take = f[j] >= tf && (uint32_t)(q0 + j * kWave) < ulen;
+            if (CAND) take = take && id[j] >= id_lo && id[j] < id_hi;
+            m[j] = __ballot(take);
+        }
+    }
     int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < CI; ++j) {
-        bool take = f[j] >= tf;
-        if (CAND) take = take && id[j] >= id_lo && id[j] < id_hi;
-        if (!inner) {
-            const int64_t p = wb + j * kWave + lane;
-            take = take && p >= r.lo && p < r.hi;
-        }
-        m[j] = __ballot(take);
-        cnt += __popcll(m[j]);
-    }
+    for (int j = 0; j < CI; ++j) cnt += (int)__popcll(m[j]);
     if (lane == 0) wcnt[w] = cnt;
     __syncthreads();
     int base = 0, total = 0;
@@ -1007,17 +1037,22 @@ __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a
     }
     float *ov = ws.cval + (row * ws.n_chunks + chunk) * CHUNK_CAP;
     int32_t *oi = ws.cid + (row * ws.n_chunks + chunk) * CHUNK_CAP;
-    int pos = base;
+    const uint64_t lanebit = 1ull << lane;
+    const int32_t id0 = (int32_t)wb + lane; // flat rows: id = position
+    uint32_t pos = (uint32_t)base;
 #pragma unroll
     for (int j = 0; j < CI; ++j) {
-        if (m[j] == 0) continue;
-        if ((m[j] >> lane) & 1) {
-            const int s = pos + (int)__builtin_amdgcn_mbcnt_hi(
-                                    (uint32_t)(m[j] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[j], 0u));
-            ov[s] = f[j];
-            oi[s] = CAND ? id[j] : (int32_t)(wb + j * kWave + lane);
+        const uint64_t mj = m[j];
+        if (mj == 0u) continue;
+        if (mj & lanebit) {
+            const uint32_t slot = pos + __builtin_amdgcn_mbcnt_hi(
+                                            (uint32_t)(mj >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mj, 0u));
+            // 32-bit byte offsets from a wave-uniform base: scalar-base stores
+            *reinterpret_cast<float *>(reinterpret_cast<char *>(ov) + slot * 4u) = f[j];
+            *reinterpret_cast<int32_t *>(reinterpret_cast<char *>(oi) + slot * 4u) =
+                CAND ? id[j] : id0 + j * kWave;
         }
-        pos += __popcll(m[j]);
+        pos += (uint32_t)__popcll(mj);
     }
     if (threadIdx.x == 0) *cntp = total;
 }
@@ -1064,33 +1099,50 @@ __global__ __launch_bounds__(NT) void chunk_finish_kernel(SelectArgs a, ChunkWs 
         const int inc = wave_inclusive_scan(cg);
         const int off = run + inc - cg;
         run += __shfl(inc, kWave - 1, kWave);
-        // this wave copies slices g + s, s = w, w + NW, ...: loads of up to 4 rounds of 64 are
-        // issued together (clamped to the slice's first element), then written
-        for (int s = w; s < kWave && g + s < nc; s += NW) {
-            const int cs = __shfl(cg, s, kWave), os = __shfl(off, s, kWave);
-            const float *sv = ws.cval + (row * nc + g + s) * CHUNK_CAP;
-            const int32_t *si = ws.cid + (row * nc + g + s) * CHUNK_CAP;
-            for (int e0 = 0; e0 < cs; e0 += 4 * kWave) {
-                float v[4];
-                int32_t d[4];
+        // this wave copies slices g + s, s = w, w + NW, ..., two at a time, two rounds of 64
+        // entries each per pass: all of a pass's loads are issued (clamped to the slice's first
+        // entry, or to slice g + w) before any is written
+        const int ng = min(kWave, nc - g);
+        for (int s0 = w; s0 < ng; s0 += 2 * NW) {
+            int cs[2], os[2];
+            const float *sv[2];
+            const int32_t *si[2];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int e = e0 + u * kWave + lane;
-                    const int ec = e < cs ? e : 0;
-                    v[u] = sv[ec];
-                    d[u] = si[ec];
-                }
+            for (int t = 0; t < 2; ++t) {
+                const int sl = s0 + t * NW;
+                const bool ok = sl < ng;
+                cs[t] = ok ? __shfl(cg, sl, kWave) : 0;
+                os[t] = __shfl(off, ok ? sl : s0, kWave);
+                const int64_t slice = (row * nc + g + (ok ? sl : s0)) * CHUNK_CAP;
+                sv[t] = ws.cval + slice;
+                si[t] = ws.cid + slice;
+            }
+            const int cmax = max(cs[0], cs[1]);
+            for (int e0 = 0; e0 < cmax; e0 += 2 * kWave) {
+                float v[2][2];
+                int32_t d[2][2];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int e = e0 + u * kWave + lane;
-                    if (e < cs) {
-                        const uint32_t k = order_key(v[u]);
-                        sm.buf_key[os + e] = k;
-                        sm.buf_id[os + e] = d[u];
-                        kmin = min(kmin, k);
-                        kmax = max(kmax, k);
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int e = e0 + u * kWave + lane;
+                        const int ec = e < cs[t] ? e : 0;
+                        v[t][u] = sv[t][ec];
+                        d[t][u] = si[t][ec];
                     }
-                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int e = e0 + u * kWave + lane;
+                        if (e < cs[t]) {
+                            const uint32_t k = order_key(v[t][u]);
+                            sm.buf_key[os[t] + e] = k;
+                            sm.buf_id[os[t] + e] = d[t][u];
+                            kmin = min(kmin, k);
+                            kmax = max(kmax, k);
+                        }
+                    }
             }
         }
     }
