@@ -128,7 +128,7 @@ def test_scores_prefill_8k_sampled():
 
 
 # ------------------------------------------------------------------------------ selection
-@pytest.mark.parametrize("ties", ["none", "zeros", "coarse", "const"])
+@pytest.mark.parametrize("ties", ["none", "zeros", "coarse", "const", "inf"])
 def test_select_flat_exact(ties):
     rows, L = 40, 3001
     k, S, W = 96, 8, 40
@@ -180,7 +180,7 @@ def test_select_decode_128k_full_exact():
         assert np.array_equal(idx[r], expect), r
 
 
-@pytest.mark.parametrize("ties", ["none", "zeros", "coarse", "const", "ramp"])
+@pytest.mark.parametrize("ties", ["none", "zeros", "coarse", "const", "ramp", "inf"])
 def test_select_sampled_rows_exact(ties):
     """Rows longer than the LDS buffer on the one-workgroup path: the sampled threshold and its
     fallbacks (heavy ties: too many elements reach the threshold; "ramp": every pick in the last
@@ -196,7 +196,7 @@ def test_select_sampled_rows_exact(ties):
             assert np.array_equal(idx[b], expect), (ties, pos0, b)
 
 
-@pytest.mark.parametrize("ties", ["none", "zeros", "coarse", "const", "ramp"])
+@pytest.mark.parametrize("ties", ["none", "zeros", "coarse", "const", "ramp", "inf"])
 def test_select_chunked_rows_exact(ties):
     """Few long rows (the chunked path), every tie pattern: heavy ties overflow the per-chunk
     slices and fall back to one workgroup per row; rows with V <= k take everything."""

@@ -196,7 +196,7 @@ def test_select_plain_topk_matches_argpartition():
     assert np.array_equal(idx, tk)
 
 
-@pytest.mark.parametrize("ties", ["zeros", "coarse", "const", "none"])
+@pytest.mark.parametrize("ties", ["zeros", "coarse", "const", "none", "inf"])
 def test_select_sink_window_dynamic_against_lexsort(ties):
     T, L, k, S, W = 5, 700, 96, 8, 40
     s = inputs.synthetic_scores(T, L, seed=3, ties=ties).numpy()

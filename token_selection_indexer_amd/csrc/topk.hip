@@ -11,28 +11,32 @@
 // so they come out ascending without a sort.  Sink [0,S) and window [V-W,V) are written
 // arithmetically, never scored or compared.
 //
-// A sampled threshold makes the common case one pass over long rows: 64-element blocks spread
-// over the row give T (from the sampled key of a rank that puts about twice the needed count of
-// the row at or above T); every element >= T is compacted (in position order) into LDS, and the
-// exact selection runs there -- the buffer then holds every element that can be picked, ties at
-// the boundary included.  When fewer than the needed count, or more than the buffer holds, reach
-// T, the exact histogram path below runs instead, so T affects speed only.
+// Every path ends the same way: a position-ordered set of the row's elements that contains its
+// best lies in an LDS buffer (8192 entries), and the exact selection runs there.  Bins over the
+// buffer's own range are refined (first linear in the score when the keys span many binades,
+// then 11-bit digits of the key offset from the least key) until the bin holding the k-th key
+// has at most 64 keys; one wave ranks those exactly, which fixes the threshold key T and how many
+// copies of T are taken; one ordered emission writes the picks.
 //
-// Two paths:
-//  * one workgroup per row (many rows: prefill, page recall):
-//      rows of 32K and more: the sampled threshold as above; otherwise, or if it fails,
-//      1. histogram of key bits 31..21 (2048 bins in LDS) over the row;
-//      2. the bin b* holding the k-th key; bins above are taken outright;
-//      3. if bins >= b* fit in LDS, one ordered pass compacts them there and bits 20..10, 9..0
-//         are resolved in LDS; otherwise the next digit is histogrammed from the row again;
-//      4. keys > T, then the first (k - #greater) keys == T, in position order.
+// Getting the buffer:
+//  * one workgroup per row (many rows: prefill, page recall; also a fallback of the chunked
+//    path):
+//      rows that fit the buffer are copied into it as they are;
+//      rows of 16K and more: a sampled threshold T (64-element blocks spread over the row; T is
+//      the sampled key of a rank that puts about twice the needed count of the row at or above
+//      it) lets one ordered pass compact every element >= T, ties at the boundary included;
+//      otherwise, or when fewer than the needed count or more than the buffer holds reach T, a
+//      histogram of key bits 31..21 over the row finds the bin of the k-th key and one ordered
+//      pass compacts the bins at and above it (with heavy ties beyond the buffer, further digits
+//      are histogrammed from the row and the picks written directly).
 //  * chunked (few long rows: decode): the row is cut into 4096-element chunks, one workgroup
 //    each, so a handful of rows still fills the chip:
 //      collect   every chunk derives the row's sampled threshold (the same in every chunk) and
 //                compacts its elements >= T (in order) into its own slice of the workspace
 //      finish    one workgroup per row concatenates the slices (chunk order = position order)
-//                into LDS and selects exactly there; a row whose slices overflowed, or hold
-//                fewer than the needed count, falls back to the one-workgroup path over the row.
+//                into the buffer; a row whose slices overflowed, or hold fewer than the needed
+//                count, falls back to the one-workgroup path over the row.
+// A threshold only ever decides what reaches the buffer, never the result.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -44,7 +48,7 @@ constexpr int CAP = 8192;           // LDS candidate buffer entries (key, id)
 constexpr int CHUNK = 4096;         // chunked path: elements per workgroup
 constexpr int CHUNK_CAP = 512;      // chunked path: candidates kept per chunk
 constexpr int CNT_THREADS = 256;    // chunked path: threads per chunk workgroup
-constexpr int64_t SAMPLE_MIN = 32768; // one-workgroup rows at least this long use the sample
+constexpr int64_t SAMPLE_MIN = 16384; // one-workgroup rows at least this long use the sample
 
 // ------------------------------------------------------------------------------------------
 // Row access
@@ -391,8 +395,8 @@ struct Smem {
     int scratch[NW + 8];
     int cnt[ITEMS * NW];
     alignas(16) uint32_t small[kWave];
-    uint32_t buf_key[CAP];
-    int32_t buf_id[CAP];
+    alignas(16) uint32_t buf_key[CAP];
+    alignas(16) int32_t buf_id[CAP];
 };
 
 __device__ __forceinline__ int64_t round_begin(const Row &r) { return r.lo; }
@@ -419,20 +423,6 @@ __device__ __forceinline__ void hist_row(Smem &sm, const Row &r, int shift, int 
             if (pbits && (hs >= 32 ? 0u : (key >> hs)) != prefix) continue;
             atomicAdd(&sm.hist[(key >> shift) & (uint32_t)(nbins - 1)], 1);
         }
-    }
-    __syncthreads();
-}
-
-// pbits == 0: every buffered key counts (the level-0 digit).
-__device__ __forceinline__ void hist_buf(Smem &sm, int nbuf, int shift, int nbins, uint32_t prefix,
-                                         int pbits = 1)
-{
-    clear_hist(sm);
-    const int hs = shift + __builtin_ctz((unsigned)nbins);
-    for (int i = threadIdx.x; i < nbuf; i += NT) {
-        const uint32_t key = sm.buf_key[i];
-        if (pbits && (key >> hs) != prefix) continue;
-        atomicAdd(&sm.hist[(key >> shift) & (uint32_t)(nbins - 1)], 1);
     }
     __syncthreads();
 }
@@ -477,88 +467,103 @@ __device__ __forceinline__ int select_row(Smem &sm, const Row &r, uint32_t T, in
     return taken; // may exceed limit: only the first `limit` were written
 }
 
-// The same over the LDS buffer (already in position order).  Wave w takes the contiguous
-// entries [512w, 512(w+1)) (item j of lane l: + 64j + l), so one exchange of per-wave counts
-// orders the picks.  eq_all: every key == T is taken (eq_take is
-// their count).
-__device__ __forceinline__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq_take, int32_t *dst,
-                                          int limit, bool eq_all = false)
+// The LDS buffer is worked on from registers: with span = 64 * ceil(nbuf / (64 NW)), thread
+// (wave w, lane l) holds entries span*w + 64u + l for u < span/64 (<= BI), so every wave has a
+// like share and position order is (wave, u, lane).  Items past span/64 hold key 0.
+constexpr int BI = CAP / NT;
+__device__ __forceinline__ int buf_items(int nbuf) { return (nbuf + NW * kWave - 1) / (NW * kWave); }
+__device__ __forceinline__ int buf_index(int nu, int u) { return (wave_id() * nu + u) * kWave + lane_id(); }
+
+__device__ __forceinline__ void load_keys(const Smem &sm, int nbuf, uint32_t (&k)[BI])
 {
-    constexpr int BI = CAP / NT; // items per lane: one round covers the buffer
-    constexpr int WSPAN = BI * kWave;
-    const int lane = lane_id(), w = wave_id();
-    int taken = 0, eq_seen = 0;
-    for (int base = 0; base < nbuf; base += NT * BI) {
-        const int i0 = base + w * WSPAN + lane;
-        uint64_t mg[BI], me[BI];
-        int cg = 0, ce = 0;
+    const int nu = buf_items(nbuf);
 #pragma unroll
-        for (int j = 0; j < BI; ++j) {
-            const int i = i0 + j * kWave;
-            const uint32_t key = i < nbuf ? sm.buf_key[i] : 0u;
-            mg[j] = __ballot(eq_all ? (key != 0u && key >= T) : key > T);
-            me[j] = eq_all ? 0u : __ballot(key != 0u && key == T);
-            cg += (int)__popcll(mg[j]);
-            ce += (int)__popcll(me[j]);
-        }
-        if (lane == 0) {
-            sm.cnt[w] = cg;
-            sm.cnt[NW + w] = ce;
-        }
-        __syncthreads();
-        // lane k < NW holds wave k's counts; prefix sums give this wave's bases
-        const int wu = __builtin_amdgcn_readfirstlane(w);
-        const int ck = lane < NW ? sm.cnt[lane] : 0, ek = lane < NW ? sm.cnt[NW + lane] : 0;
-        const int ick = wave_inclusive_scan(ck), iek = wave_inclusive_scan(ek);
-        const int bg = __builtin_amdgcn_readlane(ick, wu) - __builtin_amdgcn_readlane(ck, wu);
-        const int be = __builtin_amdgcn_readlane(iek, wu) - __builtin_amdgcn_readlane(ek, wu);
-        const int tg = __builtin_amdgcn_readlane(ick, NW - 1);
-        const int te = __builtin_amdgcn_readlane(iek, NW - 1);
-        // equal keys of earlier waves that are taken: global equal ranks [eq_seen, eq_seen + be)
-        auto eq_taken = [&](int before) { return max(0, min(eq_take - eq_seen, before)); };
-        int pos = taken + bg + eq_taken(be);
-        int er = eq_seen + be; // equal rank of the wave's next equal key
-#pragma unroll
-        for (int j = 0; j < BI; ++j) {
-            uint64_t mt = mg[j];
-            if (me[j]) {
-                const int r = er + (int)__builtin_amdgcn_mbcnt_hi(
-                                       (uint32_t)(me[j] >> 32),
-                                       __builtin_amdgcn_mbcnt_lo((uint32_t)me[j], 0u));
-                mt |= __ballot(((me[j] >> lane) & 1u) && r < eq_take);
-                er += (int)__popcll(me[j]);
-            }
-            if ((mt >> lane) & 1u) {
-                const int slot = pos + (int)__builtin_amdgcn_mbcnt_hi(
-                                           (uint32_t)(mt >> 32),
-                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mt, 0u));
-                if (slot < limit) dst[slot] = sm.buf_id[i0 + j * kWave];
-            }
-            pos += (int)__popcll(mt);
-        }
-        taken += tg + eq_taken(te);
-        eq_seen += te;
-        if (base + NT * BI < nbuf) __syncthreads(); // sm.cnt is rewritten by the next round
+    for (int u = 0; u < BI; ++u) {
+        const int i = buf_index(nu, u);
+        k[u] = u < nu && i < nbuf ? sm.buf_key[i] : 0u;
     }
-    return taken;
 }
 
-// The buffer holds, in position order, every element whose top `pbits` key bits are >= prefix
-// (pbits == 11).  Resolve the remaining digits and emit `need` picks.
-__device__ __forceinline__ void finish_in_buf(Smem &sm, int nbuf, uint32_t prefix, int need_rem,
-                                              int32_t *dst, int need)
+// Ordered emission from the buffer (keys k as load_keys gives them): key > T, then the first
+// eq_take keys == T in position order, into dst[0, limit).  Key 0 never competes.  eq_all: every
+// key == T is taken (eq_take is their count), i.e. simply key >= T.  One exchange of per-wave
+// counts orders the picks.  Returns the number taken (which may exceed limit).
+__device__ __forceinline__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq_take, int32_t *dst,
+                                          int limit, bool eq_all, const uint32_t (&k)[BI])
 {
-    const int shifts[2] = {10, 0};
-    const int bitsv[2] = {11, 10};
-    int at = 0;
-    for (int lvl = 0; lvl < 2; ++lvl) {
-        hist_buf(sm, nbuf, shifts[lvl], 1 << bitsv[lvl], prefix);
-        const Digit g = find_digit<NT>(sm.hist, 1 << bitsv[lvl], need_rem, sm.scratch);
-        prefix = (prefix << bitsv[lvl]) | (uint32_t)g.d;
-        need_rem -= g.above;
-        at = g.at;
+    const int lane = lane_id(), w = wave_id();
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int nu = buf_items(nbuf);
+    int32_t idv[BI];
+#pragma unroll
+    for (int u = 0; u < BI; ++u) {
+        const int i = buf_index(nu, u);
+        idv[u] = u < nu && i < nbuf ? sm.buf_id[i] : 0;
     }
-    select_buf(sm, nbuf, prefix, need_rem, dst, need, need_rem == at);
+    auto put = [&](uint32_t slot, int32_t v) { // 32-bit offset from the uniform base
+        if (slot < (uint32_t)limit) *reinterpret_cast<int32_t *>(reinterpret_cast<char *>(dst) + slot * 4u) = v;
+    };
+    auto below = [](uint64_t m) {
+        return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    };
+    if (eq_all) {
+        uint64_t mg[BI];
+        int cg = 0;
+#pragma unroll
+        for (int u = 0; u < BI; ++u) {
+            mg[u] = __ballot(k[u] != 0u && k[u] >= T);
+            cg += (int)__popcll(mg[u]);
+        }
+        if (lane == 0) sm.cnt[w] = cg;
+        __syncthreads();
+        // lane q < NW holds wave q's count; the prefix sum gives this wave's base
+        const int ck = lane < NW ? sm.cnt[lane] : 0;
+        const int ick = wave_inclusive_scan(ck);
+        uint32_t pos = (uint32_t)(__builtin_amdgcn_readlane(ick, wu) - __builtin_amdgcn_readlane(ck, wu));
+#pragma unroll
+        for (int u = 0; u < BI; ++u) {
+            if (u >= nu) break;
+            if (k[u] != 0u && k[u] >= T) put(pos + below(mg[u]), idv[u]);
+            pos += (uint32_t)__popcll(mg[u]);
+        }
+        return __builtin_amdgcn_readlane(ick, NW - 1);
+    }
+    uint64_t mg[BI], me[BI];
+    int cg = 0, ce = 0;
+#pragma unroll
+    for (int u = 0; u < BI; ++u) {
+        mg[u] = __ballot(k[u] > T);
+        me[u] = __ballot(k[u] != 0u && k[u] == T);
+        cg += (int)__popcll(mg[u]);
+        ce += (int)__popcll(me[u]);
+    }
+    if (lane == 0) {
+        sm.cnt[w] = cg;
+        sm.cnt[NW + w] = ce;
+    }
+    __syncthreads();
+    const int ck = lane < NW ? sm.cnt[lane] : 0, ek = lane < NW ? sm.cnt[NW + lane] : 0;
+    const int ick = wave_inclusive_scan(ck), iek = wave_inclusive_scan(ek);
+    const int bg = __builtin_amdgcn_readlane(ick, wu) - __builtin_amdgcn_readlane(ck, wu);
+    const int be = __builtin_amdgcn_readlane(iek, wu) - __builtin_amdgcn_readlane(ek, wu);
+    const int tg = __builtin_amdgcn_readlane(ick, NW - 1);
+    const int te = __builtin_amdgcn_readlane(iek, NW - 1);
+    // equal keys of earlier waves that are taken: equal ranks [0, be)
+    int pos = bg + max(0, min(eq_take, be));
+    int er = be; // equal rank of the wave's next equal key
+#pragma unroll
+    for (int u = 0; u < BI; ++u) {
+        if (u >= nu) break;
+        uint64_t mt = mg[u];
+        if (me[u]) {
+            const int r = er + (int)below(me[u]);
+            mt |= __ballot(((me[u] >> lane) & 1u) && r < eq_take);
+            er += (int)__popcll(me[u]);
+        }
+        if ((mt >> lane) & 1u) put((uint32_t)pos + below(mt), idv[u]);
+        pos += (int)__popcll(mt);
+    }
+    return tg + max(0, min(eq_take, te));
 }
 
 // Wave-wide unsigned min / max in the DPP steps of wave_inclusive_scan (lane 63 ends with the
@@ -577,40 +582,100 @@ __device__ __forceinline__ uint32_t wave_reduce_u(uint32_t x)
     return (uint32_t)__builtin_amdgcn_readlane((int)x, kWave - 1);
 }
 
-// The buffer holds, in position order, a set of elements that contains the row's `need` best,
-// nbuf > need of them, with keys in [kmin, kmax].  Emit exactly the `need` best.  On entry
-// sm.hist, sm.small and sm.scratch[NW + 4] are zero and a barrier has passed since.
+// The buffer holds nbuf entries in position order; its competing elements (key != 0; entries
+// with key 0 do not compete) include the row's `need` best.  kmin / kmax: the least and greatest
+// nonzero key (kmin > kmax when there is none).  Emit exactly the `need` best (all competing
+// ones, padded with -1, if there are at most `need`).  On entry sm.hist, sm.small and
+// sm.scratch[NW + 4] are zero and a barrier has passed since.
 //
-// Level 0 bins the buffer over its own key range, digit (key - kmin) >> s with the smallest s
-// that fits 2048 bins, so the bins spread evenly however narrow the range.  When the bin holding
-// the need-th key has at most 64 keys, one wave ranks them exactly; otherwise two more digits of
-// the key are resolved as usual.
+// Bins are refined until the bin holding the need-th key has at most 64 keys, which one wave
+// then ranks exactly.  The first level is linear in the score over [min, max] when the keys
+// span more than a few binades and both ends and the span are finite (a monotone digit, so bins
+// stay small even where a whole score distribution crowds a few exponents).  Further levels take digits of rel = key - kmin:
+// rel >> s0 with the smallest s0 that fits 2048 bins, then the next (up to) 11 bits below, each
+// among the keys of the bins chosen so far -- down to a single key value if need be, of which
+// the needed count of copies is taken.
 __device__ __forceinline__ void select_in_buf_range(Smem &sm, int nbuf, int need, int32_t *dst,
-                                                    uint32_t kmin, uint32_t kmax)
+                                                    uint32_t kmin, uint32_t kmax,
+                                                    const uint32_t (&k)[BI])
 {
-    const uint32_t range = kmax - kmin;
-    const int s = range ? max(0, 32 - (int)__builtin_clz(range) - 11) : 0;
-    for (int i = threadIdx.x; i < nbuf; i += NT) atomicAdd(&sm.hist[(sm.buf_key[i] - kmin) >> s], 1);
-    __syncthreads();
-    const Digit g = find_digit_w0<NT>(sm.hist, need, sm.scratch);
-    if (g.at <= kWave) {
-        uint32_t *small = sm.small;
-        for (int i = threadIdx.x; i < nbuf; i += NT) {
-            const uint32_t k = sm.buf_key[i];
-            if (((k - kmin) >> s) == (uint32_t)g.d) small[atomicAdd(&sm.scratch[NW + 4], 1)] = k;
+    const float fmin = key_to_float(kmin), fmax = key_to_float(kmax);
+    const float span = fmax - fmin;
+    // (over at most a few binades, 11-bit digits of the key are as fine as linear bins)
+    const bool lin = kmin < kmax && (kmax - kmin) >= (1u << 24) && fmin > -INFINITY &&
+                     fmax < INFINITY && span > 0.0f && span < INFINITY;
+    const float scale = lin ? (float)NBIN / span : 0.0f;
+    auto fdigit = [&](uint32_t k) {
+        return (uint32_t)min(NBIN - 1, (int)((key_to_float(k) - fmin) * scale));
+    };
+    const uint32_t range = kmin <= kmax ? kmax - kmin : 0u;
+    const int nu = buf_items(nbuf); // items held per thread (the rest are key 0)
+    bool lin_done = false;          // the linear level has chosen bin fd
+    uint32_t fd = 0u;
+    int key_lvls = 0, sh = 0;       // key levels applied; the last one's shift
+    uint32_t pref = 0u;             // ... and the chosen rel >> sh
+    int next_sh = range ? max(0, 32 - (int)__builtin_clz(range) - 11) : 0, next_hi = 32;
+    auto in_bin = [&](uint32_t k) {
+        return (!lin_done || fdigit(k) == fd) && (key_lvls == 0 || ((k - kmin) >> sh) == pref);
+    };
+    int rem = need;
+    bool take_all = false;
+    Digit g;
+    for (bool first = true;; first = false) {
+        const bool use_lin = lin && !lin_done;
+        const uint32_t dmask = next_hi == 32 ? ~0u : (1u << (next_hi - next_sh)) - 1u;
+#pragma unroll
+        for (int u = 0; u < BI; ++u)
+            if (u < nu && k[u] != 0u && in_bin(k[u]))
+                atomicAdd(&sm.hist[use_lin ? fdigit(k[u]) : ((k[u] - kmin) >> next_sh) & dmask], 1);
+        __syncthreads();
+        g = find_digit_w0<NT>(sm.hist, rem, sm.scratch);
+        if (first && g.total <= need) { // at most `need` compete: all of them, then -1
+            take_all = true;
+            break;
         }
+        rem -= g.above;
+        if (use_lin) {
+            lin_done = true;
+            fd = (uint32_t)g.d;
+        } else {
+            pref = key_lvls == 0 ? (uint32_t)g.d : (pref << (next_hi - next_sh)) | (uint32_t)g.d;
+            sh = next_sh;
+            ++key_lvls;
+            next_hi = next_sh;
+            next_sh = max(0, next_sh - 11);
+        }
+        if (g.at <= kWave || (key_lvls > 0 && sh == 0)) break;
+        int4 *h4 = reinterpret_cast<int4 *>(sm.hist);
+        for (int i = threadIdx.x; i < NBIN / 4; i += NT) h4[i] = make_int4(0, 0, 0, 0);
         __syncthreads();
-        if (threadIdx.x < kWave) rank_small(small, g.at, need - g.above, sm.scratch + NW + 5);
-        __syncthreads();
-        const uint32_t T = (uint32_t)sm.scratch[NW + 5];
-        const int eq_take = sm.scratch[NW + 6];
-        const bool eq_all = sm.scratch[NW + 7] != 0;
-        select_buf(sm, nbuf, T, eq_take, dst, need, eq_all);
-        return;
     }
-    hist_buf(sm, nbuf, 21, NBIN, 0u, 0);
-    const Digit h = find_digit<NT>(sm.hist, NBIN, need, sm.scratch);
-    finish_in_buf(sm, nbuf, (uint32_t)h.d, need - h.above, dst, need);
+    uint32_t T;
+    int eq_take;
+    bool eq_all;
+    if (take_all) {
+        T = 1u;
+        eq_take = 0;
+        eq_all = true;
+    } else if (g.at <= kWave) { // rank the bin's keys: the rem-th largest is the need-th
+        uint32_t *small = sm.small;
+#pragma unroll
+        for (int u = 0; u < BI; ++u)
+            if (u < nu && k[u] != 0u && in_bin(k[u])) small[atomicAdd(&sm.scratch[NW + 4], 1)] = k[u];
+        __syncthreads();
+        if (threadIdx.x < kWave) rank_small(small, g.at, rem, sm.scratch + NW + 5);
+        __syncthreads();
+        T = (uint32_t)sm.scratch[NW + 5];
+        eq_take = sm.scratch[NW + 6];
+        eq_all = sm.scratch[NW + 7] != 0;
+    } else { // the bin is one key value (sh == 0): rem of its g.at copies are taken
+        T = kmin + pref;
+        eq_take = rem;
+        eq_all = rem == g.at;
+    }
+    const int got = select_buf(sm, nbuf, T, eq_take, dst, need, eq_all, k);
+    if (take_all)
+        for (int i = min(got, need) + (int)threadIdx.x; i < need; i += NT) dst[i] = -1;
 }
 
 // Per-wave extremes -> LDS (the caller's next barrier publishes them); read back with
@@ -642,26 +707,25 @@ __device__ __forceinline__ void clear_hist_nobar(Smem &sm)
     if (threadIdx.x == 0) sm.scratch[NW + 4] = 0;
 }
 
-// The buffer holds, in position order, a set of elements that contains the row's `need` best.
-// Emit exactly those (all of them, padded with -1, if there are at most `need`).
-__device__ __forceinline__ void select_in_buf(Smem &sm, int nbuf, int need, int32_t *dst)
+// The buffer holds nbuf entries in position order whose competing elements (key != 0) include
+// the row's `need` best, and a barrier has passed since its last write.  Emit exactly those (all
+// competing ones, padded with -1, if there are at most `need`).
+__device__ __forceinline__ void select_from_buf(Smem &sm, int nbuf, int need, int32_t *dst)
 {
-    if (nbuf <= need) {
-        const int got = select_buf(sm, nbuf, 0u, 0, dst, need);
-        for (int i = got + (int)threadIdx.x; i < need; i += NT) dst[i] = -1;
-        return;
-    }
+    uint32_t k[BI];
+    load_keys(sm, nbuf, k);
     uint32_t kmin = ~0u, kmax = 0u;
-    for (int i = threadIdx.x; i < nbuf; i += NT) {
-        const uint32_t k = sm.buf_key[i];
-        kmin = min(kmin, k);
-        kmax = max(kmax, k);
-    }
+#pragma unroll
+    for (int u = 0; u < BI; ++u)
+        if (k[u] != 0u) {
+            kmin = min(kmin, k[u]);
+            kmax = max(kmax, k[u]);
+        }
     wave_extremes(sm, kmin, kmax);
     clear_hist_nobar(sm);
     __syncthreads();
     block_extremes(sm, kmin, kmax);
-    select_in_buf_range(sm, nbuf, need, dst, kmin, kmax);
+    select_in_buf_range(sm, nbuf, need, dst, kmin, kmax, k);
 }
 
 // ---- streaming passes: each wave owns a contiguous segment of the row (no block barriers) ----
@@ -809,11 +873,31 @@ __device__ __forceinline__ bool collect_row_seg(Smem &sm, const Row &r, uint32_t
     return true;
 }
 
-// Select `need` elements of the row by (key desc, position asc) into dst, ascending; pad -1.
-__device__ __forceinline__ void select_top(Smem &sm, const Row &r, int need, int32_t *dst)
+// Gathers into the LDS buffer a position-ordered set of the row's elements that contains its
+// `need` best (need > 0) and returns its size, with a barrier passed after the last write -- or
+// completes the row itself (everything competing taken, or heavy ties) and returns -1.
+__device__ __forceinline__ int prepare_buf(Smem &sm, const Row &r, int need, int32_t *dst)
 {
-    if (need <= 0) return;
     const int64_t len = r.hi - r.lo;
+    // rows that fit the buffer are copied there as they are (key 0 where an element does not
+    // compete): entry i holds position a0 + i
+    const int64_t a0 = r.lo & ~int64_t(3);
+    if (r.hi - a0 <= CAP) {
+        const int n4 = (int)((r.hi - a0 + 3) & ~int64_t(3));
+#pragma unroll
+        for (int u = 0; u < CAP / (4 * NT); ++u) {
+            const int i = 4 * ((int)threadIdx.x + u * NT);
+            if (i < n4) {
+                uint32_t key[4];
+                int32_t id[4];
+                elem4(r, a0 + i, key, id, r.hi);
+                *reinterpret_cast<uint4 *>(&sm.buf_key[i]) = make_uint4(key[0], key[1], key[2], key[3]);
+                *reinterpret_cast<int4 *>(&sm.buf_id[i]) = make_int4(id[0], id[1], id[2], id[3]);
+            }
+        }
+        __syncthreads();
+        return n4;
+    }
     // long rows: a sampled threshold lets one pass collect everything at or above it
     const uint32_t T = len >= SAMPLE_MIN
                            ? sample_threshold<NT, 4>(sm.hist, sm.scratch, sm.small, r, need, len)
@@ -826,31 +910,26 @@ __device__ __forceinline__ void select_top(Smem &sm, const Row &r, int need, int
             __syncthreads();
             ok = true;
         }
-        if (ok && nbuf >= need) {
-            select_in_buf(sm, nbuf, need, dst);
-            return;
-        }
+        if (ok && nbuf >= need) return nbuf;
     }
     // exact histogram path
     hist_row_seg(sm, r);
-    Digit g = find_digit<NT>(sm.hist, NBIN, need, sm.scratch);
+    Digit g = find_digit_w0<NT>(sm.hist, need, sm.scratch);
     if (g.total <= need) { // everything competes: take all, pad
         const int got = min(select_row(sm, r, 0u, 0, dst, false, need), need);
         for (int i = got + (int)threadIdx.x; i < need; i += NT) dst[i] = -1;
-        return;
+        return -1;
     }
     uint32_t prefix = (uint32_t)g.d;
     int pbits = 11;
     int need_rem = need - g.above;
-    int taken_above = g.above, at = g.at;
-    if (taken_above + at <= CAP) {
+    if (g.above + g.at <= CAP) { // the buffer takes bins >= d: the need best
         int nbuf, total;
         if (!collect_row_seg(sm, r, prefix << 21, nbuf, total)) { // uneven segments: ordered pass
             nbuf = select_row(sm, r, prefix << 21, INT32_MAX, nullptr, true, CAP);
             __syncthreads();
         }
-        finish_in_buf(sm, nbuf, prefix, need_rem, dst, need);
-        return;
+        return nbuf;
     }
     // heavy ties: refine the threshold from the row itself
     const int shifts[2] = {10, 0};
@@ -861,9 +940,9 @@ __device__ __forceinline__ void select_top(Smem &sm, const Row &r, int need, int
         prefix = (prefix << bitsv[lvl]) | (uint32_t)h.d;
         pbits += bitsv[lvl];
         need_rem -= h.above;
-        taken_above += h.above;
     }
     select_row(sm, r, prefix, need_rem, dst, false, need);
+    return -1;
 }
 
 // Row setup shared by both paths.  Returns false when the row needs no selection (all of it
@@ -923,7 +1002,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
     int32_t *dst;
     int need;
     if (!setup_row(a, blockIdx.x, r, dst, need, true)) return;
-    select_top(sm, r, need, dst);
+    const int nbuf = prepare_buf(sm, r, need, dst);
+    if (nbuf >= 0) select_from_buf(sm, nbuf, need, dst);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1087,74 +1167,63 @@ __global__ __launch_bounds__(NT) void chunk_finish_kernel(SelectArgs a, ChunkWs 
     }
     // the same in every wave: every element >= T of the row sits in the slices, which hold at
     // least `need` elements and fit the buffer -- else the one-workgroup path over the row
+    int nbuf = total;
     if (__ballot(bad) != 0 || total > CAP || total < need) {
-        select_top(sm, r, need, dst);
-        return;
-    }
-    clear_hist_nobar(sm);
-    uint32_t kmin = ~0u, kmax = 0u;
-    int run = 0;
-    for (int g = 0; g < nc; g += kWave) {
-        const int cg = g == 0 ? cfirst : (g + lane < nc ? counts[g + lane] : 0);
-        const int inc = wave_inclusive_scan(cg);
-        const int off = run + inc - cg;
-        run += __shfl(inc, kWave - 1, kWave);
-        // this wave copies slices g + s, s = w, w + NW, ..., two at a time, two rounds of 64
-        // entries each per pass: all of a pass's loads are issued (clamped to the slice's first
-        // entry, or to slice g + w) before any is written
-        const int ng = min(kWave, nc - g);
-        for (int s0 = w; s0 < ng; s0 += 2 * NW) {
-            int cs[2], os[2];
-            const float *sv[2];
-            const int32_t *si[2];
+        nbuf = prepare_buf(sm, r, need, dst);
+    } else {
+        int run = 0;
+        for (int g = 0; g < nc; g += kWave) {
+            const int cg = g == 0 ? cfirst : (g + lane < nc ? counts[g + lane] : 0);
+            const int inc = wave_inclusive_scan(cg);
+            const int off = run + inc - cg;
+            run += __shfl(inc, kWave - 1, kWave);
+            // this wave copies slices g + s, s = w, w + NW, ..., two at a time, two rounds of 64
+            // entries each per pass: all of a pass's loads are issued (clamped to the slice's first
+            // entry, or to slice g + w) before any is written
+            const int ng = min(kWave, nc - g);
+            for (int s0 = w; s0 < ng; s0 += 2 * NW) {
+                int cs[2], os[2];
+                const float *sv[2];
+                const int32_t *si[2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int sl = s0 + t * NW;
-                const bool ok = sl < ng;
-                cs[t] = ok ? __shfl(cg, sl, kWave) : 0;
-                os[t] = __shfl(off, ok ? sl : s0, kWave);
-                const int64_t slice = (row * nc + g + (ok ? sl : s0)) * CHUNK_CAP;
-                sv[t] = ws.cval + slice;
-                si[t] = ws.cid + slice;
-            }
-            const int cmax = max(cs[0], cs[1]);
-            for (int e0 = 0; e0 < cmax; e0 += 2 * kWave) {
-                float v[2][2];
-                int32_t d[2][2];
+                for (int t = 0; t < 2; ++t) {
+                    const int sl = s0 + t * NW;
+                    const bool ok = sl < ng;
+                    cs[t] = ok ? __shfl(cg, sl, kWave) : 0;
+                    os[t] = __shfl(off, ok ? sl : s0, kWave);
+                    const int64_t slice = (row * nc + g + (ok ? sl : s0)) * CHUNK_CAP;
+                    sv[t] = ws.cval + slice;
+                    si[t] = ws.cid + slice;
+                }
+                const int cmax = max(cs[0], cs[1]);
+                for (int e0 = 0; e0 < cmax; e0 += 2 * kWave) {
+                    float v[2][2];
+                    int32_t d[2][2];
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                    for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int e = e0 + u * kWave + lane;
-                        const int ec = e < cs[t] ? e : 0;
-                        v[t][u] = sv[t][ec];
-                        d[t][u] = si[t][ec];
-                    }
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int e = e0 + u * kWave + lane;
-                        if (e < cs[t]) {
-                            const uint32_t k = order_key(v[t][u]);
-                            sm.buf_key[os[t] + e] = k;
-                            sm.buf_id[os[t] + e] = d[t][u];
-                            kmin = min(kmin, k);
-                            kmax = max(kmax, k);
+                        for (int u = 0; u < 2; ++u) {
+                            const int e = e0 + u * kWave + lane;
+                            const int ec = e < cs[t] ? e : 0;
+                            v[t][u] = sv[t][ec];
+                            d[t][u] = si[t][ec];
                         }
-                    }
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int e = e0 + u * kWave + lane;
+                            if (e < cs[t]) {
+                                sm.buf_key[os[t] + e] = order_key(v[t][u]);
+                                sm.buf_id[os[t] + e] = d[t][u];
+                            }
+                        }
+                }
             }
         }
-    }
-    if (total <= need) { // exactly `need` (total >= need): take them all
         __syncthreads();
-        select_in_buf(sm, total, need, dst);
-        return;
     }
-    wave_extremes(sm, kmin, kmax);
-    __syncthreads();
-    block_extremes(sm, kmin, kmax);
-    select_in_buf_range(sm, total, need, dst, kmin, kmax);
+    if (nbuf >= 0) select_from_buf(sm, nbuf, need, dst);
 }
 
 bool use_chunked(const SelectArgs &a)

@@ -116,7 +116,8 @@ def synthetic_scores(rows: int, n: int, seed: int, ties: str = "none", device="c
     """Score rows for selection tests.  ties: "none" (continuous N(0,1)), "zeros" (a third of the
     entries exactly +0 or -0), "coarse" (values on a grid of 17 levels: heavy exact ties),
     "const" (every entry equal), "ramp" (rising with position plus small noise: the best
-    entries all sit at the end of the row)."""
+    entries all sit at the end of the row), "inf" (1% of the entries +inf, 2% -inf: infinite
+    scores still compete, +inf above and -inf below every finite one)."""
     x = _randn((rows, n), device, seed, "scores")
     if ties == "zeros":
         g = _gen(device, seed, "scores", 1)
@@ -129,6 +130,11 @@ def synthetic_scores(rows: int, n: int, seed: int, ties: str = "none", device="c
         x = torch.full_like(x, 0.75)
     elif ties == "ramp":
         x = torch.linspace(-1.0, 1.0, n, device=device).unsqueeze(0) + 0.01 * x
+    elif ties == "inf":
+        g = _gen(device, seed, "scores", 2)
+        m = torch.rand((rows, n), generator=g, device=device)
+        x = torch.where(m < 0.01, torch.full_like(x, float("inf")), x)
+        x = torch.where((m >= 0.01) & (m < 0.03), torch.full_like(x, float("-inf")), x)
     return x.contiguous()
 
 
