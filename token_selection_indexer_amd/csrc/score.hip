@@ -27,6 +27,9 @@
 //   r' = 16*MT*g + 16*mt + r,   (query slot, head) = (r' / H, r' % H)
 // so with 16*MT >= H every lane holds whole queries and the head sum stays in the lane; with
 // H = 32*MT the two halves each hold half of one query's heads and one cross-half add finishes.
+#include <algorithm>
+#include <type_traits>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -199,16 +202,17 @@ struct KeyBlock {
     }
 };
 
-// PD: blocks prefetched ahead of the one being computed (register ring of PD + 1 blocks).  The
-// block loop is fully unrolled: every ring slot and LDS slab index is a compile-time constant and
-// consecutive blocks' instructions can interleave.
+// PD: blocks prefetched ahead of the one being computed (register ring of PD + 1 blocks).
+// BPW > 0: each wave takes BPW blocks, the block loop fully unrolled.  BPW == 0: each wave takes
+// ceil(blocks / (gridDim.x * WAVES)) blocks in a loop whose body is one turn of the ring, so
+// every ring slot is still a compile-time constant while the code stays one ring long.
 template <bool FP8, int D, int H, int MT, bool ONEQ, bool FINE, int WAVES, int BPW, int PD = 1>
 __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
 {
     using G = Geo<H, MT, ONEQ>;
     using KB = KeyBlock<FP8, D>;
     constexpr int KS = D / 16;
-    static_assert(PD >= 1 && PD < BPW, "ring shape");
+    static_assert(PD >= 1 && (BPW == 0 || PD < BPW), "ring shape");
     // two slabs per wave: block i is transposed in slab i&1 while block i-1 may still be read
     __shared__ __attribute__((aligned(16))) uint8_t slabs[WAVES][2][KB::BB];
     const int b = blockIdx.z;
@@ -260,6 +264,9 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
     const float *scale_b = FP8 ? a.kscale + (int64_t)b * a.n_keys : nullptr;
     const int32_t *pages_row = FINE ? a.pages + ((int64_t)b * a.n_q + t0) * a.m_pages : nullptr;
     const int64_t n_blocks = (a.n_out + 31) / 32;
+    // blocks per wave; the workgroup's waves interleave over its contiguous range of blocks
+    const int bpw = BPW ? BPW : (int)((n_blocks + (int64_t)gridDim.x * WAVES - 1) /
+                                      ((int64_t)gridDim.x * WAVES));
     // this lane's byte offsets inside a block (contiguous 1 KB pieces)
     uint32_t lane_off[KB::NP];
 #pragma unroll
@@ -272,10 +279,21 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         int64_t s0, row0; // first output slot and first key row of the block
         bool valid, live;
     };
+    // BPW == 0 (flat rows, n_out == n_keys >= 32): every block is loaded in full and without a
+    // branch, since a conditional load makes the compiler drain all loads in flight where the
+    // branches merge.  The last block is moved back to end at the last key (its rows overlap
+    // the previous block's, whose scores it rewrites identically); blocks past the end reload
+    // the last one and are not computed.
+    constexpr bool FLAT_LOOP = BPW == 0 && !FINE;
     auto locate = [&](int it) {
         Blk k;
-        const int64_t blk = ((int64_t)blockIdx.x * BPW + it) * WAVES + wv_id;
+        const int64_t blk = ((int64_t)blockIdx.x * bpw + it) * WAVES + wv_id;
         k.valid = blk < n_blocks;
+        if constexpr (FLAT_LOOP) {
+            k.s0 = k.row0 = min(blk * 32, a.n_keys - 32);
+            k.live = k.valid && k.s0 < hi_all && k.s0 + 32 > lo_all;
+            return k;
+        }
         k.s0 = blk * 32;
         k.live = false;
         k.row0 = 0;
@@ -292,6 +310,13 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         return k;
     };
     auto fetch = [&](const Blk &k, KB &kb, float &sc) {
+        if constexpr (FLAT_LOOP) {
+            const uint8_t *base = keys_b + k.row0 * KB::RB;
+#pragma unroll
+            for (int i = 0; i < KB::NP; ++i) kb.raw[i] = ld16(base + lane_off[i]);
+            if (FP8) sc = scale_b[k.row0 + n];
+            return;
+        }
         if (!k.live) return;
         if (k.row0 + 32 <= a.n_keys) {
             const uint8_t *base = keys_b + k.row0 * KB::RB;
@@ -309,15 +334,19 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
     float sq[PD + 1];
     static_for<0, PD>([&](auto I) {
         constexpr int i = decltype(I)::value;
-        bq[i] = locate(i);
+        bq[i] = locate(FLAT_LOOP ? min(i, bpw - 1) : i);
         sq[i] = 1.0f;
         fetch(bq[i], kq[i], sq[i]);
     });
-    static_for<0, BPW>([&](auto IT) {
-        constexpr int it = decltype(IT)::value;
-        constexpr int cs = it % (PD + 1);        // slot of block it
-        constexpr int ns = (it + PD) % (PD + 1); // slot that receives block it + PD
-        if constexpr (it + PD < BPW) {
+    // block `it` of the wave, held in ring slot CS = it % (PD + 1)
+    auto step = [&](auto CS, int it) {
+        constexpr int cs = decltype(CS)::value;
+        constexpr int ns = (cs + PD) % (PD + 1); // slot that receives block it + PD
+        if (it >= bpw) return;
+        if constexpr (FLAT_LOOP) { // past the wave's last block: that block again (an L2 hit)
+            bq[ns] = locate(min(it + PD, bpw - 1));
+            fetch(bq[ns], kq[ns], sq[ns]);
+        } else if (it + PD < bpw) {
             bq[ns] = locate(it + PD);
             sq[ns] = 1.0f;
             fetch(bq[ns], kq[ns], sq[ns]);
@@ -381,7 +410,16 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
                 }
             }
         }
-    });
+    };
+    if constexpr (BPW > 0) {
+        static_for<0, BPW>([&](auto IT) {
+            constexpr int it = decltype(IT)::value;
+            step(std::integral_constant<int, it % (PD + 1)>{}, it);
+        });
+    } else {
+        for (int it0 = 0; it0 < bpw; it0 += PD + 1)
+            static_for<0, PD + 1>([&](auto J) { step(J, it0 + (int)decltype(J)::value); });
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -561,19 +599,25 @@ hipError_t launch_flat(const ScoreArgs &a, hipStream_t st)
     constexpr int MT = H == 64 ? 2 : 1;
     using G = Geo<H, MT, false>;
     if (a.n_q <= 2 * G::NQW) {
-        // Long-lived waves (32 blocks = 1024 keys each) amortise the per-wave load of q and w,
-        // and up to 3 blocks in flight per wave (12 KB of keys at 4 KB per block) keep enough
-        // bytes outstanding per CU at two waves per SIMD.
-        // Short launches (page keys of Hierarchical Indexing, small batches) need many
-        // workgroups more than long waves: two blocks per wave there.
-        constexpr int WAVES = 4, BPW = 32, BPW_SHORT = 2;
+        // Long launches (at least 32 blocks = 1024 keys per wave with 512 workgroups): long-lived
+        // waves amortise the per-wave load of q and w, and up to 3 blocks in flight per wave
+        // (12 KB of keys at 4 KB per block) keep enough bytes outstanding per CU at two waves
+        // per SIMD.  Short launches (page keys of Hierarchical Indexing, small batches) need
+        // many workgroups more than long waves: two blocks per wave there.
+        constexpr int WAVES = 4, BPW_LONG = 32, BPW_SHORT = 2;
         constexpr int PD = KeyBlock<FP8, D>::BB <= 4096 ? 3 : 1;
         const int64_t n_blocks = (a.n_out + 31) / 32;
         const int64_t rows = (a.n_q + G::NQW - 1) / G::NQW;
-        if (n_blocks * rows * a.batch >= (int64_t)512 * WAVES * BPW) {
-            dim3 grid((unsigned)((n_blocks + WAVES * BPW - 1) / (WAVES * BPW)), (unsigned)rows,
-                      (unsigned)a.batch);
-            hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, false, false, WAVES, BPW, PD>),
+        if (n_blocks * rows * a.batch >= (int64_t)512 * WAVES * BPW_LONG && a.n_keys >= 32 &&
+            a.n_out == a.n_keys) {
+            // one round of workgroups, two per CU (as many as are resident at once), each wave
+            // streaming its share of blocks: no tail round, and the per-wave load of q and w
+            // amortised over as many blocks as possible
+            const int64_t units = rows * a.batch;
+            const int64_t gx = std::max<int64_t>(1, (512 + units - 1) / units);
+            dim3 grid((unsigned)std::min<int64_t>(gx, (n_blocks + WAVES - 1) / WAVES),
+                      (unsigned)rows, (unsigned)a.batch);
+            hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, false, false, WAVES, 0, PD>),
                                grid, dim3(WAVES * kWave), 0, st, a);
         } else {
             dim3 grid((unsigned)((n_blocks + WAVES * BPW_SHORT - 1) / (WAVES * BPW_SHORT)),
