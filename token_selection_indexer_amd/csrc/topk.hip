@@ -995,16 +995,26 @@ __device__ __forceinline__ bool setup_row(const SelectArgs &a, int64_t row, Row 
     return need > 0;
 }
 
-__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
+// CAND: candidate rows (ids from the list); flat rows get a null id pointer the compiler can see,
+// so the flat kernel carries no id loads.
+template <bool CAND>
+__device__ __forceinline__ void select_one_row(const SelectArgs &a)
 {
     __shared__ Smem sm;
     Row r;
     int32_t *dst;
     int need;
     if (!setup_row(a, blockIdx.x, r, dst, need, true)) return;
+    if (!CAND) r.ids = nullptr;
     const int nbuf = prepare_buf(sm, r, need, dst);
     if (nbuf >= 0) select_from_buf(sm, nbuf, need, dst);
 }
+
+// Flat rows (prefill, page recall): at most 64 VGPRs and 96 SGPRs, so two workgroups share a CU
+// (with one, the CU's memory path idles through each row's sampling and in-buffer selection).
+__global__ __launch_bounds__(NT, 8) void select_kernel_flat(SelectArgs a) { select_one_row<false>(a); }
+
+__global__ __launch_bounds__(NT) void select_kernel_cand(SelectArgs a) { select_one_row<true>(a); }
 
 // ------------------------------------------------------------------------------------------
 // Chunked path
@@ -1253,7 +1263,10 @@ hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream)
     const int64_t rows = (int64_t)a.batch * a.n_q;
     if (rows == 0) return hipSuccess;
     if (!use_chunked(a)) {
-        hipLaunchKernelGGL(select_kernel, dim3((unsigned)rows), dim3(NT), 0, stream, a);
+        if (a.cand_ids)
+            hipLaunchKernelGGL(select_kernel_cand, dim3((unsigned)rows), dim3(NT), 0, stream, a);
+        else
+            hipLaunchKernelGGL(select_kernel_flat, dim3((unsigned)rows), dim3(NT), 0, stream, a);
         return hipGetLastError();
     }
     const int64_t nc = (a.n_in + CHUNK - 1) / CHUNK;
