@@ -134,7 +134,9 @@ def headline(torch, lsa, inputs, cfg, steps, warmup):
         if ev: ev[3].record()
 
     log("[bench] headline: timing")
-    wall, st = run_timed(torch, step, ["score", "topk", "attn"], steps, warmup)
+    # wall time of the bare step; per-stage times from a second run with events between stages
+    wall, _ = run_timed(torch, lambda _ev: step(None), [], steps, warmup)
+    _, st = run_timed(torch, step, ["score", "topk", "attn"], steps, warmup)
     n_q = B * s.n_q
     sb = score_bytes(n_q * L, s.head_dim, True, s.heads, n_q)
     ab = attn_bytes(n_q * b.k, a.d_qk * 2, n_q, a.heads, a.d_qk, a.d_v, b.k)
