@@ -112,6 +112,23 @@ def test_scores_decode_128k_sampled():
         say(f"decode_128k seq {b} ok")
 
 
+@pytest.mark.parametrize("back", [1, 1000])
+def test_scores_long_launch_ragged(back):
+    """A long decode launch (one round of workgroups, each wave looping over ~64 blocks) whose key
+    count is not a multiple of the 32-key block: the last block is moved back to end at the last
+    key and rewrites its overlap with the previous block.  Whole rows of three sequences against
+    the oracle; back = 1000 also cuts the causal range short of the end."""
+    L = 131072 - 5
+    w = shrink(DECODE_128K, batch=17, kv_len=L, q_pos0=L - back)
+    inp = inputs.index_inputs(w, DEV)
+    s = lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=w.index.q_pos0)
+    torch.cuda.synchronize()
+    for b in (0, 8, 16):
+        I, A, E = oracle_scores(inp, b, [0], w.index.q_pos0)
+        assert_scores(s[b, 0].cpu().numpy(), I[0], A[0], E[0], f"seq {b}")
+        say(f"long ragged launch (back {back}) seq {b} ok")
+
+
 def test_scores_prefill_8k_sampled():
     """Full chunked-prefill workload (8192 queries x 128K bf16 keys, 4.3 GB of scores); the
     oracle checks whole rows at the first, a middle and the last query."""
