@@ -369,7 +369,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): the LSA path "
-              f"is built and measured on a single MI355X; see DESIGN.md for how it would shard.",
+              f"is built and measured on a single MI355X (decode would shard the batch across "
+              f"GPUs, longer contexts the key length; that exchange is not built).",
               file=sys.stderr)
         sys.exit(2)
 
