@@ -44,6 +44,13 @@ __device__ __forceinline__ uint4 ld16(const void *p)
     return bitcast<uint4>(*reinterpret_cast<const u32x4_t *>(p));
 }
 
+// The same with the non-temporal hint, for data read once (a key stream, gathered rows): it
+// need not stay in the caches, which keeps them for what is read again.
+__device__ __forceinline__ uint4 ld16_nt(const void *p)
+{
+    return bitcast<uint4>(__builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p)));
+}
+
 // D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).  Lane l supplies A row l%32 and B column
 // l%32, each with K elements 8*(l/32) .. 8*(l/32)+7; it receives D[8*(r/4) + 4*(l/32) + r%4][l%32]
 // in register r.
