@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void page_summary_wave_kernel(const void *keys
         static_for<0, TPL>([&](auto J) {
             constexpr int j = decltype(J)::value;
             const bool ok = t0 + j < kv_len;
-            raw[j] = ok ? ld16(kb + (t0 + j) * ROW) : make_uint4(0u, 0u, 0u, 0u);
+            raw[j] = ok ? ld16_nt(kb + (t0 + j) * ROW) : make_uint4(0u, 0u, 0u, 0u); // read once
             if constexpr (FP8) scl[j] = ok ? sb[t0 + j] : 0.0f;
         });
     };

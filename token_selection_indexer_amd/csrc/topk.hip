@@ -109,8 +109,11 @@ __device__ __forceinline__ void elem4f(const Row &r, int64_t p, float (&f)[4], i
                                        int64_t hi)
 {
     if (r.vec && p >= r.lo && p + 4 <= hi) {
-        const float4 v = *reinterpret_cast<const float4 *>(r.sc + p);
-        f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+        const uint4 v = ld16_nt(r.sc + p); // streaming pass: read once
+        f[0] = __uint_as_float(v.x);
+        f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z);
+        f[3] = __uint_as_float(v.w);
         if (r.ids) {
             const int4 iv = *reinterpret_cast<const int4 *>(r.ids + p);
             id[0] = iv.x; id[1] = iv.y; id[2] = iv.z; id[3] = iv.w;
@@ -1065,7 +1068,7 @@ __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a
     if (inner) {
         const float *ps = r.sc + wb + lane;
 #pragma unroll
-        for (int j = 0; j < CI; ++j) f[j] = ps[j * kWave];
+        for (int j = 0; j < CI; ++j) f[j] = __builtin_nontemporal_load(ps + j * kWave); // read once
         if (CAND) {
             const int32_t *pi = r.ids + wb + lane;
 #pragma unroll
