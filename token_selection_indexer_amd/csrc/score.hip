@@ -600,13 +600,12 @@ hipError_t launch_flat(const ScoreArgs &a, hipStream_t st)
     using G = Geo<H, MT, false>;
     if (a.n_q <= 2 * G::NQW) {
         // Long launches (at least 32 blocks = 1024 keys per wave with 512 workgroups): long-lived
-        // waves amortise the per-wave load of q and w, and up to 2 blocks in flight per wave
-        // (8 KB of keys at 4 KB per block) keep enough bytes outstanding per CU at two waves
+        // waves amortise the per-wave load of q and w, and up to 3 blocks in flight per wave
+        // (12 KB of keys at 4 KB per block) keep enough bytes outstanding per CU at two waves
         // per SIMD.  Short launches (page keys of Hierarchical Indexing, small batches) need
         // many workgroups more than long waves: two blocks per wave there.
         constexpr int WAVES = 4, BPW_LONG = 32, BPW_SHORT = 2;
-        // (a 3-block ring measured 2% faster than a 4-block one in the long launch)
-        constexpr int PD = KeyBlock<FP8, D>::BB <= 4096 ? 2 : 1;
+        constexpr int PD = KeyBlock<FP8, D>::BB <= 4096 ? 3 : 1;
         const int64_t n_blocks = (a.n_out + 31) / 32;
         const int64_t rows = (a.n_q + G::NQW - 1) / G::NQW;
         if (n_blocks * rows * a.batch >= (int64_t)512 * WAVES * BPW_LONG && a.n_keys >= 32 &&
