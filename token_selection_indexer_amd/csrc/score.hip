@@ -309,9 +309,14 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         }
         return k;
     };
-    auto fetch = [&](const Blk &k, KB &kb, float &sc) {
+    const uint8_t *dummy_base =
+        (int64_t)a.batch * a.n_q * H * D * 2 >= KB::BB ? reinterpret_cast<const uint8_t *>(a.q)
+                                                        : keys_b;
+    auto fetch = [&](const Blk &k, KB &kb, float &sc, bool dummy = false) {
         if constexpr (FLAT_LOOP) { // keys are read once: non-temporal (about 10% faster)
-            const uint8_t *base = keys_b + k.row0 * KB::RB;
+            // a prefetch past the wave's last block (never used) reads a cached, in-bounds
+            // block instead: q when it holds a block's bytes, else the sequence's first keys
+            const uint8_t *base = dummy ? dummy_base : keys_b + k.row0 * KB::RB;
 #pragma unroll
             for (int i = 0; i < KB::NP; ++i) kb.raw[i] = ld16_nt(base + lane_off[i]);
             if (FP8) sc = scale_b[k.row0 + n];
@@ -343,9 +348,9 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         constexpr int cs = decltype(CS)::value;
         constexpr int ns = (cs + PD) % (PD + 1); // slot that receives block it + PD
         if (it >= bpw) return;
-        if constexpr (FLAT_LOOP) { // past the wave's last block: that block again (an L2 hit)
+        if constexpr (FLAT_LOOP) { // past the wave's last block: a dummy load (see fetch)
             bq[ns] = locate(min(it + PD, bpw - 1));
-            fetch(bq[ns], kq[ns], sq[ns]);
+            fetch(bq[ns], kq[ns], sq[ns], it + PD >= bpw);
         } else if (it + PD < bpw) {
             bq[ns] = locate(it + PD);
             sq[ns] = 1.0f;
