@@ -312,16 +312,17 @@ def test_page_summary_bit_exact(kd, P, L, d):
 
 
 # ------------------------------------------------------------------------------ HI recall
-def _hi_case(w: Workload, b: int, inp, pk, res, check_cands=True):
-    """Compare GPU page recall of sequence b (decode, one query) with the oracle."""
+def _hi_case(w: Workload, b: int, inp, pk, res, check_cands=True, t=0):
+    """Compare GPU page recall of query t of sequence b with the oracle."""
     s, bud, hi = w.index, w.budget, w.hi
     keys, scale = keys_np(inp, b)
-    q = bits(inp["q"][b])
-    wt = f32(inp["w"][b])
+    q = bits(inp["q"][b, t:t + 1])
+    wt = f32(inp["w"][b, t:t + 1])
     pkn = bits(pk[b])
-    r = ref.page_recall(q, wt, pkn, keys, scale, np.array([s.q_pos0]), bud.k, bud.sink,
+    pos = s.q_pos0 + t
+    r = ref.page_recall(q, wt, pkn, keys, scale, np.array([pos]), bud.k, bud.sink,
                         bud.window, hi.page, hi.m_pages)
-    gp = res[0][b, 0].cpu().numpy()
+    gp = res[0][b, t].cpu().numpy()
     rp = r["page_ids"][0]
     coarse = r["coarse"][0]
     if not np.array_equal(gp, rp):
@@ -334,8 +335,8 @@ def _hi_case(w: Workload, b: int, inp, pk, res, check_cands=True):
                             min_recall=0.99)
     if check_cands:
         # candidates: ids follow the GPU's own recalled pages; scores checked against the oracle
-        gi = res[2][b, 0].cpu().numpy()
-        gs = res[1][b, 0].cpu().numpy()
+        gi = res[2][b, t].cpu().numpy()
+        gs = res[1][b, t].cpu().numpy()
         ok = gi >= 0
         P = hi.page
         for i, p in enumerate(gp):
@@ -344,7 +345,7 @@ def _hi_case(w: Workload, b: int, inp, pk, res, check_cands=True):
                 assert np.all(seg == -1)
                 continue
             tok = p * P + np.arange(P)
-            V = min(s.kv_len, s.q_pos0 + 1)
+            V = min(s.kv_len, pos + 1)
             inmid = (tok >= bud.sink) & (tok < V - bud.window)
             assert np.array_equal(seg, np.where(inmid, tok, -1))
         if ok.any():
@@ -367,6 +368,39 @@ def test_page_recall_small():
                           q_pos0=8999)
     for b in range(3):
         _hi_case(w, b, inp, pk, res)
+
+
+def test_page_recall_causal_prefill():
+    """Hierarchical Indexing for a causal chunk of queries: every query has its own valid length,
+    so its own eligible pages and candidates.  The first rows have V <= k (nothing recalled);
+    the window covers at least one page (W >= P - 1).  Recall and candidates of sampled rows are
+    checked against the oracle, and the candidate-mode selection of every row against the
+    oracle's selection over the GPU's own candidate list."""
+    L, T, P, M, k, S, W = 5000, 300, 32, 8, 512, 32, 96
+    pos0 = 400  # the last row sees 700 keys: 19 eligible pages, 8 recalled
+    w = Workload(name="hi_prefill", index=IndexShape(
+        batch=2, n_q=T, kv_len=L, q_pos0=pos0, heads=64, head_dim=128, key_dtype="fp8"),
+        budget=Budget(k=k, sink=S, window=W), attn=DECODE_1M_HI.attn, seed=21,
+        hi=HiParams(page=P, m_pages=M), planted_frac=0.05)
+    inp = inputs.index_inputs(w, DEV)
+    pk = lsa.page_summary(inp["keys"], inp["scale"], P)
+    res = lsa.page_recall(inp["q"], inp["w"], pk, inp["keys"], inp["scale"], k, S, W, P, M,
+                          q_pos0=pos0)
+    idx = lsa.topk_select(res[1], k, S, W, kv_len=L, q_pos0=pos0, cand_ids=res[2])
+    torch.cuda.synchronize()
+    n_small = k - pos0  # rows with V <= k
+    assert 0 < n_small < T
+    pid = res[0].cpu().numpy()
+    assert np.all(pid[:, :n_small] == -1)
+    assert np.all(res[2][:, :n_small].cpu().numpy() == -1)
+    for b in range(2):
+        for t in (n_small, n_small + 1, 201, T - 1):
+            _hi_case(w, b, inp, pk, res, t=t)
+    cs, ci, gi = res[1].cpu().numpy(), res[2].cpu().numpy(), idx.cpu().numpy()
+    V = ref.valid_lengths(L, pos0, T)
+    for b in range(2):
+        want = ref.select(cs[b], V, k, S, W, cand_ids=ci[b])
+        assert np.array_equal(gi[b], want), b
 
 
 def test_hi_all_pages_equals_flat_on_gpu():

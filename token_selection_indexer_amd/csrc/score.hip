@@ -538,6 +538,10 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
         fetch(kt_begin);
         commit(0);
     }
+    // q and w must be in registers before the loop: without this wait the compiler places the
+    // wait for them inside the loop body, where in every iteration it also waits for the next
+    // tile's prefetch and so serialises the key loads with the MFMAs.
+    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0)
     __syncthreads();
     for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
         const int buf = (int)((kt - kt_begin) & 1);
@@ -577,14 +581,22 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
                     }
                 }
             };
+            // The next tile is written to the other buffer (read by nobody in this tile) before
+            // the last two epilogues: its wait for the prefetched keys then covers only stores
+            // issued at least one block of MFMAs earlier, not the latest ones.
             mma(0, acc[0]);
             static_for<0, KB / 32>([&](auto NTI) {
                 constexpr int nt = decltype(NTI)::value;
                 if constexpr (nt + 1 < KB / 32) mma(nt + 1, acc[(nt + 1) & 1]);
+                if constexpr (nt + 2 == KB / 32)
+                    if (kt + 1 < kt_end) commit(buf ^ 1);
                 epi(nt, acc[nt & 1]);
             });
+            if constexpr (KB / 32 < 2)
+                if (kt + 1 < kt_end) commit(buf ^ 1);
+        } else if (kt + 1 < kt_end) {
+            commit(buf ^ 1);
         }
-        if (kt + 1 < kt_end) commit(buf ^ 1);
         __syncthreads();
     }
 
