@@ -529,6 +529,29 @@ def test_mla_attn_decode_128k_sampled():
                     out[s:s + 1], lse[s:s + 1], True, 512)
 
 
+@pytest.mark.parametrize("L", [1, 2, 5, 31, 33, 100])
+def test_degenerate_lengths_end_to_end(L):
+    """Caches shorter than one 32-key block, than the budget, or than sink plus window: scores,
+    selection and MLA attention of a short causal chunk against the oracle."""
+    T = min(3, L)
+    k, S, W = 16, 2, 4
+    w = Workload(name="deg", index=IndexShape(
+        batch=2, n_q=T, kv_len=L, q_pos0=L - T, heads=64, head_dim=128, key_dtype="fp8"),
+        budget=Budget(k=k, sink=S, window=W), attn=DECODE_128K.attn, seed=30 + L)
+    inp = inputs.index_inputs(w, DEV)
+    sc = lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=L - T)
+    idx = lsa.topk_select(sc, k, S, W, kv_len=L, q_pos0=L - T)
+    sn, gi = sc.cpu().numpy(), idx.cpu().numpy()
+    V = ref.valid_lengths(L, L - T, T)
+    for b in range(2):
+        I, A, E = oracle_scores(inp, b, np.arange(T), L - T)
+        assert_scores(sn[b], I, A, E, f"b={b}")
+        assert np.array_equal(gi[b], ref.select(sn[b], V, k, S, W)), b
+    att = inputs.attn_inputs(w, 0, DEV)
+    out, lse = lsa.sparse_attn(att["q"], att["kv"], None, idx, w.attn.scale, S, W, d_v=512)
+    _attn_check(att["q"], att["kv"], None, idx, w.attn.scale, out, lse, True, 512)
+
+
 def test_cross_layer_reuse_bitwise_and_oracle():
     """One index list, four layers: each layer's output equals that layer's single call
     bitwise, and matches the oracle."""
