@@ -12,11 +12,12 @@
 // their per-token scale is applied once after the head sum.
 //
 // Two kernels:
-//  * stream: each wave owns its own 32-key blocks and loads them straight from HBM into the
-//    MFMA operand registers (no reuse between waves: decode has one query per sequence, so the
-//    key cache is read exactly once).  Also runs the fine stage of Hierarchical Indexing, where
+//  * stream: each wave owns its own 32-key blocks, loads them from HBM in contiguous 16-byte
+//    pieces (non-temporal: no reuse between waves, since decode has one query per sequence and
+//    the key cache is read exactly once) and passes them through its own LDS slab into the MFMA
+//    operand layout.  Also runs the fine stage of Hierarchical Indexing, where
 //    the blocks come from each query's recalled pages.
-//  * tile: prefill.  A workgroup owns WAVES*NQW queries; 64-key tiles are staged once in LDS
+//  * tile: prefill.  A workgroup owns WAVES*NQW queries; 128-key tiles are staged once in LDS
 //    (bf16, padded rows) and shared by every wave, double-buffered against the next tile's
 //    global loads.
 //
