@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -164,3 +165,24 @@ def test_sparse_attn_rejects(L):
     assert call(lsa.AttnShape(1, 128, 128, 0, 100, 128, 0.1)) == 2   # stride % 8
     assert call(lsa.AttnShape(1, 512, 128, 0, 512, 128, 0.1)) == 4   # per-head d <= 256
     assert call(lsa.AttnShape(1, 128, 128, 0, 64, 128, 0.1)) == 2    # stride < d_qk
+
+
+def test_no_host_fallback_and_missing_library_fails_loudly(tmp_path):
+    """The binding has no CPU path: host tensors are refused, and without the built library every
+    call raises instead of computing anything some other way."""
+    import torch
+    q = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16)
+    w = torch.zeros((1, 1, 64), dtype=torch.float32)
+    keys = torch.zeros((1, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        lsa.index_scores(q, w, keys)
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from token_selection_indexer_amd import lsa\n"
+            "lsa.LIB_PATH = %r\n"
+            "try:\n"
+            "    lsa.lib()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n") % (ROOT, str(tmp_path / "liblsa.so"))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True,
+                         text=True, timeout=120)
+    assert "raised: HIP library not built" in out.stdout, out.stdout + out.stderr
