@@ -445,6 +445,7 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
     constexpr int NT = WAVES * kWave;
     constexpr int CPT = (CHUNKS + NT - 1) / NT;       // chunks per thread per tile
     static_assert(KB % 32 == 0, "tile of whole MFMA blocks");
+    static_assert(CHUNKS % NT == 0, "whole chunks per thread");
 
     __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][KB * ROWB];
     __shared__ float lds_s[2][KB];
@@ -501,26 +502,26 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
 
     uint4 stage[CPT];
     float stage_s = 0.0f;
+    // Unconditional loads (rows past the last key re-read the last key; their scores are never
+    // stored): a conditional load, or a zero written to a register a load may still be filling,
+    // makes the compiler wait for every load and store in flight, including the epilogue's.
     auto fetch = [&](int64_t kt) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = threadIdx.x + i * NT;
+        static_for<0, CPT>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            const int c = (int)threadIdx.x + i * NT;
             const int key = c / CPR, col = c % CPR;
-            const int64_t row = kt * KB + key;
-            stage[i] = (c < CHUNKS && row < a.n_keys)
-                           ? reinterpret_cast<const uint4 *>(keys_b + row * D * ESZ)[col]
-                           : make_uint4(0, 0, 0, 0);
-        }
-        if (FP8 && threadIdx.x < KB) {
-            const int64_t row = kt * KB + threadIdx.x;
-            stage_s = row < a.n_keys ? scale_b[row] : 0.0f;
+            const int64_t row = min(kt * KB + key, a.n_keys - 1);
+            stage[i] = reinterpret_cast<const uint4 *>(keys_b + row * D * ESZ)[col];
+        });
+        if (FP8) {
+            const int64_t row = min(kt * KB + (int)(threadIdx.x % KB), a.n_keys - 1);
+            stage_s = scale_b[row];
         }
     };
     auto commit = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
+        static_for<0, CPT>([&](auto I) {
+            constexpr int i = decltype(I)::value;
             const int c = threadIdx.x + i * NT;
-            if (c >= CHUNKS) continue;
             const int key = c / CPR, col = c % CPR;
             uint8_t *dst = &lds_k[buf][key * ROWB];
             if (FP8) {
@@ -529,9 +530,9 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
                 reinterpret_cast<uint4 *>(dst + col * 32)[0] = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
                 reinterpret_cast<uint4 *>(dst + col * 32)[1] = make_uint4(lo3.x, lo3.y, hi3.x, hi3.y);
             } else {
-                reinterpret_cast<uint4 *>(dst)[col] = stage[i];
+                *reinterpret_cast<u32x4_t *>(dst + col * 16) = bitcast<u32x4_t>(stage[i]);
             }
-        }
+        });
         if (FP8 && threadIdx.x < KB) lds_s[buf][threadIdx.x] = stage_s;
     };
 
