@@ -584,18 +584,18 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
                 }
             };
             // The next tile is written to the other buffer (read by nobody in this tile) before
-            // the last two epilogues: its wait for the prefetched keys then covers only stores
-            // issued at least one block of MFMAs earlier, not the latest ones.
+            // the epilogue of block CN: its wait for the prefetched keys then covers only the
+            // stores of the first CN epilogues, each issued a block of MFMAs earlier, and the
+            // keys have had CN + 1 blocks of MFMAs to arrive (measured best: CN = 2).
+            constexpr int CN = KB / 32 >= 3 ? 2 : 0;
             mma(0, acc[0]);
             static_for<0, KB / 32>([&](auto NTI) {
                 constexpr int nt = decltype(NTI)::value;
                 if constexpr (nt + 1 < KB / 32) mma(nt + 1, acc[(nt + 1) & 1]);
-                if constexpr (nt + 2 == KB / 32)
+                if constexpr (nt == CN)
                     if (kt + 1 < kt_end) commit(buf ^ 1);
                 epi(nt, acc[nt & 1]);
             });
-            if constexpr (KB / 32 < 2)
-                if (kt + 1 < kt_end) commit(buf ^ 1);
         } else if (kt + 1 < kt_end) {
             commit(buf ^ 1);
         }
@@ -645,7 +645,10 @@ hipError_t launch_flat(const ScoreArgs &a, hipStream_t st)
                                grid, dim3(WAVES * kWave), 0, st, a);
         }
     } else {
-        constexpr int WAVES = 8, KB = 128; // 128-key tiles: half the barriers of 64
+        // 256-key tiles (139 KB of LDS, one workgroup per CU) where registers already limit
+        // the CU to one workgroup (H = 64, d = 128: 252 VGPRs); 128-key tiles elsewhere, so two
+        // workgroups can share a CU
+        constexpr int WAVES = 8, KB = (H == 64 && D == 128) ? 256 : 128;
         constexpr int QPB = WAVES * G::NQW;
         dim3 grid((unsigned)((a.n_q + QPB - 1) / QPB), (unsigned)a.batch);
         hipLaunchKernelGGL((score_tile_kernel<FP8, D, H, MT, WAVES, KB>), grid,
