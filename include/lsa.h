@@ -137,7 +137,7 @@ LSA_API lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budg
  * n_p = number of tokens of page p that exist.  Pages [page_lo, page_hi) are (re)written, so a
  * decode loop can extend the table one completed page at a time.
  *   page_size  P, a power of two in [1, 256]
- *   page_keys  [B, ceil(L/P), d] bf16
+ *   page_keys  [B, ceil(L/P), d] bf16, 16-byte aligned (keys too)
  */
 LSA_API lsa_status lsa_page_summary(const lsa_index_shape *shape, int32_t page_size, const void *keys,
                             lsa_key_dtype key_dtype, const float *key_scale, int64_t page_lo,
@@ -160,8 +160,11 @@ LSA_API lsa_status lsa_page_summary(const lsa_index_shape *shape, int32_t page_s
  *   page_ids     [B, n_q, m_pages] int32
  *   cand_scores  [B, n_q, m_pages * P] fp32;  cand_ids  [B, n_q, m_pages * P] int32
  *   ws           lsa_workspace_bytes(LSA_OP_PAGE_RECALL, ...) bytes
- * Limits: page_size a power of two in [32, 256] with head_dim 128 or [32, 256] with 64;
- *         1 <= m_pages <= 65536.
+ * Causality: a query with V < kv_len (a causal prefill chunk) may only recall pages that end
+ *   before V, or a page key (a mean over the whole page) would carry later tokens into its
+ *   coarse score.  The last eligible page ends before V exactly when window >= page_size - 1,
+ *   so a call with q_pos0 + 1 < kv_len and window < page_size - 1 returns LSA_ERR_UNSUPPORTED.
+ * Limits: page_size a power of two in [32, 256]; 1 <= m_pages <= 65536.
  */
 LSA_API lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int32_t page_size,
                            int32_t m_pages, const void *q, const float *w, const void *page_keys,

@@ -145,6 +145,14 @@ def test_page_recall_rejects(L):
     assert call(q=0) == 1
     assert call(ws=0) == 5
     assert call(nbytes=1024) == 5
+    # a causal chunk whose window is shorter than a page could recall a page holding later
+    # tokens: refused
+    pre = _shape(B=1, T=512, Lk=1 << 20, pos=(1 << 20) - 1024)
+    nb = lsa.lsa_workspace_bytes(lsa.OP_PAGE_RECALL, pre, b, 64, 256)
+    for W, want in ((32, 4), (63, 5)):  # 63 = P - 1 passes the check (and then lacks a ws)
+        assert L.lsa_page_recall(ctypes.byref(pre), lsa.Budget(2048, 128, W), 64, 256, v(FAKE),
+                                 v(FAKE), v(FAKE), v(FAKE), lsa.KEY_FP8_E4M3, v(FAKE), v(FAKE),
+                                 v(FAKE), v(FAKE), None, nb, None) == want
 
 
 def test_sparse_attn_rejects(L):
@@ -186,3 +194,57 @@ def test_no_host_fallback_and_missing_library_fails_loudly(tmp_path):
     out = subprocess.run([sys.executable, "-c", code], capture_output=True,
                          text=True, timeout=120)
     assert "raised: HIP library not built" in out.stdout, out.stdout + out.stderr
+
+
+def test_binding_checks_every_tensor(monkeypatch):
+    """Every tensor the binding hands to the library is checked (device, dtype, shape,
+    contiguity) before the call: a host key_scale, a wrong-shaped out= or a mismatched w is
+    refused with ValueError, so no host pointer or undersized buffer reaches a kernel.  Host
+    tensors stand in for device ones here (no GPU); the library itself must never be reached."""
+    import torch
+
+    def no_lib():
+        raise AssertionError("the library was called despite a bad argument")
+
+    monkeypatch.setattr(lsa, "lib", no_lib)
+    host_scale = torch.ones((1, 64), dtype=torch.float32)
+    monkeypatch.setattr(lsa, "_on_device", lambda t: t is not host_scale)
+    q = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16)
+    w = torch.zeros((1, 1, 64), dtype=torch.float32)
+    keys8 = torch.zeros((1, 64, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="key_scale must be a device tensor"):
+        lsa.index_scores(q, w, keys8, host_scale)
+    with pytest.raises(ValueError, match="key_scale must have shape"):
+        lsa.index_scores(q, w, keys8, torch.ones((1, 63), dtype=torch.float32))
+    with pytest.raises(ValueError, match="out must have shape"):
+        lsa.index_scores(q, w, keys8, torch.ones((1, 64)), out=torch.empty((1, 1, 63)))
+    with pytest.raises(ValueError, match="out must be"):
+        lsa.index_scores(q, w, keys8, torch.ones((1, 64)), out=torch.empty((1, 1, 64),
+                                                                            dtype=torch.float64))
+    with pytest.raises(ValueError, match="w must have shape"):
+        lsa.index_scores(q, torch.zeros((1, 1, 32)), keys8, torch.ones((1, 64)))
+    with pytest.raises(ValueError, match="keys .* do not match"):
+        lsa.index_scores(q, w, torch.zeros((2, 64, 128), dtype=torch.uint8), torch.ones((2, 64)))
+    with pytest.raises(ValueError, match="bf16 keys take no key_scale"):
+        lsa.index_scores(q, w, keys8.to(torch.bfloat16), torch.ones((1, 64)))
+    sc = torch.zeros((1, 1, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="cand_ids must have shape"):
+        lsa.topk_select(sc, 16, 2, 4, kv_len=64, q_pos0=63,
+                        cand_ids=torch.zeros((1, 1, 32), dtype=torch.int32))
+    with pytest.raises(ValueError, match="out must have shape"):
+        lsa.topk_select(sc, 16, 2, 4, kv_len=64, q_pos0=63, out=torch.empty((1, 1, 8),
+                                                                             dtype=torch.int32))
+    aq = torch.zeros((1, 1, 16, 576), dtype=torch.bfloat16)
+    kv = torch.zeros((1, 64, 576), dtype=torch.bfloat16)
+    idx = torch.zeros((1, 1, 16), dtype=torch.int32)
+    with pytest.raises(ValueError, match="out must have shape"):
+        lsa.sparse_attn(aq, kv, None, idx, 0.04, d_v=512,
+                        out=torch.empty((1, 1, 16, 256), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="idx .* does not match"):
+        lsa.sparse_attn(aq, kv, None, torch.zeros((2, 1, 16), dtype=torch.int32), 0.04, d_v=512)
+    with pytest.raises(ValueError, match="v .* does not match"):
+        lsa.sparse_attn(aq[..., :128].contiguous(), kv[..., :128].contiguous(),
+                        torch.zeros((1, 32, 128), dtype=torch.bfloat16), idx, 0.1)
+    with pytest.raises(ValueError, match="page_keys must have shape"):
+        lsa.page_recall(q, w, torch.zeros((1, 3, 128), dtype=torch.bfloat16), keys8,
+                        torch.ones((1, 64)), 16, 2, 4, 32, 1)

@@ -92,7 +92,6 @@ size_t lsa_workspace_bytes(int op, const lsa_index_shape *shape, lsa_budget budg
                            int32_t page_size, int32_t m_pages, int64_t n_cand,
                            const lsa_attn_shape *attn)
 {
-    (void)n_cand;
     switch (op) {
     case LSA_OP_TOPK_SELECT: {
         if (!shape || shape->batch < 0 || shape->n_q < 0 || shape->kv_len < 1 ||
@@ -195,7 +194,7 @@ lsa_status lsa_page_summary(const lsa_index_shape *shape, int32_t page_size, con
     lsa_status st = check_keys(key_dtype, keys, key_scale);
     if (st != LSA_OK) return st;
     if (!page_keys) return LSA_ERR_NULL_POINTER;
-    if (!aligned(page_keys, 4)) return LSA_ERR_BAD_SHAPE;
+    if (!aligned(page_keys, 16)) return LSA_ERR_BAD_SHAPE;
     const int64_t n_pages = (shape->kv_len + page_size - 1) / page_size;
     if (page_lo < 0 || page_hi < page_lo || page_hi > n_pages) return LSA_ERR_BAD_SHAPE;
     if (shape->batch == 0 || page_hi == page_lo) return LSA_OK;
@@ -217,6 +216,11 @@ lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int3
     if ((st = check_budget(budget)) != LSA_OK) return st;
     if (!pow2(page_size) || page_size < 32 || page_size > 256) return LSA_ERR_BAD_SHAPE;
     if (m_pages < 1 || m_pages > 65536) return LSA_ERR_BAD_SHAPE;
+    // A query that sees fewer than kv_len keys (causal prefill) must not recall a page that
+    // extends past its last valid key: that page's key is a mean over later tokens.  The last
+    // eligible page ends before V when the window covers at least P - 1 tokens.
+    if (shape->q_pos0 + 1 < shape->kv_len && budget.window < page_size - 1)
+        return LSA_ERR_UNSUPPORTED;
     if ((st = check_keys(key_dtype, keys, key_scale)) != LSA_OK) return st;
     if (!q || !w || !page_keys || !page_ids || !cand_scores || !cand_ids) return LSA_ERR_NULL_POINTER;
     if (!aligned(q, 16) || !aligned(page_keys, 16) || !aligned(w, 4) || !aligned(page_ids, 4) ||

@@ -100,7 +100,7 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint2 v)
 }
 
 // Monotone map of a finite binary32 onto uint32: a > b  <=>  key(a) > key(b); -0 maps like +0.
-// Every finite value (and -inf) maps to a key >= 0x00800000, so 0 is free as "no element".
+// Every finite value maps to a key >= 0x00800000 and -inf to 0x007FFFFF, so 0 is free as "no element".
 __device__ __forceinline__ uint32_t order_key(float f)
 {
     uint32_t u = __float_as_uint(f);

@@ -232,12 +232,12 @@ template <bool FP8>
 hipError_t launch_p(const void *keys, const float *kscale, int batch, int64_t kv_len, int D,
                     int P, int64_t page_lo, int64_t page_hi, uint16_t *pk, hipStream_t st)
 {
+    // pages of at least one 16-byte piece per lane group take the one-wave-per-page kernel;
+    // smaller pages (P <= 8) the per-element one.  Both pointers are 16-byte aligned (checked
+    // by the entry point).
     bool done = false;
     hipError_t e = hipSuccess;
-    const bool a16 = ((reinterpret_cast<uintptr_t>(keys) | reinterpret_cast<uintptr_t>(pk)) & 15) == 0;
-    if (!a16)
-        ;
-    else if (D == 128)
+    if (D == 128)
         e = launch_wave_p<FP8, 128>(keys, kscale, batch, kv_len, P, page_lo, page_hi, pk, st, done);
     else if (D == 64)
         e = launch_wave_p<FP8, 64>(keys, kscale, batch, kv_len, P, page_lo, page_hi, pk, st, done);
@@ -251,7 +251,7 @@ hipError_t launch_p(const void *keys, const float *kscale, int batch, int64_t kv
         hipLaunchKernelGGL((page_summary_kernel<FP8, PP>), grid, dim3(256), 0, st, keys, kscale,    \
                            kv_len, D, page_lo, page_hi, n_pages, pk);                               \
         break;
-        LSA_PS(1) LSA_PS(2) LSA_PS(4) LSA_PS(8) LSA_PS(16) LSA_PS(32) LSA_PS(64) LSA_PS(128) LSA_PS(256)
+        LSA_PS(1) LSA_PS(2) LSA_PS(4) LSA_PS(8)
 #undef LSA_PS
     default: return hipErrorInvalidValue;
     }

@@ -159,25 +159,57 @@ class Workspace:
         return self.buf
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, dim=None):
-    if not t.is_cuda:
+def _on_device(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dim=None, shape=None, device=None):
+    """Refuse what would hand the library a host pointer, a strided view, the wrong element type
+    or a buffer of the wrong size."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not _on_device(t):
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if dim is not None and t.dim() != dim:
         raise ValueError(f"{name} must have {dim} dims, got {t.dim()}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _out(out, name, shape, dtype, device):
+    """A caller-supplied output must match exactly; otherwise allocate one."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(out, name, dtype, shape=shape, device=device)
+    return out
 
 
 def _key_args(keys: torch.Tensor, key_scale: Optional[torch.Tensor]):
+    """(key dtype code, scale) after checking that the scale matches the keys [B, L, d]."""
     if keys.dtype == torch.bfloat16:
+        if key_scale is not None:
+            raise ValueError("bf16 keys take no key_scale")
         return KEY_BF16, None
     if keys.dtype in (torch.uint8, torch.float8_e4m3fn):
         if key_scale is None:
             raise ValueError("fp8 keys need key_scale")
+        _need(key_scale, "key_scale", torch.float32, shape=keys.shape[:2], device=keys.device)
         return KEY_FP8_E4M3, key_scale
     raise ValueError(f"keys must be bf16 or e4m3 codes, got {keys.dtype}")
+
+
+def _check_index_operands(q, w, keys):
+    B, T, H, _ = q.shape
+    _need(w, "w", torch.float32, shape=(B, T, H), device=q.device)
+    _need(keys, "keys", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), dim=3, device=q.device)
+    if keys.shape[0] != B or keys.shape[2] != q.shape[3]:
+        raise ValueError(f"keys {tuple(keys.shape)} do not match q {tuple(q.shape)}")
 
 
 def index_shape(q: torch.Tensor, keys: torch.Tensor, q_pos0: Optional[int] = None) -> IndexShape:
@@ -189,13 +221,10 @@ def index_shape(q: torch.Tensor, keys: torch.Tensor, q_pos0: Optional[int] = Non
 def index_scores(q, w, keys, key_scale=None, q_pos0=None, out=None, stream=None):
     """scores [B, n_q, L] fp32 (q_pos0 defaults to L - n_q: the queries are the last tokens)."""
     _need(q, "q", torch.bfloat16, 4)
-    _need(w, "w", torch.float32, 3)
-    _need(keys, "keys", dim=3)
+    _check_index_operands(q, w, keys)
     kd, ks = _key_args(keys, key_scale)
     shape = index_shape(q, keys, q_pos0)
-    if out is None:
-        out = torch.empty((shape.batch, shape.n_q, shape.kv_len), dtype=torch.float32,
-                          device=q.device)
+    out = _out(out, "out", (shape.batch, shape.n_q, shape.kv_len), torch.float32, q.device)
     lsa_index_scores(shape, q, w, keys, kd, ks, out, stream)
     return out
 
@@ -207,9 +236,8 @@ def topk_select(scores, k, sink, window, kv_len, q_pos0, cand_ids=None, out=None
     B, T, n = scores.shape
     shape = IndexShape(B, T, 1, 64, kv_len, q_pos0)
     if cand_ids is not None:
-        _need(cand_ids, "cand_ids", torch.int32, 3)
-    if out is None:
-        out = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
+        _need(cand_ids, "cand_ids", torch.int32, shape=scores.shape, device=scores.device)
+    out = _out(out, "out", (B, T, k), torch.int32, scores.device)
     bud = Budget(k, sink, window)
     nb = lsa_workspace_bytes(OP_TOPK_SELECT, shape, bud, n_cand=n)
     wsb = (ws or Workspace()).get(nb, scores.device)
@@ -219,12 +247,11 @@ def topk_select(scores, k, sink, window, kv_len, q_pos0, cand_ids=None, out=None
 
 def page_summary(keys, key_scale, page, page_lo=0, page_hi=None, out=None, stream=None):
     """page keys [B, ceil(L/P), d] bf16."""
-    _need(keys, "keys", dim=3)
+    _need(keys, "keys", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), dim=3)
     kd, ks = _key_args(keys, key_scale)
     B, L, d = keys.shape
     n_pages = (L + page - 1) // page
-    if out is None:
-        out = torch.empty((B, n_pages, d), dtype=torch.bfloat16, device=keys.device)
+    out = _out(out, "out", (B, n_pages, d), torch.bfloat16, keys.device)
     shape = IndexShape(B, 1, 64, d, L, L - 1)
     lsa_page_summary(shape, page, keys, kd, ks, page_lo, n_pages if page_hi is None else page_hi,
                      out, stream)
@@ -235,10 +262,11 @@ def page_recall(q, w, page_keys, keys, key_scale, k, sink, window, page, m_pages
                 ws: Optional[Workspace] = None, stream=None):
     """(page_ids [B,n_q,M], cand_scores [B,n_q,M*P], cand_ids [B,n_q,M*P])."""
     _need(q, "q", torch.bfloat16, 4)
-    _need(w, "w", torch.float32, 3)
-    _need(page_keys, "page_keys", torch.bfloat16, 3)
+    _check_index_operands(q, w, keys)
     kd, ks = _key_args(keys, key_scale)
     shape = index_shape(q, keys, q_pos0)
+    _need(page_keys, "page_keys", torch.bfloat16, device=q.device,
+          shape=(shape.batch, (shape.kv_len + page - 1) // page, shape.head_dim))
     B, T = shape.batch, shape.n_q
     bud = Budget(k, sink, window)
     dev = q.device
@@ -265,14 +293,24 @@ def sparse_attn(q, k, v, idx, scale, sink=0, window=0, d_v=None, latent=None, wa
         v = k
     B, T, Hq, dqk = q.shape
     L = k.shape[1]
+    dev = q.device
+    _need(k, "k", torch.bfloat16, device=dev)
+    if k.shape[0] != B or k.shape[2] < dqk:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    _need(v, "v", torch.bfloat16, 3, device=dev)
+    if v.shape[:2] != k.shape[:2]:
+        raise ValueError(f"v {tuple(v.shape)} does not match k {tuple(k.shape)}")
+    _need(idx, "idx", torch.int32, device=dev)
+    if idx.shape[:2] != (B, T):
+        raise ValueError(f"idx {tuple(idx.shape)} does not match q {tuple(q.shape)}")
     if d_v is None:
         d_v = v.shape[2] if not latent else dqk
+    if d_v > v.shape[2]:
+        raise ValueError(f"d_v {d_v} exceeds the value rows ({v.shape[2]})")
     attn = AttnShape(Hq, dqk, d_v, 1 if latent else 0, k.shape[2], v.shape[2], scale)
     shape = IndexShape(B, T, 64, 128, L, 0)
     bud = Budget(idx.shape[2], sink, window)
-    dev = q.device
-    if out is None:
-        out = torch.empty((B, T, Hq, d_v), dtype=torch.bfloat16, device=dev)
+    out = _out(out, "out", (B, T, Hq, d_v), torch.bfloat16, dev)
     lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev) if want_lse else None
     nb = lsa_workspace_bytes(OP_SPARSE_ATTN, shape, bud, attn=attn)
     wsb = (ws or Workspace()).get(nb, dev)
