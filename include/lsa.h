@@ -128,6 +128,25 @@ LSA_API lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budg
                            size_t ws_bytes, void *stream);
 
 /*
+ * lsa_topk_select_noalloc -- lsa_topk_select without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The selection and its result are those of lsa_topk_select with the
+ * same arguments; the chunked path (few long rows) uses a scratch array the library holds on
+ * each GPU instead of `ws`.  It calls no allocator.
+ *   Scratch   16 MiB per GPU, part of the library's code object, held until the process ends.
+ *             Calls whose chunked path would need more (lsa_workspace_bytes(LSA_OP_TOPK_SELECT,
+ *             ...) > 16 MiB) return LSA_ERR_UNSUPPORTED and enqueue nothing.
+ *   Races     Every call on one GPU shares that GPU's scratch: calls that may overlap on the
+ *             same GPU (different streams, or concurrent host threads) race and must be
+ *             serialised by the caller.  Calls on one stream are ordered and safe.
+ *   Set-up    The first call on a device looks up that device's address of the scratch (a HIP
+ *             runtime query, no allocation); a failure there returns LSA_ERR_DEVICE.
+ */
+LSA_API lsa_status lsa_topk_select_noalloc(const lsa_index_shape *shape, lsa_budget budget,
+                                           const float *scores, int64_t n_cand,
+                                           const int32_t *cand_ids, int32_t *idx, void *stream);
+
+/*
  * lsa_page_summary -- page keys for Hierarchical Indexing.  The model card's HI bullet recalls
  * blocks of tokens by coarse scores but does not define a block's coarse key; this library
  * defines it as the mean of the block's dequantised keys, fixed to the bit:

@@ -248,3 +248,22 @@ def test_binding_checks_every_tensor(monkeypatch):
     with pytest.raises(ValueError, match="page_keys must have shape"):
         lsa.page_recall(q, w, torch.zeros((1, 3, 128), dtype=torch.bfloat16), keys8,
                         torch.ones((1, 64)), 16, 2, 4, 32, 1)
+
+
+def test_topk_select_noalloc_rejects(L):
+    """The no-allocation selection validates like lsa_topk_select and refuses, before any HIP
+    call, a chunked selection whose scratch would exceed the library's 16 MiB."""
+    sh = _shape()
+    v = ctypes.c_void_p
+
+    def call(shape, budget, n_cand, scores=FAKE, cand=None):
+        return L.lsa_topk_select_noalloc(ctypes.byref(shape), budget,
+                                         v(scores) if scores else None, n_cand,
+                                         v(cand) if cand else None, v(FAKE), None)
+    assert call(sh, lsa.Budget(0, 0, 0), sh.kv_len) == 2
+    assert call(sh, lsa.Budget(64, 4, 4), sh.kv_len - 1) == 2
+    assert call(sh, lsa.Budget(64, 4, 4), sh.kv_len, scores=0) == 1
+    huge = _shape(B=1000, Lk=1 << 20)  # 1000 long rows: far beyond the scratch
+    b = lsa.Budget(2048, 128, 896)
+    assert lsa.lsa_workspace_bytes(lsa.OP_TOPK_SELECT, huge, b) > 16 << 20
+    assert call(huge, b, huge.kv_len) == 4

@@ -143,9 +143,12 @@ lsa_status lsa_index_scores(const lsa_index_shape *shape, const void *q, const f
     return device_status(lsa::launch_scores(a, static_cast<hipStream_t>(stream)));
 }
 
-lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budget, const float *scores,
-                           int64_t n_cand, const int32_t *cand_ids, int32_t *idx, void *ws,
-                           size_t ws_bytes, void *stream)
+namespace {
+
+// Validation and argument block shared by the two selection entry points.
+lsa_status prepare_select(const lsa_index_shape *shape, lsa_budget budget, const float *scores,
+                          int64_t n_cand, const int32_t *cand_ids, int32_t *idx,
+                          lsa::SelectArgs &a, int64_t &rows)
 {
     if (!shape) return LSA_ERR_NULL_POINTER;
     if (shape->batch < 0 || shape->n_q < 0 || shape->kv_len < 1 ||
@@ -159,12 +162,9 @@ lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budget, cons
     if (cand_ids && (n_cand < 1 || n_cand >= (int64_t(1) << 31))) return LSA_ERR_BAD_SHAPE;
     if (!aligned(scores, 16) || (cand_ids && !aligned(cand_ids, 16)) || !aligned(idx, 4))
         return LSA_ERR_BAD_SHAPE;
-    const int64_t rows = (int64_t)shape->batch * shape->n_q;
+    rows = (int64_t)shape->batch * shape->n_q;
     if (rows >= (int64_t(1) << 31)) return LSA_ERR_UNSUPPORTED;
-    if (rows == 0) return LSA_OK;
-    const size_t need = lsa::select_workspace_bytes(rows, n_cand, lsa::SELECT_SI);
-    if (need && (!ws || ws_bytes < need || !aligned(ws, 256))) return LSA_ERR_WORKSPACE_TOO_SMALL;
-    lsa::SelectArgs a{};
+    a = lsa::SelectArgs{};
     a.scores = scores;
     a.cand_ids = cand_ids;
     a.out = idx;
@@ -178,6 +178,38 @@ lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budget, cons
     a.window = budget.window;
     a.mode = lsa::SELECT_SI;
     a.out_stride = budget.k;
+    return LSA_OK;
+}
+
+} // namespace
+
+lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budget, const float *scores,
+                           int64_t n_cand, const int32_t *cand_ids, int32_t *idx, void *ws,
+                           size_t ws_bytes, void *stream)
+{
+    lsa::SelectArgs a;
+    int64_t rows = 0;
+    lsa_status st = prepare_select(shape, budget, scores, n_cand, cand_ids, idx, a, rows);
+    if (st != LSA_OK) return st;
+    if (rows == 0) return LSA_OK;
+    const size_t need = lsa::select_workspace_bytes(rows, n_cand, lsa::SELECT_SI);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, 256))) return LSA_ERR_WORKSPACE_TOO_SMALL;
+    return device_status(lsa::launch_select(a, ws, static_cast<hipStream_t>(stream)));
+}
+
+lsa_status lsa_topk_select_noalloc(const lsa_index_shape *shape, lsa_budget budget,
+                                   const float *scores, int64_t n_cand, const int32_t *cand_ids,
+                                   int32_t *idx, void *stream)
+{
+    lsa::SelectArgs a;
+    int64_t rows = 0;
+    lsa_status st = prepare_select(shape, budget, scores, n_cand, cand_ids, idx, a, rows);
+    if (st != LSA_OK) return st;
+    if (rows == 0) return LSA_OK;
+    const size_t need = lsa::select_workspace_bytes(rows, n_cand, lsa::SELECT_SI);
+    if (need > lsa::select_scratch_bytes()) return LSA_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    if (need && lsa::select_scratch(&ws) != hipSuccess) return LSA_ERR_DEVICE;
     return device_status(lsa::launch_select(a, ws, static_cast<hipStream_t>(stream)));
 }
 

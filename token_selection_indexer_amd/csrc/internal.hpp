@@ -60,6 +60,10 @@ enum SelectMode : int {
 // Workspace of the selection (0 when one workgroup per row is used).
 size_t select_workspace_bytes(int64_t rows, int64_t n_in, int mode);
 hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream);
+// The library's own per-device scratch for callers that cannot allocate: its size, and the
+// current device's address of it (looked up on the first call on each device).
+size_t select_scratch_bytes();
+hipError_t select_scratch(void **ptr);
 
 hipError_t launch_page_summary(const void *keys, int fp8, const float *kscale, int batch,
                                int64_t kv_len, int dim, int page, int64_t page_lo,

@@ -40,6 +40,8 @@
 #include "device.hpp"
 #include "internal.hpp"
 
+#include <mutex>
+
 namespace lsa {
 namespace {
 
@@ -1290,6 +1292,41 @@ hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream)
                            dim3(CNT_THREADS), 0, stream, a, w);
     hipLaunchKernelGGL(chunk_finish_kernel, dim3((unsigned)rows), dim3(NT), 0, stream, a, w);
     return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Library-held scratch for the selection's chunked path, for callers that cannot allocate.
+// One fixed array per device (the code object's own copy on each GPU, alive until the process
+// ends).  Host code never uses the array's name as an address: the first call on a device asks
+// the runtime for that device's address of it and keeps it.
+// ------------------------------------------------------------------------------------------
+constexpr size_t kSelectScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kSelectScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+} // namespace
+
+size_t select_scratch_bytes() { return kSelectScratchBytes; }
+
+hipError_t select_scratch(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 } // namespace lsa

@@ -25,7 +25,8 @@ OP_TOPK_SELECT, OP_PAGE_RECALL, OP_SPARSE_ATTN = 1, 2, 3
 STATUS = {0: "LSA_OK", 1: "LSA_ERR_NULL_POINTER", 2: "LSA_ERR_BAD_SHAPE", 3: "LSA_ERR_BAD_DTYPE",
           4: "LSA_ERR_UNSUPPORTED", 5: "LSA_ERR_WORKSPACE_TOO_SMALL", 6: "LSA_ERR_DEVICE"}
 EXPORTS = ("lsa_index_scores", "lsa_topk_select", "lsa_page_summary", "lsa_page_recall",
-           "lsa_sparse_attn", "lsa_workspace_bytes", "lsa_status_string")
+           "lsa_sparse_attn", "lsa_workspace_bytes", "lsa_status_string",
+           "lsa_topk_select_noalloc")
 
 
 class IndexShape(ctypes.Structure):
@@ -64,6 +65,7 @@ def lib():
         ip, bud, ap = ctypes.POINTER(IndexShape), Budget, ctypes.POINTER(AttnShape)
         L.lsa_index_scores.argtypes = [ip, _VP, _VP, _VP, _I32, _VP, _VP, _VP]
         L.lsa_topk_select.argtypes = [ip, bud, _VP, _I64, _VP, _VP, _VP, _SZ, _VP]
+        L.lsa_topk_select_noalloc.argtypes = [ip, bud, _VP, _I64, _VP, _VP, _VP]
         L.lsa_page_summary.argtypes = [ip, _I32, _VP, _I32, _VP, _I64, _I64, _VP, _VP]
         L.lsa_page_recall.argtypes = [ip, bud, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
                                       _VP, _VP, _SZ, _VP]
@@ -72,7 +74,7 @@ def lib():
         L.lsa_workspace_bytes.restype = _SZ
         L.lsa_status_string.argtypes = [_I32]
         L.lsa_status_string.restype = ctypes.c_char_p
-        for f in EXPORTS[:5]:
+        for f in EXPORTS[:5] + ("lsa_topk_select_noalloc",):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -106,6 +108,12 @@ def lsa_topk_select(shape: IndexShape, budget: Budget, scores, n_cand: int, cand
     _check("lsa_topk_select", lib().lsa_topk_select(
         ctypes.byref(shape), budget, _p(scores), n_cand, _p(cand_ids), _p(idx), _p(ws),
         ws_bytes, _s(stream)))
+
+
+def lsa_topk_select_noalloc(shape: IndexShape, budget: Budget, scores, n_cand: int, cand_ids,
+                            idx, stream=None):
+    _check("lsa_topk_select_noalloc", lib().lsa_topk_select_noalloc(
+        ctypes.byref(shape), budget, _p(scores), n_cand, _p(cand_ids), _p(idx), _s(stream)))
 
 
 def lsa_page_summary(shape: IndexShape, page_size: int, keys, key_dtype: int, key_scale,
