@@ -1,17 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the LSA token-selection path on one MI355X.
 
-Headline step: one decode step of the 32-sequence x 128K-token workload (fp8 indexer keys,
-64 x 128 indexer, k = 2048 with a 64-token sink and a 960-token window, 16-head MLA attention
-over a 576-wide latent cache), all of it on the GPU:
+Headline workload: decode, 32 sequences x 131072 tokens (fp8 indexer keys, 64 x 128 indexer,
+k = 2048 with a 64-token sink and a 960-token window, 16-head MLA attention over a 576-wide
+latent cache).  One step is the whole path on the GPU, inputs resident in HBM:
     lsa_index_scores -> lsa_topk_select -> lsa_sparse_attn
-`value` = queries completed per second through that whole step (inputs resident in HBM).
-Per-stage HIP-event times give the indexed queries/s (score + top-k) and the sparse-attention
-TB/s.  Extra sections (not the headline): chunked prefill 8K @ 128K, Hierarchical Indexing at
-1M tokens (with flat indexing at 1M for comparison), and Cross-Layer Indexing over 4 layers at
-256K.  The CPU oracle is timed on a bounded sample of the headline workload.
+`value` is the metric's indexed queries/s: queries / (score + top-k time), from HIP events
+recorded around each stage of the K timed steps; `ms_per_step` is the wall time of a whole step
+(attention included).  Every stage is also timed on its own, >= 50 runs (or >= 200 ms), warm
+(back to back) and cold (L2 and the 256 MB MALL flushed by reading 1 GiB before each run), as
+median / p10 / p90 / mean.  Extra sections: chunked prefill 8K @ 128K, Hierarchical Indexing at
+1M tokens and at 256K (flat indexing timed beside it, planted-page recall and HI/flat overlap
+reported), cross-layer reuse over 4 layers.  The CPU oracle is timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
+    python bench.py --only STAGE [--cold] --steps N     (one stage N times, for rocprofv3)
 """
 from __future__ import annotations
 
@@ -30,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "indexed queries/s (score+top-k) and sparse-attn TB/s at 128K and 1M ctx, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
+FLUSH_BYTES = 1 << 30
 
 
 def log(*a):
@@ -37,16 +41,24 @@ def log(*a):
 
 
 # ----------------------------------------------------------------------------- byte / flop counts
-def score_bytes(n_queries_keys: int, d: int, fp8: bool, H: int, n_queries: int) -> float:
-    """Algorithmic bytes of scoring: keys (+ per-token scale) once per (query, key) pair for
-    decode, q and w per query, one fp32 score written per pair."""
+def score_bytes(n_pairs: int, d: int, fp8: bool, H: int, n_queries: int) -> float:
+    """Algorithmic bytes of decode scoring: every valid (query, key) pair reads the key row (+ its
+    fp32 scale) and writes one fp32 score; every query reads its q and w."""
     kb = d * (1 if fp8 else 2) + (4 if fp8 else 0)
-    return n_queries_keys * (kb + 4) + n_queries * H * (2 * d + 4)
+    return n_pairs * (kb + 4) + n_queries * H * (2 * d + 4)
 
 
 def attn_bytes(n_sel: int, row_bytes: int, n_queries: int, Hq: int, d_qk: int, d_v: int,
                k: int) -> float:
+    """Selected rows gathered once each, plus q, out and the index list per query."""
     return n_sel * row_bytes + n_queries * (Hq * d_qk * 2 + Hq * d_v * 2 + k * 4)
+
+
+def recall_bytes(n_q: int, n_elig: int, d: int, M: int, P: int, fp8: bool) -> float:
+    """Page recall per query: eligible page keys (bf16) + coarse score written, then the recalled
+    pages' key rows (+ scales) with one fp32 score and one id written per candidate."""
+    kb = d * (1 if fp8 else 2) + (4 if fp8 else 0)
+    return n_q * (n_elig * (2 * d + 4) + M * P * (kb + 8))
 
 
 # ----------------------------------------------------------------------------- profile lookup
@@ -58,59 +70,83 @@ def source_digest(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def profile_traffic(name: str, kernel_sources) -> tuple:
+def profile_traffic(name: str, kernel_sources):
     """HBM bytes per launch recorded in profiles/<name>.txt by the PMC runs, if the kernel's
     sources are unchanged since (else None)."""
     path = os.path.join(ROOT, "profiles", name + ".txt")
     if not os.path.exists(path):
-        return None, None
+        return None
     txt = open(path).read()
     m_src = re.search(r"source_digest:\s*(\w+)", txt)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_src or not m_b:
-        return None, None
-    if m_src.group(1) != source_digest(kernel_sources):
-        return None, "stale"
-    return float(m_b.group(1)), path
+    if not m_src or not m_b or m_src.group(1) != source_digest(kernel_sources):
+        return None
+    return float(m_b.group(1))
 
 
-# ----------------------------------------------------------------------------- timing helper
-class StageTimer:
-    """HIP events recorded on the current stream around each stage of each step."""
+# ----------------------------------------------------------------------------- timing
+class Timing:
+    """HIP events on the current stream (the stream the binding hands the library), and a 1 GiB
+    buffer streamed through to flush L2 and the MALL before cold runs."""
 
-    def __init__(self, torch, names):
+    def __init__(self, torch):
         self.torch = torch
-        self.names = names
-        self.events = []
+        self._flush = None
 
-    def step(self):
-        evs = [self.torch.cuda.Event(enable_timing=True) for _ in range(len(self.names) + 1)]
-        self.events.append(evs)
-        return evs
+    def flush(self):
+        """Read 1 GiB (a sum into one preallocated scalar): every line of L2 and the MALL is
+        replaced by a clean one.  A read-only stream on purpose: a flush that wrote its buffer
+        would leave dirty lines whose write-back lands in the timed run that follows."""
+        if self._flush is None:
+            self._flush = self.torch.ones(FLUSH_BYTES // 4, dtype=self.torch.float32,
+                                          device="cuda")
+            self._acc = self.torch.zeros((), dtype=self.torch.float32, device="cuda")
+        self.torch.sum(self._flush, dim=0, out=self._acc)
 
-    def mean_ms(self):
-        out = {n: 0.0 for n in self.names}
-        for evs in self.events:
-            for i, n in enumerate(self.names):
-                out[n] += evs[i].elapsed_time(evs[i + 1])
-        return {n: v / max(1, len(self.events)) for n, v in out.items()}
+    def stats(self, fn, est_ms: float, cold: bool, runs=None):
+        """>= 50 runs (>= 200 ms for long stages) of fn, each between two events; returns
+        mean / median / p10 / p90 / min in ms."""
+        torch = self.torch
+        if runs is None:
+            runs = 50 if est_ms * 50 <= 1000 else max(15, math.ceil(200.0 / est_ms))
+        fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(runs):
+            if cold:
+                self.flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in evs)
+
+        def pct(p):
+            x = (len(t) - 1) * p
+            lo, hi = int(math.floor(x)), int(math.ceil(x))
+            return t[lo] + (t[hi] - t[lo]) * (x - lo)
+        return {"n": runs, "mean": sum(t) / len(t), "median": pct(0.5), "p10": pct(0.1),
+                "p90": pct(0.9), "min": t[0]}
+
+    def both(self, fn, est_ms, cold_too=True):
+        out = {"warm": self.stats(fn, est_ms, cold=False)}
+        if cold_too:
+            out["cold"] = self.stats(fn, est_ms, cold=True)
+        return out
 
 
-def run_timed(torch, fn, names, steps, warmup):
-    for _ in range(warmup):
-        fn(None)
-    torch.cuda.synchronize()
-    timer = StageTimer(torch, names)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        fn(timer.step())
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps * 1e3
-    return wall, timer.mean_ms()
+def rnd(x, nd=4):
+    if isinstance(x, dict):
+        return {k: rnd(v, nd) for k, v in x.items()}
+    if isinstance(x, float):
+        return float(f"{x:.{nd}g}")
+    return x
 
 
-# ----------------------------------------------------------------------------- sections
-def headline(torch, lsa, inputs, cfg, steps, warmup):
+# ----------------------------------------------------------------------------- headline
+def headline(torch, lsa, inputs, cfg, tm: Timing, steps, warmup):
     w = cfg.DECODE_128K
     s, b, a = w.index, w.budget, w.attn
     dev = "cuda"
@@ -123,40 +159,66 @@ def headline(torch, lsa, inputs, cfg, steps, warmup):
     out = torch.empty((B, 1, a.heads, a.d_v), dtype=torch.bfloat16, device=dev)
     ws, ws_sel = lsa.Workspace(), lsa.Workspace()
 
-    def step(ev):
-        if ev: ev[0].record()
+    def f_score():
         lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0, out=scores)
-        if ev: ev[1].record()
-        lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=L, q_pos0=s.q_pos0, out=idx, ws=ws_sel)
-        if ev: ev[2].record()
+
+    def f_topk():
+        lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=L, q_pos0=s.q_pos0, out=idx,
+                        ws=ws_sel)
+
+    def f_attn():
         lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale, b.sink, b.window, d_v=a.d_v,
                         ws=ws, out=out, want_lse=True)
-        if ev: ev[3].record()
 
-    log("[bench] headline: timing")
-    # wall time of the bare step; per-stage times from a second run with events between stages
-    wall, _ = run_timed(torch, lambda _ev: step(None), [], steps, warmup)
-    _, st = run_timed(torch, step, ["score", "topk", "attn"], steps, warmup)
+    for _ in range(warmup):
+        f_score(), f_topk(), f_attn()
+    torch.cuda.synchronize()
+    log(f"[bench] headline: {steps} timed steps")
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        f_score()
+        e[1].record()
+        f_topk()
+        e[2].record()
+        f_attn()
+        e[3].record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) / steps * 1e3
+    st = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps
+          for i, n in enumerate(("score", "topk", "attn"))}
+    log("[bench] headline: per-stage distributions (warm and cold)")
+    dist = {"score": tm.both(f_score, st["score"]), "topk": tm.both(f_topk, st["topk"]),
+            "attn": tm.both(f_attn, st["attn"])}
     n_q = B * s.n_q
     sb = score_bytes(n_q * L, s.head_dim, True, s.heads, n_q)
     ab = attn_bytes(n_q * b.k, a.d_qk * 2, n_q, a.heads, a.d_qk, a.d_v, b.k)
+    tb = n_q * (L - b.sink - b.window) * 4 + n_q * b.k * 4
     res = {
-        "wall_ms_per_step": wall,
-        "stage_ms": st,
+        "wall_ms_per_step": wall_ms, "stage_ms": st, "dist": dist,
         "indexed_qps": n_q / ((st["score"] + st["topk"]) * 1e-3),
-        "score_GBps": sb / (st["score"] * 1e-3) / 1e9,
-        "score_hbm_frac": sb / (st["score"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "score_algorithmic_bytes": sb,
-        "topk_GBps": n_q * (L - b.sink - b.window) * 4 / (st["topk"] * 1e-3) / 1e9,
+        "step_qps": n_q / (wall_ms * 1e-3),
+        "score_algorithmic_bytes": sb, "attn_algorithmic_bytes": ab, "topk_algorithmic_bytes": tb,
         "sparse_attn_TBps": ab / (st["attn"] * 1e-3) / 1e12,
-        "attn_algorithmic_bytes": ab,
+        "hbm_frac_cold_mean": {
+            "score": sb / (dist["score"]["cold"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "topk": tb / (dist["topk"]["cold"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "attn": ab / (dist["attn"]["cold"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "hbm_frac_warm_mean": {
+            "score": sb / (dist["score"]["warm"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "topk": tb / (dist["topk"]["warm"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "attn": ab / (dist["attn"]["warm"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
     del inp, att, scores, idx, out
     torch.cuda.empty_cache()
     return w, res
 
 
-def extra_prefill(torch, lsa, inputs, cfg, iters=3):
+# ----------------------------------------------------------------------------- extras
+def extra_prefill(torch, lsa, inputs, cfg, tm: Timing):
     w = cfg.PREFILL_8K_AT_128K
     s, b, a = w.index, w.budget, w.attn
     dev = "cuda"
@@ -167,163 +229,212 @@ def extra_prefill(torch, lsa, inputs, cfg, iters=3):
     out = torch.empty((1, s.n_q, a.heads, a.d_v), dtype=torch.bfloat16, device=dev)
     ws = lsa.Workspace()
 
-    def step(ev):
-        if ev: ev[0].record()
+    def f_score():
         lsa.index_scores(inp["q"], inp["w"], inp["keys"], None, q_pos0=s.q_pos0, out=scores)
-        if ev: ev[1].record()
+
+    def f_topk():
         lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=s.kv_len, q_pos0=s.q_pos0, out=idx,
                         ws=ws)
-        if ev: ev[2].record()
+
+    def f_attn():
         lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale, b.sink, b.window, d_v=a.d_v,
                         ws=ws, out=out, want_lse=False)
-        if ev: ev[3].record()
 
-    wall, st = run_timed(torch, step, ["score", "topk", "attn"], iters, 1)
+    f_score(), f_topk(), f_attn()
+    d = {"score": tm.both(f_score, 14.0),               # keys + q: 170 MB, cold matters
+         "topk": tm.both(f_topk, 0.85, cold_too=False),  # reads 4.2 GB: never cache-resident
+         "attn": tm.both(f_attn, 2.1)}
     V = [min(s.kv_len, s.q_pos0 + t + 1) for t in range(s.n_q)]
-    pairs = sum(V)
-    flops = 2.0 * pairs * s.heads * s.head_dim
+    flops = 2.0 * sum(V) * s.heads * s.head_dim
     mid = sum(max(0, v - b.sink - b.window) for v in V)
-    n_sel = s.n_q * b.k
+    t_s, t_k, t_a = (d["score"]["warm"]["mean"], d["topk"]["warm"]["mean"],
+                     d["attn"]["warm"]["mean"])
     res = {
-        "workload": w.name, "stage_ms": st, "wall_ms_per_step": wall,
-        "score_TFLOPs": flops / (st["score"] * 1e-3) / 1e12,
-        "score_mfma_frac": flops / (st["score"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
-        "topk_GBps": mid * 4 / (st["topk"] * 1e-3) / 1e9,
-        "topk_hbm_frac": mid * 4 / (st["topk"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "sparse_attn_effective_TBps": attn_bytes(n_sel, a.d_qk * 2, s.n_q, a.heads, a.d_qk, a.d_v, b.k)
-        / (st["attn"] * 1e-3) / 1e12,
-        "indexed_qps": s.n_q / ((st["score"] + st["topk"]) * 1e-3),
+        "workload": w.name, "dist": d,
+        "score_TFLOPs": flops / (t_s * 1e-3) / 1e12,
+        "score_mfma_frac": flops / (t_s * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+        "score_mfma_frac_cold": flops / (d["score"]["cold"]["mean"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+        "score_flops": flops,
+        "topk_GBps": (mid + s.n_q * b.k) * 4 / (t_k * 1e-3) / 1e9,
+        "topk_hbm_frac": (mid + s.n_q * b.k) * 4 / (t_k * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "sparse_attn_effective_TBps": attn_bytes(s.n_q * b.k, a.d_qk * 2, s.n_q, a.heads, a.d_qk,
+                                                 a.d_v, b.k) / (t_a * 1e-3) / 1e12,
+        "indexed_qps": s.n_q / ((t_s + t_k) * 1e-3),
     }
     del inp, att, scores, idx, out
     torch.cuda.empty_cache()
     return res
 
 
-def extra_hi(torch, lsa, inputs, w, iters=10, layers=1):
+def extra_hi(torch, lsa, inputs, w, tm: Timing):
+    import numpy as np
     s, b, a, hi = w.index, w.budget, w.attn, w.hi
     dev = "cuda"
     inp = inputs.index_inputs(w, dev)
     B, L = s.batch, s.kv_len
-    pk = torch.empty((B, (L + hi.page - 1) // hi.page, s.head_dim), dtype=torch.bfloat16, device=dev)
+    n_pages = (L + hi.page - 1) // hi.page
+    pk = torch.empty((B, n_pages, s.head_dim), dtype=torch.bfloat16, device=dev)
     ws, ws_sel = lsa.Workspace(), lsa.Workspace()
-    # page keys: built once per completed page in a decode loop; timed as a full rebuild
-    wall_pk, st_pk = run_timed(
-        torch, lambda ev: (ev and ev[0].record(), lsa.page_summary(inp["keys"], inp["scale"],
-                                                                   hi.page, out=pk),
-                           ev and ev[1].record()), ["summary"], 3, 1)
+    n_q = B * s.n_q
+
+    def f_summary():  # built once per completed page in a decode loop; timed as a full rebuild
+        lsa.page_summary(inp["keys"], inp["scale"], hi.page, out=pk)
+
+    f_summary()
+    res_hold = {}
+
+    def f_recall():
+        res_hold["r"] = lsa.page_recall(inp["q"], inp["w"], pk, inp["keys"], inp["scale"], b.k,
+                                        b.sink, b.window, hi.page, hi.m_pages, q_pos0=s.q_pos0,
+                                        ws=ws)
+
+    f_recall()
     idx = torch.empty((B, 1, b.k), dtype=torch.int32, device=dev)
 
-    def hi_step(ev):
-        if ev: ev[0].record()
-        pid, cs, ci = lsa.page_recall(inp["q"], inp["w"], pk, inp["keys"], inp["scale"], b.k,
-                                      b.sink, b.window, hi.page, hi.m_pages, q_pos0=s.q_pos0, ws=ws)
-        if ev: ev[1].record()
-        lsa.topk_select(cs, b.k, b.sink, b.window, kv_len=L, q_pos0=s.q_pos0, cand_ids=ci, out=idx,
-                        ws=ws_sel)
-        if ev: ev[2].record()
+    def f_hi_topk():
+        _, cs, ci = res_hold["r"]
+        lsa.topk_select(cs, b.k, b.sink, b.window, kv_len=L, q_pos0=s.q_pos0, cand_ids=ci,
+                        out=idx, ws=ws_sel)
 
-    _, st_hi = run_timed(torch, hi_step, ["recall", "topk"], iters, 2)
     scores = torch.empty((B, 1, L), dtype=torch.float32, device=dev)
     idx_f = torch.empty_like(idx)
 
-    def flat_step(ev):
-        if ev: ev[0].record()
+    def f_flat_score():
         lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0, out=scores)
-        if ev: ev[1].record()
+
+    def f_flat_topk():
         lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=L, q_pos0=s.q_pos0, out=idx_f,
                         ws=ws_sel)
-        if ev: ev[2].record()
 
-    _, st_flat = run_timed(torch, flat_step, ["score", "topk"], iters, 2)
-    del scores, idx_f
+    f_hi_topk(), f_flat_score(), f_flat_topk()
+    d = {"page_summary": tm.both(f_summary, 0.12), "recall": tm.both(f_recall, 0.04),
+         "hi_topk": tm.both(f_hi_topk, 0.02), "flat_score": tm.both(f_flat_score, 0.1),
+         "flat_topk": tm.both(f_flat_topk, 0.03)}
+    f_recall(), f_hi_topk(), f_flat_score(), f_flat_topk()
+    torch.cuda.synchronize()
+    # quality: planted pages recalled, overlap of the HI and flat dynamic picks
+    gi, fl = idx.cpu().numpy(), idx_f.cpu().numpy()
+    dd = b.sink + b.window
+    overlap = float(np.mean([np.isin(gi[r, 0, dd:], fl[r, 0, dd:]).mean() for r in range(B)]))
+    quality = {"hi_flat_dynamic_overlap": overlap}
+    if w.planted_frac > 0:
+        pid = res_hold["r"][0].cpu().numpy()
+        rec = [float(np.isin(inputs.planted_pages(w, r, dev).cpu().numpy(), pid[r, 0]).mean())
+               for r in range(B)]
+        quality["planted_pages_per_seq"] = int(round(w.planted_frac * n_pages))
+        quality["planted_recall_mean"] = float(np.mean(rec))
+        quality["planted_recall_min"] = float(np.min(rec))
+    del scores, idx_f, res_hold
+    torch.cuda.empty_cache()
     # attention layers sharing the HI index list
-    atts = [inputs.attn_inputs(w, l, dev) for l in range(layers)]
+    atts = [inputs.attn_inputs(w, l, dev) for l in range(w.layers)]
     outs = [torch.empty((B, 1, a.heads, a.d_v), dtype=torch.bfloat16, device=dev) for _ in atts]
 
-    def attn_step(ev):
-        if ev: ev[0].record()
+    def f_attn():
         for at, o in zip(atts, outs):
             lsa.sparse_attn(at["q"], at["kv"], None, idx, a.scale, b.sink, b.window, d_v=a.d_v,
                             ws=ws, out=o, want_lse=False)
-        if ev: ev[1].record()
 
-    _, st_attn = run_timed(torch, attn_step, ["attn"], iters, 2)
-    n_q = B * s.n_q
-    t_hi = st_hi["recall"] + st_hi["topk"]
-    t_flat = st_flat["score"] + st_flat["topk"]
-    ab = attn_bytes(n_q * b.k, a.d_qk * 2, n_q, a.heads, a.d_qk, a.d_v, b.k) * layers
+    d["attn_all_layers"] = tm.both(f_attn, 0.02 * w.layers)
+    t = {k: v["warm"]["mean"] for k, v in d.items()}
+    tc = {k: v["cold"]["mean"] for k, v in d.items()}
+    t_hi, t_flat = t["recall"] + t["hi_topk"], t["flat_score"] + t["flat_topk"]
+    ab = attn_bytes(n_q * b.k, a.d_qk * 2, n_q, a.heads, a.d_qk, a.d_v, b.k) * w.layers
+    n_elig = (L - b.window - 1) // hi.page - b.sink // hi.page + 1
+    rb = recall_bytes(n_q, n_elig, s.head_dim, hi.m_pages, hi.page, s.key_dtype == "fp8")
     res = {
-        "workload": w.name,
-        "page_summary_ms": st_pk["summary"],
-        "page_summary_GBps": B * L * (s.head_dim + 4) / (st_pk["summary"] * 1e-3) / 1e9,
-        "hi_stage_ms": st_hi, "flat_stage_ms": st_flat,
-        "hi_indexed_qps": n_q / (t_hi * 1e-3),
-        "flat_indexed_qps": n_q / (t_flat * 1e-3),
+        "workload": w.name, "dist": d, "quality": quality,
+        "page_summary_GBps": B * L * (s.head_dim + 4) / (t["page_summary"] * 1e-3) / 1e9,
+        "page_summary_hbm_frac_cold": B * L * (s.head_dim + 4 + 2 * s.head_dim / hi.page)
+        / (tc["page_summary"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "recall_algorithmic_bytes": rb,
+        "hi_indexed_qps": n_q / (t_hi * 1e-3), "flat_indexed_qps": n_q / (t_flat * 1e-3),
         "hi_speedup_vs_flat": t_flat / t_hi,
-        "attn_layers": layers,
-        "attn_ms_all_layers": st_attn["attn"],
-        "sparse_attn_TBps": ab / (st_attn["attn"] * 1e-3) / 1e12,
+        "hi_speedup_vs_flat_cold": (tc["flat_score"] + tc["flat_topk"]) / (tc["recall"] + tc["hi_topk"]),
+        "attn_layers": w.layers,
+        "sparse_attn_TBps": ab / (t["attn_all_layers"] * 1e-3) / 1e12,
     }
     del inp, atts, outs, pk, idx
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(inputs, cfg, budget_s=15.0):
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inputs, cfg, budget_s=12.0, budget_1t_s=8.0):
     """The oracle, as it stands, on a bounded sample of the headline workload: whole decode
-    steps (scores, selection, attention) of as many sequences as fit in ~budget_s seconds."""
+    queries (scores over 131072 fp8 keys, selection, 16-head MLA attention), each stage timed,
+    on all the threads it is given and on one.  The value is indexed queries/s (score +
+    selection), the metric's own quantity."""
     import numpy as np
     import torch
 
     from oracle import ref
     w = cfg.DECODE_128K
     s, b, a = w.index, w.budget, w.attn
-    n_max = 16
-    inp = inputs.index_inputs(cfg.shrink(w, batch=n_max), "cpu")
-    att = inputs.attn_inputs(cfg.shrink(w, batch=n_max), 0, "cpu")
+    n_max = 8
+    small = cfg.shrink(w, batch=n_max)
+    inp = inputs.index_inputs(small, "cpu")
+    att = inputs.attn_inputs(small, 0, "cpu")
 
     def np16(t):
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
-    done, t0 = 0, time.perf_counter()
-    while done < n_max:
-        q, wt = np16(inp["q"][done]), inp["w"][done].numpy()
-        keys, scale = inp["keys"][done].numpy().view(np.uint8), inp["scale"][done].numpy()
-        I, _, _ = ref.index_scores(q, wt, keys, scale, np.array([s.q_pos0]))
-        idx = ref.select(I.astype(np.float32), np.array([s.kv_len]), b.k, b.sink, b.window)
-        ref.sparse_attn(np16(att["q"][done]), np16(att["kv"][done]), None, idx, a.scale,
-                        d_qk=a.d_qk, d_v=a.d_v)
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "queries/s", "cores": ref.num_threads(), "kind": "oracle",
-            "sample": f"{done} of the 32 decode queries (whole step: scores over 131072 fp8 keys, "
-                      f"selection, 16-head MLA attention), {dt:.1f} s"}
+    def run(limit_s, threads):
+        ref.set_num_threads(threads)
+        tot = {"score": 0.0, "select": 0.0, "attn": 0.0}
+        done, t_start = 0, time.perf_counter()
+        while done < n_max:
+            q, wt = np16(inp["q"][done]), inp["w"][done].numpy()
+            keys, scale = inp["keys"][done].numpy().view(np.uint8), inp["scale"][done].numpy()
+            t0 = time.perf_counter()
+            I, _, _ = ref.index_scores(q, wt, keys, scale, np.array([s.q_pos0]))
+            t1 = time.perf_counter()
+            idx = ref.select(I.astype(np.float32), np.array([s.kv_len]), b.k, b.sink, b.window)
+            t2 = time.perf_counter()
+            ref.sparse_attn(np16(att["q"][done]), np16(att["kv"][done]), None, idx, a.scale,
+                            d_qk=a.d_qk, d_v=a.d_v)
+            t3 = time.perf_counter()
+            tot["score"] += t1 - t0
+            tot["select"] += t2 - t1
+            tot["attn"] += t3 - t2
+            done += 1
+            if time.perf_counter() - t_start > limit_s:
+                break
+        per_q = {k: v / done for k, v in tot.items()}
+        return done, per_q
+
+    nthreads = ref.num_threads()
+    done, per_q = run(budget_s, nthreads)
+    done1, per_q1 = run(budget_1t_s, 1)
+    ref.set_num_threads(nthreads)
+    return {"value": 1.0 / (per_q["score"] + per_q["select"]), "unit": "queries/s",
+            "cores": nthreads, "kind": "oracle",
+            "sample": f"{done} of the 32 decode queries of the 32 x 131072 workload (fp64 scores "
+                      f"over 131072 fp8 keys + selection; attention timed beside), {nthreads} "
+                      f"OpenMP threads",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "stage_s_per_query": per_q,
+            "value_1thread": 1.0 / (per_q1["score"] + per_q1["select"]),
+            "stage_s_per_query_1thread": per_q1,
+            "sample_1thread": f"{done1} decode queries on 1 thread"}
 
 
-def only_stage(torch, lsa, inputs, cfg, stage, steps):
-    """One stage of the headline decode step (or of the chunked prefill), `steps` times, for
-    counter runs.  `copy` is the calibration kernel: out = src + 0 over 256 MiB of fp32 (reads
-    and writes 256 MiB)."""
+# ----------------------------------------------------------------------------- single stages
+def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
+    """One stage, `steps` times (cold: L2 + MALL flushed before each), for counter and trace
+    runs.  `copy` is the calibration kernel: out = src + 0 over 256 MiB of fp32."""
     dev = "cuda"
-    if stage.startswith("prefill_"):
-        w = cfg.PREFILL_8K_AT_128K
-        s, b = w.index, w.budget
-        inp = inputs.index_inputs(w, dev)
-        scores = lsa.index_scores(inp["q"], inp["w"], inp["keys"], None, q_pos0=s.q_pos0)
-        ws = lsa.Workspace()
-        idx = lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=s.kv_len, q_pos0=s.q_pos0, ws=ws)
-        torch.cuda.synchronize()
-        for _ in range(steps):
-            if stage == "prefill_score":
-                lsa.index_scores(inp["q"], inp["w"], inp["keys"], None, q_pos0=s.q_pos0, out=scores)
-            else:
-                lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=s.kv_len, q_pos0=s.q_pos0,
-                                out=idx, ws=ws)
-        torch.cuda.synchronize()
-        log(f"[bench] {stage} x{steps} done")
-        return
+    tm = Timing(torch)
     if stage == "copy":
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -332,39 +443,77 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps):
         torch.cuda.synchronize()
         log(f"[bench] copy x{steps}: {src.numel() * 4} bytes read and written per launch")
         return
-    w = cfg.DECODE_128K
-    s, b, a = w.index, w.budget, w.attn
-    inp = inputs.index_inputs(w, dev)
-    L = s.kv_len
-    scores = lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0)
-    ws = lsa.Workspace()
-    idx = lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=L, q_pos0=s.q_pos0, ws=ws)
-    att = inputs.attn_inputs(w, 0, dev) if stage == "attn" else None
+    if stage.startswith("prefill_"):
+        w = cfg.PREFILL_8K_AT_128K
+        s, b, a = w.index, w.budget, w.attn
+        inp = inputs.index_inputs(w, dev)
+        scores = lsa.index_scores(inp["q"], inp["w"], inp["keys"], None, q_pos0=s.q_pos0)
+        ws = lsa.Workspace()
+        idx = lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=s.kv_len, q_pos0=s.q_pos0, ws=ws)
+        att = inputs.attn_inputs(w, 0, dev) if stage == "prefill_attn" else None
+        fns = {"prefill_score": lambda: lsa.index_scores(inp["q"], inp["w"], inp["keys"], None,
+                                                          q_pos0=s.q_pos0, out=scores),
+               "prefill_topk": lambda: lsa.topk_select(scores, b.k, b.sink, b.window,
+                                                        kv_len=s.kv_len, q_pos0=s.q_pos0,
+                                                        out=idx, ws=ws),
+               "prefill_attn": lambda: lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale,
+                                                        b.sink, b.window, d_v=a.d_v, ws=ws,
+                                                        want_lse=False)}
+    elif stage.startswith("hi1m_"):
+        w = cfg.DECODE_1M_HI
+        s, b, hi = w.index, w.budget, w.hi
+        inp = inputs.index_inputs(w, dev)
+        pk = lsa.page_summary(inp["keys"], inp["scale"], hi.page)
+        ws, ws_sel = lsa.Workspace(), lsa.Workspace()
+        r = lsa.page_recall(inp["q"], inp["w"], pk, inp["keys"], inp["scale"], b.k, b.sink,
+                            b.window, hi.page, hi.m_pages, q_pos0=s.q_pos0, ws=ws)
+        fns = {"hi1m_summary": lambda: lsa.page_summary(inp["keys"], inp["scale"], hi.page, out=pk),
+               "hi1m_recall": lambda: lsa.page_recall(inp["q"], inp["w"], pk, inp["keys"],
+                                                      inp["scale"], b.k, b.sink, b.window,
+                                                      hi.page, hi.m_pages, q_pos0=s.q_pos0, ws=ws),
+               "hi1m_topk": lambda: lsa.topk_select(r[1], b.k, b.sink, b.window, kv_len=s.kv_len,
+                                                    q_pos0=s.q_pos0, cand_ids=r[2], ws=ws_sel)}
+    else:
+        w = cfg.DECODE_128K
+        s, b, a = w.index, w.budget, w.attn
+        inp = inputs.index_inputs(w, dev)
+        L = s.kv_len
+        scores = lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0)
+        ws = lsa.Workspace()
+        idx = lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=L, q_pos0=s.q_pos0, ws=ws)
+        att = inputs.attn_inputs(w, 0, dev) if stage == "attn" else None
+        fns = {"score": lambda: lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"],
+                                                 q_pos0=s.q_pos0, out=scores),
+               "topk": lambda: lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=L,
+                                               q_pos0=s.q_pos0, out=idx, ws=ws),
+               "attn": lambda: lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale, b.sink,
+                                               b.window, d_v=a.d_v, ws=ws)}
+    fn = fns[stage]
+    fn()
     torch.cuda.synchronize()
     for _ in range(steps):
-        if stage == "score":
-            lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0,
-                             out=scores)
-        elif stage == "topk":
-            lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=L, q_pos0=s.q_pos0, out=idx,
-                            ws=ws)
-        else:
-            lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale, b.sink, b.window,
-                            d_v=a.d_v, ws=ws)
+        if cold:
+            tm.flush()
+        fn()
     torch.cuda.synchronize()
-    log(f"[bench] {stage} x{steps} done")
+    log(f"[bench] {stage} x{steps} ({'cold' if cold else 'warm'}) done")
+
+
+STAGES = ["score", "topk", "attn", "copy", "prefill_score", "prefill_topk", "prefill_attn",
+          "hi1m_summary", "hi1m_recall", "hi1m_topk"]
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--extras", action=argparse.BooleanOptionalAction, default=True)
     ap.add_argument("--cpu-baseline", action=argparse.BooleanOptionalAction, default=True)
-    ap.add_argument("--only", choices=["score", "topk", "attn", "copy", "prefill_score", "prefill_topk"],
-                    help="run one stage of the headline step (or a plain 256 MiB device copy) "
-                         "--steps times and exit; for hardware-counter runs under rocprofv3")
+    ap.add_argument("--only", choices=STAGES,
+                    help="run one stage --steps times and exit (for rocprofv3 runs); copy is a "
+                         "plain 256 MiB device copy used to calibrate the traffic counters")
+    ap.add_argument("--cold", action="store_true", help="with --only: flush L2 and MALL first")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -384,51 +533,60 @@ def main():
     lsa.lib()
     torch.cuda.set_device(0)
     if args.only:
-        only_stage(torch, lsa, inputs, cfg, args.only, args.steps)
+        only_stage(torch, lsa, inputs, cfg, args.only, args.steps, args.cold)
         return
 
-    w, head = headline(torch, lsa, inputs, cfg, args.steps, args.warmup)
+    tm = Timing(torch)
+    w, head = headline(torch, lsa, inputs, cfg, tm, args.steps, args.warmup)
     s, b = w.index, w.budget
     n_q = s.batch * s.n_q
-    value = n_q / (head["wall_ms_per_step"] * 1e-3)
 
     score_src = ["token_selection_indexer_amd/csrc/score.hip",
                  "token_selection_indexer_amd/csrc/device.hpp"]
-    traffic, _ = profile_traffic("score_stream_decode_b32_128k_pmc", score_src)
-    t_score = head["stage_ms"]["score"] * 1e-3
-    roof = {"kernel": "score_stream_kernel (lsa_index_scores, fp8 keys, decode)",
-            "bound": "hbm", "achieved": head["score_algorithmic_bytes"] / t_score / 1e9,
-            "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": head["score_algorithmic_bytes"] / t_score / 1e9 / HBM_PEAK_GBS,
-            "traffic": traffic}
+    t_cold = head["dist"]["score"]["cold"]["mean"] * 1e-3
+    t_warm = head["dist"]["score"]["warm"]["mean"] * 1e-3
+    sb = head["score_algorithmic_bytes"]
+    roof = {"kernel": "score_stream_kernel (lsa_index_scores, fp8 keys, decode 32 x 131072)",
+            "bound": "hbm", "achieved": sb / t_cold / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": sb / t_cold / 1e9 / HBM_PEAK_GBS,
+            "traffic": profile_traffic("score_stream_decode_b32_128k_pmc", score_src),
+            "algorithmic_bytes_per_launch": sb,
+            "timing": "mean of 50 cold runs (L2 + MALL flushed by a 1 GiB read before each), "
+                      "HIP events on the library's stream",
+            "frac_warm": sb / t_warm / 1e9 / HBM_PEAK_GBS}
 
     extras = {}
     if args.extras:
         log("[bench] extra: chunked prefill 8K @ 128K")
-        extras["prefill_8k_128k"] = extra_prefill(torch, lsa, inputs, cfg)
+        extras["prefill_8k_128k"] = extra_prefill(torch, lsa, inputs, cfg, tm)
         log("[bench] extra: HI at 1M")
-        extras["decode_1m_hi"] = extra_hi(torch, lsa, inputs, cfg.DECODE_1M_HI)
+        extras["decode_1m_hi"] = extra_hi(torch, lsa, inputs, cfg.DECODE_1M_HI, tm)
         log("[bench] extra: HI + cross-layer x4 at 256K")
-        extras["decode_256k_hi_cli4"] = extra_hi(torch, lsa, inputs, cfg.DECODE_256K_HI_CLI,
-                                                 layers=cfg.DECODE_256K_HI_CLI.layers)
+        extras["decode_256k_hi_cli4"] = extra_hi(torch, lsa, inputs, cfg.DECODE_256K_HI_CLI, tm)
     cpu = None
     if args.cpu_baseline:
         log("[bench] CPU oracle baseline")
         cpu = cpu_baseline(inputs, cfg)
 
     line = {
-        "metric": METRIC, "value": value, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": head["wall_ms_per_step"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "metric": METRIC, "value": head["indexed_qps"], "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["wall_ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
         "config": {"workload": w.name, "batch": s.batch, "kv_len": s.kv_len,
                    "indexer": f"{s.heads}x{s.head_dim} fp8-e4m3 keys", "k": b.k,
                    "sink": b.sink, "window": b.window, "attn": "MLA 16 heads, 576/512 latent"},
-        "indexed_qps": head["indexed_qps"],
+        "value_def": "queries / (score + top-k) from HIP events around each stage of the timed "
+                     "steps; ms_per_step is the whole step (score + top-k + attention)",
+        "step_qps": head["step_qps"],
         "sparse_attn_TBps": head["sparse_attn_TBps"],
         "stage_ms": head["stage_ms"],
+        "stage_dist_ms": rnd(head["dist"]),
+        "hbm_frac_cold_mean": head["hbm_frac_cold_mean"],
+        "hbm_frac_warm_mean": head["hbm_frac_warm_mean"],
         "roofline": roof,
         "cpu_baseline": cpu,
-        "extras": extras,
+        "extras": rnd(extras, 5),
     }
     print(json.dumps(line), flush=True)
 

@@ -37,6 +37,9 @@
 /* Threads the parallel loops below use (for reporting CPU timings). */
 int lsa_ref_num_threads(void) { return omp_get_max_threads(); }
 
+/* Set the thread count of the parallel loops (timing runs on one core, or on all of them). */
+void lsa_ref_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* ------------------------------------------------------------------------------------------ */
 /* Number formats.                                                                             */
 /* ------------------------------------------------------------------------------------------ */

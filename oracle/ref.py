@@ -32,6 +32,7 @@ def lib():
                                f"({LIB_PATH})")
         L = ctypes.CDLL(LIB_PATH)
         L.lsa_ref_num_threads.restype = ctypes.c_int
+        L.lsa_ref_set_num_threads.argtypes = [ctypes.c_int]
         L.lsa_ref_bf16_to_double.argtypes = [ctypes.c_uint16]
         L.lsa_ref_bf16_to_double.restype = ctypes.c_double
         L.lsa_ref_e4m3fn_to_double.argtypes = [ctypes.c_uint8]
@@ -68,6 +69,10 @@ def _key_args(keys, scale):
 
 def num_threads() -> int:
     return lib().lsa_ref_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().lsa_ref_set_num_threads(int(n))
 
 
 # --------------------------------------------------------------------------------- formats
