@@ -4,10 +4,10 @@
 Headline workload: decode, 32 sequences x 131072 tokens (fp8 indexer keys, 64 x 128 indexer,
 k = 2048 with a 64-token sink and a 960-token window, 16-head MLA attention over a 576-wide
 latent cache).  One step is the whole path on the GPU, inputs resident in HBM:
-    lsa_index_scores -> lsa_topk_select -> lsa_sparse_attn
+    lsa_index_select (scores + selection, fused) -> lsa_sparse_attn
 `value` is the metric's indexed queries/s: queries / (score + top-k time), from HIP events
 recorded around each stage of the K timed steps; `ms_per_step` is the wall time of a whole step
-(attention included).  Every stage is also timed on its own, >= 50 runs (or >= 200 ms), warm
+(attention included).  The unfused stages (lsa_index_scores, lsa_topk_select) are timed too.  Every stage is also timed on its own, >= 50 runs (or >= 200 ms), warm
 (back to back) and cold (L2 and the 256 MB MALL flushed by reading 1 GiB before each run), as
 median / p10 / p90 / mean.  Extra sections: chunked prefill 8K @ 128K, Hierarchical Indexing at
 1M tokens and at 256K (flat indexing timed beside it, planted-page recall and HI/flat overlap
@@ -157,7 +157,11 @@ def headline(torch, lsa, inputs, cfg, tm: Timing, steps, warmup):
     scores = torch.empty((B, 1, L), dtype=torch.float32, device=dev)
     idx = torch.empty((B, 1, b.k), dtype=torch.int32, device=dev)
     out = torch.empty((B, 1, a.heads, a.d_v), dtype=torch.bfloat16, device=dev)
-    ws, ws_sel = lsa.Workspace(), lsa.Workspace()
+    ws, ws_sel, ws_idx = lsa.Workspace(), lsa.Workspace(), lsa.Workspace()
+
+    def f_index():  # scores + selection, fused
+        lsa.index_select(inp["q"], inp["w"], inp["keys"], inp["scale"], b.k, b.sink, b.window,
+                         q_pos0=s.q_pos0, scores=scores, idx=idx, ws=ws_idx)
 
     def f_score():
         lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0, out=scores)
@@ -171,43 +175,45 @@ def headline(torch, lsa, inputs, cfg, tm: Timing, steps, warmup):
                         ws=ws, out=out, want_lse=True)
 
     for _ in range(warmup):
-        f_score(), f_topk(), f_attn()
+        f_index(), f_attn()
     torch.cuda.synchronize()
     log(f"[bench] headline: {steps} timed steps")
     evs = []
     t0 = time.perf_counter()
     for _ in range(steps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         e[0].record()
-        f_score()
+        f_index()
         e[1].record()
-        f_topk()
-        e[2].record()
         f_attn()
-        e[3].record()
+        e[2].record()
         evs.append(e)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) / steps * 1e3
     st = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps
-          for i, n in enumerate(("score", "topk", "attn"))}
+          for i, n in enumerate(("index", "attn"))}
     log("[bench] headline: per-stage distributions (warm and cold)")
-    dist = {"score": tm.both(f_score, st["score"]), "topk": tm.both(f_topk, st["topk"]),
-            "attn": tm.both(f_attn, st["attn"])}
+    dist = {"index": tm.both(f_index, st["index"]), "score": tm.both(f_score, 0.1),
+            "topk": tm.both(f_topk, 0.02), "attn": tm.both(f_attn, st["attn"])}
+    f_index()
     n_q = B * s.n_q
     sb = score_bytes(n_q * L, s.head_dim, True, s.heads, n_q)
     ab = attn_bytes(n_q * b.k, a.d_qk * 2, n_q, a.heads, a.d_qk, a.d_v, b.k)
     tb = n_q * (L - b.sink - b.window) * 4 + n_q * b.k * 4
     res = {
         "wall_ms_per_step": wall_ms, "stage_ms": st, "dist": dist,
-        "indexed_qps": n_q / ((st["score"] + st["topk"]) * 1e-3),
+        "indexed_qps": n_q / (st["index"] * 1e-3),
+        "indexed_qps_unfused": n_q / ((dist["score"]["warm"]["mean"] + dist["topk"]["warm"]["mean"]) * 1e-3),
         "step_qps": n_q / (wall_ms * 1e-3),
         "score_algorithmic_bytes": sb, "attn_algorithmic_bytes": ab, "topk_algorithmic_bytes": tb,
         "sparse_attn_TBps": ab / (st["attn"] * 1e-3) / 1e12,
         "hbm_frac_cold_mean": {
+            "index_fused": (sb + tb) / (dist["index"]["cold"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "score": sb / (dist["score"]["cold"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "topk": tb / (dist["topk"]["cold"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "attn": ab / (dist["attn"]["cold"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "hbm_frac_warm_mean": {
+            "index_fused": (sb + tb) / (dist["index"]["warm"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "score": sb / (dist["score"]["warm"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "topk": tb / (dist["topk"]["warm"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "attn": ab / (dist["attn"]["warm"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
@@ -306,11 +312,17 @@ def extra_hi(torch, lsa, inputs, w, tm: Timing):
         lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=L, q_pos0=s.q_pos0, out=idx_f,
                         ws=ws_sel)
 
-    f_hi_topk(), f_flat_score(), f_flat_topk()
+    ws_idx = lsa.Workspace()
+
+    def f_flat_index():  # flat scores + selection, fused (the faster flat path)
+        lsa.index_select(inp["q"], inp["w"], inp["keys"], inp["scale"], b.k, b.sink, b.window,
+                         q_pos0=s.q_pos0, scores=scores, idx=idx_f, ws=ws_idx)
+
+    f_hi_topk(), f_flat_score(), f_flat_topk(), f_flat_index()
     d = {"page_summary": tm.both(f_summary, 0.12), "recall": tm.both(f_recall, 0.04),
          "hi_topk": tm.both(f_hi_topk, 0.02), "flat_score": tm.both(f_flat_score, 0.1),
-         "flat_topk": tm.both(f_flat_topk, 0.03)}
-    f_recall(), f_hi_topk(), f_flat_score(), f_flat_topk()
+         "flat_topk": tm.both(f_flat_topk, 0.03), "flat_index_fused": tm.both(f_flat_index, 0.12)}
+    f_recall(), f_hi_topk(), f_flat_index()
     torch.cuda.synchronize()
     # quality: planted pages recalled, overlap of the HI and flat dynamic picks
     gi, fl = idx.cpu().numpy(), idx_f.cpu().numpy()
@@ -338,7 +350,7 @@ def extra_hi(torch, lsa, inputs, w, tm: Timing):
     d["attn_all_layers"] = tm.both(f_attn, 0.02 * w.layers)
     t = {k: v["warm"]["mean"] for k, v in d.items()}
     tc = {k: v["cold"]["mean"] for k, v in d.items()}
-    t_hi, t_flat = t["recall"] + t["hi_topk"], t["flat_score"] + t["flat_topk"]
+    t_hi, t_flat = t["recall"] + t["hi_topk"], t["flat_index_fused"]
     ab = attn_bytes(n_q * b.k, a.d_qk * 2, n_q, a.heads, a.d_qk, a.d_v, b.k) * w.layers
     n_elig = (L - b.window - 1) // hi.page - b.sink // hi.page + 1
     rb = recall_bytes(n_q, n_elig, s.head_dim, hi.m_pages, hi.page, s.key_dtype == "fp8")
@@ -350,7 +362,8 @@ def extra_hi(torch, lsa, inputs, w, tm: Timing):
         "recall_algorithmic_bytes": rb,
         "hi_indexed_qps": n_q / (t_hi * 1e-3), "flat_indexed_qps": n_q / (t_flat * 1e-3),
         "hi_speedup_vs_flat": t_flat / t_hi,
-        "hi_speedup_vs_flat_cold": (tc["flat_score"] + tc["flat_topk"]) / (tc["recall"] + tc["hi_topk"]),
+        "hi_speedup_vs_flat_cold": tc["flat_index_fused"] / (tc["recall"] + tc["hi_topk"]),
+        "hi_speedup_vs_flat_unfused": (t["flat_score"] + t["flat_topk"]) / t_hi,
         "attn_layers": w.layers,
         "sparse_attn_TBps": ab / (t["attn_all_layers"] * 1e-3) / 1e12,
     }
@@ -479,13 +492,16 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
         inp = inputs.index_inputs(w, dev)
         L = s.kv_len
         scores = lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0)
-        ws = lsa.Workspace()
+        ws, ws_idx = lsa.Workspace(), lsa.Workspace()
         idx = lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=L, q_pos0=s.q_pos0, ws=ws)
         att = inputs.attn_inputs(w, 0, dev) if stage == "attn" else None
         fns = {"score": lambda: lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"],
                                                  q_pos0=s.q_pos0, out=scores),
                "topk": lambda: lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=L,
                                                q_pos0=s.q_pos0, out=idx, ws=ws),
+               "index": lambda: lsa.index_select(inp["q"], inp["w"], inp["keys"], inp["scale"],
+                                                 b.k, b.sink, b.window, q_pos0=s.q_pos0,
+                                                 scores=scores, idx=idx, ws=ws_idx),
                "attn": lambda: lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale, b.sink,
                                                b.window, d_v=a.d_v, ws=ws)}
     fn = fns[stage]
@@ -499,7 +515,7 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
     log(f"[bench] {stage} x{steps} ({'cold' if cold else 'warm'}) done")
 
 
-STAGES = ["score", "topk", "attn", "copy", "prefill_score", "prefill_topk", "prefill_attn",
+STAGES = ["score", "topk", "index", "attn", "copy", "prefill_score", "prefill_topk", "prefill_attn",
           "hi1m_summary", "hi1m_recall", "hi1m_topk"]
 
 
@@ -576,8 +592,10 @@ def main():
         "config": {"workload": w.name, "batch": s.batch, "kv_len": s.kv_len,
                    "indexer": f"{s.heads}x{s.head_dim} fp8-e4m3 keys", "k": b.k,
                    "sink": b.sink, "window": b.window, "attn": "MLA 16 heads, 576/512 latent"},
-        "value_def": "queries / (score + top-k) from HIP events around each stage of the timed "
-                     "steps; ms_per_step is the whole step (score + top-k + attention)",
+        "value_def": "queries / (score + top-k time): HIP events around lsa_index_select "
+                     "(fused scores + selection) in each timed step; ms_per_step is the whole "
+                     "step (scores + selection + attention)",
+        "indexed_qps_unfused": head["indexed_qps_unfused"],
         "step_qps": head["step_qps"],
         "sparse_attn_TBps": head["sparse_attn_TBps"],
         "stage_ms": head["stage_ms"],

@@ -128,6 +128,28 @@ LSA_API lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budg
                            size_t ws_bytes, void *stream);
 
 /*
+ * lsa_index_select -- lsa_index_scores followed by lsa_topk_select (flat mode), fused for decode
+ * (Baidu Cloud article, "Engineering Implementation Breakthroughs: 1. Operator Fusion
+ * Optimization": scoring and selection as one operator, so the selection does not start from a
+ * cold pass over the score rows).  Outputs are bitwise those of the two calls with the same
+ * arguments: `scores` as lsa_index_scores writes it, `idx` as lsa_topk_select selects from it.
+ * For few long flat rows (decode: n_q <= 2, heads 32 or 64, enough keys for the long scoring
+ * launch, and rows long enough for the chunked selection) the scoring workgroups also histogram
+ * their middle-region scores while the scores are in registers, and the selection reads each
+ * row's exact threshold bin from those histograms instead of sampling the row before it
+ * compacts what lies at or above it.  Other shapes run the two ordinary paths.
+ *   q, w, keys, key_scale, scores   as for lsa_index_scores (scores 16-byte aligned)
+ *   idx     [B, n_q, k] int32 as for lsa_topk_select
+ *   ws      lsa_workspace_bytes(LSA_OP_INDEX_SELECT, shape, budget, 0, 0, 0, NULL) bytes,
+ *           256-byte aligned; its contents on entry do not matter
+ * Limits: those of lsa_index_scores and lsa_topk_select.
+ */
+LSA_API lsa_status lsa_index_select(const lsa_index_shape *shape, lsa_budget budget, const void *q,
+                                    const float *w, const void *keys, lsa_key_dtype key_dtype,
+                                    const float *key_scale, float *scores, int32_t *idx, void *ws,
+                                    size_t ws_bytes, void *stream);
+
+/*
  * lsa_topk_select_noalloc -- lsa_topk_select without a caller workspace, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation).  The selection and its result are those of lsa_topk_select with the
@@ -219,7 +241,8 @@ LSA_API lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_
                            const int32_t *idx, void *out, float *lse, void *ws, size_t ws_bytes,
                            void *stream);
 
-enum { LSA_OP_TOPK_SELECT = 1, LSA_OP_PAGE_RECALL = 2, LSA_OP_SPARSE_ATTN = 3 };
+enum { LSA_OP_TOPK_SELECT = 1, LSA_OP_PAGE_RECALL = 2, LSA_OP_SPARSE_ATTN = 3,
+       LSA_OP_INDEX_SELECT = 4 };
 
 /* Workspace bytes needed by `op` for these arguments (0 if none).  Arguments an op does not
  * use may be NULL / 0 (LSA_OP_TOPK_SELECT reads n_cand; 0 means flat, n_cand = kv_len).

@@ -1,0 +1,141 @@
+"""Decode scoring with the selection's histogram fused in (lsa_index_select) on the GPU.
+
+Its outputs must be bitwise those of lsa_index_scores followed by lsa_topk_select (which the
+other GPU tests tie to the oracle), and its selection bit-exact against the oracle's selection
+on the same fp32 scores.  Cases: the decode workload at full size, fp8 and bf16 keys, 32 and 64
+heads, a key count off the 32-key block (the moved-back last block must not be counted twice in
+the histogram), a causal cut short of the cache end, a second query per sequence, rows with
+V <= k, a row where every score ties (the histogram's threshold bin overflows the buffer: the
+exact fallback), and an unfused shape (the two ordinary launches).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref
+from token_selection_indexer_amd import inputs, lsa
+from token_selection_indexer_amd.configs import DECODE_128K, Budget, IndexShape, Workload, shrink
+from tests.gpu_checks import check_rows_exact, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lsa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _fused(q, w, keys, scale, b, q_pos0):
+    return lsa.index_select(q, w, keys, scale, b.k, b.sink, b.window, q_pos0=q_pos0)
+
+
+def _separate(q, w, keys, scale, b, q_pos0):
+    sc = lsa.index_scores(q, w, keys, scale, q_pos0=q_pos0)
+    idx = lsa.topk_select(sc, b.k, b.sink, b.window, kv_len=keys.shape[1], q_pos0=q_pos0)
+    return sc, idx
+
+
+def _is_fused(wl):
+    s, b = wl.index, wl.budget
+    shape = lsa.IndexShape(s.batch, s.n_q, s.heads, s.head_dim, s.kv_len, s.q_pos0)
+    fused = lsa.lsa_workspace_bytes(lsa.OP_INDEX_SELECT, shape, lsa.Budget(b.k, b.sink, b.window))
+    plain = lsa.lsa_workspace_bytes(lsa.OP_TOPK_SELECT, shape, lsa.Budget(b.k, b.sink, b.window))
+    return fused != plain
+
+
+def _case(wl, check_rows=None):
+    s, b = wl.index, wl.budget
+    inp = inputs.index_inputs(wl, DEV)
+    sc1, i1 = _fused(inp["q"], inp["w"], inp["keys"], inp["scale"], b, s.q_pos0)
+    sc2, i2 = _separate(inp["q"], inp["w"], inp["keys"], inp["scale"], b, s.q_pos0)
+    torch.cuda.synchronize()
+    assert torch.equal(sc1.view(torch.int32), sc2.view(torch.int32))
+    assert torch.equal(i1, i2)
+    scn, gi = sc1.cpu().numpy(), i1.cpu().numpy()
+    V = ref.valid_lengths(s.kv_len, s.q_pos0, s.n_q)
+    for r in (range(s.batch) if check_rows is None else check_rows):
+        check_rows_exact(gi[r], scn[r], V, b.k, b.sink, b.window)
+    return inp, sc1, i1
+
+
+def test_fused_decode_128k_full():
+    wl = DECODE_128K
+    assert _is_fused(wl)
+    _case(wl)
+    say("fused decode 32 x 128K: bitwise equal to the separate calls")
+
+
+# batch x blocks of 32 keys reach the long scoring launch (at least 65536 blocks), which is the
+# one that emits the histograms
+@pytest.mark.parametrize("kd,H,L,back,nq,B", [("fp8", 64, 131072 - 5, 0, 1, 16),
+                                              ("bf16", 64, 70000, 3000, 1, 32),
+                                              ("fp8", 32, 100003, 0, 2, 11),
+                                              ("bf16", 32, 90000, 17, 1, 24)])
+def test_fused_shapes(kd, H, L, back, nq, B):
+    wl = Workload(name="f", index=IndexShape(batch=B, n_q=nq, kv_len=L, q_pos0=L - nq - back,
+                                             heads=H, head_dim=128, key_dtype=kd),
+                  budget=Budget(k=2048, sink=64, window=960), attn=DECODE_128K.attn, seed=61 + H)
+    assert _is_fused(wl)
+    _case(wl)
+
+
+def test_fused_rows_within_budget_and_ties():
+    """Sequences whose query sees at most k keys take everything; a sequence whose keys are all
+    equal has one score for every key: its threshold bin holds the whole middle, which cannot
+    fit the buffer, so the exact one-workgroup path selects (lowest ids win the ties)."""
+    L, B = 131072, 16
+    wl = Workload(name="ft", index=IndexShape(batch=B, n_q=1, kv_len=L, q_pos0=L - 1, heads=64,
+                                              head_dim=128, key_dtype="fp8"),
+                  budget=Budget(k=2048, sink=64, window=960), attn=DECODE_128K.attn, seed=71)
+    inp = inputs.index_inputs(wl, DEV)
+    keys, scale = inp["keys"].clone(), inp["scale"].clone()
+    keys[1] = keys[1, 5]       # every key of sequence 1 equal
+    scale[1] = scale[1, 5]
+    b = wl.budget
+    assert _is_fused(wl)
+    for pos0 in (L - 1, 1000):  # decode, then a query that sees 1001 <= k keys
+        sc1, i1 = _fused(inp["q"], inp["w"], keys, scale, b, pos0)
+        sc2, i2 = _separate(inp["q"], inp["w"], keys, scale, b, pos0)
+        torch.cuda.synchronize()
+        assert torch.equal(sc1.view(torch.int32), sc2.view(torch.int32)), pos0
+        assert torch.equal(i1, i2), pos0
+        V = ref.valid_lengths(L, pos0, 1)
+        scn, gi = sc1.cpu().numpy(), i1.cpu().numpy()
+        for r in range(B):
+            check_rows_exact(gi[r], scn[r], V, b.k, b.sink, b.window)
+    sc1, i1 = _fused(inp["q"], inp["w"], keys, scale, b, L - 1)
+    gi = i1.cpu().numpy()
+    dyn = gi[1, 0, b.sink + b.window:]
+    assert np.array_equal(dyn, np.arange(b.sink, b.sink + b.k - b.sink - b.window))
+
+
+def test_unfused_shape_matches():
+    """A prefill chunk is not fused; lsa_index_select runs the two ordinary launches."""
+    wl = shrink(DECODE_128K, batch=1, n_q=40, kv_len=5000, q_pos0=4960)
+    assert not _is_fused(wl)
+    _case(wl)
+
+
+def test_fused_repeated_calls_reuse_workspace():
+    """The workspace is reused across calls with stale contents from the previous call (the
+    fine bins of groups that were empty are never read): identical results every time."""
+    wl = shrink(DECODE_128K, batch=32, kv_len=65536, q_pos0=65535)
+    s, b = wl.index, wl.budget
+    assert _is_fused(wl)
+    inp = inputs.index_inputs(wl, DEV)
+    ws = lsa.Workspace()
+    first = None
+    for rep in range(4):
+        sc, idx = lsa.index_select(inp["q"], inp["w"], inp["keys"], inp["scale"], b.k, b.sink,
+                                   b.window, q_pos0=s.q_pos0, ws=ws)
+        torch.cuda.synchronize()
+        if first is None:
+            first = (sc.clone(), idx.clone())
+        assert torch.equal(idx, first[1]) and torch.equal(sc, first[0]), rep
+    _, i2 = _separate(inp["q"], inp["w"], inp["keys"], inp["scale"], b, s.q_pos0)
+    assert torch.equal(first[1], i2)

@@ -70,6 +70,69 @@ lsa_status check_attn(const lsa_index_shape *s, const lsa_attn_shape *a, lsa_bud
     return LSA_OK;
 }
 
+// The fused score + select plan for a shape: histogram groups per row (0: not fused) and the
+// workspace layout (histograms, then the chunked selection's slices).
+struct FusedPlan {
+    int groups = 0;
+    size_t hist_fine = 0, hist_coarse = 0, select = 0, total = 0;
+};
+
+lsa::ScoreArgs score_args(const lsa_index_shape *shape, lsa_budget budget)
+{
+    lsa::ScoreArgs a{};
+    a.batch = shape->batch;
+    a.n_q = shape->n_q;
+    a.heads = shape->n_heads;
+    a.dim = shape->head_dim;
+    a.n_keys = shape->kv_len;
+    a.n_out = shape->kv_len;
+    a.kv_len = shape->kv_len;
+    a.q_pos0 = shape->q_pos0;
+    a.mask = lsa::MASK_CAUSAL;
+    a.k = budget.k;
+    a.sink = budget.sink;
+    a.window = budget.window;
+    return a;
+}
+
+lsa::SelectArgs select_args(const lsa_index_shape *shape, lsa_budget budget)
+{
+    lsa::SelectArgs a{};
+    a.batch = shape->batch;
+    a.n_q = shape->n_q;
+    a.n_in = shape->kv_len;
+    a.kv_len = shape->kv_len;
+    a.q_pos0 = shape->q_pos0;
+    a.k = budget.k;
+    a.sink = budget.sink;
+    a.window = budget.window;
+    a.mode = lsa::SELECT_SI;
+    a.out_stride = budget.k;
+    return a;
+}
+
+FusedPlan fused_plan(const lsa_index_shape *shape, lsa_budget budget)
+{
+    FusedPlan p;
+    const int64_t rows = (int64_t)shape->batch * shape->n_q;
+    p.select = lsa::select_workspace_bytes(rows, shape->kv_len, lsa::SELECT_SI);
+    p.total = p.select;
+    // fused only where the selection takes its chunked path (few long rows)
+    if (rows == 0 || p.select == 0) return p;
+    const int groups = lsa::score_hist_groups(score_args(shape, budget));
+    if (groups == 0) return p;
+    p.groups = groups;
+    p.hist_fine = round256((size_t)rows * groups * 2048 * 4);
+    p.hist_coarse = round256((size_t)rows * groups * 32 * 4);
+    p.total = p.hist_fine + p.hist_coarse + p.select;
+    return p;
+}
+
+size_t index_select_ws(const lsa_index_shape *shape, lsa_budget budget)
+{
+    return fused_plan(shape, budget).total;
+}
+
 } // namespace
 
 extern "C" {
@@ -105,6 +168,11 @@ size_t lsa_workspace_bytes(int op, const lsa_index_shape *shape, lsa_budget budg
             page_size > 256 || m_pages < 1)
             return (size_t)-1;
         return recall_ws(shape, page_size);
+    case LSA_OP_INDEX_SELECT: {
+        if (check_index_shape(shape) != LSA_OK || check_budget(budget) != LSA_OK)
+            return (size_t)-1;
+        return index_select_ws(shape, budget);
+    }
     case LSA_OP_SPARSE_ATTN:
         if (check_attn(shape, attn, budget) != LSA_OK) return (size_t)-1;
         return round256(lsa::attn_workspace_bytes(shape->batch, shape->n_q, attn->n_heads, attn->d_v,
@@ -182,6 +250,49 @@ lsa_status prepare_select(const lsa_index_shape *shape, lsa_budget budget, const
 }
 
 } // namespace
+
+lsa_status lsa_index_select(const lsa_index_shape *shape, lsa_budget budget, const void *q,
+                            const float *w, const void *keys, lsa_key_dtype key_dtype,
+                            const float *key_scale, float *scores, int32_t *idx, void *ws,
+                            size_t ws_bytes, void *stream)
+{
+    lsa_status st = check_index_shape(shape);
+    if (st != LSA_OK) return st;
+    if ((st = check_budget(budget)) != LSA_OK) return st;
+    if (budget.k - budget.sink - budget.window > 65536) return LSA_ERR_UNSUPPORTED;
+    if ((st = check_keys(key_dtype, keys, key_scale)) != LSA_OK) return st;
+    if (!q || !w || !scores || !idx) return LSA_ERR_NULL_POINTER;
+    if (!aligned(q, 16) || !aligned(w, 4) || !aligned(scores, 16) || !aligned(idx, 4))
+        return LSA_ERR_BAD_SHAPE;
+    if (shape->n_q > kMaxGridYZ * 64) return LSA_ERR_UNSUPPORTED;
+    const int64_t rows = (int64_t)shape->batch * shape->n_q;
+    if (rows >= (int64_t(1) << 31)) return LSA_ERR_UNSUPPORTED;
+    if (rows == 0) return LSA_OK;
+    const size_t need = index_select_ws(shape, budget);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, 256))) return LSA_ERR_WORKSPACE_TOO_SMALL;
+    const hipStream_t sm = static_cast<hipStream_t>(stream);
+    lsa::ScoreArgs a = score_args(shape, budget);
+    a.q = static_cast<const uint16_t *>(q);
+    a.w = w;
+    a.keys = keys;
+    a.kscale = key_scale;
+    a.out = scores;
+    a.fp8 = key_dtype == LSA_KEY_FP8_E4M3;
+    lsa::SelectArgs s = select_args(shape, budget);
+    s.scores = scores;
+    s.out = idx;
+    const FusedPlan p = fused_plan(shape, budget);
+    if (!p.groups) { // not the decode shape: the two ordinary paths
+        if ((st = device_status(lsa::launch_scores(a, sm))) != LSA_OK) return st;
+        return device_status(lsa::launch_select(s, ws, sm));
+    }
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    a.hist_fine = reinterpret_cast<uint32_t *>(base);
+    a.hist_coarse = reinterpret_cast<uint32_t *>(base + p.hist_fine);
+    if ((st = device_status(lsa::launch_scores(a, sm))) != LSA_OK) return st;
+    return device_status(lsa::launch_select_hist(s, base + p.hist_fine + p.hist_coarse,
+                                                 a.hist_fine, a.hist_coarse, p.groups, sm));
+}
 
 lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budget, const float *scores,
                            int64_t n_cand, const int32_t *cand_ids, int32_t *idx, void *ws,

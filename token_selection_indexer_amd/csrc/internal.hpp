@@ -30,6 +30,12 @@ struct ScoreArgs {
     int page;             // P (coarse and fine modes)
     int m_pages;          // fine mode
     int fp8;              // keys are e4m3 with per-row scales
+    // Decode selection fused into scoring (flat rows, one query per workgroup): each workgroup
+    // also writes the 2048-bin histogram (key bits 31..21) of its middle-region scores, as 32
+    // coarse sums of 64 bins each and the 64 fine bins of every non-empty group, to slice
+    // [row][blockIdx.x].
+    uint32_t *hist_fine;  // [rows][groups][2048] or nullptr
+    uint32_t *hist_coarse; // [rows][groups][32]
 };
 
 // Flat or coarse scores: out[b,t,s] for s < n_out == n_keys, -inf outside the row's range.
@@ -37,6 +43,9 @@ hipError_t launch_scores(const ScoreArgs &a, hipStream_t stream);
 // Fine scores over recalled pages: out / out_ids [b,t, i*P + j].
 hipError_t launch_fine_scores(const ScoreArgs &a, hipStream_t stream);
 bool scores_supported(int heads, int dim);
+// Workgroups per query row ("groups") of the flat launch when it can emit the selection
+// histograms (the long decode launch, one query per workgroup); 0 when it cannot.
+int score_hist_groups(const ScoreArgs &a);
 
 struct SelectArgs {
     const float *scores;     // [rows, n_in]
@@ -60,6 +69,10 @@ enum SelectMode : int {
 // Workspace of the selection (0 when one workgroup per row is used).
 size_t select_workspace_bytes(int64_t rows, int64_t n_in, int mode);
 hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream);
+// The same, with the scoring launch's row histograms (ScoreArgs::hist_*) for flat rows: the
+// chunked path reads each row's threshold bin from them instead of sampling the row.
+hipError_t launch_select_hist(const SelectArgs &a, void *ws, const uint32_t *hist_fine,
+                              const uint32_t *hist_coarse, int groups, hipStream_t stream);
 // The library's own per-device scratch for callers that cannot allocate: its size, and the
 // current device's address of it (looked up on the first call on each device).
 size_t select_scratch_bytes();

@@ -207,15 +207,29 @@ struct KeyBlock {
 // BPW > 0: each wave takes BPW blocks, the block loop fully unrolled.  BPW == 0: each wave takes
 // ceil(blocks / (gridDim.x * WAVES)) blocks in a loop whose body is one turn of the ring, so
 // every ring slot is still a compile-time constant while the code stays one ring long.
-template <bool FP8, int D, int H, int MT, bool ONEQ, bool FINE, int WAVES, int BPW, int PD = 1>
+// HIST (flat decode launch, one query per workgroup): the workgroup also counts its middle-region
+// scores [S, V-W) into a 2048-bin LDS histogram of key bits 31..21 while they are in registers,
+// and writes it (32 coarse sums of 64 bins, and the fine bins of the non-empty groups) to its
+// slice of a.hist_fine / a.hist_coarse, so the selection that follows reads the row's exact
+// threshold bin instead of sampling the row.
+template <bool FP8, int D, int H, int MT, bool ONEQ, bool FINE, int WAVES, int BPW, int PD = 1,
+          bool HIST = false>
 __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
 {
     using G = Geo<H, MT, ONEQ>;
     using KB = KeyBlock<FP8, D>;
     constexpr int KS = D / 16;
     static_assert(PD >= 1 && (BPW == 0 || PD < BPW), "ring shape");
+    static_assert(!HIST || (BPW == 0 && !FINE && G::NQW == 1 && G::SPLIT), "histogram launch");
+    constexpr int HBINS = 2048;
     // two slabs per wave: block i is transposed in slab i&1 while block i-1 may still be read
     __shared__ __attribute__((aligned(16))) uint8_t slabs[WAVES][2][KB::BB];
+    __shared__ __attribute__((aligned(16))) uint32_t lhist[HIST ? HBINS : 4];
+    if constexpr (HIST) {
+        for (int i = threadIdx.x; i < HBINS / 4; i += WAVES * kWave)
+            reinterpret_cast<uint4 *>(lhist)[i] = make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();
+    }
     const int b = blockIdx.z;
     const int64_t t0 = (int64_t)blockIdx.y * G::NQW;
     const int nq_avail = (int)min((int64_t)G::NQW, (int64_t)a.n_q - t0);
@@ -260,6 +274,14 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         }
     }
     hi_in = min(hi_in, a.n_keys);
+    // middle region of the (single) query row, for the histogram
+    int64_t mid_lo = 0, mid_hi = 0;
+    if constexpr (HIST) {
+        if (hi[0] > a.k) {
+            mid_lo = a.sink;
+            mid_hi = hi[0] - a.window;
+        }
+    }
 
     const uint8_t *keys_b = reinterpret_cast<const uint8_t *>(a.keys) + (int64_t)b * a.n_keys * KB::RB;
     const float *scale_b = FP8 ? a.kscale + (int64_t)b * a.n_keys : nullptr;
@@ -278,6 +300,7 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
 
     struct Blk {
         int64_t s0, row0; // first output slot and first key row of the block
+        int64_t fresh;    // rows below this were already covered by the previous block
         bool valid, live;
     };
     // BPW == 0 (flat rows, n_out == n_keys >= 32): every block is loaded in full and without a
@@ -290,8 +313,10 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         Blk k;
         const int64_t blk = ((int64_t)blockIdx.x * bpw + it) * WAVES + wv_id;
         k.valid = blk < n_blocks;
+        k.fresh = 0;
         if constexpr (FLAT_LOOP) {
             k.s0 = k.row0 = min(blk * 32, a.n_keys - 32);
+            k.fresh = blk * 32;
             k.live = k.valid && k.s0 < hi_all && k.s0 + 32 > lo_all;
             return k;
         }
@@ -397,6 +422,13 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
                               cb.s0 + 32 <= a.n_out && nq_avail == G::NQW;
             float *ob = a.out + ((int64_t)b * a.n_q + t0) * a.n_out + cb.s0;
             int32_t *ib = FINE ? a.out_ids + ((int64_t)b * a.n_q + t0) * a.n_out + cb.s0 : nullptr;
+            if constexpr (HIST) {
+                // each key once (the moved-back last block skips the rows it repeats), middle
+                // region only
+                const int64_t row = cb.row0 + n;
+                if (cb.live && row >= cb.fresh && row >= mid_lo && row < mid_hi)
+                    atomicAdd(&lhist[order_key(part[0]) >> 21], 1u);
+            }
             if (full) {
 #pragma unroll
                 for (int u = 0; u < G::NQL; ++u) {
@@ -425,6 +457,30 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
     } else {
         for (int it0 = 0; it0 < bpw; it0 += PD + 1)
             static_for<0, PD + 1>([&](auto J) { step(J, it0 + (int)decltype(J)::value); });
+    }
+    if constexpr (HIST) {
+        // every wave ran the same number of ring turns: all of them reach this barrier
+        __syncthreads();
+        const int64_t row = (int64_t)b * a.n_q + t0;
+        const int64_t slice = row * gridDim.x + blockIdx.x;
+        // coarse sums of 64 bins first; only the groups that hold keys (a few of the 32) have
+        // their 64 fine bins written -- the reader ignores the fine bins of an empty group
+        __shared__ uint32_t lcoarse[32];
+        if (threadIdx.x < 32) {
+            const uint4 *h4 = reinterpret_cast<const uint4 *>(lhist + 64 * threadIdx.x);
+            uint32_t c = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint4 v = h4[i];
+                c += v.x + v.y + v.z + v.w;
+            }
+            lcoarse[threadIdx.x] = c;
+            a.hist_coarse[slice * 32 + threadIdx.x] = c;
+        }
+        __syncthreads();
+        uint4 *hf = reinterpret_cast<uint4 *>(a.hist_fine + slice * HBINS);
+        for (int i = threadIdx.x; i < HBINS / 4; i += WAVES * kWave)
+            if (lcoarse[i / 16]) hf[i] = reinterpret_cast<const uint4 *>(lhist)[i];
     }
 }
 
@@ -612,6 +668,25 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
     }
 }
 
+constexpr int STREAM_WAVES = 4, STREAM_BPW_LONG = 32;
+
+// The long flat launch: one round of workgroups (about 512, two per CU), each wave streaming its
+// share of the row's 32-key blocks.
+bool long_launch(const ScoreArgs &a, int64_t rows)
+{
+    const int64_t n_blocks = (a.n_out + 31) / 32;
+    return n_blocks * rows * a.batch >= (int64_t)512 * STREAM_WAVES * STREAM_BPW_LONG &&
+           a.n_keys >= 32 && a.n_out == a.n_keys;
+}
+
+int64_t long_groups(const ScoreArgs &a, int64_t rows)
+{
+    const int64_t n_blocks = (a.n_out + 31) / 32;
+    const int64_t units = rows * a.batch;
+    const int64_t gx = std::max<int64_t>(1, (512 + units - 1) / units);
+    return std::min<int64_t>(gx, (n_blocks + STREAM_WAVES - 1) / STREAM_WAVES);
+}
+
 template <bool FP8, int D, int H>
 hipError_t launch_flat(const ScoreArgs &a, hipStream_t st)
 {
@@ -623,28 +698,35 @@ hipError_t launch_flat(const ScoreArgs &a, hipStream_t st)
         // (12 KB of keys at 4 KB per block) keep enough bytes outstanding per CU at two waves
         // per SIMD.  Short launches (page keys of Hierarchical Indexing, small batches) need
         // many workgroups more than long waves: two blocks per wave there.
-        constexpr int WAVES = 4, BPW_LONG = 32, BPW_SHORT = 2;
+        constexpr int WAVES = STREAM_WAVES, BPW_SHORT = 2;
         constexpr int PD = KeyBlock<FP8, D>::BB <= 4096 ? 3 : 1;
         const int64_t n_blocks = (a.n_out + 31) / 32;
         const int64_t rows = (a.n_q + G::NQW - 1) / G::NQW;
-        if (n_blocks * rows * a.batch >= (int64_t)512 * WAVES * BPW_LONG && a.n_keys >= 32 &&
-            a.n_out == a.n_keys) {
+        if (long_launch(a, rows)) {
             // one round of workgroups, two per CU (as many as are resident at once), each wave
             // streaming its share of blocks: no tail round, and the per-wave load of q and w
             // amortised over as many blocks as possible
-            const int64_t units = rows * a.batch;
-            const int64_t gx = std::max<int64_t>(1, (512 + units - 1) / units);
-            dim3 grid((unsigned)std::min<int64_t>(gx, (n_blocks + WAVES - 1) / WAVES),
-                      (unsigned)rows, (unsigned)a.batch);
+            dim3 grid((unsigned)long_groups(a, rows), (unsigned)rows, (unsigned)a.batch);
+            if constexpr (G::NQW == 1 && G::SPLIT) {
+                if (a.hist_fine) {
+                    hipLaunchKernelGGL(
+                        (score_stream_kernel<FP8, D, H, MT, false, false, WAVES, 0, PD, true>),
+                        grid, dim3(WAVES * kWave), 0, st, a);
+                    return hipGetLastError();
+                }
+            }
+            if (a.hist_fine) return hipErrorInvalidValue;
             hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, false, false, WAVES, 0, PD>),
                                grid, dim3(WAVES * kWave), 0, st, a);
         } else {
+            if (a.hist_fine) return hipErrorInvalidValue;
             dim3 grid((unsigned)((n_blocks + WAVES * BPW_SHORT - 1) / (WAVES * BPW_SHORT)),
                       (unsigned)rows, (unsigned)a.batch);
             hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, false, false, WAVES, BPW_SHORT, 1>),
                                grid, dim3(WAVES * kWave), 0, st, a);
         }
     } else {
+        if (a.hist_fine) return hipErrorInvalidValue;
         // 256-key tiles (139 KB of LDS, one workgroup per CU) where registers already limit
         // the CU to one workgroup (H = 64, d = 128: 252 VGPRs); 128-key tiles elsewhere, so two
         // workgroups can share a CU
@@ -701,6 +783,17 @@ bool scores_supported(int heads, int dim)
 }
 
 hipError_t launch_scores(const ScoreArgs &a, hipStream_t stream) { return dispatch(a, stream, false); }
+
+int score_hist_groups(const ScoreArgs &a)
+{
+    // the histogram launch: one query per wave row group (H = 32 or 64, split over the lane
+    // halves), few enough queries for the stream kernel, and the long launch
+    if (a.mask != MASK_CAUSAL || (a.heads != 32 && a.heads != 64)) return 0;
+    if (a.n_q > 2) return 0;
+    const int64_t rows = a.n_q;
+    if (!long_launch(a, rows)) return 0;
+    return (int)long_groups(a, rows);
+}
 
 hipError_t launch_fine_scores(const ScoreArgs &a, hipStream_t stream) { return dispatch(a, stream, true); }
 

@@ -1021,6 +1021,93 @@ __global__ __launch_bounds__(NT, 8) void select_kernel_flat(SelectArgs a) { sele
 
 __global__ __launch_bounds__(NT) void select_kernel_cand(SelectArgs a) { select_one_row<true>(a); }
 
+constexpr int HGROUPS = 32; // coarse sums of 64 bins each in the scoring launch's histograms
+
+// The row's threshold bin from the scoring workgroups' histograms: the 11-bit bin d (key bits
+// 31..21) holding the need-th largest middle-region key, how many keys lie above it and in it,
+// and the row's middle-region total.  First the 32 coarse sums (64 bins each) locate the 64-bin
+// group, then that group's 64 bins locate d; at each level the block's threads share the
+// groups x bins loads (all in flight at once) and one wave finishes the sums from LDS.  d = -1
+// when fewer than `need` keys compete.  Every thread of the NTH-thread block calls it; the
+// result is the same in every thread.  `part` holds 2 * NTH ints of LDS, `scratch` 6.
+template <int NTH>
+__device__ __forceinline__ Digit hist_threshold(int *part, int *scratch, const uint32_t *hist_fine,
+                                                const uint32_t *hist_coarse, int groups,
+                                                int64_t row, int need)
+{
+    static_assert(NTH % 64 == 0 && NTH >= 64, "whole waves");
+    constexpr int XC = NTH / HGROUPS, XF = NTH / 64; // slice strides per level
+    const int l = lane_id(), t = (int)threadIdx.x;
+    const uint32_t *hc = hist_coarse + row * groups * HGROUPS;
+    const uint32_t *hf = hist_fine + row * groups * NBIN;
+    {
+        const int bin = t % HGROUPS, x0 = t / HGROUPS;
+        int c = 0;
+        for (int x = x0; x < groups; x += XC) c += (int)hc[x * HGROUPS + bin];
+        part[t] = c;
+    }
+    __syncthreads();
+    if (t < kWave) {
+        // lane l < 32 holds coarse group 31 - l (top-down)
+        int mine = 0;
+        if (l < HGROUPS)
+#pragma unroll
+            for (int i = 0; i < XC; ++i) mine += part[i * HGROUPS + (HGROUPS - 1 - l)];
+        const int inc = wave_inclusive_scan(mine);
+        const uint64_t ge = __ballot(l < HGROUPS && inc >= need);
+        const int L = ge ? (int)__builtin_ctzll(ge) : 0;
+        const int exL = __builtin_amdgcn_readlane(inc, L) - __builtin_amdgcn_readlane(mine, L);
+        if (l == 0) {
+            scratch[0] = __builtin_amdgcn_readlane(inc, kWave - 1);
+            scratch[1] = ge ? L : -1;
+            scratch[2] = exL;
+        }
+    }
+    __syncthreads();
+    Digit r;
+    r.total = scratch[0];
+    r.d = -1;
+    r.above = 0;
+    r.at = 0;
+    const int L = scratch[1];
+    if (L < 0) return r; // uniform
+    const int exL = scratch[2];
+    const int top = 64 * (HGROUPS - 1 - L) + 63; // bin top - i is the i-th from the top
+    {
+        // a slice's fine bins are written only for the groups that hold keys: a group whose
+        // coarse sum is 0 contributes 0 (its fine bins are left from earlier calls)
+        const int i = t & 63, x0 = t >> 6, G = HGROUPS - 1 - L;
+        int c = 0;
+        for (int x = x0; x < groups; x += XF) {
+            const int cg = (int)hc[x * HGROUPS + G];
+            const int f = (int)hf[x * NBIN + top - i];
+            c += cg ? f : 0;
+        }
+        part[NTH + t] = c;
+    }
+    __syncthreads();
+    if (t < kWave) {
+        int c = 0;
+#pragma unroll
+        for (int k = 0; k < XF; ++k) c += part[NTH + k * 64 + l];
+        const int inc2 = exL + wave_inclusive_scan(c);
+        const uint64_t ge2 = __ballot(inc2 >= need);
+        const int i = (int)__builtin_ctzll(ge2); // exists: the group's keys reach `need`
+        const int ab = __builtin_amdgcn_readlane(inc2, i) - __builtin_amdgcn_readlane(c, i);
+        const int at = __builtin_amdgcn_readlane(c, i);
+        if (l == 0) {
+            scratch[3] = top - i;
+            scratch[4] = ab;
+            scratch[5] = at;
+        }
+    }
+    __syncthreads();
+    r.d = scratch[3];
+    r.above = scratch[4];
+    r.at = scratch[5];
+    return r;
+}
+
 // ------------------------------------------------------------------------------------------
 // Chunked path
 // ------------------------------------------------------------------------------------------
@@ -1034,6 +1121,10 @@ struct ChunkWs {
     float *cval;    // [rows][n_chunks][CHUNK_CAP] scores of the collected elements
     int32_t *cid;   // [rows][n_chunks][CHUNK_CAP] their ids
     int n_chunks;
+    // the scoring launch's histograms of the rows (flat decode rows), or nullptr: then the
+    // threshold is sampled from the row
+    const uint32_t *hist_fine, *hist_coarse;
+    int groups;
 };
 
 // Every chunk of a row derives the row's sampled threshold T (the same T in every workgroup)
@@ -1045,6 +1136,7 @@ __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a
 {
     __shared__ __align__(16) int hist[NBIN];
     __shared__ int scratch[CNT_WAVES + 8];
+    static_assert(2 * CNT_THREADS <= NBIN, "histogram partial sums fit");
     __shared__ __align__(16) uint32_t small[kWave];
     __shared__ int wcnt[CNT_WAVES];
     const int64_t row = blockIdx.y;
@@ -1085,11 +1177,21 @@ __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a
             if (CAND) id[j] = r.ids[pc];
         }
     }
-    // 1024 samples up to 256K positions, 4096 beyond (the expected sampled rank stays >= 16)
     const int64_t len = r.hi - r.lo;
-    const uint32_t T = len <= (int64_t)1 << 18
-                           ? sample_threshold<CNT_THREADS, 4>(hist, scratch, small, r, need, len)
-                           : sample_threshold<CNT_THREADS, 16>(hist, scratch, small, r, need, len);
+    uint32_t T;
+    if (ws.hist_fine) {
+        // the row's exact threshold bin, from the scoring launch's histograms: every element in
+        // a bin at or above it is collected (the row's best above + at, at least `need`)
+        const Digit g = hist_threshold<CNT_THREADS>(hist, scratch, ws.hist_fine, ws.hist_coarse,
+                                                    ws.groups, row, need);
+        const uint32_t Tg = g.d >= 0 ? (uint32_t)g.d << 21 : 0u;
+        T = (g.d >= 0 && g.above + g.at <= CAP && Tg > order_key(-INFINITY)) ? Tg : 0u;
+    } else {
+        // 1024 samples up to 256K positions, 4096 beyond (the expected sampled rank stays >= 16)
+        T = len <= (int64_t)1 << 18
+                ? sample_threshold<CNT_THREADS, 4>(hist, scratch, small, r, need, len)
+                : sample_threshold<CNT_THREADS, 16>(hist, scratch, small, r, need, len);
+    }
     if (T == 0u) { // no usable threshold: the finish kernel falls back to the exact path
         if (threadIdx.x == 0) *cntp = CHUNK_CAP + 1;
         return;
@@ -1152,31 +1254,28 @@ __global__ __launch_bounds__(CNT_THREADS) void chunk_collect_kernel(SelectArgs a
     if (threadIdx.x == 0) *cntp = total;
 }
 
-// One workgroup per row: concatenates the row's slices (chunk order = position order) into LDS
-// and selects exactly there.
-__global__ __launch_bounds__(NT) void chunk_finish_kernel(SelectArgs a, ChunkWs ws)
+// Concatenates a row's slices (chunk order = position order) into the LDS buffer and selects
+// exactly there.  counts[c] > CAPC marks a chunk that overflowed or found no threshold; then, or
+// when the slices hold fewer than `need` or more than the buffer, the row is done by the
+// one-workgroup path.  Every thread of the (NT-thread) block calls it.
+template <int CAPC>
+__device__ __forceinline__ void finish_row(Smem &sm, const Row &r, int need, int32_t *dst,
+                                           const int *counts, const float *cval,
+                                           const int32_t *cid, int nc)
 {
-    __shared__ Smem sm;
-    const int64_t row = blockIdx.x;
-    Row r;
-    int32_t *dst;
-    int need;
-    if (!setup_row(a, row, r, dst, need, true)) return;
-    const int nc = ws.n_chunks;
-    const int *counts = ws.count + row * nc;
     const int lane = lane_id(), w = wave_id();
     // every wave scans the counts itself (no block barrier); the first 64 stay in registers
     const int cfirst = lane < nc ? counts[lane] : 0;
-    bool bad = cfirst > CHUNK_CAP;
+    bool bad = cfirst > CAPC;
     int total = 0;
     {
-        const int c = cfirst > CHUNK_CAP ? 0 : cfirst;
+        const int c = cfirst > CAPC ? 0 : cfirst;
         total = __shfl(wave_inclusive_scan(c), kWave - 1, kWave);
         for (int g = kWave; g < nc; g += kWave) {
             const int i = g + lane;
             int cg = i < nc ? counts[i] : 0;
-            bad |= cg > CHUNK_CAP;
-            cg = cg > CHUNK_CAP ? 0 : cg;
+            bad |= cg > CAPC;
+            cg = cg > CAPC ? 0 : cg;
             total += __shfl(wave_inclusive_scan(cg), kWave - 1, kWave);
         }
     }
@@ -1206,9 +1305,9 @@ __global__ __launch_bounds__(NT) void chunk_finish_kernel(SelectArgs a, ChunkWs 
                     const bool ok = sl < ng;
                     cs[t] = ok ? __shfl(cg, sl, kWave) : 0;
                     os[t] = __shfl(off, ok ? sl : s0, kWave);
-                    const int64_t slice = (row * nc + g + (ok ? sl : s0)) * CHUNK_CAP;
-                    sv[t] = ws.cval + slice;
-                    si[t] = ws.cid + slice;
+                    const int64_t slice = (int64_t)(g + (ok ? sl : s0)) * CAPC;
+                    sv[t] = cval + slice;
+                    si[t] = cid + slice;
                 }
                 const int cmax = max(cs[0], cs[1]);
                 for (int e0 = 0; e0 < cmax; e0 += 2 * kWave) {
@@ -1241,6 +1340,20 @@ __global__ __launch_bounds__(NT) void chunk_finish_kernel(SelectArgs a, ChunkWs 
     if (nbuf >= 0) select_from_buf(sm, nbuf, need, dst);
 }
 
+// One workgroup per row: concatenates the row's slices into LDS and selects exactly there.
+__global__ __launch_bounds__(NT) void chunk_finish_kernel(SelectArgs a, ChunkWs ws)
+{
+    __shared__ Smem sm;
+    const int64_t row = blockIdx.x;
+    Row r;
+    int32_t *dst;
+    int need;
+    if (!setup_row(a, row, r, dst, need, true)) return;
+    const int64_t base = row * ws.n_chunks;
+    finish_row<CHUNK_CAP>(sm, r, need, dst, ws.count + base, ws.cval + base * CHUNK_CAP,
+                          ws.cid + base * CHUNK_CAP, ws.n_chunks);
+}
+
 bool use_chunked(const SelectArgs &a)
 {
     const int64_t rows = (int64_t)a.batch * a.n_q;
@@ -1265,6 +1378,12 @@ size_t select_workspace_bytes(int64_t rows, int64_t n_in, int mode)
 
 hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream)
 {
+    return launch_select_hist(a, ws, nullptr, nullptr, 0, stream);
+}
+
+hipError_t launch_select_hist(const SelectArgs &a, void *ws, const uint32_t *hist_fine,
+                              const uint32_t *hist_coarse, int groups, hipStream_t stream)
+{
     const int64_t rows = (int64_t)a.batch * a.n_q;
     if (rows == 0) return hipSuccess;
     if (!use_chunked(a)) {
@@ -1284,6 +1403,9 @@ hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream)
     p += r256(rows * nc * CHUNK_CAP * 4);
     w.cid = reinterpret_cast<int32_t *>(p);
     w.n_chunks = (int)nc;
+    w.hist_fine = a.cand_ids ? nullptr : hist_fine;
+    w.hist_coarse = hist_coarse;
+    w.groups = groups;
     if (a.cand_ids)
         hipLaunchKernelGGL(chunk_collect_kernel<true>, dim3((unsigned)nc, (unsigned)rows),
                            dim3(CNT_THREADS), 0, stream, a, w);

@@ -21,12 +21,12 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsa.so")
 
 KEY_BF16, KEY_FP8_E4M3 = 1, 2
-OP_TOPK_SELECT, OP_PAGE_RECALL, OP_SPARSE_ATTN = 1, 2, 3
+OP_TOPK_SELECT, OP_PAGE_RECALL, OP_SPARSE_ATTN, OP_INDEX_SELECT = 1, 2, 3, 4
 STATUS = {0: "LSA_OK", 1: "LSA_ERR_NULL_POINTER", 2: "LSA_ERR_BAD_SHAPE", 3: "LSA_ERR_BAD_DTYPE",
           4: "LSA_ERR_UNSUPPORTED", 5: "LSA_ERR_WORKSPACE_TOO_SMALL", 6: "LSA_ERR_DEVICE"}
 EXPORTS = ("lsa_index_scores", "lsa_topk_select", "lsa_page_summary", "lsa_page_recall",
            "lsa_sparse_attn", "lsa_workspace_bytes", "lsa_status_string",
-           "lsa_topk_select_noalloc")
+           "lsa_topk_select_noalloc", "lsa_index_select")
 
 
 class IndexShape(ctypes.Structure):
@@ -66,6 +66,7 @@ def lib():
         L.lsa_index_scores.argtypes = [ip, _VP, _VP, _VP, _I32, _VP, _VP, _VP]
         L.lsa_topk_select.argtypes = [ip, bud, _VP, _I64, _VP, _VP, _VP, _SZ, _VP]
         L.lsa_topk_select_noalloc.argtypes = [ip, bud, _VP, _I64, _VP, _VP, _VP]
+        L.lsa_index_select.argtypes = [ip, bud, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]
         L.lsa_page_summary.argtypes = [ip, _I32, _VP, _I32, _VP, _I64, _I64, _VP, _VP]
         L.lsa_page_recall.argtypes = [ip, bud, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
                                       _VP, _VP, _SZ, _VP]
@@ -74,7 +75,7 @@ def lib():
         L.lsa_workspace_bytes.restype = _SZ
         L.lsa_status_string.argtypes = [_I32]
         L.lsa_status_string.restype = ctypes.c_char_p
-        for f in EXPORTS[:5] + ("lsa_topk_select_noalloc",):
+        for f in EXPORTS[:5] + ("lsa_topk_select_noalloc", "lsa_index_select"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -108,6 +109,13 @@ def lsa_topk_select(shape: IndexShape, budget: Budget, scores, n_cand: int, cand
     _check("lsa_topk_select", lib().lsa_topk_select(
         ctypes.byref(shape), budget, _p(scores), n_cand, _p(cand_ids), _p(idx), _p(ws),
         ws_bytes, _s(stream)))
+
+
+def lsa_index_select(shape: IndexShape, budget: Budget, q, w, keys, key_dtype: int, key_scale,
+                     scores, idx, ws=None, ws_bytes: int = 0, stream=None):
+    _check("lsa_index_select", lib().lsa_index_select(
+        ctypes.byref(shape), budget, _p(q), _p(w), _p(keys), key_dtype, _p(key_scale),
+        _p(scores), _p(idx), _p(ws), ws_bytes, _s(stream)))
 
 
 def lsa_topk_select_noalloc(shape: IndexShape, budget: Budget, scores, n_cand: int, cand_ids,
@@ -235,6 +243,24 @@ def index_scores(q, w, keys, key_scale=None, q_pos0=None, out=None, stream=None)
     out = _out(out, "out", (shape.batch, shape.n_q, shape.kv_len), torch.float32, q.device)
     lsa_index_scores(shape, q, w, keys, kd, ks, out, stream)
     return out
+
+
+def index_select(q, w, keys, key_scale, k, sink, window, q_pos0=None, scores=None, idx=None,
+                 ws: Optional[Workspace] = None, stream=None):
+    """Scores [B, n_q, L] fp32 and the selection idx [B, n_q, k] int32 in one call (fused for
+    decode): the outputs of index_scores followed by topk_select."""
+    _need(q, "q", torch.bfloat16, 4)
+    _check_index_operands(q, w, keys)
+    kd, ks = _key_args(keys, key_scale)
+    shape = index_shape(q, keys, q_pos0)
+    B, T, L = shape.batch, shape.n_q, shape.kv_len
+    scores = _out(scores, "scores", (B, T, L), torch.float32, q.device)
+    idx = _out(idx, "idx", (B, T, k), torch.int32, q.device)
+    bud = Budget(k, sink, window)
+    nb = lsa_workspace_bytes(OP_INDEX_SELECT, shape, bud)
+    wsb = (ws or Workspace()).get(nb, q.device)
+    lsa_index_select(shape, bud, q, w, keys, kd, ks, scores, idx, wsb, nb, stream)
+    return scores, idx
 
 
 def topk_select(scores, k, sink, window, kv_len, q_pos0, cand_ids=None, out=None,
