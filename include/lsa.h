@@ -66,10 +66,22 @@ typedef enum {
 } lsa_key_dtype;
 
 /* Shape of an indexing problem.  head_dim in {64, 128}; n_heads in {4, 8, 16, 32, 64};
- * 1 <= kv_len < 2^31; q_pos0 >= 0. */
+ * 1 <= kv_len < 2^31; q_pos0 >= 0.
+ * Ragged batches (model card, HI bullet: sequences of different lengths share a batch): every
+ * key / latent cache is laid out [B, kv_len, ...] with kv_len the capacity, and two optional
+ * DEVICE arrays of B int32 (4-byte aligned, read by the kernels) give each sequence its own
+ *   seq_len[b]   keys of sequence b (rows [0, seq_len[b]) of its cache; the rest is never read
+ *                as a key: scores -inf, page keys of pages wholly past it 0, attention skips
+ *                ids >= seq_len[b]); clamped into [0, kv_len].  NULL: kv_len for every b.
+ *   seq_pos0[b]  position of sequence b's first query (query i sees keys
+ *                [0, min(seq_len[b], seq_pos0[b] + i + 1))); negative values count as 0.
+ *                NULL: q_pos0 for every b.  Ragged decode: seq_pos0[b] = seq_len[b] - 1.
+ * With either array set, q_pos0 only serves where an array is NULL. */
 typedef struct {
     int32_t batch, n_q, n_heads, head_dim;
     int64_t kv_len, q_pos0;
+    const int32_t *seq_len;
+    const int32_t *seq_pos0;
 } lsa_index_shape;
 
 /* Selection budget per query: k tokens = sink [0,S) + window (the W latest valid tokens) +
@@ -204,7 +216,8 @@ LSA_API lsa_status lsa_page_summary(const lsa_index_shape *shape, int32_t page_s
  * Causality: a query with V < kv_len (a causal prefill chunk) may only recall pages that end
  *   before V, or a page key (a mean over the whole page) would carry later tokens into its
  *   coarse score.  The last eligible page ends before V exactly when window >= page_size - 1,
- *   so a call with q_pos0 + 1 < kv_len and window < page_size - 1 returns LSA_ERR_UNSUPPORTED.
+ *   so a call with q_pos0 + 1 < kv_len, or with per-sequence arrays (whose positions the host
+ *   does not see), and window < page_size - 1 returns LSA_ERR_UNSUPPORTED.
  * Limits: page_size a power of two in [32, 256]; 1 <= m_pages <= 65536.
  */
 LSA_API lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int32_t page_size,
@@ -223,7 +236,7 @@ LSA_API lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budg
  * Entries of -1 (or outside [0, kv_len)) are skipped; a row with none gives out = 0,
  * lse = -inf.  Cross-Layer Indexing (paper summary page, strategy (2)): call once per layer with
  * that layer's q / cache and the same idx.
- *   shape   uses batch, n_q and kv_len
+ *   shape   uses batch, n_q, kv_len and seq_len (ids at or past a sequence's length are skipped)
  *   budget  sink/window say idx[.., 0:S] and idx[.., S:S+W] are contiguous runs (the layout
  *           lsa_topk_select writes when V > k); rows whose first entry is not 0 or whose
  *           runs are not contiguous fall back to a plain gather.  {0,0,0} = always gather.

@@ -1,0 +1,193 @@
+"""Ragged batches: per-sequence key counts (seq_len) and first-query positions (seq_pos0) over a
+padded [B, kv_len, ...] cache, through every entry point, against the oracle run on each
+sequence alone (its keys truncated to its own length).
+
+The padding rows hold random keys and latent rows on purpose: any kernel that read past a
+sequence's end would change the result.  Lengths mix 0, 1000 (<= k), 4096, 70001, 100000 and
+131072 keys.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref
+from token_selection_indexer_amd import inputs, lsa
+from token_selection_indexer_amd.configs import (DECODE_128K, DECODE_1M_HI, Budget, HiParams,
+                                                 IndexShape, Workload)
+from tests.gpu_checks import assert_scores, attn_check, check_rows_exact, say
+from tests.util import NearTie, bits, check_si_layout, f32, score_tol
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+CAP = 131072
+LENS = [4096, 100000, CAP, 1000, 0, 70001, 4096, CAP, 100000, 1, 33, 131071, 65536, 2048, 2049,
+        90000]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lsa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _workload(B, n_q, kd="fp8", seed=81):
+    return Workload(name="ragged", index=IndexShape(batch=B, n_q=n_q, kv_len=CAP, q_pos0=CAP - n_q,
+                                                    heads=64, head_dim=128, key_dtype=kd),
+                    budget=Budget(k=2048, sink=64, window=960), attn=DECODE_128K.attn, seed=seed)
+
+
+def _keys_b(inp, b, L):
+    k = inp["keys"][b, :L]
+    if k.dtype == torch.bfloat16:
+        return bits(k), None
+    return k.cpu().numpy().view(np.uint8), f32(inp["scale"][b, :L])
+
+
+def test_ragged_decode_scores_and_selection():
+    """16 decode sequences of mixed lengths (query at seq_len - 1): scores against the oracle,
+    selection bit-exact against ref.select on the GPU's scores, and the fused call (the batch
+    reaches the long scoring launch) bitwise equal to the separate calls."""
+    B = len(LENS)
+    wl = _workload(B, 1)
+    b = wl.budget
+    inp = inputs.index_inputs(wl, DEV)
+    lens = torch.tensor(LENS, dtype=torch.int32, device=DEV)
+    pos0 = (lens - 1).clamp(min=0)
+    sc = lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], seq_lens=lens,
+                          seq_pos0=pos0)
+    idx = lsa.topk_select(sc, b.k, b.sink, b.window, kv_len=CAP, q_pos0=CAP - 1, seq_lens=lens,
+                          seq_pos0=pos0)
+    sc2, idx2 = lsa.index_select(inp["q"], inp["w"], inp["keys"], inp["scale"], b.k, b.sink,
+                                 b.window, seq_lens=lens, seq_pos0=pos0)
+    torch.cuda.synchronize()
+    assert torch.equal(sc.view(torch.int32), sc2.view(torch.int32))
+    assert torch.equal(idx, idx2)
+    shape = lsa.IndexShape(B, 1, 64, 128, CAP, CAP - 1)
+    bud = lsa.Budget(b.k, b.sink, b.window)
+    assert (lsa.lsa_workspace_bytes(lsa.OP_INDEX_SELECT, shape, bud)
+            != lsa.lsa_workspace_bytes(lsa.OP_TOPK_SELECT, shape, bud))  # the fused path ran
+    scn, gi = sc.cpu().numpy(), idx.cpu().numpy()
+    for r, L in enumerate(LENS):
+        V = np.array([L])
+        check_rows_exact(gi[r], scn[r], V, b.k, b.sink, b.window)
+        assert np.all(np.isneginf(scn[r, 0, L:]))  # nothing at or past the sequence's end
+    for r in (0, 1, 3, 9, 11):  # oracle scores on the truncated sequence
+        L = LENS[r]
+        keys, scale = _keys_b(inp, r, L)
+        I, A, E = ref.index_scores(bits(inp["q"][r]), f32(inp["w"][r]), keys, scale,
+                                   np.array([L - 1]))
+        assert_scores(scn[r, 0, :L], I[0], A[0], E[0], f"seq {r} (L={L})")
+    say("ragged decode: scores, selection and the fused call agree")
+
+
+def test_ragged_prefill_chunks():
+    """Prefill chunks of 40 queries per sequence, each sequence at its own position and length
+    (the tile scoring kernel and one-workgroup selection)."""
+    lens_l = [5000, 3000, 131072, 9000]
+    p0_l = [4960, 100, 131000, 4000]   # every query of sequence 1 sees at most k keys
+    B, T = len(lens_l), 40
+    wl = _workload(B, T, kd="bf16", seed=82)
+    b = wl.budget
+    inp = inputs.index_inputs(wl, DEV)
+    lens = torch.tensor(lens_l, dtype=torch.int32, device=DEV)
+    p0 = torch.tensor(p0_l, dtype=torch.int32, device=DEV)
+    sc = lsa.index_scores(inp["q"], inp["w"], inp["keys"], None, seq_lens=lens, seq_pos0=p0)
+    idx = lsa.topk_select(sc, b.k, b.sink, b.window, kv_len=CAP, q_pos0=0, seq_lens=lens,
+                          seq_pos0=p0)
+    torch.cuda.synchronize()
+    scn, gi = sc.cpu().numpy(), idx.cpu().numpy()
+    for r, (L, P0) in enumerate(zip(lens_l, p0_l)):
+        V = np.minimum(L, P0 + np.arange(T) + 1)
+        check_rows_exact(gi[r], scn[r], V, b.k, b.sink, b.window)
+        rows = [0, 17, T - 1]
+        keys, _ = _keys_b(inp, r, L)
+        I, A, E = ref.index_scores(bits(inp["q"][r])[rows], f32(inp["w"][r])[rows], keys, None,
+                                   P0 + np.array(rows))
+        for i, t in enumerate(rows):
+            assert_scores(scn[r, t, :L], I[i], A[i], E[i], f"seq {r} row {t}")
+            assert np.all(np.isneginf(scn[r, t, L:]))
+
+
+def test_ragged_pages_and_recall():
+    """Page keys per sequence (pages wholly past a sequence's end are zero keys) and decode page
+    recall with each sequence's own eligible pages, against the oracle on each sequence."""
+    lens_l = [9000, 20000, 1000, 64 * 50 + 7]
+    B, P, M = len(lens_l), 64, 32
+    bud = Budget(k=512, sink=32, window=224)
+    wl = Workload(name="rhi", index=IndexShape(batch=B, n_q=1, kv_len=20000, q_pos0=19999,
+                                               heads=64, head_dim=128, key_dtype="fp8"),
+                  budget=bud, attn=DECODE_1M_HI.attn, seed=83, hi=HiParams(page=P, m_pages=M),
+                  planted_frac=0.05)
+    inp = inputs.index_inputs(wl, DEV)
+    lens = torch.tensor(lens_l, dtype=torch.int32, device=DEV)
+    pos0 = lens - 1
+    pk = lsa.page_summary(inp["keys"], inp["scale"], P, seq_lens=lens)
+    res = lsa.page_recall(inp["q"], inp["w"], pk, inp["keys"], inp["scale"], bud.k, bud.sink,
+                          bud.window, P, M, seq_lens=lens, seq_pos0=pos0)
+    idx = lsa.topk_select(res[1], bud.k, bud.sink, bud.window, kv_len=20000, q_pos0=19999,
+                          cand_ids=res[2], seq_lens=lens, seq_pos0=pos0)
+    torch.cuda.synchronize()
+    pkn = bits(pk)
+    nt = NearTie()
+    for r, L in enumerate(lens_l):
+        keys, scale = _keys_b(inp, r, L)
+        n_pages = (L + P - 1) // P
+        want = ref.page_keys(keys, scale, P)
+        assert np.array_equal(pkn[r, :n_pages], want), r
+        assert not pkn[r, n_pages:].any(), r
+        q, wt = bits(inp["q"][r, 0:1]), f32(inp["w"][r, 0:1])
+        o = ref.page_recall(q, wt, want, keys, scale, np.array([L - 1]), bud.k, bud.sink,
+                            bud.window, P, M)
+        gp = res[0][r, 0].cpu().numpy()
+        rp = o["page_ids"][0]
+        if np.array_equal(gp, rp):
+            nt.add(gp, rp, {}, 0.0, 0.0)
+        else:
+            coarse = o["coarse"][0]
+            sel = rp[rp >= 0]
+            kth = sel[np.argmin(coarse[sel])]
+            _, Ac, Ec = ref.index_scores(q, wt, want, None, np.array([len(want)]))
+            nt.add(gp, rp, coarse, coarse[kth], score_tol(Ac[0][kth], Ec[0][kth]))
+        ci = res[2][r, 0].cpu().numpy()
+        for i, p in enumerate(gp):  # candidate ids follow the GPU's pages, inside the middle
+            seg = ci[i * P:(i + 1) * P]
+            if p < 0:
+                assert np.all(seg == -1)
+                continue
+            tok = p * P + np.arange(P)
+            assert np.array_equal(seg, np.where((tok >= bud.sink) & (tok < L - bud.window), tok, -1))
+        check_rows_exact(idx[r].cpu().numpy(), res[1][r].cpu().numpy(), np.array([L]), bud.k,
+                         bud.sink, bud.window, cand_ids=res[2][r].cpu().numpy())
+    nt.check(0.999)
+
+
+def test_ragged_attention():
+    """MLA attention where each sequence has its own length: index entries at or past a
+    sequence's end (here: pointing into its padding) are skipped like -1."""
+    lens_l = [3000, 9000, 1, 0]
+    B, T, k = len(lens_l), 2, 300
+    wl = Workload(name="ra", index=IndexShape(batch=B, n_q=T, kv_len=9000, q_pos0=8998, heads=64,
+                                              head_dim=128, key_dtype="fp8"),
+                  budget=Budget(k=k, sink=16, window=100), attn=DECODE_128K.attn, seed=84)
+    att = inputs.attn_inputs(wl, 0, DEV)
+    g = torch.Generator().manual_seed(5)
+    idx = torch.randint(0, 9000, (B, T, k), generator=g, dtype=torch.int32)
+    idx[:, :, ::11] = -1
+    idx = idx.to(DEV)
+    lens = torch.tensor(lens_l, dtype=torch.int32, device=DEV)
+    out, lse = lsa.sparse_attn(att["q"], att["kv"], None, idx, wl.attn.scale, d_v=512,
+                               seq_lens=lens)
+    # reference: the same lists with every id past the sequence's length masked to -1
+    idx_m = idx.clone()
+    for r, L in enumerate(lens_l):
+        idx_m[r][idx_m[r] >= L] = -1
+    worst = attn_check(att["q"], att["kv"], None, idx_m, wl.attn.scale, out, lse, True, 512)
+    out2, _ = lsa.sparse_attn(att["q"], att["kv"], None, idx_m, wl.attn.scale, d_v=512,
+                              seq_lens=lens)
+    assert torch.equal(out, out2)
+    o = out.float().cpu()
+    assert torch.all(o[3] == 0) and torch.all(torch.isneginf(lse[3].cpu()))  # empty sequence
+    say(f"ragged attention: worst |err| {worst:.2e}")

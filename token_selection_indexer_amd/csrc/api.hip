@@ -13,6 +13,14 @@ constexpr int64_t kMaxGridYZ = 65535;
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
+bool ragged(const lsa_index_shape *s) { return s->seq_len || s->seq_pos0; }
+
+lsa_status check_ragged(const lsa_index_shape *s)
+{
+    if (!aligned(s->seq_len, 4) || !aligned(s->seq_pos0, 4)) return LSA_ERR_BAD_SHAPE;
+    return LSA_OK;
+}
+
 lsa_status check_index_shape(const lsa_index_shape *s)
 {
     if (!s) return LSA_ERR_NULL_POINTER;
@@ -21,7 +29,7 @@ lsa_status check_index_shape(const lsa_index_shape *s)
         return LSA_ERR_BAD_SHAPE;
     if (s->n_heads < 1 || s->head_dim < 1) return LSA_ERR_BAD_SHAPE;
     if (!lsa::scores_supported(s->n_heads, s->head_dim)) return LSA_ERR_UNSUPPORTED;
-    return LSA_OK;
+    return check_ragged(s);
 }
 
 lsa_status check_keys(lsa_key_dtype kd, const void *keys, const float *scale)
@@ -88,6 +96,8 @@ lsa::ScoreArgs score_args(const lsa_index_shape *shape, lsa_budget budget)
     a.n_out = shape->kv_len;
     a.kv_len = shape->kv_len;
     a.q_pos0 = shape->q_pos0;
+    a.seq_len = shape->seq_len;
+    a.seq_pos0 = shape->seq_pos0;
     a.mask = lsa::MASK_CAUSAL;
     a.k = budget.k;
     a.sink = budget.sink;
@@ -103,6 +113,8 @@ lsa::SelectArgs select_args(const lsa_index_shape *shape, lsa_budget budget)
     a.n_in = shape->kv_len;
     a.kv_len = shape->kv_len;
     a.q_pos0 = shape->q_pos0;
+    a.seq_len = shape->seq_len;
+    a.seq_pos0 = shape->seq_pos0;
     a.k = budget.k;
     a.sink = budget.sink;
     a.window = budget.window;
@@ -206,6 +218,8 @@ lsa_status lsa_index_scores(const lsa_index_shape *shape, const void *q, const f
     a.n_out = shape->kv_len;
     a.kv_len = shape->kv_len;
     a.q_pos0 = shape->q_pos0;
+    a.seq_len = shape->seq_len;
+    a.seq_pos0 = shape->seq_pos0;
     a.mask = lsa::MASK_CAUSAL;
     a.fp8 = key_dtype == LSA_KEY_FP8_E4M3;
     return device_status(lsa::launch_scores(a, static_cast<hipStream_t>(stream)));
@@ -224,6 +238,7 @@ lsa_status prepare_select(const lsa_index_shape *shape, lsa_budget budget, const
         return LSA_ERR_BAD_SHAPE;
     lsa_status st = check_budget(budget);
     if (st != LSA_OK) return st;
+    if ((st = check_ragged(shape)) != LSA_OK) return st;
     if (budget.k - budget.sink - budget.window > 65536) return LSA_ERR_UNSUPPORTED;
     if (!scores || !idx) return LSA_ERR_NULL_POINTER;
     if (!cand_ids && n_cand != shape->kv_len) return LSA_ERR_BAD_SHAPE;
@@ -241,6 +256,8 @@ lsa_status prepare_select(const lsa_index_shape *shape, lsa_budget budget, const
     a.n_in = n_cand;
     a.kv_len = shape->kv_len;
     a.q_pos0 = shape->q_pos0;
+    a.seq_len = shape->seq_len;
+    a.seq_pos0 = shape->seq_pos0;
     a.k = budget.k;
     a.sink = budget.sink;
     a.window = budget.window;
@@ -336,14 +353,15 @@ lsa_status lsa_page_summary(const lsa_index_shape *shape, int32_t page_size, con
     if (!pow2(page_size) || page_size > 256) return LSA_ERR_BAD_SHAPE;
     lsa_status st = check_keys(key_dtype, keys, key_scale);
     if (st != LSA_OK) return st;
+    if ((st = check_ragged(shape)) != LSA_OK) return st;
     if (!page_keys) return LSA_ERR_NULL_POINTER;
     if (!aligned(page_keys, 16)) return LSA_ERR_BAD_SHAPE;
     const int64_t n_pages = (shape->kv_len + page_size - 1) / page_size;
     if (page_lo < 0 || page_hi < page_lo || page_hi > n_pages) return LSA_ERR_BAD_SHAPE;
     if (shape->batch == 0 || page_hi == page_lo) return LSA_OK;
     return device_status(lsa::launch_page_summary(keys, key_dtype == LSA_KEY_FP8_E4M3, key_scale,
-                                                  shape->batch, shape->kv_len, shape->head_dim,
-                                                  page_size, page_lo, page_hi,
+                                                  shape->batch, shape->kv_len, shape->seq_len,
+                                                  shape->head_dim, page_size, page_lo, page_hi,
                                                   static_cast<uint16_t *>(page_keys),
                                                   static_cast<hipStream_t>(stream)));
 }
@@ -362,7 +380,8 @@ lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int3
     // A query that sees fewer than kv_len keys (causal prefill) must not recall a page that
     // extends past its last valid key: that page's key is a mean over later tokens.  The last
     // eligible page ends before V when the window covers at least P - 1 tokens.
-    if (shape->q_pos0 + 1 < shape->kv_len && budget.window < page_size - 1)
+    // (With per-sequence arrays the host cannot see the positions: the window must cover it.)
+    if ((ragged(shape) || shape->q_pos0 + 1 < shape->kv_len) && budget.window < page_size - 1)
         return LSA_ERR_UNSUPPORTED;
     if ((st = check_keys(key_dtype, keys, key_scale)) != LSA_OK) return st;
     if (!q || !w || !page_keys || !page_ids || !cand_scores || !cand_ids) return LSA_ERR_NULL_POINTER;
@@ -395,6 +414,8 @@ lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int3
     c.n_out = n_pages;
     c.kv_len = shape->kv_len;
     c.q_pos0 = shape->q_pos0;
+    c.seq_len = shape->seq_len;
+    c.seq_pos0 = shape->seq_pos0;
     c.mask = lsa::MASK_PAGES;
     c.k = budget.k;
     c.sink = budget.sink;
@@ -413,6 +434,8 @@ lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int3
     s.n_in = n_pages;
     s.kv_len = shape->kv_len;
     s.q_pos0 = shape->q_pos0;
+    s.seq_len = shape->seq_len;
+    s.seq_pos0 = shape->seq_pos0;
     s.k = budget.k;
     s.sink = budget.sink;
     s.window = budget.window;
@@ -439,6 +462,8 @@ lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int3
     f.n_out = (int64_t)m_pages * page_size;
     f.kv_len = shape->kv_len;
     f.q_pos0 = shape->q_pos0;
+    f.seq_len = shape->seq_len;
+    f.seq_pos0 = shape->seq_pos0;
     f.k = budget.k;
     f.sink = budget.sink;
     f.window = budget.window;
@@ -457,6 +482,7 @@ lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_shape *a
     if (st != LSA_OK) return st;
     if (!q || !k || !v || !idx || !out) return LSA_ERR_NULL_POINTER;
     if (attn->latent && v != k) return LSA_ERR_BAD_SHAPE;
+    if ((st = check_ragged(shape)) != LSA_OK) return st;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(idx, 4) ||
         !aligned(out, 4) || (lse && !aligned(lse, 4)))
         return LSA_ERR_BAD_SHAPE;
@@ -484,6 +510,7 @@ lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_shape *a
     a.n_idx = budget.k;
     a.latent = attn->latent;
     a.kv_len = shape->kv_len;
+    a.seq_len = shape->seq_len;
     a.k_stride = attn->k_row_stride;
     a.v_stride = attn->v_row_stride;
     a.sink = budget.sink;

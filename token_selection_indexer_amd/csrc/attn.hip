@@ -115,6 +115,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     const int n_rounds = c_end > c_begin ? (c_end - c_begin + AR - 1) / AR : 0;
 
     const int32_t *idx_row = a.idx + qrow * a.n_idx;
+    const int64_t seq_rows = seq_keys(a.seq_len, b, a.kv_len); // valid rows of this sequence
     // Row id (threadIdx.x % AR) of a round: an unconditional load of a clamped, always valid
     // entry (a conditional load would make the compiler wait for it at once), masked at use.
     auto id_load = [&](int round) -> int32_t {
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     };
     auto id_mask = [&](int round, int32_t raw) -> int32_t {
         const int j = c_begin + round * AR + (int)(threadIdx.x % AR);
-        return (round < n_rounds && j < c_end && row_ok(raw, a.kv_len)) ? raw : -1;
+        return (round < n_rounds && j < c_end && row_ok(raw, seq_rows)) ? raw : -1;
     };
     auto id_of = [&](int round) -> int32_t { return id_mask(round, id_load(round)); };
     if (threadIdx.x < AR) {
@@ -363,6 +364,7 @@ __global__ __launch_bounds__(256) void mha_attn_kernel(AttnArgs a)
     for (int d = l; d < a.d_qk; d += kWave) qs[w][d] = bf16_bits_to_f32(qp[d]);
     const uint16_t *kb = a.k + (int64_t)b * a.kv_len * a.k_stride;
     const uint16_t *vb = a.v + (int64_t)b * a.kv_len * a.v_stride;
+    const int64_t seq_rows = seq_keys(a.seq_len, b, a.kv_len);
     const int32_t *idx_row = a.idx + qrow * a.n_idx;
     const float sl2 = a.scale * kLog2e;
     constexpr int VPL = MHA_MAXD / kWave; // output columns per lane (at most)
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(256) void mha_attn_kernel(AttnArgs a)
         for (int j = l; j < cn; j += kWave) {
             const int32_t id = idx_row[c0 + j];
             float lg = -INFINITY;
-            if (row_ok(id, a.kv_len)) {
+            if (row_ok(id, seq_rows)) {
                 const uint16_t *kr = kb + (int64_t)id * a.k_stride;
                 float dot = 0.0f;
                 for (int d = 0; d < a.d_qk; d += 8) {
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(256) void mha_attn_kernel(AttnArgs a)
                 lg = dot * sl2;
             }
             ps[w][j] = lg;
-            ids[w][j] = row_ok(id, a.kv_len) ? id : -1;
+            ids[w][j] = row_ok(id, seq_rows) ? id : -1;
             cmax = fmaxf(cmax, lg);
         }
         cmax = wave_max(cmax);

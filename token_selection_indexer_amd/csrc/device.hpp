@@ -108,6 +108,32 @@ __device__ __forceinline__ uint32_t order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Ragged batches: sequence b holds seq_len[b] valid keys of the kv_len-row (padded) cache, and
+// its query i sits at position seq_pos0[b] + i.  Null arrays: every sequence has kv_len keys and
+// starts at q_pos0.  Lengths are clamped into [0, kv_len], positions below 0 to 0.
+__device__ __forceinline__ int64_t seq_keys(const int32_t *seq_len, int b, int64_t kv_len)
+{
+    if (!seq_len) return kv_len;
+    const int64_t L = seq_len[b];
+    return L < 0 ? 0 : (L > kv_len ? kv_len : L);
+}
+
+__device__ __forceinline__ int64_t seq_first(const int32_t *seq_pos0, int b, int64_t q_pos0)
+{
+    if (!seq_pos0) return q_pos0;
+    const int64_t p = seq_pos0[b];
+    return p < 0 ? 0 : p;
+}
+
+// Keys query t of sequence b sees: [0, V).
+__device__ __forceinline__ int64_t valid_len(const int32_t *seq_len, const int32_t *seq_pos0,
+                                             int b, int64_t t, int64_t kv_len, int64_t q_pos0)
+{
+    const int64_t L = seq_keys(seq_len, b, kv_len);
+    const int64_t V = seq_first(seq_pos0, b, q_pos0) + t + 1;
+    return V < L ? V : L;
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 

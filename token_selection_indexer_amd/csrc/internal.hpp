@@ -25,6 +25,7 @@ struct ScoreArgs {
     int64_t n_keys;       // key rows per sequence
     int64_t n_out;        // outputs per query row
     int64_t kv_len, q_pos0;
+    const int32_t *seq_len, *seq_pos0; // [B] ragged batch (device) or nullptr
     int mask;             // RowMask (flat / coarse modes)
     int k, sink, window;  // budget (coarse and fine modes)
     int page;             // P (coarse and fine modes)
@@ -54,6 +55,7 @@ struct SelectArgs {
     int batch, n_q;
     int64_t n_in;
     int64_t kv_len, q_pos0;
+    const int32_t *seq_len, *seq_pos0; // [B] ragged batch (device) or nullptr
     int k, sink, window;     // SI budget
     int mode;                // SelectMode
     int page;                // MODE_PAGES: P
@@ -79,8 +81,9 @@ size_t select_scratch_bytes();
 hipError_t select_scratch(void **ptr);
 
 hipError_t launch_page_summary(const void *keys, int fp8, const float *kscale, int batch,
-                               int64_t kv_len, int dim, int page, int64_t page_lo,
-                               int64_t page_hi, uint16_t *page_keys, hipStream_t stream);
+                               int64_t kv_len, const int32_t *seq_len, int dim, int page,
+                               int64_t page_lo, int64_t page_hi, uint16_t *page_keys,
+                               hipStream_t stream);
 
 struct AttnArgs {
     const uint16_t *q;    // [B, n_q, Hq, d_qk]
@@ -92,6 +95,7 @@ struct AttnArgs {
     float *ws;            // split partials
     int batch, n_q, heads, d_qk, d_v, n_idx, latent;
     int64_t kv_len, k_stride, v_stride;
+    const int32_t *seq_len; // [B] valid rows per sequence (device) or nullptr
     int sink, window;
     float scale;
     int n_split;          // chunks of the index list per (query, head group)

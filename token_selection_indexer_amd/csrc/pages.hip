@@ -3,7 +3,8 @@
 // The model card's HI bullet recalls candidate blocks by coarse scores without defining a
 // block's coarse key.  This library defines the key of page p (P tokens, P a power of two) as the
 // mean of its dequantised indexer keys with a fixed binary32 rounding sequence:
-//   v[j]  = fp32(scale[s] * e4m3(kq[s][i]))  (bf16 keys: the value), s = p*P + j; +0 past kv_len
+//   v[j]  = fp32(scale[s] * e4m3(kq[s][i]))  (bf16 keys: the value), s = p*P + j; +0 past the
+//           sequence's last key (a page wholly past it is the zero key)
 //   sum   = pairwise tree sum of v[0..P): halves summed separately, then added, recursively
 //   pk    = bf16_rne(sum / n_p), n_p = tokens of the page that exist
 // Every multiply, add and divide rounds on its own: contraction into FMA is switched off for
@@ -30,7 +31,8 @@ namespace {
 
 template <bool FP8, int P>
 __global__ __launch_bounds__(256) void page_summary_kernel(const void *keys, const float *kscale,
-                                                           int64_t kv_len, int D, int64_t page_lo,
+                                                           int64_t kv_len, const int32_t *seq_len,
+                                                           int D, int64_t page_lo,
                                                            int64_t page_hi, int64_t n_pages,
                                                            uint16_t *pk)
 {
@@ -41,7 +43,12 @@ __global__ __launch_bounds__(256) void page_summary_kernel(const void *keys, con
     const int pair = (int)(gid % tpp);
     if (p >= page_hi) return;
     const int64_t s0 = p * P;
-    const int64_t n_p = min((int64_t)P, kv_len - s0);
+    const int64_t L = seq_keys(seq_len, b, kv_len); // this sequence's keys
+    const int64_t n_p = min((int64_t)P, L - s0);
+    if (n_p <= 0) { // a page past the sequence's end: zero key
+        *reinterpret_cast<uint32_t *>(pk + ((int64_t)b * n_pages + p) * D + 2 * pair) = 0u;
+        return;
+    }
 
     // binary counter over the tokens: before token j the stack holds popcount(j) completed
     // subtrees; token j closes ctz(~j) of them (left + right), all positions known at compile time
@@ -92,7 +99,8 @@ struct PageGeo {
 
 template <bool FP8, int D, int P>
 __global__ __launch_bounds__(256) void page_summary_wave_kernel(const void *keys, const float *kscale,
-                                                                int64_t kv_len, int64_t page_lo,
+                                                                int64_t kv_len, const int32_t *seq_len,
+                                                                int64_t page_lo,
                                                                 int64_t page_hi, int64_t n_pages,
                                                                 uint16_t *pk)
 {
@@ -106,15 +114,16 @@ __global__ __launch_bounds__(256) void page_summary_wave_kernel(const void *keys
     const int lane = lane_id(), g = lane / LPR, c = lane % LPR;
     const uint8_t *kb = reinterpret_cast<const uint8_t *>(keys) + (int64_t)b * kv_len * ROW + 16 * c;
     const float *sb = FP8 ? kscale + (int64_t)b * kv_len : nullptr;
+    const int64_t L = seq_keys(seq_len, b, kv_len); // this sequence's keys (rows past: +0)
 
-    // a lane's raw data for one page: TPL pieces (+ TPL scales); zero past kv_len
+    // a lane's raw data for one page: TPL pieces (+ TPL scales); zero past the sequence's end
     uint4 raw[TPL];
     float scl[TPL];
     auto load = [&](int64_t p) {
         const int64_t t0 = p * P + g * TPL;
         static_for<0, TPL>([&](auto J) {
             constexpr int j = decltype(J)::value;
-            const bool ok = t0 + j < kv_len;
+            const bool ok = t0 + j < L;
             raw[j] = ok ? ld16_nt(kb + (t0 + j) * ROW) : make_uint4(0u, 0u, 0u, 0u); // read once
             if constexpr (FP8) scl[j] = ok ? sb[t0 + j] : 0.0f;
         });
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(256) void page_summary_wave_kernel(const void *keys
             for (int e = 0; e < EPL; ++e)
                 stk[0][e] = __fadd_rn(stk[0][e], __shfl_xor(stk[0][e], m, kWave));
         if (g == 0) {
-            const int64_t n_p = min((int64_t)P, kv_len - p * P);
+            const int64_t n_p = min((int64_t)P, L - p * P); // <= 0: past the end, a zero key
             // a full page divides by P = 2^k: multiplying by the exact 2^-k rounds identically
             const bool full = n_p == P;
             const float nf = (float)n_p;
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(256) void page_summary_wave_kernel(const void *keys
             for (int e = 0; e < EPL / 2; ++e) {
                 const float m0 = full ? __fmul_rn(stk[0][2 * e], 1.0f / P) : __fdiv_rn(stk[0][2 * e], nf);
                 const float m1 = full ? __fmul_rn(stk[0][2 * e + 1], 1.0f / P) : __fdiv_rn(stk[0][2 * e + 1], nf);
-                o[e] = f32_to_bf16_bits(m0) | (f32_to_bf16_bits(m1) << 16);
+                o[e] = n_p > 0 ? f32_to_bf16_bits(m0) | (f32_to_bf16_bits(m1) << 16) : 0u;
             }
             uint16_t *dst = pk + ((int64_t)b * n_pages + p) * D + c * EPL;
 #pragma unroll
@@ -196,7 +205,8 @@ __global__ __launch_bounds__(256) void page_summary_wave_kernel(const void *keys
 
 template <bool FP8, int D, int P>
 hipError_t launch_wave(const void *keys, const float *kscale, int batch, int64_t kv_len,
-                       int64_t page_lo, int64_t page_hi, uint16_t *pk, hipStream_t st)
+                       const int32_t *seq_len, int64_t page_lo, int64_t page_hi, uint16_t *pk,
+                       hipStream_t st)
 {
     const int64_t n_pages = (kv_len + P - 1) / P;
     // about 2048 workgroups in all (8 per CU), each wave looping over its share of the pages
@@ -205,20 +215,21 @@ hipError_t launch_wave(const void *keys, const float *kscale, int batch, int64_t
     const int64_t wg = need < want ? need : want;
     const dim3 grid((unsigned)wg, (unsigned)batch);
     hipLaunchKernelGGL((page_summary_wave_kernel<FP8, D, P>), grid, dim3(256), 0, st, keys, kscale,
-                       kv_len, page_lo, page_hi, n_pages, pk);
+                       kv_len, seq_len, page_lo, page_hi, n_pages, pk);
     return hipGetLastError();
 }
 
 template <bool FP8, int D>
-hipError_t launch_wave_p(const void *keys, const float *kscale, int batch, int64_t kv_len, int P,
-                         int64_t page_lo, int64_t page_hi, uint16_t *pk, hipStream_t st, bool &done)
+hipError_t launch_wave_p(const void *keys, const float *kscale, int batch, int64_t kv_len,
+                         const int32_t *seq_len, int P, int64_t page_lo, int64_t page_hi,
+                         uint16_t *pk, hipStream_t st, bool &done)
 {
     done = true;
     switch (P) {
 #define LSA_PW(PP)                                                                                  \
     case PP:                                                                                        \
         if constexpr (PP >= PageGeo<FP8, D>::G)                                                     \
-            return launch_wave<FP8, D, PP>(keys, kscale, batch, kv_len, page_lo, page_hi, pk, st); \
+            return launch_wave<FP8, D, PP>(keys, kscale, batch, kv_len, seq_len, page_lo, page_hi, pk, st); \
         break;
         LSA_PW(1) LSA_PW(2) LSA_PW(4) LSA_PW(8) LSA_PW(16) LSA_PW(32) LSA_PW(64) LSA_PW(128) LSA_PW(256)
 #undef LSA_PW
@@ -229,8 +240,9 @@ hipError_t launch_wave_p(const void *keys, const float *kscale, int batch, int64
 }
 
 template <bool FP8>
-hipError_t launch_p(const void *keys, const float *kscale, int batch, int64_t kv_len, int D,
-                    int P, int64_t page_lo, int64_t page_hi, uint16_t *pk, hipStream_t st)
+hipError_t launch_p(const void *keys, const float *kscale, int batch, int64_t kv_len,
+                    const int32_t *seq_len, int D, int P, int64_t page_lo, int64_t page_hi,
+                    uint16_t *pk, hipStream_t st)
 {
     // pages of at least one 16-byte piece per lane group take the one-wave-per-page kernel;
     // smaller pages (P <= 8) the per-element one.  Both pointers are 16-byte aligned (checked
@@ -238,9 +250,9 @@ hipError_t launch_p(const void *keys, const float *kscale, int batch, int64_t kv
     bool done = false;
     hipError_t e = hipSuccess;
     if (D == 128)
-        e = launch_wave_p<FP8, 128>(keys, kscale, batch, kv_len, P, page_lo, page_hi, pk, st, done);
+        e = launch_wave_p<FP8, 128>(keys, kscale, batch, kv_len, seq_len, P, page_lo, page_hi, pk, st, done);
     else if (D == 64)
-        e = launch_wave_p<FP8, 64>(keys, kscale, batch, kv_len, P, page_lo, page_hi, pk, st, done);
+        e = launch_wave_p<FP8, 64>(keys, kscale, batch, kv_len, seq_len, P, page_lo, page_hi, pk, st, done);
     if (done) return e;
     const int64_t n_pages = (kv_len + P - 1) / P;
     const int64_t threads = (page_hi - page_lo) * (D / 2);
@@ -249,7 +261,7 @@ hipError_t launch_p(const void *keys, const float *kscale, int batch, int64_t kv
 #define LSA_PS(PP)                                                                                  \
     case PP:                                                                                        \
         hipLaunchKernelGGL((page_summary_kernel<FP8, PP>), grid, dim3(256), 0, st, keys, kscale,    \
-                           kv_len, D, page_lo, page_hi, n_pages, pk);                               \
+                           kv_len, seq_len, D, page_lo, page_hi, n_pages, pk);                      \
         break;
         LSA_PS(1) LSA_PS(2) LSA_PS(4) LSA_PS(8)
 #undef LSA_PS
@@ -261,12 +273,15 @@ hipError_t launch_p(const void *keys, const float *kscale, int batch, int64_t kv
 } // namespace
 
 hipError_t launch_page_summary(const void *keys, int fp8, const float *kscale, int batch,
-                               int64_t kv_len, int dim, int page, int64_t page_lo,
-                               int64_t page_hi, uint16_t *page_keys, hipStream_t stream)
+                               int64_t kv_len, const int32_t *seq_len, int dim, int page,
+                               int64_t page_lo, int64_t page_hi, uint16_t *page_keys,
+                               hipStream_t stream)
 {
     if (page_hi <= page_lo || batch == 0) return hipSuccess;
-    return fp8 ? launch_p<true>(keys, kscale, batch, kv_len, dim, page, page_lo, page_hi, page_keys, stream)
-               : launch_p<false>(keys, kscale, batch, kv_len, dim, page, page_lo, page_hi, page_keys, stream);
+    return fp8 ? launch_p<true>(keys, kscale, batch, kv_len, seq_len, dim, page, page_lo, page_hi,
+                                page_keys, stream)
+               : launch_p<false>(keys, kscale, batch, kv_len, seq_len, dim, page, page_lo, page_hi,
+                                 page_keys, stream);
 }
 
 } // namespace lsa

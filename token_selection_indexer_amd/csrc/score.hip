@@ -70,11 +70,11 @@ __device__ __forceinline__ void rprime_to_qh(int rp, int &qs, int &h, bool &vali
     }
 }
 
-// Valid key range [lo, hi) of query t.
-__device__ __forceinline__ void row_range(const ScoreArgs &a, int64_t t, int64_t &lo, int64_t &hi)
+// Valid key range [lo, hi) of query t of sequence b.
+__device__ __forceinline__ void row_range(const ScoreArgs &a, int b, int64_t t, int64_t &lo,
+                                          int64_t &hi)
 {
-    int64_t V = a.q_pos0 + t + 1;
-    if (V > a.kv_len) V = a.kv_len;
+    const int64_t V = valid_len(a.seq_len, a.seq_pos0, b, t, a.kv_len, a.q_pos0);
     if (a.mask == MASK_CAUSAL) {
         lo = 0;
         hi = V;
@@ -248,15 +248,14 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
     for (int u = 0; u < G::NQL; ++u) {
         const int qs = G::SPLIT ? 0 : g * G::NQL + u;
         if (qs < nq_avail) {
-            row_range(a, t0 + qs, lo[u], hi[u]);
+            row_range(a, b, t0 + qs, lo[u], hi[u]);
         } else {
             lo[u] = 0;
             hi[u] = 0;
         }
     }
     if (FINE) {
-        int64_t V = a.q_pos0 + t0 + 1;
-        if (V > a.kv_len) V = a.kv_len;
+        const int64_t V = valid_len(a.seq_len, a.seq_pos0, b, t0, a.kv_len, a.q_pos0);
         lo_all = lo_in = a.sink;
         hi_all = hi_in = V > a.k ? V - a.window : 0;
         lo[0] = lo_all;
@@ -264,7 +263,7 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
     } else {
         for (int qs = 0; qs < nq_avail; ++qs) {
             int64_t x, y;
-            row_range(a, t0 + qs, x, y);
+            row_range(a, b, t0 + qs, x, y);
             lo_in = max(lo_in, x);
             hi_in = min(hi_in, y);
             if (y > x) {
@@ -530,7 +529,7 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
     for (int u = 0; u < G::NQL; ++u) {
         const int qs = G::SPLIT ? 0 : g * G::NQL + u;
         if (qs < nq_avail) {
-            row_range(a, t0 + qs, lo[u], hi[u]);
+            row_range(a, b, t0 + qs, lo[u], hi[u]);
         } else {
             lo[u] = 0;
             hi[u] = 0;
@@ -541,7 +540,7 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
     int64_t lo_blk = INT64_MAX, hi_blk = 0;
     for (int qs = 0; qs < nq_blk; ++qs) {
         int64_t x, y;
-        row_range(a, tq0 + qs, x, y);
+        row_range(a, b, tq0 + qs, x, y);
         if (y > x) {
             lo_blk = min(lo_blk, x);
             hi_blk = max(hi_blk, y);

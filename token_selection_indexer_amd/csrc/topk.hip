@@ -957,8 +957,7 @@ __device__ __forceinline__ bool setup_row(const SelectArgs &a, int64_t row, Row 
                           bool write_fixed)
 {
     const int64_t t = row % a.n_q;
-    int64_t V = a.q_pos0 + t + 1;
-    if (V > a.kv_len) V = a.kv_len;
+    const int64_t V = valid_len(a.seq_len, a.seq_pos0, (int)(row / a.n_q), t, a.kv_len, a.q_pos0);
     int32_t *out = a.out + row * a.out_stride;
     r.sc = a.scores + row * a.n_in;
     r.ids = a.cand_ids ? a.cand_ids + row * a.n_in : nullptr;

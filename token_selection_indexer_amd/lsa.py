@@ -30,9 +30,12 @@ EXPORTS = ("lsa_index_scores", "lsa_topk_select", "lsa_page_summary", "lsa_page_
 
 
 class IndexShape(ctypes.Structure):
+    """lsa_index_shape.  seq_len / seq_pos0: device pointers of per-sequence int32 arrays (ragged
+    batches) or None."""
     _fields_ = [("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("kv_len", ctypes.c_int64),
-                ("q_pos0", ctypes.c_int64)]
+                ("q_pos0", ctypes.c_int64), ("seq_len", ctypes.c_void_p),
+                ("seq_pos0", ctypes.c_void_p)]
 
 
 class Budget(ctypes.Structure):
@@ -228,31 +231,45 @@ def _check_index_operands(q, w, keys):
         raise ValueError(f"keys {tuple(keys.shape)} do not match q {tuple(q.shape)}")
 
 
-def index_shape(q: torch.Tensor, keys: torch.Tensor, q_pos0: Optional[int] = None) -> IndexShape:
+def _ragged(shape: IndexShape, device, seq_lens=None, seq_pos0=None) -> IndexShape:
+    """Attach per-sequence lengths / first-query positions (int32 device tensors [B])."""
+    for t, name in ((seq_lens, "seq_lens"), (seq_pos0, "seq_pos0")):
+        if t is not None:
+            _need(t, name, torch.int32, shape=(shape.batch,), device=device)
+    shape.seq_len = None if seq_lens is None else seq_lens.data_ptr()
+    shape.seq_pos0 = None if seq_pos0 is None else seq_pos0.data_ptr()
+    return shape
+
+
+def index_shape(q: torch.Tensor, keys: torch.Tensor, q_pos0: Optional[int] = None,
+                seq_lens=None, seq_pos0=None) -> IndexShape:
     B, T, H, d = q.shape
     L = keys.shape[1]
-    return IndexShape(B, T, H, d, L, L - T if q_pos0 is None else q_pos0)
+    sh = IndexShape(B, T, H, d, L, L - T if q_pos0 is None else q_pos0)
+    return _ragged(sh, q.device, seq_lens, seq_pos0)
 
 
-def index_scores(q, w, keys, key_scale=None, q_pos0=None, out=None, stream=None):
-    """scores [B, n_q, L] fp32 (q_pos0 defaults to L - n_q: the queries are the last tokens)."""
+def index_scores(q, w, keys, key_scale=None, q_pos0=None, out=None, stream=None, seq_lens=None,
+                 seq_pos0=None):
+    """scores [B, n_q, L] fp32 (q_pos0 defaults to L - n_q: the queries are the last tokens;
+    seq_lens / seq_pos0: per-sequence int32 device tensors for a ragged batch)."""
     _need(q, "q", torch.bfloat16, 4)
     _check_index_operands(q, w, keys)
     kd, ks = _key_args(keys, key_scale)
-    shape = index_shape(q, keys, q_pos0)
+    shape = index_shape(q, keys, q_pos0, seq_lens, seq_pos0)
     out = _out(out, "out", (shape.batch, shape.n_q, shape.kv_len), torch.float32, q.device)
     lsa_index_scores(shape, q, w, keys, kd, ks, out, stream)
     return out
 
 
 def index_select(q, w, keys, key_scale, k, sink, window, q_pos0=None, scores=None, idx=None,
-                 ws: Optional[Workspace] = None, stream=None):
+                 ws: Optional[Workspace] = None, stream=None, seq_lens=None, seq_pos0=None):
     """Scores [B, n_q, L] fp32 and the selection idx [B, n_q, k] int32 in one call (fused for
     decode): the outputs of index_scores followed by topk_select."""
     _need(q, "q", torch.bfloat16, 4)
     _check_index_operands(q, w, keys)
     kd, ks = _key_args(keys, key_scale)
-    shape = index_shape(q, keys, q_pos0)
+    shape = index_shape(q, keys, q_pos0, seq_lens, seq_pos0)
     B, T, L = shape.batch, shape.n_q, shape.kv_len
     scores = _out(scores, "scores", (B, T, L), torch.float32, q.device)
     idx = _out(idx, "idx", (B, T, k), torch.int32, q.device)
@@ -264,11 +281,11 @@ def index_select(q, w, keys, key_scale, k, sink, window, q_pos0=None, scores=Non
 
 
 def topk_select(scores, k, sink, window, kv_len, q_pos0, cand_ids=None, out=None,
-                ws: Optional[Workspace] = None, stream=None):
+                ws: Optional[Workspace] = None, stream=None, seq_lens=None, seq_pos0=None):
     """idx [B, n_q, k] int32 from flat scores [B, n_q, L] or candidates (scores, cand_ids)."""
     _need(scores, "scores", torch.float32, 3)
     B, T, n = scores.shape
-    shape = IndexShape(B, T, 1, 64, kv_len, q_pos0)
+    shape = _ragged(IndexShape(B, T, 1, 64, kv_len, q_pos0), scores.device, seq_lens, seq_pos0)
     if cand_ids is not None:
         _need(cand_ids, "cand_ids", torch.int32, shape=scores.shape, device=scores.device)
     out = _out(out, "out", (B, T, k), torch.int32, scores.device)
@@ -279,26 +296,27 @@ def topk_select(scores, k, sink, window, kv_len, q_pos0, cand_ids=None, out=None
     return out
 
 
-def page_summary(keys, key_scale, page, page_lo=0, page_hi=None, out=None, stream=None):
+def page_summary(keys, key_scale, page, page_lo=0, page_hi=None, out=None, stream=None,
+                 seq_lens=None):
     """page keys [B, ceil(L/P), d] bf16."""
     _need(keys, "keys", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), dim=3)
     kd, ks = _key_args(keys, key_scale)
     B, L, d = keys.shape
     n_pages = (L + page - 1) // page
     out = _out(out, "out", (B, n_pages, d), torch.bfloat16, keys.device)
-    shape = IndexShape(B, 1, 64, d, L, L - 1)
+    shape = _ragged(IndexShape(B, 1, 64, d, L, L - 1), keys.device, seq_lens)
     lsa_page_summary(shape, page, keys, kd, ks, page_lo, n_pages if page_hi is None else page_hi,
                      out, stream)
     return out
 
 
 def page_recall(q, w, page_keys, keys, key_scale, k, sink, window, page, m_pages, q_pos0=None,
-                ws: Optional[Workspace] = None, stream=None):
+                ws: Optional[Workspace] = None, stream=None, seq_lens=None, seq_pos0=None):
     """(page_ids [B,n_q,M], cand_scores [B,n_q,M*P], cand_ids [B,n_q,M*P])."""
     _need(q, "q", torch.bfloat16, 4)
     _check_index_operands(q, w, keys)
     kd, ks = _key_args(keys, key_scale)
-    shape = index_shape(q, keys, q_pos0)
+    shape = index_shape(q, keys, q_pos0, seq_lens, seq_pos0)
     _need(page_keys, "page_keys", torch.bfloat16, device=q.device,
           shape=(shape.batch, (shape.kv_len + page - 1) // page, shape.head_dim))
     B, T = shape.batch, shape.n_q
@@ -315,7 +333,7 @@ def page_recall(q, w, page_keys, keys, key_scale, k, sink, window, page, m_pages
 
 
 def sparse_attn(q, k, v, idx, scale, sink=0, window=0, d_v=None, latent=None, want_lse=True,
-                ws: Optional[Workspace] = None, out=None, stream=None):
+                ws: Optional[Workspace] = None, out=None, stream=None, seq_lens=None):
     """out [B, n_q, Hq, d_v] bf16 and lse [B, n_q, Hq] fp32 (or None).  Latent cache: pass v=None
     (or v is k) and d_v = the value width."""
     _need(q, "q", torch.bfloat16, 4)
@@ -342,7 +360,7 @@ def sparse_attn(q, k, v, idx, scale, sink=0, window=0, d_v=None, latent=None, wa
     if d_v > v.shape[2]:
         raise ValueError(f"d_v {d_v} exceeds the value rows ({v.shape[2]})")
     attn = AttnShape(Hq, dqk, d_v, 1 if latent else 0, k.shape[2], v.shape[2], scale)
-    shape = IndexShape(B, T, 64, 128, L, 0)
+    shape = _ragged(IndexShape(B, T, 64, 128, L, 0), dev, seq_lens)
     bud = Budget(idx.shape[2], sink, window)
     out = _out(out, "out", (B, T, Hq, d_v), torch.bfloat16, dev)
     lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev) if want_lse else None
