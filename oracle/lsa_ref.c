@@ -113,15 +113,30 @@ static double key_elem(const void *keys, int key_dtype, const float *scale, int 
  *   E  sum_h |w[t,h]| * sum_i |q[t,h,i] * k[s,i]|     (magnitude before cancellation)
  * A and E are the error scales the tolerance on I is stated against.
  */
+/* The formula above for one query row t whose H x d query values are qd (as doubles). */
+static void index_scores_row(int64_t t, int H, int d, int64_t L, int64_t pos, const double *qd,
+                             const float *w, const void *keys, int key_dtype, const float *scale,
+                             double *I, double *A, double *E);
+
 void lsa_ref_index_scores(int64_t n_rows, int H, int d, int64_t L, const int64_t *pos,
                           const uint16_t *q, const float *w, const void *keys, int key_dtype,
                           const float *scale, double *I, double *A, double *E)
 {
+    double *qd = (double *)malloc(sizeof(double) * (size_t)H * (size_t)d);
     for (int64_t t = 0; t < n_rows; ++t) {
-        int64_t V = pos[t] + 1 < L ? pos[t] + 1 : L;
-        double *qd = (double *)malloc(sizeof(double) * (size_t)H * (size_t)d);
         for (int64_t j = 0; j < (int64_t)H * d; ++j)
             qd[j] = lsa_ref_bf16_to_double(q[t * H * d + j]);
+        index_scores_row(t, H, d, L, pos[t], qd, w, keys, key_dtype, scale, I, A, E);
+    }
+    free(qd);
+}
+
+static void index_scores_row(int64_t t, int H, int d, int64_t L, int64_t pos, const double *qd,
+                             const float *w, const void *keys, int key_dtype, const float *scale,
+                             double *I, double *A, double *E)
+{
+    {
+        int64_t V = pos + 1 < L ? pos + 1 : L;
 #pragma omp parallel for schedule(static)
         for (int64_t s = 0; s < L; ++s) {
             double score = 0.0, amag = 0.0, emag = 0.0;
@@ -148,8 +163,77 @@ void lsa_ref_index_scores(int64_t n_rows, int H, int d, int64_t L, const int64_t
             if (A) A[t * L + s] = amag;
             if (E) E[t * L + s] = emag;
         }
-        free(qd);
     }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* fp8 queries: per-(query, head) e4m3 quantisation, then the scores of the quantised queries. */
+/* ------------------------------------------------------------------------------------------ */
+
+/*
+ * [DSA] 1. Lightweight Scoring Module, "Quantized computation": the indexer may run its
+ * products in 8-bit floating point.  Here a query row q[t,h,:] (bf16) is quantised the way the
+ * fp8 key rows are:
+ *     s      = max_i |q[t,h,i]| / 448           (binary32 division; 1 for an all-zero row)
+ *     code_i = e4m3fn( q[t,h,i] / s )           (binary32 division, then round to nearest with
+ *                                                ties to even, saturating at +-448)
+ * and the scores are the formula of lsa_ref_index_scores with q[t,h,i] replaced by
+ * s * e4m3(code_i) (exact in binary64).
+ */
+
+/* binary32 -> e4m3fn code: the nearest of the 127 non-negative finite values (magnitudes at or
+ * beyond the largest, 448, give 448), ties to the even code; the sign is copied (+-0 keep their
+ * sign).  NaN gives the NaN code 0x7F. */
+uint8_t lsa_ref_f32_to_e4m3fn_sat(float x)
+{
+    if (x != x) return 0x7F;
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs((double)x);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    int best = 0;
+    double best_err = a;
+    for (int c = 1; c <= 0x7E; ++c) {
+        double err = fabs(a - lsa_ref_e4m3fn_to_double((uint8_t)c));
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+void lsa_ref_quantize_rows(int64_t n_rows, int d, const uint16_t *x, uint8_t *codes,
+                           float *scale)
+{
+    for (int64_t r = 0; r < n_rows; ++r) {
+        float amax = 0.0f;
+        for (int i = 0; i < d; ++i) {
+            float v = fabsf((float)lsa_ref_bf16_to_double(x[r * d + i]));
+            if (v > amax) amax = v;
+        }
+        volatile float s = amax > 0.0f ? amax / 448.0f : 1.0f; /* one binary32 division */
+        scale[r] = s;
+        for (int i = 0; i < d; ++i) {
+            volatile float y = (float)lsa_ref_bf16_to_double(x[r * d + i]) / s;
+            codes[r * d + i] = lsa_ref_f32_to_e4m3fn_sat(y);
+        }
+    }
+}
+
+void lsa_ref_index_scores_q8(int64_t n_rows, int H, int d, int64_t L, const int64_t *pos,
+                             const uint8_t *q8, const float *q_scale, const float *w,
+                             const void *keys, int key_dtype, const float *scale, double *I,
+                             double *A, double *E)
+{
+    double *qd = (double *)malloc(sizeof(double) * (size_t)H * (size_t)d);
+    for (int64_t t = 0; t < n_rows; ++t) {
+        for (int h = 0; h < H; ++h)
+            for (int i = 0; i < d; ++i)
+                qd[h * d + i] = (double)q_scale[t * H + h] *
+                                lsa_ref_e4m3fn_to_double(q8[(t * H + h) * d + i]);
+        index_scores_row(t, H, d, L, pos[t], qd, w, keys, key_dtype, scale, I, A, E);
+    }
+    free(qd);
 }
 
 /* ------------------------------------------------------------------------------------------ */

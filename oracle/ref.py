@@ -42,6 +42,11 @@ def lib():
         L.lsa_ref_index_scores.argtypes = [_I64, _I32, _I32, _I64, _P, _P, _P, _P, _I32, _P,
                                            _P, _P, _P]
         L.lsa_ref_select.argtypes = [_I64, _I64, _P, _P, _P, _I32, _I32, _I32, _P]
+        L.lsa_ref_f32_to_e4m3fn_sat.argtypes = [ctypes.c_float]
+        L.lsa_ref_f32_to_e4m3fn_sat.restype = ctypes.c_uint8
+        L.lsa_ref_quantize_rows.argtypes = [_I64, _I32, _P, _P, _P]
+        L.lsa_ref_index_scores_q8.argtypes = [_I64, _I32, _I32, _I64, _P, _P, _P, _P, _P, _I32,
+                                              _P, _P, _P, _P]
         L.lsa_ref_page_keys.argtypes = [_I64, _I32, _I32, _P, _I32, _P, _P]
         L.lsa_ref_page_recall.argtypes = [_I64, _I32, _I32, _I64, _P, _P, _P, _P, _P, _I32, _P,
                                           _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]
@@ -103,6 +108,41 @@ def index_scores(q, w, keys, scale, pos):
     E = np.empty((T, L), np.float64)
     lib().lsa_ref_index_scores(T, H, d, L, _ptr(pos), _ptr(q), _ptr(w), _ptr(keys), kd,
                                _ptr(scale), _ptr(I), _ptr(A), _ptr(E))
+    return I, A, E
+
+
+# --------------------------------------------------------------------------------- fp8 queries
+def f32_to_e4m3fn_sat(x: float) -> int:
+    return lib().lsa_ref_f32_to_e4m3fn_sat(float(x))
+
+
+def quantize_rows(x):
+    """x uint16 (bf16 bits) [..., d] -> (codes uint8 [..., d], scale f32 [...]): per-row e4m3
+    quantisation (scale = amax / 448)."""
+    x = _c(x, np.uint16)
+    d = x.shape[-1]
+    rows = x.size // d
+    codes = np.empty(x.shape, np.uint8)
+    scale = np.empty(x.shape[:-1], np.float32)
+    lib().lsa_ref_quantize_rows(rows, d, _ptr(x), _ptr(codes), _ptr(scale))
+    return codes, scale
+
+
+def index_scores_q8(q8, q_scale, w, keys, scale, pos):
+    """q8 uint8 [T,H,d] e4m3 codes, q_scale f32 [T,H], w f32 [T,H], keys / scale as for
+    index_scores -> (I, A, E) fp64 [T,L]."""
+    q8 = _c(q8, np.uint8)
+    T, H, d = q8.shape
+    keys, kd, scale = _key_args(keys, scale)
+    L = keys.shape[0]
+    qs = _c(q_scale, np.float32)
+    w = _c(w, np.float32)
+    pos = _c(pos, np.int64)
+    I = np.empty((T, L), np.float64)
+    A = np.empty((T, L), np.float64)
+    E = np.empty((T, L), np.float64)
+    lib().lsa_ref_index_scores_q8(T, H, d, L, _ptr(pos), _ptr(q8), _ptr(qs), _ptr(w), _ptr(keys),
+                                  kd, _ptr(scale), _ptr(I), _ptr(A), _ptr(E))
     return I, A, E
 
 

@@ -178,6 +178,89 @@ def test_scores_weight_homogeneity_and_head_permutation():
     np.testing.assert_allclose(Ip, I, rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------------------------ fp8 queries
+def _e4m3_torch(x: np.ndarray) -> np.ndarray:
+    """Library routine: torch's binary32 -> float8_e4m3fn conversion (after a clamp to the
+    format's range, so the conversion saturates)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_f32_to_e4m3fn_matches_torch_including_ties_and_saturation():
+    codes = np.arange(0x7F, dtype=np.uint8)  # non-negative finite codes
+    vals = np.array([ref.e4m3fn_to_double(c) for c in codes])
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)  # exact halfway points (ties)
+    r = np.random.default_rng(3)
+    rand = (r.standard_normal(4000) * 60).astype(np.float32)
+    edge = np.float32([0.0, -0.0, 1e-30, -1e-30, 2.0 ** -10, 2.0 ** -9, 447.9, 448.0, 449.0,
+                       463.9, 464.0, 1e6, -1e6])
+    x = np.concatenate([vals.astype(np.float32), -vals.astype(np.float32), mids, -mids, rand, edge])
+    ours = np.array([ref.f32_to_e4m3fn_sat(v) for v in x], np.uint8)
+    lib = _e4m3_torch(x)
+    # +-0: both give a zero of the input's sign
+    assert np.array_equal(ours, lib)
+
+
+def test_quantize_rows_scale_codes_and_error_bound():
+    r = np.random.default_rng(4)
+    x = bf16_bits(r.standard_normal((50, 128)) * np.exp(r.uniform(-6, 6, (50, 1))))
+    x[7] = 0  # an all-zero row: scale 1, codes 0
+    codes, scale = ref.quantize_rows(x)
+    xv = bf16_vals(x)
+    amax = np.abs(xv).max(axis=1)
+    want_scale = np.where(amax > 0, (amax.astype(np.float32) / np.float32(448.0)), 1.0)
+    assert np.array_equal(scale, want_scale.astype(np.float32))
+    assert not codes[7].any() and scale[7] == 1.0
+    # codes are the library conversion of x / scale (binary32 division)
+    y = (xv.astype(np.float32) / scale[:, None]).astype(np.float32)
+    assert np.array_equal(codes, _e4m3_torch(y))
+    # every row's largest magnitude maps to +-448; dequantised values within half a step
+    deq = np.array([[ref.e4m3fn_to_double(c) for c in row] for row in codes]) * scale[:, None]
+    top = np.abs(np.array([[ref.e4m3fn_to_double(c) for c in row] for row in codes])).max(axis=1)
+    assert np.all(top[amax > 0] == 448.0)
+    rel = np.abs(deq - xv) / np.maximum(np.abs(xv), 2.0 ** -6 * scale[:, None])
+    assert rel.max() <= 2.0 ** -4 + 1e-12
+
+
+def test_quantize_rows_power_of_two_scaling():
+    """Scaling a row by 2^m scales its scale by 2^m and keeps its codes."""
+    r = np.random.default_rng(5)
+    xv = r.standard_normal((20, 64)).astype(np.float32)
+    c1, s1 = ref.quantize_rows(bf16_bits(xv))
+    c2, s2 = ref.quantize_rows(bf16_bits(xv * np.float32(2.0 ** 5)))
+    assert np.array_equal(c1, c2)
+    assert np.array_equal(s2, s1 * np.float32(32.0))
+
+
+def test_scores_q8_equal_scores_of_the_dequantised_query():
+    """With the scales folded into exactly representable values, the quantised-query scores are
+    the ordinary scores of the dequantised query: unit scales give the scores of q = e4m3(code)
+    (every e4m3 value is a bf16 value); power-of-two scales move into the head weights."""
+    r = np.random.default_rng(6)
+    T, H, d, L = 3, 4, 64, 200
+    q8 = r.integers(0, 0x7F, size=(T, H, d), dtype=np.uint8) | (r.integers(0, 2, (T, H, d)) << 7).astype(np.uint8)
+    w = r.standard_normal((T, H)).astype(np.float32)
+    keys = bf16_bits(r.standard_normal((L, d)))
+    pos = np.array([L - 1, 50, 120])
+    qv = np.array([[[ref.e4m3fn_to_double(c) for c in hd] for hd in row] for row in q8])
+    qb = bf16_bits(qv)
+    assert np.array_equal(bf16_vals(qb), qv)  # exactly representable
+    ones = np.ones((T, H), np.float32)
+    I8, A8, E8 = ref.index_scores_q8(q8, ones, w, keys, None, pos)
+    Ib, Ab, Eb = ref.index_scores(qb, w, keys, None, pos)
+    assert np.array_equal(I8, Ib) and np.array_equal(A8, Ab) and np.array_equal(E8, Eb)
+    p2 = (2.0 ** r.integers(-8, 8, size=(T, H))).astype(np.float32)
+    I8s, _, _ = ref.index_scores_q8(q8, p2, w, keys, None, pos)
+    Ibs, _, _ = ref.index_scores(qb, w * p2, keys, None, pos)
+    assert np.array_equal(I8s, Ibs)
+    # fp8 keys as well (their own per-token scales)
+    k8 = r.integers(0, 0x7F, size=(L, d), dtype=np.uint8)
+    ks = (r.uniform(0.5, 2, L)).astype(np.float32)
+    I8k, _, _ = ref.index_scores_q8(q8, ones, w, k8, ks, pos)
+    Ibk, _, _ = ref.index_scores(qb, w, k8, ks, pos)
+    assert np.array_equal(I8k, Ibk)
+
+
 # ------------------------------------------------------------------------------ a2 select
 def _lexsort_top(scores_row, ids, need):
     """Library sort: order by (score desc, id asc), keep need, return ascending ids."""
