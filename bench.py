@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "indexed queries/s (score+top-k) and sparse-attn TB/s at 128K and 1M ctx, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
+MFMA_FP8_PEAK_TFS = 5000.0
 FLUSH_BYTES = 1 << 30
 
 
@@ -272,6 +273,44 @@ def extra_prefill(torch, lsa, inputs, cfg, tm: Timing):
     return res
 
 
+def extra_prefill_q8(torch, lsa, inputs, cfg, tm: Timing):
+    """The chunked-prefill shape with fp8 keys, scored with fp8 queries on the 8-bit MFMA
+    (quantisation timed apart) and, beside it, with bf16 queries against the same fp8 keys."""
+    from dataclasses import replace
+    base = cfg.PREFILL_8K_AT_128K
+    w = replace(base, name=base.name + "_fp8keys", index=replace(base.index, key_dtype="fp8"))
+    s, b = w.index, w.budget
+    dev = "cuda"
+    inp = inputs.index_inputs(w, dev)
+    scores = torch.empty((1, s.n_q, s.kv_len), dtype=torch.float32, device=dev)
+    q8, qs = lsa.quantize_queries(inp["q"])
+
+    def f_quant():
+        lsa.quantize_queries(inp["q"], q8=q8, q_scale=qs)
+
+    def f_q8():
+        lsa.index_scores_q8(q8, qs, inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0, out=scores)
+
+    def f_bf16q():
+        lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0, out=scores)
+
+    f_quant(), f_q8(), f_bf16q()
+    d = {"quantize": tm.both(f_quant, 0.05, cold_too=False), "score_q8": tm.both(f_q8, 8.0),
+         "score_bf16q": tm.both(f_bf16q, 14.0)}
+    V = [min(s.kv_len, s.q_pos0 + t + 1) for t in range(s.n_q)]
+    flops = 2.0 * sum(V) * s.heads * s.head_dim
+    t8, t16 = d["score_q8"]["warm"]["mean"], d["score_bf16q"]["warm"]["mean"]
+    res = {"workload": w.name, "dist": d, "score_flops": flops,
+           "score_q8_TFLOPs": flops / (t8 * 1e-3) / 1e12,
+           "score_q8_mfma_frac_fp8_peak": flops / (t8 * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFS,
+           "score_bf16q_TFLOPs": flops / (t16 * 1e-3) / 1e12,
+           "speedup_q8_vs_bf16q": t16 / t8,
+           "indexed_qps_q8": s.n_q / ((t8 + d["quantize"]["warm"]["mean"]) * 1e-3)}
+    del inp, scores, q8, qs
+    torch.cuda.empty_cache()
+    return res
+
+
 def extra_hi(torch, lsa, inputs, w, tm: Timing):
     import numpy as np
     s, b, a, hi = w.index, w.budget, w.attn, w.hi
@@ -456,7 +495,18 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
         torch.cuda.synchronize()
         log(f"[bench] copy x{steps}: {src.numel() * 4} bytes read and written per launch")
         return
-    if stage.startswith("prefill_"):
+    if stage == "prefill_q8":
+        from dataclasses import replace
+        base = cfg.PREFILL_8K_AT_128K
+        w = replace(base, index=replace(base.index, key_dtype="fp8"))
+        s = w.index
+        inp = inputs.index_inputs(w, dev)
+        q8, qs = lsa.quantize_queries(inp["q"])
+        scores = lsa.index_scores_q8(q8, qs, inp["w"], inp["keys"], inp["scale"], q_pos0=s.q_pos0)
+        fns = {"prefill_q8": lambda: lsa.index_scores_q8(q8, qs, inp["w"], inp["keys"],
+                                                         inp["scale"], q_pos0=s.q_pos0,
+                                                         out=scores)}
+    elif stage.startswith("prefill_"):
         w = cfg.PREFILL_8K_AT_128K
         s, b, a = w.index, w.budget, w.attn
         inp = inputs.index_inputs(w, dev)
@@ -516,6 +566,7 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
 
 
 STAGES = ["score", "topk", "index", "attn", "copy", "prefill_score", "prefill_topk", "prefill_attn",
+          "prefill_q8",
           "hi1m_summary", "hi1m_recall", "hi1m_topk"]
 
 
@@ -575,6 +626,8 @@ def main():
     if args.extras:
         log("[bench] extra: chunked prefill 8K @ 128K")
         extras["prefill_8k_128k"] = extra_prefill(torch, lsa, inputs, cfg, tm)
+        log("[bench] extra: chunked prefill with fp8 queries")
+        extras["prefill_8k_128k_fp8q"] = extra_prefill_q8(torch, lsa, inputs, cfg, tm)
         log("[bench] extra: HI at 1M")
         extras["decode_1m_hi"] = extra_hi(torch, lsa, inputs, cfg.DECODE_1M_HI, tm)
         log("[bench] extra: HI + cross-layer x4 at 256K")

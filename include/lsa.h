@@ -140,6 +140,37 @@ LSA_API lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budg
                            size_t ws_bytes, void *stream);
 
 /*
+ * lsa_quantize_queries -- fp8 queries for the quantised indexer (Baidu Cloud article, "1.
+ * Lightweight Scoring Module": the indexer's products may run in 8-bit floating point).  Each
+ * query row q[b,i,h,:] is quantised the way fp8 key rows are:
+ *     q_scale[b,i,h] = max_j |q[b,i,h,j]| / 448      (binary32 division; 1 for an all-zero row)
+ *     q8[b,i,h,j]    = e4m3fn( q[b,i,h,j] / q_scale[b,i,h] )   (binary32 division, round to
+ *                                                      nearest even, saturating at +-448)
+ *   q        [B, n_q, H, d] bf16 (4-byte aligned); uses batch, n_q, n_heads, head_dim of shape
+ *   q8       [B, n_q, H, d] e4m3 codes (2-byte aligned);  q_scale  [B, n_q, H] fp32
+ * Limits: head_dim 64 or 128.
+ */
+LSA_API lsa_status lsa_quantize_queries(const lsa_index_shape *shape, const void *q, uint8_t *q8,
+                                        float *q_scale, void *stream);
+
+/*
+ * lsa_index_scores_q8 -- lsa_index_scores with fp8 queries (from lsa_quantize_queries) against
+ * fp8 keys, the contraction on gfx950's 8-bit MFMA (v_mfma_f32_32x32x64_f8f6f4, fp32
+ * accumulation; twice the bf16 rate):
+ *     scores[b,i,s] = key_scale[b,s] * sum_h w[b,i,h] q_scale[b,i,h] ReLU( e4m3(q8[b,i,h,:]) .
+ *                     e4m3(keys[b,s,:]) )                     for s < V_i, -inf beyond
+ * i.e. the indexer scores of the dequantised queries.  These differ from the bf16-query scores
+ * by the query quantisation (relative error up to 2^-4 per element); the selection they give is
+ * an approximation of the bf16-query selection, not the same set.
+ *   key_dtype  must be LSA_KEY_FP8_E4M3 (else LSA_ERR_BAD_DTYPE);  q8 16-byte aligned
+ *   other arguments as for lsa_index_scores (ragged arrays included)
+ */
+LSA_API lsa_status lsa_index_scores_q8(const lsa_index_shape *shape, const uint8_t *q8,
+                                       const float *q_scale, const float *w, const void *keys,
+                                       lsa_key_dtype key_dtype, const float *key_scale,
+                                       float *scores, void *stream);
+
+/*
  * lsa_index_select -- lsa_index_scores followed by lsa_topk_select (flat mode), fused for decode
  * (Baidu Cloud article, "Engineering Implementation Breakthroughs: 1. Operator Fusion
  * Optimization": scoring and selection as one operator, so the selection does not start from a

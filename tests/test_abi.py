@@ -267,3 +267,17 @@ def test_topk_select_noalloc_rejects(L):
     b = lsa.Budget(2048, 128, 896)
     assert lsa.lsa_workspace_bytes(lsa.OP_TOPK_SELECT, huge, b) > 16 << 20
     assert call(huge, b, huge.kv_len) == 4
+
+
+def test_q8_entry_points_reject(L):
+    """fp8 queries need fp8 keys; quantisation needs d in {64, 128}."""
+    v = ctypes.c_void_p
+    sh = _shape()
+    assert L.lsa_index_scores_q8(ctypes.byref(sh), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                                 lsa.KEY_BF16, None, v(FAKE), None) == 3
+    assert L.lsa_index_scores_q8(ctypes.byref(sh), None, v(FAKE), v(FAKE), v(FAKE),
+                                 lsa.KEY_FP8_E4M3, v(FAKE), v(FAKE), None) == 1
+    assert L.lsa_index_scores_q8(ctypes.byref(sh), v(FAKE + 4), v(FAKE), v(FAKE), v(FAKE),
+                                 lsa.KEY_FP8_E4M3, v(FAKE), v(FAKE), None) == 2
+    assert L.lsa_quantize_queries(ctypes.byref(_shape(d=96)), v(FAKE), v(FAKE), v(FAKE), None) == 4
+    assert L.lsa_quantize_queries(ctypes.byref(_shape()), None, v(FAKE), v(FAKE), None) == 1

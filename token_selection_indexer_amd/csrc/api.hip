@@ -268,6 +268,58 @@ lsa_status prepare_select(const lsa_index_shape *shape, lsa_budget budget, const
 
 } // namespace
 
+lsa_status lsa_quantize_queries(const lsa_index_shape *shape, const void *q, uint8_t *q8,
+                                float *q_scale, void *stream)
+{
+    if (!shape) return LSA_ERR_NULL_POINTER;
+    if (shape->batch < 0 || shape->n_q < 0 || shape->n_heads < 1) return LSA_ERR_BAD_SHAPE;
+    if (shape->head_dim != 64 && shape->head_dim != 128) return LSA_ERR_UNSUPPORTED;
+    if (!q || !q8 || !q_scale) return LSA_ERR_NULL_POINTER;
+    if (!aligned(q, 4) || !aligned(q8, 2) || !aligned(q_scale, 4)) return LSA_ERR_BAD_SHAPE;
+    const int64_t rows = (int64_t)shape->batch * shape->n_q * shape->n_heads;
+    if (rows == 0) return LSA_OK;
+    if ((rows + 3) / 4 >= (int64_t(1) << 31)) return LSA_ERR_UNSUPPORTED;
+    return device_status(lsa::launch_quantize_rows(static_cast<const uint16_t *>(q), rows,
+                                                   shape->head_dim, q8, q_scale,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+lsa_status lsa_index_scores_q8(const lsa_index_shape *shape, const uint8_t *q8,
+                               const float *q_scale, const float *w, const void *keys,
+                               lsa_key_dtype key_dtype, const float *key_scale, float *scores,
+                               void *stream)
+{
+    lsa_status st = check_index_shape(shape);
+    if (st != LSA_OK) return st;
+    if ((st = check_keys(key_dtype, keys, key_scale)) != LSA_OK) return st;
+    if (key_dtype != LSA_KEY_FP8_E4M3) return LSA_ERR_BAD_DTYPE; // 8-bit x 8-bit products
+    if (!q8 || !q_scale || !w || !scores) return LSA_ERR_NULL_POINTER;
+    if (!aligned(q8, 16) || !aligned(q_scale, 4) || !aligned(w, 4) || !aligned(scores, 4))
+        return LSA_ERR_BAD_SHAPE;
+    if ((int64_t)shape->n_q > kMaxGridYZ * 8) return LSA_ERR_UNSUPPORTED;
+    if ((int64_t)shape->batch * shape->n_q == 0) return LSA_OK;
+    lsa::ScoreArgs a{};
+    a.q8 = q8;
+    a.q_scale = q_scale;
+    a.w = w;
+    a.keys = keys;
+    a.kscale = key_scale;
+    a.out = scores;
+    a.batch = shape->batch;
+    a.n_q = shape->n_q;
+    a.heads = shape->n_heads;
+    a.dim = shape->head_dim;
+    a.n_keys = shape->kv_len;
+    a.n_out = shape->kv_len;
+    a.kv_len = shape->kv_len;
+    a.q_pos0 = shape->q_pos0;
+    a.seq_len = shape->seq_len;
+    a.seq_pos0 = shape->seq_pos0;
+    a.mask = lsa::MASK_CAUSAL;
+    a.fp8 = 1;
+    return device_status(lsa::launch_scores(a, static_cast<hipStream_t>(stream)));
+}
+
 lsa_status lsa_index_select(const lsa_index_shape *shape, lsa_budget budget, const void *q,
                             const float *w, const void *keys, lsa_key_dtype key_dtype,
                             const float *key_scale, float *scores, int32_t *idx, void *ws,

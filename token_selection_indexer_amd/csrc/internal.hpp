@@ -37,7 +37,16 @@ struct ScoreArgs {
     // [row][blockIdx.x].
     uint32_t *hist_fine;  // [rows][groups][2048] or nullptr
     uint32_t *hist_coarse; // [rows][groups][32]
+    // fp8 queries (q8 != nullptr): e4m3 codes [B, n_q, H, d] with one fp32 scale per (query,
+    // head); `q` is then unused and the keys must be e4m3 too
+    const uint8_t *q8;
+    const float *q_scale; // [B, n_q, H]
 };
+
+// Per-row e4m3 quantisation: scale[r] = amax / 448 (1 for a zero row), codes = round to
+// nearest even e4m3fn of x / scale, saturating.  x bf16 [rows, d], d in {64, 128}.
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int d, uint8_t *codes,
+                                float *scale, hipStream_t stream);
 
 // Flat or coarse scores: out[b,t,s] for s < n_out == n_keys, -inf outside the row's range.
 hipError_t launch_scores(const ScoreArgs &a, hipStream_t stream);

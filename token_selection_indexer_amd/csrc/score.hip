@@ -109,6 +109,42 @@ __device__ __forceinline__ void load_q(bf16x8_t (&qf)[MT][D / 16], const uint16_
     }
 }
 
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// fp8 query fragments for v_mfma_f32_32x32x64_f8f6f4: lane l supplies A row l%32 (the indexer
+// row of load_q) and 32 codes of it; lane half g takes d in [g*D/2, (g+1)*D/2), K-step kk the 32
+// codes g*D/2 + 32*kk + [0, 32) -- the same (half, byte) -> d map the key operand uses, so the
+// contraction covers every d once.
+template <int D, int H, int MT>
+__device__ __forceinline__ void load_q8(i32x8_t (&qf)[MT][D / 64], const uint8_t *qbase,
+                                        int nq_avail)
+{
+    const int l = lane_id(), rho = l & 31, gk = l >> 5;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        int qs, h;
+        bool valid;
+        rprime_to_qh<H, false>(a_row_to_rprime<MT>(mt, rho), qs, h, valid);
+        valid = valid && qs < nq_avail;
+        const uint8_t *src = qbase + ((int64_t)qs * H + h) * D + (D / 2) * gk;
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk) {
+            const uint4 x = valid ? ld16(src + 32 * kk) : make_uint4(0, 0, 0, 0);
+            const uint4 y = valid ? ld16(src + 32 * kk + 16) : make_uint4(0, 0, 0, 0);
+            qf[mt][kk] = i32x8_t{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                                 (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        }
+    }
+}
+
+// D(32x32, fp32) += A(32x64, e4m3) * B(64x32, e4m3), no block scales: lane l supplies A row
+// l%32 and B column l%32 with the same 32 K slots for the same (l/32, byte); D in the layout of
+// mfma_32x32x16.
+__device__ __forceinline__ f32x16_t mfma_32x32x64_f8(i32x8_t a, i32x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 template <int H, int MT, bool ONEQ>
 __device__ __forceinline__ void load_w(float (&wv)[16 * MT], const float *wbase, int nq_avail)
 {
@@ -487,13 +523,17 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
 // tile kernel (prefill)
 // ------------------------------------------------------------------------------------------
 
-template <bool FP8, int D, int H, int MT, int WAVES, int KB>
+// Q8: fp8 queries (a.q8, a.q_scale) against e4m3 keys on v_mfma_f32_32x32x64_f8f6f4; the keys
+// are staged in LDS as the codes themselves (a 144-byte padded row at d = 128) and each query
+// scale is folded into its head weight.
+template <bool FP8, int D, int H, int MT, int WAVES, int KB, bool Q8 = false>
 __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
 {
+    static_assert(!Q8 || FP8, "fp8 queries meet fp8 keys");
     using G = Geo<H, MT, false>;
-    constexpr int KS = D / 16;
+    constexpr int KS = Q8 ? D / 64 : D / 16;          // MFMA K-steps per key block
     constexpr int QPB = WAVES * G::NQW;
-    constexpr int ROWB = D * 2 + 16;                  // LDS bytes per staged key (bf16 + pad)
+    constexpr int ROWB = Q8 ? D + 16 : D * 2 + 16;    // LDS bytes per staged key (+ pad)
     constexpr int ESZ = FP8 ? 1 : 2;
     constexpr int CPR = D * ESZ / 16;                 // 16-byte source chunks per key row
     constexpr int CHUNKS = KB * CPR;
@@ -511,16 +551,26 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
     const int64_t t0 = tq0 + (int64_t)wv_id * G::NQW;
     const int nq_avail = (int)max((int64_t)0, min((int64_t)G::NQW, (int64_t)a.n_q - t0));
 
-    bf16x8_t qf[MT][KS];
+    using QF = std::conditional_t<Q8, i32x8_t, bf16x8_t>;
+    QF qf[MT][KS];
     float wv[G::VPL];
     if (nq_avail > 0) {
-        load_q<D, H, MT, false>(qf, a.q + ((int64_t)b * a.n_q + t0) * H * D, nq_avail);
-        load_w<H, MT, false>(wv, a.w + ((int64_t)b * a.n_q + t0) * H, nq_avail);
+        if constexpr (Q8) {
+            load_q8<D, H, MT>(qf, a.q8 + ((int64_t)b * a.n_q + t0) * H * D, nq_avail);
+            load_w<H, MT, false>(wv, a.w + ((int64_t)b * a.n_q + t0) * H, nq_avail);
+            float qs[G::VPL];
+            load_w<H, MT, false>(qs, a.q_scale + ((int64_t)b * a.n_q + t0) * H, nq_avail);
+#pragma unroll
+            for (int v = 0; v < G::VPL; ++v) wv[v] *= qs[v]; // ReLU(s x) = s ReLU(x), s > 0
+        } else {
+            load_q<D, H, MT, false>(qf, a.q + ((int64_t)b * a.n_q + t0) * H * D, nq_avail);
+            load_w<H, MT, false>(wv, a.w + ((int64_t)b * a.n_q + t0) * H, nq_avail);
+        }
     } else {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) qf[mt][kk] = bf16x8_t{};
+            for (int kk = 0; kk < KS; ++kk) qf[mt][kk] = QF{};
 #pragma unroll
         for (int v = 0; v < G::VPL; ++v) wv[v] = 0.0f;
     }
@@ -579,7 +629,9 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
             const int c = threadIdx.x + i * NT;
             const int key = c / CPR, col = c % CPR;
             uint8_t *dst = &lds_k[buf][key * ROWB];
-            if (FP8) {
+            if constexpr (Q8) { // the codes as they are
+                *reinterpret_cast<u32x4_t *>(dst + col * 16) = bitcast<u32x4_t>(stage[i]);
+            } else if (FP8) {
                 const uint2 lo2 = e4m3x4_to_bf16x4(stage[i].x), hi2 = e4m3x4_to_bf16x4(stage[i].y);
                 const uint2 lo3 = e4m3x4_to_bf16x4(stage[i].z), hi3 = e4m3x4_to_bf16x4(stage[i].w);
                 reinterpret_cast<uint4 *>(dst + col * 32)[0] = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
@@ -608,14 +660,24 @@ __global__ __launch_bounds__(WAVES *kWave) void score_tile_kernel(ScoreArgs a)
             // issued before the epilogue of block nt, so the epilogue's VALU work overlaps them.
             f32x16_t acc[2][MT];
             auto mma = [&](int nt, f32x16_t (&ac)[MT]) {
-                const uint8_t *src = &lds_k[buf][(nt * 32 + n) * ROWB + D * g];
+                // lane half g: the key bytes of d in [g*D/2, (g+1)*D/2)
+                const uint8_t *src = &lds_k[buf][(nt * 32 + n) * ROWB + (Q8 ? D / 2 : D) * g];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) ac[mt] = f32x16_t{};
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
-                    const bf16x8_t bk = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(src + 16 * kk));
+                    if constexpr (Q8) {
+                        const uint4 x = *reinterpret_cast<const uint4 *>(src + 32 * kk);
+                        const uint4 y = *reinterpret_cast<const uint4 *>(src + 32 * kk + 16);
+                        const i32x8_t bk = i32x8_t{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                                                   (int)y.x, (int)y.y, (int)y.z, (int)y.w};
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) ac[mt] = mfma_32x32x16(qf[mt][kk], bk, ac[mt]);
+                        for (int mt = 0; mt < MT; ++mt) ac[mt] = mfma_32x32x64_f8(qf[mt][kk], bk, ac[mt]);
+                    } else {
+                        const bf16x8_t bk = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(src + 16 * kk));
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) ac[mt] = mfma_32x32x16(qf[mt][kk], bk, ac[mt]);
+                    }
                 }
             };
             auto epi = [&](int nt, const f32x16_t (&ac)[MT]) {
@@ -691,6 +753,20 @@ hipError_t launch_flat(const ScoreArgs &a, hipStream_t st)
 {
     constexpr int MT = H == 64 ? 2 : 1;
     using G = Geo<H, MT, false>;
+    if (a.q8) { // fp8 queries: the tile kernel for every shape (keys e4m3)
+        if constexpr (FP8) {
+            if (a.hist_fine) return hipErrorInvalidValue;
+            // 256-key tiles: 2 x 36 KB of LDS at d = 128
+            constexpr int WAVES = 8, KB = 256;
+            constexpr int QPB = WAVES * G::NQW;
+            dim3 grid((unsigned)((a.n_q + QPB - 1) / QPB), (unsigned)a.batch);
+            hipLaunchKernelGGL((score_tile_kernel<true, D, H, MT, WAVES, KB, true>), grid,
+                               dim3(WAVES * kWave), 0, st, a);
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
     if (a.n_q <= 2 * G::NQW) {
         // Long launches (at least 32 blocks = 1024 keys per wave with 512 workgroups): long-lived
         // waves amortise the per-wave load of q and w, and up to 3 blocks in flight per wave
@@ -779,6 +855,72 @@ bool scores_supported(int heads, int dim)
 {
     return (dim == 64 || dim == 128) &&
            (heads == 4 || heads == 8 || heads == 16 || heads == 32 || heads == 64);
+}
+
+// ------------------------------------------------------------------------------------------
+// fp8 query quantisation
+// ------------------------------------------------------------------------------------------
+
+namespace {
+
+// binary32 -> e4m3fn code, round to nearest with ties to even, saturating at +-448 (the format:
+// bias 7, 3 mantissa bits, subnormals m * 2^-9, no infinities).  Finite inputs.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float y)
+{
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a >= 0x43e00000u) return sign | 0x7eu;             // |y| >= 448
+    if (a < 0x3c800000u) {                                   // |y| < 2^-6: subnormal codes
+        // m = round_even(|y| * 2^9) in 0..8; 8 is the smallest normal's code (0x08)
+        const float m = __builtin_rintf(__uint_as_float(a) * 512.0f); // exact scaling
+        return sign | (uint32_t)m;
+    }
+    // normal: keep 3 mantissa bits of the binary32 with round to nearest even (a carry moves
+    // into the exponent), then rebias 127 -> 7
+    const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+    const uint32_t code = r - ((127u - 7u) << 3);
+    return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+// One wave per row: amax, the binary32 scale, then every element's code.
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t *x, int64_t rows,
+                                                            int d, uint8_t *codes, float *scale)
+{
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave_id();
+    if (r >= rows) return;
+    const int l = lane_id();
+    const int per = d / kWave; // 1 or 2 elements per lane
+    float v[2] = {0.0f, 0.0f};
+    if (per == 2) {
+        const uint32_t p = *reinterpret_cast<const uint32_t *>(x + r * d + 2 * l);
+        v[0] = __uint_as_float(p << 16);
+        v[1] = __uint_as_float(p & 0xffff0000u);
+    } else {
+        v[0] = __uint_as_float((uint32_t)x[r * d + l] << 16);
+    }
+    const float amax = wave_max(fmaxf(fabsf(v[0]), fabsf(v[1])));
+    const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    if (l == 0) scale[r] = s;
+    if (per == 2) {
+        const uint32_t c0 = f32_to_e4m3_sat(__fdiv_rn(v[0], s));
+        const uint32_t c1 = f32_to_e4m3_sat(__fdiv_rn(v[1], s));
+        *reinterpret_cast<uint16_t *>(codes + r * d + 2 * l) = (uint16_t)(c0 | (c1 << 8));
+    } else {
+        codes[r * d + l] = (uint8_t)f32_to_e4m3_sat(__fdiv_rn(v[0], s));
+    }
+}
+
+} // namespace
+
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int d, uint8_t *codes,
+                                float *scale, hipStream_t stream)
+{
+    if (rows == 0) return hipSuccess;
+    if (d != 64 && d != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                       stream, x, rows, d, codes, scale);
+    return hipGetLastError();
 }
 
 hipError_t launch_scores(const ScoreArgs &a, hipStream_t stream) { return dispatch(a, stream, false); }

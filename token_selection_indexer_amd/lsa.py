@@ -26,7 +26,8 @@ STATUS = {0: "LSA_OK", 1: "LSA_ERR_NULL_POINTER", 2: "LSA_ERR_BAD_SHAPE", 3: "LS
           4: "LSA_ERR_UNSUPPORTED", 5: "LSA_ERR_WORKSPACE_TOO_SMALL", 6: "LSA_ERR_DEVICE"}
 EXPORTS = ("lsa_index_scores", "lsa_topk_select", "lsa_page_summary", "lsa_page_recall",
            "lsa_sparse_attn", "lsa_workspace_bytes", "lsa_status_string",
-           "lsa_topk_select_noalloc", "lsa_index_select")
+           "lsa_topk_select_noalloc", "lsa_index_select", "lsa_quantize_queries",
+           "lsa_index_scores_q8")
 
 
 class IndexShape(ctypes.Structure):
@@ -70,6 +71,8 @@ def lib():
         L.lsa_topk_select.argtypes = [ip, bud, _VP, _I64, _VP, _VP, _VP, _SZ, _VP]
         L.lsa_topk_select_noalloc.argtypes = [ip, bud, _VP, _I64, _VP, _VP, _VP]
         L.lsa_index_select.argtypes = [ip, bud, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]
+        L.lsa_quantize_queries.argtypes = [ip, _VP, _VP, _VP, _VP]
+        L.lsa_index_scores_q8.argtypes = [ip, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]
         L.lsa_page_summary.argtypes = [ip, _I32, _VP, _I32, _VP, _I64, _I64, _VP, _VP]
         L.lsa_page_recall.argtypes = [ip, bud, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
                                       _VP, _VP, _SZ, _VP]
@@ -78,7 +81,7 @@ def lib():
         L.lsa_workspace_bytes.restype = _SZ
         L.lsa_status_string.argtypes = [_I32]
         L.lsa_status_string.restype = ctypes.c_char_p
-        for f in EXPORTS[:5] + ("lsa_topk_select_noalloc", "lsa_index_select"):
+        for f in EXPORTS[:5] + EXPORTS[7:]:
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -112,6 +115,18 @@ def lsa_topk_select(shape: IndexShape, budget: Budget, scores, n_cand: int, cand
     _check("lsa_topk_select", lib().lsa_topk_select(
         ctypes.byref(shape), budget, _p(scores), n_cand, _p(cand_ids), _p(idx), _p(ws),
         ws_bytes, _s(stream)))
+
+
+def lsa_quantize_queries(shape: IndexShape, q, q8, q_scale, stream=None):
+    _check("lsa_quantize_queries", lib().lsa_quantize_queries(
+        ctypes.byref(shape), _p(q), _p(q8), _p(q_scale), _s(stream)))
+
+
+def lsa_index_scores_q8(shape: IndexShape, q8, q_scale, w, keys, key_dtype: int, key_scale,
+                        scores, stream=None):
+    _check("lsa_index_scores_q8", lib().lsa_index_scores_q8(
+        ctypes.byref(shape), _p(q8), _p(q_scale), _p(w), _p(keys), key_dtype, _p(key_scale),
+        _p(scores), _s(stream)))
 
 
 def lsa_index_select(shape: IndexShape, budget: Budget, q, w, keys, key_dtype: int, key_scale,
@@ -259,6 +274,35 @@ def index_scores(q, w, keys, key_scale=None, q_pos0=None, out=None, stream=None,
     shape = index_shape(q, keys, q_pos0, seq_lens, seq_pos0)
     out = _out(out, "out", (shape.batch, shape.n_q, shape.kv_len), torch.float32, q.device)
     lsa_index_scores(shape, q, w, keys, kd, ks, out, stream)
+    return out
+
+
+def quantize_queries(q, q8=None, q_scale=None, stream=None):
+    """(q8 [B, n_q, H, d] uint8 e4m3 codes, q_scale [B, n_q, H] fp32) from bf16 q."""
+    _need(q, "q", torch.bfloat16, 4)
+    B, T, H, d = q.shape
+    q8 = _out(q8, "q8", (B, T, H, d), torch.uint8, q.device)
+    q_scale = _out(q_scale, "q_scale", (B, T, H), torch.float32, q.device)
+    lsa_quantize_queries(IndexShape(B, T, H, d, 1, 0), q, q8, q_scale, stream)
+    return q8, q_scale
+
+
+def index_scores_q8(q8, q_scale, w, keys, key_scale, q_pos0=None, out=None, stream=None,
+                    seq_lens=None, seq_pos0=None):
+    """scores [B, n_q, L] fp32 of fp8 queries (quantize_queries) against fp8 keys."""
+    _need(q8, "q8", torch.uint8, 4)
+    B, T, H, d = q8.shape
+    _need(q_scale, "q_scale", torch.float32, shape=(B, T, H), device=q8.device)
+    _need(w, "w", torch.float32, shape=(B, T, H), device=q8.device)
+    _need(keys, "keys", (torch.uint8, torch.float8_e4m3fn), dim=3, device=q8.device)
+    if keys.shape[0] != B or keys.shape[2] != d:
+        raise ValueError(f"keys {tuple(keys.shape)} do not match q8 {tuple(q8.shape)}")
+    kd, ks = _key_args(keys, key_scale)
+    L = keys.shape[1]
+    shape = _ragged(IndexShape(B, T, H, d, L, L - T if q_pos0 is None else q_pos0), q8.device,
+                    seq_lens, seq_pos0)
+    out = _out(out, "out", (B, T, L), torch.float32, q8.device)
+    lsa_index_scores_q8(shape, q8, q_scale, w, keys, kd, ks, out, stream)
     return out
 
 
