@@ -268,9 +268,13 @@ LSA_API lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budg
  * lse = -inf.  Cross-Layer Indexing (paper summary page, strategy (2)): call once per layer with
  * that layer's q / cache and the same idx.
  *   shape   uses batch, n_q, kv_len and seq_len (ids at or past a sequence's length are skipped)
- *   budget  sink/window say idx[.., 0:S] and idx[.., S:S+W] are contiguous runs (the layout
- *           lsa_topk_select writes when V > k); rows whose first entry is not 0 or whose
- *           runs are not contiguous fall back to a plain gather.  {0,0,0} = always gather.
+ *   budget  k = entries per idx row.  sink / window describe the layout lsa_topk_select
+ *           writes (idx[.., 0:S] and idx[.., S:S+W] are runs of consecutive tokens when V > k)
+ *           but change nothing in the computation: every entry is gathered by its id.  A
+ *           latent row is one contiguous d_qk * 2-byte run in HBM that the kernel loads in
+ *           whole 16-byte pieces, so the consecutive rows of the sink and window runs already
+ *           arrive as one contiguous span and need no path of their own.  Checked:
+ *           0 <= sink, 0 <= window, sink + window <= k.
  *   q       [B, n_q, Hq, d_qk] bf16
  *   k, v    [B, L, row_stride] bf16 (latent: v == k)
  *   idx     [B, n_q, k] int32
