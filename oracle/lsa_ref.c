@@ -520,3 +520,275 @@ void lsa_ref_sparse_attn(int64_t n_rows, int Hq, int d_qk, int d_v, int k, const
         }
     }
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* f4. Backward of the sparse attention and of the indexer scores (the training path).         */
+/* ------------------------------------------------------------------------------------------ */
+
+/*
+ * [LSA] abstract: LSA trains natively (to one million tokens), so the attention over the
+ * selected tokens and the indexer's scores both carry gradients.  The pages print no backward
+ * pass; the functions below are the derivatives of the forward definitions above, written out,
+ * on binary64 inputs (bf16 and e4m3 values convert exactly; callers pass the converted arrays).
+ * Their pins are central finite differences of the forward functions on binary64 inputs
+ * (lsa_ref_sparse_attn_f64, lsa_ref_index_scores_sel_f64), so that they are checked against the
+ * forward definitions and not against a second copy of themselves.
+ */
+
+/* For every key row r in [0, n_keys), the entries (t, j) of an index list with idx[t][j] == r,
+ * in increasing (t, j) order: CSR arrays start[n_keys + 1] and ent[] (ent = t * k + j). */
+static void invert_idx(int64_t n_rows, int k, const int32_t *idx, int64_t n_keys, int64_t **start,
+                       int64_t **ent)
+{
+    int64_t *st = (int64_t *)calloc((size_t)n_keys + 1, sizeof(int64_t));
+    for (int64_t e = 0; e < n_rows * k; ++e)
+        if (idx[e] >= 0 && idx[e] < n_keys) ++st[idx[e] + 1];
+    for (int64_t r = 0; r < n_keys; ++r) st[r + 1] += st[r];
+    int64_t *fill = (int64_t *)malloc(sizeof(int64_t) * ((size_t)n_keys + 1));
+    memcpy(fill, st, sizeof(int64_t) * ((size_t)n_keys + 1));
+    int64_t *en = (int64_t *)malloc(sizeof(int64_t) * ((size_t)st[n_keys] + 1));
+    for (int64_t e = 0; e < n_rows * k; ++e)
+        if (idx[e] >= 0 && idx[e] < n_keys) en[fill[idx[e]]++] = e;
+    free(fill);
+    *start = st;
+    *ent = en;
+}
+
+/*
+ * The sparse attention of lsa_ref_sparse_attn on binary64 inputs, with entries outside
+ * [0, n_keys) skipped: q [n_rows][Hq][d_qk], K rows k_stride apart, V rows v_stride apart.
+ */
+void lsa_ref_sparse_attn_f64(int64_t n_rows, int Hq, int d_qk, int d_v, int k, const double *q,
+                             const double *K, int64_t k_stride, const double *V, int64_t v_stride,
+                             const int32_t *idx, int64_t n_keys, double tau, double *o,
+                             double *lse)
+{
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int64_t t = 0; t < n_rows; ++t) {
+        for (int h = 0; h < Hq; ++h) {
+            const int32_t *sel = idx + t * k;
+            const double *qh = q + (t * Hq + h) * d_qk;
+            double *oh = o + (t * Hq + h) * d_v;
+            double *logit = (double *)malloc(sizeof(double) * (size_t)k);
+            double mx = -INFINITY;
+            for (int j = 0; j < k; ++j) {
+                if (sel[j] < 0 || sel[j] >= n_keys) continue;
+                const double *kr = K + (int64_t)sel[j] * k_stride;
+                double dot = 0.0;
+                for (int i = 0; i < d_qk; ++i) dot += qh[i] * kr[i];
+                logit[j] = tau * dot;
+                if (logit[j] > mx) mx = logit[j];
+            }
+            for (int c = 0; c < d_v; ++c) oh[c] = 0.0;
+            if (mx == -INFINITY) {
+                if (lse) lse[t * Hq + h] = -INFINITY;
+                free(logit);
+                continue;
+            }
+            double den = 0.0;
+            for (int j = 0; j < k; ++j) {
+                if (sel[j] < 0 || sel[j] >= n_keys) continue;
+                const double e = exp(logit[j] - mx);
+                den += e;
+                const double *vr = V + (int64_t)sel[j] * v_stride;
+                for (int c = 0; c < d_v; ++c) oh[c] += e * vr[c];
+            }
+            for (int c = 0; c < d_v; ++c) oh[c] /= den;
+            if (lse) lse[t * Hq + h] = mx + log(den);
+            free(logit);
+        }
+    }
+}
+
+/*
+ * Gradients of the sparse attention.  With P_j = softmax(logit)_j over the valid entries j of
+ * idx[t] (logit_j = tau q[t,h] . K[idx_j]) and the output gradient g = dLoss/do[t,h]:
+ *   dP_j = g . V[idx_j]
+ *   dS_j = P_j (dP_j - sum_i P_i dP_i)           (the softmax Jacobian applied to dP)
+ *   dq[t,h]      = tau sum_j dS_j K[idx_j]
+ *   dK[idx_j]   += tau dS_j q[t,h]               (over every row t and head h that selected it)
+ *   dV[idx_j]   += P_j g
+ * dq [n_rows][Hq][d_qk] is written; dK [n_keys][d_qk] and dV [n_keys][d_v] are written too
+ * (rows nobody selected get 0).  A latent cache, whose rows serve as K and as V, has the
+ * gradient dK[r][c] + (c < d_v ? dV[r][c] : 0) on row r.  The forward is recomputed in fp64.
+ * Pass 1 handles one (t, h) at a time (dq); pass 2 one key row at a time, over the entries
+ * that selected it in increasing order (dK, dV).
+ */
+void lsa_ref_sparse_attn_backward(int64_t n_rows, int Hq, int d_qk, int d_v, int k,
+                                  const double *q, const double *K, int64_t k_stride,
+                                  const double *V, int64_t v_stride, const int32_t *idx,
+                                  int64_t n_keys, double tau, const double *g, double *dq,
+                                  double *dK, double *dV)
+{
+    double *lse = (double *)malloc(sizeof(double) * (size_t)(n_rows * Hq + 1));
+    double *D = (double *)malloc(sizeof(double) * (size_t)(n_rows * Hq + 1));
+    /* pass 1: lse, D = sum_j P_j dP_j, dq */
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int64_t t = 0; t < n_rows; ++t) {
+        for (int h = 0; h < Hq; ++h) {
+            const int32_t *sel = idx + t * k;
+            const double *qh = q + (t * Hq + h) * d_qk;
+            const double *gh = g + (t * Hq + h) * d_v;
+            double *dqh = dq + (t * Hq + h) * d_qk;
+            double *logit = (double *)malloc(sizeof(double) * (size_t)k);
+            double *dP = (double *)malloc(sizeof(double) * (size_t)k);
+            double mx = -INFINITY;
+            for (int j = 0; j < k; ++j) {
+                if (sel[j] < 0 || sel[j] >= n_keys) continue;
+                const double *kr = K + (int64_t)sel[j] * k_stride;
+                const double *vr = V + (int64_t)sel[j] * v_stride;
+                double dot = 0.0, gv = 0.0;
+                for (int i = 0; i < d_qk; ++i) dot += qh[i] * kr[i];
+                for (int c = 0; c < d_v; ++c) gv += gh[c] * vr[c];
+                logit[j] = tau * dot;
+                dP[j] = gv;
+                if (logit[j] > mx) mx = logit[j];
+            }
+            for (int i = 0; i < d_qk; ++i) dqh[i] = 0.0;
+            double den = 0.0, pdp = 0.0;
+            if (mx != -INFINITY) {
+                for (int j = 0; j < k; ++j)
+                    if (sel[j] >= 0 && sel[j] < n_keys) den += exp(logit[j] - mx);
+                const double ls = mx + log(den);
+                for (int j = 0; j < k; ++j)
+                    if (sel[j] >= 0 && sel[j] < n_keys) pdp += exp(logit[j] - ls) * dP[j];
+                for (int j = 0; j < k; ++j) {
+                    if (sel[j] < 0 || sel[j] >= n_keys) continue;
+                    const double dS = exp(logit[j] - ls) * (dP[j] - pdp);
+                    const double *kr = K + (int64_t)sel[j] * k_stride;
+                    for (int i = 0; i < d_qk; ++i) dqh[i] += tau * dS * kr[i];
+                }
+                lse[t * Hq + h] = ls;
+            } else {
+                lse[t * Hq + h] = -INFINITY;
+            }
+            D[t * Hq + h] = pdp;
+            free(logit);
+            free(dP);
+        }
+    }
+    /* pass 2: dK, dV per key row */
+    int64_t *start, *ent;
+    invert_idx(n_rows, k, idx, n_keys, &start, &ent);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t r = 0; r < n_keys; ++r) {
+        double *dk = dK + r * d_qk;
+        double *dv = dV + r * d_v;
+        for (int i = 0; i < d_qk; ++i) dk[i] = 0.0;
+        for (int c = 0; c < d_v; ++c) dv[c] = 0.0;
+        const double *kr = K + r * k_stride;
+        const double *vr = V + r * v_stride;
+        for (int64_t e = start[r]; e < start[r + 1]; ++e) {
+            const int64_t t = ent[e] / k;
+            for (int h = 0; h < Hq; ++h) {
+                const double *qh = q + (t * Hq + h) * d_qk;
+                const double *gh = g + (t * Hq + h) * d_v;
+                double dot = 0.0, gv = 0.0;
+                for (int i = 0; i < d_qk; ++i) dot += qh[i] * kr[i];
+                for (int c = 0; c < d_v; ++c) gv += gh[c] * vr[c];
+                const double P = exp(tau * dot - lse[t * Hq + h]);
+                const double dS = P * (gv - D[t * Hq + h]);
+                for (int i = 0; i < d_qk; ++i) dk[i] += tau * dS * qh[i];
+                for (int c = 0; c < d_v; ++c) dv[c] += P * gh[c];
+            }
+        }
+    }
+    free(start);
+    free(ent);
+    free(lse);
+    free(D);
+}
+
+/*
+ * The indexer scores of lsa_ref_index_scores at the selected entries only, on binary64 inputs:
+ *   I[t][j] = sum_h w[t,h] ReLU(q[t,h] . keys[idx[t][j]])   for 0 <= idx[t][j] < V_t,
+ * V_t = min(n_keys, pos_t + 1); other entries get 0 (they carry no score).
+ */
+void lsa_ref_index_scores_sel_f64(int64_t n_rows, int H, int d, int k, const int64_t *pos,
+                                  const double *q, const double *w, const double *keys,
+                                  const int32_t *idx, int64_t n_keys, double *I)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < n_rows; ++t) {
+        const int64_t V = pos[t] + 1 < n_keys ? pos[t] + 1 : n_keys;
+        for (int j = 0; j < k; ++j) {
+            const int32_t s = idx[t * k + j];
+            double acc = 0.0;
+            if (s >= 0 && s < V) {
+                for (int h = 0; h < H; ++h) {
+                    double dot = 0.0;
+                    for (int i = 0; i < d; ++i) dot += q[(t * H + h) * d + i] * keys[(int64_t)s * d + i];
+                    acc += w[t * H + h] * (dot > 0.0 ? dot : 0.0);
+                }
+            }
+            I[t * k + j] = acc;
+        }
+    }
+}
+
+/*
+ * Gradients of the indexer scores at the selected entries, given gI[t][j] = dLoss/dI[t][j]
+ * (entries outside [0, V_t) carry none), with ReLU'(0) taken as 0:
+ *   dw[t,h]   = sum_j gI[t,j] ReLU(q[t,h] . keys[s_j])
+ *   dq[t,h]   = sum_j gI[t,j] w[t,h] [q[t,h] . keys[s_j] > 0] keys[s_j]
+ *   dk[s]     = sum over entries (t, j) with s_j = s of sum_h gI[t,j] w[t,h] [q[t,h] . keys[s] > 0] q[t,h]
+ * dq [n_rows][H][d], dw [n_rows][H] and dk [n_keys][d] are written (rows nobody selected get 0).
+ */
+void lsa_ref_index_scores_backward(int64_t n_rows, int H, int d, int k, const int64_t *pos,
+                                   const double *q, const double *w, const double *keys,
+                                   const int32_t *idx, int64_t n_keys, const double *gI,
+                                   double *dq, double *dw, double *dk)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < n_rows; ++t) {
+        const int64_t V = pos[t] + 1 < n_keys ? pos[t] + 1 : n_keys;
+        for (int h = 0; h < H; ++h) {
+            const double *qh = q + (t * H + h) * d;
+            double *dqh = dq + (t * H + h) * d;
+            double dwh = 0.0;
+            for (int i = 0; i < d; ++i) dqh[i] = 0.0;
+            for (int j = 0; j < k; ++j) {
+                const int32_t s = idx[t * k + j];
+                if (s < 0 || s >= V) continue;
+                const double *kr = keys + (int64_t)s * d;
+                double dot = 0.0;
+                for (int i = 0; i < d; ++i) dot += qh[i] * kr[i];
+                if (dot > 0.0) {
+                    dwh += gI[t * k + j] * dot;
+                    for (int i = 0; i < d; ++i) dqh[i] += gI[t * k + j] * w[t * H + h] * kr[i];
+                }
+            }
+            dw[t * H + h] = dwh;
+        }
+    }
+    /* the entries outside [0, V_t) are dropped before the inversion */
+    int32_t *vidx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n_rows * k + 1));
+    for (int64_t t = 0; t < n_rows; ++t) {
+        const int64_t V = pos[t] + 1 < n_keys ? pos[t] + 1 : n_keys;
+        for (int j = 0; j < k; ++j) {
+            const int32_t s = idx[t * k + j];
+            vidx[t * k + j] = (s >= 0 && s < V) ? s : -1;
+        }
+    }
+    int64_t *start, *ent;
+    invert_idx(n_rows, k, vidx, n_keys, &start, &ent);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t r = 0; r < n_keys; ++r) {
+        double *dkr = dk + r * d;
+        for (int i = 0; i < d; ++i) dkr[i] = 0.0;
+        const double *kr = keys + r * d;
+        for (int64_t e = start[r]; e < start[r + 1]; ++e) {
+            const int64_t t = ent[e] / k;
+            for (int h = 0; h < H; ++h) {
+                const double *qh = q + (t * H + h) * d;
+                double dot = 0.0;
+                for (int i = 0; i < d; ++i) dot += qh[i] * kr[i];
+                if (dot > 0.0)
+                    for (int i = 0; i < d; ++i) dkr[i] += gI[ent[e]] * w[t * H + h] * qh[i];
+            }
+        }
+    }
+    free(start);
+    free(ent);
+    free(vidx);
+}

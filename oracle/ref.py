@@ -52,6 +52,15 @@ def lib():
                                           _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]
         L.lsa_ref_sparse_attn.argtypes = [_I64, _I32, _I32, _I32, _I32, _P, _P, _I64, _P, _I64,
                                           _P, ctypes.c_double, _P, _P]
+        L.lsa_ref_sparse_attn_f64.argtypes = [_I64, _I32, _I32, _I32, _I32, _P, _P, _I64, _P,
+                                              _I64, _P, _I64, ctypes.c_double, _P, _P]
+        L.lsa_ref_sparse_attn_backward.argtypes = [_I64, _I32, _I32, _I32, _I32, _P, _P, _I64, _P,
+                                                   _I64, _P, _I64, ctypes.c_double, _P, _P, _P,
+                                                   _P]
+        L.lsa_ref_index_scores_sel_f64.argtypes = [_I64, _I32, _I32, _I32, _P, _P, _P, _P, _P,
+                                                   _I64, _P]
+        L.lsa_ref_index_scores_backward.argtypes = [_I64, _I32, _I32, _I32, _P, _P, _P, _P, _P,
+                                                    _I64, _P, _P, _P, _P]
         _lib = L
     return _lib
 
@@ -215,6 +224,92 @@ def sparse_attn(q, kmat, vmat, idx, tau, d_qk=None, d_v=None):
 def cross_layer_attn(layers, idx, tau, d_qk=None, d_v=None):
     """Cross-Layer Indexing: every layer (q, kmat, vmat) attends over the same idx."""
     return [sparse_attn(q, km, vm, idx, tau, d_qk, d_v) for (q, km, vm) in layers]
+
+
+# --------------------------------------------------------------------------------- f4 backward
+def sparse_attn_f64(q, kmat, vmat, idx, tau, d_qk=None, d_v=None):
+    """The sparse attention on float64 inputs: q [T,Hq,d_qk]; kmat [L,ks] (first d_qk columns
+    are K); vmat [L,vs] (first d_v columns are V, may be kmat); idx int32 [T,k], entries outside
+    [0, L) skipped -> (o [T,Hq,d_v], lse [T,Hq])."""
+    q = _c(q, np.float64)
+    T, Hq, dq = q.shape
+    d_qk = dq if d_qk is None else d_qk
+    kmat = _c(kmat, np.float64)
+    vmat = kmat if vmat is None else _c(vmat, np.float64)
+    d_v = vmat.shape[1] if d_v is None else d_v
+    idx = _c(idx, np.int32)
+    k = idx.shape[1]
+    o = np.empty((T, Hq, d_v), np.float64)
+    lse = np.empty((T, Hq), np.float64)
+    lib().lsa_ref_sparse_attn_f64(T, Hq, d_qk, d_v, k, _ptr(q), _ptr(kmat), kmat.shape[1],
+                                  _ptr(vmat), vmat.shape[1], _ptr(idx), kmat.shape[0], float(tau),
+                                  _ptr(o), _ptr(lse))
+    return o, lse
+
+
+def sparse_attn_backward(q, kmat, vmat, idx, tau, g, d_qk=None, d_v=None):
+    """Gradients of sparse_attn_f64 for the output gradient g [T,Hq,d_v] ->
+    (dq [T,Hq,d_qk], dK [L,d_qk], dV [L,d_v]) in float64.  A latent cache (vmat is kmat) has
+    the row gradient dK + dV (dV on the first d_v columns)."""
+    q = _c(q, np.float64)
+    T, Hq, dq_ = q.shape
+    d_qk = dq_ if d_qk is None else d_qk
+    kmat = _c(kmat, np.float64)
+    vmat = kmat if vmat is None else _c(vmat, np.float64)
+    d_v = vmat.shape[1] if d_v is None else d_v
+    idx = _c(idx, np.int32)
+    k = idx.shape[1]
+    g = _c(g, np.float64)
+    assert g.shape == (T, Hq, d_v)
+    L = kmat.shape[0]
+    dq = np.empty((T, Hq, d_qk), np.float64)
+    dK = np.empty((L, d_qk), np.float64)
+    dV = np.empty((L, d_v), np.float64)
+    lib().lsa_ref_sparse_attn_backward(T, Hq, d_qk, d_v, k, _ptr(q), _ptr(kmat), kmat.shape[1],
+                                       _ptr(vmat), vmat.shape[1], _ptr(idx), L, float(tau), _ptr(g),
+                                       _ptr(dq), _ptr(dK), _ptr(dV))
+    return dq, dK, dV
+
+
+def index_scores_sel_f64(q, w, keys, idx, pos):
+    """Indexer scores at the selected entries on float64 inputs: q [T,H,d], w [T,H], keys
+    [L,d], idx int32 [T,k], pos int64 [T] -> I [T,k] (0 where the entry is not in [0, V_t))."""
+    q = _c(q, np.float64)
+    T, H, d = q.shape
+    w = _c(w, np.float64)
+    keys = _c(keys, np.float64)
+    idx = _c(idx, np.int32)
+    pos = _c(pos, np.int64)
+    k = idx.shape[1]
+    I = np.empty((T, k), np.float64)
+    lib().lsa_ref_index_scores_sel_f64(T, H, d, k, _ptr(pos), _ptr(q), _ptr(w), _ptr(keys),
+                                       _ptr(idx), keys.shape[0], _ptr(I))
+    return I
+
+
+def index_scores_backward(q, w, keys, idx, pos, gI):
+    """Gradients of index_scores_sel_f64 for gI [T,k] -> (dq [T,H,d], dw [T,H], dk [L,d])."""
+    q = _c(q, np.float64)
+    T, H, d = q.shape
+    w = _c(w, np.float64)
+    keys = _c(keys, np.float64)
+    idx = _c(idx, np.int32)
+    pos = _c(pos, np.int64)
+    gI = _c(gI, np.float64)
+    k = idx.shape[1]
+    L = keys.shape[0]
+    dq = np.empty((T, H, d), np.float64)
+    dw = np.empty((T, H), np.float64)
+    dk = np.empty((L, d), np.float64)
+    lib().lsa_ref_index_scores_backward(T, H, d, k, _ptr(pos), _ptr(q), _ptr(w), _ptr(keys),
+                                        _ptr(idx), L, _ptr(gI), _ptr(dq), _ptr(dw), _ptr(dk))
+    return dq, dw, dk
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """uint16 bf16 bit patterns -> float64 (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 # --------------------------------------------------------------------------------- helpers
