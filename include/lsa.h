@@ -8,6 +8,8 @@
  *   4. lsa_page_recall   -- Hierarchical Indexing: coarse page recall, fine scores in the pages
  *   5. lsa_sparse_attn   -- attention over the selected tokens (MLA latent cache or MHA),
  *                           reusable by several layers with one index list (Cross-Layer Indexing)
+ *   6. lsa_sparse_attn_backward, lsa_index_scores_backward -- the gradients of 5 and of the
+ *                           indexer scores at the selected entries (the training path)
  *
  * Sources.  "LongCat Sparse Attention: Taming the Lightning via Streaming-aware Hierarchical
  * Cross-Layer Indexing" (paper summary page: abstract, key contributions, limitations); the
@@ -32,7 +34,8 @@
  *   Validity   Query i of a sequence sits at absolute position q_pos0 + i and sees the keys
  *              [0, V_i), V_i = min(kv_len, q_pos0 + i + 1).  Decode: n_q = 1, q_pos0 = kv_len-1.
  *   Order      Selections are deterministic: ties in score go to the lower token index (-0 and
- *              +0 are equal).  Identical calls give bitwise-identical outputs.
+ *              +0 are equal).  Identical calls give bitwise-identical outputs, except the
+ *              gradients of the backward entry points (fp32 atomic sums).
  */
 #ifndef LSA_H
 #define LSA_H
@@ -288,6 +291,57 @@ LSA_API lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_
                            lsa_budget budget, const void *q, const void *k, const void *v,
                            const int32_t *idx, void *out, float *lse, void *ws, size_t ws_bytes,
                            void *stream);
+
+/*
+ * lsa_sparse_attn_backward -- gradients of lsa_sparse_attn (the training path: the paper summary
+ * page's abstract reports native training to one million tokens).  For query i, head h and the
+ * valid entries j of idx[b,i,:] (the entries lsa_sparse_attn uses), with
+ * P_j = exp(scale q . K_j - lse) the forward's attention weights:
+ *     dP_j = d_out[b,i,h,:] . V_j,   D = d_out[b,i,h,:] . out[b,i,h,:],   dS_j = P_j (dP_j - D)
+ *     d_q[b,i,h,:]      += scale sum_j dS_j K_j
+ *     d_k[b, idx_j, :]  += scale dS_j q[b,i,h,:]      (d_qk columns)
+ *     d_v[b, idx_j, :]  += P_j d_out[b,i,h,:]         (d_v columns)
+ * D uses the forward output (the P-weighted sum of dP equals d_out . out in exact arithmetic).
+ * The gradients are ADDED into (fp32; zero them first for plain gradients): layers that share
+ * a cache, or the chunks of a chunked prefill, accumulate.  A latent cache (attn->latent) has
+ * one gradient array: pass d_v == d_k; its rows get dK + dV (dV on the first d_v columns).  A
+ * non-latent call needs d_v != d_k.  The additions are fp32 atomics, so the order of the
+ * partial sums (and the last bits) can differ between runs.
+ *   shape, attn, budget, q, k, v, idx   as for lsa_sparse_attn (budget: k entries per row)
+ *   out     [B, n_q, Hq, d_v] bf16, 16-byte aligned;  lse  [B, n_q, Hq] fp32 (required)
+ *   d_out   [B, n_q, Hq, d_v] bf16, 16-byte aligned
+ *   d_q     [B, n_q, Hq, d_qk] fp32
+ *   d_k     [B, L, d_qk] fp32 (dense rows);  d_v  [B, L, d_v] fp32 (latent: == d_k)
+ * Limits: as lsa_sparse_attn.  No workspace.
+ */
+LSA_API lsa_status lsa_sparse_attn_backward(const lsa_index_shape *shape, const lsa_attn_shape *attn,
+                                            lsa_budget budget, const void *q, const void *k,
+                                            const void *v, const int32_t *idx, const void *out,
+                                            const float *lse, const void *d_out, float *d_q,
+                                            float *d_k, float *d_v, void *stream);
+
+/*
+ * lsa_index_scores_backward -- gradients of the indexer scores at the selected entries (the
+ * training path of the Lightning Indexer, Baidu Cloud article, "1. Lightweight Scoring
+ * Module").  Given d_scores[b,t,j], the gradient of the score of query t at its entry
+ * s_j = idx[b,t,j] (entries outside [0, V_t) carry none), with ReLU'(0) = 0 and
+ * G_jh = d_scores[b,t,j] w[b,t,h] [q[b,t,h] . keys[b,s_j] > 0]:
+ *     d_w[b,t,h]      += sum_j d_scores[b,t,j] ReLU(q[b,t,h] . keys[b,s_j])
+ *     d_q[b,t,h,:]    += sum_j G_jh keys[b,s_j,:]
+ *     d_keys[b,s_j,:] += sum_h G_jh q[b,t,h,:]
+ * (the dot products in fp32 from the bf16 inputs).  bf16 keys only: the 8-bit key format is an
+ * inference-side encoding.  The gradients are ADDED into (fp32; zero them first), with fp32
+ * atomics (summation order, and the last bits, can differ between runs).
+ *   shape     as for lsa_index_scores (n_heads H <= 64, head_dim 64 or 128, ragged arrays allowed)
+ *   k         entries per idx row
+ *   q [B, n_q, H, d] bf16, 16-byte aligned;  w [B, n_q, H] fp32;  keys [B, L, d] bf16, 16-byte aligned
+ *   idx [B, n_q, k] int32;  d_scores [B, n_q, k] fp32
+ *   d_q [B, n_q, H, d] fp32;  d_w [B, n_q, H] fp32;  d_keys [B, L, d] fp32
+ */
+LSA_API lsa_status lsa_index_scores_backward(const lsa_index_shape *shape, int32_t k, const void *q,
+                                             const float *w, const void *keys, const int32_t *idx,
+                                             const float *d_scores, float *d_q, float *d_w,
+                                             float *d_keys, void *stream);
 
 enum { LSA_OP_TOPK_SELECT = 1, LSA_OP_PAGE_RECALL = 2, LSA_OP_SPARSE_ATTN = 3,
        LSA_OP_INDEX_SELECT = 4 };

@@ -281,3 +281,36 @@ def test_q8_entry_points_reject(L):
                                  lsa.KEY_FP8_E4M3, v(FAKE), v(FAKE), None) == 2
     assert L.lsa_quantize_queries(ctypes.byref(_shape(d=96)), v(FAKE), v(FAKE), v(FAKE), None) == 4
     assert L.lsa_quantize_queries(ctypes.byref(_shape()), None, v(FAKE), v(FAKE), None) == 1
+
+
+def test_backward_entry_points_reject(L):
+    """The training-path calls validate like the forward ones: a latent cache has one gradient
+    array, a non-latent one two; the indexer backward takes up to 64 heads of width 64 or 128."""
+    v = ctypes.c_void_p
+    sh = _shape(B=4)
+    b = lsa.Budget(2048, 0, 0)
+    mla = lsa.AttnShape(16, 576, 512, 1, 576, 576, 0.04)
+    mha = lsa.AttnShape(1, 128, 128, 0, 128, 128, 0.1)
+
+    def attn_call(attn, k=FAKE, vv=FAKE, dk=FAKE + 8192, dv=FAKE + 8192, lse=FAKE, dout=FAKE):
+        return L.lsa_sparse_attn_backward(ctypes.byref(sh), ctypes.byref(attn), b, v(FAKE), v(k),
+                                          v(vv), v(FAKE), v(FAKE), v(lse) if lse else None,
+                                          v(dout) if dout else None, v(FAKE), v(dk), v(dv), None)
+    assert attn_call(mla, dv=FAKE + 16384) == 2          # latent: one gradient array
+    assert attn_call(mla, vv=FAKE + 4096) == 2           # latent: v must be k
+    assert attn_call(mha) == 2                           # per-head: separate dK and dV
+    assert attn_call(mla, lse=0) == 1                    # the forward's lse is required
+    assert attn_call(mla, dout=0) == 1
+    assert attn_call(mla, dk=FAKE + 2, dv=FAKE + 2) == 2  # fp32 alignment
+    assert attn_call(lsa.AttnShape(8, 576, 512, 1, 576, 576, 0.04)) == 4
+
+    def idx_call(shape, k=2048, q=FAKE, keys=FAKE, dsc=FAKE):
+        return L.lsa_index_scores_backward(ctypes.byref(shape), k, v(q) if q else None, v(FAKE),
+                                           v(keys), v(FAKE), v(dsc) if dsc else None, v(FAKE),
+                                           v(FAKE), v(FAKE), None)
+    assert idx_call(_shape(H=128)) == 4                  # at most 64 heads
+    assert idx_call(_shape(d=96)) == 4                   # head_dim 64 or 128
+    assert idx_call(_shape(), k=0) == 2
+    assert idx_call(_shape(), q=0) == 1
+    assert idx_call(_shape(), dsc=0) == 1
+    assert idx_call(_shape(), keys=FAKE + 8) == 2        # 16-byte aligned keys

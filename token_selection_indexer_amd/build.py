@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblsa.so")
-SOURCES = ["api.hip", "score.hip", "topk.hip", "pages.hip", "attn.hip"]
+SOURCES = ["api.hip", "score.hip", "topk.hip", "pages.hip", "attn.hip", "attn_bwd.hip",
+           "index_bwd.hip"]
 ARCH = os.environ.get("LSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -28,7 +29,9 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
 # per-file extras: the scoring kernels keep their MFMA accumulators in VGPRs (their epilogue
 # reads every accumulator with VALU instructions; AGPR-resident results would each need a copy)
 # the page keys are defined with separately rounded multiplies and adds: no FMA contraction
-EXTRA = {"score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "pages.hip": ["-ffp-contract=off"]}
+# the backward kernels add their gradients with the hardware's fp32 atomics (device memory)
+EXTRA = {"score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "pages.hip": ["-ffp-contract=off"],
+         "attn_bwd.hip": ["-munsafe-fp-atomics"], "index_bwd.hip": ["-munsafe-fp-atomics"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

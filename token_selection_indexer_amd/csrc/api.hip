@@ -572,4 +572,95 @@ lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_shape *a
     return device_status(lsa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)));
 }
 
+
+lsa_status lsa_sparse_attn_backward(const lsa_index_shape *shape, const lsa_attn_shape *attn,
+                                    lsa_budget budget, const void *q, const void *k, const void *v,
+                                    const int32_t *idx, const void *out, const float *lse,
+                                    const void *d_out, float *d_q, float *d_k, float *d_v,
+                                    void *stream)
+{
+    lsa_status st = check_attn(shape, attn, budget);
+    if (st != LSA_OK) return st;
+    if (!q || !k || !v || !idx || !out || !lse || !d_out || !d_q || !d_k || !d_v)
+        return LSA_ERR_NULL_POINTER;
+    if (attn->latent && (v != k || d_v != d_k)) return LSA_ERR_BAD_SHAPE;
+    if (!attn->latent && d_v == d_k) return LSA_ERR_BAD_SHAPE;
+    if ((st = check_ragged(shape)) != LSA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(idx, 4) ||
+        !aligned(out, 16) || !aligned(lse, 4) || !aligned(d_out, 16) || !aligned(d_q, 4) ||
+        !aligned(d_k, 4) || !aligned(d_v, 4))
+        return LSA_ERR_BAD_SHAPE;
+    if (budget.sink < 0 || budget.window < 0 || (int64_t)budget.sink + budget.window > budget.k)
+        return LSA_ERR_BAD_SHAPE;
+    const int64_t rows = (int64_t)shape->batch * shape->n_q;
+    if (rows == 0) return LSA_OK;
+    if (rows * attn->n_heads >= (int64_t(1) << 31) * 4) return LSA_ERR_UNSUPPORTED;
+    lsa::AttnBwdArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.idx = idx;
+    a.out = static_cast<const uint16_t *>(out);
+    a.lse = lse;
+    a.dout = static_cast<const uint16_t *>(d_out);
+    a.dq = d_q;
+    a.dk = d_k;
+    a.dv = d_v;
+    a.batch = shape->batch;
+    a.n_q = shape->n_q;
+    a.heads = attn->n_heads;
+    a.d_qk = attn->d_qk;
+    a.d_v = attn->d_v;
+    a.n_idx = budget.k;
+    a.latent = attn->latent;
+    a.kv_len = shape->kv_len;
+    a.seq_len = shape->seq_len;
+    a.k_stride = attn->k_row_stride;
+    a.v_stride = attn->v_row_stride;
+    a.scale = attn->scale;
+    a.n_split = lsa::attn_bwd_splits(shape->batch, shape->n_q, attn->n_heads, budget.k, attn->latent);
+    return device_status(lsa::launch_sparse_attn_backward(a, static_cast<hipStream_t>(stream)));
+}
+
+lsa_status lsa_index_scores_backward(const lsa_index_shape *shape, int32_t k, const void *q,
+                                     const float *w, const void *keys, const int32_t *idx,
+                                     const float *d_scores, float *d_q, float *d_w, float *d_keys,
+                                     void *stream)
+{
+    if (!shape) return LSA_ERR_NULL_POINTER;
+    if (shape->batch < 0 || shape->n_q < 0 || shape->kv_len < 1 ||
+        shape->kv_len >= (int64_t(1) << 31) || shape->q_pos0 < 0 || shape->batch > kMaxGridYZ ||
+        shape->n_heads < 1 || shape->head_dim < 1 || k < 1)
+        return LSA_ERR_BAD_SHAPE;
+    if (!lsa::index_bwd_supported(shape->n_heads, shape->head_dim)) return LSA_ERR_UNSUPPORTED;
+    if (shape->n_q > kMaxGridYZ) return LSA_ERR_UNSUPPORTED;
+    lsa_status st = check_ragged(shape);
+    if (st != LSA_OK) return st;
+    if (!q || !w || !keys || !idx || !d_scores || !d_q || !d_w || !d_keys) return LSA_ERR_NULL_POINTER;
+    if (!aligned(q, 16) || !aligned(w, 4) || !aligned(keys, 16) || !aligned(idx, 4) ||
+        !aligned(d_scores, 4) || !aligned(d_q, 4) || !aligned(d_w, 4) || !aligned(d_keys, 4))
+        return LSA_ERR_BAD_SHAPE;
+    if ((int64_t)shape->batch * shape->n_q == 0) return LSA_OK;
+    lsa::IndexBwdArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.w = w;
+    a.keys = static_cast<const uint16_t *>(keys);
+    a.idx = idx;
+    a.dscore = d_scores;
+    a.dq = d_q;
+    a.dw = d_w;
+    a.dkeys = d_keys;
+    a.batch = shape->batch;
+    a.n_q = shape->n_q;
+    a.heads = shape->n_heads;
+    a.dim = shape->head_dim;
+    a.n_idx = k;
+    a.kv_len = shape->kv_len;
+    a.q_pos0 = shape->q_pos0;
+    a.seq_len = shape->seq_len;
+    a.seq_pos0 = shape->seq_pos0;
+    a.n_split = lsa::index_bwd_splits(shape->batch, shape->n_q, k);
+    return device_status(lsa::launch_index_scores_backward(a, static_cast<hipStream_t>(stream)));
+}
+
 } // extern "C"

@@ -111,6 +111,49 @@ struct AttnArgs {
 };
 
 int attn_splits(int batch, int n_q, int heads, int n_idx, int latent);
+
+// Backward of the sparse attention: the forward's operands plus its output and lse, the output
+// gradient, and three fp32 gradients that are added into (d_k == d_v for a latent cache).
+struct AttnBwdArgs {
+    const uint16_t *q;    // [B, n_q, Hq, d_qk]
+    const uint16_t *k;    // [B, L, k_stride]
+    const uint16_t *v;    // [B, L, v_stride]
+    const int32_t *idx;   // [B, n_q, n_idx]
+    const uint16_t *out;  // [B, n_q, Hq, d_v] forward output
+    const float *lse;     // [B, n_q, Hq] forward log-sum-exp (natural log)
+    const uint16_t *dout; // [B, n_q, Hq, d_v]
+    float *dq;            // [B, n_q, Hq, d_qk]
+    float *dk;            // [B, L, d_qk]
+    float *dv;            // [B, L, d_v] (latent: == dk)
+    int batch, n_q, heads, d_qk, d_v, n_idx, latent;
+    int64_t kv_len, k_stride, v_stride;
+    const int32_t *seq_len; // [B] valid rows per sequence (device) or nullptr
+    float scale;
+    int n_split;          // chunks of the index list per (query, head group)
+};
+
+int attn_bwd_splits(int batch, int n_q, int heads, int n_idx, int latent);
+hipError_t launch_sparse_attn_backward(const AttnBwdArgs &a, hipStream_t stream);
+
+// Backward of the indexer scores at the selected entries (bf16 keys): gradients added into.
+struct IndexBwdArgs {
+    const uint16_t *q;        // [B, n_q, H, d]
+    const float *w;           // [B, n_q, H]
+    const uint16_t *keys;     // [B, L, d] bf16
+    const int32_t *idx;       // [B, n_q, n_idx]
+    const float *dscore;      // [B, n_q, n_idx]
+    float *dq;                // [B, n_q, H, d]
+    float *dw;                // [B, n_q, H]
+    float *dkeys;             // [B, L, d]
+    int batch, n_q, heads, dim, n_idx;
+    int64_t kv_len, q_pos0;
+    const int32_t *seq_len, *seq_pos0; // [B] ragged batch (device) or nullptr
+    int n_split;              // chunks of the index list per query
+};
+
+bool index_bwd_supported(int heads, int dim);
+int index_bwd_splits(int batch, int n_q, int n_idx);
+hipError_t launch_index_scores_backward(const IndexBwdArgs &a, hipStream_t stream);
 size_t attn_workspace_bytes(int batch, int n_q, int heads, int d_v, int n_idx, int latent);
 hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t stream);
 bool attn_supported(int heads, int d_qk, int d_v, int latent);

@@ -27,7 +27,7 @@ STATUS = {0: "LSA_OK", 1: "LSA_ERR_NULL_POINTER", 2: "LSA_ERR_BAD_SHAPE", 3: "LS
 EXPORTS = ("lsa_index_scores", "lsa_topk_select", "lsa_page_summary", "lsa_page_recall",
            "lsa_sparse_attn", "lsa_workspace_bytes", "lsa_status_string",
            "lsa_topk_select_noalloc", "lsa_index_select", "lsa_quantize_queries",
-           "lsa_index_scores_q8")
+           "lsa_index_scores_q8", "lsa_sparse_attn_backward", "lsa_index_scores_backward")
 
 
 class IndexShape(ctypes.Structure):
@@ -77,6 +77,10 @@ def lib():
         L.lsa_page_recall.argtypes = [ip, bud, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
                                       _VP, _VP, _SZ, _VP]
         L.lsa_sparse_attn.argtypes = [ip, ap, bud, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]
+        L.lsa_sparse_attn_backward.argtypes = [ip, ap, bud, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                               _VP, _VP, _VP, _VP]
+        L.lsa_index_scores_backward.argtypes = [ip, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                _VP]
         L.lsa_workspace_bytes.argtypes = [_I32, ip, bud, _I32, _I32, _I64, ap]
         L.lsa_workspace_bytes.restype = _SZ
         L.lsa_status_string.argtypes = [_I32]
@@ -163,6 +167,20 @@ def lsa_sparse_attn(shape: IndexShape, attn: AttnShape, budget: Budget, q, k, v,
     _check("lsa_sparse_attn", lib().lsa_sparse_attn(
         ctypes.byref(shape), ctypes.byref(attn), budget, _p(q), _p(k), _p(v), _p(idx), _p(out),
         _p(lse), _p(ws), ws_bytes, _s(stream)))
+
+
+def lsa_sparse_attn_backward(shape: IndexShape, attn: AttnShape, budget: Budget, q, k, v, idx,
+                             out, lse, d_out, d_q, d_k, d_v, stream=None):
+    _check("lsa_sparse_attn_backward", lib().lsa_sparse_attn_backward(
+        ctypes.byref(shape), ctypes.byref(attn), budget, _p(q), _p(k), _p(v), _p(idx), _p(out),
+        _p(lse), _p(d_out), _p(d_q), _p(d_k), _p(d_v), _s(stream)))
+
+
+def lsa_index_scores_backward(shape: IndexShape, k: int, q, w, keys, idx, d_scores, d_q, d_w,
+                              d_keys, stream=None):
+    _check("lsa_index_scores_backward", lib().lsa_index_scores_backward(
+        ctypes.byref(shape), k, _p(q), _p(w), _p(keys), _p(idx), _p(d_scores), _p(d_q), _p(d_w),
+        _p(d_keys), _s(stream)))
 
 
 def lsa_workspace_bytes(op: int, shape: Optional[IndexShape], budget: Budget, page_size: int = 0,
@@ -412,3 +430,80 @@ def sparse_attn(q, k, v, idx, scale, sink=0, window=0, d_v=None, latent=None, wa
     wsb = (ws or Workspace()).get(nb, dev)
     lsa_sparse_attn(shape, attn, bud, q, k, v, idx, out, lse, wsb, nb, stream)
     return out, lse
+
+
+def sparse_attn_backward(q, k, v, idx, out, lse, d_out, scale, d_v=None, latent=None, d_q=None,
+                         d_k=None, d_vg=None, stream=None, seq_lens=None):
+    """Gradients of sparse_attn, ADDED into fp32 d_q [B,n_q,Hq,d_qk], d_k [B,L,d_qk] and d_vg
+    [B,L,d_v] (zeros are allocated for the ones not given).  Latent cache (v None or v is k):
+    one cache gradient d_k, whose first d_v columns also take dV; d_vg is then d_k."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 3, device=q.device)
+    _need(idx, "idx", torch.int32, 3, device=q.device)
+    if latent is None:
+        latent = v is None or v is k
+    if v is None:
+        v = k
+    B, T, Hq, dqk = q.shape
+    L = k.shape[1]
+    dev = q.device
+    if k.shape[0] != B or k.shape[2] < dqk:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    _need(v, "v", torch.bfloat16, 3, device=dev)
+    if v.shape[:2] != k.shape[:2]:
+        raise ValueError(f"v {tuple(v.shape)} does not match k {tuple(k.shape)}")
+    if idx.shape[:2] != (B, T):
+        raise ValueError(f"idx {tuple(idx.shape)} does not match q {tuple(q.shape)}")
+    if d_v is None:
+        d_v = v.shape[2] if not latent else dqk
+    if d_v > v.shape[2]:
+        raise ValueError(f"d_v {d_v} exceeds the value rows ({v.shape[2]})")
+    _need(out, "out", torch.bfloat16, shape=(B, T, Hq, d_v), device=dev)
+    _need(lse, "lse", torch.float32, shape=(B, T, Hq), device=dev)
+    _need(d_out, "d_out", torch.bfloat16, shape=(B, T, Hq, d_v), device=dev)
+    d_q = _zeros_or(d_q, "d_q", (B, T, Hq, dqk), dev)
+    d_k = _zeros_or(d_k, "d_k", (B, L, dqk), dev)
+    if latent:
+        if d_vg is not None and d_vg is not d_k:
+            raise ValueError("a latent cache has one gradient: d_vg must be d_k or None")
+        d_vg = d_k
+    else:
+        d_vg = _zeros_or(d_vg, "d_vg", (B, L, d_v), dev)
+    attn = AttnShape(Hq, dqk, d_v, 1 if latent else 0, k.shape[2], v.shape[2], scale)
+    shape = _ragged(IndexShape(B, T, 64, 128, L, 0), dev, seq_lens)
+    lsa_sparse_attn_backward(shape, attn, Budget(idx.shape[2], 0, 0), q, k, v, idx, out, lse,
+                             d_out, d_q, d_k, d_vg, stream)
+    return d_q, d_k, d_vg
+
+
+def index_scores_backward(q, w, keys, idx, d_scores, q_pos0=None, d_q=None, d_w=None,
+                          d_keys=None, stream=None, seq_lens=None, seq_pos0=None):
+    """Gradients of the indexer scores at the selected entries idx [B,n_q,k] for d_scores
+    [B,n_q,k] fp32, ADDED into fp32 d_q [B,n_q,H,d], d_w [B,n_q,H], d_keys [B,L,d] (zeros are
+    allocated for the ones not given).  bf16 keys."""
+    _need(q, "q", torch.bfloat16, 4)
+    _check_index_operands(q, w, keys)
+    if keys.dtype != torch.bfloat16:
+        raise ValueError("the indexer backward takes bf16 keys")
+    B, T, H, d = q.shape
+    L = keys.shape[1]
+    dev = q.device
+    _need(idx, "idx", torch.int32, 3, device=dev)
+    if idx.shape[:2] != (B, T):
+        raise ValueError(f"idx {tuple(idx.shape)} does not match q {tuple(q.shape)}")
+    _need(d_scores, "d_scores", torch.float32, shape=idx.shape, device=dev)
+    d_q = _zeros_or(d_q, "d_q", (B, T, H, d), dev)
+    d_w = _zeros_or(d_w, "d_w", (B, T, H), dev)
+    d_keys = _zeros_or(d_keys, "d_keys", (B, L, d), dev)
+    shape = index_shape(q, keys, q_pos0, seq_lens, seq_pos0)
+    lsa_index_scores_backward(shape, idx.shape[2], q, w, keys, idx, d_scores, d_q, d_w, d_keys,
+                              stream)
+    return d_q, d_w, d_keys
+
+
+def _zeros_or(t, name, shape, device):
+    """A caller-supplied gradient accumulator (checked), or a fresh zero one."""
+    if t is None:
+        return torch.zeros(shape, dtype=torch.float32, device=device)
+    _need(t, name, torch.float32, shape=shape, device=device)
+    return t
