@@ -311,6 +311,65 @@ def extra_prefill_q8(torch, lsa, inputs, cfg, tm: Timing):
     return res
 
 
+def _bwd_setup(torch, lsa, inputs, cfg):
+    """The chunked-prefill shape's training step: its selection, the forward attention (out,
+    lse) and random output / score gradients, for the two backward calls."""
+    w = cfg.PREFILL_8K_AT_128K
+    s, b, a = w.index, w.budget, w.attn
+    dev = "cuda"
+    inp = inputs.index_inputs(w, dev)
+    att = inputs.attn_inputs(w, 0, dev)
+    scores = lsa.index_scores(inp["q"], inp["w"], inp["keys"], None, q_pos0=s.q_pos0)
+    idx = lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=s.kv_len, q_pos0=s.q_pos0)
+    del scores
+    out, lse = lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale, b.sink, b.window, d_v=a.d_v)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 100)
+    d_out = torch.randn(out.shape, generator=g, device=dev).to(torch.bfloat16)
+    d_sc = torch.randn(idx.shape, generator=g, device=dev)
+    grads = {"d_q": torch.zeros((1, s.n_q, a.heads, a.d_qk), dtype=torch.float32, device=dev),
+             "d_kv": torch.zeros((1, s.kv_len, a.d_qk), dtype=torch.float32, device=dev),
+             "di_q": torch.zeros((1, s.n_q, s.heads, s.head_dim), dtype=torch.float32, device=dev),
+             "di_w": torch.zeros((1, s.n_q, s.heads), dtype=torch.float32, device=dev),
+             "di_k": torch.zeros((1, s.kv_len, s.head_dim), dtype=torch.float32, device=dev)}
+
+    def f_attn_bwd():
+        lsa.sparse_attn_backward(att["q"], att["kv"], None, idx, out, lse, d_out, a.scale,
+                                 d_v=a.d_v, d_q=grads["d_q"], d_k=grads["d_kv"])
+
+    def f_index_bwd():
+        lsa.index_scores_backward(inp["q"], inp["w"], inp["keys"], idx, d_sc, q_pos0=s.q_pos0,
+                                  d_q=grads["di_q"], d_w=grads["di_w"], d_keys=grads["di_k"])
+    return w, f_attn_bwd, f_index_bwd
+
+
+def extra_backward(torch, lsa, inputs, cfg, tm: Timing):
+    """The training path at the chunked-prefill shape (8192 queries over 128K keys, k = 2048):
+    the sparse-attention backward (MLA 16 x 576/512) and the indexer backward (64 x 128, bf16
+    keys) over the GPU's own selection.  Gradients are added into fp32 arrays, so repeated calls
+    accumulate; the timed region is the call alone."""
+    w, f_attn_bwd, f_index_bwd = _bwd_setup(torch, lsa, inputs, cfg)
+    s, b, a = w.index, w.budget, w.attn
+    f_attn_bwd(), f_index_bwd()
+    d = {"attn_bwd": tm.both(f_attn_bwd, 60.0, cold_too=False),
+         "index_bwd": tm.both(f_index_bwd, 30.0, cold_too=False)}
+    n_sel = s.n_q * b.k
+    attn_flops = 2.0 * n_sel * a.heads * (3 * a.d_qk + 2 * a.d_v)
+    idx_flops = 2.0 * 3 * n_sel * s.heads * s.head_dim
+    ta, ti = d["attn_bwd"]["warm"]["mean"], d["index_bwd"]["warm"]["mean"]
+    res = {"workload": w.name + "_backward", "dist": d,
+           "attn_bwd_flops": attn_flops, "attn_bwd_TFLOPs": attn_flops / (ta * 1e-3) / 1e12,
+           "attn_bwd_mfma_frac": attn_flops / (ta * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+           "attn_bwd_atomic_updates": n_sel * a.d_qk,
+           "attn_bwd_G_updates_per_s": n_sel * a.d_qk / (ta * 1e-3) / 1e9,
+           "index_bwd_flops": idx_flops, "index_bwd_TFLOPs": idx_flops / (ti * 1e-3) / 1e12,
+           "index_bwd_mfma_frac": idx_flops / (ti * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
+           "index_bwd_atomic_updates": n_sel * s.head_dim,
+           "index_bwd_G_updates_per_s": n_sel * s.head_dim / (ti * 1e-3) / 1e9}
+    torch.cuda.empty_cache()
+    return res
+
+
 def extra_hi(torch, lsa, inputs, w, tm: Timing):
     import numpy as np
     s, b, a, hi = w.index, w.budget, w.attn, w.hi
@@ -506,6 +565,9 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
         fns = {"prefill_q8": lambda: lsa.index_scores_q8(q8, qs, inp["w"], inp["keys"],
                                                          inp["scale"], q_pos0=s.q_pos0,
                                                          out=scores)}
+    elif stage.startswith("bwd_"):
+        _, f_attn_bwd, f_index_bwd = _bwd_setup(torch, lsa, inputs, cfg)
+        fns = {"bwd_attn": f_attn_bwd, "bwd_index": f_index_bwd}
     elif stage.startswith("prefill_"):
         w = cfg.PREFILL_8K_AT_128K
         s, b, a = w.index, w.budget, w.attn
@@ -566,7 +628,7 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
 
 
 STAGES = ["score", "topk", "index", "attn", "copy", "prefill_score", "prefill_topk", "prefill_attn",
-          "prefill_q8",
+          "prefill_q8", "bwd_attn", "bwd_index",
           "hi1m_summary", "hi1m_recall", "hi1m_topk"]
 
 
@@ -628,6 +690,8 @@ def main():
         extras["prefill_8k_128k"] = extra_prefill(torch, lsa, inputs, cfg, tm)
         log("[bench] extra: chunked prefill with fp8 queries")
         extras["prefill_8k_128k_fp8q"] = extra_prefill_q8(torch, lsa, inputs, cfg, tm)
+        log("[bench] extra: backward at the chunked-prefill shape")
+        extras["prefill_8k_128k_backward"] = extra_backward(torch, lsa, inputs, cfg, tm)
         log("[bench] extra: HI at 1M")
         extras["decode_1m_hi"] = extra_hi(torch, lsa, inputs, cfg.DECODE_1M_HI, tm)
         log("[bench] extra: HI + cross-layer x4 at 256K")
