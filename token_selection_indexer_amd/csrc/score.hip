@@ -17,9 +17,10 @@
 //    the key cache is read exactly once) and passes them through its own LDS slab into the MFMA
 //    operand layout.  Also runs the fine stage of Hierarchical Indexing, where
 //    the blocks come from each query's recalled pages.
-//  * tile: prefill.  A workgroup owns WAVES*NQW queries; 128-key tiles are staged once in LDS
-//    (bf16, padded rows) and shared by every wave, double-buffered against the next tile's
-//    global loads.
+//  * tile: prefill.  A workgroup owns WAVES*NQW queries; key tiles (256 keys at 64 heads of
+//    width 128, 128 keys otherwise) are staged once in LDS (bf16, padded rows) and shared by
+//    every wave, double-buffered against the next tile's global loads.  With fp8 queries the
+//    same kernel runs on the 8-bit MFMA.
 //
 // Operand layout.  The two lane halves split d: half g = l/32 holds d in [g*D/2, (g+1)*D/2);
 // K-step kk feeds d = g*D/2 + 8*kk + [0,8) as the MFMA's K index 8*g + [0,8).  This permutes the
