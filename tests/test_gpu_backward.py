@@ -281,3 +281,98 @@ def test_index_backward_decode_shape():
 def test_index_backward_ragged():
     _index_case(B=3, T=2, H=64, d=128, L=900, k=128, seed=23, seq_lens=[900, 300, 0],
                 seq_pos0=[898, 298, 0])
+
+
+# ------------------------------------------------------------------------------ full shape
+def _sample_rows(kv_f64, ids):
+    """The selected rows of one query, re-indexed 0..k-1 (-1 kept): the oracle then needs only
+    those rows (a query's own gradient depends on its own rows alone)."""
+    ok = ids >= 0
+    rows = kv_f64[np.where(ok, ids, 0)]
+    return rows, np.where(ok, np.arange(ids.size), -1).astype(np.int32)[None]
+
+
+def test_backward_prefill_8k_128k_full_shape():
+    """The training path at the chunked-prefill shape (8192 queries, 128K keys, k = 2048), on
+    the GPU's own selection: sampled queries' dq (all heads) and dw against the oracle, and over
+    the whole launch the identities the gradients obey exactly:
+      attention  sum_r dV_r = sum_(t,h) dO_(t,h)            (softmax rows sum to one)
+                 <dKV, KV> - <dq, q> = sum_(t,h) dO . out    (the logits are bilinear in q and K;
+                                                             <dV, V> = sum dO . O)
+      indexer    <dq, q> = <dk, K> = <dw, w>                 (the score has degree 1 in each)
+    The identities pair every row's gradient with its own row, so misrouted or dropped updates
+    break them.  Tolerances: 2^-8 of the magnitude for terms carrying the forward's bf16 output
+    and lse (reading in the header), plus 1e-6 of the magnitude of the inner products (sum of
+    the absolute products) for the fp32 gradients' rounding.  That last term is statistical, not
+    a worst case: the atomic sums' rounding errors have random signs, so their effect on an
+    inner product of N terms scales like 2^-24 sqrt(n) / sqrt(N) of the magnitude, over 100
+    times below 1e-6 here; and 1e-6 of the magnitude stays well below each identity's own value,
+    so a dropped or misrouted share of the gradient fails."""
+    from token_selection_indexer_amd import configs, inputs
+    w = configs.PREFILL_8K_AT_128K
+    s, b, a = w.index, w.budget, w.attn
+    inp = inputs.index_inputs(w, DEV)
+    att = inputs.attn_inputs(w, 0, DEV)
+    scores = lsa.index_scores(inp["q"], inp["w"], inp["keys"], None, q_pos0=s.q_pos0)
+    idx = lsa.topk_select(scores, b.k, b.sink, b.window, kv_len=s.kv_len, q_pos0=s.q_pos0)
+    del scores
+    out, lse = lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale, b.sink, b.window, d_v=a.d_v)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(17)
+    dout = torch.randn(out.shape, generator=g, device=DEV).to(torch.bfloat16)
+    dsc = torch.randn(idx.shape, generator=g, device=DEV)
+    d_q, d_kv, _ = lsa.sparse_attn_backward(att["q"], att["kv"], None, idx, out, lse, dout,
+                                            a.scale, d_v=a.d_v)
+    di_q, di_w, di_k = lsa.index_scores_backward(inp["q"], inp["w"], inp["keys"], idx, dsc,
+                                                 q_pos0=s.q_pos0)
+    torch.cuda.synchronize()
+    dv = a.d_v
+    # attention identities
+    dO = dout.double()
+    lhs = d_kv[0, :, :dv].double().sum(0)
+    rhs = dO.sum((0, 1, 2))
+    tol = 2.0 ** -8 * dO.abs().sum((0, 1, 2)) + 1e-3
+    assert bool(((lhs - rhs).abs() <= tol).all()), float(((lhs - rhs).abs() / tol).max())
+    kvd, qd = att["kv"].double(), att["q"].double()
+    e_kv, e_q = (d_kv.double() * kvd), (d_q.double() * qd)
+    euler = float(e_kv.sum() - e_q.sum())
+    want = float((dO * out.double()).sum())
+    tol = (2.0 ** -8 * float((dO.abs() * out.double().abs()).sum())
+           + 1e-6 * float(e_kv.abs().sum() + e_q.abs().sum()))
+    say(f"[bwd] attention full shape: sum dV vs sum dO ok; <dKV,KV> - <dq,q> = {euler:.6g}, "
+        f"sum dO.out = {want:.6g}, tol {tol:.3g}")
+    assert abs(euler - want) <= tol
+    # indexer identity
+    iq = float((di_q.double() * inp["q"].double()).sum())
+    ik = float((di_k.double() * inp["keys"].double()).sum())
+    iw = float((di_w.double() * inp["w"].double()).sum())
+    mag = float((di_q.double() * inp["q"].double()).abs().sum() +
+                (di_k.double() * inp["keys"].double()).abs().sum() +
+                (di_w.double() * inp["w"].double()).abs().sum())
+    say(f"[bwd] indexer full shape: <dq,q> {iq:.6g}, <dk,K> {ik:.6g}, <dw,w> {iw:.6g}, mag {mag:.3g}")
+    assert abs(iq - ik) <= 1e-6 * mag and abs(iq - iw) <= 1e-6 * mag
+    # sampled queries against the oracle
+    kv_f = _f64(att["kv"][0])
+    keys_f = _f64(inp["keys"][0])
+    tau = a.scale
+    for t in (0, 1, 4095, 4096, 8191):
+        ids = idx[0, t].cpu().numpy()
+        rows, ir = _sample_rows(kv_f, ids)
+        qt = _f64(att["q"][0, t:t + 1])
+        gt = _f64(dout[0, t:t + 1])
+        rq, _, _ = ref.sparse_attn_backward(qt, rows, rows, ir, tau, gt, d_qk=a.d_qk, d_v=dv)
+        Mq, MDq, _, _, _ = _attn_mag(qt, rows, rows[:, :dv], ir, tau, gt, rows.shape[0])
+        _check(f"full-shape dq t={t}", d_q[0, t:t + 1].cpu().numpy().astype(np.float64), rq, Mq,
+               MDq, 4e-3)
+        krows, kir = _sample_rows(keys_f, ids)
+        qi = _f64(inp["q"][0, t:t + 1])
+        wi = inp["w"][0, t:t + 1].cpu().numpy().astype(np.float64)
+        gi = dsc[0, t:t + 1].cpu().numpy().astype(np.float64)
+        pos = np.array([ids.size], np.int64)  # every re-indexed row is in the past
+        rq2, rw2, _ = ref.index_scores_backward(qi, wi, krows, kir, pos, gi)
+        (Mq2, Aq2), (Mw2, Aw2), _ = _index_mag(qi, wi, krows, kir, pos, gi, krows.shape[0])
+        for name, gpu, want2, M, A in (("dq", di_q[0, t:t + 1], rq2, Mq2, Aq2),
+                                       ("dw", di_w[0, t:t + 1], rw2, Mw2, Aw2)):
+            err = np.abs(gpu.cpu().numpy().astype(np.float64) - want2)
+            assert (err <= 1e-4 * M + A + 1e-6).all(), (name, t, float(err.max()))
+    say("[bwd] full-shape sampled queries ok")

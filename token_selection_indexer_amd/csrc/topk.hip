@@ -50,7 +50,7 @@ constexpr int CAP = 8192;           // LDS candidate buffer entries (key, id)
 constexpr int CHUNK = 4096;         // chunked path: elements per workgroup
 constexpr int CHUNK_CAP = 512;      // chunked path: candidates kept per chunk
 constexpr int CNT_THREADS = 256;    // chunked path: threads per chunk workgroup
-constexpr int64_t SAMPLE_MIN = 16384; // one-workgroup rows at least this long use the sample
+constexpr int64_t SAMPLE_MIN = 8192;  // one-workgroup rows longer than the buffer use the sample
 
 // ------------------------------------------------------------------------------------------
 // Row access
