@@ -183,7 +183,11 @@ LSA_API lsa_status lsa_index_scores_q8(const lsa_index_shape *shape, const uint8
  * launch, and rows long enough for the chunked selection) the scoring workgroups also histogram
  * their middle-region scores while the scores are in registers, and the selection reads each
  * row's exact threshold bin from those histograms instead of sampling the row before it
- * compacts what lies at or above it.  Other shapes run the two ordinary paths.
+ * compacts what lies at or above it.  Where a row has at most 16 scoring workgroups of at most
+ * 8192 keys each (32 sequences of up to 128K keys, for one), each workgroup also keeps its own
+ * best scores (the histogram bins holding about twice its share of the row's picks) in a slice
+ * of `ws`, and a single selection launch gathers the slices instead of passing over the score
+ * rows again.  Other shapes run the two ordinary paths.
  *   q, w, keys, key_scale, scores   as for lsa_index_scores (scores 16-byte aligned)
  *   idx     [B, n_q, k] int32 as for lsa_topk_select
  *   ws      lsa_workspace_bytes(LSA_OP_INDEX_SELECT, shape, budget, 0, 0, 0, NULL) bytes,

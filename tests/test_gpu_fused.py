@@ -6,7 +6,9 @@ on the same fp32 scores.  Cases: the decode workload at full size, fp8 and bf16 
 heads, a key count off the 32-key block (the moved-back last block must not be counted twice in
 the histogram), a causal cut short of the cache end, a second query per sequence, rows with
 V <= k, a row where every score ties (the histogram's threshold bin overflows the buffer: the
-exact fallback), and an unfused shape (the two ordinary launches).
+exact fallback), rows whose best keys crowd into one scoring workgroup's range (its slice does
+not reach the row's threshold bin: that range is read from the score row), and an unfused shape
+(the two ordinary launches).
 """
 import numpy as np
 import pytest
@@ -112,6 +114,48 @@ def test_fused_rows_within_budget_and_ties():
     gi = i1.cpu().numpy()
     dyn = gi[1, 0, b.sink + b.window:]
     assert np.array_equal(dyn, np.arange(b.sink, b.sink + b.k - b.sink - b.window))
+
+
+@pytest.mark.parametrize("B", [16, 32])
+def test_fused_clustered_best_keys(B):
+    """With 32 sequences each scoring workgroup keeps only its own best few (about twice its
+    share of the row's picks) in a slice; with 16 the selection reads the rows through the
+    histograms.  Here one sequence's best keys crowd into one stretch (copies of its best key
+    with rising scales, so distinct and far above the rest), another's into tied copies: the
+    slices of the stretch's workgroups lack keys at the row's threshold bin, so the selection
+    reads those ranges from the score row.  Results stay bitwise those of the separate calls."""
+    L = 131072
+    wl = Workload(name="fc", index=IndexShape(batch=B, n_q=1, kv_len=L, q_pos0=L - 1, heads=64,
+                                              head_dim=128, key_dtype="fp8"),
+                  budget=Budget(k=2048, sink=64, window=960), attn=DECODE_128K.attn, seed=73)
+    b = wl.budget
+    inp = inputs.index_inputs(wl, DEV)
+    keys, scale = inp["keys"].clone(), inp["scale"].clone()
+    sc0, _ = _separate(inp["q"], inp["w"], keys, scale, b, L - 1)
+    top = sc0[:, 0, b.sink:L - b.window].argmax(dim=1) + b.sink
+    lo, n = 7000, 2000  # straddles a workgroup boundary (every 4096 or 8192 keys here)
+    a1, a2 = int(top[1]), int(top[2])
+    keys[1, lo:lo + n] = keys[1, a1]
+    scale[1, lo:lo + n] = scale[1, a1] * torch.linspace(1.0, 3.0, n, device=DEV)
+    keys[2, lo:lo + n] = keys[2, a2]
+    scale[2, lo:lo + n] = scale[2, a2]
+    assert _is_fused(wl)
+    sc1, i1 = _fused(inp["q"], inp["w"], keys, scale, b, L - 1)
+    sc2, i2 = _separate(inp["q"], inp["w"], keys, scale, b, L - 1)
+    torch.cuda.synchronize()
+    assert torch.equal(sc1.view(torch.int32), sc2.view(torch.int32))
+    assert torch.equal(i1, i2)
+    V = ref.valid_lengths(L, L - 1, 1)
+    scn, gi = sc1.cpu().numpy(), i1.cpu().numpy()
+    for r in range(B):
+        check_rows_exact(gi[r], scn[r], V, b.k, b.sink, b.window)
+    need = b.k - b.sink - b.window
+    # sequence 2: the tied copies outrank everything but the original, lowest ids first
+    dyn2 = gi[2, 0, b.sink + b.window:]
+    expect = np.concatenate([[a2], np.arange(lo, lo + need - 1)]) if a2 < lo else np.arange(lo, lo + need)
+    assert np.array_equal(dyn2, expect)
+    # sequence 1: the copies with the largest scales (factors 2 .. 3, above every other key)
+    assert np.array_equal(gi[1, 0, b.sink + b.window:], np.arange(lo + n - need, lo + n))
 
 
 def test_unfused_shape_matches():

@@ -46,6 +46,31 @@ def _keys_b(inp, b, L):
     return k.cpu().numpy().view(np.uint8), f32(inp["scale"][b, :L])
 
 
+def test_ragged_fused_slices_32():
+    """32 decode sequences of mixed lengths: the fused call takes the per-workgroup slices (one
+    scoring workgroup per 8192 keys) and must be bitwise equal to the separate calls, with every
+    row bit-exact against ref.select on the GPU's scores."""
+    lens_l = LENS + LENS[::-1]
+    B = len(lens_l)
+    wl = _workload(B, 1, seed=83)
+    b = wl.budget
+    inp = inputs.index_inputs(wl, DEV)
+    lens = torch.tensor(lens_l, dtype=torch.int32, device=DEV)
+    pos0 = (lens - 1).clamp(min=0)
+    sc = lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], seq_lens=lens,
+                          seq_pos0=pos0)
+    idx = lsa.topk_select(sc, b.k, b.sink, b.window, kv_len=CAP, q_pos0=CAP - 1, seq_lens=lens,
+                          seq_pos0=pos0)
+    sc2, idx2 = lsa.index_select(inp["q"], inp["w"], inp["keys"], inp["scale"], b.k, b.sink,
+                                 b.window, seq_lens=lens, seq_pos0=pos0)
+    torch.cuda.synchronize()
+    assert torch.equal(sc.view(torch.int32), sc2.view(torch.int32))
+    assert torch.equal(idx, idx2)
+    scn, gi = sc.cpu().numpy(), idx.cpu().numpy()
+    for r, L in enumerate(lens_l):
+        check_rows_exact(gi[r], scn[r], np.array([L]), b.k, b.sink, b.window)
+
+
 def test_ragged_decode_scores_and_selection():
     """16 decode sequences of mixed lengths (query at seq_len - 1): scores against the oracle,
     selection bit-exact against ref.select on the GPU's scores, and the fused call (the batch

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "internal.hpp"
 
 namespace {
@@ -79,10 +81,13 @@ lsa_status check_attn(const lsa_index_shape *s, const lsa_attn_shape *a, lsa_bud
 }
 
 // The fused score + select plan for a shape: histogram groups per row (0: not fused) and the
-// workspace layout (histograms, then the chunked selection's slices).
+// workspace layout.  With slices (each scoring workgroup owns at most kSliceSpan keys and the
+// selection has a wave per scoring workgroup of the row): histograms, slice headers and entries,
+// and one selection launch.  Else histograms, then the chunked selection's workspace.
 struct FusedPlan {
     int groups = 0;
-    size_t hist_fine = 0, hist_coarse = 0, select = 0, total = 0;
+    bool slices = false;
+    size_t hist_fine = 0, hist_coarse = 0, slice_hdr = 0, slice_ent = 0, select = 0, total = 0;
 };
 
 lsa::ScoreArgs score_args(const lsa_index_shape *shape, lsa_budget budget)
@@ -129,14 +134,22 @@ FusedPlan fused_plan(const lsa_index_shape *shape, lsa_budget budget)
     const int64_t rows = (int64_t)shape->batch * shape->n_q;
     p.select = lsa::select_workspace_bytes(rows, shape->kv_len, lsa::SELECT_SI);
     p.total = p.select;
-    // fused only where the selection takes its chunked path (few long rows)
+    // fused only where the selection alone would take its chunked path (few long rows)
     if (rows == 0 || p.select == 0) return p;
-    const int groups = lsa::score_hist_groups(score_args(shape, budget));
+    const lsa::ScoreArgs sa = score_args(shape, budget);
+    const int groups = lsa::score_hist_groups(sa);
     if (groups == 0) return p;
     p.groups = groups;
     p.hist_fine = round256((size_t)rows * groups * 2048 * 4);
     p.hist_coarse = round256((size_t)rows * groups * 32 * 4);
-    p.total = p.hist_fine + p.hist_coarse + p.select;
+    p.slices = groups <= lsa::select_slice_groups_max() &&
+               lsa::score_hist_span(sa, groups) <= lsa::kSliceSpan;
+    if (p.slices) {
+        p.select = 0;
+        p.slice_hdr = round256((size_t)rows * groups * 16);
+        p.slice_ent = round256((size_t)rows * groups * lsa::kSliceCap * 8);
+    }
+    p.total = p.hist_fine + p.hist_coarse + p.slice_hdr + p.slice_ent + p.select;
     return p;
 }
 
@@ -357,10 +370,25 @@ lsa_status lsa_index_select(const lsa_index_shape *shape, lsa_budget budget, con
     }
     uint8_t *base = static_cast<uint8_t *>(ws);
     a.hist_fine = reinterpret_cast<uint32_t *>(base);
-    a.hist_coarse = reinterpret_cast<uint32_t *>(base + p.hist_fine);
+    base += p.hist_fine;
+    a.hist_coarse = reinterpret_cast<uint32_t *>(base);
+    base += p.hist_coarse;
+    if (!p.slices) {
+        if ((st = device_status(lsa::launch_scores(a, sm))) != LSA_OK) return st;
+        return device_status(
+            lsa::launch_select_hist(s, base, a.hist_fine, a.hist_coarse, p.groups, sm));
+    }
+    a.slice_hdr = reinterpret_cast<int4 *>(base);
+    a.slice_ent = reinterpret_cast<uint2 *>(base + p.slice_hdr);
+    // a slice keeps the bins holding about twice its workgroup's expected share of the row's
+    // `need` best: enough that the slices' keys at or above their highest bin almost always
+    // number at least `need`, few enough to keep the selection's buffer small
+    const int need_dyn = budget.k - budget.sink - budget.window;
+    const int share = (need_dyn + p.groups - 1) / p.groups;
+    a.slice_target = std::max(1, std::min({need_dyn, 2 * share + 32, lsa::kSliceCap}));
     if ((st = device_status(lsa::launch_scores(a, sm))) != LSA_OK) return st;
-    return device_status(lsa::launch_select_hist(s, base + p.hist_fine + p.hist_coarse,
-                                                 a.hist_fine, a.hist_coarse, p.groups, sm));
+    return device_status(lsa::launch_select_slices(s, a.hist_fine, a.hist_coarse, a.slice_hdr,
+                                                   a.slice_ent, p.groups, sm));
 }
 
 lsa_status lsa_topk_select(const lsa_index_shape *shape, lsa_budget budget, const float *scores,

@@ -152,6 +152,17 @@ __device__ __forceinline__ int wave_inclusive_scan(int x)
     return x;
 }
 
+// Inclusive prefix sum within each row of 16 lanes (the first four steps above): a row's last
+// lane ends with the row's total.
+__device__ __forceinline__ uint32_t row_inclusive_scan(uint32_t x)
+{
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false); // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false); // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false); // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false); // row_shr:8
+    return x;
+}
+
 __device__ __forceinline__ float wave_max(float x)
 {
 #pragma unroll

@@ -13,6 +13,11 @@ enum RowMask : int {
     MASK_PAGES = 1,  // page keys: pages overlapping the middle [S, V_t - W), none when V_t <= k
 };
 
+// Entries per workgroup slice of the fused decode selection (ScoreArgs::slice_ent), and the
+// most keys a scoring workgroup may own for it (its scores are staged in LDS).
+constexpr int kSliceCap = 1024;
+constexpr int kSliceSpan = 8192;
+
 struct ScoreArgs {
     const uint16_t *q;    // [B, n_q, H, d] bf16
     const float *w;       // [B, n_q, H]
@@ -37,6 +42,14 @@ struct ScoreArgs {
     // [row][blockIdx.x].
     uint32_t *hist_fine;  // [rows][groups][2048] or nullptr
     uint32_t *hist_coarse; // [rows][groups][32]
+    // With the histograms, each workgroup also keeps its middle-region scores in bins at or above
+    // a local threshold bin (the bin of its slice_target-th best, one bin higher when more than
+    // kSliceCap would be kept) in position order: slice [row][blockIdx.x] of slice_ent, entries
+    // {score bits, position}, with header {bin, count, first position, end position} of the
+    // workgroup's middle-region range.
+    int4 *slice_hdr;      // [rows][groups]
+    uint2 *slice_ent;     // [rows][groups][kSliceCap]
+    int slice_target;
     // fp8 queries (q8 != nullptr): e4m3 codes [B, n_q, H, d] with one fp32 scale per (query,
     // head); `q` is then unused and the keys must be e4m3 too
     const uint8_t *q8;
@@ -56,6 +69,8 @@ bool scores_supported(int heads, int dim);
 // Workgroups per query row ("groups") of the flat launch when it can emit the selection
 // histograms (the long decode launch, one query per workgroup); 0 when it cannot.
 int score_hist_groups(const ScoreArgs &a);
+// Keys each workgroup of that launch owns (slices need at most kSliceSpan).
+int64_t score_hist_span(const ScoreArgs &a, int groups);
 
 struct SelectArgs {
     const float *scores;     // [rows, n_in]
@@ -84,6 +99,15 @@ hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream);
 // chunked path reads each row's threshold bin from them instead of sampling the row.
 hipError_t launch_select_hist(const SelectArgs &a, void *ws, const uint32_t *hist_fine,
                               const uint32_t *hist_coarse, int groups, hipStream_t stream);
+// The fused decode path with slices: one launch, one workgroup per row, that gathers the
+// scoring workgroups' slices (ScoreArgs::slice_*) at or above their highest local bin -- or,
+// when those hold fewer than the row needs, takes the row's threshold bin from the histograms --
+// and selects exactly.  No workspace of its own; at most select_slice_groups_max() scoring
+// workgroups per row.
+int select_slice_groups_max();
+hipError_t launch_select_slices(const SelectArgs &a, const uint32_t *hist_fine,
+                                const uint32_t *hist_coarse, const int4 *slice_hdr,
+                                const uint2 *slice_ent, int groups, hipStream_t stream);
 // The library's own per-device scratch for callers that cannot allocate: its size, and the
 // current device's address of it (looked up on the first call on each device).
 size_t select_scratch_bytes();

@@ -240,6 +240,104 @@ struct KeyBlock {
     }
 };
 
+// LDS stage of a scoring workgroup's scores for the fused selection's slice: block b (32
+// positions) of the workgroup's range sits in quarter b / 64 at column b % 64, position j of the
+// block in row j of 65 words (the padding keeps both the block's write and the column reads of
+// the compaction free of bank conflicts).
+constexpr int kStageQ = 32 * 65;
+__device__ __forceinline__ int stage_index(int blk, int j) { return (blk >> 6) * kStageQ + j * 65 + (blk & 63); }
+
+// The fused selection's slice of one scoring workgroup (flat decode launch, after its histogram
+// and stage are complete).  Every wave finds the highest bin L whose suffix count in the
+// workgroup's histogram reaches a.slice_target (one bin higher if that would keep more than
+// kSliceCap; 0 = every bin when the workgroup holds fewer), then compacts the scores of its
+// quarter of the range in bins >= L: lane l takes block 64 w + l, so lane order is position
+// order and a lane's picks are contiguous.  Positions outside the middle region [o_lo, o_hi) are
+// skipped.  Wave 0 also leaves the 32 coarse sums of the histogram in `lcoarse`.  A selection
+// whose row threshold bin is >= L finds all of this range's candidates in the slice.
+template <int WAVES>
+__device__ __forceinline__ void slice_compact(const ScoreArgs &a, const uint32_t *lhist,
+                                              uint32_t *lcoarse, const float *lsc, int64_t slice,
+                                              int64_t o_base, int64_t o_lo, int64_t o_hi)
+{
+    static_assert(WAVES * 64 * 32 == kSliceSpan, "one quarter of 64 blocks per wave");
+    __shared__ int sinfo[WAVES];
+    __shared__ uint32_t lcw[WAVES - 1][32]; // the coarse sums of waves 1.. (wave 0: lcoarse)
+    const int l = lane_id(), w = wave_id();
+    // The 32 coarse sums (64 bins each), read without bank conflicts: lane l sums the 4-bin
+    // chunks l + 64 i (i < 8), which lie in group l / 16 + 4 i; a scan over each 16-lane row
+    // leaves a group's sum in the row's last lane.  Each wave keeps its own copy in LDS (a wave's
+    // LDS accesses complete in order: no barrier).
+    uint32_t *cw = w == 0 ? lcoarse : lcw[w - 1];
+    {
+        const uint4 *h4 = reinterpret_cast<const uint4 *>(lhist);
+        uint32_t part[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint4 x = h4[l + 64 * i];
+            part[i] = x.x + x.y + x.z + x.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            part[i] = row_inclusive_scan(part[i]);
+            if ((l & 15) == 15) cw[(l >> 4) + 4 * i] = part[i];
+        }
+    }
+    const uint32_t c = l < 32 ? cw[31 - l] : 0u; // lane i < 32: coarse group 31 - i (top down)
+    const int t = a.slice_target;
+    const int inc = wave_inclusive_scan((int)c);
+    const uint64_t ge = __ballot(l < 32 && inc >= t);
+    uint32_t L = 0;
+    if (ge) {
+        const int g = (int)__builtin_ctzll(ge), grp = 31 - g;
+        const int exg = __builtin_amdgcn_readlane(inc, g) - __builtin_amdgcn_readlane((int)c, g);
+        const int f = (int)lhist[64 * grp + 63 - l];
+        const int inc2 = exg + wave_inclusive_scan(f);
+        const int i = (int)__builtin_ctzll(__ballot(inc2 >= t)); // exists: the group reaches t
+        L = (uint32_t)(64 * grp + 63 - i);
+        if (__builtin_amdgcn_readlane(inc2, i) > kSliceCap) L += 1;
+    }
+    // Per lane, not per position: a lane's 32 positions are consecutive, so a bit mask and one
+    // wave scan of the lane counts order the picks, and the write loop runs over picks only.
+    const int q0 = (64 * w + l) * 32; // the lane's first position, relative to o_base
+    const int lo = (int)(o_lo - o_base), hi = max(lo, (int)(o_hi - o_base)); // may be empty
+    const float *col = lsc + w * kStageQ + l;
+    // key(f) >> 21 >= L as one float comparison: f >= the float whose key is L << 21 (every
+    // finite f when L << 21 lies below key(-inf), none when L is past the last bin: NaN).
+    // Every read is issued before any is used; stage slots outside the middle region hold stale
+    // values and are masked out.
+    const uint32_t T = L << 21;
+    const float tf = L <= 3u      ? -INFINITY
+                     : L >= 2048u ? __uint_as_float(0x7fc00000u)
+                                  : __uint_as_float((T & 0x80000000u) ? T & 0x7fffffffu : ~T);
+    uint32_t mask = 0;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+        const uint32_t in = (uint32_t)(q0 + j - lo) < (uint32_t)(hi - lo);
+        mask |= (in & (uint32_t)(col[j * 65] >= tf)) << j;
+    }
+    const int cnt = __popc(mask);
+    const int incl = wave_inclusive_scan(cnt);
+    if (l == kWave - 1) sinfo[w] = incl;
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int i = 0; i < WAVES; ++i) {
+        const int x = sinfo[i];
+        base += i < w ? x : 0;
+        total += x;
+    }
+    uint2 *ent = a.slice_ent + slice * kSliceCap;
+    uint32_t slot = (uint32_t)(base + incl - cnt);
+    const uint32_t p0 = (uint32_t)o_base + (uint32_t)q0;
+    // total <= kSliceCap by the choice of L
+    for (uint32_t m = mask; m != 0u && slot < (uint32_t)kSliceCap; m &= m - 1u, ++slot) {
+        const int j = __builtin_ctz(m);
+        ent[slot] = make_uint2(__float_as_uint(col[j * 65]), p0 + (uint32_t)j);
+    }
+    if (threadIdx.x == 0)
+        a.slice_hdr[slice] = make_int4((int)L, total, (int)o_lo, (int)max(o_hi, o_lo));
+}
+
 // PD: blocks prefetched ahead of the one being computed (register ring of PD + 1 blocks).
 // BPW > 0: each wave takes BPW blocks, the block loop fully unrolled.  BPW == 0: each wave takes
 // ceil(blocks / (gridDim.x * WAVES)) blocks in a loop whose body is one turn of the ring, so
@@ -248,7 +346,8 @@ struct KeyBlock {
 // scores [S, V-W) into a 2048-bin LDS histogram of key bits 31..21 while they are in registers,
 // and writes it (32 coarse sums of 64 bins, and the fine bins of the non-empty groups) to its
 // slice of a.hist_fine / a.hist_coarse, so the selection that follows reads the row's exact
-// threshold bin instead of sampling the row.
+// threshold bin instead of sampling the row.  With a.slice_ent (a workgroup owns at most
+// kSliceSpan keys) it also stages those scores in LDS and leaves its slice (slice_compact).
 template <bool FP8, int D, int H, int MT, bool ONEQ, bool FINE, int WAVES, int BPW, int PD = 1,
           bool HIST = false>
 __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
@@ -262,6 +361,8 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
     // two slabs per wave: block i is transposed in slab i&1 while block i-1 may still be read
     __shared__ __attribute__((aligned(16))) uint8_t slabs[WAVES][2][KB::BB];
     __shared__ __attribute__((aligned(16))) uint32_t lhist[HIST ? HBINS : 4];
+    // HIST with slices: the workgroup's middle-region scores, by position within its range
+    __shared__ float lsc[HIST ? kSliceSpan / 2048 * kStageQ : 1];
     if constexpr (HIST) {
         for (int i = threadIdx.x; i < HBINS / 4; i += WAVES * kWave)
             reinterpret_cast<uint4 *>(lhist)[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -326,6 +427,8 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
     // blocks per wave; the workgroup's waves interleave over its contiguous range of blocks
     const int bpw = BPW ? BPW : (int)((n_blocks + (int64_t)gridDim.x * WAVES - 1) /
                                       ((int64_t)gridDim.x * WAVES));
+    // the slices need the workgroup's range staged whole in LDS (the host launches them so)
+    const bool stage = HIST && a.slice_ent && bpw * WAVES * 32 <= kSliceSpan;
     // this lane's byte offsets inside a block (contiguous 1 KB pieces)
     uint32_t lane_off[KB::NP];
 #pragma unroll
@@ -462,8 +565,11 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
                 // each key once (the moved-back last block skips the rows it repeats), middle
                 // region only
                 const int64_t row = cb.row0 + n;
-                if (cb.live && row >= cb.fresh && row >= mid_lo && row < mid_hi)
+                if (cb.live && row >= cb.fresh && row >= mid_lo && row < mid_hi) {
                     atomicAdd(&lhist[order_key(part[0]) >> 21], 1u);
+                    // block `it` of wave w is block it * WAVES + w of the workgroup's range
+                    if (stage) lsc[stage_index(it * WAVES + wv_id, (int)(row - cb.fresh))] = part[0];
+                }
             }
             if (full) {
 #pragma unroll
@@ -502,18 +608,26 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         // coarse sums of 64 bins first; only the groups that hold keys (a few of the 32) have
         // their 64 fine bins written -- the reader ignores the fine bins of an empty group
         __shared__ uint32_t lcoarse[32];
-        if (threadIdx.x < 32) {
-            const uint4 *h4 = reinterpret_cast<const uint4 *>(lhist + 64 * threadIdx.x);
-            uint32_t c = 0;
+        if (stage) {
+            // the workgroup's own blocks: positions [x * span, (x + 1) * span) of the row
+            const int64_t span = (int64_t)bpw * WAVES * 32, o_base = (int64_t)blockIdx.x * span;
+            slice_compact<WAVES>(a, lhist, lcoarse, lsc, slice, o_base, max(o_base, mid_lo),
+                                 min(o_base + span, mid_hi));
+        } else {
+            if (threadIdx.x < 32) {
+                const uint4 *h4 = reinterpret_cast<const uint4 *>(lhist + 64 * threadIdx.x);
+                uint32_t c = 0;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint4 v = h4[i];
-                c += v.x + v.y + v.z + v.w;
+                for (int i = 0; i < 16; ++i) {
+                    const uint4 v = h4[i];
+                    c += v.x + v.y + v.z + v.w;
+                }
+                lcoarse[threadIdx.x] = c;
             }
-            lcoarse[threadIdx.x] = c;
-            a.hist_coarse[slice * 32 + threadIdx.x] = c;
+            __syncthreads();
         }
-        __syncthreads();
+        // the global stores come last: a barrier after a store waits until it completes
+        if (threadIdx.x < 32) a.hist_coarse[slice * 32 + threadIdx.x] = lcoarse[threadIdx.x];
         uint4 *hf = reinterpret_cast<uint4 *>(a.hist_fine + slice * HBINS);
         for (int i = threadIdx.x; i < HBINS / 4; i += WAVES * kWave)
             if (lcoarse[i / 16]) hf[i] = reinterpret_cast<const uint4 *>(lhist)[i];
@@ -925,6 +1039,12 @@ hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int d, uint8_t 
 }
 
 hipError_t launch_scores(const ScoreArgs &a, hipStream_t stream) { return dispatch(a, stream, false); }
+
+int64_t score_hist_span(const ScoreArgs &a, int groups)
+{
+    const int64_t n_blocks = (a.n_out + 31) / 32, per = (int64_t)groups * STREAM_WAVES;
+    return (n_blocks + per - 1) / per * STREAM_WAVES * 32;
+}
 
 int score_hist_groups(const ScoreArgs &a)
 {

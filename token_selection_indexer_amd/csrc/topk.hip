@@ -1353,6 +1353,150 @@ __global__ __launch_bounds__(NT) void chunk_finish_kernel(SelectArgs a, ChunkWs 
                           ws.cid + base * CHUNK_CAP, ws.n_chunks);
 }
 
+// The fused decode path where the row's scoring workgroups number at most one per wave of this
+// block, one workgroup per row.  Scoring workgroup x kept, in its slice, every middle-region key
+// of its range in bins >= its local bin L_x, in position order.  With Lmax the largest L_x, every
+// slice holds all of its range's keys in bins >= Lmax, so the slices' entries in bins >= Lmax are
+// exactly the row's keys there.  When they number at least `need` (and fit the buffer) the row's
+// `need` best are among them: wave x counts its slice's entries in bins >= Lmax, a block scan of
+// the counts places them (position order = workgroup order), and the buffer is selected exactly.
+// Otherwise the row's threshold bin G comes from the scoring launch's histograms: a slice with
+// L_x <= G provides its range's keys in bins >= G, any other range is read from the score row.
+// A row whose bins >= G exceed the buffer takes the one-workgroup path.
+struct SliceWs {
+    const uint32_t *hist_fine, *hist_coarse;
+    const int4 *hdr; // per scoring workgroup: {L, count, range begin, range end}
+    const uint2 *ent; // per scoring workgroup: kSliceCap x {score bits, position}
+    int groups;
+};
+
+constexpr int SLE = kSliceCap / kWave; // slice entries per lane
+constexpr int SLE_FIRST = SLE / 2;     // loaded before the count is known
+
+__global__ __launch_bounds__(NT) void slice_finish_kernel(SelectArgs a, SliceWs ws)
+{
+    __shared__ Smem sm;
+    const int64_t row = blockIdx.x;
+    Row r;
+    int32_t *dst;
+    int need;
+    if (!setup_row(a, row, r, dst, need, true)) return;
+    const int l = lane_id(), x = wave_id();
+    const bool has = x < ws.groups; // wave-uniform
+    const int64_t sx = row * ws.groups + x;
+    // the first half of the slots is loaded with the header (slots past the count hold stale
+    // values and are ignored); the rest only for a slice that holds more
+    int4 h = make_int4(0, 0, 0, 0);
+    uint2 e[SLE];
+    const uint2 *pe = ws.ent + sx * kSliceCap;
+    if (has) {
+        h = ws.hdr[sx];
+#pragma unroll
+        for (int u = 0; u < SLE_FIRST; ++u) e[u] = pe[u * kWave + l];
+    }
+    const bool valid = !has || (h.y >= 0 && h.y <= kSliceCap); // wave-uniform
+    if (has && h.y > SLE_FIRST * kWave) {
+#pragma unroll
+        for (int u = SLE_FIRST; u < SLE; ++u) e[u] = pe[u * kWave + l];
+    }
+    int *cnt = sm.cnt, *lbin = sm.cnt + NW; // NW counts, NW bins (sm.cnt holds ITEMS * NW)
+    if (l == 0) lbin[x] = has ? (valid ? h.x : NBIN) : 0;
+    __syncthreads();
+    // lane i < groups reads slice i's entry (here and for the counts below)
+    const uint32_t lmax = wave_reduce_u<true>(l < ws.groups ? (uint32_t)lbin[l] : 0u);
+    // a slice's entries in bins >= T, in slot order, as (take, key, id) to `emit`
+    auto slice = [&](uint32_t T, auto &&emit) {
+#pragma unroll
+        for (int u = 0; u < SLE; ++u) {
+            if (u >= SLE_FIRST && h.y <= SLE_FIRST * kWave) break; // wave-uniform
+            const uint32_t key = order_key(__uint_as_float(e[u].x));
+            emit(u * kWave + l < h.y && (key >> 21) >= T, key, (int32_t)e[u].y);
+        }
+    };
+    // the range's keys in bins >= T from the score row, four rounds of 64 positions in flight
+    auto scan = [&](uint32_t T, auto &&emit) {
+        for (int64_t p0 = h.z; p0 < h.w; p0 += 4 * kWave) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t p = p0 + u * kWave + l;
+                v[u] = p < h.w ? r.sc[p] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t p = p0 + u * kWave + l;
+                const uint32_t key = order_key(v[u]);
+                emit(p < h.w && (key >> 21) >= T, key, (int32_t)p);
+            }
+        }
+    };
+    int c = 0;
+    auto count = [&](bool tk, uint32_t, int32_t) { c += (int)__popcll(__ballot(tk)); };
+    uint32_t pos = 0;
+    auto put = [&](bool tk, uint32_t key, int32_t id) {
+        const uint64_t m = __ballot(tk);
+        if (tk) {
+            const uint32_t slot = pos + __builtin_amdgcn_mbcnt_hi(
+                                            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (slot < (uint32_t)CAP) {
+                sm.buf_key[slot] = key;
+                sm.buf_id[slot] = id;
+            }
+        }
+        pos += (uint32_t)__popcll(m);
+    };
+    // counts of every wave -> this wave's offset and the total (one barrier)
+    auto place = [&](int &total) {
+        if (l == 0) cnt[x] = c;
+        __syncthreads();
+        const int ci = l < ws.groups ? cnt[l] : 0;
+        const int inc = wave_inclusive_scan(ci);
+        total = __builtin_amdgcn_readlane(inc, kWave - 1);
+        const int xu = __builtin_amdgcn_readfirstlane(x);
+        pos = (uint32_t)(__builtin_amdgcn_readlane(inc, xu) - __builtin_amdgcn_readlane(ci, xu));
+    };
+    int nbuf = -1, total = 0;
+    if (lmax < (uint32_t)NBIN) {
+        if (has) slice(lmax, count);
+        place(total);
+        if (total >= need && total <= CAP) {
+            if (has && c > 0) slice(lmax, put);
+            __syncthreads();
+            nbuf = total;
+        } else {
+            __syncthreads(); // every wave has read the counts before they are rewritten
+        }
+    }
+    if (nbuf < 0) {
+        const Digit g = hist_threshold<NT>(sm.hist, sm.scratch, ws.hist_fine, ws.hist_coarse,
+                                           ws.groups, row, need);
+        const uint32_t Tg = g.d >= 0 ? (uint32_t)g.d << 21 : 0u;
+        if (!(g.d >= 0 && g.above + g.at <= CAP && Tg > order_key(-INFINITY))) {
+            nbuf = prepare_buf(sm, r, need, dst);
+        } else {
+            const uint32_t G = (uint32_t)g.d;
+            const bool from_slice = valid && h.x <= g.d; // wave-uniform
+            c = 0;
+            if (has) {
+                if (from_slice)
+                    slice(G, count);
+                else
+                    scan(G, count);
+            }
+            place(total);
+            nbuf = min(total, CAP);
+            if (has && c > 0) {
+                if (from_slice)
+                    slice(G, put);
+                else
+                    scan(G, put);
+            }
+            __syncthreads();
+        }
+    }
+    if (nbuf >= 0) select_from_buf(sm, nbuf, need, dst);
+}
+
 bool use_chunked(const SelectArgs &a)
 {
     const int64_t rows = (int64_t)a.batch * a.n_q;
@@ -1373,6 +1517,20 @@ size_t select_workspace_bytes(int64_t rows, int64_t n_in, int mode)
     const int64_t nc = (n_in + CHUNK - 1) / CHUNK;
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
     return r256(rows * nc * 4) + 2 * r256(rows * nc * CHUNK_CAP * 4);
+}
+
+int select_slice_groups_max() { return NW; }
+
+hipError_t launch_select_slices(const SelectArgs &a, const uint32_t *hist_fine,
+                                const uint32_t *hist_coarse, const int4 *slice_hdr,
+                                const uint2 *slice_ent, int groups, hipStream_t stream)
+{
+    const int64_t rows = (int64_t)a.batch * a.n_q;
+    if (rows == 0) return hipSuccess;
+    if (a.cand_ids || a.mode != SELECT_SI || groups < 1 || groups > NW) return hipErrorInvalidValue;
+    const SliceWs w{hist_fine, hist_coarse, slice_hdr, slice_ent, groups};
+    hipLaunchKernelGGL(slice_finish_kernel, dim3((unsigned)rows), dim3(NT), 0, stream, a, w);
+    return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectArgs &a, void *ws, hipStream_t stream)
