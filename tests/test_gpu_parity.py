@@ -196,6 +196,45 @@ def test_select_sampled_rows_exact(ties):
 
 
 @pytest.mark.parametrize("ties", ["none", "zeros", "coarse", "const", "ramp", "inf"])
+def test_select_register_rows_exact(ties):
+    """Flat rows past the LDS buffer but within 16 elements per thread of the one-workgroup path
+    are read once into registers and histogrammed whole (heavy ties fall back to the streaming
+    path).  Lengths around both limits; 12001 lacks 16-byte rows and 17500 is past the limit
+    (the streaming paths); rows with V <= k and just past it."""
+    B, T = 2, 3
+    k, S, W = 2048, 64, 960
+    for L in (9000, 12000, 12001, 16384, 17400, 17500):
+        sc = inputs.synthetic_scores(B * T, L, seed=17, ties=ties, device=DEV).reshape(B, T, L)
+        for pos0 in (L - T, 2046, 9000 - T):
+            idx = lsa.topk_select(sc, k, S, W, kv_len=L, q_pos0=pos0).cpu().numpy()
+            V = ref.valid_lengths(L, pos0, T)
+            for b in range(B):
+                expect = ref.select(sc[b].cpu().numpy(), V, k, S, W)
+                assert np.array_equal(idx[b], expect), (ties, L, pos0, b)
+
+
+def test_select_hi_candidate_rows_exact():
+    """Candidate rows of Hierarchical Indexing's size (16384 candidates: past the LDS buffer,
+    sampled on the one-workgroup path): holes, and a row with fewer candidates than the dynamic
+    budget."""
+    B, n = 3, 16384
+    k, S, W = 2048, 64, 960
+    sc = inputs.synthetic_scores(B, n, seed=19, ties="coarse", device=DEV).reshape(B, 1, n)
+    g = torch.Generator().manual_seed(2)
+    ids = torch.stack([torch.sort(torch.randperm(1 << 20, generator=g)[:n]).values for _ in range(B)])
+    ids = ids.to(torch.int32).reshape(B, 1, n)
+    ids[:, :, 5::9] = -1
+    ids[2, 0, 700:] = -1  # fewer candidates than the dynamic budget
+    idx = lsa.topk_select(sc, k, S, W, kv_len=1 << 20, q_pos0=(1 << 20) - 1,
+                          cand_ids=ids.to(DEV)).cpu().numpy()
+    for b in range(B):
+        expect = ref.select(sc[b].cpu().numpy(), np.array([1 << 20]), k, S, W,
+                            cand_ids=ids[b].numpy())
+        assert np.array_equal(idx[b], expect), b
+        check_si_layout(idx[b, 0], 1 << 20, k, S, W, cand_ids=ids[b, 0].numpy())
+
+
+@pytest.mark.parametrize("ties", ["none", "zeros", "coarse", "const", "ramp", "inf"])
 def test_select_chunked_rows_exact(ties):
     """Few long rows (the chunked path), every tie pattern: heavy ties overflow the per-chunk
     slices and fall back to one workgroup per row; rows with V <= k take everything."""

@@ -493,17 +493,19 @@ __device__ __forceinline__ void load_keys(const Smem &sm, int nbuf, uint32_t (&k
 // eq_take keys == T in position order, into dst[0, limit).  Key 0 never competes.  eq_all: every
 // key == T is taken (eq_take is their count), i.e. simply key >= T.  One exchange of per-wave
 // counts orders the picks.  Returns the number taken (which may exceed limit).
+template <int NI>
 __device__ __forceinline__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq_take, int32_t *dst,
-                                          int limit, bool eq_all, const uint32_t (&k)[BI])
+                                          int limit, bool eq_all, const uint32_t (&k)[NI],
+                                          const int32_t *ids)
 {
     const int lane = lane_id(), w = wave_id();
     const int wu = __builtin_amdgcn_readfirstlane(w);
     const int nu = buf_items(nbuf);
-    int32_t idv[BI];
+    int32_t idv[NI];
 #pragma unroll
-    for (int u = 0; u < BI; ++u) {
+    for (int u = 0; u < NI; ++u) {
         const int i = buf_index(nu, u);
-        idv[u] = u < nu && i < nbuf ? sm.buf_id[i] : 0;
+        idv[u] = u < nu && i < nbuf ? ids[i] : 0;
     }
     auto put = [&](uint32_t slot, int32_t v) { // 32-bit offset from the uniform base
         if (slot < (uint32_t)limit) *reinterpret_cast<int32_t *>(reinterpret_cast<char *>(dst) + slot * 4u) = v;
@@ -511,14 +513,12 @@ __device__ __forceinline__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq
     auto below = [](uint64_t m) {
         return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
     };
+    // the masks are taken twice (count, then place) rather than kept: NI of them per kind would
+    // hold 2 NI scalar registers each
     if (eq_all) {
-        uint64_t mg[BI];
         int cg = 0;
 #pragma unroll
-        for (int u = 0; u < BI; ++u) {
-            mg[u] = __ballot(k[u] != 0u && k[u] >= T);
-            cg += (int)__popcll(mg[u]);
-        }
+        for (int u = 0; u < NI; ++u) cg += (int)__popcll(__ballot(k[u] != 0u && k[u] >= T));
         if (lane == 0) sm.cnt[w] = cg;
         __syncthreads();
         // lane q < NW holds wave q's count; the prefix sum gives this wave's base
@@ -526,21 +526,20 @@ __device__ __forceinline__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq
         const int ick = wave_inclusive_scan(ck);
         uint32_t pos = (uint32_t)(__builtin_amdgcn_readlane(ick, wu) - __builtin_amdgcn_readlane(ck, wu));
 #pragma unroll
-        for (int u = 0; u < BI; ++u) {
+        for (int u = 0; u < NI; ++u) {
             if (u >= nu) break;
-            if (k[u] != 0u && k[u] >= T) put(pos + below(mg[u]), idv[u]);
-            pos += (uint32_t)__popcll(mg[u]);
+            const bool tk = k[u] != 0u && k[u] >= T;
+            const uint64_t mg = __ballot(tk);
+            if (tk) put(pos + below(mg), idv[u]);
+            pos += (uint32_t)__popcll(mg);
         }
         return __builtin_amdgcn_readlane(ick, NW - 1);
     }
-    uint64_t mg[BI], me[BI];
     int cg = 0, ce = 0;
 #pragma unroll
-    for (int u = 0; u < BI; ++u) {
-        mg[u] = __ballot(k[u] > T);
-        me[u] = __ballot(k[u] != 0u && k[u] == T);
-        cg += (int)__popcll(mg[u]);
-        ce += (int)__popcll(me[u]);
+    for (int u = 0; u < NI; ++u) {
+        cg += (int)__popcll(__ballot(k[u] > T));
+        ce += (int)__popcll(__ballot(k[u] != 0u && k[u] == T));
     }
     if (lane == 0) {
         sm.cnt[w] = cg;
@@ -557,13 +556,14 @@ __device__ __forceinline__ int select_buf(Smem &sm, int nbuf, uint32_t T, int eq
     int pos = bg + max(0, min(eq_take, be));
     int er = be; // equal rank of the wave's next equal key
 #pragma unroll
-    for (int u = 0; u < BI; ++u) {
+    for (int u = 0; u < NI; ++u) {
         if (u >= nu) break;
-        uint64_t mt = mg[u];
-        if (me[u]) {
-            const int r = er + (int)below(me[u]);
-            mt |= __ballot(((me[u] >> lane) & 1u) && r < eq_take);
-            er += (int)__popcll(me[u]);
+        uint64_t mt = __ballot(k[u] > T);
+        const uint64_t me = __ballot(k[u] != 0u && k[u] == T);
+        if (me) {
+            const int r = er + (int)below(me);
+            mt |= __ballot(((me >> lane) & 1u) && r < eq_take);
+            er += (int)__popcll(me);
         }
         if ((mt >> lane) & 1u) put((uint32_t)pos + below(mt), idv[u]);
         pos += (int)__popcll(mt);
@@ -600,9 +600,10 @@ __device__ __forceinline__ uint32_t wave_reduce_u(uint32_t x)
 // rel >> s0 with the smallest s0 that fits 2048 bins, then the next (up to) 11 bits below, each
 // among the keys of the bins chosen so far -- down to a single key value if need be, of which
 // the needed count of copies is taken.
+template <int NI>
 __device__ __forceinline__ void select_in_buf_range(Smem &sm, int nbuf, int need, int32_t *dst,
                                                     uint32_t kmin, uint32_t kmax,
-                                                    const uint32_t (&k)[BI])
+                                                    const uint32_t (&k)[NI], const int32_t *ids)
 {
     const float fmin = key_to_float(kmin), fmax = key_to_float(kmax);
     const float span = fmax - fmin;
@@ -630,7 +631,7 @@ __device__ __forceinline__ void select_in_buf_range(Smem &sm, int nbuf, int need
         const bool use_lin = lin && !lin_done;
         const uint32_t dmask = next_hi == 32 ? ~0u : (1u << (next_hi - next_sh)) - 1u;
 #pragma unroll
-        for (int u = 0; u < BI; ++u)
+        for (int u = 0; u < NI; ++u)
             if (u < nu && k[u] != 0u && in_bin(k[u]))
                 atomicAdd(&sm.hist[use_lin ? fdigit(k[u]) : ((k[u] - kmin) >> next_sh) & dmask], 1);
         __syncthreads();
@@ -665,7 +666,7 @@ __device__ __forceinline__ void select_in_buf_range(Smem &sm, int nbuf, int need
     } else if (g.at <= kWave) { // rank the bin's keys: the rem-th largest is the need-th
         uint32_t *small = sm.small;
 #pragma unroll
-        for (int u = 0; u < BI; ++u)
+        for (int u = 0; u < NI; ++u)
             if (u < nu && k[u] != 0u && in_bin(k[u])) small[atomicAdd(&sm.scratch[NW + 4], 1)] = k[u];
         __syncthreads();
         if (threadIdx.x < kWave) rank_small(small, g.at, rem, sm.scratch + NW + 5);
@@ -678,7 +679,7 @@ __device__ __forceinline__ void select_in_buf_range(Smem &sm, int nbuf, int need
         eq_take = rem;
         eq_all = rem == g.at;
     }
-    const int got = select_buf(sm, nbuf, T, eq_take, dst, need, eq_all, k);
+    const int got = select_buf<NI>(sm, nbuf, T, eq_take, dst, need, eq_all, k, ids);
     if (take_all)
         for (int i = min(got, need) + (int)threadIdx.x; i < need; i += NT) dst[i] = -1;
 }
@@ -730,7 +731,7 @@ __device__ __forceinline__ void select_from_buf(Smem &sm, int nbuf, int need, in
     clear_hist_nobar(sm);
     __syncthreads();
     block_extremes(sm, kmin, kmax);
-    select_in_buf_range(sm, nbuf, need, dst, kmin, kmax, k);
+    select_in_buf_range<BI>(sm, nbuf, need, dst, kmin, kmax, k, sm.buf_id);
 }
 
 // ---- streaming passes: each wave owns a contiguous segment of the row (no block barriers) ----
@@ -881,6 +882,80 @@ __device__ __forceinline__ bool collect_row_seg(Smem &sm, const Row &r, uint32_t
 // Gathers into the LDS buffer a position-ordered set of the row's elements that contains its
 // `need` best (need > 0) and returns its size, with a barrier passed after the last write -- or
 // completes the row itself (everything competing taken, or heavy ties) and returns -1.
+// Flat rows of at most NT * RI elements past the buffer (Hierarchical Indexing's page rows, for
+// one) are read once, into registers: thread t holds positions a0 + RI t + [0, RI) (16-byte
+// loads; thread order is position order).  An LDS histogram of every element's top 11 key bits
+// gives the row's exact threshold bin (refined by the next 11 bits when the bin would overflow
+// the buffer), and what lies at or above it is compacted into the buffer straight from the
+// registers (the streaming paths pass over the row twice: a sample, then a collection).
+constexpr int RI = 16;
+constexpr int REGS_FALLBACK = -2;
+
+// The buffer count, -1 when every competing element was written to dst (at most `need`), or
+// REGS_FALLBACK when even the second digit leaves too many to fit the buffer.  Rows with 16-byte
+// vector access and hi - (lo & ~3) <= NT * RI only.
+__device__ __forceinline__ int prepare_buf_regs(Smem &sm, const Row &r, int need, int32_t *dst)
+{
+    const int64_t a0 = r.lo & ~int64_t(3);
+    const int64_t last = (r.hi - 1) & ~int64_t(3); // the last quad holding an element
+    const int64_t p0 = a0 + (int64_t)threadIdx.x * RI;
+    float f[RI];
+    // every quad is loaded (clamped to the last one) before any is used, masked afterwards
+#pragma unroll
+    for (int q = 0; q < RI / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4 *>(r.sc + min(p0 + 4 * q, last));
+        f[4 * q] = v.x;
+        f[4 * q + 1] = v.y;
+        f[4 * q + 2] = v.z;
+        f[4 * q + 3] = v.w;
+    }
+    clear_hist(sm);
+    uint32_t key[RI];
+#pragma unroll
+    for (int j = 0; j < RI; ++j) {
+        const int64_t p = p0 + j;
+        key[j] = p >= r.lo && p < r.hi ? order_key(f[j]) : 0u;
+        if (key[j]) atomicAdd(&sm.hist[key[j] >> 21], 1);
+    }
+    __syncthreads();
+    const Digit g = find_digit_w0<NT>(sm.hist, need, sm.scratch);
+    const bool all = g.total <= need;
+    uint32_t T = all ? 0u : (uint32_t)g.d << 21;
+    if (!all && g.above + g.at > CAP) { // uniform: refine within bin d by key bits 20..10
+        clear_hist(sm);
+#pragma unroll
+        for (int j = 0; j < RI; ++j)
+            if (key[j] && (key[j] >> 21) == (uint32_t)g.d) atomicAdd(&sm.hist[(key[j] >> 10) & (NBIN - 1)], 1);
+        __syncthreads();
+        const Digit g2 = find_digit_w0<NT>(sm.hist, need - g.above, sm.scratch);
+        if (g.above + g2.above + g2.at > CAP) return REGS_FALLBACK; // heavy ties
+        T |= (uint32_t)g2.d << 10;
+    }
+    uint32_t take = 0; // bit j: element j competes and lies at or above the threshold
+#pragma unroll
+    for (int j = 0; j < RI; ++j) take |= (uint32_t)(key[j] != 0u && key[j] >= T) << j;
+    int total;
+    int slot = block_exclusive_scan<NW>(__popc(take), sm.scratch, &total);
+#pragma unroll
+    for (int j = 0; j < RI; ++j) {
+        if (!((take >> j) & 1u)) continue;
+        if (all) {
+            dst[slot] = (int32_t)(p0 + j);
+        } else {
+            sm.buf_key[slot] = key[j];
+            sm.buf_id[slot] = (int32_t)(p0 + j);
+        }
+        ++slot;
+    }
+    if (all) {
+        for (int i = total + (int)threadIdx.x; i < need; i += NT) dst[i] = -1;
+        return -1;
+    }
+    __syncthreads();
+    return total;
+}
+
+template <bool REGS = false>
 __device__ __forceinline__ int prepare_buf(Smem &sm, const Row &r, int need, int32_t *dst)
 {
     const int64_t len = r.hi - r.lo;
@@ -902,6 +977,12 @@ __device__ __forceinline__ int prepare_buf(Smem &sm, const Row &r, int need, int
         }
         __syncthreads();
         return n4;
+    }
+    if constexpr (REGS) {
+        if (!r.ids && r.vec && r.hi - a0 <= (int64_t)NT * RI) {
+            const int n = prepare_buf_regs(sm, r, need, dst);
+            if (n != REGS_FALLBACK) return n;
+        }
     }
     // long rows: a sampled threshold lets one pass collect everything at or above it
     const uint32_t T = len >= SAMPLE_MIN
@@ -1001,7 +1082,7 @@ __device__ __forceinline__ bool setup_row(const SelectArgs &a, int64_t row, Row 
 
 // CAND: candidate rows (ids from the list); flat rows get a null id pointer the compiler can see,
 // so the flat kernel carries no id loads.
-template <bool CAND>
+template <bool CAND, bool REGS = false>
 __device__ __forceinline__ void select_one_row(const SelectArgs &a)
 {
     __shared__ Smem sm;
@@ -1010,7 +1091,7 @@ __device__ __forceinline__ void select_one_row(const SelectArgs &a)
     int need;
     if (!setup_row(a, blockIdx.x, r, dst, need, true)) return;
     if (!CAND) r.ids = nullptr;
-    const int nbuf = prepare_buf(sm, r, need, dst);
+    const int nbuf = prepare_buf<REGS>(sm, r, need, dst);
     if (nbuf >= 0) select_from_buf(sm, nbuf, need, dst);
 }
 
@@ -1019,6 +1100,10 @@ __device__ __forceinline__ void select_one_row(const SelectArgs &a)
 __global__ __launch_bounds__(NT, 8) void select_kernel_flat(SelectArgs a) { select_one_row<false>(a); }
 
 __global__ __launch_bounds__(NT) void select_kernel_cand(SelectArgs a) { select_one_row<true>(a); }
+
+// Flat rows of CAP < n_in <= NT * RI elements: the register-resident path (one pass over the
+// row).  Few such rows run at once (page recall), so the kernel may use more registers.
+__global__ __launch_bounds__(NT) void select_kernel_regs(SelectArgs a) { select_one_row<false, true>(a); }
 
 constexpr int HGROUPS = 32; // coarse sums of 64 bins each in the scoring launch's histograms
 
@@ -1546,6 +1631,8 @@ hipError_t launch_select_hist(const SelectArgs &a, void *ws, const uint32_t *his
     if (!use_chunked(a)) {
         if (a.cand_ids)
             hipLaunchKernelGGL(select_kernel_cand, dim3((unsigned)rows), dim3(NT), 0, stream, a);
+        else if (a.n_in > CAP && a.n_in <= (int64_t)NT * RI)
+            hipLaunchKernelGGL(select_kernel_regs, dim3((unsigned)rows), dim3(NT), 0, stream, a);
         else
             hipLaunchKernelGGL(select_kernel_flat, dim3((unsigned)rows), dim3(NT), 0, stream, a);
         return hipGetLastError();
