@@ -933,7 +933,9 @@ template <bool FP8, int D, int H>
 hipError_t launch_fine(const ScoreArgs &a, hipStream_t st)
 {
     constexpr int MT = H > 32 ? 2 : 1;
-    constexpr int WAVES = 4, BPW = 4;
+    // two blocks per wave: both in flight from the start (Hierarchical Indexing's candidate rows
+    // are short, so the launch is one round of latency, not a chain of them)
+    constexpr int WAVES = 4, BPW = 2;
     const int64_t n_blocks = (a.n_out + 31) / 32;
     dim3 grid((unsigned)((n_blocks + WAVES * BPW - 1) / (WAVES * BPW)), (unsigned)a.n_q,
               (unsigned)a.batch);
