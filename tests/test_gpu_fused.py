@@ -74,14 +74,15 @@ def test_fused_decode_128k_full():
 
 # batch x blocks of 32 keys reach the long scoring launch (at least 65536 blocks), which is the
 # one that emits the histograms.  32 query rows or more with at most 8192 keys per scoring
-# workgroup take the slices (32 x 70000, and the two 16 x 2-query cases); the others read the
-# rows through the histograms.
+# workgroup take the slices (32 x 70000, the two 16 x 2-query cases, 64 x 65536 with 8 scoring
+# workgroups per row); the others read the rows through the histograms.
 @pytest.mark.parametrize("kd,H,L,back,nq,B", [("fp8", 64, 131072 - 5, 0, 1, 16),
                                               ("bf16", 64, 70000, 3000, 1, 32),
                                               ("fp8", 32, 100003, 0, 2, 11),
                                               ("bf16", 32, 90000, 17, 1, 24),
                                               ("fp8", 64, 131072 - 77, 5, 2, 16),
-                                              ("bf16", 32, 120001, 0, 2, 16)])
+                                              ("bf16", 32, 120001, 0, 2, 16),
+                                              ("fp8", 64, 65536, 0, 1, 64)])
 def test_fused_shapes(kd, H, L, back, nq, B):
     wl = Workload(name="f", index=IndexShape(batch=B, n_q=nq, kv_len=L, q_pos0=L - nq - back,
                                              heads=H, head_dim=128, key_dtype=kd),
