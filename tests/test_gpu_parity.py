@@ -213,13 +213,14 @@ def test_select_register_rows_exact(ties):
                 assert np.array_equal(idx[b], expect), (ties, L, pos0, b)
 
 
-def test_select_hi_candidate_rows_exact():
+@pytest.mark.parametrize("ties", ["coarse", "none", "const", "ramp", "inf"])
+def test_select_hi_candidate_rows_exact(ties):
     """Candidate rows of Hierarchical Indexing's size (16384 candidates: past the LDS buffer,
-    sampled on the one-workgroup path): holes, and a row with fewer candidates than the dynamic
-    budget."""
+    sampled on the one-workgroup path): holes, a row with fewer candidates than the dynamic
+    budget, and every tie pattern's scores."""
     B, n = 3, 16384
     k, S, W = 2048, 64, 960
-    sc = inputs.synthetic_scores(B, n, seed=19, ties="coarse", device=DEV).reshape(B, 1, n)
+    sc = inputs.synthetic_scores(B, n, seed=19, ties=ties, device=DEV).reshape(B, 1, n)
     g = torch.Generator().manual_seed(2)
     ids = torch.stack([torch.sort(torch.randperm(1 << 20, generator=g)[:n]).values for _ in range(B)])
     ids = ids.to(torch.int32).reshape(B, 1, n)
