@@ -1499,19 +1499,21 @@ __global__ __launch_bounds__(NT) void slice_finish_kernel(SelectArgs a, SliceWs 
         }
     };
     // the range's keys in bins >= T from the score row, four rounds of 64 positions in flight
+    // (the range is clamped into the row's middle region, which it always lies in)
+    const int64_t zlo = max((int64_t)h.z, r.lo), zhi = min((int64_t)h.w, r.hi);
     auto scan = [&](uint32_t T, auto &&emit) {
-        for (int64_t p0 = h.z; p0 < h.w; p0 += 4 * kWave) {
+        for (int64_t p0 = zlo; p0 < zhi; p0 += 4 * kWave) {
             float v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int64_t p = p0 + u * kWave + l;
-                v[u] = p < h.w ? r.sc[p] : 0.0f;
+                v[u] = p < zhi ? r.sc[p] : 0.0f;
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int64_t p = p0 + u * kWave + l;
                 const uint32_t key = order_key(v[u]);
-                emit(p < h.w && (key >> 21) >= T, key, (int32_t)p);
+                emit(p < zhi && (key >> 21) >= T, key, (int32_t)p);
             }
         }
     };
