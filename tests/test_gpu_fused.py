@@ -170,6 +170,29 @@ def test_unfused_shape_matches():
     _case(wl)
 
 
+def test_fused_slices_workspace_across_shapes():
+    """One workspace through sliced calls of different shapes (32 x 128K, then 32 x 70000 and 16
+    x 2 queries): every slice header and entry the selection reads is written by the scoring
+    launch of the same call, whatever the previous call left."""
+    ws = lsa.Workspace()
+    shapes = [(131072, 1, 32, 81), (70000, 1, 32, 82), (120001, 2, 16, 83), (131072, 1, 32, 84)]
+    for L, nq, B, seed in shapes:
+        wl = Workload(name="fw", index=IndexShape(batch=B, n_q=nq, kv_len=L, q_pos0=L - nq,
+                                                  heads=64, head_dim=128, key_dtype="fp8"),
+                      budget=Budget(k=2048, sink=64, window=960), attn=DECODE_128K.attn, seed=seed)
+        s, b = wl.index, wl.budget
+        assert _is_fused(wl)
+        inp = inputs.index_inputs(wl, DEV)
+        sc1, i1 = lsa.index_select(inp["q"], inp["w"], inp["keys"], inp["scale"], b.k, b.sink,
+                                   b.window, q_pos0=s.q_pos0, ws=ws)
+        sc2, i2 = _separate(inp["q"], inp["w"], inp["keys"], inp["scale"], b, s.q_pos0)
+        torch.cuda.synchronize()
+        assert torch.equal(sc1.view(torch.int32), sc2.view(torch.int32)), (L, nq, B)
+        assert torch.equal(i1, i2), (L, nq, B)
+        del inp, sc1, sc2, i1, i2
+        torch.cuda.empty_cache()
+
+
 def test_fused_repeated_calls_reuse_workspace():
     """The workspace is reused across calls with stale contents from the previous call (the
     fine bins of groups that were empty are never read): identical results every time."""
