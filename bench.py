@@ -335,7 +335,8 @@ def _bwd_setup(torch, lsa, inputs, cfg):
 
     def f_attn_bwd():
         lsa.sparse_attn_backward(att["q"], att["kv"], None, idx, out, lse, d_out, a.scale,
-                                 d_v=a.d_v, d_q=grads["d_q"], d_k=grads["d_kv"])
+                                 d_v=a.d_v, d_q=grads["d_q"], d_k=grads["d_kv"], sink=b.sink,
+                                 window=b.window, q_pos0=s.q_pos0)
 
     def f_index_bwd():
         lsa.index_scores_backward(inp["q"], inp["w"], inp["keys"], idx, d_sc, q_pos0=s.q_pos0,

@@ -312,6 +312,15 @@ LSA_API lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_
  * non-latent call needs d_v != d_k.  The additions are fp32 atomics, so the order of the
  * partial sums (and the last bits) can differ between runs.
  *   shape, attn, budget, q, k, v, idx   as for lsa_sparse_attn (budget: k entries per row)
+ *   budget.sink / budget.window, shape->q_pos0: the Streaming-Aware layout the lists were
+ *           selected with (lsa_topk_select: entries [0, S) the sink rows 0..S-1, entries
+ *           [S, S+W) the window rows V_i-W .. V_i-1, V_i = min(kv_len, q_pos0 + i + 1)).  Where
+ *           an entry holds the row its position names and the query's sink and window are
+ *           disjoint, its cache-gradient share is summed over the queries that share the row
+ *           before it is added (one update per row column for many queries: the prefill
+ *           chunks' sink and window rows); every other entry is added as described above.  The
+ *           sum is the same, in another order.  Uniform batches only (no seq_len / seq_pos0);
+ *           sink = window = 0 adds every entry per query.
  *   out     [B, n_q, Hq, d_v] bf16, 16-byte aligned;  lse  [B, n_q, Hq] fp32 (required)
  *   d_out   [B, n_q, Hq, d_v] bf16, 16-byte aligned
  *   d_q     [B, n_q, Hq, d_qk] fp32

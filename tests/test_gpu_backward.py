@@ -90,9 +90,12 @@ def _check(label, gpu, want, M, MD, rel):
                            f"gpu {gpu[tuple(bad[0])]}, ref {want[tuple(bad[0])]}, tol {tol[tuple(bad[0])]}")
 
 
-def _attn_case(B, T, H, L, k, latent, dqk=576, dv=512, seed=0, seq_lens=None, pad=0.0):
+def _attn_case(B, T, H, L, k, latent, dqk=576, dv=512, seed=0, seq_lens=None, pad=0.0,
+               lists=None, si=None):
     """Random bf16 q / cache / output gradient, index lists with skipped (-1), out-of-range and
-    repeated entries; forward and backward on the GPU; oracle backward per sequence."""
+    repeated entries (or the given lists); forward and backward on the GPU; oracle backward per
+    sequence.  si = (sink, window, q_pos0): the lists' Streaming-Aware layout, passed on to the
+    backward call."""
     g = _gen(seed)
     q = torch.randn((B, T, H, dqk), generator=g).to(torch.bfloat16)
     if latent:
@@ -109,13 +112,17 @@ def _attn_case(B, T, H, L, k, latent, dqk=576, dv=512, seed=0, seq_lens=None, pa
     if k > 8:
         idx[:, :, 3] = idx[:, :, 5]          # a row selected twice by one query
         idx[:, 0, 7] = L + 3                 # past the cache: skipped
+    if lists is not None:
+        idx = torch.from_numpy(lists)
     tau = 1.0 / math.sqrt(dqk)
     qd, kvd, dod, idd = q.to(DEV), kv.to(DEV), dout.to(DEV), idx.to(DEV)
     vd = None if latent else v.to(DEV)
     lens = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
     out, lse = lsa.sparse_attn(qd, kvd, vd, idd, tau, d_v=dv, seq_lens=lens)
+    sink, window, q_pos0 = si if si is not None else (0, 0, 0)
     d_q, d_k, d_v = lsa.sparse_attn_backward(qd, kvd, vd, idd, out, lse, dod, tau, d_v=dv,
-                                             seq_lens=lens)
+                                             seq_lens=lens, sink=sink, window=window,
+                                             q_pos0=q_pos0)
     torch.cuda.synchronize()
     gq, gk, gv = (x.cpu().numpy().astype(np.float64) for x in (d_q, d_k, d_v))
     for b in range(B):
@@ -168,6 +175,56 @@ def test_mla_backward_prefill_rows_shared_by_many_queries():
 
 def test_mla_backward_ragged():
     _attn_case(B=3, T=2, H=16, L=700, k=96, latent=True, seed=5, seq_lens=[700, 250, 0])
+
+
+def _si_lists(B, T, L, q_pos0, k, S, W, seed):
+    """Index lists in the layout lsa_topk_select writes: with V = min(L, q_pos0 + t + 1), a
+    query with V <= k takes rows 0 .. V-1; else sink rows 0 .. S-1, window rows V-W .. V-1, then
+    distinct rows from [S, V - W) and -1 padding."""
+    rng = np.random.default_rng(seed)
+    idx = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            V = min(L, q_pos0 + t + 1)
+            if V <= k:
+                idx[b, t, :V] = np.arange(V)
+                continue
+            idx[b, t, :S] = np.arange(S)
+            idx[b, t, S:S + W] = np.arange(V - W, V)
+            pool = np.arange(S, V - W)
+            dyn = rng.choice(pool, size=min(k - S - W, pool.size), replace=False)
+            idx[b, t, S + W:S + W + dyn.size] = dyn
+    return idx
+
+
+@pytest.mark.parametrize("H", [16, 32])
+def test_mla_backward_streaming_aware_lists(H):
+    """Prefill-shaped lists in the Streaming-Aware layout, with the layout passed to the
+    backward call: the sink and window entries' cache gradient is summed row by row over the
+    queries (the key-major pass), the rest per query.  Entries that break the layout are left
+    to the per-query path: a window entry holding another row, a sink entry holding another
+    row, a skipped (-1) sink entry, and a window row selected a second time among the dynamic
+    picks (added once by each path).  Queries past the cache end (V = L for the last ones)."""
+    B, T, L, q0, k, S, W = 2, 300, 1480, 1200, 256, 16, 112
+    idx = _si_lists(B, T, L, q0, k, S, W, seed=21)
+    idx[:, 5, S + 3] = 40
+    idx[:, 7, 2] = 500
+    idx[:, 9, 1] = -1
+    idx[:, 11, S + W] = idx[:, 11, S + W - 1]
+    if H == 32:
+        B, T = 1, 120
+        idx = idx[:1, :T]
+    _attn_case(B=B, T=T, H=H, L=L, k=k, latent=True, seed=22, lists=idx, si=(S, W, q0))
+
+
+def test_mla_backward_streaming_aware_early_queries():
+    """A chunk from the start of a sequence: the first queries see fewer than k rows and take
+    all of them, so their sink entries match the layout and their window entries mostly do not;
+    the earliest have a window reaching into the sink (no entry of theirs is key-major).  64
+    sink rows (one whole block) and a 64-row window."""
+    B, T, L, q0, k, S, W = 1, 400, 400, 0, 200, 64, 64
+    idx = _si_lists(B, T, L, q0, k, S, W, seed=23)
+    _attn_case(B=B, T=T, H=16, L=L, k=k, latent=True, seed=24, lists=idx, si=(S, W, q0))
 
 
 def test_mha_backward():
@@ -294,7 +351,9 @@ def _sample_rows(kv_f64, ids):
 
 def test_backward_prefill_8k_128k_full_shape():
     """The training path at the chunked-prefill shape (8192 queries, 128K keys, k = 2048), on
-    the GPU's own selection: sampled queries' dq (all heads) and dw against the oracle, and over
+    the GPU's own selection, whose Streaming-Aware layout is passed on (the sink and window
+    entries' cache gradient goes through the key-major pass, about half of all entries): sampled
+    queries' dq (all heads) and dw against the oracle, and over
     the whole launch the identities the gradients obey exactly:
       attention  sum_r dV_r = sum_(t,h) dO_(t,h)            (softmax rows sum to one)
                  <dKV, KV> - <dq, q> = sum_(t,h) dO . out    (the logits are bilinear in q and K;
@@ -322,7 +381,8 @@ def test_backward_prefill_8k_128k_full_shape():
     dout = torch.randn(out.shape, generator=g, device=DEV).to(torch.bfloat16)
     dsc = torch.randn(idx.shape, generator=g, device=DEV)
     d_q, d_kv, _ = lsa.sparse_attn_backward(att["q"], att["kv"], None, idx, out, lse, dout,
-                                            a.scale, d_v=a.d_v)
+                                            a.scale, d_v=a.d_v, sink=b.sink, window=b.window,
+                                            q_pos0=s.q_pos0)
     di_q, di_w, di_k = lsa.index_scores_backward(inp["q"], inp["w"], inp["keys"], idx, dsc,
                                                  q_pos0=s.q_pos0)
     torch.cuda.synchronize()

@@ -647,6 +647,10 @@ lsa_status lsa_sparse_attn_backward(const lsa_index_shape *shape, const lsa_attn
     a.v_stride = attn->v_row_stride;
     a.scale = attn->scale;
     a.n_split = lsa::attn_bwd_splits(shape->batch, shape->n_q, attn->n_heads, budget.k, attn->latent);
+    a.sink = budget.sink;
+    a.window = budget.window;
+    a.q_pos0 = shape->seq_pos0 ? -1 : shape->q_pos0; // the key-major pass: uniform batches only
+    a.si = 0;
     return device_status(lsa::launch_sparse_attn_backward(a, static_cast<hipStream_t>(stream)));
 }
 

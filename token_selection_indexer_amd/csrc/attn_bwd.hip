@@ -84,6 +84,56 @@ __device__ __forceinline__ void ring_barrier()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// ---- Streaming-Aware entries: which (query, row) pairs the key-major pass takes ----
+constexpr int SRB = 64;  // cache rows per key-major workgroup
+constexpr int SQC = 128; // queries per key-major workgroup
+
+struct SiPlan {
+    int nsb;      // sink blocks: rows [SRB i, min(S, SRB (i + 1)))
+    int64_t wlo;  // window blocks follow: rows [wlo + SRB j, + SRB)
+    int64_t t_si; // first query whose sink and window are disjoint
+    int cs, cw;   // query chunks per sink block and per window block
+};
+
+__host__ __device__ __forceinline__ int64_t imin(int64_t x, int64_t y) { return x < y ? x : y; }
+__host__ __device__ __forceinline__ int64_t imax(int64_t x, int64_t y) { return x > y ? x : y; }
+
+// V_t, the valid length the selection gives query t (causal, uniform batch)
+__host__ __device__ __forceinline__ int64_t si_valid_len(const AttnBwdArgs &a, int64_t t)
+{
+    return imin(a.kv_len, a.q_pos0 + t + 1);
+}
+
+// Entry j (holding id) of the list of a query of valid length V: the key-major pass takes it
+// when the query's sink and window are disjoint and the entry holds the row the Streaming-Aware
+// layout puts there (sink row j, or window row V - W + j - S).
+__device__ __forceinline__ bool si_entry(const AttnBwdArgs &a, int64_t V, int j, int32_t id)
+{
+    if (V - a.window < a.sink) return false;
+    if (j < a.sink) return id == j;
+    if (j < a.sink + a.window) return (int64_t)id == V - a.window + (j - a.sink);
+    return false;
+}
+
+// Rows [r0, r1) of key-major block blk and the queries [t_lo, t_hi) whose sink or window can
+// reach them (V_t > r0 and V_t - W < r1 for a window block).
+__host__ __device__ __forceinline__ void si_block(const AttnBwdArgs &a, const SiPlan &p, int blk,
+                                                  int64_t &r0, int64_t &r1, int64_t &t_lo,
+                                                  int64_t &t_hi)
+{
+    if (blk < p.nsb) {
+        r0 = (int64_t)SRB * blk;
+        r1 = imin(a.sink, r0 + SRB);
+        t_lo = p.t_si;
+        t_hi = a.n_q;
+        return;
+    }
+    r0 = p.wlo + (int64_t)SRB * (blk - p.nsb);
+    r1 = imin(r0 + SRB, a.kv_len);
+    t_lo = imax(p.t_si, r0 - a.q_pos0);
+    t_hi = a.kv_len < r1 + a.window ? a.n_q : imin(a.n_q, r1 + a.window - a.q_pos0 - 1);
+}
+
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 2) void mla_attn_bwd_kernel(AttnBwdArgs a)
 {
@@ -125,6 +175,9 @@ __global__ __launch_bounds__(256, 2) void mla_attn_bwd_kernel(AttnBwdArgs a)
     const int n_rounds = c_end > c_begin ? (c_end - c_begin + BR - 1) / BR : 0;
     const int32_t *idx_row = a.idx + qrow * a.n_idx;
     const int64_t seq_rows = seq_keys(a.seq_len, b, a.kv_len);
+    // the key-major pass adds this query's Streaming-Aware entries to the cache gradient
+    const int64_t v_si = si_valid_len(a, t);
+    const bool si_q = a.si && v_si - a.window >= a.sink;
     auto id_load = [&](int round) -> int32_t { // unconditional load of a clamped entry
         const int j = c_begin + round * BR + (int)(threadIdx.x % BR);
         return idx_row[min(j, max(c_end - 1, 0))];
@@ -282,9 +335,13 @@ __global__ __launch_bounds__(256, 2) void mla_attn_bwd_kernel(AttnBwdArgs a)
             const s16x4_t sal = *reinterpret_cast<const s16x4_t *>(&sA[1][c16][4 * g4]);
             const s16x4_t pah = *reinterpret_cast<const s16x4_t *>(&pA[0][c16][4 * g4]);
             const s16x4_t pal = *reinterpret_cast<const s16x4_t *>(&pA[1][c16][4 * g4]);
-            int32_t rowid[4];
+            int32_t rowid[4]; // -1: no atomic update for this row (skipped, or key-major)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rowid[e] = ids[4 * g4 + e];
+            for (int e = 0; e < 4; ++e) {
+                rowid[e] = ids[4 * g4 + e];
+                if (si_q && rowid[e] >= 0 && si_entry(a, v_si, c_begin + i * BR + 4 * g4 + e, rowid[e]))
+                    rowid[e] = -1;
+            }
             // transposing reads: lane j of group g4 addresses row 4 g4 + j/4, columns
             // 16 T + 4 (j%4) .. +3
             const int vr = 4 * g4 + (c16 >> 2);
@@ -315,6 +372,233 @@ __global__ __launch_bounds__(256, 2) void mla_attn_bwd_kernel(AttnBwdArgs a)
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) atomicAdd(dqp + 16 * (NT * w + tt) + 4 * g4 + e, dq[tt][e]);
+}
+
+// Key-major pass over the Streaming-Aware entries.  Neighbouring queries of a prefill chunk
+// share their sink rows and most of their window rows, and the kernel above adds each of those
+// rows' gradient once per query through fp32 atomics, whose rate bounds it.  Here a workgroup
+// of 8 waves owns SRB consecutive cache rows (a block of the sink, or of the band the windows
+// cover) and up to SQC of the queries whose sink or window reach them; it sums their
+// contributions in registers and adds each row column once.  Per query (q, dO and out staged
+// through registers, the next query's loads in flight during this one's products):
+//   S^T  [64 rows x 16 heads] = K . Q^T    v_mfma_f32_16x16x32_bf16, one 16-row tile per wave,
+//   dP^T [64 rows x 16 heads] = V . dO^T   waves 0-3 S, waves 4-7 dP
+//   P, dS per (row, head) in fp32 (zero where the pair is not this pass's: si_entry), as bf16
+//   hi + lo pairs as above
+//   dKV [64 rows x d_qk] += (scale dS)^T . Q + P^T . dO   v_mfma_f32_16x16x16_bf16, 2 row tiles
+//                                                        x 9 column tiles per wave, Q and dO
+//                                                        by transposing LDS reads
+template <int DQK, int DV>
+__global__ __launch_bounds__(512, 1) void mla_attn_bwd_si_kernel(AttnBwdArgs a, SiPlan p)
+{
+    constexpr int ROWB = DQK * 2;          // LDS bytes per cache row
+    constexpr int CPR = ROWB / 16;         // 16-byte chunks per cache row
+    constexpr int QST = DQK * 2 + 16;      // padded LDS bytes per staged q row
+    constexpr int OST = DV * 2 + 16;       // padded LDS bytes per staged dO row
+    constexpr int QCH = 16 * DQK / 8;      // 16-byte chunks of the 16 heads' q
+    constexpr int QPT = (QCH + 511) / 512; // ... per thread (the last step partial)
+    constexpr int KS = DQK / 32, VS = DV / 32;
+    constexpr int CTW = DQK / 16 / 4;      // column tiles per wave
+    static_assert(16 * DV / 8 == 2 * 512 && (DQK / 16) % 4 == 0 && DV % 16 == 0, "shape");
+
+    __shared__ __attribute__((aligned(16))) uint8_t kblk[SRB * ROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t qs[16 * QST];
+    __shared__ __attribute__((aligned(16))) uint8_t dos[16 * OST];
+    __shared__ float part[2][SRB][17];                               // S, dP   [row][head]
+    __shared__ __attribute__((aligned(16))) uint16_t pA[2][SRB][16]; // P hi / lo  [row][head]
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][SRB][16]; // dS hi / lo [row][head]
+    __shared__ float Dh[16], lse2[16];
+    __shared__ int rsel[SRB];                                        // the pair is this pass's
+
+    const int HG = a.heads / 16;
+    const int b = blockIdx.z / HG, hg = blockIdx.z % HG;
+    // workgroup -> (block, query chunk): the sink blocks' chunks, then the window blocks'
+    const int gs = p.nsb * p.cs, g = (int)blockIdx.x;
+    const int blk = g < gs ? g / p.cs : p.nsb + (g - gs) / p.cw;
+    const int chunk = g < gs ? g % p.cs : (g - gs) % p.cw;
+    int64_t r0, r1, t_lo, t_hi;
+    si_block(a, p, blk, r0, r1, t_lo, t_hi);
+    const int64_t c0 = t_lo + (int64_t)chunk * SQC;
+    const int64_t c1 = imin(t_hi, c0 + SQC);
+    if (c0 >= c1 || r0 >= r1) return; // the same for every thread
+    const bool sink_blk = blk < p.nsb;
+    const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+    const int g4 = l >> 4, c16 = l & 15;
+
+    // the block's rows, chunks swizzled as in the query-major kernel; rows past r1 are zeros
+    const uint8_t *kv_b = reinterpret_cast<const uint8_t *>(a.k) + (int64_t)b * a.kv_len * a.k_stride * 2;
+    for (int f = tid; f < SRB * CPR; f += 512) {
+        const int r = f / CPR, c = f % CPR;
+        const int64_t row = imin(r0 + r, r1 - 1);
+        const uint4 v = ld16(kv_b + row * a.k_stride * 2 + c * 16);
+        *reinterpret_cast<uint4 *>(kblk + r * ROWB + swz(c, r) * 16) =
+            r0 + r < r1 ? v : make_uint4(0, 0, 0, 0);
+    }
+
+    // one query's operands through registers: q chunk f = 512 u + tid (head f / (DQK / 8));
+    // dO and out: thread tid holds chunks 2 (tid % 32) + {0, 1} of head tid / 32; lse of head
+    // tid (tid < 16); the index entry the layout gives row r0 + tid (tid < SRB)
+    uint4 qreg[QPT], dreg[2], oreg[2];
+    float lreg = 0.0f;
+    int32_t ireg = -1;
+    auto load_query = [&](int64_t t) {
+        const int64_t qrow = (int64_t)b * a.n_q + t;
+        const int64_t qh0 = qrow * a.heads + 16 * hg;
+        const uint16_t *qp = a.q + qh0 * DQK;
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) qreg[u] = ld16(qp + 8 * min(512 * u + tid, QCH - 1));
+        const int64_t ob = (qh0 + (tid >> 5)) * DV + 16 * (tid & 31);
+        dreg[0] = ld16(a.dout + ob);
+        dreg[1] = ld16(a.dout + ob + 8);
+        oreg[0] = ld16(a.out + ob);
+        oreg[1] = ld16(a.out + ob + 8);
+        lreg = a.lse[qh0 + (tid & 15)];
+        const int64_t V = si_valid_len(a, t), r = r0 + (tid & (SRB - 1));
+        const int64_t j = sink_blk ? r : a.sink + r - (V - a.window);
+        ireg = a.idx[qrow * a.n_idx + imin(imax(j, 0), a.n_idx - 1)]; // clamped, always valid
+    };
+    auto stage_query = [&](int64_t t) {
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) {
+            const int f = 512 * u + tid;
+            if (f < QCH)
+                *reinterpret_cast<uint4 *>(qs + (f / (DQK / 8)) * QST + (f % (DQK / 8)) * 16) = qreg[u];
+        }
+        const int h = tid >> 5, c = 2 * (tid & 31);
+        *reinterpret_cast<uint4 *>(dos + h * OST + c * 16) = dreg[0];
+        *reinterpret_cast<uint4 *>(dos + h * OST + (c + 1) * 16) = dreg[1];
+        // D = dO . out for head h: 32 threads x 16 columns
+        float acc = 0.0f;
+        const uint32_t xs[8] = {dreg[0].x, dreg[0].y, dreg[0].z, dreg[0].w,
+                                dreg[1].x, dreg[1].y, dreg[1].z, dreg[1].w};
+        const uint32_t ys[8] = {oreg[0].x, oreg[0].y, oreg[0].z, oreg[0].w,
+                                oreg[1].x, oreg[1].y, oreg[1].z, oreg[1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc = fmaf(__uint_as_float(xs[e] << 16), __uint_as_float(ys[e] << 16), acc);
+            acc = fmaf(__uint_as_float(xs[e] & 0xffff0000u), __uint_as_float(ys[e] & 0xffff0000u), acc);
+        }
+        // sum over the head's 32 lanes: row sums of 16 lanes, then row 1 (3) adds row 0 (2)
+#define LSA_DPP_ADD(CTRL, ROWS) \
+    acc += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc), CTRL, ROWS, 0xf, false))
+        LSA_DPP_ADD(0x111, 0xf); // row_shr:1
+        LSA_DPP_ADD(0x112, 0xf); // row_shr:2
+        LSA_DPP_ADD(0x114, 0xf); // row_shr:4
+        LSA_DPP_ADD(0x118, 0xf); // row_shr:8
+        LSA_DPP_ADD(0x142, 0xa); // row_bcast:15
+#undef LSA_DPP_ADD
+        if ((tid & 31) == 31) Dh[h] = acc;
+        if (tid < 16) lse2[tid] = lreg * kLog2e;
+        if (tid < SRB) {
+            const int64_t V = si_valid_len(a, t), r = r0 + tid;
+            const bool in = r < r1 && (sink_blk || (r >= V - a.window && r < V));
+            rsel[tid] = in && (int64_t)ireg == r;
+        }
+    };
+
+    f32x4_t acc[2][CTW];
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int tt = 0; tt < CTW; ++tt) acc[q2][tt] = f32x4_t{};
+    const float sl2 = a.scale * kLog2e;
+    const int rt = w & 3, role = w >> 2; // S / dP phase: row tile and operand
+    // dKV phase: row tiles rp, rp + 1 and column tiles cg + 4 tt (every wave gets one of the
+    // last four tiles, which have no dO part)
+    const int rp = 2 * (w >> 2), cg = w & 3;
+    load_query(c0);
+    for (int64_t t = c0; t < c1; ++t) {
+        ring_barrier(); // the previous query's LDS operands are consumed
+        stage_query(t);
+        if (t + 1 < c1) load_query(t + 1);
+        ring_barrier();
+        {
+            // two accumulator chains (even and odd K-steps), added at the end
+            f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
+            const int rr = 16 * rt + c16;
+            const uint8_t *kr = kblk + rr * ROWB;
+            if (role == 0) {
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) {
+                    const int c = 4 * kk + g4;
+                    sacc[kk & 1] = mfma_16x16x32(bitcast<bf16x8_t>(ld16(kr + 16 * swz(c, rr))),
+                                                 bitcast<bf16x8_t>(ld16(qs + c16 * QST + c * 16)),
+                                                 sacc[kk & 1]);
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < VS; ++kk) {
+                    const int c = 4 * kk + g4;
+                    sacc[kk & 1] = mfma_16x16x32(bitcast<bf16x8_t>(ld16(kr + 16 * swz(c, rr))),
+                                                 bitcast<bf16x8_t>(ld16(dos + c16 * OST + c * 16)),
+                                                 sacc[kk & 1]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[role][16 * rt + 4 * g4 + e][c16] = sacc[0][e] + sacc[1][e];
+        }
+        ring_barrier();
+#pragma unroll
+        for (int i = 0; i < SRB * 16 / 512; ++i) {
+            const int x = tid + 512 * i, r = x >> 4, h = x & 15;
+            const float P = rsel[r] ? exp2f(part[0][r][h] * sl2 - lse2[h]) : 0.0f;
+            const float dS = P * (part[1][r][h] - Dh[h]) * a.scale;
+            uint16_t ph, pl, sh, sl;
+            split_bf16(P, ph, pl);
+            split_bf16(dS, sh, sl);
+            pA[0][r][h] = ph;
+            pA[1][r][h] = pl;
+            sA[0][r][h] = sh;
+            sA[1][r][h] = sl;
+        }
+        ring_barrier();
+        {
+            // K index k of the products: hi / lo part k / 16 of head k % 16.  Lane (g4, l%16)
+            // supplies A row l%16 with k = 8 g4 .. +7: part g4 / 2, heads 8 (g4 & 1) .. +7
+            bf16x8_t sa[2], pa[2];
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const int r = 16 * (rp + q2) + c16;
+                sa[q2] = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(&sA[g4 >> 1][r][8 * (g4 & 1)]));
+                pa[q2] = bitcast<bf16x8_t>(*reinterpret_cast<const uint4 *>(&pA[g4 >> 1][r][8 * (g4 & 1)]));
+            }
+            // B column l%16 with the same k: heads 8 (g4 & 1) .. +7 of Q (dO), by two transposing
+            // reads in which lane j of group g4 addresses head hb + j/4 (hb + 4 + j/4), columns
+            // 16 T + 4 (j%4) .. +3; lane l receives [head hb + e][column 16 T + l%16]
+            const int hb = 8 * (g4 & 1) + (c16 >> 2);
+            auto cat8 = [](s16x4_t lo, s16x4_t hi) {
+                const uint2 x = bitcast<uint2>(lo), y = bitcast<uint2>(hi);
+                return bitcast<bf16x8_t>(make_uint4(x.x, x.y, y.x, y.y));
+            };
+#pragma unroll
+            for (int tt = 0; tt < CTW; ++tt) {
+                const int T = cg + 4 * tt;
+                const int col = 16 * T + 4 * (c16 & 3);
+                const bf16x8_t qb = cat8(ds_read_tr16(qs + hb * QST + col * 2),
+                                         ds_read_tr16(qs + (hb + 4) * QST + col * 2));
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) acc[q2][tt] = mfma_16x16x32(sa[q2], qb, acc[q2][tt]);
+                if (16 * T < DV) {
+                    const bf16x8_t db = cat8(ds_read_tr16(dos + hb * OST + col * 2),
+                                             ds_read_tr16(dos + (hb + 4) * OST + col * 2));
+#pragma unroll
+                    for (int q2 = 0; q2 < 2; ++q2) acc[q2][tt] = mfma_16x16x32(pa[q2], db, acc[q2][tt]);
+                }
+            }
+        }
+    }
+    // the block's sums into the cache gradient (lane: [row 16 R + 4 g4 + e][column 16 T + l%16])
+    float *dkv_b = a.dk + (int64_t)b * a.kv_len * DQK;
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int tt = 0; tt < CTW; ++tt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = r0 + 16 * (rp + q2) + 4 * g4 + e;
+                const float v = acc[q2][tt][e];
+                if (row < r1 && v != 0.0f) atomicAdd(dkv_b + row * DQK + 16 * (cg + 4 * tt) + c16, v);
+            }
 }
 
 // Per-head kernel: one wave per (query, head); lane l owns columns l, l + 64, ... (d <= 256).
@@ -393,13 +677,62 @@ int attn_bwd_splits(int batch, int n_q, int heads, int n_idx, int latent)
     return want < 1 ? 1 : (int)want;
 }
 
-hipError_t launch_sparse_attn_backward(const AttnBwdArgs &a, hipStream_t st)
+namespace {
+
+// The key-major pass's blocks and query chunks, or false where it does not apply (a ragged
+// batch, no sink or window, no query whose sink and window are disjoint) or would not pay: it
+// pays when each row update it makes stands for many queries' updates (prefill chunks), and
+// not when every row is reached by one query or few (decode).
+bool si_plan(const AttnBwdArgs &a, SiPlan &p, int &nblk, int &nchunk)
 {
-    const int64_t rows = (int64_t)a.batch * a.n_q;
+    const int64_t S = a.sink, W = a.window;
+    if (!a.latent || a.seq_len || a.q_pos0 < 0 || S < 0 || W < 0 || S + W == 0 || a.n_q < 1 ||
+        a.kv_len < S + W)
+        return false;
+    p.t_si = imax(0, S + W - a.q_pos0 - 1);
+    if (p.t_si >= a.n_q) return false;
+    p.nsb = (int)((S + SRB - 1) / SRB);
+    const int64_t vmin = si_valid_len(a, p.t_si), vmax = si_valid_len(a, a.n_q - 1);
+    p.wlo = S + SRB * ((vmin - W - S) / SRB); // vmin >= S + W
+    const int64_t nwb = W > 0 ? (vmax - p.wlo + SRB - 1) / SRB : 0;
+    if (p.nsb + nwb > (int64_t(1) << 30)) return false;
+    nblk = (int)(p.nsb + nwb);
+    int64_t span_s = 0, span_w = 0;
+    for (int blk = 0; blk < nblk; ++blk) {
+        int64_t r0, r1, t_lo, t_hi;
+        si_block(a, p, blk, r0, r1, t_lo, t_hi);
+        if (r0 < r1) (blk < p.nsb ? span_s : span_w) = imax(blk < p.nsb ? span_s : span_w, t_hi - t_lo);
+    }
+    p.cs = (int)((span_s + SQC - 1) / SQC);
+    p.cw = (int)((span_w + SQC - 1) / SQC);
+    if (p.nsb > 0 && p.cs < 1) p.cs = 1;
+    if (nwb > 0 && p.cw < 1) p.cw = 1;
+    const int64_t groups = (int64_t)p.nsb * p.cs + nwb * p.cw;
+    if (groups < 1 || groups >= (int64_t(1) << 31) || (int64_t)a.batch * (a.heads / 16) > 65535)
+        return false;
+    nchunk = (int)groups; // workgroups per (sequence, head group)
+    const int64_t taken = (int64_t)(a.n_q - p.t_si) * (S + W); // entries the pass takes
+    const int64_t own = groups * SRB;                          // row updates it makes
+    return taken >= 8 * own;
+}
+
+} // namespace
+
+hipError_t launch_sparse_attn_backward(const AttnBwdArgs &args, hipStream_t st)
+{
+    const int64_t rows = (int64_t)args.batch * args.n_q;
     if (rows == 0) return hipSuccess;
+    AttnBwdArgs a = args;
     if (a.latent) {
+        SiPlan p{};
+        int nblk = 0, nchunk = 0;
+        a.si = si_plan(a, p, nblk, nchunk) ? 1 : 0;
         dim3 grid((unsigned)a.n_split, (unsigned)(a.n_q * (a.heads / 16)), (unsigned)a.batch);
         hipLaunchKernelGGL((mla_attn_bwd_kernel<MLA_DQK, MLA_DV>), grid, dim3(256), 0, st, a);
+        if (a.si) {
+            dim3 sgrid((unsigned)nchunk, 1u, (unsigned)(a.batch * (a.heads / 16)));
+            hipLaunchKernelGGL((mla_attn_bwd_si_kernel<MLA_DQK, MLA_DV>), sgrid, dim3(512), 0, st, a, p);
+        }
     } else {
         const int64_t units = rows * a.heads;
         hipLaunchKernelGGL(mha_attn_bwd_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, st, a);

@@ -154,6 +154,10 @@ struct AttnBwdArgs {
     const int32_t *seq_len; // [B] valid rows per sequence (device) or nullptr
     float scale;
     int n_split;          // chunks of the index list per (query, head group)
+    // Streaming-Aware entries (sink [0, S) and window [S, S + W) of each list, as the selection
+    // lays them out for V_t = min(kv_len, q_pos0 + t + 1)) taken by the key-major pass: si != 0
+    int sink, window, si;
+    int64_t q_pos0;
 };
 
 int attn_bwd_splits(int batch, int n_q, int heads, int n_idx, int latent);

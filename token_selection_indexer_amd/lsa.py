@@ -433,10 +433,13 @@ def sparse_attn(q, k, v, idx, scale, sink=0, window=0, d_v=None, latent=None, wa
 
 
 def sparse_attn_backward(q, k, v, idx, out, lse, d_out, scale, d_v=None, latent=None, d_q=None,
-                         d_k=None, d_vg=None, stream=None, seq_lens=None):
+                         d_k=None, d_vg=None, stream=None, seq_lens=None, sink=0, window=0,
+                         q_pos0=0):
     """Gradients of sparse_attn, ADDED into fp32 d_q [B,n_q,Hq,d_qk], d_k [B,L,d_qk] and d_vg
     [B,L,d_v] (zeros are allocated for the ones not given).  Latent cache (v None or v is k):
-    one cache gradient d_k, whose first d_v columns also take dV; d_vg is then d_k."""
+    one cache gradient d_k, whose first d_v columns also take dV; d_vg is then d_k.  sink,
+    window and q_pos0 describe the lists' Streaming-Aware layout (as topk_select writes it),
+    which lets the library sum the sink and window rows' gradients key by key."""
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 3, device=q.device)
     _need(idx, "idx", torch.int32, 3, device=q.device)
@@ -470,9 +473,9 @@ def sparse_attn_backward(q, k, v, idx, out, lse, d_out, scale, d_v=None, latent=
     else:
         d_vg = _zeros_or(d_vg, "d_vg", (B, L, d_v), dev)
     attn = AttnShape(Hq, dqk, d_v, 1 if latent else 0, k.shape[2], v.shape[2], scale)
-    shape = _ragged(IndexShape(B, T, 64, 128, L, 0), dev, seq_lens)
-    lsa_sparse_attn_backward(shape, attn, Budget(idx.shape[2], 0, 0), q, k, v, idx, out, lse,
-                             d_out, d_q, d_k, d_vg, stream)
+    shape = _ragged(IndexShape(B, T, 64, 128, L, int(q_pos0)), dev, seq_lens)
+    lsa_sparse_attn_backward(shape, attn, Budget(idx.shape[2], int(sink), int(window)), q, k, v,
+                             idx, out, lse, d_out, d_q, d_k, d_vg, stream)
     return d_q, d_k, d_vg
 
 
