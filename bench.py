@@ -355,14 +355,20 @@ def extra_backward(torch, lsa, inputs, cfg, tm: Timing):
     d = {"attn_bwd": tm.both(f_attn_bwd, 60.0, cold_too=False),
          "index_bwd": tm.both(f_index_bwd, 30.0, cold_too=False)}
     n_sel = s.n_q * b.k
+    # entries whose cache gradient the key-major pass sums over queries before adding it (the
+    # sink and window entries of every query whose sink and window are disjoint); the
+    # query-major kernel adds the rest, one fp32 atomic per row column
+    t_si = max(0, b.sink + b.window - s.q_pos0 - 1)
+    n_si = max(0, s.n_q - t_si) * (b.sink + b.window)
     attn_flops = 2.0 * n_sel * a.heads * (3 * a.d_qk + 2 * a.d_v)
     idx_flops = 2.0 * 3 * n_sel * s.heads * s.head_dim
     ta, ti = d["attn_bwd"]["warm"]["mean"], d["index_bwd"]["warm"]["mean"]
     res = {"workload": w.name + "_backward", "dist": d,
            "attn_bwd_flops": attn_flops, "attn_bwd_TFLOPs": attn_flops / (ta * 1e-3) / 1e12,
            "attn_bwd_mfma_frac": attn_flops / (ta * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
-           "attn_bwd_atomic_updates": n_sel * a.d_qk,
-           "attn_bwd_G_updates_per_s": n_sel * a.d_qk / (ta * 1e-3) / 1e9,
+           "attn_bwd_entries": n_sel, "attn_bwd_entries_key_major": n_si,
+           "attn_bwd_G_entries_per_s": n_sel / (ta * 1e-3) / 1e9,
+           "attn_bwd_atomic_updates_query_major": (n_sel - n_si) * a.d_qk,
            "index_bwd_flops": idx_flops, "index_bwd_TFLOPs": idx_flops / (ti * 1e-3) / 1e12,
            "index_bwd_mfma_frac": idx_flops / (ti * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
            "index_bwd_atomic_updates": n_sel * s.head_dim,
