@@ -274,14 +274,16 @@ LSA_API lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budg
  * Entries of -1 (or outside [0, kv_len)) are skipped; a row with none gives out = 0,
  * lse = -inf.  Cross-Layer Indexing (paper summary page, strategy (2)): call once per layer with
  * that layer's q / cache and the same idx.
- *   shape   uses batch, n_q, kv_len and seq_len (ids at or past a sequence's length are skipped)
- *   budget  k = entries per idx row.  sink / window describe the layout lsa_topk_select
- *           writes (idx[.., 0:S] and idx[.., S:S+W] are runs of consecutive tokens when V > k)
- *           but change nothing in the computation: every entry is gathered by its id.  A
- *           latent row is one contiguous d_qk * 2-byte run in HBM that the kernel loads in
- *           whole 16-byte pieces, so the consecutive rows of the sink and window runs already
- *           arrive as one contiguous span and need no path of their own.  Checked:
- *           0 <= sink, 0 <= window, sink + window <= k.
+ *   shape   uses batch, n_q, kv_len and seq_len (ids at or past a sequence's length are skipped),
+ *           and q_pos0 / seq_pos0 (the queries' positions) as a layout hint, below
+ *   budget  k = entries per idx row.  sink / window, with the query positions, describe the
+ *           layout lsa_topk_select writes: with V = min(length, position + 1), a query with
+ *           V <= k lists rows 0 .. V-1 then -1, otherwise idx[.., 0:S] = rows 0 .. S-1 and
+ *           idx[.., S:S+W] = rows V-W .. V-1.  The latent kernel loads the first rows it
+ *           processes from that layout while the list itself is still arriving, and compares
+ *           them with the list; where they differ it loads the listed rows instead.  The layout
+ *           is a hint: every result is that of the list as given, whatever sink, window and
+ *           the positions say.  Checked: 0 <= sink, 0 <= window, sink + window <= k.
  *   q       [B, n_q, Hq, d_qk] bf16
  *   k, v    [B, L, row_stride] bf16 (latent: v == k)
  *   idx     [B, n_q, k] int32

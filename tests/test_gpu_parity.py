@@ -444,6 +444,77 @@ def test_mla_attn_small(B, T, k, L):
     attn_check(att["q"], att["kv"], None, idx, w.attn.scale, out, lse, True, 512)
 
 
+def _layout_case(B, T, L, k, S, W, seed, perturb=None, hint_pos0=None, seq_lens=None):
+    """Attention over Streaming-Aware lists with the layout passed as a hint, and again with no
+    hint: the kernel loads each split's first rows from the layout before the list arrives and
+    falls back to the listed rows where they differ, so the two calls agree bit for bit; the
+    hinted call also matches the oracle."""
+    w = Workload(name="a", index=IndexShape(
+        batch=B, n_q=T, kv_len=L, q_pos0=L - T, heads=64, head_dim=128, key_dtype="fp8"),
+        budget=DECODE_128K.budget, attn=DECODE_128K.attn, seed=seed)
+    att = inputs.attn_inputs(w, 0, DEV)
+    lens = [L] * B if seq_lens is None else seq_lens
+    idx = torch.stack([inputs.synthetic_index_lists(T, k, S, W, ref.valid_lengths(lens[b], L - T, T),
+                                                    seed=seed + b) for b in range(B)])
+    if perturb is not None:
+        perturb(idx)
+    idx = idx.to(DEV)
+    sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    pos0 = L - T if hint_pos0 is None else hint_pos0
+    out, lse = lsa.sparse_attn(att["q"], att["kv"], None, idx, w.attn.scale, S, W, d_v=512,
+                               q_pos0=pos0, seq_lens=sl)
+    out0, lse0 = lsa.sparse_attn(att["q"], att["kv"], None, idx, w.attn.scale, 0, 0, d_v=512,
+                                 q_pos0=0, seq_lens=sl)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out0.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse0.view(torch.int32))
+    kv = att["kv"]
+    if seq_lens is not None:  # rows past a sequence's length are skipped: the oracle's view
+        ids = idx.clone()
+        for b in range(B):
+            ids[b][ids[b] >= seq_lens[b]] = -1
+        idx = ids
+    attn_check(att["q"], kv, None, idx, w.attn.scale, out, lse, True, 512)
+
+
+def _hole_sink(idx):
+    idx[0, 0, 3] = -1
+
+
+def _move_window(idx):
+    idx[1, 0, 20] = 7
+
+
+def _past_cache(idx):
+    idx[2, 0, 0] = 1 << 20
+
+
+def _swap_first_round(idx):
+    idx[3, 0, [0, 31]] = idx[3, 0, [31, 0]]
+
+
+@pytest.mark.parametrize("perturb", [None, _hole_sink, _move_window, _past_cache, _swap_first_round])
+def test_mla_attn_layout_hint_decode(perturb):
+    """Decode shape, 8 splits of 32-entry rounds dealt in turn: splits 0-3 start on sink and
+    window rounds (predicted), 4-7 on dynamic ones; with one list per case made to differ from
+    the layout inside a predicted round (a skipped sink entry, a window entry naming another
+    row, an entry past the cache, two entries swapped)."""
+    _layout_case(B=4, T=1, L=5000, k=256, S=16, W=112, seed=41, perturb=perturb)
+
+
+def test_mla_attn_layout_hint_short_rows_and_wrong_positions():
+    """Rows with V <= k (the list is rows 0 .. V-1, then -1) are predicted whole; a hint with
+    wrong query positions predicts the window wrongly and every such round falls back."""
+    _layout_case(B=2, T=3, L=150, k=256, S=16, W=112, seed=43)
+    _layout_case(B=2, T=1, L=5000, k=256, S=16, W=112, seed=45, hint_pos0=100)
+    _layout_case(B=1, T=40, L=3000, k=300, S=64, W=100, seed=47)
+
+
+def test_mla_attn_layout_hint_ragged():
+    """Per-sequence lengths: the layout's window ends at each sequence's own length."""
+    _layout_case(B=3, T=1, L=4000, k=256, S=16, W=112, seed=49, seq_lens=[4000, 1200, 200])
+
+
 def test_mla_attn_empty_and_single_rows():
     L, k = 1000, 128
     w = shrink(DECODE_128K, batch=1, n_q=3, kv_len=L, q_pos0=L - 3)

@@ -595,6 +595,8 @@ lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_shape *a
     a.v_stride = attn->v_row_stride;
     a.sink = budget.sink;
     a.window = budget.window;
+    a.q_pos0 = shape->q_pos0;
+    a.seq_pos0 = shape->seq_pos0;
     a.scale = attn->scale;
     a.n_split = lsa::attn_splits(shape->batch, shape->n_q, attn->n_heads, budget.k, attn->latent);
     return device_status(lsa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)));

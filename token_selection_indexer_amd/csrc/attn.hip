@@ -95,6 +95,8 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     __shared__ float S2[2][16][AR + 1];    // logit halves (two K halves)
     __shared__ __attribute__((aligned(16))) uint16_t Pm[16][AR + 8];
     __shared__ int32_t rid[NBUF][AR];      // row ids of the rounds in the buffers, -1 = skip
+    __shared__ int32_t rid_p[AR];          // round 0's row ids as the layout predicts them
+    __shared__ bool pred_ok;               // ... and they are the list's
     __shared__ float m_run[16], l_run[16], alpha[16];
     auto slot_buf = [&](auto SLOT) -> uint8_t * {
         if constexpr (decltype(SLOT)::value == 0) return buf0;
@@ -109,27 +111,40 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     const int l = lane_id(), w = wave_id();
     const int64_t qrow = (int64_t)b * a.n_q + t;
 
-    const int chunk = ((a.n_idx + a.n_split - 1) / a.n_split + AR - 1) / AR * AR;
-    const int c_begin = split * chunk;
-    const int c_end = min(a.n_idx, c_begin + chunk);
-    const int n_rounds = c_end > c_begin ? (c_end - c_begin + AR - 1) / AR : 0;
+    // The list's rounds of AR entries are dealt to the splits in turn: split s takes rounds
+    // s, s + n_split, ...  With the Streaming-Aware layout in front, every split then starts on
+    // sink or window entries, whose rows the layout names without reading the list.
+    const int rounds_all = (a.n_idx + AR - 1) / AR;
+    const int n_rounds = split < rounds_all ? (rounds_all - split + a.n_split - 1) / a.n_split : 0;
+    auto entry = [&](int round) { return (split + round * a.n_split) * AR + (int)(threadIdx.x % AR); };
 
     const int32_t *idx_row = a.idx + qrow * a.n_idx;
     const int64_t seq_rows = seq_keys(a.seq_len, b, a.kv_len); // valid rows of this sequence
     // Row id (threadIdx.x % AR) of a round: an unconditional load of a clamped, always valid
     // entry (a conditional load would make the compiler wait for it at once), masked at use.
-    auto id_load = [&](int round) -> int32_t {
-        const int j = c_begin + round * AR + (int)(threadIdx.x % AR);
-        return idx_row[min(j, c_end - 1)];
-    };
+    auto id_load = [&](int round) -> int32_t { return idx_row[min(entry(round), a.n_idx - 1)]; };
     auto id_mask = [&](int round, int32_t raw) -> int32_t {
-        const int j = c_begin + round * AR + (int)(threadIdx.x % AR);
-        return (round < n_rounds && j < c_end && row_ok(raw, seq_rows)) ? raw : -1;
+        return (round < n_rounds && entry(round) < a.n_idx && row_ok(raw, seq_rows)) ? raw : -1;
     };
-    auto id_of = [&](int round) -> int32_t { return id_mask(round, id_load(round)); };
+    // The rows round 0 holds if the list has the layout lsa_topk_select writes: with
+    // V = min(rows, position + 1), a query with V <= k lists rows 0 .. V-1 then -1; otherwise
+    // entries [0, S) are rows 0 .. S-1 and entries [S, S+W) rows V-W .. V-1.  Round 0 is
+    // predicted when all its entries lie there; its rows are then loaded together with the
+    // list, q and nothing else in the way, and checked against the list once it is in.
+    const int64_t V = valid_len(a.seq_len, a.seq_pos0, b, t, a.kv_len, a.q_pos0);
+    const int e0 = split * AR;
+    const bool predicted = n_rounds > 0 && (V <= a.n_idx || min(e0 + AR, a.n_idx) <= a.sink + a.window);
+    int32_t raw0 = 0, raw1 = 0, pid = -1;
     if (threadIdx.x < AR) {
-        rid[0][threadIdx.x] = n_rounds > 0 ? id_of(0) : -1;
-        rid[1][threadIdx.x] = n_rounds > 1 ? id_of(1) : -1;
+        raw0 = id_load(0);
+        raw1 = id_load(1);
+        const int e = e0 + (int)threadIdx.x;
+        const int64_t p = e >= a.n_idx ? -1
+                          : V <= a.n_idx ? (e < V ? e : -1)
+                          : e < a.sink ? e
+                          : V - a.window + (e - a.sink);
+        pid = p >= 0 && p < seq_rows ? (int32_t)p : -1;
+        rid_p[threadIdx.x] = pid;
     }
     // Q fragments: wave w computes row tile (w & 1) over K-half (w >> 1); lane l holds head
     // 16*hg + l%16, d = 32*(KH*(w>>1) + kk) + 8*(l/16) + [0,8)
@@ -149,7 +164,6 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     for (int nt = 0; nt < NTW; ++nt) oacc[nt] = f32x4_t{};
     const uint8_t *kv_b = reinterpret_cast<const uint8_t *>(a.k) + (int64_t)b * a.kv_len * a.k_stride * 2;
     const float sl2 = a.scale * kLog2e;
-    __syncthreads();
 
     // A round's rows through registers: thread t loads the 16-byte chunks f = 256*j + t of the
     // round (row f / CPR, chunk f % CPR; consecutive threads read consecutive chunks of a row)
@@ -174,8 +188,19 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
         }
     };
 
+    ring_barrier(); // rid_p is visible; the list and q loads stay in flight
+    if (predicted) load_round(rid_p);
+    if (threadIdx.x < AR) {
+        rid[0][threadIdx.x] = n_rounds > 0 ? id_mask(0, raw0) : -1;
+        rid[1][threadIdx.x] = n_rounds > 1 ? id_mask(1, raw1) : -1;
+    }
+    if (w == 0) { // a prediction that differs from the list in any entry is discarded
+        const uint64_t miss = __ballot(threadIdx.x < AR && pid != rid[0][threadIdx.x]);
+        if (l == 0) pred_ok = predicted && miss == 0u;
+    }
+    __syncthreads();
     if (n_rounds > 0) {
-        load_round(rid[0]);
+        if (!pred_ok) load_round(rid[0]);
         store_round(buf0);
     }
     // Q, the ids and round 0 are in: the loop starts with nothing outstanding, so the waits the

@@ -130,8 +130,10 @@ struct AttnArgs {
     int64_t kv_len, k_stride, v_stride;
     const int32_t *seq_len; // [B] valid rows per sequence (device) or nullptr
     int sink, window;
+    int64_t q_pos0;         // query positions (with seq_pos0): where the layout puts the window
+    const int32_t *seq_pos0;
     float scale;
-    int n_split;          // chunks of the index list per (query, head group)
+    int n_split;          // workgroups per (query, head group); rounds are dealt to them in turn
 };
 
 int attn_splits(int batch, int n_q, int heads, int n_idx, int latent);

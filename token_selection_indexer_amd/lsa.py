@@ -395,9 +395,13 @@ def page_recall(q, w, page_keys, keys, key_scale, k, sink, window, page, m_pages
 
 
 def sparse_attn(q, k, v, idx, scale, sink=0, window=0, d_v=None, latent=None, want_lse=True,
-                ws: Optional[Workspace] = None, out=None, stream=None, seq_lens=None):
+                ws: Optional[Workspace] = None, out=None, stream=None, seq_lens=None, q_pos0=None,
+                seq_pos0=None):
     """out [B, n_q, Hq, d_v] bf16 and lse [B, n_q, Hq] fp32 (or None).  Latent cache: pass v=None
-    (or v is k) and d_v = the value width."""
+    (or v is k) and d_v = the value width.  sink, window and the query positions (q_pos0, default
+    L - n_q; seq_pos0 for a ragged batch) describe the lists' Streaming-Aware layout: the kernel
+    starts loading the rows that layout names before the lists arrive (the result never depends
+    on them)."""
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 3)
     _need(idx, "idx", torch.int32, 3)
@@ -422,7 +426,8 @@ def sparse_attn(q, k, v, idx, scale, sink=0, window=0, d_v=None, latent=None, wa
     if d_v > v.shape[2]:
         raise ValueError(f"d_v {d_v} exceeds the value rows ({v.shape[2]})")
     attn = AttnShape(Hq, dqk, d_v, 1 if latent else 0, k.shape[2], v.shape[2], scale)
-    shape = _ragged(IndexShape(B, T, 64, 128, L, 0), dev, seq_lens)
+    pos0 = max(0, L - T) if q_pos0 is None else q_pos0
+    shape = _ragged(IndexShape(B, T, 64, 128, L, pos0), dev, seq_lens, seq_pos0)
     bud = Budget(idx.shape[2], sink, window)
     out = _out(out, "out", (B, T, Hq, d_v), torch.bfloat16, dev)
     lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev) if want_lse else None
