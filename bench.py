@@ -453,6 +453,15 @@ def extra_hi(torch, lsa, inputs, w, tm: Timing):
                             ws=ws, out=o, want_lse=False)
 
     d["attn_all_layers"] = tm.both(f_attn, 0.02 * w.layers)
+    ws_layers = lsa.Workspace()
+
+    def f_attn_layers():  # the same layers in one call: one gather launch, one combine launch
+        lsa.sparse_attn_layers([at["q"] for at in atts], [at["kv"] for at in atts], idx, a.scale,
+                               b.sink, b.window, d_v=a.d_v, ws=ws_layers, outs=outs,
+                               want_lse=False)
+
+    if w.layers > 1:
+        d["attn_layers_one_call"] = tm.both(f_attn_layers, 0.02 * w.layers)
     t = {k: v["warm"]["mean"] for k, v in d.items()}
     tc = {k: v["cold"]["mean"] for k, v in d.items()}
     t_hi, t_flat = t["recall"] + t["hi_topk"], t["flat_index_fused"]
@@ -472,6 +481,11 @@ def extra_hi(torch, lsa, inputs, w, tm: Timing):
         "attn_layers": w.layers,
         "sparse_attn_TBps": ab / (t["attn_all_layers"] * 1e-3) / 1e12,
     }
+    if w.layers > 1:
+        res["sparse_attn_TBps_one_call"] = ab / (t["attn_layers_one_call"] * 1e-3) / 1e12
+        res["attn_layers_one_call_speedup"] = t["attn_all_layers"] / t["attn_layers_one_call"]
+        res["attn_layers_one_call_speedup_cold"] = (tc["attn_all_layers"]
+                                                    / tc["attn_layers_one_call"])
     del inp, atts, outs, pk, idx
     torch.cuda.empty_cache()
     return res
@@ -605,6 +619,29 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
                                                       hi.page, hi.m_pages, q_pos0=s.q_pos0, ws=ws),
                "hi1m_topk": lambda: lsa.topk_select(r[1], b.k, b.sink, b.window, kv_len=s.kv_len,
                                                     q_pos0=s.q_pos0, cand_ids=r[2], ws=ws_sel)}
+    elif stage.startswith("cli4_"):
+        # 4 attention layers on one Hierarchical-Indexing list (8 x 256K decode): per-layer calls
+        # or one multi-layer call
+        w = cfg.DECODE_256K_HI_CLI
+        s, b, a, hi = w.index, w.budget, w.attn, w.hi
+        inp = inputs.index_inputs(w, dev)
+        pk = lsa.page_summary(inp["keys"], inp["scale"], hi.page)
+        _, cs, ci = lsa.page_recall(inp["q"], inp["w"], pk, inp["keys"], inp["scale"], b.k, b.sink,
+                                    b.window, hi.page, hi.m_pages, q_pos0=s.q_pos0)
+        idx = lsa.topk_select(cs, b.k, b.sink, b.window, kv_len=s.kv_len, q_pos0=s.q_pos0,
+                              cand_ids=ci)
+        del inp, pk, cs, ci
+        atts = [inputs.attn_inputs(w, l, dev) for l in range(w.layers)]
+        ws = lsa.Workspace()
+
+        def per_layer():
+            for at in atts:
+                lsa.sparse_attn(at["q"], at["kv"], None, idx, a.scale, b.sink, b.window, d_v=a.d_v,
+                                ws=ws, want_lse=False)
+        fns = {"cli4_attn": per_layer,
+               "cli4_attn_layers": lambda: lsa.sparse_attn_layers(
+                   [at["q"] for at in atts], [at["kv"] for at in atts], idx, a.scale, b.sink,
+                   b.window, d_v=a.d_v, ws=ws, want_lse=False)}
     else:
         w = cfg.DECODE_128K
         s, b, a = w.index, w.budget, w.attn
@@ -636,7 +673,7 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
 
 STAGES = ["score", "topk", "index", "attn", "copy", "prefill_score", "prefill_topk", "prefill_attn",
           "prefill_q8", "bwd_attn", "bwd_index",
-          "hi1m_summary", "hi1m_recall", "hi1m_topk"]
+          "hi1m_summary", "hi1m_recall", "hi1m_topk", "cli4_attn", "cli4_attn_layers"]
 
 
 def main():

@@ -7,7 +7,8 @@
  *   3. lsa_page_summary  -- page keys for Hierarchical Indexing (mean of a page's keys)
  *   4. lsa_page_recall   -- Hierarchical Indexing: coarse page recall, fine scores in the pages
  *   5. lsa_sparse_attn   -- attention over the selected tokens (MLA latent cache or MHA),
- *                           reusable by several layers with one index list (Cross-Layer Indexing)
+ *                           reusable by several layers with one index list (Cross-Layer Indexing);
+ *                           lsa_sparse_attn_layers runs such a group of layers in one call
  *   6. lsa_sparse_attn_backward, lsa_index_scores_backward -- the gradients of 5 and of the
  *                           indexer scores at the selected entries (the training path)
  *
@@ -297,6 +298,30 @@ LSA_API lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_
                            lsa_budget budget, const void *q, const void *k, const void *v,
                            const int32_t *idx, void *out, float *lse, void *ws, size_t ws_bytes,
                            void *stream);
+
+/*
+ * lsa_sparse_attn_layers -- lsa_sparse_attn for n_layers consecutive layers that share one index
+ * list (paper summary page, strategy (2): Cross-Layer Indexing computes the index once for a
+ * group of layers; model card, CLI bullet).  Layer l's result is exactly (bit for bit) that of
+ * lsa_sparse_attn(shape, attn, budget, q[l], k[l], v[l], idx, out[l], lse[l], ...): the same
+ * arithmetic in the same order.  With a latent cache every layer's gathers run in one launch and
+ * every layer's split partials are merged in one more, instead of two launches per layer.
+ *   n_layers   1 .. 8
+ *   q, k, v, out   host arrays of n_layers device pointers, each as for lsa_sparse_attn (the
+ *              arrays are read during the call only; the caller keeps ownership)
+ *   lse        NULL, or a host array of n_layers device pointers (each may be NULL)
+ *   shape, attn, budget, idx   shared by every layer, as for lsa_sparse_attn
+ *   ws         n_layers * lsa_workspace_bytes(LSA_OP_SPARSE_ATTN, ...) bytes (rounded up to a
+ *              multiple of 256), 256-byte aligned
+ * Errors as lsa_sparse_attn; n_layers outside [1, 8] is LSA_ERR_BAD_SHAPE, a NULL array or
+ * entry LSA_ERR_NULL_POINTER; batch * n_layers > 65535 is LSA_ERR_UNSUPPORTED.
+ */
+LSA_API lsa_status lsa_sparse_attn_layers(const lsa_index_shape *shape, const lsa_attn_shape *attn,
+                                          lsa_budget budget, int32_t n_layers,
+                                          const void *const *q, const void *const *k,
+                                          const void *const *v, const int32_t *idx,
+                                          void *const *out, float *const *lse, void *ws,
+                                          size_t ws_bytes, void *stream);
 
 /*
  * lsa_sparse_attn_backward -- gradients of lsa_sparse_attn (the training path: the paper summary

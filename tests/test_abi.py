@@ -175,6 +175,33 @@ def test_sparse_attn_rejects(L):
     assert call(lsa.AttnShape(1, 128, 128, 0, 64, 128, 0.1)) == 2    # stride < d_qk
 
 
+def test_sparse_attn_layers_rejects(L):
+    sh = _shape(B=32)
+    b = lsa.Budget(2048, 64, 960)
+    v = ctypes.c_void_p
+    mla = lsa.AttnShape(16, 576, 512, 1, 576, 576, 0.04)
+    arr = lambda *p: (v * len(p))(*p)
+
+    def call(n, q=None, k=None, out=None, ws=None, nb=0, idx=FAKE):
+        q = q or arr(*[FAKE] * max(n, 1))
+        k = k or arr(*[FAKE + 4096] * max(n, 1))
+        out = out or arr(*[FAKE + 8192] * max(n, 1))
+        return L.lsa_sparse_attn_layers(ctypes.byref(sh), ctypes.byref(mla), b, n, q, k, k,
+                                        v(idx) if idx else None, out, None, v(ws) if ws else None,
+                                        nb, None)
+    assert call(0) == 2 and call(9) == 2                         # 1 .. 8 layers
+    assert call(2, q=arr(FAKE, None)) == 1                       # a NULL entry
+    assert call(2, idx=0) == 1
+    assert call(2, k=arr(FAKE + 4096, FAKE + 4100)) == 2         # a misaligned cache
+    one = lsa.lsa_workspace_bytes(lsa.OP_SPARSE_ATTN, sh, b, attn=mla)
+    assert one > 0
+    assert call(3, ws=FAKE, nb=2 * one) == 5                     # n_layers workspaces
+    nullarr = ctypes.cast(None, ctypes.POINTER(v))
+    assert L.lsa_sparse_attn_layers(ctypes.byref(sh), ctypes.byref(mla), b, 2, nullarr,
+                                    arr(FAKE, FAKE), arr(FAKE, FAKE), v(FAKE), arr(FAKE, FAKE),
+                                    None, None, 0, None) == 1
+
+
 def test_no_host_fallback_and_missing_library_fails_loudly(tmp_path):
     """The binding has no CPU path: host tensors are refused, and without the built library every
     call raises instead of computing anything some other way."""

@@ -610,6 +610,61 @@ def test_cross_layer_reuse_bitwise_and_oracle():
     assert not torch.equal(outs[0], outs[1])
 
 
+def _layers_case(B, T, L, k, S, W, n, seed, seq_lens=None, want_lse=True):
+    """n latent layers over one index list in one lsa_sparse_attn_layers call: every layer's out
+    and lse equal its own lsa_sparse_attn call bit for bit; the last layer also against the
+    oracle."""
+    w = Workload(name="a", index=IndexShape(
+        batch=B, n_q=T, kv_len=L, q_pos0=L - T, heads=64, head_dim=128, key_dtype="fp8"),
+        budget=DECODE_128K.budget, attn=DECODE_128K.attn, seed=seed)
+    lens = [L] * B if seq_lens is None else seq_lens
+    idx = torch.stack([inputs.synthetic_index_lists(T, k, S, W, ref.valid_lengths(lens[b], L - T, T),
+                                                    seed=seed + b) for b in range(B)]).to(DEV)
+    sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    atts = [inputs.attn_inputs(w, layer, DEV) for layer in range(n)]
+    outs, lses = lsa.sparse_attn_layers([a["q"] for a in atts], [a["kv"] for a in atts], idx,
+                                        w.attn.scale, S, W, d_v=512, seq_lens=sl, want_lse=want_lse)
+    for layer, a in enumerate(atts):
+        o, l1 = lsa.sparse_attn(a["q"], a["kv"], None, idx, w.attn.scale, S, W, d_v=512, seq_lens=sl)
+        assert torch.equal(outs[layer].view(torch.int16), o.view(torch.int16)), layer
+        if want_lse:
+            assert torch.equal(lses[layer].view(torch.int32), l1.view(torch.int32)), layer
+    assert lses is None or len(lses) == n
+    if seq_lens is None:
+        attn_check(atts[-1]["q"], atts[-1]["kv"], None, idx, w.attn.scale, outs[-1],
+                   None if lses is None else lses[-1], True, 512)
+
+
+@pytest.mark.parametrize("B,T,L,k,n", [(8, 1, 6000, 256, 4), (2, 3, 3000, 2048, 3),
+                                       (1, 40, 3000, 300, 2), (3, 1, 700, 128, 8)])
+def test_attn_layers_match_single_calls(B, T, L, k, n):
+    """Decode (split partials merged for all layers in one combine launch), a query row per
+    workgroup with no splits (the prefill form), and the 8-layer limit."""
+    _layers_case(B, T, L, k, min(64, k // 4), min(200, k // 4), n, seed=51 + n)
+
+
+def test_attn_layers_ragged_and_no_lse():
+    _layers_case(3, 1, 4000, 256, 16, 112, 3, seed=61, seq_lens=[4000, 900, 0])
+    _layers_case(2, 1, 4000, 256, 16, 112, 2, seed=63, want_lse=False)
+
+
+def test_attn_layers_per_head_cache():
+    """A per-head (non-latent) cache: the layers run one after another, each equal to its own
+    call."""
+    B, T, H, L, k, d = 2, 3, 2, 400, 64, 64
+    g = torch.Generator().manual_seed(71)
+    qs = [torch.randn((B, T, H, d), generator=g).to(torch.bfloat16).to(DEV) for _ in range(2)]
+    ks = [torch.randn((B, L, d), generator=g).to(torch.bfloat16).to(DEV) for _ in range(2)]
+    vs = [torch.randn((B, L, d), generator=g).to(torch.bfloat16).to(DEV) for _ in range(2)]
+    idx = torch.randint(-1, L, (B, T, k), generator=g, dtype=torch.int32).to(DEV)
+    outs, lses = lsa.sparse_attn_layers(qs, ks, idx, 0.125, vs=vs, latent=False)
+    for layer in range(2):
+        o, l1 = lsa.sparse_attn(qs[layer], ks[layer], vs[layer], idx, 0.125, latent=False)
+        assert torch.equal(outs[layer].view(torch.int16), o.view(torch.int16))
+        assert torch.equal(lses[layer].view(torch.int32), l1.view(torch.int32))
+    attn_check(qs[1], ks[1], vs[1], idx, 0.125, outs[1], lses[1], False, d)
+
+
 # ------------------------------------------------------------------------------ determinism
 def test_determinism_decode_path():
     w = shrink(DECODE_128K, batch=4, kv_len=20000, q_pos0=19999)

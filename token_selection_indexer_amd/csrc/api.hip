@@ -553,34 +553,48 @@ lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int3
     return device_status(lsa::launch_fine_scores(f, sm));
 }
 
-lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_shape *attn,
-                           lsa_budget budget, const void *q, const void *k, const void *v,
-                           const int32_t *idx, void *out, float *lse, void *ws, size_t ws_bytes,
-                           void *stream)
+} // extern "C"
+
+namespace {
+
+// lsa_sparse_attn over n_layers layers that share one index list (n_layers == 1: the
+// single-layer call).  The pointer arrays are host arrays of device pointers.
+lsa_status sparse_attn_layers(const lsa_index_shape *shape, const lsa_attn_shape *attn,
+                              lsa_budget budget, int32_t n_layers, const void *const *q,
+                              const void *const *k, const void *const *v, const int32_t *idx,
+                              void *const *out, float *const *lse, void *ws, size_t ws_bytes,
+                              void *stream)
 {
     lsa_status st = check_attn(shape, attn, budget);
     if (st != LSA_OK) return st;
+    if (n_layers < 1 || n_layers > lsa::kMaxAttnLayers) return LSA_ERR_BAD_SHAPE;
     if (!q || !k || !v || !idx || !out) return LSA_ERR_NULL_POINTER;
-    if (attn->latent && v != k) return LSA_ERR_BAD_SHAPE;
+    for (int l = 0; l < n_layers; ++l) {
+        if (!q[l] || !k[l] || !v[l] || !out[l]) return LSA_ERR_NULL_POINTER;
+        if (attn->latent && v[l] != k[l]) return LSA_ERR_BAD_SHAPE;
+        if (!aligned(q[l], 16) || !aligned(k[l], 16) || !aligned(v[l], 16) || !aligned(out[l], 4) ||
+            (lse && lse[l] && !aligned(lse[l], 4)))
+            return LSA_ERR_BAD_SHAPE;
+    }
     if ((st = check_ragged(shape)) != LSA_OK) return st;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(idx, 4) ||
-        !aligned(out, 4) || (lse && !aligned(lse, 4)))
-        return LSA_ERR_BAD_SHAPE;
+    if (!aligned(idx, 4)) return LSA_ERR_BAD_SHAPE;
     if (budget.sink < 0 || budget.window < 0 || (int64_t)budget.sink + budget.window > budget.k)
         return LSA_ERR_BAD_SHAPE;
     const int64_t rows = (int64_t)shape->batch * shape->n_q;
     if (rows == 0) return LSA_OK;
-    if (rows * attn->n_heads >= (int64_t(1) << 31) * 4) return LSA_ERR_UNSUPPORTED;
-    const size_t need = round256(lsa::attn_workspace_bytes(shape->batch, shape->n_q, attn->n_heads,
-                                                           attn->d_v, budget.k, attn->latent));
+    if (rows * attn->n_heads * n_layers >= (int64_t(1) << 31) * 4) return LSA_ERR_UNSUPPORTED;
+    if ((int64_t)shape->batch * n_layers > kMaxGridYZ) return LSA_ERR_UNSUPPORTED;
+    const size_t per_layer = lsa::attn_workspace_bytes(shape->batch, shape->n_q, attn->n_heads,
+                                                       attn->d_v, budget.k, attn->latent);
+    const size_t need = round256(per_layer * n_layers);
     if (need && (!ws || ws_bytes < need || !aligned(ws, 256))) return LSA_ERR_WORKSPACE_TOO_SMALL;
     lsa::AttnArgs a{};
-    a.q = static_cast<const uint16_t *>(q);
-    a.k = static_cast<const uint16_t *>(k);
-    a.v = static_cast<const uint16_t *>(v);
+    a.q = static_cast<const uint16_t *>(q[0]);
+    a.k = static_cast<const uint16_t *>(k[0]);
+    a.v = static_cast<const uint16_t *>(v[0]);
     a.idx = idx;
-    a.out = static_cast<uint16_t *>(out);
-    a.lse = lse;
+    a.out = static_cast<uint16_t *>(out[0]);
+    a.lse = lse ? lse[0] : nullptr;
     a.ws = static_cast<float *>(ws);
     a.batch = shape->batch;
     a.n_q = shape->n_q;
@@ -598,8 +612,42 @@ lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_shape *a
     a.q_pos0 = shape->q_pos0;
     a.seq_pos0 = shape->seq_pos0;
     a.scale = attn->scale;
+    // the split count of one layer, so each layer's result is the single-layer call's, bit for bit
     a.n_split = lsa::attn_splits(shape->batch, shape->n_q, attn->n_heads, budget.k, attn->latent);
+    a.layers = n_layers;
+    a.ws_layer = (int64_t)(per_layer / sizeof(float));
+    for (int l = 0; l < n_layers; ++l) {
+        a.lq[l] = static_cast<const uint16_t *>(q[l]);
+        a.lk[l] = static_cast<const uint16_t *>(k[l]);
+        a.lv[l] = static_cast<const uint16_t *>(v[l]);
+        a.lout[l] = static_cast<uint16_t *>(out[l]);
+        a.llse[l] = lse ? lse[l] : nullptr;
+    }
     return device_status(lsa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)));
+}
+
+} // namespace
+
+extern "C" {
+
+lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_shape *attn,
+                           lsa_budget budget, const void *q, const void *k, const void *v,
+                           const int32_t *idx, void *out, float *lse, void *ws, size_t ws_bytes,
+                           void *stream)
+{
+    float *lse1[1] = {lse};
+    return sparse_attn_layers(shape, attn, budget, 1, &q, &k, &v, idx, &out, lse1, ws, ws_bytes,
+                              stream);
+}
+
+lsa_status lsa_sparse_attn_layers(const lsa_index_shape *shape, const lsa_attn_shape *attn,
+                                  lsa_budget budget, int32_t n_layers, const void *const *q,
+                                  const void *const *k, const void *const *v, const int32_t *idx,
+                                  void *const *out, float *const *lse, void *ws, size_t ws_bytes,
+                                  void *stream)
+{
+    return sparse_attn_layers(shape, attn, budget, n_layers, q, k, v, idx, out, lse, ws, ws_bytes,
+                              stream);
 }
 
 

@@ -104,7 +104,12 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     };
 
     const int HG = a.heads / 16;
-    const int b = blockIdx.z;
+    const int b = blockIdx.z % a.batch;
+    const int layer = blockIdx.z / a.batch;
+    const uint16_t *q_l = a.lq[layer], *k_l = a.lk[layer];
+    uint16_t *out_l = a.lout[layer];
+    float *lse_l = a.llse[layer];
+    float *ws_l = a.ws + layer * a.ws_layer;
     const int t = blockIdx.y / HG;
     const int hg = blockIdx.y % HG;
     const int split = blockIdx.x;
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     const int tile = w & 1, kh = w >> 1;
     bf16x8_t qf[KH];
     {
-        const uint16_t *qp = a.q + (qrow * a.heads + 16 * hg + (l & 15)) * DQK + 8 * (l >> 4) + 32 * KH * kh;
+        const uint16_t *qp = q_l + (qrow * a.heads + 16 * hg + (l & 15)) * DQK + 8 * (l >> 4) + 32 * KH * kh;
 #pragma unroll
         for (int kk = 0; kk < KH; ++kk) qf[kk] = bitcast<bf16x8_t>(ld16(qp + 32 * kk));
     }
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     f32x4_t oacc[NTW];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) oacc[nt] = f32x4_t{};
-    const uint8_t *kv_b = reinterpret_cast<const uint8_t *>(a.k) + (int64_t)b * a.kv_len * a.k_stride * 2;
+    const uint8_t *kv_b = reinterpret_cast<const uint8_t *>(k_l) + (int64_t)b * a.kv_len * a.k_stride * 2;
     const float sl2 = a.scale * kLog2e;
 
     // A round's rows through registers: thread t loads the 16-byte chunks f = 256*j + t of the
@@ -306,16 +311,16 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
             const int h = 4 * (l >> 4) + e;
             const float lr = l_run[h];
             const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-            uint16_t *op = a.out + (qrow * a.heads + 16 * hg + h) * DV;
+            uint16_t *op = out_l + (qrow * a.heads + 16 * hg + h) * DV;
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
                 const int col = w * (DV / 4) + 16 * nt + (l & 15);
                 op[col] = (uint16_t)f32_to_bf16_bits(oacc[nt][e] * inv);
             }
         }
-        if (a.lse && threadIdx.x < 16) {
+        if (lse_l && threadIdx.x < 16) {
             const float lr = l_run[threadIdx.x];
-            a.lse[qrow * a.heads + 16 * hg + threadIdx.x] =
+            lse_l[qrow * a.heads + 16 * hg + threadIdx.x] =
                 lr > 0.0f ? (m_run[threadIdx.x] + log2f(lr)) * kLn2 : -INFINITY;
         }
     } else {
@@ -324,12 +329,12 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int h = 4 * (l >> 4) + e;
-            float *pp = a.ws + ((qrow * a.heads + 16 * hg + h) * a.n_split + split) * stride;
+            float *pp = ws_l + ((qrow * a.heads + 16 * hg + h) * a.n_split + split) * stride;
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) pp[w * (DV / 4) + 16 * nt + (l & 15)] = oacc[nt][e];
         }
         if (threadIdx.x < 16) {
-            float *pp = a.ws + ((qrow * a.heads + 16 * hg + threadIdx.x) * a.n_split + split) * stride;
+            float *pp = ws_l + ((qrow * a.heads + 16 * hg + threadIdx.x) * a.n_split + split) * stride;
             pp[DV] = m_run[threadIdx.x];
             pp[DV + 1] = l_run[threadIdx.x];
         }
@@ -343,9 +348,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
 {
     __shared__ float wsp[MAX_SPLIT];
     __shared__ float inv_l;
-    const int64_t qh = blockIdx.x; // (b * n_q + t) * heads + h
+    const int64_t per_layer = (int64_t)a.batch * a.n_q * a.heads;
+    const int layer = (int)(blockIdx.x / per_layer);
+    const int64_t qh = blockIdx.x % per_layer; // (b * n_q + t) * heads + h
     const int64_t stride = a.d_v + 2;
-    const float *base = a.ws + qh * a.n_split * stride;
+    const float *base = a.ws + layer * a.ws_layer + qh * a.n_split * stride;
+    float *lse_l = a.llse[layer];
+    uint16_t *out_l = a.lout[layer];
     if (threadIdx.x < kWave) {
         const int s = threadIdx.x;
         const float m = s < a.n_split ? base[s * stride + a.d_v] : -INFINITY;
@@ -356,7 +365,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
         if (s < MAX_SPLIT) wsp[s] = e;
         if (s == 0) {
             inv_l = L > 0.0f ? 1.0f / L : 0.0f;
-            if (a.lse) a.lse[qh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+            if (lse_l) lse_l[qh] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
         }
     }
     __syncthreads();
@@ -365,7 +374,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
         float o = 0.0f;
 #pragma unroll 8
         for (int s = 0; s < a.n_split; ++s) o = fmaf(base[s * stride + c], wsp[s], o);
-        a.out[qh * a.d_v + c] = (uint16_t)f32_to_bf16_bits(o * il);
+        out_l[qh * a.d_v + c] = (uint16_t)f32_to_bf16_bits(o * il);
     }
 }
 
@@ -492,14 +501,26 @@ hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t st)
 {
     const int64_t rows = (int64_t)a.batch * a.n_q;
     if (rows == 0) return hipSuccess;
+    if (a.layers < 1 || a.layers > kMaxAttnLayers) return hipErrorInvalidValue;
     if (a.latent) {
-        dim3 grid((unsigned)a.n_split, (unsigned)(a.n_q * (a.heads / 16)), (unsigned)a.batch);
+        // every layer's gathers in one launch, then every layer's splits merged in one launch
+        dim3 grid((unsigned)a.n_split, (unsigned)(a.n_q * (a.heads / 16)),
+                  (unsigned)(a.batch * a.layers));
         hipLaunchKernelGGL((mla_attn_kernel<MLA_MAX_DQK, MLA_MAX_DV>), grid, dim3(256), 0, st, a);
         if (a.n_split > 1)
-            hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows * a.heads)), dim3(256), 0, st, a);
+            hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows * a.heads * a.layers)),
+                               dim3(256), 0, st, a);
     } else {
         const int64_t units = rows * a.heads;
-        hipLaunchKernelGGL(mha_attn_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, st, a);
+        for (int layer = 0; layer < a.layers; ++layer) {
+            AttnArgs al = a;
+            al.q = a.lq[layer];
+            al.k = a.lk[layer];
+            al.v = a.lv[layer];
+            al.out = a.lout[layer];
+            al.lse = a.llse[layer];
+            hipLaunchKernelGGL(mha_attn_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, st, al);
+        }
     }
     return hipGetLastError();
 }

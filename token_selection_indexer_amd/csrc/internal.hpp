@@ -118,6 +118,8 @@ hipError_t launch_page_summary(const void *keys, int fp8, const float *kscale, i
                                int64_t page_lo, int64_t page_hi, uint16_t *page_keys,
                                hipStream_t stream);
 
+constexpr int kMaxAttnLayers = 8;
+
 struct AttnArgs {
     const uint16_t *q;    // [B, n_q, Hq, d_qk]
     const uint16_t *k;    // [B, L, k_stride]
@@ -134,6 +136,15 @@ struct AttnArgs {
     const int32_t *seq_pos0;
     float scale;
     int n_split;          // workgroups per (query, head group); rounds are dealt to them in turn
+    // Latent kernel: `layers` layers over the one index list (grid z = layer * batch + b), each
+    // with its own q, cache, out and lse; the split partials of layer l start at ws + l * ws_layer
+    int layers;
+    int64_t ws_layer;
+    const uint16_t *lq[kMaxAttnLayers];
+    const uint16_t *lk[kMaxAttnLayers];
+    const uint16_t *lv[kMaxAttnLayers];
+    uint16_t *lout[kMaxAttnLayers];
+    float *llse[kMaxAttnLayers];
 };
 
 int attn_splits(int batch, int n_q, int heads, int n_idx, int latent);

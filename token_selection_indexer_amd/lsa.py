@@ -27,7 +27,9 @@ STATUS = {0: "LSA_OK", 1: "LSA_ERR_NULL_POINTER", 2: "LSA_ERR_BAD_SHAPE", 3: "LS
 EXPORTS = ("lsa_index_scores", "lsa_topk_select", "lsa_page_summary", "lsa_page_recall",
            "lsa_sparse_attn", "lsa_workspace_bytes", "lsa_status_string",
            "lsa_topk_select_noalloc", "lsa_index_select", "lsa_quantize_queries",
-           "lsa_index_scores_q8", "lsa_sparse_attn_backward", "lsa_index_scores_backward")
+           "lsa_index_scores_q8", "lsa_sparse_attn_backward", "lsa_index_scores_backward",
+           "lsa_sparse_attn_layers")
+MAX_ATTN_LAYERS = 8
 
 
 class IndexShape(ctypes.Structure):
@@ -77,6 +79,8 @@ def lib():
         L.lsa_page_recall.argtypes = [ip, bud, _I32, _I32, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP,
                                       _VP, _VP, _SZ, _VP]
         L.lsa_sparse_attn.argtypes = [ip, ap, bud, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]
+        L.lsa_sparse_attn_layers.argtypes = [ip, ap, bud, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                             _SZ, _VP]
         L.lsa_sparse_attn_backward.argtypes = [ip, ap, bud, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                                _VP, _VP, _VP, _VP]
         L.lsa_index_scores_backward.argtypes = [ip, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -394,14 +398,9 @@ def page_recall(q, w, page_keys, keys, key_scale, k, sink, window, page, m_pages
     return page_ids, cs, ci
 
 
-def sparse_attn(q, k, v, idx, scale, sink=0, window=0, d_v=None, latent=None, want_lse=True,
-                ws: Optional[Workspace] = None, out=None, stream=None, seq_lens=None, q_pos0=None,
-                seq_pos0=None):
-    """out [B, n_q, Hq, d_v] bf16 and lse [B, n_q, Hq] fp32 (or None).  Latent cache: pass v=None
-    (or v is k) and d_v = the value width.  sink, window and the query positions (q_pos0, default
-    L - n_q; seq_pos0 for a ragged batch) describe the lists' Streaming-Aware layout: the kernel
-    starts loading the rows that layout names before the lists arrive (the result never depends
-    on them)."""
+def _attn_layer(q, k, v, idx, d_v, latent, ref=None):
+    """Checks one layer's q [B, n_q, Hq, d_qk] / cache / index lists; returns (v, d_v, latent,
+    AttnShape args).  ref: the first layer's q and cache, which every later layer must match."""
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 3)
     _need(idx, "idx", torch.int32, 3)
@@ -410,7 +409,6 @@ def sparse_attn(q, k, v, idx, scale, sink=0, window=0, d_v=None, latent=None, wa
     if v is None:
         v = k
     B, T, Hq, dqk = q.shape
-    L = k.shape[1]
     dev = q.device
     _need(k, "k", torch.bfloat16, device=dev)
     if k.shape[0] != B or k.shape[2] < dqk:
@@ -425,16 +423,81 @@ def sparse_attn(q, k, v, idx, scale, sink=0, window=0, d_v=None, latent=None, wa
         d_v = v.shape[2] if not latent else dqk
     if d_v > v.shape[2]:
         raise ValueError(f"d_v {d_v} exceeds the value rows ({v.shape[2]})")
-    attn = AttnShape(Hq, dqk, d_v, 1 if latent else 0, k.shape[2], v.shape[2], scale)
+    if ref is not None:
+        q0, k0, v0 = ref
+        if q.shape != q0.shape or k.shape != k0.shape or v.shape != v0.shape or q.device != q0.device:
+            raise ValueError("every layer needs the first layer's q and cache shapes")
+    return v, d_v, latent, (Hq, dqk, d_v, 1 if latent else 0, k.shape[2], v.shape[2])
+
+
+def _attn_shape(q, k, idx, sink, window, seq_lens, q_pos0, seq_pos0):
+    B, T = q.shape[0], q.shape[1]
+    L = k.shape[1]
     pos0 = max(0, L - T) if q_pos0 is None else q_pos0
-    shape = _ragged(IndexShape(B, T, 64, 128, L, pos0), dev, seq_lens, seq_pos0)
-    bud = Budget(idx.shape[2], sink, window)
+    shape = _ragged(IndexShape(B, T, 64, 128, L, pos0), q.device, seq_lens, seq_pos0)
+    return shape, Budget(idx.shape[2], sink, window)
+
+
+def sparse_attn(q, k, v, idx, scale, sink=0, window=0, d_v=None, latent=None, want_lse=True,
+                ws: Optional[Workspace] = None, out=None, stream=None, seq_lens=None, q_pos0=None,
+                seq_pos0=None):
+    """out [B, n_q, Hq, d_v] bf16 and lse [B, n_q, Hq] fp32 (or None).  Latent cache: pass v=None
+    (or v is k) and d_v = the value width.  sink, window and the query positions (q_pos0, default
+    L - n_q; seq_pos0 for a ragged batch) describe the lists' Streaming-Aware layout: the kernel
+    starts loading the rows that layout names before the lists arrive (the result never depends
+    on them)."""
+    v, d_v, latent, ashape = _attn_layer(q, k, v, idx, d_v, latent)
+    attn = AttnShape(*ashape, scale)
+    shape, bud = _attn_shape(q, k, idx, sink, window, seq_lens, q_pos0, seq_pos0)
+    B, T, Hq = q.shape[:3]
+    dev = q.device
     out = _out(out, "out", (B, T, Hq, d_v), torch.bfloat16, dev)
     lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev) if want_lse else None
     nb = lsa_workspace_bytes(OP_SPARSE_ATTN, shape, bud, attn=attn)
     wsb = (ws or Workspace()).get(nb, dev)
     lsa_sparse_attn(shape, attn, bud, q, k, v, idx, out, lse, wsb, nb, stream)
     return out, lse
+
+
+def lsa_sparse_attn_layers(shape: IndexShape, attn: AttnShape, budget: Budget, qs, ks, vs, idx,
+                           outs, lses, ws, ws_bytes: int, stream=None):
+    n = len(qs)
+    arr = lambda ts: (ctypes.c_void_p * n)(*[None if t is None else t.data_ptr() for t in ts])
+    lse_arr = None if lses is None else arr(lses)
+    _check("lsa_sparse_attn_layers", lib().lsa_sparse_attn_layers(
+        ctypes.byref(shape), ctypes.byref(attn), budget, n, arr(qs), arr(ks), arr(vs), _p(idx),
+        arr(outs), lse_arr, _p(ws), ws_bytes, _s(stream)))
+
+
+def sparse_attn_layers(qs, ks, idx, scale, sink=0, window=0, d_v=None, vs=None, latent=None,
+                       want_lse=True, ws: Optional[Workspace] = None, outs=None, stream=None,
+                       seq_lens=None, q_pos0=None, seq_pos0=None):
+    """sparse_attn for a group of layers sharing one index list (Cross-Layer Indexing) in one
+    call: lists of per-layer q and cache (vs: per-layer value caches, None for latent caches)
+    -> lists of out and lse, each layer's bit-identical to its own sparse_attn call."""
+    n = len(qs)
+    if not 1 <= n <= MAX_ATTN_LAYERS or len(ks) != n or (vs is not None and len(vs) != n):
+        raise ValueError(f"1..{MAX_ATTN_LAYERS} layers, one q and one cache each")
+    vs = [None] * n if vs is None else list(vs)
+    v0, d_v0, latent0, ashape = _attn_layer(qs[0], ks[0], vs[0], idx, d_v, latent)
+    vv = [v0]
+    for l in range(1, n):
+        v, _, lat, ash = _attn_layer(qs[l], ks[l], vs[l], idx, d_v, latent, (qs[0], ks[0], v0))
+        if lat != latent0 or ash != ashape:
+            raise ValueError("every layer needs the first layer's attention shape")
+        vv.append(v)
+    attn = AttnShape(*ashape, scale)
+    shape, bud = _attn_shape(qs[0], ks[0], idx, sink, window, seq_lens, q_pos0, seq_pos0)
+    B, T, Hq = qs[0].shape[:3]
+    dev = qs[0].device
+    outs = [_out(None if outs is None else outs[l], "out", (B, T, Hq, d_v0), torch.bfloat16, dev)
+            for l in range(n)]
+    lses = ([torch.empty((B, T, Hq), dtype=torch.float32, device=dev) for _ in range(n)]
+            if want_lse else None)
+    nb = n * lsa_workspace_bytes(OP_SPARSE_ATTN, shape, bud, attn=attn)
+    wsb = (ws or Workspace()).get(nb, dev)
+    lsa_sparse_attn_layers(shape, attn, bud, qs, ks, vv, idx, outs, lses, wsb, nb, stream)
+    return outs, lses
 
 
 def sparse_attn_backward(q, k, v, idx, out, lse, d_out, scale, d_v=None, latent=None, d_q=None,
