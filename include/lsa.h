@@ -302,10 +302,14 @@ LSA_API lsa_status lsa_sparse_attn(const lsa_index_shape *shape, const lsa_attn_
 /*
  * lsa_sparse_attn_layers -- lsa_sparse_attn for n_layers consecutive layers that share one index
  * list (paper summary page, strategy (2): Cross-Layer Indexing computes the index once for a
- * group of layers; model card, CLI bullet).  Layer l's result is exactly (bit for bit) that of
- * lsa_sparse_attn(shape, attn, budget, q[l], k[l], v[l], idx, out[l], lse[l], ...): the same
- * arithmetic in the same order.  With a latent cache every layer's gathers run in one launch and
- * every layer's split partials are merged in one more, instead of two launches per layer.
+ * group of layers; model card, CLI bullet).  Layer l computes what
+ * lsa_sparse_attn(shape, attn, budget, q[l], k[l], v[l], idx, out[l], lse[l], ...) computes.
+ * With a latent cache every layer's gathers run in one launch and every layer's split partials
+ * are merged in one more, instead of two launches per layer; the number of parts the list is
+ * cut into for that merge is chosen for the whole launch (as for one layer of a batch n_layers
+ * times larger), so a layer's result can differ from the single call's in the last bits of the
+ * merge (it is bit-identical where both cut the list alike, and identical calls give identical
+ * bits).
  *   n_layers   1 .. 8
  *   q, k, v, out   host arrays of n_layers device pointers, each as for lsa_sparse_attn (the
  *              arrays are read during the call only; the caller keeps ownership)

@@ -195,7 +195,8 @@ def test_sparse_attn_layers_rejects(L):
     assert call(2, k=arr(FAKE + 4096, FAKE + 4100)) == 2         # a misaligned cache
     one = lsa.lsa_workspace_bytes(lsa.OP_SPARSE_ATTN, sh, b, attn=mla)
     assert one > 0
-    assert call(3, ws=FAKE, nb=2 * one) == 5                     # n_layers workspaces
+    assert call(3, ws=FAKE, nb=one // 2) == 5                    # too small for 3 layers
+    assert call(3, ws=None, nb=0) == 5                           # split-K needs a workspace
     nullarr = ctypes.cast(None, ctypes.POINTER(v))
     assert L.lsa_sparse_attn_layers(ctypes.byref(sh), ctypes.byref(mla), b, 2, nullarr,
                                     arr(FAKE, FAKE), arr(FAKE, FAKE), v(FAKE), arr(FAKE, FAKE),

@@ -584,9 +584,12 @@ lsa_status sparse_attn_layers(const lsa_index_shape *shape, const lsa_attn_shape
     if (rows == 0) return LSA_OK;
     if (rows * attn->n_heads * n_layers >= (int64_t(1) << 31) * 4) return LSA_ERR_UNSUPPORTED;
     if ((int64_t)shape->batch * n_layers > kMaxGridYZ) return LSA_ERR_UNSUPPORTED;
-    const size_t per_layer = lsa::attn_workspace_bytes(shape->batch, shape->n_q, attn->n_heads,
-                                                       attn->d_v, budget.k, attn->latent);
-    const size_t need = round256(per_layer * n_layers);
+    // the splits are chosen for the whole grid (every layer's workgroups), so a group of layers
+    // needs no more partials than one layer of a batch n_layers times larger
+    const size_t all_layers = lsa::attn_workspace_bytes(shape->batch * n_layers, shape->n_q,
+                                                        attn->n_heads, attn->d_v, budget.k,
+                                                        attn->latent);
+    const size_t need = round256(all_layers);
     if (need && (!ws || ws_bytes < need || !aligned(ws, 256))) return LSA_ERR_WORKSPACE_TOO_SMALL;
     lsa::AttnArgs a{};
     a.q = static_cast<const uint16_t *>(q[0]);
@@ -612,10 +615,10 @@ lsa_status sparse_attn_layers(const lsa_index_shape *shape, const lsa_attn_shape
     a.q_pos0 = shape->q_pos0;
     a.seq_pos0 = shape->seq_pos0;
     a.scale = attn->scale;
-    // the split count of one layer, so each layer's result is the single-layer call's, bit for bit
-    a.n_split = lsa::attn_splits(shape->batch, shape->n_q, attn->n_heads, budget.k, attn->latent);
+    a.n_split = lsa::attn_splits(shape->batch * n_layers, shape->n_q, attn->n_heads, budget.k,
+                                 attn->latent);
     a.layers = n_layers;
-    a.ws_layer = (int64_t)(per_layer / sizeof(float));
+    a.ws_layer = (int64_t)(all_layers / n_layers / sizeof(float));
     for (int l = 0; l < n_layers; ++l) {
         a.lq[l] = static_cast<const uint16_t *>(q[l]);
         a.lk[l] = static_cast<const uint16_t *>(k[l]);

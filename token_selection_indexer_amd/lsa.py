@@ -474,7 +474,8 @@ def sparse_attn_layers(qs, ks, idx, scale, sink=0, window=0, d_v=None, vs=None, 
                        seq_lens=None, q_pos0=None, seq_pos0=None):
     """sparse_attn for a group of layers sharing one index list (Cross-Layer Indexing) in one
     call: lists of per-layer q and cache (vs: per-layer value caches, None for latent caches)
-    -> lists of out and lse, each layer's bit-identical to its own sparse_attn call."""
+    -> lists of out and lse.  Each layer computes what its own sparse_attn call computes; the
+    split merge is planned for the whole launch, so the last bits can differ from that call."""
     n = len(qs)
     if not 1 <= n <= MAX_ATTN_LAYERS or len(ks) != n or (vs is not None and len(vs) != n):
         raise ValueError(f"1..{MAX_ATTN_LAYERS} layers, one q and one cache each")
