@@ -75,7 +75,10 @@ __device__ __forceinline__ void ring_barrier()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int DQK, int DV>
+// MULTI: several layers in one grid (z = layer * batch + b), each layer's pointers taken from the
+// argument arrays; the single-layer form reads them from the plain fields, with no lookup that
+// depends on the layer before its first loads can issue.
+template <int DQK, int DV, bool MULTI>
 __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
 {
     constexpr int ROWB = DQK * 2;          // LDS bytes per gathered row
@@ -104,12 +107,13 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     };
 
     const int HG = a.heads / 16;
-    const int b = blockIdx.z % a.batch;
-    const int layer = blockIdx.z / a.batch;
-    const uint16_t *q_l = a.lq[layer], *k_l = a.lk[layer];
-    uint16_t *out_l = a.lout[layer];
-    float *lse_l = a.llse[layer];
-    float *ws_l = a.ws + layer * a.ws_layer;
+    const int b = MULTI ? (int)(blockIdx.z % (unsigned)a.batch) : (int)blockIdx.z;
+    const int layer = MULTI ? (int)(blockIdx.z / (unsigned)a.batch) : 0;
+    const uint16_t *q_l = MULTI ? a.lq[layer] : a.q;
+    const uint16_t *k_l = MULTI ? a.lk[layer] : a.k;
+    uint16_t *out_l = MULTI ? a.lout[layer] : a.out;
+    float *lse_l = MULTI ? a.llse[layer] : a.lse;
+    float *ws_l = MULTI ? a.ws + layer * a.ws_layer : a.ws;
     const int t = blockIdx.y / HG;
     const int hg = blockIdx.y % HG;
     const int split = blockIdx.x;
@@ -344,17 +348,20 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
 // Merge the splits of one (query, head): fixed order over splits.
 constexpr int MAX_SPLIT = 32;
 
+template <bool MULTI>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
 {
     __shared__ float wsp[MAX_SPLIT];
     __shared__ float inv_l;
-    const int64_t per_layer = (int64_t)a.batch * a.n_q * a.heads;
-    const int layer = (int)(blockIdx.x / per_layer);
-    const int64_t qh = blockIdx.x % per_layer; // (b * n_q + t) * heads + h
+    // the split form only runs for small grids (fewer than 512 units of 16 heads): 32 bits hold
+    // every index here
+    const unsigned per_layer = (unsigned)a.batch * a.n_q * a.heads;
+    const int layer = MULTI ? (int)(blockIdx.x / per_layer) : 0;
+    const int64_t qh = MULTI ? blockIdx.x % per_layer : blockIdx.x; // (b * n_q + t) * heads + h
     const int64_t stride = a.d_v + 2;
-    const float *base = a.ws + layer * a.ws_layer + qh * a.n_split * stride;
-    float *lse_l = a.llse[layer];
-    uint16_t *out_l = a.lout[layer];
+    const float *base = (MULTI ? a.ws + layer * a.ws_layer : a.ws) + qh * a.n_split * stride;
+    float *lse_l = MULTI ? a.llse[layer] : a.lse;
+    uint16_t *out_l = MULTI ? a.lout[layer] : a.out;
     if (threadIdx.x < kWave) {
         const int s = threadIdx.x;
         const float m = s < a.n_split ? base[s * stride + a.d_v] : -INFINITY;
@@ -506,10 +513,14 @@ hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t st)
         // every layer's gathers in one launch, then every layer's splits merged in one launch
         dim3 grid((unsigned)a.n_split, (unsigned)(a.n_q * (a.heads / 16)),
                   (unsigned)(a.batch * a.layers));
-        hipLaunchKernelGGL((mla_attn_kernel<MLA_MAX_DQK, MLA_MAX_DV>), grid, dim3(256), 0, st, a);
-        if (a.n_split > 1)
-            hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows * a.heads * a.layers)),
-                               dim3(256), 0, st, a);
+        const dim3 cgrid((unsigned)(rows * a.heads * a.layers));
+        if (a.layers == 1) {
+            hipLaunchKernelGGL((mla_attn_kernel<MLA_MAX_DQK, MLA_MAX_DV, false>), grid, dim3(256), 0, st, a);
+            if (a.n_split > 1) hipLaunchKernelGGL(attn_combine_kernel<false>, cgrid, dim3(256), 0, st, a);
+        } else {
+            hipLaunchKernelGGL((mla_attn_kernel<MLA_MAX_DQK, MLA_MAX_DV, true>), grid, dim3(256), 0, st, a);
+            if (a.n_split > 1) hipLaunchKernelGGL(attn_combine_kernel<true>, cgrid, dim3(256), 0, st, a);
+        }
     } else {
         const int64_t units = rows * a.heads;
         for (int layer = 0; layer < a.layers; ++layer) {
