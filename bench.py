@@ -104,6 +104,17 @@ class Timing:
             self._acc = self.torch.zeros((), dtype=self.torch.float32, device="cuda")
         self.torch.sum(self._flush, dim=0, out=self._acc)
 
+    def queue_ahead(self, runs: int):
+        """Warm runs: hold the GPU in a timed-out wait (about 0.3 ms per run, at most 40 ms)
+        while the host enqueues every run, so that each run's events bracket its kernels and
+        not the host's time to launch them (stages shorter than their Python call would
+        otherwise time the host).  The wait itself is outside every event pair.  Cold runs need
+        none: the flush before each keeps the GPU busy while the host catches up."""
+        try:
+            self.torch.cuda._sleep(int(2.4e9 * min(0.04, 3e-4 * runs)))
+        except (AttributeError, RuntimeError):
+            pass
+
     def stats(self, fn, est_ms: float, cold: bool, runs=None):
         """>= 50 runs (>= 200 ms for long stages) of fn, each between two events; returns
         mean / median / p10 / p90 / min in ms."""
@@ -112,6 +123,8 @@ class Timing:
             runs = 50 if est_ms * 50 <= 1000 else max(15, math.ceil(200.0 / est_ms))
         fn()
         torch.cuda.synchronize()
+        if not cold:
+            self.queue_ahead(runs)
         evs = []
         for _ in range(runs):
             if cold:

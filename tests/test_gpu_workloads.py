@@ -178,9 +178,11 @@ def _hi_end_to_end(w, check_seqs, attn_seqs, flat_overlap_seqs):
         report[f"hi_flat_overlap_seq{r}"] = float(np.isin(gi[r, 0, d:], fl[r, 0, d:]).mean())
     del sc, flat, res
     torch.cuda.empty_cache()
-    # attention of every layer over the one HI index list
-    for layer in range(w.layers):
-        att = inputs.attn_inputs(w, layer, DEV)
+    # attention of every layer over the one HI index list: one call per layer, then (several
+    # layers) the same layers in one lsa_sparse_attn_layers call
+    atts = [inputs.attn_inputs(w, layer, DEV) for layer in range(w.layers)]
+    singles = []
+    for layer, att in enumerate(atts):
         o1, l1 = lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale, b.sink, b.window,
                                  d_v=a.d_v)
         if layer == 0:
@@ -190,8 +192,18 @@ def _hi_end_to_end(w, check_seqs, attn_seqs, flat_overlap_seqs):
         worst = attn_check(att["q"], att["kv"], None, idx, a.scale, o1, l1, True, a.d_v,
                            seqs=attn_seqs)
         say(f"{w.name}: layer {layer} attention worst |err| {worst:.2e}")
-        del att, o1, l1
-        torch.cuda.empty_cache()
+        singles.append(o1)
+    if w.layers > 1:
+        outs, lses = lsa.sparse_attn_layers([x["q"] for x in atts], [x["kv"] for x in atts], idx,
+                                            a.scale, b.sink, b.window, d_v=a.d_v)
+        for layer, att in enumerate(atts):
+            assert (outs[layer].float() - singles[layer].float()).abs().max().item() <= 2e-2
+            worst = attn_check(att["q"], att["kv"], None, idx, a.scale, outs[layer], lses[layer],
+                               True, a.d_v, seqs=attn_seqs)
+            say(f"{w.name}: layer {layer} of one multi-layer call, worst |err| {worst:.2e}")
+        del outs, lses
+    del atts, singles
+    torch.cuda.empty_cache()
     say(f"{w.name}: {report}")
     return report
 
@@ -206,6 +218,6 @@ def test_decode_b4_1m_hi_end_to_end():
 
 def test_decode_b8_256k_hi_cli4_end_to_end():
     """8 x 256K fp8 keys, HI with P = 64, M = 128, one index list reused by 4 MLA layers with
-    independent caches."""
+    independent caches, per layer and in one multi-layer call."""
     _hi_end_to_end(DECODE_256K_HI_CLI, check_seqs=(0, 7), attn_seqs=(0, 7),
                    flat_overlap_seqs=(0, 7))
