@@ -86,6 +86,9 @@ def profile_traffic(name: str, kernel_sources):
 
 
 # ----------------------------------------------------------------------------- timing
+SHORT_STAGE_MS = 0.06  # warm runs of stages up to this long are queued behind a GPU wait
+
+
 class Timing:
     """HIP events on the current stream (the stream the binding hands the library), and a 1 GiB
     buffer streamed through to flush L2 and the MALL before cold runs."""
@@ -105,17 +108,19 @@ class Timing:
         self.torch.sum(self._flush, dim=0, out=self._acc)
 
     def queue_ahead(self, runs: int):
-        """Warm runs: hold the GPU in a timed-out wait (about 0.3 ms per run, at most 40 ms)
-        while the host enqueues every run, so that each run's events bracket its kernels and
-        not the host's time to launch them (stages shorter than their Python call would
-        otherwise time the host).  The wait itself is outside every event pair.  Cold runs need
-        none: the flush before each keeps the GPU busy while the host catches up."""
+        """Warm runs of short stages: hold the GPU in a timed-out wait (about 0.3 ms per run, at
+        most 40 ms) while the host enqueues every run, so that each run's events bracket its
+        kernels and not the host's time to launch them (a stage shorter than its Python call
+        would otherwise time the host).  The wait itself is outside every event pair.  Long
+        stages keep the GPU ahead of the host by themselves, and after such a wait the chip
+        runs them slower (its clocks drop while it idles), so they are not queued; cold runs
+        need none either: the flush before each keeps the GPU busy while the host catches up."""
         try:
             self.torch.cuda._sleep(int(2.4e9 * min(0.04, 3e-4 * runs)))
         except (AttributeError, RuntimeError):
             pass
 
-    def stats(self, fn, est_ms: float, cold: bool, runs=None):
+    def stats(self, fn, est_ms: float, cold: bool, runs=None, queue=None):
         """>= 50 runs (>= 200 ms for long stages) of fn, each between two events; returns
         mean / median / p10 / p90 / min in ms."""
         torch = self.torch
@@ -123,7 +128,7 @@ class Timing:
             runs = 50 if est_ms * 50 <= 1000 else max(15, math.ceil(200.0 / est_ms))
         fn()
         torch.cuda.synchronize()
-        if not cold:
+        if not cold and (est_ms <= SHORT_STAGE_MS if queue is None else queue):
             self.queue_ahead(runs)
         evs = []
         for _ in range(runs):
@@ -144,8 +149,9 @@ class Timing:
         return {"n": runs, "mean": sum(t) / len(t), "median": pct(0.5), "p10": pct(0.1),
                 "p90": pct(0.9), "min": t[0]}
 
-    def both(self, fn, est_ms, cold_too=True):
-        out = {"warm": self.stats(fn, est_ms, cold=False)}
+    def both(self, fn, est_ms, cold_too=True, queue=None):
+        """queue: force (True) or forbid (False) queueing the warm runs; None decides by est_ms."""
+        out = {"warm": self.stats(fn, est_ms, cold=False, queue=queue)}
         if cold_too:
             out["cold"] = self.stats(fn, est_ms, cold=True)
         return out
@@ -465,7 +471,9 @@ def extra_hi(torch, lsa, inputs, w, tm: Timing):
             lsa.sparse_attn(at["q"], at["kv"], None, idx, a.scale, b.sink, b.window, d_v=a.d_v,
                             ws=ws, out=o, want_lse=False)
 
-    d["attn_all_layers"] = tm.both(f_attn, 0.02 * w.layers)
+    # several Python calls (or one with per-layer checks) cost the host more than the GPU time:
+    # both forms are queued
+    d["attn_all_layers"] = tm.both(f_attn, 0.02 * w.layers, queue=True)
     ws_layers = lsa.Workspace()
 
     def f_attn_layers():  # the same layers in one call: one gather launch, one combine launch
@@ -474,7 +482,7 @@ def extra_hi(torch, lsa, inputs, w, tm: Timing):
                                want_lse=False)
 
     if w.layers > 1:
-        d["attn_layers_one_call"] = tm.both(f_attn_layers, 0.02 * w.layers)
+        d["attn_layers_one_call"] = tm.both(f_attn_layers, 0.02 * w.layers, queue=True)
     t = {k: v["warm"]["mean"] for k, v in d.items()}
     tc = {k: v["cold"]["mean"] for k, v in d.items()}
     t_hi, t_flat = t["recall"] + t["hi_topk"], t["flat_index_fused"]
