@@ -7,11 +7,15 @@
 // several consecutive layers.)
 //
 // Latent (MLA) kernel.  A workgroup of 4 waves owns one (sequence, query, group of 16 heads) and
-// a contiguous chunk of the index list, in rounds of 32 selected rows (d_qk bf16 each).  While
-// round i is computed from LDS, every thread holds its share of round i+1's rows in registers
-// (16-byte loads; each row is one contiguous run in HBM, and the sink / window runs are
-// contiguous across rows) and writes them to the other LDS buffer afterwards.  The workgroup
-// uses under half a CU's LDS, so two of them share a CU and hide each other's latencies.
+// a share of the index list: the list's rounds of 32 selected rows (d_qk bf16 each) are dealt
+// to the workgroups of that query in turn.  While round i is computed from LDS, every thread
+// holds its share of round i+1's rows in registers (16-byte loads; each row is one contiguous
+// run in HBM, and the sink / window runs are contiguous across rows) and writes them to the
+// other LDS buffer afterwards.  A first round that lies in the sink and window is loaded from
+// the Streaming-Aware layout (model card, SI bullet) while the list itself is still arriving,
+// then checked against it.  The workgroup uses under half a CU's LDS, so two of them share a CU
+// and hide each other's latencies.  Several layers over one index list (Cross-Layer Indexing)
+// run in one grid, z = layer * batch + sequence.
 //   logits  S[16 x 32] = Q[16 x d_qk] . K^T   v_mfma_f32_16x16x32_bf16; each wave takes one
 //                                              16-row tile over half of d_qk
 //   softmax online, fp32, base-2 exponent, per head over the rounds
