@@ -515,6 +515,31 @@ def test_mla_attn_layout_hint_ragged():
     _layout_case(B=3, T=1, L=4000, k=256, S=16, W=112, seed=49, seq_lens=[4000, 1200, 200])
 
 
+@pytest.mark.parametrize("shift", [0, 7])
+def test_mla_attn_layout_hint_per_sequence_positions(shift):
+    """Per-sequence query positions (seq_pos0) with per-sequence lengths: two queries per
+    sequence at its last two positions, so V differs per sequence and per query.  shift = 7
+    hands the kernel positions 7 short of the lists' own: the window rounds fall back."""
+    B, T, L, k, S, W = 3, 2, 4000, 256, 16, 112
+    lens, pos = [4000, 1500, 300], [3998, 1498, 298]
+    w = Workload(name="a", index=IndexShape(
+        batch=B, n_q=T, kv_len=L, q_pos0=L - T, heads=64, head_dim=128, key_dtype="fp8"),
+        budget=DECODE_128K.budget, attn=DECODE_128K.attn, seed=53)
+    att = inputs.attn_inputs(w, 0, DEV)
+    idx = torch.stack([inputs.synthetic_index_lists(T, k, S, W, ref.valid_lengths(lens[b], pos[b], T),
+                                                    seed=55 + b) for b in range(B)]).to(DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    sp = torch.tensor([p - shift for p in pos], dtype=torch.int32, device=DEV)
+    out, lse = lsa.sparse_attn(att["q"], att["kv"], None, idx, w.attn.scale, S, W, d_v=512,
+                               seq_lens=sl, seq_pos0=sp)
+    out0, lse0 = lsa.sparse_attn(att["q"], att["kv"], None, idx, w.attn.scale, 0, 0, d_v=512,
+                                 seq_lens=sl)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out0.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse0.view(torch.int32))
+    attn_check(att["q"], att["kv"], None, idx, w.attn.scale, out, lse, True, 512)
+
+
 def test_mla_attn_empty_and_single_rows():
     L, k = 1000, 128
     w = shrink(DECODE_128K, batch=1, n_q=3, kv_len=L, q_pos0=L - 3)
