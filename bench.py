@@ -359,7 +359,8 @@ def _bwd_setup(torch, lsa, inputs, cfg):
 
     def f_index_bwd():
         lsa.index_scores_backward(inp["q"], inp["w"], inp["keys"], idx, d_sc, q_pos0=s.q_pos0,
-                                  d_q=grads["di_q"], d_w=grads["di_w"], d_keys=grads["di_k"])
+                                  d_q=grads["di_q"], d_w=grads["di_w"], d_keys=grads["di_k"],
+                                  sink=b.sink, window=b.window)
     return w, f_attn_bwd, f_index_bwd
 
 
@@ -374,9 +375,9 @@ def extra_backward(torch, lsa, inputs, cfg, tm: Timing):
     d = {"attn_bwd": tm.both(f_attn_bwd, 60.0, cold_too=False),
          "index_bwd": tm.both(f_index_bwd, 30.0, cold_too=False)}
     n_sel = s.n_q * b.k
-    # entries whose cache gradient the key-major pass sums over queries before adding it (the
-    # sink and window entries of every query whose sink and window are disjoint); the
-    # query-major kernel adds the rest, one fp32 atomic per row column
+    # entries whose cache (key) gradient the key-major passes sum over queries before adding it
+    # (the sink and window entries of every query whose sink and window are disjoint); the
+    # query-major kernels add the rest, one fp32 atomic per row column
     t_si = max(0, b.sink + b.window - s.q_pos0 - 1)
     n_si = max(0, s.n_q - t_si) * (b.sink + b.window)
     attn_flops = 2.0 * n_sel * a.heads * (3 * a.d_qk + 2 * a.d_v)
@@ -390,8 +391,9 @@ def extra_backward(torch, lsa, inputs, cfg, tm: Timing):
            "attn_bwd_atomic_updates_query_major": (n_sel - n_si) * a.d_qk,
            "index_bwd_flops": idx_flops, "index_bwd_TFLOPs": idx_flops / (ti * 1e-3) / 1e12,
            "index_bwd_mfma_frac": idx_flops / (ti * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS,
-           "index_bwd_atomic_updates": n_sel * s.head_dim,
-           "index_bwd_G_updates_per_s": n_sel * s.head_dim / (ti * 1e-3) / 1e9}
+           "index_bwd_entries": n_sel, "index_bwd_entries_key_major": n_si,
+           "index_bwd_G_entries_per_s": n_sel / (ti * 1e-3) / 1e9,
+           "index_bwd_atomic_updates_query_major": (n_sel - n_si) * s.head_dim}
     torch.cuda.empty_cache()
     return res
 

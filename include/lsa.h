@@ -377,15 +377,21 @@ LSA_API lsa_status lsa_sparse_attn_backward(const lsa_index_shape *shape, const 
  * inference-side encoding.  The gradients are ADDED into (fp32; zero them first), with fp32
  * atomics (summation order, and the last bits, can differ between runs).
  *   shape     as for lsa_index_scores (n_heads H <= 64, head_dim 64 or 128, ragged arrays allowed)
- *   k         entries per idx row
+ *   budget    k = entries per idx row.  sink / window with shape->q_pos0: the Streaming-Aware
+ *             layout the lists were selected with, as for lsa_sparse_attn_backward.  Where an
+ *             entry holds the row its position names and the query's sink and window are
+ *             disjoint, its d_keys share is summed over the queries that share the row before it
+ *             is added (uniform batches, head_dim 128); every other entry is added per query.
+ *             The sum is the same, in another order.  sink = window = 0 adds every entry per
+ *             query.  Checked: 0 <= sink, 0 <= window, sink + window <= k.
  *   q [B, n_q, H, d] bf16, 16-byte aligned;  w [B, n_q, H] fp32;  keys [B, L, d] bf16, 16-byte aligned
  *   idx [B, n_q, k] int32;  d_scores [B, n_q, k] fp32
  *   d_q [B, n_q, H, d] fp32;  d_w [B, n_q, H] fp32;  d_keys [B, L, d] fp32
  */
-LSA_API lsa_status lsa_index_scores_backward(const lsa_index_shape *shape, int32_t k, const void *q,
-                                             const float *w, const void *keys, const int32_t *idx,
-                                             const float *d_scores, float *d_q, float *d_w,
-                                             float *d_keys, void *stream);
+LSA_API lsa_status lsa_index_scores_backward(const lsa_index_shape *shape, lsa_budget budget,
+                                             const void *q, const float *w, const void *keys,
+                                             const int32_t *idx, const float *d_scores, float *d_q,
+                                             float *d_w, float *d_keys, void *stream);
 
 enum { LSA_OP_TOPK_SELECT = 1, LSA_OP_PAGE_RECALL = 2, LSA_OP_SPARSE_ATTN = 3,
        LSA_OP_INDEX_SELECT = 4 };

@@ -332,13 +332,15 @@ def test_backward_entry_points_reject(L):
     assert attn_call(mla, dk=FAKE + 2, dv=FAKE + 2) == 2  # fp32 alignment
     assert attn_call(lsa.AttnShape(8, 576, 512, 1, 576, 576, 0.04)) == 4
 
-    def idx_call(shape, k=2048, q=FAKE, keys=FAKE, dsc=FAKE):
-        return L.lsa_index_scores_backward(ctypes.byref(shape), k, v(q) if q else None, v(FAKE),
-                                           v(keys), v(FAKE), v(dsc) if dsc else None, v(FAKE),
-                                           v(FAKE), v(FAKE), None)
+    def idx_call(shape, k=2048, q=FAKE, keys=FAKE, dsc=FAKE, sink=0, window=0):
+        return L.lsa_index_scores_backward(ctypes.byref(shape), lsa.Budget(k, sink, window),
+                                           v(q) if q else None, v(FAKE), v(keys), v(FAKE),
+                                           v(dsc) if dsc else None, v(FAKE), v(FAKE), v(FAKE), None)
     assert idx_call(_shape(H=128)) == 4                  # at most 64 heads
     assert idx_call(_shape(d=96)) == 4                   # head_dim 64 or 128
     assert idx_call(_shape(), k=0) == 2
     assert idx_call(_shape(), q=0) == 1
     assert idx_call(_shape(), dsc=0) == 1
     assert idx_call(_shape(), keys=FAKE + 8) == 2        # 16-byte aligned keys
+    assert idx_call(_shape(), sink=-1) == 2              # the layout: 0 <= S, W; S + W <= k
+    assert idx_call(_shape(), sink=1024, window=1025) == 2

@@ -277,7 +277,11 @@ def _index_mag(q, w, K, idx, pos, gI, n_rows):
     return (Mq, Aq), (Mw, Aw), (MK, AK)
 
 
-def _index_case(B, T, H, d, L, k, seed, q_pos0=None, seq_lens=None, seq_pos0=None):
+def _index_case(B, T, H, d, L, k, seed, q_pos0=None, seq_lens=None, seq_pos0=None, lists=None,
+                si=(0, 0)):
+    """Random bf16 q / keys, head weights and score gradients over random lists with skipped and
+    repeated entries (or the given lists); the GPU backward against the oracle per sequence.
+    si = (sink, window): the lists' Streaming-Aware layout, passed on to the backward call."""
     g = _gen(seed)
     q = torch.randn((B, T, H, d), generator=g).to(torch.bfloat16)
     w = (torch.randn((B, T, H), generator=g) / 2).to(torch.float32)
@@ -287,12 +291,15 @@ def _index_case(B, T, H, d, L, k, seed, q_pos0=None, seq_lens=None, seq_pos0=Non
     idx[:, :, 1] = -1
     if k > 6:
         idx[:, :, 4] = idx[:, :, 6]
+    if lists is not None:
+        idx = torch.from_numpy(lists)
     gI = torch.randn((B, T, k), generator=g).to(torch.float32)
     pos0 = L - T if q_pos0 is None else q_pos0
     lens = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
     p0 = None if seq_pos0 is None else torch.tensor(seq_pos0, dtype=torch.int32, device=DEV)
     d_q, d_w, d_k = lsa.index_scores_backward(q.to(DEV), w.to(DEV), keys.to(DEV), idx.to(DEV),
-                                              gI.to(DEV), q_pos0=pos0, seq_lens=lens, seq_pos0=p0)
+                                              gI.to(DEV), q_pos0=pos0, seq_lens=lens, seq_pos0=p0,
+                                              sink=si[0], window=si[1])
     torch.cuda.synchronize()
     gq, gw, gk = (x.cpu().numpy().astype(np.float64) for x in (d_q, d_w, d_k))
     for b in range(B):
@@ -323,6 +330,32 @@ def _index_case(B, T, H, d, L, k, seed, q_pos0=None, seq_lens=None, seq_pos0=Non
 def test_index_backward_heads_and_widths(H, d):
     """One to four waves per workgroup (16 heads each, the last one padded)."""
     _index_case(B=2, T=4, H=H, d=d, L=500, k=128, seed=11 + H)
+
+
+@pytest.mark.parametrize("H", [64, 20])
+def test_index_backward_streaming_aware_lists(H):
+    """Prefill-shaped lists in the Streaming-Aware layout with the layout passed on: the sink and
+    window entries' key gradient is summed row by row over the queries (the key-major pass), the
+    rest per query.  Entries that break the layout stay with the per-query path: a window entry
+    holding another row, a sink entry holding another row, a skipped sink entry, and a window
+    row selected again among the dynamic picks.  Queries past the cache end (V = L for the
+    last ones); 20 heads leave the pass's missing heads zero."""
+    B, T, L, q0, k, S, W = 2, 300, 1480, 1200, 256, 16, 112
+    idx = _si_lists(B, T, L, q0, k, S, W, seed=31)
+    idx[:, 5, S + 3] = 40
+    idx[:, 7, 2] = 500
+    idx[:, 9, 1] = -1
+    idx[:, 11, S + W] = idx[:, 11, S + W - 1]
+    _index_case(B=B, T=T, H=H, d=128, L=L, k=k, seed=32 + H, q_pos0=q0, lists=idx, si=(S, W))
+
+
+def test_index_backward_streaming_aware_early_queries():
+    """A chunk from the start of a sequence: the first queries see fewer than k rows and take
+    all of them; the earliest have a window reaching into the sink (none of their entries is
+    key-major).  64 sink rows (one whole block) and a 64-row window."""
+    B, T, L, q0, k, S, W = 1, 400, 400, 0, 200, 64, 64
+    idx = _si_lists(B, T, L, q0, k, S, W, seed=33)
+    _index_case(B=B, T=T, H=64, d=128, L=L, k=k, seed=34, q_pos0=q0, lists=idx, si=(S, W))
 
 
 def test_index_backward_causal_prefill_and_splits():
@@ -384,7 +417,7 @@ def test_backward_prefill_8k_128k_full_shape():
                                             a.scale, d_v=a.d_v, sink=b.sink, window=b.window,
                                             q_pos0=s.q_pos0)
     di_q, di_w, di_k = lsa.index_scores_backward(inp["q"], inp["w"], inp["keys"], idx, dsc,
-                                                 q_pos0=s.q_pos0)
+                                                 q_pos0=s.q_pos0, sink=b.sink, window=b.window)
     torch.cuda.synchronize()
     dv = a.d_v
     # attention identities

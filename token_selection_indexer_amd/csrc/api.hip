@@ -707,15 +707,18 @@ lsa_status lsa_sparse_attn_backward(const lsa_index_shape *shape, const lsa_attn
     return device_status(lsa::launch_sparse_attn_backward(a, static_cast<hipStream_t>(stream)));
 }
 
-lsa_status lsa_index_scores_backward(const lsa_index_shape *shape, int32_t k, const void *q,
-                                     const float *w, const void *keys, const int32_t *idx,
-                                     const float *d_scores, float *d_q, float *d_w, float *d_keys,
-                                     void *stream)
+lsa_status lsa_index_scores_backward(const lsa_index_shape *shape, lsa_budget budget,
+                                     const void *q, const float *w, const void *keys,
+                                     const int32_t *idx, const float *d_scores, float *d_q,
+                                     float *d_w, float *d_keys, void *stream)
 {
     if (!shape) return LSA_ERR_NULL_POINTER;
+    const int32_t k = budget.k;
     if (shape->batch < 0 || shape->n_q < 0 || shape->kv_len < 1 ||
         shape->kv_len >= (int64_t(1) << 31) || shape->q_pos0 < 0 || shape->batch > kMaxGridYZ ||
         shape->n_heads < 1 || shape->head_dim < 1 || k < 1)
+        return LSA_ERR_BAD_SHAPE;
+    if (budget.sink < 0 || budget.window < 0 || (int64_t)budget.sink + budget.window > k)
         return LSA_ERR_BAD_SHAPE;
     if (!lsa::index_bwd_supported(shape->n_heads, shape->head_dim)) return LSA_ERR_UNSUPPORTED;
     if (shape->n_q > kMaxGridYZ) return LSA_ERR_UNSUPPORTED;
@@ -745,6 +748,9 @@ lsa_status lsa_index_scores_backward(const lsa_index_shape *shape, int32_t k, co
     a.seq_len = shape->seq_len;
     a.seq_pos0 = shape->seq_pos0;
     a.n_split = lsa::index_bwd_splits(shape->batch, shape->n_q, k);
+    a.sink = budget.sink;
+    a.window = budget.window;
+    a.si = 0; // decided at launch
     return device_status(lsa::launch_index_scores_backward(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -25,6 +25,7 @@
 // lanes own columns; the two dot products per row are wave sums.
 #include "device.hpp"
 #include "internal.hpp"
+#include "si_layout.hpp"
 
 namespace lsa {
 namespace {
@@ -84,55 +85,12 @@ __device__ __forceinline__ void ring_barrier()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// ---- Streaming-Aware entries: which (query, row) pairs the key-major pass takes ----
-constexpr int SRB = 64;  // cache rows per key-major workgroup
-constexpr int SQC = 128; // queries per key-major workgroup
-
-struct SiPlan {
-    int nsb;      // sink blocks: rows [SRB i, min(S, SRB (i + 1)))
-    int64_t wlo;  // window blocks follow: rows [wlo + SRB j, + SRB)
-    int64_t t_si; // first query whose sink and window are disjoint
-    int cs, cw;   // query chunks per sink block and per window block
-};
-
-__host__ __device__ __forceinline__ int64_t imin(int64_t x, int64_t y) { return x < y ? x : y; }
-__host__ __device__ __forceinline__ int64_t imax(int64_t x, int64_t y) { return x > y ? x : y; }
-
-// V_t, the valid length the selection gives query t (causal, uniform batch)
-__host__ __device__ __forceinline__ int64_t si_valid_len(const AttnBwdArgs &a, int64_t t)
-{
-    return imin(a.kv_len, a.q_pos0 + t + 1);
-}
-
-// Entry j (holding id) of the list of a query of valid length V: the key-major pass takes it
-// when the query's sink and window are disjoint and the entry holds the row the Streaming-Aware
-// layout puts there (sink row j, or window row V - W + j - S).
-__device__ __forceinline__ bool si_entry(const AttnBwdArgs &a, int64_t V, int j, int32_t id)
-{
-    if (V - a.window < a.sink) return false;
-    if (j < a.sink) return id == j;
-    if (j < a.sink + a.window) return (int64_t)id == V - a.window + (j - a.sink);
-    return false;
-}
-
-// Rows [r0, r1) of key-major block blk and the queries [t_lo, t_hi) whose sink or window can
-// reach them (V_t > r0 and V_t - W < r1 for a window block).
-__host__ __device__ __forceinline__ void si_block(const AttnBwdArgs &a, const SiPlan &p, int blk,
-                                                  int64_t &r0, int64_t &r1, int64_t &t_lo,
-                                                  int64_t &t_hi)
-{
-    if (blk < p.nsb) {
-        r0 = (int64_t)SRB * blk;
-        r1 = imin(a.sink, r0 + SRB);
-        t_lo = p.t_si;
-        t_hi = a.n_q;
-        return;
-    }
-    r0 = p.wlo + (int64_t)SRB * (blk - p.nsb);
-    r1 = imin(r0 + SRB, a.kv_len);
-    t_lo = imax(p.t_si, r0 - a.q_pos0);
-    t_hi = a.kv_len < r1 + a.window ? a.n_q : imin(a.n_q, r1 + a.window - a.q_pos0 - 1);
-}
+// ---- Streaming-Aware entries: which (query, row) pairs the key-major pass takes (si_layout.hpp) ----
+using si::SQC;
+using si::SRB;
+using si::imax;
+using si::imin;
+using SiPlan = si::Plan;
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 2) void mla_attn_bwd_kernel(AttnBwdArgs a)
@@ -176,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_bwd_kernel(AttnBwdArgs a)
     const int32_t *idx_row = a.idx + qrow * a.n_idx;
     const int64_t seq_rows = seq_keys(a.seq_len, b, a.kv_len);
     // the key-major pass adds this query's Streaming-Aware entries to the cache gradient
-    const int64_t v_si = si_valid_len(a, t);
+    const int64_t v_si = si::valid_len(a, t);
     const bool si_q = a.si && v_si - a.window >= a.sink;
     auto id_load = [&](int round) -> int32_t { // unconditional load of a clamped entry
         const int j = c_begin + round * BR + (int)(threadIdx.x % BR);
@@ -339,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_bwd_kernel(AttnBwdArgs a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 rowid[e] = ids[4 * g4 + e];
-                if (si_q && rowid[e] >= 0 && si_entry(a, v_si, c_begin + i * BR + 4 * g4 + e, rowid[e]))
+                if (si_q && rowid[e] >= 0 && si::taken(a, v_si, c_begin + i * BR + 4 * g4 + e, rowid[e]))
                     rowid[e] = -1;
             }
             // transposing reads: lane j of group g4 addresses row 4 g4 + j/4, columns
@@ -413,11 +371,10 @@ __global__ __launch_bounds__(512, 1) void mla_attn_bwd_si_kernel(AttnBwdArgs a, 
     const int HG = a.heads / 16;
     const int b = blockIdx.z / HG, hg = blockIdx.z % HG;
     // workgroup -> (block, query chunk): the sink blocks' chunks, then the window blocks'
-    const int gs = p.nsb * p.cs, g = (int)blockIdx.x;
-    const int blk = g < gs ? g / p.cs : p.nsb + (g - gs) / p.cw;
-    const int chunk = g < gs ? g % p.cs : (g - gs) % p.cw;
+    int blk, chunk;
+    si::workgroup(p, (int)blockIdx.x, blk, chunk);
     int64_t r0, r1, t_lo, t_hi;
-    si_block(a, p, blk, r0, r1, t_lo, t_hi);
+    si::block(a, p, blk, r0, r1, t_lo, t_hi);
     const int64_t c0 = t_lo + (int64_t)chunk * SQC;
     const int64_t c1 = imin(t_hi, c0 + SQC);
     if (c0 >= c1 || r0 >= r1) return; // the same for every thread
@@ -453,7 +410,7 @@ __global__ __launch_bounds__(512, 1) void mla_attn_bwd_si_kernel(AttnBwdArgs a, 
         oreg[0] = ld16(a.out + ob);
         oreg[1] = ld16(a.out + ob + 8);
         lreg = a.lse[qh0 + (tid & 15)];
-        const int64_t V = si_valid_len(a, t), r = r0 + (tid & (SRB - 1));
+        const int64_t V = si::valid_len(a, t), r = r0 + (tid & (SRB - 1));
         const int64_t j = sink_blk ? r : a.sink + r - (V - a.window);
         ireg = a.idx[qrow * a.n_idx + imin(imax(j, 0), a.n_idx - 1)]; // clamped, always valid
     };
@@ -490,7 +447,7 @@ __global__ __launch_bounds__(512, 1) void mla_attn_bwd_si_kernel(AttnBwdArgs a, 
         if ((tid & 31) == 31) Dh[h] = acc;
         if (tid < 16) lse2[tid] = lreg * kLog2e;
         if (tid < SRB) {
-            const int64_t V = si_valid_len(a, t), r = r0 + tid;
+            const int64_t V = si::valid_len(a, t), r = r0 + tid;
             const bool in = r < r1 && (sink_blk || (r >= V - a.window && r < V));
             rsel[tid] = in && (int64_t)ireg == r;
         }
@@ -677,46 +634,6 @@ int attn_bwd_splits(int batch, int n_q, int heads, int n_idx, int latent)
     return want < 1 ? 1 : (int)want;
 }
 
-namespace {
-
-// The key-major pass's blocks and query chunks, or false where it does not apply (a ragged
-// batch, no sink or window, no query whose sink and window are disjoint) or would not pay: it
-// pays when each row update it makes stands for many queries' updates (prefill chunks), and
-// not when every row is reached by one query or few (decode).
-bool si_plan(const AttnBwdArgs &a, SiPlan &p, int &nblk, int &nchunk)
-{
-    const int64_t S = a.sink, W = a.window;
-    if (!a.latent || a.seq_len || a.q_pos0 < 0 || S < 0 || W < 0 || S + W == 0 || a.n_q < 1 ||
-        a.kv_len < S + W)
-        return false;
-    p.t_si = imax(0, S + W - a.q_pos0 - 1);
-    if (p.t_si >= a.n_q) return false;
-    p.nsb = (int)((S + SRB - 1) / SRB);
-    const int64_t vmin = si_valid_len(a, p.t_si), vmax = si_valid_len(a, a.n_q - 1);
-    p.wlo = S + SRB * ((vmin - W - S) / SRB); // vmin >= S + W
-    const int64_t nwb = W > 0 ? (vmax - p.wlo + SRB - 1) / SRB : 0;
-    if (p.nsb + nwb > (int64_t(1) << 30)) return false;
-    nblk = (int)(p.nsb + nwb);
-    int64_t span_s = 0, span_w = 0;
-    for (int blk = 0; blk < nblk; ++blk) {
-        int64_t r0, r1, t_lo, t_hi;
-        si_block(a, p, blk, r0, r1, t_lo, t_hi);
-        if (r0 < r1) (blk < p.nsb ? span_s : span_w) = imax(blk < p.nsb ? span_s : span_w, t_hi - t_lo);
-    }
-    p.cs = (int)((span_s + SQC - 1) / SQC);
-    p.cw = (int)((span_w + SQC - 1) / SQC);
-    if (p.nsb > 0 && p.cs < 1) p.cs = 1;
-    if (nwb > 0 && p.cw < 1) p.cw = 1;
-    const int64_t groups = (int64_t)p.nsb * p.cs + nwb * p.cw;
-    if (groups < 1 || groups >= (int64_t(1) << 31) || (int64_t)a.batch * (a.heads / 16) > 65535)
-        return false;
-    nchunk = (int)groups; // workgroups per (sequence, head group)
-    const int64_t taken = (int64_t)(a.n_q - p.t_si) * (S + W); // entries the pass takes
-    const int64_t own = groups * SRB;                          // row updates it makes
-    return taken >= 8 * own;
-}
-
-} // namespace
 
 hipError_t launch_sparse_attn_backward(const AttnBwdArgs &args, hipStream_t st)
 {
@@ -726,7 +643,10 @@ hipError_t launch_sparse_attn_backward(const AttnBwdArgs &args, hipStream_t st)
     if (a.latent) {
         SiPlan p{};
         int nblk = 0, nchunk = 0;
-        a.si = si_plan(a, p, nblk, nchunk) ? 1 : 0;
+        a.si = a.latent && !a.seq_len &&
+                       si::plan(a, p, nblk, nchunk, (int64_t)a.batch * (a.heads / 16))
+                   ? 1
+                   : 0;
         dim3 grid((unsigned)a.n_split, (unsigned)(a.n_q * (a.heads / 16)), (unsigned)a.batch);
         hipLaunchKernelGGL((mla_attn_bwd_kernel<MLA_DQK, MLA_DV>), grid, dim3(256), 0, st, a);
         if (a.si) {

@@ -190,6 +190,9 @@ struct IndexBwdArgs {
     int64_t kv_len, q_pos0;
     const int32_t *seq_len, *seq_pos0; // [B] ragged batch (device) or nullptr
     int n_split;              // chunks of the index list per query
+    // Streaming-Aware entries (sink [0, S) and window [S, S + W) of each list, as the selection
+    // lays them out) whose key gradient the key-major pass adds: si != 0
+    int sink, window, si;
 };
 
 bool index_bwd_supported(int heads, int dim);

@@ -83,7 +83,7 @@ def lib():
                                              _SZ, _VP]
         L.lsa_sparse_attn_backward.argtypes = [ip, ap, bud, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                                _VP, _VP, _VP, _VP]
-        L.lsa_index_scores_backward.argtypes = [ip, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+        L.lsa_index_scores_backward.argtypes = [ip, bud, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                                 _VP]
         L.lsa_workspace_bytes.argtypes = [_I32, ip, bud, _I32, _I32, _I64, ap]
         L.lsa_workspace_bytes.restype = _SZ
@@ -180,11 +180,11 @@ def lsa_sparse_attn_backward(shape: IndexShape, attn: AttnShape, budget: Budget,
         _p(lse), _p(d_out), _p(d_q), _p(d_k), _p(d_v), _s(stream)))
 
 
-def lsa_index_scores_backward(shape: IndexShape, k: int, q, w, keys, idx, d_scores, d_q, d_w,
-                              d_keys, stream=None):
+def lsa_index_scores_backward(shape: IndexShape, budget: Budget, q, w, keys, idx, d_scores, d_q,
+                              d_w, d_keys, stream=None):
     _check("lsa_index_scores_backward", lib().lsa_index_scores_backward(
-        ctypes.byref(shape), k, _p(q), _p(w), _p(keys), _p(idx), _p(d_scores), _p(d_q), _p(d_w),
-        _p(d_keys), _s(stream)))
+        ctypes.byref(shape), budget, _p(q), _p(w), _p(keys), _p(idx), _p(d_scores), _p(d_q),
+        _p(d_w), _p(d_keys), _s(stream)))
 
 
 def lsa_workspace_bytes(op: int, shape: Optional[IndexShape], budget: Budget, page_size: int = 0,
@@ -549,10 +549,12 @@ def sparse_attn_backward(q, k, v, idx, out, lse, d_out, scale, d_v=None, latent=
 
 
 def index_scores_backward(q, w, keys, idx, d_scores, q_pos0=None, d_q=None, d_w=None,
-                          d_keys=None, stream=None, seq_lens=None, seq_pos0=None):
+                          d_keys=None, stream=None, seq_lens=None, seq_pos0=None, sink=0, window=0):
     """Gradients of the indexer scores at the selected entries idx [B,n_q,k] for d_scores
     [B,n_q,k] fp32, ADDED into fp32 d_q [B,n_q,H,d], d_w [B,n_q,H], d_keys [B,L,d] (zeros are
-    allocated for the ones not given).  bf16 keys."""
+    allocated for the ones not given).  bf16 keys.  sink and window (with q_pos0) describe the
+    lists' Streaming-Aware layout, which lets the library sum the sink and window rows' key
+    gradients row by row."""
     _need(q, "q", torch.bfloat16, 4)
     _check_index_operands(q, w, keys)
     if keys.dtype != torch.bfloat16:
@@ -568,8 +570,8 @@ def index_scores_backward(q, w, keys, idx, d_scores, q_pos0=None, d_q=None, d_w=
     d_w = _zeros_or(d_w, "d_w", (B, T, H), dev)
     d_keys = _zeros_or(d_keys, "d_keys", (B, L, d), dev)
     shape = index_shape(q, keys, q_pos0, seq_lens, seq_pos0)
-    lsa_index_scores_backward(shape, idx.shape[2], q, w, keys, idx, d_scores, d_q, d_w, d_keys,
-                              stream)
+    lsa_index_scores_backward(shape, Budget(idx.shape[2], sink, window), q, w, keys, idx,
+                              d_scores, d_q, d_w, d_keys, stream)
     return d_q, d_w, d_keys
 
 
