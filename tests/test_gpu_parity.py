@@ -678,6 +678,7 @@ def _layers_case(B, T, L, k, S, W, n, seed, exact, seq_lens=None, want_lse=True,
     (2, 3, 3000, 2048, 3, False, None),    # 32 splits alone, 29 over the 3 layers
     (1, 600, 3000, 256, 2, True, [0, 1, 299, 599]),  # one part either way (the prefill form)
     (3, 1, 700, 128, 8, True, None),       # 4 splits either way; the 8-layer limit
+    (4, 1, 6000, 256, 1, True, None),      # one layer: the single-layer launch itself
 ])
 def test_attn_layers_against_single_calls_and_oracle(B, T, L, k, n, exact, rows):
     _layers_case(B, T, L, k, min(64, k // 4), min(200, k // 4), n, seed=51 + n, exact=exact,
