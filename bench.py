@@ -157,6 +157,21 @@ class Timing:
         return out
 
 
+PAGE_BLOCK = 64  # rows per block of the paged cache timed beside the dense one
+
+
+def paged_copy(torch, kv, bs):
+    """A dense cache [B, L, row] as a pool of bs-row blocks in a random order, and its block
+    table [B, L / bs] (L a multiple of bs)."""
+    B, L, row = kv.shape
+    n = B * (L // bs)
+    g = torch.Generator(device=kv.device).manual_seed(7)
+    perm = torch.randperm(n, device=kv.device, generator=g)
+    pool = torch.empty((n, bs, row), dtype=kv.dtype, device=kv.device)
+    pool[perm] = kv.reshape(n, bs, row)
+    return pool, perm.view(B, L // bs).to(torch.int32)
+
+
 def rnd(x, nd=4):
     if isinstance(x, dict):
         return {k: rnd(v, nd) for k, v in x.items()}
@@ -215,6 +230,15 @@ def headline(torch, lsa, inputs, cfg, tm: Timing, steps, warmup):
     log("[bench] headline: per-stage distributions (warm and cold)")
     dist = {"index": tm.both(f_index, st["index"]), "score": tm.both(f_score, 0.1),
             "topk": tm.both(f_topk, 0.02), "attn": tm.both(f_attn, st["attn"])}
+    # the same attention over a paged copy of the cache: 64-row blocks in a shuffled pool
+    pool, tab = paged_copy(torch, att["kv"], PAGE_BLOCK)
+
+    def f_attn_paged():
+        lsa.sparse_attn(att["q"], pool, None, idx, a.scale, b.sink, b.window, d_v=a.d_v, ws=ws,
+                        out=out, want_lse=True, block_table=tab, kv_len=L)
+    f_attn_paged()
+    dist["attn_paged"] = tm.both(f_attn_paged, st["attn"])
+    del pool, tab
     f_index()
     n_q = B * s.n_q
     sb = score_bytes(n_q * L, s.head_dim, True, s.heads, n_q)
@@ -683,6 +707,12 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
                                                  scores=scores, idx=idx, ws=ws_idx),
                "attn": lambda: lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale, b.sink,
                                                b.window, d_v=a.d_v, ws=ws)}
+        if stage == "attn_paged":
+            att = inputs.attn_inputs(w, 0, dev)
+            pool, tab = paged_copy(torch, att["kv"], PAGE_BLOCK)
+            fns[stage] = lambda: lsa.sparse_attn(att["q"], pool, None, idx, a.scale, b.sink,
+                                                 b.window, d_v=a.d_v, ws=ws, block_table=tab,
+                                                 kv_len=L)
     fn = fns[stage]
     fn()
     torch.cuda.synchronize()
@@ -696,7 +726,7 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
 
 STAGES = ["score", "topk", "index", "attn", "copy", "prefill_score", "prefill_topk", "prefill_attn",
           "prefill_q8", "bwd_attn", "bwd_index",
-          "hi1m_summary", "hi1m_recall", "hi1m_topk", "cli4_attn", "cli4_attn_layers"]
+          "hi1m_summary", "hi1m_recall", "hi1m_topk", "cli4_attn", "cli4_attn_layers", "attn_paged"]
 
 
 def main():
@@ -782,6 +812,9 @@ def main():
         "indexed_qps_unfused": head["indexed_qps_unfused"],
         "step_qps": head["step_qps"],
         "sparse_attn_TBps": head["sparse_attn_TBps"],
+        "sparse_attn_paged_vs_dense": {
+            m: head["dist"]["attn_paged"][m]["mean"] / head["dist"]["attn"][m]["mean"]
+            for m in ("warm", "cold")},
         "stage_ms": head["stage_ms"],
         "stage_dist_ms": rnd(head["dist"]),
         "hbm_frac_cold_mean": head["hbm_frac_cold_mean"],

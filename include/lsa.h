@@ -101,6 +101,17 @@ typedef struct {
     int32_t n_heads, d_qk, d_v, latent;
     int64_t k_row_stride, v_row_stride;
     float scale; /* softmax temperature applied to q . k */
+    /* Paged latent cache (optional; block_table NULL = dense caches [B, L, row]).  The cache
+     * k (== v) is then a pool of n_blocks blocks of block_size rows, [n_blocks * block_size,
+     * row], and token s of sequence b is pool row
+     *     block_table[b * blocks_per_seq + s / block_size] * block_size + s % block_size.
+     * A table entry outside [0, n_blocks) makes the tokens of that block skipped entries.
+     * block_size a power of two; blocks_per_seq * block_size >= kv_len;
+     * n_blocks * block_size < 2^31.  lsa_sparse_attn and lsa_sparse_attn_layers (latent
+     * caches) take it; the per-head cache and the backward do not. */
+    const int32_t *block_table; /* [B, blocks_per_seq] int32, device */
+    int32_t block_size, blocks_per_seq;
+    int64_t n_blocks;
 } lsa_attn_shape;
 
 /*
@@ -286,7 +297,8 @@ LSA_API lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budg
  *           is a hint: every result is that of the list as given, whatever sink, window and
  *           the positions say.  Checked: 0 <= sink, 0 <= window, sink + window <= k.
  *   q       [B, n_q, Hq, d_qk] bf16
- *   k, v    [B, L, row_stride] bf16 (latent: v == k)
+ *   k, v    [B, L, row_stride] bf16 (latent: v == k), or with attn->block_table a pool of
+ *           blocks (see lsa_attn_shape): the ids stay token positions, the table finds the rows
  *   idx     [B, n_q, k] int32
  *   out     [B, n_q, Hq, d_v] bf16;  lse  [B, n_q, Hq] fp32 or NULL
  *   ws      lsa_workspace_bytes(LSA_OP_SPARSE_ATTN, ...) bytes
@@ -356,7 +368,8 @@ LSA_API lsa_status lsa_sparse_attn_layers(const lsa_index_shape *shape, const ls
  *   d_out   [B, n_q, Hq, d_v] bf16, 16-byte aligned
  *   d_q     [B, n_q, Hq, d_qk] fp32
  *   d_k     [B, L, d_qk] fp32 (dense rows);  d_v  [B, L, d_v] fp32 (latent: == d_k)
- * Limits: as lsa_sparse_attn.  No workspace.
+ * Limits: as lsa_sparse_attn, with dense caches only (attn->block_table must be NULL, else
+ *         LSA_ERR_UNSUPPORTED).  No workspace.
  */
 LSA_API lsa_status lsa_sparse_attn_backward(const lsa_index_shape *shape, const lsa_attn_shape *attn,
                                             lsa_budget budget, const void *q, const void *k,

@@ -273,6 +273,16 @@ def test_binding_checks_every_tensor(monkeypatch):
     with pytest.raises(ValueError, match="v .* does not match"):
         lsa.sparse_attn(aq[..., :128].contiguous(), kv[..., :128].contiguous(),
                         torch.zeros((1, 32, 128), dtype=torch.bfloat16), idx, 0.1)
+    pool = torch.zeros((4, 64, 576), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="paged cache is a latent cache"):
+        lsa.sparse_attn(torch.zeros((1, 1, 1, 128), dtype=torch.bfloat16),
+                        pool[..., :128].contiguous(), torch.zeros((4, 64, 128), dtype=torch.bfloat16),
+                        torch.zeros((1, 1, 16), dtype=torch.int32), 0.1, latent=False,
+                        block_table=torch.zeros((1, 4), dtype=torch.int32))
+    with pytest.raises(ValueError, match="block_table .* does not match"):
+        lsa.sparse_attn(torch.zeros((2, 1, 16, 576), dtype=torch.bfloat16), pool, None,
+                        torch.zeros((2, 1, 16), dtype=torch.int32), 0.04, d_v=512,
+                        block_table=torch.zeros((1, 4), dtype=torch.int32))
     with pytest.raises(ValueError, match="page_keys must have shape"):
         lsa.page_recall(q, w, torch.zeros((1, 3, 128), dtype=torch.bfloat16), keys8,
                         torch.ones((1, 64)), 16, 2, 4, 32, 1)
@@ -309,6 +319,38 @@ def test_q8_entry_points_reject(L):
                                  lsa.KEY_FP8_E4M3, v(FAKE), v(FAKE), None) == 2
     assert L.lsa_quantize_queries(ctypes.byref(_shape(d=96)), v(FAKE), v(FAKE), v(FAKE), None) == 4
     assert L.lsa_quantize_queries(ctypes.byref(_shape()), None, v(FAKE), v(FAKE), None) == 1
+
+
+def test_sparse_attn_paged_rejects(L):
+    """A paged cache is a latent cache with a power-of-two block size, a table that covers
+    kv_len and a pool under 2^31 rows; the backward takes dense caches only."""
+    sh = _shape(B=32)
+    b = lsa.Budget(2048, 64, 960)
+    v = ctypes.c_void_p
+
+    def paged(latent=True, bs=64, bps=None, nblk=4096, tab=FAKE):
+        att = (lsa.AttnShape(16, 576, 512, 1, 576, 576, 0.04) if latent
+               else lsa.AttnShape(1, 128, 128, 0, 128, 128, 0.1))
+        att.block_table, att.block_size, att.n_blocks = tab, bs, nblk
+        att.blocks_per_seq = -(-sh.kv_len // bs) if bps is None else bps
+        return att
+
+    def call(attn, ws=None, nb=0):
+        vv = FAKE if attn.latent else FAKE + 4096
+        return L.lsa_sparse_attn(ctypes.byref(sh), ctypes.byref(attn), b, v(FAKE), v(FAKE), v(vv),
+                                 v(FAKE), v(FAKE), None, v(ws) if ws else None, nb, None)
+    assert call(paged(latent=False)) == 4                 # per-head caches are dense
+    assert call(paged(bs=48)) == 2                        # a power of two
+    assert call(paged(bs=1 << 21)) == 2                   # at most 2^20
+    assert call(paged(bps=sh.kv_len // 64 - 1)) == 2      # the table must cover kv_len
+    assert call(paged(nblk=0)) == 2
+    assert call(paged(nblk=(1 << 31) // 64)) == 2         # pool rows must fit int32
+    assert call(paged(tab=FAKE + 2)) == 2                 # int32 alignment
+    assert call(paged()) == 5                             # valid: then the workspace is missing
+    assert call(paged(bs=1, nblk=1 << 20)) == 5           # one-row blocks are blocks too
+    assert L.lsa_sparse_attn_backward(ctypes.byref(sh), ctypes.byref(paged()), b, v(FAKE),
+                                      v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                                      v(FAKE), v(FAKE + 8192), v(FAKE + 8192), None) == 4
 
 
 def test_backward_entry_points_reject(L):

@@ -49,3 +49,15 @@ def test_algorithmic_bytes_of_the_decode_workload():
 def test_warm_queueing_only_for_short_stages():
     b = _bench()
     assert 0.0 < b.SHORT_STAGE_MS < 0.1  # the decode index stage (about 0.12 ms) is not queued
+
+
+def test_paged_copy_places_every_block_by_its_table_entry():
+    import torch
+    b = _bench()
+    kv = torch.arange(3 * 256 * 8, dtype=torch.float32).view(3, 256, 8)
+    pool, tab = b.paged_copy(torch, kv, 64)
+    assert pool.shape == (12, 64, 8) and tab.shape == (3, 4) and tab.dtype == torch.int32
+    assert sorted(tab.view(-1).tolist()) == list(range(12))
+    for s in range(3):
+        for j in range(4):
+            assert torch.equal(pool[tab[s, j]], kv[s, 64 * j:64 * (j + 1)])

@@ -690,6 +690,99 @@ def test_attn_layers_ragged_and_no_lse():
     _layers_case(2, 1, 4000, 256, 16, 112, 2, seed=63, exact=True, want_lse=False)
 
 
+def _to_pool(kvs, bs, spare, seed, bad=()):
+    """Dense latent caches [B, L, row] (one per layer) as pools of bs-row blocks under one block
+    table [B, ceil(L / bs)]: the blocks in a random order among `spare` unused ones, which hold
+    noise.  bad: (b, j, entry) table entries to overwrite (outside the pool: skipped tokens)."""
+    B, L, row = kvs[0].shape
+    bps = -(-L // bs)
+    n = B * bps + spare
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(n, generator=g)[:B * bps].view(B, bps)
+    pools = []
+    for kv in kvs:
+        pool = torch.randn((n, bs, row), generator=g).to(torch.bfloat16).to(kv.device)
+        pad = torch.zeros((B, bps * bs, row), dtype=kv.dtype, device=kv.device)
+        pad[:, :L] = kv
+        pool[perm.view(-1).to(kv.device)] = pad.view(B * bps, bs, row)
+        pools.append(pool)
+    tab = perm.to(torch.int32)
+    for b, j, e in bad:
+        tab[b, j] = e
+    return pools, tab.to(kvs[0].device)
+
+
+def _paged_case(B, T, L, k, S, W, bs, seed, n=1, seq_lens=None, spare=5, bad=()):
+    """The attention over a paged copy of the caches equals the attention over the dense caches
+    bit for bit (the same rows in the same order: only their addresses differ), for one layer and
+    for n layers in one call; table entries outside the pool equal the dense call with those
+    blocks' ids replaced by -1."""
+    w = Workload(name="a", index=IndexShape(
+        batch=B, n_q=T, kv_len=L, q_pos0=L - T, heads=64, head_dim=128, key_dtype="fp8"),
+        budget=DECODE_128K.budget, attn=DECODE_128K.attn, seed=seed)
+    lens = [L] * B if seq_lens is None else seq_lens
+    idx = torch.stack([inputs.synthetic_index_lists(T, k, S, W, ref.valid_lengths(lens[b], L - T, T),
+                                                    seed=seed + b) for b in range(B)]).to(DEV)
+    sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    atts = [inputs.attn_inputs(w, layer, DEV) for layer in range(n)]
+    qs, kvs = [a["q"] for a in atts], [a["kv"] for a in atts]
+    pools, tab = _to_pool(kvs, bs, spare, seed + 100, bad)
+    didx = idx.clone()
+    for b, j, _ in bad:
+        blk = (didx[b] >= j * bs) & (didx[b] < (j + 1) * bs)
+        didx[b][blk] = -1
+    say(f"paged B={B} T={T} L={L} k={k} bs={bs} layers={n} bad={len(bad)}")
+    scale = w.attn.scale
+    for layer in range(n):
+        o_d, l_d = lsa.sparse_attn(qs[layer], kvs[layer], None, didx, scale, S, W, d_v=512,
+                                   seq_lens=sl)
+        o_p, l_p = lsa.sparse_attn(qs[layer], pools[layer], None, idx, scale, S, W, d_v=512,
+                                   seq_lens=sl, block_table=tab, kv_len=L)
+        assert torch.equal(o_p.view(torch.int16), o_d.view(torch.int16)), layer
+        assert torch.equal(l_p.view(torch.int32), l_d.view(torch.int32)), layer
+    if n > 1:
+        outs_d, lses_d = lsa.sparse_attn_layers(qs, kvs, didx, scale, S, W, d_v=512, seq_lens=sl)
+        outs_p, lses_p = lsa.sparse_attn_layers(qs, pools, idx, scale, S, W, d_v=512, seq_lens=sl,
+                                                block_table=tab, kv_len=L)
+        for layer in range(n):
+            assert torch.equal(outs_p[layer].view(torch.int16), outs_d[layer].view(torch.int16))
+            assert torch.equal(lses_p[layer].view(torch.int32), lses_d[layer].view(torch.int32))
+    if not bad:  # and the dense call against the oracle, so the paged one is pinned too
+        oidx = idx.clone()
+        if seq_lens is not None:
+            for b in range(B):
+                oidx[b][oidx[b] >= seq_lens[b]] = -1
+        o_p, l_p = lsa.sparse_attn(qs[0], pools[0], None, idx, scale, S, W, d_v=512, seq_lens=sl,
+                                   block_table=tab, kv_len=L)
+        attn_check(qs[0], kvs[0], None, oidx, scale, o_p, l_p, True, 512,
+                   rows=None if B * T <= 8 else [0, B * T - 1])
+
+
+@pytest.mark.parametrize("B,T,L,k,S,W,bs", [
+    (4, 1, 6000, 256, 16, 112, 64),     # decode, the layout hint taken through the table
+    (2, 3, 3000, 2048, 64, 960, 16),    # every row listed: split-K over the whole cache
+    (3, 1, 700, 128, 16, 48, 1),        # one-row blocks
+    (2, 1, 900, 128, 8, 24, 4096),      # one block per sequence, larger than the cache
+    (1, 300, 2000, 256, 16, 112, 128),  # a prefill chunk (one split per query)
+])
+def test_attn_paged_equals_dense(B, T, L, k, S, W, bs):
+    _paged_case(B, T, L, k, S, W, bs, seed=81 + bs)
+
+
+def test_attn_paged_layers_and_ragged():
+    _paged_case(3, 1, 4000, 256, 16, 112, 64, seed=91, n=3)
+    _paged_case(3, 1, 4000, 256, 16, 112, 32, seed=93, seq_lens=[4000, 900, 0])
+
+
+def test_attn_paged_entries_outside_the_pool():
+    """Table entries of -1 or >= n_blocks (one in the sink's block, one in the window's, one in
+    the middle) skip those blocks' tokens, exactly as -1 ids would."""
+    L, bs = 6000, 64
+    last = (L - 1) // bs
+    _paged_case(2, 1, L, 256, 16, 112, bs, seed=97,
+                bad=[(0, 0, -1), (0, last, 1 << 30), (1, 40, 2 * ((L + bs - 1) // bs) + 5)])
+
+
 def test_attn_layers_per_head_cache():
     """A per-head (non-latent) cache: the layers run one after another, each equal to its own
     call."""

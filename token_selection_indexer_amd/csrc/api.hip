@@ -580,6 +580,16 @@ lsa_status sparse_attn_layers(const lsa_index_shape *shape, const lsa_attn_shape
     if (!aligned(idx, 4)) return LSA_ERR_BAD_SHAPE;
     if (budget.sink < 0 || budget.window < 0 || (int64_t)budget.sink + budget.window > budget.k)
         return LSA_ERR_BAD_SHAPE;
+    int lbs = 0;
+    if (attn->block_table) { // a paged latent cache
+        if (!attn->latent) return LSA_ERR_UNSUPPORTED;
+        const int64_t bs = attn->block_size;
+        if (!pow2(attn->block_size) || bs > (1 << 20) || attn->blocks_per_seq < 1 ||
+            attn->n_blocks < 1 || (int64_t)attn->blocks_per_seq * bs < shape->kv_len ||
+            attn->n_blocks * bs >= (int64_t(1) << 31) || !aligned(attn->block_table, 4))
+            return LSA_ERR_BAD_SHAPE;
+        while ((int64_t(1) << lbs) < bs) ++lbs;
+    }
     const int64_t rows = (int64_t)shape->batch * shape->n_q;
     if (rows == 0) return LSA_OK;
     if (rows * attn->n_heads * n_layers >= (int64_t(1) << 31) * 4) return LSA_ERR_UNSUPPORTED;
@@ -619,6 +629,10 @@ lsa_status sparse_attn_layers(const lsa_index_shape *shape, const lsa_attn_shape
                                  attn->latent);
     a.layers = n_layers;
     a.ws_layer = (int64_t)(all_layers / n_layers / sizeof(float));
+    a.btab = attn->block_table;
+    a.lbs = lbs;
+    a.bps = attn->block_table ? attn->blocks_per_seq : 0;
+    a.n_blocks = attn->block_table ? attn->n_blocks : 0;
     for (int l = 0; l < n_layers; ++l) {
         a.lq[l] = static_cast<const uint16_t *>(q[l]);
         a.lk[l] = static_cast<const uint16_t *>(k[l]);
@@ -666,6 +680,7 @@ lsa_status lsa_sparse_attn_backward(const lsa_index_shape *shape, const lsa_attn
         return LSA_ERR_NULL_POINTER;
     if (attn->latent && (v != k || d_v != d_k)) return LSA_ERR_BAD_SHAPE;
     if (!attn->latent && d_v == d_k) return LSA_ERR_BAD_SHAPE;
+    if (attn->block_table) return LSA_ERR_UNSUPPORTED; // the gradients are dense
     if ((st = check_ragged(shape)) != LSA_OK) return st;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(idx, 4) ||
         !aligned(out, 16) || !aligned(lse, 4) || !aligned(d_out, 16) || !aligned(d_q, 4) ||

@@ -82,7 +82,11 @@ __device__ __forceinline__ void ring_barrier()
 // MULTI: several layers in one grid (z = layer * batch + b), each layer's pointers taken from the
 // argument arrays; the single-layer form reads them from the plain fields, with no lookup that
 // depends on the layer before its first loads can issue.
-template <int DQK, int DV, bool MULTI>
+// PAGED: the cache is a pool of blocks (a.btab).  The row arrays then hold pool rows: a round's
+// ids are translated through the block table while the round before is computed (the table
+// loads in flight with that round's row loads), and round 0's predicted rows through the table
+// before anything else.
+template <int DQK, int DV, bool MULTI, bool PAGED>
 __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
 {
     constexpr int ROWB = DQK * 2;          // LDS bytes per gathered row
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) uint8_t buf1[AR * ROWB];
     __shared__ float S2[2][16][AR + 1];    // logit halves (two K halves)
     __shared__ __attribute__((aligned(16))) uint16_t Pm[16][AR + 8];
-    __shared__ int32_t rid[NBUF][AR];      // row ids of the rounds in the buffers, -1 = skip
+    __shared__ int32_t rid[NBUF][AR];      // rows of the rounds in the buffers, -1 = skip
     __shared__ int32_t rid_p[AR];          // round 0's row ids as the layout predicts them
     __shared__ bool pred_ok;               // ... and they are the list's
     __shared__ float m_run[16], l_run[16], alpha[16];
@@ -147,16 +151,28 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     const int64_t V = valid_len(a.seq_len, a.seq_pos0, b, t, a.kv_len, a.q_pos0);
     const int e0 = split * AR;
     const bool predicted = n_rounds > 0 && (V <= a.n_idx || min(e0 + AR, a.n_idx) <= a.sink + a.window);
+    // PAGED: the block-table entry of a (masked) id, by an unconditional in-bounds load, and
+    // the pool row it gives (-1: skipped, or its block lies outside the pool)
+    const int32_t *btab_b = PAGED ? a.btab + (int64_t)b * a.bps : nullptr;
+    auto table_entry = [&](int32_t id) -> int32_t { return btab_b[(id < 0 ? 0 : id) >> a.lbs]; };
+    auto pool_row = [&](int32_t id, int32_t tab) -> int32_t {
+        return id >= 0 && tab >= 0 && tab < a.n_blocks
+                   ? (tab << a.lbs) | (id & ((1 << a.lbs) - 1))
+                   : -1;
+    };
     int32_t raw0 = 0, raw1 = 0, pid = -1;
     if (threadIdx.x < AR) {
-        raw0 = id_load(0);
-        raw1 = id_load(1);
         const int e = e0 + (int)threadIdx.x;
         const int64_t p = e >= a.n_idx ? -1
                           : V <= a.n_idx ? (e < V ? e : -1)
                           : e < a.sink ? e
                           : V - a.window + (e - a.sink);
         pid = p >= 0 && p < seq_rows ? (int32_t)p : -1;
+        // the predicted rows' table entries first: they wait for nothing issued after them
+        const int32_t tab_p = PAGED ? table_entry(pid) : 0;
+        raw0 = id_load(0);
+        raw1 = id_load(1);
+        if constexpr (PAGED) pid = pool_row(pid, tab_p);
         rid_p[threadIdx.x] = pid;
     }
     // Q fragments: wave w computes row tile (w & 1) over K-half (w >> 1); lane l holds head
@@ -175,7 +191,8 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     f32x4_t oacc[NTW];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) oacc[nt] = f32x4_t{};
-    const uint8_t *kv_b = reinterpret_cast<const uint8_t *>(k_l) + (int64_t)b * a.kv_len * a.k_stride * 2;
+    const uint8_t *kv_b = reinterpret_cast<const uint8_t *>(k_l) +
+                          (PAGED ? 0 : (int64_t)b * a.kv_len * a.k_stride * 2); // a pool: rows are pool rows
     const float sl2 = a.scale * kLog2e;
 
     // A round's rows through registers: thread t loads the 16-byte chunks f = 256*j + t of the
@@ -204,8 +221,15 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
     ring_barrier(); // rid_p is visible; the list and q loads stay in flight
     if (predicted) load_round(rid_p);
     if (threadIdx.x < AR) {
-        rid[0][threadIdx.x] = n_rounds > 0 ? id_mask(0, raw0) : -1;
-        rid[1][threadIdx.x] = n_rounds > 1 ? id_mask(1, raw1) : -1;
+        int32_t id0 = n_rounds > 0 ? id_mask(0, raw0) : -1;
+        int32_t id1 = n_rounds > 1 ? id_mask(1, raw1) : -1;
+        if constexpr (PAGED) {
+            const int32_t tab0 = table_entry(id0), tab1 = table_entry(id1);
+            id0 = pool_row(id0, tab0);
+            id1 = pool_row(id1, tab1);
+        }
+        rid[0][threadIdx.x] = id0;
+        rid[1][threadIdx.x] = id1;
     }
     if (w == 0) { // a prediction that differs from the list in any entry is discarded
         const uint64_t miss = __ballot(threadIdx.x < AR && pid != rid[0][threadIdx.x]);
@@ -232,6 +256,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
         // the compiler wait for every load at the merge that follows it).
         const int32_t next_raw = id_load(i + 2); // first: waiting for it then waits for no row
         load_round(rid[O]);
+        int32_t next_id = -1, next_tab = 0; // PAGED: round i + 2's ids and table entries
         const uint8_t *cb = slot_buf(SLOT);
         // logits, half of d per wave: S2[kh][h][r] for rows 16*tile .. 16*tile + 15
         {
@@ -280,7 +305,14 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
                 l_run[h] = l_run[h] * al + sum;
                 m_run[h] = m_new;
             }
-            if (threadIdx.x < AR) rid[S][threadIdx.x] = id_mask(i + 2, next_raw);
+            if (threadIdx.x < AR) {
+                if constexpr (PAGED) { // translated at the end of the round
+                    next_id = id_mask(i + 2, next_raw);
+                    next_tab = table_entry(next_id);
+                } else {
+                    rid[S][threadIdx.x] = id_mask(i + 2, next_raw);
+                }
+            }
         }
         ring_barrier();
         // O = O * alpha + P . V ; wave w owns columns [w*DV/4, (w+1)*DV/4).  K = the 32 rows:
@@ -308,6 +340,8 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(AttnArgs a)
                 oacc[nt] = mfma_16x16x32(pf, vf, oacc[nt]);
             }
         }
+        if constexpr (PAGED) // the table entries arrive with the round's rows, awaited below
+            if (threadIdx.x < AR) rid[S][threadIdx.x] = pool_row(next_id, next_tab);
         store_round(slot_buf(std::integral_constant<int, O>{}));
     });
     __syncthreads(); // m_run / l_run final
@@ -518,14 +552,22 @@ hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t st)
         dim3 grid((unsigned)a.n_split, (unsigned)(a.n_q * (a.heads / 16)),
                   (unsigned)(a.batch * a.layers));
         const dim3 cgrid((unsigned)(rows * a.heads * a.layers));
+        const bool paged = a.btab != nullptr;
         if (a.layers == 1) {
-            hipLaunchKernelGGL((mla_attn_kernel<MLA_MAX_DQK, MLA_MAX_DV, false>), grid, dim3(256), 0, st, a);
+            if (paged)
+                hipLaunchKernelGGL((mla_attn_kernel<MLA_MAX_DQK, MLA_MAX_DV, false, true>), grid, dim3(256), 0, st, a);
+            else
+                hipLaunchKernelGGL((mla_attn_kernel<MLA_MAX_DQK, MLA_MAX_DV, false, false>), grid, dim3(256), 0, st, a);
             if (a.n_split > 1) hipLaunchKernelGGL(attn_combine_kernel<false>, cgrid, dim3(256), 0, st, a);
         } else {
-            hipLaunchKernelGGL((mla_attn_kernel<MLA_MAX_DQK, MLA_MAX_DV, true>), grid, dim3(256), 0, st, a);
+            if (paged)
+                hipLaunchKernelGGL((mla_attn_kernel<MLA_MAX_DQK, MLA_MAX_DV, true, true>), grid, dim3(256), 0, st, a);
+            else
+                hipLaunchKernelGGL((mla_attn_kernel<MLA_MAX_DQK, MLA_MAX_DV, true, false>), grid, dim3(256), 0, st, a);
             if (a.n_split > 1) hipLaunchKernelGGL(attn_combine_kernel<true>, cgrid, dim3(256), 0, st, a);
         }
     } else {
+        if (a.btab) return hipErrorInvalidValue; // the per-head cache is dense
         const int64_t units = rows * a.heads;
         for (int layer = 0; layer < a.layers; ++layer) {
             AttnArgs al = a;

@@ -140,6 +140,11 @@ struct AttnArgs {
     // with its own q, cache, out and lse; the split partials of layer l start at ws + l * ws_layer
     int layers;
     int64_t ws_layer;
+    // paged latent cache (btab != nullptr): k / lk are pools of n_blocks blocks of 2^lbs rows,
+    // token s of sequence b at pool row btab[b * bps + (s >> lbs)] << lbs | (s & mask)
+    const int32_t *btab;
+    int lbs, bps;
+    int64_t n_blocks;
     const uint16_t *lq[kMaxAttnLayers];
     const uint16_t *lk[kMaxAttnLayers];
     const uint16_t *lv[kMaxAttnLayers];

@@ -46,9 +46,13 @@ class Budget(ctypes.Structure):
 
 
 class AttnShape(ctypes.Structure):
+    """lsa_attn_shape.  block_table / block_size / blocks_per_seq / n_blocks: a paged latent
+    cache (the table a device pointer), or None / 0 for dense caches."""
     _fields_ = [("n_heads", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("latent", ctypes.c_int32), ("k_row_stride", ctypes.c_int64),
-                ("v_row_stride", ctypes.c_int64), ("scale", ctypes.c_float)]
+                ("v_row_stride", ctypes.c_int64), ("scale", ctypes.c_float),
+                ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
+                ("blocks_per_seq", ctypes.c_int32), ("n_blocks", ctypes.c_int64)]
 
 
 class LsaError(RuntimeError):
@@ -398,9 +402,10 @@ def page_recall(q, w, page_keys, keys, key_scale, k, sink, window, page, m_pages
     return page_ids, cs, ci
 
 
-def _attn_layer(q, k, v, idx, d_v, latent, ref=None):
+def _attn_layer(q, k, v, idx, d_v, latent, ref=None, paged=False):
     """Checks one layer's q [B, n_q, Hq, d_qk] / cache / index lists; returns (v, d_v, latent,
-    AttnShape args).  ref: the first layer's q and cache, which every later layer must match."""
+    AttnShape args).  ref: the first layer's q and cache, which every later layer must match.
+    paged: k is a pool [n_blocks, block_size, row] (latent only)."""
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 3)
     _need(idx, "idx", torch.int32, 3)
@@ -408,10 +413,12 @@ def _attn_layer(q, k, v, idx, d_v, latent, ref=None):
         latent = v is None or v is k
     if v is None:
         v = k
+    if paged and not latent:
+        raise ValueError("a paged cache is a latent cache (v is k)")
     B, T, Hq, dqk = q.shape
     dev = q.device
     _need(k, "k", torch.bfloat16, device=dev)
-    if k.shape[0] != B or k.shape[2] < dqk:
+    if (not paged and k.shape[0] != B) or k.shape[2] < dqk:
         raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)}")
     _need(v, "v", torch.bfloat16, 3, device=dev)
     if v.shape[:2] != k.shape[:2]:
@@ -430,25 +437,44 @@ def _attn_layer(q, k, v, idx, d_v, latent, ref=None):
     return v, d_v, latent, (Hq, dqk, d_v, 1 if latent else 0, k.shape[2], v.shape[2])
 
 
-def _attn_shape(q, k, idx, sink, window, seq_lens, q_pos0, seq_pos0):
+def _attn_shape(q, k, idx, sink, window, seq_lens, q_pos0, seq_pos0, block_table=None,
+                kv_len=None):
     B, T = q.shape[0], q.shape[1]
-    L = k.shape[1]
+    if block_table is None:
+        L = k.shape[1]
+    else:
+        _need(block_table, "block_table", torch.int32, 2, device=q.device)
+        if block_table.shape[0] != B:
+            raise ValueError(f"block_table {tuple(block_table.shape)} does not match q {tuple(q.shape)}")
+        L = block_table.shape[1] * k.shape[1] if kv_len is None else kv_len
     pos0 = max(0, L - T) if q_pos0 is None else q_pos0
     shape = _ragged(IndexShape(B, T, 64, 128, L, pos0), q.device, seq_lens, seq_pos0)
     return shape, Budget(idx.shape[2], sink, window)
 
 
+def _paged(attn: AttnShape, k, block_table):
+    """Fill the paged-cache fields of attn: k is the pool [n_blocks, block_size, row]."""
+    if block_table is not None:
+        attn.block_table = block_table.data_ptr()
+        attn.block_size = k.shape[1]
+        attn.blocks_per_seq = block_table.shape[1]
+        attn.n_blocks = k.shape[0]
+    return attn
+
+
 def sparse_attn(q, k, v, idx, scale, sink=0, window=0, d_v=None, latent=None, want_lse=True,
                 ws: Optional[Workspace] = None, out=None, stream=None, seq_lens=None, q_pos0=None,
-                seq_pos0=None):
+                seq_pos0=None, block_table=None, kv_len=None):
     """out [B, n_q, Hq, d_v] bf16 and lse [B, n_q, Hq] fp32 (or None).  Latent cache: pass v=None
     (or v is k) and d_v = the value width.  sink, window and the query positions (q_pos0, default
     L - n_q; seq_pos0 for a ragged batch) describe the lists' Streaming-Aware layout: the kernel
     starts loading the rows that layout names before the lists arrive (the result never depends
-    on them)."""
-    v, d_v, latent, ashape = _attn_layer(q, k, v, idx, d_v, latent)
-    attn = AttnShape(*ashape, scale)
-    shape, bud = _attn_shape(q, k, idx, sink, window, seq_lens, q_pos0, seq_pos0)
+    on them).  block_table [B, blocks_per_seq] int32: k is a paged latent cache, a pool
+    [n_blocks, block_size, row] (kv_len defaults to blocks_per_seq * block_size)."""
+    v, d_v, latent, ashape = _attn_layer(q, k, v, idx, d_v, latent, paged=block_table is not None)
+    attn = _paged(AttnShape(*ashape, scale), k, block_table)
+    shape, bud = _attn_shape(q, k, idx, sink, window, seq_lens, q_pos0, seq_pos0, block_table,
+                             kv_len)
     B, T, Hq = q.shape[:3]
     dev = q.device
     out = _out(out, "out", (B, T, Hq, d_v), torch.bfloat16, dev)
@@ -471,7 +497,7 @@ def lsa_sparse_attn_layers(shape: IndexShape, attn: AttnShape, budget: Budget, q
 
 def sparse_attn_layers(qs, ks, idx, scale, sink=0, window=0, d_v=None, vs=None, latent=None,
                        want_lse=True, ws: Optional[Workspace] = None, outs=None, stream=None,
-                       seq_lens=None, q_pos0=None, seq_pos0=None):
+                       seq_lens=None, q_pos0=None, seq_pos0=None, block_table=None, kv_len=None):
     """sparse_attn for a group of layers sharing one index list (Cross-Layer Indexing) in one
     call: lists of per-layer q and cache (vs: per-layer value caches, None for latent caches)
     -> lists of out and lse.  Each layer computes what its own sparse_attn call computes; the
@@ -480,15 +506,18 @@ def sparse_attn_layers(qs, ks, idx, scale, sink=0, window=0, d_v=None, vs=None, 
     if not 1 <= n <= MAX_ATTN_LAYERS or len(ks) != n or (vs is not None and len(vs) != n):
         raise ValueError(f"1..{MAX_ATTN_LAYERS} layers, one q and one cache each")
     vs = [None] * n if vs is None else list(vs)
-    v0, d_v0, latent0, ashape = _attn_layer(qs[0], ks[0], vs[0], idx, d_v, latent)
+    paged = block_table is not None
+    v0, d_v0, latent0, ashape = _attn_layer(qs[0], ks[0], vs[0], idx, d_v, latent, paged=paged)
     vv = [v0]
     for l in range(1, n):
-        v, _, lat, ash = _attn_layer(qs[l], ks[l], vs[l], idx, d_v, latent, (qs[0], ks[0], v0))
+        v, _, lat, ash = _attn_layer(qs[l], ks[l], vs[l], idx, d_v, latent, (qs[0], ks[0], v0),
+                                     paged=paged)
         if lat != latent0 or ash != ashape:
             raise ValueError("every layer needs the first layer's attention shape")
         vv.append(v)
-    attn = AttnShape(*ashape, scale)
-    shape, bud = _attn_shape(qs[0], ks[0], idx, sink, window, seq_lens, q_pos0, seq_pos0)
+    attn = _paged(AttnShape(*ashape, scale), ks[0], block_table)
+    shape, bud = _attn_shape(qs[0], ks[0], idx, sink, window, seq_lens, q_pos0, seq_pos0,
+                             block_table, kv_len)
     B, T, Hq = qs[0].shape[:3]
     dev = qs[0].device
     outs = [_out(None if outs is None else outs[l], "out", (B, T, Hq, d_v0), torch.bfloat16, dev)
