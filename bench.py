@@ -239,6 +239,19 @@ def headline(torch, lsa, inputs, cfg, tm: Timing, steps, warmup):
     f_attn_paged()
     dist["attn_paged"] = tm.both(f_attn_paged, st["attn"])
     del pool, tab
+    # and the fused scores + selection over paged indexer keys (64-row blocks, shuffled)
+    kpool, ktab = paged_copy(torch, inp["keys"], PAGE_BLOCK)
+    spool, stab = paged_copy(torch, inp["scale"].unsqueeze(-1), PAGE_BLOCK)
+    spool = spool.squeeze(-1)
+    assert torch.equal(stab, ktab)  # one seeded order for both pools
+
+    def f_index_paged():
+        lsa.index_select(inp["q"], inp["w"], kpool, spool, b.k, b.sink, b.window,
+                         q_pos0=s.q_pos0, scores=scores, idx=idx, ws=ws_idx, block_table=ktab,
+                         kv_len=L)
+    f_index_paged()
+    dist["index_paged"] = tm.both(f_index_paged, st["index"])
+    del kpool, spool, ktab
     f_index()
     n_q = B * s.n_q
     sb = score_bytes(n_q * L, s.head_dim, True, s.heads, n_q)
@@ -707,6 +720,12 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
                                                  scores=scores, idx=idx, ws=ws_idx),
                "attn": lambda: lsa.sparse_attn(att["q"], att["kv"], None, idx, a.scale, b.sink,
                                                b.window, d_v=a.d_v, ws=ws)}
+        if stage == "index_paged":
+            kpool, ktab = paged_copy(torch, inp["keys"], PAGE_BLOCK)
+            spool = paged_copy(torch, inp["scale"].unsqueeze(-1), PAGE_BLOCK)[0].squeeze(-1)
+            fns[stage] = lambda: lsa.index_select(inp["q"], inp["w"], kpool, spool, b.k, b.sink,
+                                                  b.window, q_pos0=s.q_pos0, scores=scores,
+                                                  idx=idx, ws=ws_idx, block_table=ktab, kv_len=L)
         if stage == "attn_paged":
             att = inputs.attn_inputs(w, 0, dev)
             pool, tab = paged_copy(torch, att["kv"], PAGE_BLOCK)
@@ -726,7 +745,7 @@ def only_stage(torch, lsa, inputs, cfg, stage, steps, cold):
 
 STAGES = ["score", "topk", "index", "attn", "copy", "prefill_score", "prefill_topk", "prefill_attn",
           "prefill_q8", "bwd_attn", "bwd_index",
-          "hi1m_summary", "hi1m_recall", "hi1m_topk", "cli4_attn", "cli4_attn_layers", "attn_paged"]
+          "hi1m_summary", "hi1m_recall", "hi1m_topk", "cli4_attn", "cli4_attn_layers", "attn_paged", "index_paged"]
 
 
 def main():
@@ -812,9 +831,9 @@ def main():
         "indexed_qps_unfused": head["indexed_qps_unfused"],
         "step_qps": head["step_qps"],
         "sparse_attn_TBps": head["sparse_attn_TBps"],
-        "sparse_attn_paged_vs_dense": {
-            m: head["dist"]["attn_paged"][m]["mean"] / head["dist"]["attn"][m]["mean"]
-            for m in ("warm", "cold")},
+        "paged_vs_dense": {  # time ratios with 64-row blocks in shuffled pools
+            st: {m: head["dist"][st + "_paged"][m]["mean"] / head["dist"][st][m]["mean"]
+                 for m in ("warm", "cold")} for st in ("index", "attn")},
         "stage_ms": head["stage_ms"],
         "stage_dist_ms": rnd(head["dist"]),
         "hbm_frac_cold_mean": head["hbm_frac_cold_mean"],

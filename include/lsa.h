@@ -86,6 +86,19 @@ typedef struct {
     int64_t kv_len, q_pos0;
     const int32_t *seq_len;
     const int32_t *seq_pos0;
+    /* Paged indexer keys (optional; block_table NULL = dense keys [B, kv_len, d]).  The keys
+     * (and the fp8 keys' scales) are then pools of n_blocks blocks of block_size rows,
+     * [n_blocks * block_size, d] (and [n_blocks * block_size]), and key s of sequence b is pool
+     * row  block_table[b * blocks_per_seq + s / block_size] * block_size + s % block_size.
+     * A table entry outside [0, n_blocks) gives that block's keys the score -inf.
+     * block_size a power of two in [32, 2^20]; blocks_per_seq * block_size >= kv_len;
+     * n_blocks * block_size < 2^31.  Only the calls that read indexer keys look at these
+     * fields: lsa_index_scores and lsa_index_select take them at decode shapes (see there);
+     * lsa_page_summary, lsa_page_recall, lsa_index_scores_q8 and lsa_index_scores_backward
+     * return LSA_ERR_UNSUPPORTED for them. */
+    const int32_t *block_table; /* [B, blocks_per_seq] int32, device */
+    int32_t block_size, blocks_per_seq;
+    int64_t n_blocks;
 } lsa_index_shape;
 
 /* Selection budget per query: k tokens = sink [0,S) + window (the W latest valid tokens) +
@@ -127,6 +140,10 @@ typedef struct {
  *   keys       [B, L, d]      bf16 or e4m3 codes (see lsa_key_dtype)
  *   key_scale  [B, L] fp32 (fp8 keys; each scale > 0) or NULL (bf16 keys)
  *   scores     [B, n_q, L]    fp32, written completely
+ * Paged keys (shape->block_table): keys and key_scale are the pools; scores stay [B, n_q, L]
+ *   by token position.  Taken at decode shapes (n_q at most 2 for H of 32 or 64, 4 for 16, 8
+ *   for 8, 16 for 4) where a scoring workgroup's key range spans at most 510 table blocks;
+ *   other shapes return LSA_ERR_UNSUPPORTED.
  */
 LSA_API lsa_status lsa_index_scores(const lsa_index_shape *shape, const void *q, const float *w,
                             const void *keys, lsa_key_dtype key_dtype, const float *key_scale,
@@ -200,7 +217,8 @@ LSA_API lsa_status lsa_index_scores_q8(const lsa_index_shape *shape, const uint8
  * best scores (the histogram bins holding about twice its share of the row's picks) in a slice
  * of `ws`, and a single selection launch gathers the slices instead of passing over the score
  * rows again.  Other shapes run the two ordinary paths.
- *   q, w, keys, key_scale, scores   as for lsa_index_scores (scores 16-byte aligned)
+ *   q, w, keys, key_scale, scores   as for lsa_index_scores (scores 16-byte aligned; paged
+ *           keys as there)
  *   idx     [B, n_q, k] int32 as for lsa_topk_select
  *   ws      lsa_workspace_bytes(LSA_OP_INDEX_SELECT, shape, budget, 0, 0, 0, NULL) bytes,
  *           256-byte aligned; its contents on entry do not matter

@@ -307,6 +307,37 @@ def test_topk_select_noalloc_rejects(L):
     assert call(huge, b, huge.kv_len) == 4
 
 
+def test_paged_keys_rejects(L):
+    """Paged indexer keys: a power-of-two block size of at least 32 whose table covers kv_len;
+    scoring at decode shapes only; the other key readers take dense keys only."""
+    v = ctypes.c_void_p
+
+    def paged(T=1, bs=64, bps=None, nblk=1 << 12, tab=FAKE, Lk=4096):
+        sh = _shape(B=2, T=T, Lk=Lk)
+        sh.block_table, sh.block_size, sh.n_blocks = tab, bs, nblk
+        sh.blocks_per_seq = -(-Lk // bs) if bps is None else bps
+        return sh
+    fp8 = dict(kd=lsa.KEY_FP8_E4M3, scale=FAKE)
+    assert _scores_call(L, paged(bs=16), **fp8) == 2           # at least 32 rows per block
+    assert _scores_call(L, paged(bs=96), **fp8) == 2           # a power of two
+    assert _scores_call(L, paged(bps=4096 // 64 - 1), **fp8) == 2  # the table covers kv_len
+    assert _scores_call(L, paged(nblk=0), **fp8) == 2
+    assert _scores_call(L, paged(nblk=(1 << 31) // 64), **fp8) == 2
+    assert _scores_call(L, paged(tab=FAKE + 1), **fp8) == 2
+    assert _scores_call(L, paged(T=64), **fp8) == 4             # prefill (the tile kernel)
+    sh = paged()
+    assert L.lsa_page_summary(ctypes.byref(sh), 64, v(FAKE), lsa.KEY_FP8_E4M3, v(FAKE), 0, 1,
+                              v(FAKE), None) == 4
+    assert L.lsa_page_recall(ctypes.byref(sh), lsa.Budget(256, 16, 64), 64, 8, v(FAKE), v(FAKE),
+                             v(FAKE), v(FAKE), lsa.KEY_FP8_E4M3, v(FAKE), v(FAKE), v(FAKE),
+                             v(FAKE), v(FAKE), 1 << 20, None) == 4
+    assert L.lsa_index_scores_q8(ctypes.byref(sh), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                                 lsa.KEY_FP8_E4M3, v(FAKE), v(FAKE), None) == 4
+    assert L.lsa_index_scores_backward(ctypes.byref(sh), lsa.Budget(256, 0, 0), v(FAKE), v(FAKE),
+                                       v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                                       None) == 4
+
+
 def test_q8_entry_points_reject(L):
     """fp8 queries need fp8 keys; quantisation needs d in {64, 128}."""
     v = ctypes.c_void_p

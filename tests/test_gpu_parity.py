@@ -783,6 +783,83 @@ def test_attn_paged_entries_outside_the_pool():
                 bad=[(0, 0, -1), (0, last, 1 << 30), (1, 40, 2 * ((L + bs - 1) // bs) + 5)])
 
 
+def _key_pool(keys, scale, bs, spare, seed, bad=()):
+    """Dense indexer keys [B, L, d] (and fp8 scales [B, L]) as pools of bs-row blocks under one
+    block table [B, ceil(L / bs)], in a random order among `spare` unused blocks.  Pool rows past
+    a sequence's keys and the unused blocks hold other valid keys (finite codes, positive
+    scales).  bad: (b, j, entry) table entries to overwrite."""
+    B, L, d = keys.shape
+    bps = -(-L // bs)
+    n = B * bps + spare
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(n, generator=g)[:B * bps].view(B, bps)
+    filler = keys.reshape(-1, d)[torch.randint(0, B * L, (n * bs,), generator=g).to(keys.device)]
+    pool = filler.view(n, bs, d).clone()
+    pad = pool[perm.view(-1).to(keys.device)].view(B, bps * bs, d)
+    pad[:, :L] = keys
+    pool[perm.view(-1).to(keys.device)] = pad.view(B * bps, bs, d)
+    spool = None
+    if scale is not None:
+        spool = (torch.rand((n, bs), generator=g) + 0.5).to(scale.device)
+        spad = spool[perm.view(-1).to(scale.device)].view(B, bps * bs)
+        spad[:, :L] = scale
+        spool[perm.view(-1).to(scale.device)] = spad.view(B * bps, bs)
+    tab = perm.to(torch.int32)
+    for b, j, e in bad:
+        tab[b, j] = e
+    return pool, spool, tab.to(keys.device)
+
+
+def _paged_scores_case(B, T, L, H, kd, bs, seed, fused=None, seq_lens=None, bad=()):
+    """Scores (and, with fused = (k, S, W), the fused selection) over a paged copy of the keys
+    equal those over the dense keys bit for bit; blocks whose table entry lies outside the pool
+    score -inf, and the selection is the one from those scores."""
+    w = Workload(name="p", index=IndexShape(batch=B, n_q=T, kv_len=L, q_pos0=L - T, heads=H,
+                                            head_dim=128, key_dtype=kd),
+                 budget=DECODE_128K.budget, attn=DECODE_128K.attn, seed=seed)
+    inp = inputs.index_inputs(w, DEV)
+    pool, spool, tab = _key_pool(inp["keys"], inp["scale"], bs, 3, seed + 7, bad)
+    sl = None if seq_lens is None else torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    say(f"paged scores B={B} T={T} L={L} H={H} {kd} bs={bs} fused={fused} bad={len(bad)}")
+    dense = lsa.index_scores(inp["q"], inp["w"], inp["keys"], inp["scale"], seq_lens=sl)
+    for b, j, _ in bad:
+        dense[b, :, j * bs:(j + 1) * bs] = -math.inf
+    paged = lsa.index_scores(inp["q"], inp["w"], pool, spool, seq_lens=sl, block_table=tab,
+                             kv_len=L)
+    assert torch.equal(paged.view(torch.int32), dense.view(torch.int32))
+    if fused is not None:
+        k, S, W = fused
+        sc, idx = lsa.index_select(inp["q"], inp["w"], pool, spool, k, S, W, seq_lens=sl,
+                                   block_table=tab, kv_len=L)
+        assert torch.equal(sc.view(torch.int32), dense.view(torch.int32))
+        expect = lsa.topk_select(dense, k, S, W, kv_len=L, q_pos0=L - T, seq_lens=sl)
+        assert torch.equal(idx, expect)
+
+
+@pytest.mark.parametrize("B,T,L,H,kd,bs", [
+    (2, 1, 5000, 64, "fp8", 64),      # a short launch (two blocks per wave), ragged tail
+    (3, 2, 3001, 64, "bf16", 32),     # bf16 keys, two queries, the smallest blocks
+    (2, 4, 2000, 16, "fp8", 4096),    # four queries per sequence, one block larger than the keys
+    (4, 1, 524365, 64, "fp8", 128),   # a long launch (one round of workgroups), ragged tail
+])
+def test_scores_paged_equals_dense(B, T, L, H, kd, bs):
+    _paged_scores_case(B, T, L, H, kd, bs, seed=101 + bs)
+
+
+def test_index_select_paged_fused_decode():
+    """The fused decode path (histograms and slices in the scoring launch) over paged keys."""
+    _paged_scores_case(16, 1, 131072, 64, "fp8", 64, seed=111, fused=(2048, 64, 960))
+    _paged_scores_case(16, 1, 131072, 64, "fp8", 256, seed=113, fused=(2048, 64, 960),
+                       seq_lens=[131072 - 977 * i for i in range(16)])
+
+
+def test_scores_paged_entries_outside_the_pool():
+    L, bs = 131072, 64
+    _paged_scores_case(16, 1, L, 64, "fp8", bs, seed=117, fused=(2048, 64, 960),
+                       bad=[(0, 0, -1), (3, 700, 1 << 30), (5, L // bs - 1, -7)])
+    _paged_scores_case(2, 1, 5000, 64, "fp8", bs, seed=119, bad=[(1, 10, -1)])
+
+
 def test_attn_layers_per_head_cache():
     """A per-head (non-latent) cache: the layers run one after another, each equal to its own
     call."""

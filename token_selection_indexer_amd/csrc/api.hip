@@ -31,7 +31,34 @@ lsa_status check_index_shape(const lsa_index_shape *s)
         return LSA_ERR_BAD_SHAPE;
     if (s->n_heads < 1 || s->head_dim < 1) return LSA_ERR_BAD_SHAPE;
     if (!lsa::scores_supported(s->n_heads, s->head_dim)) return LSA_ERR_UNSUPPORTED;
+    if (s->block_table) { // paged indexer keys
+        const int64_t bs = s->block_size;
+        if (!pow2(bs) || bs < 32 || bs > (1 << 20) || s->blocks_per_seq < 1 || s->n_blocks < 1 ||
+            (int64_t)s->blocks_per_seq * bs < s->kv_len || s->n_blocks * bs >= (int64_t(1) << 31) ||
+            !aligned(s->block_table, 4))
+            return LSA_ERR_BAD_SHAPE;
+    }
     return check_ragged(s);
+}
+
+// The indexer-key calls that take dense keys only.
+lsa_status dense_keys_only(const lsa_index_shape *s)
+{
+    return s && s->block_table ? LSA_ERR_UNSUPPORTED : LSA_OK;
+}
+
+// Paged indexer keys (shape checked): the table fields of the scoring arguments, and whether
+// the scoring launch that `a` asks for takes them.
+lsa_status set_paged_keys(const lsa_index_shape *s, lsa::ScoreArgs &a)
+{
+    if (!s->block_table) return LSA_OK;
+    int lbs = 0;
+    while ((int64_t(1) << lbs) < s->block_size) ++lbs;
+    a.btab = s->block_table;
+    a.lbs = lbs;
+    a.bps = s->blocks_per_seq;
+    a.n_blocks = s->n_blocks;
+    return lsa::scores_paged_ok(a) ? LSA_OK : LSA_ERR_UNSUPPORTED;
 }
 
 lsa_status check_keys(lsa_key_dtype kd, const void *keys, const float *scale)
@@ -235,6 +262,7 @@ lsa_status lsa_index_scores(const lsa_index_shape *shape, const void *q, const f
     a.seq_pos0 = shape->seq_pos0;
     a.mask = lsa::MASK_CAUSAL;
     a.fp8 = key_dtype == LSA_KEY_FP8_E4M3;
+    if ((st = set_paged_keys(shape, a)) != LSA_OK) return st;
     return device_status(lsa::launch_scores(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -304,6 +332,7 @@ lsa_status lsa_index_scores_q8(const lsa_index_shape *shape, const uint8_t *q8,
 {
     lsa_status st = check_index_shape(shape);
     if (st != LSA_OK) return st;
+    if ((st = dense_keys_only(shape)) != LSA_OK) return st;
     if ((st = check_keys(key_dtype, keys, key_scale)) != LSA_OK) return st;
     if (key_dtype != LSA_KEY_FP8_E4M3) return LSA_ERR_BAD_DTYPE; // 8-bit x 8-bit products
     if (!q8 || !q_scale || !w || !scores) return LSA_ERR_NULL_POINTER;
@@ -360,6 +389,7 @@ lsa_status lsa_index_select(const lsa_index_shape *shape, lsa_budget budget, con
     a.kscale = key_scale;
     a.out = scores;
     a.fp8 = key_dtype == LSA_KEY_FP8_E4M3;
+    if ((st = set_paged_keys(shape, a)) != LSA_OK) return st;
     lsa::SelectArgs s = select_args(shape, budget);
     s.scores = scores;
     s.out = idx;
@@ -430,6 +460,7 @@ lsa_status lsa_page_summary(const lsa_index_shape *shape, int32_t page_size, con
         shape->batch > kMaxGridYZ)
         return LSA_ERR_BAD_SHAPE;
     if (shape->head_dim != 64 && shape->head_dim != 128) return LSA_ERR_UNSUPPORTED;
+    if (dense_keys_only(shape) != LSA_OK) return LSA_ERR_UNSUPPORTED;
     if (!pow2(page_size) || page_size > 256) return LSA_ERR_BAD_SHAPE;
     lsa_status st = check_keys(key_dtype, keys, key_scale);
     if (st != LSA_OK) return st;
@@ -454,6 +485,7 @@ lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int3
 {
     lsa_status st = check_index_shape(shape);
     if (st != LSA_OK) return st;
+    if ((st = dense_keys_only(shape)) != LSA_OK) return st;
     if ((st = check_budget(budget)) != LSA_OK) return st;
     if (!pow2(page_size) || page_size < 32 || page_size > 256) return LSA_ERR_BAD_SHAPE;
     if (m_pages < 1 || m_pages > 65536) return LSA_ERR_BAD_SHAPE;
@@ -736,7 +768,7 @@ lsa_status lsa_index_scores_backward(const lsa_index_shape *shape, lsa_budget bu
     if (budget.sink < 0 || budget.window < 0 || (int64_t)budget.sink + budget.window > k)
         return LSA_ERR_BAD_SHAPE;
     if (!lsa::index_bwd_supported(shape->n_heads, shape->head_dim)) return LSA_ERR_UNSUPPORTED;
-    if (shape->n_q > kMaxGridYZ) return LSA_ERR_UNSUPPORTED;
+    if (shape->n_q > kMaxGridYZ || dense_keys_only(shape) != LSA_OK) return LSA_ERR_UNSUPPORTED;
     lsa_status st = check_ragged(shape);
     if (st != LSA_OK) return st;
     if (!q || !w || !keys || !idx || !d_scores || !d_q || !d_w || !d_keys) return LSA_ERR_NULL_POINTER;

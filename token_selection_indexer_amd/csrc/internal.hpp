@@ -54,7 +54,19 @@ struct ScoreArgs {
     // head); `q` is then unused and the keys must be e4m3 too
     const uint8_t *q8;
     const float *q_scale; // [B, n_q, H]
+    // Paged keys (btab != nullptr): keys and kscale are pools of n_blocks blocks of 2^lbs rows,
+    // and key row s of sequence b is pool row btab[b * bps + (s >> lbs)] << lbs | s & (2^lbs - 1)
+    // (a table entry outside [0, n_blocks): that block's scores are -inf).  Flat stream path.
+    const int32_t *btab;
+    int lbs, bps;
+    int64_t n_blocks;
 };
+
+// Block-table entries a paged scoring workgroup caches in LDS (its key range's blocks).
+constexpr int kPagedTab = 512;
+// Whether the paged form of the scoring launch takes this shape (the flat stream path, with a
+// workgroup's key range covering at most kPagedTab table entries).
+bool scores_paged_ok(const ScoreArgs &a);
 
 // Per-row e4m3 quantisation: scale[r] = amax / 448 (1 for a zero row), codes = round to
 // nearest even e4m3fn of x / scale, saturating.  x bf16 [rows, d], d in {64, 128}.

@@ -348,14 +348,20 @@ __device__ __forceinline__ void slice_compact(const ScoreArgs &a, const uint32_t
 // slice of a.hist_fine / a.hist_coarse, so the selection that follows reads the row's exact
 // threshold bin instead of sampling the row.  With a.slice_ent (a workgroup owns at most
 // kSliceSpan keys) it also stages those scores in LDS and leaves its slice (slice_compact).
+// PAGED: the keys (and scales) are pools of blocks of 2^lbs >= 32 rows under a block table.  A
+// 32-key block then lies inside one table block (blocks start at multiples of 32 and the last
+// one is not moved back: its rows past the keys are pool rows of the same table block, read and
+// masked).  The workgroup's table entries are cached in LDS first, so a lookup waits on LDS
+// only, never behind the key loads in flight.
 template <bool FP8, int D, int H, int MT, bool ONEQ, bool FINE, int WAVES, int BPW, int PD = 1,
-          bool HIST = false>
+          bool HIST = false, bool PAGED = false>
 __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
 {
     using G = Geo<H, MT, ONEQ>;
     using KB = KeyBlock<FP8, D>;
     constexpr int KS = D / 16;
     static_assert(PD >= 1 && (BPW == 0 || PD < BPW), "ring shape");
+    static_assert(!(PAGED && FINE), "paged keys: flat rows only");
     static_assert(!HIST || (BPW == 0 && !FINE && G::NQW == 1 && G::SPLIT), "histogram launch");
     constexpr int HBINS = 2048;
     // two slabs per wave: block i is transposed in slab i&1 while block i-1 may still be read
@@ -420,8 +426,9 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         }
     }
 
-    const uint8_t *keys_b = reinterpret_cast<const uint8_t *>(a.keys) + (int64_t)b * a.n_keys * KB::RB;
-    const float *scale_b = FP8 ? a.kscale + (int64_t)b * a.n_keys : nullptr;
+    const uint8_t *keys_b = reinterpret_cast<const uint8_t *>(a.keys) +
+                            (PAGED ? 0 : (int64_t)b * a.n_keys * KB::RB); // a pool: pool rows
+    const float *scale_b = FP8 ? a.kscale + (PAGED ? 0 : (int64_t)b * a.n_keys) : nullptr;
     const int32_t *pages_row = FINE ? a.pages + ((int64_t)b * a.n_q + t0) * a.m_pages : nullptr;
     const int64_t n_blocks = (a.n_out + 31) / 32;
     // blocks per wave; the workgroup's waves interleave over its contiguous range of blocks
@@ -429,6 +436,23 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
                                       ((int64_t)gridDim.x * WAVES));
     // the slices need the workgroup's range staged whole in LDS (the host launches them so)
     const bool stage = HIST && a.slice_ent && bpw * WAVES * 32 <= kSliceSpan;
+    // PAGED: the table entries of the workgroup's blocks [x * bpw * WAVES, (x + 1) * bpw * WAVES)
+    // (the host keeps them within kPagedTab; entries past the table read as outside the pool)
+    __shared__ int32_t ptab[PAGED ? kPagedTab : 1];
+    int64_t pg0 = 0;
+    if constexpr (PAGED) {
+        pg0 = ((int64_t)blockIdx.x * bpw * WAVES * 32) >> a.lbs;
+        const int32_t *tab_b = a.btab + (int64_t)b * a.bps;
+        for (int i = threadIdx.x; i < kPagedTab; i += WAVES * kWave)
+            ptab[i] = pg0 + i < a.bps ? tab_b[pg0 + i] : -1;
+        __syncthreads();
+    }
+    // pool row of key row `row` (a multiple of 32 in the workgroup's range), -1: outside the pool
+    auto pool_row = [&](int64_t row) -> int64_t {
+        const int32_t e = ptab[(int)((row >> a.lbs) - pg0)];
+        return e >= 0 && e < a.n_blocks ? ((int64_t)e << a.lbs) | (row & ((int64_t(1) << a.lbs) - 1))
+                                        : int64_t(-1);
+    };
     // this lane's byte offsets inside a block (contiguous 1 KB pieces)
     uint32_t lane_off[KB::NP];
 #pragma unroll
@@ -440,6 +464,7 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
     struct Blk {
         int64_t s0, row0; // first output slot and first key row of the block
         int64_t fresh;    // rows below this were already covered by the previous block
+        int64_t pool;     // PAGED: pool row of row0 (-1: outside the pool; its scores are -inf)
         bool valid, live;
     };
     // BPW == 0 (flat rows, n_out == n_keys >= 32): every block is loaded in full and without a
@@ -453,10 +478,12 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         const int64_t blk = ((int64_t)blockIdx.x * bpw + it) * WAVES + wv_id;
         k.valid = blk < n_blocks;
         k.fresh = 0;
+        k.pool = 0;
         if constexpr (FLAT_LOOP) {
-            k.s0 = k.row0 = min(blk * 32, a.n_keys - 32);
+            k.s0 = k.row0 = PAGED ? blk * 32 : min(blk * 32, a.n_keys - 32);
             k.fresh = blk * 32;
             k.live = k.valid && k.s0 < hi_all && k.s0 + 32 > lo_all;
+            if constexpr (PAGED) k.pool = pool_row(k.row0);
             return k;
         }
         k.s0 = blk * 32;
@@ -471,6 +498,7 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         } else {
             k.row0 = k.s0;
             k.live = k.s0 < hi_all && k.s0 + 32 > lo_all;
+            if constexpr (PAGED) k.pool = pool_row(k.row0);
         }
         return k;
     };
@@ -478,6 +506,15 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
         (int64_t)a.batch * a.n_q * H * D * 2 >= KB::BB ? reinterpret_cast<const uint8_t *>(a.q)
                                                         : keys_b;
     auto fetch = [&](const Blk &k, KB &kb, float &sc, bool dummy = false) {
+        if constexpr (PAGED) { // the whole block from one table block (pool row 0 if outside)
+            if (!FLAT_LOOP && !k.live) return;
+            const int64_t r0 = k.pool < 0 ? 0 : k.pool;
+            const uint8_t *base = FLAT_LOOP && dummy ? dummy_base : keys_b + r0 * KB::RB;
+#pragma unroll
+            for (int i = 0; i < KB::NP; ++i) kb.raw[i] = ld16_nt(base + lane_off[i]);
+            if (FP8) sc = scale_b[r0 + n];
+            return;
+        }
         if constexpr (FLAT_LOOP) { // keys are read once: non-temporal (about 10% faster)
             // a prefetch past the wave's last block (never used) reads a cached, in-bounds
             // block instead: q when it holds a block's bytes, else the sequence's first keys
@@ -552,6 +589,12 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
             if (FP8) {
 #pragma unroll
                 for (int u = 0; u < G::NQL; ++u) part[u] *= sq[cs];
+            }
+            if constexpr (PAGED) {
+                if (cb.pool < 0) {
+#pragma unroll
+                    for (int u = 0; u < G::NQL; ++u) part[u] = -INFINITY;
+                }
             }
         }
 
@@ -870,7 +913,7 @@ hipError_t launch_flat(const ScoreArgs &a, hipStream_t st)
     using G = Geo<H, MT, false>;
     if (a.q8) { // fp8 queries: the tile kernel for every shape (keys e4m3)
         if constexpr (FP8) {
-            if (a.hist_fine) return hipErrorInvalidValue;
+            if (a.hist_fine || a.btab) return hipErrorInvalidValue;
             // 256-key tiles: 2 x 36 KB of LDS at d = 128
             constexpr int WAVES = 8, KB = 256;
             constexpr int QPB = WAVES * G::NQW;
@@ -899,24 +942,40 @@ hipError_t launch_flat(const ScoreArgs &a, hipStream_t st)
             dim3 grid((unsigned)long_groups(a, rows), (unsigned)rows, (unsigned)a.batch);
             if constexpr (G::NQW == 1 && G::SPLIT) {
                 if (a.hist_fine) {
-                    hipLaunchKernelGGL(
-                        (score_stream_kernel<FP8, D, H, MT, false, false, WAVES, 0, PD, true>),
-                        grid, dim3(WAVES * kWave), 0, st, a);
+                    if (a.btab)
+                        hipLaunchKernelGGL(
+                            (score_stream_kernel<FP8, D, H, MT, false, false, WAVES, 0, PD, true, true>),
+                            grid, dim3(WAVES * kWave), 0, st, a);
+                    else
+                        hipLaunchKernelGGL(
+                            (score_stream_kernel<FP8, D, H, MT, false, false, WAVES, 0, PD, true>),
+                            grid, dim3(WAVES * kWave), 0, st, a);
                     return hipGetLastError();
                 }
             }
             if (a.hist_fine) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, false, false, WAVES, 0, PD>),
-                               grid, dim3(WAVES * kWave), 0, st, a);
+            if (a.btab)
+                hipLaunchKernelGGL(
+                    (score_stream_kernel<FP8, D, H, MT, false, false, WAVES, 0, PD, false, true>),
+                    grid, dim3(WAVES * kWave), 0, st, a);
+            else
+                hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, false, false, WAVES, 0, PD>),
+                                   grid, dim3(WAVES * kWave), 0, st, a);
         } else {
             if (a.hist_fine) return hipErrorInvalidValue;
             dim3 grid((unsigned)((n_blocks + WAVES * BPW_SHORT - 1) / (WAVES * BPW_SHORT)),
                       (unsigned)rows, (unsigned)a.batch);
-            hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, false, false, WAVES, BPW_SHORT, 1>),
-                               grid, dim3(WAVES * kWave), 0, st, a);
+            if (a.btab)
+                hipLaunchKernelGGL(
+                    (score_stream_kernel<FP8, D, H, MT, false, false, WAVES, BPW_SHORT, 1, false, true>),
+                    grid, dim3(WAVES * kWave), 0, st, a);
+            else
+                hipLaunchKernelGGL(
+                    (score_stream_kernel<FP8, D, H, MT, false, false, WAVES, BPW_SHORT, 1>), grid,
+                    dim3(WAVES * kWave), 0, st, a);
         }
     } else {
-        if (a.hist_fine) return hipErrorInvalidValue;
+        if (a.hist_fine || a.btab) return hipErrorInvalidValue;
         // 256-key tiles (139 KB of LDS, one workgroup per CU) where registers already limit
         // the CU to one workgroup (H = 64, d = 128: 252 VGPRs); 128-key tiles elsewhere, so two
         // workgroups can share a CU
@@ -937,6 +996,7 @@ hipError_t launch_fine(const ScoreArgs &a, hipStream_t st)
     // are short, so the launch is one round of latency, not a chain of them)
     constexpr int WAVES = 4, BPW = 2;
     const int64_t n_blocks = (a.n_out + 31) / 32;
+    if (a.btab) return hipErrorInvalidValue;
     dim3 grid((unsigned)((n_blocks + WAVES * BPW - 1) / (WAVES * BPW)), (unsigned)a.n_q,
               (unsigned)a.batch);
     hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, true, true, WAVES, BPW>), grid,
@@ -967,6 +1027,21 @@ hipError_t dispatch(const ScoreArgs &a, hipStream_t st, bool fine)
 }
 
 } // namespace
+
+bool scores_paged_ok(const ScoreArgs &a)
+{
+    if (a.q8 || a.lbs < 5 || !scores_supported(a.heads, a.dim)) return false;
+    // the flat stream path of launch_flat (queries per wave: 32 * MT / H)
+    const int nqw = 32 * (a.heads == 64 ? 2 : 1) / a.heads;
+    if (a.n_q > 2 * nqw) return false;
+    const int64_t rows = (a.n_q + nqw - 1) / nqw;
+    int64_t span = 2 * STREAM_WAVES * 32; // a short launch: two blocks per wave
+    if (long_launch(a, rows)) {
+        const int64_t n_blocks = (a.n_out + 31) / 32, gx = long_groups(a, rows);
+        span = (n_blocks + gx * STREAM_WAVES - 1) / (gx * STREAM_WAVES) * STREAM_WAVES * 32;
+    }
+    return ((span - 1) >> a.lbs) + 2 <= kPagedTab;
+}
 
 bool scores_supported(int heads, int dim)
 {

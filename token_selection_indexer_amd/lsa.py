@@ -34,11 +34,14 @@ MAX_ATTN_LAYERS = 8
 
 class IndexShape(ctypes.Structure):
     """lsa_index_shape.  seq_len / seq_pos0: device pointers of per-sequence int32 arrays (ragged
-    batches) or None."""
+    batches) or None.  block_table / block_size / blocks_per_seq / n_blocks: paged indexer keys
+    (the table a device pointer), or None / 0 for dense keys."""
     _fields_ = [("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("kv_len", ctypes.c_int64),
                 ("q_pos0", ctypes.c_int64), ("seq_len", ctypes.c_void_p),
-                ("seq_pos0", ctypes.c_void_p)]
+                ("seq_pos0", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("block_size", ctypes.c_int32), ("blocks_per_seq", ctypes.c_int32),
+                ("n_blocks", ctypes.c_int64)]
 
 
 class Budget(ctypes.Structure):
@@ -264,11 +267,12 @@ def _key_args(keys: torch.Tensor, key_scale: Optional[torch.Tensor]):
     raise ValueError(f"keys must be bf16 or e4m3 codes, got {keys.dtype}")
 
 
-def _check_index_operands(q, w, keys):
+def _check_index_operands(q, w, keys, paged=False):
+    """paged: keys is a pool [n_blocks, block_size, d] (and key_scale [n_blocks, block_size])."""
     B, T, H, _ = q.shape
     _need(w, "w", torch.float32, shape=(B, T, H), device=q.device)
     _need(keys, "keys", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), dim=3, device=q.device)
-    if keys.shape[0] != B or keys.shape[2] != q.shape[3]:
+    if (not paged and keys.shape[0] != B) or keys.shape[2] != q.shape[3]:
         raise ValueError(f"keys {tuple(keys.shape)} do not match q {tuple(q.shape)}")
 
 
@@ -283,21 +287,35 @@ def _ragged(shape: IndexShape, device, seq_lens=None, seq_pos0=None) -> IndexSha
 
 
 def index_shape(q: torch.Tensor, keys: torch.Tensor, q_pos0: Optional[int] = None,
-                seq_lens=None, seq_pos0=None) -> IndexShape:
+                seq_lens=None, seq_pos0=None, block_table=None, kv_len=None) -> IndexShape:
+    """block_table [B, blocks_per_seq] int32: keys is a pool [n_blocks, block_size, d] of paged
+    keys (kv_len defaults to blocks_per_seq * block_size)."""
     B, T, H, d = q.shape
-    L = keys.shape[1]
+    if block_table is None:
+        L = keys.shape[1]
+    else:
+        _need(block_table, "block_table", torch.int32, 2, device=q.device)
+        if block_table.shape[0] != B:
+            raise ValueError(f"block_table {tuple(block_table.shape)} does not match q {tuple(q.shape)}")
+        L = block_table.shape[1] * keys.shape[1] if kv_len is None else kv_len
     sh = IndexShape(B, T, H, d, L, L - T if q_pos0 is None else q_pos0)
+    if block_table is not None:
+        sh.block_table = block_table.data_ptr()
+        sh.block_size = keys.shape[1]
+        sh.blocks_per_seq = block_table.shape[1]
+        sh.n_blocks = keys.shape[0]
     return _ragged(sh, q.device, seq_lens, seq_pos0)
 
 
 def index_scores(q, w, keys, key_scale=None, q_pos0=None, out=None, stream=None, seq_lens=None,
-                 seq_pos0=None):
+                 seq_pos0=None, block_table=None, kv_len=None):
     """scores [B, n_q, L] fp32 (q_pos0 defaults to L - n_q: the queries are the last tokens;
-    seq_lens / seq_pos0: per-sequence int32 device tensors for a ragged batch)."""
+    seq_lens / seq_pos0: per-sequence int32 device tensors for a ragged batch; block_table:
+    paged keys, see index_shape)."""
     _need(q, "q", torch.bfloat16, 4)
-    _check_index_operands(q, w, keys)
+    _check_index_operands(q, w, keys, block_table is not None)
     kd, ks = _key_args(keys, key_scale)
-    shape = index_shape(q, keys, q_pos0, seq_lens, seq_pos0)
+    shape = index_shape(q, keys, q_pos0, seq_lens, seq_pos0, block_table, kv_len)
     out = _out(out, "out", (shape.batch, shape.n_q, shape.kv_len), torch.float32, q.device)
     lsa_index_scores(shape, q, w, keys, kd, ks, out, stream)
     return out
@@ -333,13 +351,14 @@ def index_scores_q8(q8, q_scale, w, keys, key_scale, q_pos0=None, out=None, stre
 
 
 def index_select(q, w, keys, key_scale, k, sink, window, q_pos0=None, scores=None, idx=None,
-                 ws: Optional[Workspace] = None, stream=None, seq_lens=None, seq_pos0=None):
+                 ws: Optional[Workspace] = None, stream=None, seq_lens=None, seq_pos0=None,
+                 block_table=None, kv_len=None):
     """Scores [B, n_q, L] fp32 and the selection idx [B, n_q, k] int32 in one call (fused for
-    decode): the outputs of index_scores followed by topk_select."""
+    decode): the outputs of index_scores followed by topk_select (paged keys as there)."""
     _need(q, "q", torch.bfloat16, 4)
-    _check_index_operands(q, w, keys)
+    _check_index_operands(q, w, keys, block_table is not None)
     kd, ks = _key_args(keys, key_scale)
-    shape = index_shape(q, keys, q_pos0, seq_lens, seq_pos0)
+    shape = index_shape(q, keys, q_pos0, seq_lens, seq_pos0, block_table, kv_len)
     B, T, L = shape.batch, shape.n_q, shape.kv_len
     scores = _out(scores, "scores", (B, T, L), torch.float32, q.device)
     idx = _out(idx, "idx", (B, T, k), torch.int32, q.device)
