@@ -810,12 +810,12 @@ def _key_pool(keys, scale, bs, spare, seed, bad=()):
     return pool, spool, tab.to(keys.device)
 
 
-def _paged_scores_case(B, T, L, H, kd, bs, seed, fused=None, seq_lens=None, bad=()):
+def _paged_scores_case(B, T, L, H, kd, bs, seed, fused=None, seq_lens=None, bad=(), d=128):
     """Scores (and, with fused = (k, S, W), the fused selection) over a paged copy of the keys
     equal those over the dense keys bit for bit; blocks whose table entry lies outside the pool
     score -inf, and the selection is the one from those scores."""
     w = Workload(name="p", index=IndexShape(batch=B, n_q=T, kv_len=L, q_pos0=L - T, heads=H,
-                                            head_dim=128, key_dtype=kd),
+                                            head_dim=d, key_dtype=kd),
                  budget=DECODE_128K.budget, attn=DECODE_128K.attn, seed=seed)
     inp = inputs.index_inputs(w, DEV)
     pool, spool, tab = _key_pool(inp["keys"], inp["scale"], bs, 3, seed + 7, bad)
@@ -844,6 +844,11 @@ def _paged_scores_case(B, T, L, H, kd, bs, seed, fused=None, seq_lens=None, bad=
 ])
 def test_scores_paged_equals_dense(B, T, L, H, kd, bs):
     _paged_scores_case(B, T, L, H, kd, bs, seed=101 + bs)
+
+
+@pytest.mark.parametrize("kd,H,T", [("fp8", 64, 1), ("bf16", 8, 8)])
+def test_scores_paged_head_dim_64(kd, H, T):
+    _paged_scores_case(2, T, 3000, H, kd, 64, seed=131, d=64)
 
 
 def test_index_select_paged_fused_decode():
