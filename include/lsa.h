@@ -94,8 +94,9 @@ typedef struct {
      * block_size a power of two in [32, 2^20]; blocks_per_seq * block_size >= kv_len;
      * n_blocks * block_size < 2^31.  Only the calls that read indexer keys look at these
      * fields: lsa_index_scores and lsa_index_select take them at decode shapes (see there);
-     * lsa_page_summary, lsa_page_recall, lsa_index_scores_q8 and lsa_index_scores_backward
-     * return LSA_ERR_UNSUPPORTED for them. */
+     * lsa_page_summary and lsa_page_recall with 32 <= page_size <= block_size (a page inside
+     * one table block; a page whose entry lies outside the pool gets the zero page key);
+     * lsa_index_scores_q8 and lsa_index_scores_backward return LSA_ERR_UNSUPPORTED for them. */
     const int32_t *block_table; /* [B, blocks_per_seq] int32, device */
     int32_t block_size, blocks_per_seq;
     int64_t n_blocks;

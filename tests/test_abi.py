@@ -309,7 +309,8 @@ def test_topk_select_noalloc_rejects(L):
 
 def test_paged_keys_rejects(L):
     """Paged indexer keys: a power-of-two block size of at least 32 whose table covers kv_len;
-    scoring at decode shapes only; the other key readers take dense keys only."""
+    scoring at decode shapes only, page keys and recall with pages inside one table block; the
+    fp8-query scoring and the indexer backward take dense keys only."""
     v = ctypes.c_void_p
 
     def paged(T=1, bs=64, bps=None, nblk=1 << 12, tab=FAKE, Lk=4096):
@@ -326,9 +327,14 @@ def test_paged_keys_rejects(L):
     assert _scores_call(L, paged(tab=FAKE + 1), **fp8) == 2
     assert _scores_call(L, paged(T=64), **fp8) == 4             # prefill (the tile kernel)
     sh = paged()
-    assert L.lsa_page_summary(ctypes.byref(sh), 64, v(FAKE), lsa.KEY_FP8_E4M3, v(FAKE), 0, 1,
+    # pages inside one table block: page_size <= block_size (and pages of at least 32 keys)
+    assert L.lsa_page_summary(ctypes.byref(sh), 128, v(FAKE), lsa.KEY_FP8_E4M3, v(FAKE), 0, 1,
                               v(FAKE), None) == 4
-    assert L.lsa_page_recall(ctypes.byref(sh), lsa.Budget(256, 16, 64), 64, 8, v(FAKE), v(FAKE),
+    assert L.lsa_page_summary(ctypes.byref(sh), 16, v(FAKE), lsa.KEY_FP8_E4M3, v(FAKE), 0, 1,
+                              v(FAKE), None) == 4
+    assert L.lsa_page_summary(ctypes.byref(paged(bs=48)), 32, v(FAKE), lsa.KEY_FP8_E4M3, v(FAKE),
+                              0, 1, v(FAKE), None) == 2
+    assert L.lsa_page_recall(ctypes.byref(sh), lsa.Budget(256, 16, 127), 128, 8, v(FAKE), v(FAKE),
                              v(FAKE), v(FAKE), lsa.KEY_FP8_E4M3, v(FAKE), v(FAKE), v(FAKE),
                              v(FAKE), v(FAKE), 1 << 20, None) == 4
     assert L.lsa_index_scores_q8(ctypes.byref(sh), v(FAKE), v(FAKE), v(FAKE), v(FAKE),

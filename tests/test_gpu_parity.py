@@ -865,6 +865,35 @@ def test_scores_paged_entries_outside_the_pool():
     _paged_scores_case(2, 1, 5000, 64, "fp8", bs, seed=119, bad=[(1, 10, -1)])
 
 
+@pytest.mark.parametrize("kd,P,bs", [("fp8", 64, 64), ("fp8", 64, 256), ("bf16", 32, 128)])
+def test_hi_paged_equals_dense(kd, P, bs):
+    """Page keys and page recall over paged keys equal those over the dense keys bit for bit;
+    a table entry outside the pool gives its pages the zero key and its tokens the fine score
+    -inf."""
+    B, L = 3, 40017
+    w = Workload(name="h", index=IndexShape(batch=B, n_q=1, kv_len=L, q_pos0=L - 1, heads=64,
+                                            head_dim=128, key_dtype=kd),
+                 budget=DECODE_128K.budget, attn=DECODE_128K.attn, seed=141 + P + bs)
+    inp = inputs.index_inputs(w, DEV)
+    k, S, W, M = 1024, 64, 448, 64
+    for bad in ((), ((1, 5, -1),)):
+        say(f"paged HI {kd} P={P} bs={bs} bad={bad}")
+        pool, spool, tab = _key_pool(inp["keys"], inp["scale"], bs, 3, 143, bad)
+        pk = lsa.page_summary(inp["keys"], inp["scale"], P)
+        pk_p = lsa.page_summary(pool, spool, P, block_table=tab, kv_len=L)
+        for b, j, _ in bad:
+            pk[b, j * bs // P:(j + 1) * bs // P] = 0
+        assert torch.equal(pk_p.view(torch.int16), pk.view(torch.int16))
+        ids, cs, ci = lsa.page_recall(inp["q"], inp["w"], pk, inp["keys"], inp["scale"], k, S, W,
+                                      P, M)
+        ids_p, cs_p, ci_p = lsa.page_recall(inp["q"], inp["w"], pk, pool, spool, k, S, W, P, M,
+                                            block_table=tab, kv_len=L)
+        for b, j, _ in bad:
+            cs[b][(ci[b] >= j * bs) & (ci[b] < (j + 1) * bs)] = -math.inf
+        assert torch.equal(ids_p, ids) and torch.equal(ci_p, ci)
+        assert torch.equal(cs_p.view(torch.int32), cs.view(torch.int32))
+
+
 def test_attn_layers_per_head_cache():
     """A per-head (non-latent) cache: the layers run one after another, each equal to its own
     call."""

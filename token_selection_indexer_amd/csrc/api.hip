@@ -47,6 +47,20 @@ lsa_status dense_keys_only(const lsa_index_shape *s)
     return s && s->block_table ? LSA_ERR_UNSUPPORTED : LSA_OK;
 }
 
+// The block table of paged indexer keys (shape checked), for pages of page_size keys: a page
+// must lie inside one table block.  LSA_ERR_UNSUPPORTED otherwise.
+lsa_status paged_pages(const lsa_index_shape *s, int32_t page_size, lsa::PagedTab &pt)
+{
+    pt = lsa::PagedTab{};
+    if (!s->block_table) return LSA_OK;
+    if (page_size < 32 || page_size > s->block_size) return LSA_ERR_UNSUPPORTED;
+    while ((int64_t(1) << pt.lbs) < s->block_size) ++pt.lbs;
+    pt.btab = s->block_table;
+    pt.bps = s->blocks_per_seq;
+    pt.n_blocks = s->n_blocks;
+    return LSA_OK;
+}
+
 // Paged indexer keys (shape checked): the table fields of the scoring arguments, and whether
 // the scoring launch that `a` asks for takes them.
 lsa_status set_paged_keys(const lsa_index_shape *s, lsa::ScoreArgs &a)
@@ -460,8 +474,17 @@ lsa_status lsa_page_summary(const lsa_index_shape *shape, int32_t page_size, con
         shape->batch > kMaxGridYZ)
         return LSA_ERR_BAD_SHAPE;
     if (shape->head_dim != 64 && shape->head_dim != 128) return LSA_ERR_UNSUPPORTED;
-    if (dense_keys_only(shape) != LSA_OK) return LSA_ERR_UNSUPPORTED;
     if (!pow2(page_size) || page_size > 256) return LSA_ERR_BAD_SHAPE;
+    lsa::PagedTab pt;
+    if (shape->block_table) { // paged keys: the table checks of the scoring calls
+        lsa_index_shape chk = *shape;
+        chk.n_q = 1;
+        chk.n_heads = 64;
+        chk.q_pos0 = 0;
+        const lsa_status sc = check_index_shape(&chk);
+        if (sc != LSA_OK) return sc;
+        if (paged_pages(shape, page_size, pt) != LSA_OK) return LSA_ERR_UNSUPPORTED;
+    }
     lsa_status st = check_keys(key_dtype, keys, key_scale);
     if (st != LSA_OK) return st;
     if ((st = check_ragged(shape)) != LSA_OK) return st;
@@ -474,7 +497,7 @@ lsa_status lsa_page_summary(const lsa_index_shape *shape, int32_t page_size, con
                                                   shape->batch, shape->kv_len, shape->seq_len,
                                                   shape->head_dim, page_size, page_lo, page_hi,
                                                   static_cast<uint16_t *>(page_keys),
-                                                  static_cast<hipStream_t>(stream)));
+                                                  static_cast<hipStream_t>(stream), pt));
 }
 
 lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int32_t page_size,
@@ -485,7 +508,8 @@ lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int3
 {
     lsa_status st = check_index_shape(shape);
     if (st != LSA_OK) return st;
-    if ((st = dense_keys_only(shape)) != LSA_OK) return st;
+    lsa::PagedTab pt;
+    if ((st = paged_pages(shape, page_size, pt)) != LSA_OK) return st;
     if ((st = check_budget(budget)) != LSA_OK) return st;
     if (!pow2(page_size) || page_size < 32 || page_size > 256) return LSA_ERR_BAD_SHAPE;
     if (m_pages < 1 || m_pages > 65536) return LSA_ERR_BAD_SHAPE;
@@ -582,6 +606,10 @@ lsa_status lsa_page_recall(const lsa_index_shape *shape, lsa_budget budget, int3
     f.page = page_size;
     f.m_pages = m_pages;
     f.fp8 = key_dtype == LSA_KEY_FP8_E4M3;
+    f.btab = pt.btab; // paged keys (the page keys of stage 1 are a dense array)
+    f.lbs = pt.lbs;
+    f.bps = pt.bps;
+    f.n_blocks = pt.n_blocks;
     return device_status(lsa::launch_fine_scores(f, sm));
 }
 

@@ -62,6 +62,15 @@ struct ScoreArgs {
     int64_t n_blocks;
 };
 
+// A block table over pooled keys (btab == nullptr: dense keys): key row s of sequence b is pool
+// row btab[b * bps + (s >> lbs)] << lbs | s & (2^lbs - 1); entries outside [0, n_blocks) mark
+// blocks without keys.
+struct PagedTab {
+    const int32_t *btab = nullptr;
+    int lbs = 0, bps = 0;
+    int64_t n_blocks = 0;
+};
+
 // Block-table entries a paged scoring workgroup caches in LDS (its key range's blocks).
 constexpr int kPagedTab = 512;
 // Whether the paged form of the scoring launch takes this shape (the flat stream path, with a
@@ -128,7 +137,8 @@ hipError_t select_scratch(void **ptr);
 hipError_t launch_page_summary(const void *keys, int fp8, const float *kscale, int batch,
                                int64_t kv_len, const int32_t *seq_len, int dim, int page,
                                int64_t page_lo, int64_t page_hi, uint16_t *page_keys,
-                               hipStream_t stream);
+                               hipStream_t stream,
+                               const PagedTab &paged = PagedTab{});
 
 constexpr int kMaxAttnLayers = 8;
 

@@ -97,12 +97,14 @@ struct PageGeo {
     static constexpr int G = kWave / LPR;       // lane groups
 };
 
-template <bool FP8, int D, int P>
+// PAGED: the keys (and scales) are pools under pt's block table, a page inside one table block
+// (P <= block size); a page whose table entry lies outside the pool gets the zero key.
+template <bool FP8, int D, int P, bool PAGED = false>
 __global__ __launch_bounds__(256) void page_summary_wave_kernel(const void *keys, const float *kscale,
                                                                 int64_t kv_len, const int32_t *seq_len,
                                                                 int64_t page_lo,
                                                                 int64_t page_hi, int64_t n_pages,
-                                                                uint16_t *pk)
+                                                                uint16_t *pk, PagedTab pt)
 {
     using Geo = PageGeo<FP8, D>;
     constexpr int EPL = Geo::EPL, LPR = Geo::LPR, G = Geo::G;
@@ -112,8 +114,8 @@ __global__ __launch_bounds__(256) void page_summary_wave_kernel(const void *keys
     constexpr int ROW = D * Geo::EB;            // bytes per key row
     const int b = blockIdx.y;
     const int lane = lane_id(), g = lane / LPR, c = lane % LPR;
-    const uint8_t *kb = reinterpret_cast<const uint8_t *>(keys) + (int64_t)b * kv_len * ROW + 16 * c;
-    const float *sb = FP8 ? kscale + (int64_t)b * kv_len : nullptr;
+    const uint8_t *kb = reinterpret_cast<const uint8_t *>(keys) + (PAGED ? 0 : (int64_t)b * kv_len * ROW) + 16 * c;
+    const float *sb = FP8 ? kscale + (PAGED ? 0 : (int64_t)b * kv_len) : nullptr;
     const int64_t L = seq_keys(seq_len, b, kv_len); // this sequence's keys (rows past: +0)
 
     // a lane's raw data for one page: TPL pieces (+ TPL scales); zero past the sequence's end
@@ -121,11 +123,19 @@ __global__ __launch_bounds__(256) void page_summary_wave_kernel(const void *keys
     float scl[TPL];
     auto load = [&](int64_t p) {
         const int64_t t0 = p * P + g * TPL;
+        int64_t shift = 0; // PAGED: pool row - token position, for the whole page
+        bool here = true;  // PAGED: the page's table entry lies inside the pool
+        if constexpr (PAGED) {
+            const int64_t r0 = p * P;
+            const int32_t e = pt.btab[(int64_t)b * pt.bps + (r0 >> pt.lbs)];
+            here = e >= 0 && e < pt.n_blocks;
+            shift = here ? (((int64_t)e << pt.lbs) | (r0 & ((int64_t(1) << pt.lbs) - 1))) - r0 : 0;
+        }
         static_for<0, TPL>([&](auto J) {
             constexpr int j = decltype(J)::value;
-            const bool ok = t0 + j < L;
-            raw[j] = ok ? ld16_nt(kb + (t0 + j) * ROW) : make_uint4(0u, 0u, 0u, 0u); // read once
-            if constexpr (FP8) scl[j] = ok ? sb[t0 + j] : 0.0f;
+            const bool ok = t0 + j < L && here;
+            raw[j] = ok ? ld16_nt(kb + (t0 + j + shift) * ROW) : make_uint4(0u, 0u, 0u, 0u); // read once
+            if constexpr (FP8) scl[j] = ok ? sb[t0 + j + shift] : 0.0f;
         });
     };
 
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(256) void page_summary_wave_kernel(const void *keys
 template <bool FP8, int D, int P>
 hipError_t launch_wave(const void *keys, const float *kscale, int batch, int64_t kv_len,
                        const int32_t *seq_len, int64_t page_lo, int64_t page_hi, uint16_t *pk,
-                       hipStream_t st)
+                       hipStream_t st, const PagedTab &pt)
 {
     const int64_t n_pages = (kv_len + P - 1) / P;
     // about 2048 workgroups in all (8 per CU), each wave looping over its share of the pages
@@ -214,22 +224,30 @@ hipError_t launch_wave(const void *keys, const float *kscale, int batch, int64_t
     const int64_t need = (page_hi - page_lo + 3) / 4;
     const int64_t wg = need < want ? need : want;
     const dim3 grid((unsigned)wg, (unsigned)batch);
-    hipLaunchKernelGGL((page_summary_wave_kernel<FP8, D, P>), grid, dim3(256), 0, st, keys, kscale,
-                       kv_len, seq_len, page_lo, page_hi, n_pages, pk);
+    if (pt.btab) {
+        if constexpr (P >= 32)
+            hipLaunchKernelGGL((page_summary_wave_kernel<FP8, D, P, true>), grid, dim3(256), 0, st,
+                               keys, kscale, kv_len, seq_len, page_lo, page_hi, n_pages, pk, pt);
+        else
+            return hipErrorInvalidValue;
+    } else {
+        hipLaunchKernelGGL((page_summary_wave_kernel<FP8, D, P>), grid, dim3(256), 0, st, keys,
+                           kscale, kv_len, seq_len, page_lo, page_hi, n_pages, pk, pt);
+    }
     return hipGetLastError();
 }
 
 template <bool FP8, int D>
 hipError_t launch_wave_p(const void *keys, const float *kscale, int batch, int64_t kv_len,
                          const int32_t *seq_len, int P, int64_t page_lo, int64_t page_hi,
-                         uint16_t *pk, hipStream_t st, bool &done)
+                         uint16_t *pk, hipStream_t st, bool &done, const PagedTab &pt)
 {
     done = true;
     switch (P) {
 #define LSA_PW(PP)                                                                                  \
     case PP:                                                                                        \
         if constexpr (PP >= PageGeo<FP8, D>::G)                                                     \
-            return launch_wave<FP8, D, PP>(keys, kscale, batch, kv_len, seq_len, page_lo, page_hi, pk, st); \
+            return launch_wave<FP8, D, PP>(keys, kscale, batch, kv_len, seq_len, page_lo, page_hi, pk, st, pt); \
         break;
         LSA_PW(1) LSA_PW(2) LSA_PW(4) LSA_PW(8) LSA_PW(16) LSA_PW(32) LSA_PW(64) LSA_PW(128) LSA_PW(256)
 #undef LSA_PW
@@ -242,7 +260,7 @@ hipError_t launch_wave_p(const void *keys, const float *kscale, int batch, int64
 template <bool FP8>
 hipError_t launch_p(const void *keys, const float *kscale, int batch, int64_t kv_len,
                     const int32_t *seq_len, int D, int P, int64_t page_lo, int64_t page_hi,
-                    uint16_t *pk, hipStream_t st)
+                    uint16_t *pk, hipStream_t st, const PagedTab &pt)
 {
     // pages of at least one 16-byte piece per lane group take the one-wave-per-page kernel;
     // smaller pages (P <= 8) the per-element one.  Both pointers are 16-byte aligned (checked
@@ -250,10 +268,11 @@ hipError_t launch_p(const void *keys, const float *kscale, int batch, int64_t kv
     bool done = false;
     hipError_t e = hipSuccess;
     if (D == 128)
-        e = launch_wave_p<FP8, 128>(keys, kscale, batch, kv_len, seq_len, P, page_lo, page_hi, pk, st, done);
+        e = launch_wave_p<FP8, 128>(keys, kscale, batch, kv_len, seq_len, P, page_lo, page_hi, pk, st, done, pt);
     else if (D == 64)
-        e = launch_wave_p<FP8, 64>(keys, kscale, batch, kv_len, seq_len, P, page_lo, page_hi, pk, st, done);
+        e = launch_wave_p<FP8, 64>(keys, kscale, batch, kv_len, seq_len, P, page_lo, page_hi, pk, st, done, pt);
     if (done) return e;
+    if (pt.btab) return hipErrorInvalidValue; // paged pages are at least 32 keys
     const int64_t n_pages = (kv_len + P - 1) / P;
     const int64_t threads = (page_hi - page_lo) * (D / 2);
     const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)batch);
@@ -275,13 +294,13 @@ hipError_t launch_p(const void *keys, const float *kscale, int batch, int64_t kv
 hipError_t launch_page_summary(const void *keys, int fp8, const float *kscale, int batch,
                                int64_t kv_len, const int32_t *seq_len, int dim, int page,
                                int64_t page_lo, int64_t page_hi, uint16_t *page_keys,
-                               hipStream_t stream)
+                               hipStream_t stream, const PagedTab &paged)
 {
     if (page_hi <= page_lo || batch == 0) return hipSuccess;
     return fp8 ? launch_p<true>(keys, kscale, batch, kv_len, seq_len, dim, page, page_lo, page_hi,
-                                page_keys, stream)
+                                page_keys, stream, paged)
                : launch_p<false>(keys, kscale, batch, kv_len, seq_len, dim, page, page_lo, page_hi,
-                                 page_keys, stream);
+                                 page_keys, stream, paged);
 }
 
 } // namespace lsa

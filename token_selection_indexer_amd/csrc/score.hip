@@ -361,7 +361,6 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
     using KB = KeyBlock<FP8, D>;
     constexpr int KS = D / 16;
     static_assert(PD >= 1 && (BPW == 0 || PD < BPW), "ring shape");
-    static_assert(!(PAGED && FINE), "paged keys: flat rows only");
     static_assert(!HIST || (BPW == 0 && !FINE && G::NQW == 1 && G::SPLIT), "histogram launch");
     constexpr int HBINS = 2048;
     // two slabs per wave: block i is transposed in slab i&1 while block i-1 may still be read
@@ -438,18 +437,20 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
     const bool stage = HIST && a.slice_ent && bpw * WAVES * 32 <= kSliceSpan;
     // PAGED: the table entries of the workgroup's blocks [x * bpw * WAVES, (x + 1) * bpw * WAVES)
     // (the host keeps them within kPagedTab; entries past the table read as outside the pool)
-    __shared__ int32_t ptab[PAGED ? kPagedTab : 1];
+    __shared__ int32_t ptab[PAGED && !FINE ? kPagedTab : 1];
     int64_t pg0 = 0;
-    if constexpr (PAGED) {
+    if constexpr (PAGED && !FINE) {
         pg0 = ((int64_t)blockIdx.x * bpw * WAVES * 32) >> a.lbs;
         const int32_t *tab_b = a.btab + (int64_t)b * a.bps;
         for (int i = threadIdx.x; i < kPagedTab; i += WAVES * kWave)
             ptab[i] = pg0 + i < a.bps ? tab_b[pg0 + i] : -1;
         __syncthreads();
     }
-    // pool row of key row `row` (a multiple of 32 in the workgroup's range), -1: outside the pool
+    // pool row of key row `row` (a multiple of 32 in the workgroup's range), -1: outside the pool.
+    // FINE: the rows of a recalled page, one table block per block of 32 (a wave-uniform load)
     auto pool_row = [&](int64_t row) -> int64_t {
-        const int32_t e = ptab[(int)((row >> a.lbs) - pg0)];
+        const int32_t e = FINE ? a.btab[(int64_t)b * a.bps + (row >> a.lbs)]
+                               : ptab[(int)((row >> a.lbs) - pg0)];
         return e >= 0 && e < a.n_blocks ? ((int64_t)e << a.lbs) | (row & ((int64_t(1) << a.lbs) - 1))
                                         : int64_t(-1);
     };
@@ -495,6 +496,7 @@ __global__ __launch_bounds__(WAVES *kWave) void score_stream_kernel(ScoreArgs a)
             const int pid = pages_row[pi];
             k.row0 = (int64_t)pid * a.page + (k.s0 - pi * a.page);
             k.live = pid >= 0 && k.row0 < hi_all && k.row0 + 32 > lo_all;
+            if constexpr (PAGED) k.pool = k.live ? pool_row(k.row0) : 0;
         } else {
             k.row0 = k.s0;
             k.live = k.s0 < hi_all && k.s0 + 32 > lo_all;
@@ -996,9 +998,13 @@ hipError_t launch_fine(const ScoreArgs &a, hipStream_t st)
     // are short, so the launch is one round of latency, not a chain of them)
     constexpr int WAVES = 4, BPW = 2;
     const int64_t n_blocks = (a.n_out + 31) / 32;
-    if (a.btab) return hipErrorInvalidValue;
     dim3 grid((unsigned)((n_blocks + WAVES * BPW - 1) / (WAVES * BPW)), (unsigned)a.n_q,
               (unsigned)a.batch);
+    if (a.btab) {
+        hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, true, true, WAVES, BPW, 1, false, true>),
+                           grid, dim3(WAVES * kWave), 0, st, a);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((score_stream_kernel<FP8, D, H, MT, true, true, WAVES, BPW>), grid,
                        dim3(WAVES * kWave), 0, st, a);
     return hipGetLastError();

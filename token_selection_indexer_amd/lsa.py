@@ -386,26 +386,39 @@ def topk_select(scores, k, sink, window, kv_len, q_pos0, cand_ids=None, out=None
 
 
 def page_summary(keys, key_scale, page, page_lo=0, page_hi=None, out=None, stream=None,
-                 seq_lens=None):
-    """page keys [B, ceil(L/P), d] bf16."""
+                 seq_lens=None, block_table=None, kv_len=None):
+    """page keys [B, ceil(L/P), d] bf16.  block_table [B, blocks_per_seq] int32: keys (and
+    key_scale) are pools [n_blocks, block_size, d] with page <= block_size."""
     _need(keys, "keys", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), dim=3)
     kd, ks = _key_args(keys, key_scale)
-    B, L, d = keys.shape
+    if block_table is None:
+        B, L, d = keys.shape
+    else:
+        _need(block_table, "block_table", torch.int32, 2, device=keys.device)
+        B, d = block_table.shape[0], keys.shape[2]
+        L = block_table.shape[1] * keys.shape[1] if kv_len is None else kv_len
     n_pages = (L + page - 1) // page
     out = _out(out, "out", (B, n_pages, d), torch.bfloat16, keys.device)
     shape = _ragged(IndexShape(B, 1, 64, d, L, L - 1), keys.device, seq_lens)
+    if block_table is not None:
+        shape.block_table = block_table.data_ptr()
+        shape.block_size = keys.shape[1]
+        shape.blocks_per_seq = block_table.shape[1]
+        shape.n_blocks = keys.shape[0]
     lsa_page_summary(shape, page, keys, kd, ks, page_lo, n_pages if page_hi is None else page_hi,
                      out, stream)
     return out
 
 
 def page_recall(q, w, page_keys, keys, key_scale, k, sink, window, page, m_pages, q_pos0=None,
-                ws: Optional[Workspace] = None, stream=None, seq_lens=None, seq_pos0=None):
-    """(page_ids [B,n_q,M], cand_scores [B,n_q,M*P], cand_ids [B,n_q,M*P])."""
+                ws: Optional[Workspace] = None, stream=None, seq_lens=None, seq_pos0=None,
+                block_table=None, kv_len=None):
+    """(page_ids [B,n_q,M], cand_scores [B,n_q,M*P], cand_ids [B,n_q,M*P]); paged keys as for
+    index_scores, with page <= block_size."""
     _need(q, "q", torch.bfloat16, 4)
-    _check_index_operands(q, w, keys)
+    _check_index_operands(q, w, keys, block_table is not None)
     kd, ks = _key_args(keys, key_scale)
-    shape = index_shape(q, keys, q_pos0, seq_lens, seq_pos0)
+    shape = index_shape(q, keys, q_pos0, seq_lens, seq_pos0, block_table, kv_len)
     _need(page_keys, "page_keys", torch.bfloat16, device=q.device,
           shape=(shape.batch, (shape.kv_len + page - 1) // page, shape.head_dim))
     B, T = shape.batch, shape.n_q
