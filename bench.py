@@ -158,6 +158,7 @@ class Timing:
 
 
 PAGE_BLOCK = 64  # rows per block of the paged cache timed beside the dense one
+HI_PAGE_BLOCK = 256  # ... and for Hierarchical Indexing (a table block holds whole pages)
 
 
 def paged_copy(torch, kv, bs):
@@ -485,6 +486,26 @@ def extra_hi(torch, lsa, inputs, w, tm: Timing):
     d = {"page_summary": tm.both(f_summary, 0.12), "recall": tm.both(f_recall, 0.04),
          "hi_topk": tm.both(f_hi_topk, 0.02), "flat_score": tm.both(f_flat_score, 0.1),
          "flat_topk": tm.both(f_flat_topk, 0.03), "flat_index_fused": tm.both(f_flat_index, 0.12)}
+    # page keys and recall over paged keys: 256-row blocks (4 pages each) in shuffled pools
+    if L % HI_PAGE_BLOCK == 0 and HI_PAGE_BLOCK >= hi.page:
+        kpool, ktab = paged_copy(torch, inp["keys"], HI_PAGE_BLOCK)
+        spool, stab = paged_copy(torch, inp["scale"].unsqueeze(-1), HI_PAGE_BLOCK)
+        spool = spool.squeeze(-1)
+        assert torch.equal(stab, ktab)
+        pk_p = torch.empty_like(pk)
+
+        def f_summary_paged():
+            lsa.page_summary(kpool, spool, hi.page, out=pk_p, block_table=ktab, kv_len=L)
+
+        def f_recall_paged():
+            lsa.page_recall(inp["q"], inp["w"], pk, kpool, spool, b.k, b.sink, b.window, hi.page,
+                            hi.m_pages, q_pos0=s.q_pos0, ws=ws, block_table=ktab, kv_len=L)
+        f_summary_paged(), f_recall_paged()
+        torch.cuda.synchronize()
+        assert torch.equal(pk_p.view(torch.int16), pk.view(torch.int16))
+        d["page_summary_paged"] = tm.both(f_summary_paged, 0.12)
+        d["recall_paged"] = tm.both(f_recall_paged, 0.04)
+        del kpool, spool, ktab, pk_p
     f_recall(), f_hi_topk(), f_flat_index()
     torch.cuda.synchronize()
     # quality: planted pages recalled, overlap of the HI and flat dynamic picks
@@ -541,6 +562,10 @@ def extra_hi(torch, lsa, inputs, w, tm: Timing):
         "attn_layers": w.layers,
         "sparse_attn_TBps": ab / (t["attn_all_layers"] * 1e-3) / 1e12,
     }
+    if "recall_paged" in t:  # time ratios, paged over dense keys
+        res["paged_vs_dense"] = {
+            st: {"warm": t[st + "_paged"] / t[st], "cold": tc[st + "_paged"] / tc[st]}
+            for st in ("page_summary", "recall")}
     if w.layers > 1:
         res["sparse_attn_TBps_one_call"] = ab / (t["attn_layers_one_call"] * 1e-3) / 1e12
         res["attn_layers_one_call_speedup"] = t["attn_all_layers"] / t["attn_layers_one_call"]
